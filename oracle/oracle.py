@@ -1,0 +1,260 @@
+"""Python driver for the scalar C oracle of the FlashLoop packed-KV codec.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path (the HIP library and its
+binding) never imports this module, and this module never imports the product.
+
+The arithmetic lives in ``flk_oracle.c``; this file only marshals numpy arrays.  The
+method it checks is described in the FlashLoop integration RFC (vllm-rlt issue #156),
+section 3.3, and in vllm-rlt pull request #166 ("Purpose" and the review's format notes).
+
+Array conventions: BF16 tensors are numpy ``uint16`` arrays of bit patterns shaped
+``[rows, H, D]``; codes are ``uint8`` ``[rows, H, D//2]``; params are ``uint32`` (FP16
+minimum in the low half, FP16 scale in the high half), ``[ceil(rows/64), H, D]`` for K and
+``[rows, H, ceil(D/64)]`` for V; ``rows`` are ascending ``int32`` positions or ``None``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "flk_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+K, V = 0, 1
+GROUP = 64
+
+OK, E_NONFINITE, E_RANGE, E_ARG = 0, 1, 2, 3
+
+
+class OracleError(RuntimeError):
+    """Raised when the oracle rejects its input (non-finite values, FP16 overflow, shape)."""
+
+    def __init__(self, code: int, what: str):
+        names = {E_NONFINITE: "non-finite input", E_RANGE: "FP16 parameter overflow",
+                 E_ARG: "bad argument"}
+        super().__init__(f"{what}: {names.get(code, code)}")
+        self.code = code
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with plain gcc (IEEE binary32, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+            "-frounding-math", "-fexcess-precision=standard", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        sz = ctypes.c_size_t
+        L = _lib
+        L.orc_bf16_from_f32.restype = ctypes.c_uint16
+        L.orc_bf16_from_f32.argtypes = [ctypes.c_float]
+        L.orc_f16_from_f32.restype = ctypes.c_uint16
+        L.orc_f16_from_f32.argtypes = [ctypes.c_float]
+        L.orc_f32_from_f16.restype = ctypes.c_float
+        L.orc_f32_from_f16.argtypes = [ctypes.c_uint16]
+        L.orc_f32_from_bf16.restype = ctypes.c_float
+        L.orc_f32_from_bf16.argtypes = [ctypes.c_uint16]
+        for name in ("orc_bf16_from_f32_array", "orc_f16_from_f32_array", "orc_f32_from_f16_array"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [P, P, sz]
+        L.orc_num_groups.restype = sz
+        L.orc_num_groups.argtypes = [i, i, i, i]
+        L.orc_codes_bytes.restype = sz
+        L.orc_codes_bytes.argtypes = [i, i, i]
+        L.orc_params_bytes.restype = sz
+        L.orc_params_bytes.argtypes = [i, i, i, i]
+        L.orc_rows_bytes.restype = sz
+        L.orc_rows_bytes.argtypes = [i, i]
+        L.orc_quantize.restype = i
+        L.orc_quantize.argtypes = [i, i, i, i, P, P, P, i]
+        L.orc_dequantize.restype = i
+        L.orc_dequantize.argtypes = [i, i, i, i, P, P, P]
+        L.orc_encode_base.restype = i
+        L.orc_encode_base.argtypes = [i, i, i, i, P, P, P, P, i]
+        L.orc_encode_residual.restype = i
+        L.orc_encode_residual.argtypes = [i, i, i, i, i, P, P, P, P, P, i]
+        L.orc_reconstruct.restype = i
+        L.orc_reconstruct.argtypes = [i, i, i, i, i, P, P, P, P, P]
+        L.orc_decode_attn.restype = i
+        L.orc_decode_attn.argtypes = [i, i, i, i, P, P, P, ctypes.c_double, P]
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------- conversions
+
+def bf16_from_f32(x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_bf16_from_f32_array(_p(x), _p(out), x.size)
+    return out
+
+
+def f16_from_f32(x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f16_from_f32_array(_p(x), _p(out), x.size)
+    return out
+
+
+def f32_from_f16(h: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_f32_from_f16_array(_p(h), _p(out), h.size)
+    return out
+
+
+def f32_from_bf16(b: np.ndarray) -> np.ndarray:
+    """Widening is exact: a BF16 pattern is the upper half of a binary32 pattern."""
+    return (_c(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------- sizes
+
+def num_groups(kind: int, H: int, D: int, n: int) -> int:
+    return int(lib().orc_num_groups(kind, H, D, n))
+
+
+def codes_bytes(H: int, D: int, n: int) -> int:
+    return int(lib().orc_codes_bytes(H, D, n))
+
+
+def params_bytes(kind: int, H: int, D: int, n: int) -> int:
+    return int(lib().orc_params_bytes(kind, H, D, n))
+
+
+def rows_bytes(n: int, sparse: bool) -> int:
+    return int(lib().orc_rows_bytes(n, 1 if sparse else 0))
+
+
+def params_shape(kind: int, H: int, D: int, n: int):
+    return ((n + GROUP - 1) // GROUP, H, D) if kind == K else (n, H, (D + GROUP - 1) // GROUP)
+
+
+# ----------------------------------------------------------------------------- codec
+
+@dataclass
+class Stream:
+    """One encoded loop of one tensor: n compact rows (rows None = dense), codes, params."""
+    n_rows: int
+    rows: Optional[np.ndarray]
+    codes: np.ndarray
+    params: np.ndarray
+
+    def nbytes(self) -> int:
+        return self.codes.nbytes + self.params.nbytes + (0 if self.rows is None else self.rows.nbytes)
+
+
+def _check(st: int, what: str):
+    if st != OK:
+        raise OracleError(st, what)
+
+
+def quantize(kind: int, x: np.ndarray, f32_params: bool = False):
+    x = _c(x, np.uint16)
+    n, H, D = x.shape
+    codes = np.zeros((n, H, D // 2), np.uint8)
+    params = np.zeros(params_shape(kind, H, D, n), np.uint32)
+    _check(lib().orc_quantize(kind, H, D, n, _p(x), _p(codes), _p(params), int(f32_params)), "quantize")
+    return codes, params
+
+
+def dequantize(kind: int, codes: np.ndarray, params: np.ndarray, D: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    params = _c(params, np.uint32)
+    n, H = codes.shape[0], codes.shape[1]
+    out = np.zeros((n, H, D), np.uint16)
+    _check(lib().orc_dequantize(kind, H, D, n, _p(codes), _p(params), _p(out)), "dequantize")
+    return out
+
+
+def encode_base(kind: int, x: np.ndarray, f32_params: bool = False):
+    """Returns (Stream, recon) with recon = X_hat[1] as BF16 bits."""
+    x = _c(x, np.uint16)
+    T, H, D = x.shape
+    codes = np.zeros((T, H, D // 2), np.uint8)
+    params = np.zeros(params_shape(kind, H, D, T), np.uint32)
+    recon = np.zeros_like(x)
+    _check(lib().orc_encode_base(kind, H, D, T, _p(x), _p(codes), _p(params), _p(recon), int(f32_params)),
+           "encode_base")
+    return Stream(T, None, codes, params), recon
+
+
+def encode_residual(kind: int, x_rows: np.ndarray, rows: Optional[np.ndarray], recon: np.ndarray,
+                    f32_params: bool = False) -> Stream:
+    """Encode one residual loop; `recon` (X_hat[r-1]) is updated in place to X_hat[r]."""
+    x_rows = _c(x_rows, np.uint16)
+    assert recon.dtype == np.uint16 and recon.flags.c_contiguous
+    n, H, D = x_rows.shape
+    T = recon.shape[0]
+    rows_c = None if rows is None else _c(rows, np.int32)
+    codes = np.zeros((n, H, D // 2), np.uint8)
+    params = np.zeros(params_shape(kind, H, D, n), np.uint32)
+    _check(lib().orc_encode_residual(kind, H, D, T, n, _p(rows_c), _p(x_rows), _p(recon), _p(codes),
+                                     _p(params), int(f32_params)), "encode_residual")
+    return Stream(n, rows_c, codes, params)
+
+
+def reconstruct(kind: int, chain: Sequence[Stream], T: int, H: int, D: int) -> np.ndarray:
+    n_loops = len(chain)
+    n_rows = np.array([s.n_rows for s in chain], np.int32)
+    keep = [(s.rows, _c(s.codes, np.uint8), _c(s.params, np.uint32)) for s in chain]
+    P = ctypes.c_void_p
+    rows_arr = (P * n_loops)(*[(_p(r).value if r is not None else None) for r, _, _ in keep])
+    codes_arr = (P * n_loops)(*[_p(c).value for _, c, _ in keep])
+    params_arr = (P * n_loops)(*[_p(p).value for _, _, p in keep])
+    out = np.zeros((T, H, D), np.uint16)
+    _check(lib().orc_reconstruct(kind, H, D, T, n_loops, _p(n_rows), rows_arr, codes_arr, params_arr,
+                                 _p(out)), "reconstruct")
+    return out
+
+
+def encode_chain(kind: int, xs: Sequence[np.ndarray], rows_list: Sequence[Optional[np.ndarray]],
+                 f32_params: bool = False):
+    """Encode a full loop chain.  xs[0] is X[1] over all T rows; xs[r] (r >= 1) holds X[r+1]
+    at the positions rows_list[r] (all T rows when that entry is None).  Returns the list of
+    Streams and the final in-place reconstruction X_hat[R]."""
+    base, recon = encode_base(kind, xs[0], f32_params)
+    chain: List[Stream] = [base]
+    for x, rows in zip(xs[1:], rows_list[1:]):
+        chain.append(encode_residual(kind, x, rows, recon, f32_params))
+    return chain, recon
+
+
+def decode_attn(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Binary64 softmax attention of BF16 queries [Hq, D] over BF16 K/V [T, Hkv, D]."""
+    q = _c(q, np.uint16)
+    khat = _c(khat, np.uint16)
+    vhat = _c(vhat, np.uint16)
+    Hq, D = q.shape
+    T, Hkv, _ = khat.shape
+    out = np.zeros((Hq, D), np.float64)
+    _check(lib().orc_decode_attn(Hq, Hkv, D, T, _p(q), _p(khat), _p(vhat), float(softmax_scale), _p(out)),
+           "decode_attn")
+    return out
