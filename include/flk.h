@@ -1,0 +1,194 @@
+/*
+ * flk.h -- C ABI of the MI355X packed-KV codec (FlashLoop INT4 base + cross-loop residuals).
+ *
+ * The codec stores one request/layer's logical [token, KV head, channel] BF16 K or V tensor
+ * as a quantized base plus successive cross-loop residuals, each encoded against the
+ * reconstructed predecessor, and rebuilds the tensor at any depth from the packed streams.
+ * It follows the FlashLoop integration RFC (vllm-rlt issue #156), section 3.3 "Quantized base
+ * and cross-loop KV residuals", and the standalone codec of vllm-rlt pull request #166
+ * ("Purpose": INT4 codes two per byte, FP16 minimum and scale, group 64, K grouped across
+ * compact token rows per head/channel, V across channels per token/head, subtraction and
+ * addition in the compute dtype, partial groups allowed).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensors live in device memory (HBM) unless a parameter says "host".  Every pointer is
+ *    a plain device address (for example torch.Tensor.data_ptr()).  The caller allocates and
+ *    owns every buffer, including workspace; the library never allocates, frees, or keeps a
+ *    pointer after the call returns (the RFC, section 4: the runner owns the tensors, kernels
+ *    borrow them).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  Work is
+ *    enqueued on it and the call returns without synchronizing; buffers must stay untouched
+ *    until that stream work has completed.  The library never reads device data on the host
+ *    (the RFC, section 6.2: no GPU-to-CPU readback to prepare asynchronous work).
+ *  - Validation happens on the host before anything is enqueued.  On any status other than
+ *    FLK_OK nothing has been launched and no output byte has been written (the RFC, section 4:
+ *    explicit incompatible choices fail clearly).  No C++ exception crosses the ABI.
+ *  - BF16 tensors are [rows, H, D] row-major with channels contiguous.  Element (r, h, c) is
+ *    at index (r*H + h)*D + c.  BF16 data, codes and params must be 16-byte aligned, rows
+ *    4-byte aligned.
+ *  - Preconditions not checked on the host: `rows` arrays strictly ascending with values in
+ *    [0, T); inputs finite.  Non-finite inputs, FP16 overflow of a group's minimum or scale
+ *    and rows entries outside [0, T) are reported through the optional device status word
+ *    (below); outputs are then undefined, but no kernel addresses memory outside the
+ *    buffers the call describes.
+ *
+ * Packed stream layout (one loop of one tensor, n compact rows)
+ * -------------------------------------------------------------
+ *  codes   uint8 [n][H][D/2]: byte j of (row, head) holds channel 2j in its low nibble and
+ *          channel 2j+1 in its high nibble (PR #166 lists nibble order among its tests).
+ *  params  uint32, one per group: FP16 minimum in bits 0..15, FP16 scale in bits 16..31.
+ *          K: [ceil(n/64)][H][D]  (group g of channel (h, c) covers compact rows 64g..64g+63).
+ *          V: [n][H][ceil(D/64)]  (group g of (row, h) covers channels 64g..64g+63).
+ *          The last group along the axis may be partial (statistics over its real elements).
+ *  rows    int32 [n], ascending logical positions of the compact rows (the RFC's explicit
+ *          logical-position-to-compact-row map); NULL for a dense stream (n == T).  A
+ *          position a residual stream does not list inherits its predecessor (an absent
+ *          residual is not a code-0 residual, RFC section 3.3).
+ *  Codes and params for a group are computed with the FP16-rounded minimum and scale:
+ *    scale32 = (max - min) / 15 (binary32), min16 = fp16(min), scale16 = fp16(scale32),
+ *    code = clamp(round_half_even((x - min16) / scale16), 0, 15), or 0 when scale16 == 0
+ *    (the constant group), and decoding is bf16(min16 + scale16 * code).  Min and max use
+ *    the total order in which -0 < +0.
+ */
+#ifndef FLK_H
+#define FLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLK_ABI_VERSION 1
+#define FLK_GROUP 64       /* group size (PR #166 "Purpose": default group size 64)        */
+#define FLK_MAX_LOOPS 8    /* longest chain (base + residuals) one call accepts             */
+#define FLK_MAX_HEAD_DIM 512
+
+typedef enum flk_status {
+    FLK_OK = 0,
+    FLK_E_NULL = 1,        /* a required pointer is NULL                                      */
+    FLK_E_SHAPE = 2,       /* a size is out of range (T, n_rows, H, D, n_loops, heads ...)     */
+    FLK_E_ALIGN = 3,       /* a pointer is not aligned as documented                           */
+    FLK_E_DESC = 4,        /* descriptor fields not recognised (version/format/kind/group ...) */
+    FLK_E_UNSUPPORTED = 5, /* a valid request this library does not implement                  */
+    FLK_E_WORKSPACE = 6,   /* workspace missing or smaller than flk_workspace_bytes()          */
+    FLK_E_LAUNCH = 7       /* the HIP runtime rejected a kernel launch                         */
+} flk_status;
+
+/* Which tensor a stream encodes; it selects the group axis and is recorded in the
+ * descriptor (the PR #166 review asks for format, axis and group size in the descriptor). */
+enum { FLK_KIND_K = 0, FLK_KIND_V = 1 };
+enum { FLK_FMT_INT4_AFFINE = 1 };
+enum { FLK_PARAM_FP16_MIN_SCALE = 1 };
+enum { FLK_NIBBLE_LOW_EVEN = 1 };
+
+/* Bits of the optional device status word (a uint32 in device memory the caller zeroes).
+ * Encode kernels OR these in with a device atomic; they never clear it. */
+#define FLK_DEV_NONFINITE 1u  /* a group held an Inf or NaN value                           */
+#define FLK_DEV_RANGE 2u      /* a group's minimum or scale overflowed FP16                 */
+#define FLK_DEV_ROWS 4u       /* a rows entry lay outside [0, T); that row was skipped      */
+
+/* Versioned encoding descriptor (the RFC, section 6.5: bit width, group axes and sizes and
+ * depth representation travel with the data).  Fill with flk_desc_init(). */
+typedef struct flk_desc {
+    uint16_t abi_version;   /* FLK_ABI_VERSION                                             */
+    uint8_t format;         /* FLK_FMT_INT4_AFFINE                                         */
+    uint8_t kind;           /* FLK_KIND_K or FLK_KIND_V                                    */
+    uint16_t group;         /* FLK_GROUP (64); no other size is accepted                   */
+    uint8_t param_dtype;    /* FLK_PARAM_FP16_MIN_SCALE                                    */
+    uint8_t nibble_order;   /* FLK_NIBBLE_LOW_EVEN                                         */
+    int32_t n_heads;        /* H >= 1                                                      */
+    int32_t head_dim;       /* D: 8 <= D <= FLK_MAX_HEAD_DIM, D % 8 == 0                   */
+} flk_desc;
+
+/* One encoded loop of one tensor, as the host describes it to the library.  The struct is
+ * host memory; the pointers inside are device addresses. */
+typedef struct flk_stream {
+    int32_t n_rows;         /* compact rows n (n == T for a dense stream)                  */
+    int32_t reserved;       /* must be 0                                                   */
+    const int32_t* rows;    /* device, n ascending positions in [0, T), or NULL = dense    */
+    const uint8_t* codes;   /* device, flk_codes_bytes(desc, n) bytes, 16-byte aligned     */
+    const uint32_t* params; /* device, flk_params_bytes(desc, n) bytes, 16-byte aligned    */
+} flk_stream;
+/* A stream with n_rows == 0 (an empty loop) contributes nothing; its pointers are ignored. */
+
+/* ---------------------------------------------------------------- host-only helpers --- */
+
+/* Fill a descriptor with the only format this ABI version defines. */
+void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
+
+/* FLK_OK if the descriptor is well formed, else FLK_E_NULL / FLK_E_DESC / FLK_E_SHAPE. */
+flk_status flk_desc_check(const flk_desc* d);
+
+/* Storage of one stream with n compact rows (the RFC, section 7.4: the allocator budgets
+ * payload, quantization parameters and maps).  0 for a malformed descriptor or n < 0.   */
+size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows);   /* n*H*D/2                    */
+size_t flk_params_bytes(const flk_desc* d, int32_t n_rows);  /* 4 * number of groups       */
+size_t flk_rows_bytes(int32_t n_rows, int sparse);            /* 4*n if sparse, else 0      */
+
+/* Workspace of flk_decode_attn_packed for a T-token cache and n_q_heads query heads (other
+ * calls need none).  0 for malformed arguments. */
+size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads);
+
+const char* flk_status_string(flk_status s);
+int flk_abi_version(void);
+
+/* ---------------------------------------------------------------- codec calls --------- */
+
+/* Loop 1: X_hat[1] = dequantize(quantize(X[1])) (RFC section 3.3; loop 1 is dense, section
+ * 3.1).  x: BF16 [T, H, D] (input).  codes/params: the base stream (outputs, dense, n = T).
+ * recon: BF16 [T, H, D] (output) receives X_hat[1], the predecessor of loop 2.
+ * dev_status: optional device uint32 (may be NULL), see FLK_DEV_*.
+ * Errors: FLK_E_NULL, FLK_E_DESC, FLK_E_SHAPE (T < 1), FLK_E_ALIGN, FLK_E_LAUNCH.       */
+flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t* codes,
+                           uint32_t* params, void* recon, uint32_t* dev_status, void* stream);
+
+/* Loop r >= 2 (RFC section 3.3): delta[j] = bf16(X[r][j] - X_hat[r-1][p_j]) with
+ * p_j = rows[j] (or j when rows == NULL), encoded with K groups over compact rows j; then
+ * X_hat[r][p_j] = bf16(X_hat[r-1][p_j] + dequantize(quantize(delta))[j]); positions not in
+ * rows are left untouched (inheritance).
+ * x_rows: BF16 [n_rows, H, D], X[r] at the active positions only (input).
+ * rows: device int32 [n_rows] ascending positions, or NULL for a dense loop (n_rows == T).
+ * recon: BF16 [T, H, D], X_hat[r-1] on entry, X_hat[r] on exit (updated in place).
+ * codes/params: the residual stream (outputs).  n_rows == 0 (an empty loop) is allowed,
+ * ignores x_rows, rows, codes and params, and writes nothing.
+ * Errors: as flk_encode_base, plus FLK_E_SHAPE when n_rows > T or rows == NULL with
+ * n_rows != T.                                                                            */
+flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int32_t* rows,
+                               int32_t n_rows, int32_t T, void* recon, uint8_t* codes,
+                               uint32_t* params, uint32_t* dev_status, void* stream);
+
+/* Rebuild X_hat[n_loops] from the packed chain alone (RFC section 3.3: a loop-4 read of t1
+ * resolves to base + delta2, of t2 to base + delta2 + delta3, of t4 to the full chain).
+ * chain: host array of n_loops streams; chain[0] is the dense base, chain[l] the residual of
+ * loop l+1.  Each step adds in binary32 and rounds to BF16, as the encoder did, so the
+ * result equals the encoder's in-place reconstruction bit for bit.
+ * out: BF16 [T, H, D] (output).  1 <= n_loops <= FLK_MAX_LOOPS.
+ * Errors: FLK_E_NULL, FLK_E_DESC, FLK_E_SHAPE, FLK_E_ALIGN, FLK_E_LAUNCH.                */
+flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain,
+                           int32_t n_loops, void* out, void* stream);
+
+/* Single-token decode attention read directly from the packed chains (RFC section 3.3:
+ * optimized readers consume packed base/residual tiles during QK/PV instead of building a
+ * BF16 shadow cache).  out[i] = sum_t softmax_t(scale * q[i] . K_hat[t, h]) V_hat[t, h] with
+ * h = i / (n_q_heads / H) (grouped-query attention), K_hat/V_hat the chains' final depth.
+ * q: BF16 [n_q_heads, D].  out: BF16 [n_q_heads, D].  Accumulation is binary32; the
+ * result agrees with exact attention over the reconstructed BF16 K/V to about 1e-2
+ * relative, not bit for bit.  workspace: device, >= flk_attn_workspace_bytes().
+ * Requires k_desc kind K, v_desc kind V, equal H and D, D == 128, n_q_heads % H == 0,
+ * n_q_heads / H <= 16, and both chains with the same T and n_loops.
+ * Errors: FLK_E_NULL, FLK_E_DESC, FLK_E_SHAPE, FLK_E_ALIGN, FLK_E_UNSUPPORTED,
+ * FLK_E_WORKSPACE, FLK_E_LAUNCH.                                                          */
+flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T,
+                                  const void* q, int32_t n_q_heads, const flk_stream* k_chain,
+                                  const flk_stream* v_chain, int32_t n_loops,
+                                  float softmax_scale, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLK_H */

@@ -1,0 +1,201 @@
+// flk_api.cpp -- the C ABI declared in include/flk.h: host-side validation, then launches.
+//
+// Every check that can fail runs before the first HIP call, so a rejected call enqueues
+// nothing and writes nothing (the FlashLoop RFC, vllm-rlt #156, section 4: incompatible
+// explicit choices fail clearly rather than silently changing the algorithm).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/flk.h"
+#include "flk_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+flk_status check_stream_ptrs(const void* codes, const void* params) {
+  if (!codes || !params) return FLK_E_NULL;
+  if (!aligned(codes, 16) || !aligned(params, 16)) return FLK_E_ALIGN;
+  return FLK_OK;
+}
+
+size_t n_groups(const flk_desc* d, int64_t n) {
+  if (d->kind == FLK_KIND_K) return size_t((n + FLK_GROUP - 1) / FLK_GROUP) * size_t(d->n_heads) * size_t(d->head_dim);
+  return size_t(n) * size_t(d->n_heads) * size_t((d->head_dim + FLK_GROUP - 1) / FLK_GROUP);
+}
+
+// Largest element count a launch indexes; the kernels index in 64-bit, but flattened
+// (row, head) items are divided in 32-bit, so n*H must stay below 2^31.
+bool rows_fit(const flk_desc* d, int64_t n) { return n * int64_t(d->n_heads) < (int64_t(1) << 31); }
+
+flk_status to_status(hipError_t e) { return e == hipSuccess ? FLK_OK : FLK_E_LAUNCH; }
+
+flk_status load_chain(const flk_desc* d, int32_t T, const flk_stream* chain, int32_t n_loops,
+                      flk::ChainArgs* out) {
+  if (!chain) return FLK_E_NULL;
+  if (n_loops < 1 || n_loops > FLK_MAX_LOOPS) return FLK_E_SHAPE;
+  std::memset(out, 0, sizeof(*out));
+  int kept = 0;
+  for (int l = 0; l < n_loops; ++l) {
+    const flk_stream& s = chain[l];
+    if (s.reserved != 0) return FLK_E_DESC;
+    if (l == 0 && (s.rows != nullptr || s.n_rows != T)) return FLK_E_SHAPE;   // dense base
+    if (s.n_rows < 0 || s.n_rows > T) return FLK_E_SHAPE;
+    if (s.n_rows == 0) continue;          // an empty loop: every position inherits
+    if (s.rows == nullptr && s.n_rows != T) return FLK_E_SHAPE;
+    flk_status st = check_stream_ptrs(s.codes, s.params);
+    if (st != FLK_OK) return st;
+    if (s.rows && !aligned(s.rows, 4)) return FLK_E_ALIGN;
+    out->s[kept].rows = s.rows;
+    out->s[kept].codes = s.codes;
+    out->s[kept].params = s.params;
+    out->s[kept].n = s.n_rows;
+    ++kept;
+  }
+  out->n_loops = kept;
+  return FLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim) {
+  if (!d) return;
+  std::memset(d, 0, sizeof(*d));
+  d->abi_version = FLK_ABI_VERSION;
+  d->format = FLK_FMT_INT4_AFFINE;
+  d->kind = uint8_t(kind);
+  d->group = FLK_GROUP;
+  d->param_dtype = FLK_PARAM_FP16_MIN_SCALE;
+  d->nibble_order = FLK_NIBBLE_LOW_EVEN;
+  d->n_heads = n_heads;
+  d->head_dim = head_dim;
+}
+
+flk_status flk_desc_check(const flk_desc* d) {
+  if (!d) return FLK_E_NULL;
+  if (d->abi_version != FLK_ABI_VERSION || d->format != FLK_FMT_INT4_AFFINE ||
+      (d->kind != FLK_KIND_K && d->kind != FLK_KIND_V) || d->group != FLK_GROUP ||
+      d->param_dtype != FLK_PARAM_FP16_MIN_SCALE || d->nibble_order != FLK_NIBBLE_LOW_EVEN)
+    return FLK_E_DESC;
+  if (d->n_heads < 1 || d->head_dim < 8 || d->head_dim > FLK_MAX_HEAD_DIM || d->head_dim % 8 != 0)
+    return FLK_E_SHAPE;
+  if (int64_t(d->n_heads) * d->head_dim > (int64_t(1) << 20)) return FLK_E_SHAPE;
+  return FLK_OK;
+}
+
+size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows) {
+  if (flk_desc_check(d) != FLK_OK || n_rows < 0) return 0;
+  return size_t(n_rows) * size_t(d->n_heads) * size_t(d->head_dim) / 2;
+}
+
+size_t flk_params_bytes(const flk_desc* d, int32_t n_rows) {
+  if (flk_desc_check(d) != FLK_OK || n_rows < 0) return 0;
+  return 4 * n_groups(d, n_rows);
+}
+
+size_t flk_rows_bytes(int32_t n_rows, int sparse) {
+  if (n_rows < 0) return 0;
+  return sparse ? 4 * size_t(n_rows) : 0;
+}
+
+size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads) {
+  if (flk_desc_check(k_desc) != FLK_OK || T < 1 || n_q_heads < 1) return 0;
+  return flk::attn_workspace_bytes(T, k_desc->n_heads, n_q_heads);
+}
+
+const char* flk_status_string(flk_status s) {
+  switch (s) {
+    case FLK_OK: return "ok";
+    case FLK_E_NULL: return "required pointer is NULL";
+    case FLK_E_SHAPE: return "size out of range";
+    case FLK_E_ALIGN: return "pointer misaligned";
+    case FLK_E_DESC: return "descriptor not recognised";
+    case FLK_E_UNSUPPORTED: return "unsupported request";
+    case FLK_E_WORKSPACE: return "workspace missing or too small";
+    case FLK_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int flk_abi_version(void) { return FLK_ABI_VERSION; }
+
+flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t* codes,
+                           uint32_t* params, void* recon, uint32_t* dev_status, void* stream) {
+  flk_status st = flk_desc_check(d);
+  if (st != FLK_OK) return st;
+  if (!x || !recon) return FLK_E_NULL;
+  if (T < 1 || !rows_fit(d, T)) return FLK_E_SHAPE;
+  st = check_stream_ptrs(codes, params);
+  if (st != FLK_OK) return st;
+  if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
+  return to_status(flk::launch_encode(d->kind, false, x, nullptr, T, T, d->n_heads, d->head_dim,
+                                      recon, codes, params, dev_status,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int32_t* rows,
+                               int32_t n_rows, int32_t T, void* recon, uint8_t* codes,
+                               uint32_t* params, uint32_t* dev_status, void* stream) {
+  flk_status st = flk_desc_check(d);
+  if (st != FLK_OK) return st;
+  if (!recon) return FLK_E_NULL;
+  if (T < 1 || n_rows < 0 || n_rows > T || !rows_fit(d, T)) return FLK_E_SHAPE;
+  if (!aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
+  if (n_rows == 0) return FLK_OK;                 // an empty loop: every position inherits
+  if (rows == nullptr && n_rows != T) return FLK_E_SHAPE;
+  if (!x_rows) return FLK_E_NULL;
+  st = check_stream_ptrs(codes, params);
+  if (st != FLK_OK) return st;
+  if (!aligned(x_rows, 16) || (rows && !aligned(rows, 4))) return FLK_E_ALIGN;
+  return to_status(flk::launch_encode(d->kind, true, x_rows, rows, n_rows, T, d->n_heads,
+                                      d->head_dim, recon, codes, params, dev_status,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain, int32_t n_loops,
+                           void* out, void* stream) {
+  flk_status st = flk_desc_check(d);
+  if (st != FLK_OK) return st;
+  if (!out) return FLK_E_NULL;
+  if (T < 1 || !rows_fit(d, T)) return FLK_E_SHAPE;
+  flk::ChainArgs ca;
+  st = load_chain(d, T, chain, n_loops, &ca);
+  if (st != FLK_OK) return st;
+  if (!aligned(out, 16)) return FLK_E_ALIGN;
+  return to_status(flk::launch_reconstruct(d->kind, T, d->n_heads, d->head_dim, ca, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                                  int32_t n_q_heads, const flk_stream* k_chain,
+                                  const flk_stream* v_chain, int32_t n_loops, float softmax_scale,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  flk_status st = flk_desc_check(kd);
+  if (st != FLK_OK) return st;
+  st = flk_desc_check(vd);
+  if (st != FLK_OK) return st;
+  if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
+  if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
+  if (!q || !out) return FLK_E_NULL;
+  if (T < 1 || !rows_fit(kd, T) || n_q_heads < 1 || n_q_heads % kd->n_heads != 0) return FLK_E_SHAPE;
+  if (kd->head_dim != 128 || n_q_heads / kd->n_heads > 16) return FLK_E_UNSUPPORTED;
+  flk::ChainArgs kc, vc;
+  st = load_chain(kd, T, k_chain, n_loops, &kc);
+  if (st != FLK_OK) return st;
+  st = load_chain(vd, T, v_chain, n_loops, &vc);
+  if (st != FLK_OK) return st;
+  if (!aligned(q, 16) || !aligned(out, 16)) return FLK_E_ALIGN;
+  const size_t need = flk::attn_workspace_bytes(T, kd->n_heads, n_q_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FLK_E_WORKSPACE;
+  if (workspace && !aligned(workspace, 16)) return FLK_E_ALIGN;
+  return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc,
+                                           softmax_scale, out, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

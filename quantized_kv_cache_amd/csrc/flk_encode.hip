@@ -1,0 +1,309 @@
+// flk_encode.hip -- gfx950 encode kernels: quantized base and cross-loop residuals.
+//
+// One pass per loop: each block loads its tile of X[r] (and, for a residual, the gathered
+// rows of X_hat[r-1]) once with 16-byte loads, forms the BF16 residual in registers,
+// reduces group extremes, derives FP16 params, writes nibble-packed codes and params, and
+// writes the updated reconstruction back in place.  The method is the FlashLoop RFC
+// (vllm-rlt #156) section 3.3; group axes and storage follow vllm-rlt PR #166 "Purpose".
+#include "flk_device.h"
+#include "flk_internal.h"
+
+namespace flk {
+
+constexpr int kThreads = 256;
+constexpr uint32_t kDevRows = FLK_DEV_ROWS;
+
+__device__ __forceinline__ void unpack8(const uint4& w, float v[8]) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float v[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]);
+  w.w = pack_bf16x2(v[6], v[7]);
+  return w;
+}
+
+// ---------------------------------------------------------------------------------------
+// K: groups run down 64 compact rows of one (head, channel).  A block owns one 64-row band
+// (blockIdx.x) of a 128-channel strip (blockIdx.y) of the flattened H*D channel axis.
+// Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs+16, rs+32, rs+48.
+// Extremes: in registers over 4 rows, across the 4 row slots of a wave with lane shuffles,
+// across the 4 waves through LDS; one thread per channel then derives the params.
+// ---------------------------------------------------------------------------------------
+template <bool RESID, bool SPARSE>
+__global__ __launch_bounds__(kThreads) void encode_k_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
+    int32_t W, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes, uint32_t* __restrict__ params,
+    uint32_t* __restrict__ status) {
+  __shared__ float s_min[4][128];
+  __shared__ float s_max[4][128];
+  __shared__ float s_m[128], s_s[128], s_rs[128];
+
+  const int tid = threadIdx.x;
+  const int cc = tid & 15;
+  const int rs = tid >> 4;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int band = blockIdx.x;
+  const int chunk = blockIdx.y * 16 + cc;
+  const bool cact = chunk < (W >> 3);
+  const int64_t ch = int64_t(chunk) * 8;
+
+  float v[4][8];
+  uint4 rv[4];
+  int64_t roff[4];
+  bool ract[4];
+  bool bad_row = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = band * kGroup + rs + 16 * i;
+    ract[i] = cact && j < n;
+    rv[i] = make_uint4(0, 0, 0, 0);
+    roff[i] = 0;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (ract[i]) {
+      const int32_t p = SPARSE ? rows[j] : j;
+      if (SPARSE && uint32_t(p) >= uint32_t(T)) {   // malformed map: never address outside recon
+        ract[i] = false;
+        bad_row = true;
+      } else {
+        xv = *reinterpret_cast<const uint4*>(x + int64_t(j) * W + ch);
+        roff[i] = int64_t(p) * W + ch;
+        if (RESID) rv[i] = *reinterpret_cast<const uint4*>(recon + roff[i]);
+      }
+    }
+    unpack8(xv, v[i]);
+  }
+  if (SPARSE && bad_row && status) atomicOr(status, kDevRows);
+  if (RESID) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float r[8];
+      unpack8(rv[i], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = round_bf16(v[i][e] - r[e]);
+    }
+  }
+
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (ract[i]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { mn[e] = tmin(mn[e], v[i][e]); mx[e] = tmax(mx[e], v[i][e]); }
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = tmin(mn[e], __shfl_xor(mn[e], 16));
+    mx[e] = tmax(mx[e], __shfl_xor(mx[e], 16));
+    mn[e] = tmin(mn[e], __shfl_xor(mn[e], 32));
+    mx[e] = tmax(mx[e], __shfl_xor(mx[e], 32));
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { s_min[wave][cc * 8 + e] = mn[e]; s_max[wave][cc * 8 + e] = mx[e]; }
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const float a = tmin(tmin(s_min[0][tid], s_min[1][tid]), tmin(s_min[2][tid], s_min[3][tid]));
+    const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
+    const int64_t chan = int64_t(blockIdx.y) * 128 + tid;
+    GroupParams p = make_params(a, b);
+    s_m[tid] = p.m;
+    s_s[tid] = p.s;
+    s_rs[tid] = p.rs;
+    if (chan < W) {
+      params[int64_t(band) * W + chan] = p.packed;
+      if (p.err && status) atomicOr(status, p.err);
+    }
+  }
+  __syncthreads();
+
+  GroupParams gp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    gp[e].m = s_m[cc * 8 + e];
+    gp[e].s = s_s[cc * 8 + e];
+    gp[e].rs = s_rs[cc * 8 + e];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!ract[i]) continue;
+    const int j = band * kGroup + rs + 16 * i;
+    float k[8], out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      k[e] = code_of(v[i][e], gp[e]);
+      out[e] = decode(k[e], gp[e].m, gp[e].s);
+    }
+    if (RESID) {
+      float r[8];
+      unpack8(rv[i], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
+    }
+    *reinterpret_cast<uint32_t*>(codes + ((int64_t(j) * W + ch) >> 1)) = pack_codes8(k);
+    *reinterpret_cast<uint4*>(recon + roff[i]) = pack8(out);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// V: groups run along 64 channels of one (row, head).  An item is one (compact row, head)
+// pair, flattened as it = j*H + h; LPH lanes (a power of two >= D/8) cover its D channels,
+// 8 channels per lane, so each 64-channel group is 8 consecutive lanes and its extremes
+// come from three xor-shuffles.  Each thread handles U items spaced 256/LPH apart.
+// ---------------------------------------------------------------------------------------
+template <bool RESID, bool SPARSE, int LPH>
+__global__ __launch_bounds__(kThreads) void encode_v_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
+    int32_t H, int32_t D, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes,
+    uint32_t* __restrict__ params, uint32_t* __restrict__ status) {
+  constexpr int HS = kThreads / LPH;
+  constexpr int U = 4;
+  const int tid = threadIdx.x;
+  const int w = tid & (LPH - 1);
+  const int hs = tid / LPH;
+  const int cph = D >> 3;
+  const int S = (D + kGroup - 1) / kGroup;
+  const bool wact = w < cph;
+  const int64_t total = int64_t(n) * H;
+  const int64_t base = int64_t(blockIdx.x) * (HS * U);
+
+  float v[U][8];
+  uint4 rv[U];
+  int64_t roff[U];
+  bool act[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t it = base + u * HS + hs;
+    act[u] = wact && it < total;
+    rv[u] = make_uint4(0, 0, 0, 0);
+    roff[u] = 0;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (act[u]) {
+      int64_t ro = it * D + w * 8;
+      if (SPARSE) {
+        const uint32_t j = uint32_t(it) / uint32_t(H);   // n*H < 2^31 (checked on the host)
+        const int64_t h = it - int64_t(j) * H;
+        const int32_t p = rows[j];
+        if (uint32_t(p) >= uint32_t(T)) {              // malformed map: never address outside recon
+          act[u] = false;
+          if (status) atomicOr(status, kDevRows);
+        }
+        ro = (int64_t(p) * H + h) * D + w * 8;
+      }
+      if (act[u]) {
+        xv = *reinterpret_cast<const uint4*>(x + it * D + w * 8);
+        roff[u] = ro;
+        if (RESID) rv[u] = *reinterpret_cast<const uint4*>(recon + ro);
+      }
+    }
+    unpack8(xv, v[u]);
+  }
+  if (RESID) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float r[8];
+      unpack8(rv[u], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[u][e] = round_bf16(v[u][e] - r[e]);
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    if (act[u]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { mn = tmin(mn, v[u][e]); mx = tmax(mx, v[u][e]); }
+    }
+    mn = tmin(mn, __shfl_xor(mn, 1));
+    mx = tmax(mx, __shfl_xor(mx, 1));
+    mn = tmin(mn, __shfl_xor(mn, 2));
+    mx = tmax(mx, __shfl_xor(mx, 2));
+    mn = tmin(mn, __shfl_xor(mn, 4));
+    mx = tmax(mx, __shfl_xor(mx, 4));
+    if (!act[u]) continue;
+    const int64_t it = base + u * HS + hs;
+    GroupParams p = make_params(mn, mx);
+    if ((w & 7) == 0) {
+      params[it * S + (w >> 3)] = p.packed;
+      if (p.err && status) atomicOr(status, p.err);
+    }
+    float k[8], out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      k[e] = code_of(v[u][e], p);
+      out[e] = decode(k[e], p.m, p.s);
+    }
+    if (RESID) {
+      float r[8];
+      unpack8(rv[u], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
+    }
+    *reinterpret_cast<uint32_t*>(codes + ((it * D + w * 8) >> 1)) = pack_codes8(k);
+    *reinterpret_cast<uint4*>(recon + roff[u]) = pack8(out);
+  }
+}
+
+template <bool RESID, bool SPARSE>
+static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t H, int32_t D,
+                           void* recon, uint8_t* codes, uint32_t* params, uint32_t* status,
+                           hipStream_t stream) {
+  const int cph = D / 8;
+  const int lph = cph <= 8 ? 8 : cph <= 16 ? 16 : cph <= 32 ? 32 : 64;
+  const int per_block = (kThreads / lph) * 4;
+  const int64_t items = int64_t(n) * H;
+  const dim3 grid(unsigned((items + per_block - 1) / per_block));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint16_t* rp = static_cast<uint16_t*>(recon);
+#define FLK_LAUNCH_V(L)                                                                        \
+  hipLaunchKernelGGL((encode_v_kernel<RESID, SPARSE, L>), grid, dim3(kThreads), 0, stream, xp, \
+                     rows, n, T, H, D, rp, codes, params, status)
+  switch (lph) {
+    case 8: FLK_LAUNCH_V(8); break;
+    case 16: FLK_LAUNCH_V(16); break;
+    case 32: FLK_LAUNCH_V(32); break;
+    default: FLK_LAUNCH_V(64); break;
+  }
+#undef FLK_LAUNCH_V
+  return hipGetLastError();
+}
+
+template <bool RESID, bool SPARSE>
+static hipError_t launch_k(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t W, void* recon,
+                           uint8_t* codes, uint32_t* params, uint32_t* status, hipStream_t stream) {
+  const int cpr = W / 8;
+  const dim3 grid(unsigned((n + kGroup - 1) / kGroup), unsigned((cpr + 15) / 16));
+  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), rows, n, T, W, static_cast<uint16_t*>(recon),
+                     codes, params, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* rows, int32_t n,
+                         int32_t T, int32_t H, int32_t D, void* recon, uint8_t* codes,
+                         uint32_t* params, uint32_t* status, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const bool sparse = rows != nullptr;
+  if (kind == FLK_KIND_K) {
+    const int32_t W = H * D;
+    if (!resid) return launch_k<false, false>(x, rows, n, T, W, recon, codes, params, status, stream);
+    if (!sparse) return launch_k<true, false>(x, rows, n, T, W, recon, codes, params, status, stream);
+    return launch_k<true, true>(x, rows, n, T, W, recon, codes, params, status, stream);
+  }
+  if (!resid) return launch_v<false, false>(x, rows, n, T, H, D, recon, codes, params, status, stream);
+  if (!sparse) return launch_v<true, false>(x, rows, n, T, H, D, recon, codes, params, status, stream);
+  return launch_v<true, true>(x, rows, n, T, H, D, recon, codes, params, status, stream);
+}
+
+}  // namespace flk

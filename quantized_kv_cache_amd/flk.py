@@ -1,0 +1,209 @@
+"""ctypes binding of libflk.so, the gfx950 packed-KV codec (include/flk.h).
+
+Argument marshalling only: every step of the codec runs in the HIP kernels behind the C ABI.
+torch supplies device memory and the current stream.  There is no CPU fallback: if the
+library is missing or cannot load, every call raises.
+
+Tensors: BF16 data are torch.bfloat16 [rows, H, D] (contiguous, on the GPU); codes are
+torch.uint8 [n, H, D//2]; params torch.int32 (FP16 min | FP16 scale << 16, bit pattern),
+shaped [ceil(n/64), H, D] for K and [n, H, ceil(D/64)] for V; rows are torch.int32 [n]
+ascending positions or None (dense).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflk.so")
+
+K, V = 0, 1
+GROUP = 64
+MAX_LOOPS = 8
+DEV_NONFINITE, DEV_RANGE = 1, 2
+
+
+class FlkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = _lib.flk_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint16), ("format", ctypes.c_uint8), ("kind", ctypes.c_uint8),
+                ("group", ctypes.c_uint16), ("param_dtype", ctypes.c_uint8), ("nibble_order", ctypes.c_uint8),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class StreamC(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflk.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_kv_cache_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(Desc)
+        S = ctypes.POINTER(StreamC)
+        L.flk_desc_init.restype = None
+        L.flk_desc_init.argtypes = [D, ctypes.c_int, i32, i32]
+        L.flk_desc_check.restype = ctypes.c_int
+        L.flk_desc_check.argtypes = [D]
+        L.flk_codes_bytes.restype = sz
+        L.flk_codes_bytes.argtypes = [D, i32]
+        L.flk_params_bytes.restype = sz
+        L.flk_params_bytes.argtypes = [D, i32]
+        L.flk_rows_bytes.restype = sz
+        L.flk_rows_bytes.argtypes = [i32, ctypes.c_int]
+        L.flk_attn_workspace_bytes.restype = sz
+        L.flk_attn_workspace_bytes.argtypes = [D, i32, i32]
+        L.flk_status_string.restype = ctypes.c_char_p
+        L.flk_status_string.argtypes = [ctypes.c_int]
+        L.flk_abi_version.restype = ctypes.c_int
+        L.flk_abi_version.argtypes = []
+        L.flk_encode_base.restype = ctypes.c_int
+        L.flk_encode_base.argtypes = [D, P, i32, P, P, P, P, P]
+        L.flk_encode_residual.restype = ctypes.c_int
+        L.flk_encode_residual.argtypes = [D, P, P, i32, i32, P, P, P, P, P]
+        L.flk_reconstruct.restype = ctypes.c_int
+        L.flk_reconstruct.argtypes = [D, i32, S, i32, P, P]
+        L.flk_decode_attn_packed.restype = ctypes.c_int
+        L.flk_decode_attn_packed.argtypes = [D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P, sz, P]
+        _lib = L
+    return _lib
+
+
+def desc(kind: int, H: int, D: int) -> Desc:
+    d = Desc()
+    lib().flk_desc_init(ctypes.byref(d), kind, H, D)
+    return d
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise FlkError(st, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous {dtype} GPU tensor, got {t.dtype} {tuple(t.shape)}")
+
+
+# ----------------------------------------------------------------------------- sizes
+
+def codes_bytes(kind: int, H: int, D: int, n: int) -> int:
+    return int(lib().flk_codes_bytes(ctypes.byref(desc(kind, H, D)), n))
+
+
+def params_bytes(kind: int, H: int, D: int, n: int) -> int:
+    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D)), n))
+
+
+def rows_bytes(n: int, sparse: bool) -> int:
+    return int(lib().flk_rows_bytes(n, 1 if sparse else 0))
+
+
+def attn_workspace_bytes(H: int, D: int, T: int, n_q_heads: int) -> int:
+    return int(lib().flk_attn_workspace_bytes(ctypes.byref(desc(K, H, D)), T, n_q_heads))
+
+
+def params_shape(kind: int, H: int, D: int, n: int):
+    return ((n + GROUP - 1) // GROUP, H, D) if kind == K else (n, H, (D + GROUP - 1) // GROUP)
+
+
+@dataclass
+class Packed:
+    """Device buffers of one encoded loop (caller-owned torch tensors)."""
+    n_rows: int
+    rows: Optional[torch.Tensor]
+    codes: torch.Tensor
+    params: torch.Tensor
+
+    @staticmethod
+    def empty(kind: int, H: int, D: int, n: int, rows: Optional[torch.Tensor] = None,
+              device="cuda") -> "Packed":
+        codes = torch.empty((n, H, D // 2), dtype=torch.uint8, device=device)
+        params = torch.empty(params_shape(kind, H, D, n), dtype=torch.int32, device=device)
+        return Packed(n, rows, codes, params)
+
+    def c(self) -> StreamC:
+        return StreamC(self.n_rows, 0, None if self.rows is None else self.rows.data_ptr(),
+                       self.codes.data_ptr(), self.params.data_ptr())
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + 4 * self.params.numel() + (0 if self.rows is None else 4 * self.rows.numel())
+
+
+# ----------------------------------------------------------------------------- codec calls
+
+def encode_base(kind: int, x: torch.Tensor, out: Packed, recon: torch.Tensor,
+                status: Optional[torch.Tensor] = None, stream=None) -> None:
+    _need(x, torch.bfloat16, "x")
+    _need(recon, torch.bfloat16, "recon")
+    T, H, D = x.shape
+    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D)), _ptr(x), T, _ptr(out.codes),
+                                 _ptr(out.params), _ptr(recon), _ptr(status), _stream(stream)),
+           "flk_encode_base")
+
+
+def encode_residual(kind: int, x_rows: torch.Tensor, rows: Optional[torch.Tensor], recon: torch.Tensor,
+                    out: Packed, status: Optional[torch.Tensor] = None, stream=None) -> None:
+    _need(x_rows, torch.bfloat16, "x_rows")
+    _need(recon, torch.bfloat16, "recon")
+    if rows is not None:
+        _need(rows, torch.int32, "rows")
+    n, H, D = x_rows.shape
+    T = recon.shape[0]
+    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D)), _ptr(x_rows), _ptr(rows), n, T,
+                                     _ptr(recon), _ptr(out.codes), _ptr(out.params), _ptr(status),
+                                     _stream(stream)),
+           "flk_encode_residual")
+
+
+def _chain(chain: Sequence[Packed]):
+    arr = (StreamC * len(chain))(*[p.c() for p in chain])
+    return arr
+
+
+def reconstruct(kind: int, chain: Sequence[Packed], out: torch.Tensor, stream=None) -> None:
+    _need(out, torch.bfloat16, "out")
+    T, H, D = out.shape
+    arr = _chain(chain)
+    _check(lib().flk_reconstruct(ctypes.byref(desc(kind, H, D)), T, arr, len(chain), _ptr(out),
+                                 _stream(stream)), "flk_reconstruct")
+
+
+def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int,
+                       H: int, softmax_scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                       stream=None) -> None:
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    Hq, D = q.shape
+    ka, va = _chain(k_chain), _chain(v_chain)
+    _check(lib().flk_decode_attn_packed(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), T, _ptr(q),
+                                        Hq, ka, va, len(k_chain), float(softmax_scale), _ptr(out),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "flk_decode_attn_packed")

@@ -1,0 +1,144 @@
+"""CPU-side checks of the C ABI: the library loads, exports what include/flk.h declares, the
+size functions agree with the closed forms, and host validation rejects bad calls before
+anything is enqueued (no kernel runs here: every call below fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_kv_cache_amd import flk
+from oracle import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flk_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = flk.lib()
+    names = declared_functions()
+    assert "flk_encode_base" in names and "flk_decode_attn_packed" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.flk_abi_version() == 1
+
+
+@pytest.mark.parametrize("kind", [flk.K, flk.V])
+@pytest.mark.parametrize("H,D,n", [(1, 8, 1), (2, 64, 256), (8, 96, 1000), (8, 128, 32768), (16, 128, 4353),
+                                   (3, 24, 65), (1, 512, 130)])
+def test_sizes_match_closed_forms(kind, H, D, n):
+    assert flk.codes_bytes(kind, H, D, n) == n * H * D // 2 == orc.codes_bytes(H, D, n)
+    assert flk.params_bytes(kind, H, D, n) == orc.params_bytes(kind, H, D, n)
+    groups = -(-n // 64) * H * D if kind == flk.K else n * H * -(-D // 64)
+    assert flk.params_bytes(kind, H, D, n) == 4 * groups
+    assert flk.rows_bytes(n, True) == 4 * n and flk.rows_bytes(n, False) == 0
+
+
+def test_descriptor_checks():
+    L = flk.lib()
+    d = flk.desc(flk.K, 8, 128)
+    assert L.flk_desc_check(ctypes.byref(d)) == 0
+    assert L.flk_desc_check(None) == 1
+    for field, bad in [("abi_version", 2), ("format", 0), ("kind", 2), ("group", 32), ("param_dtype", 0),
+                       ("nibble_order", 2)]:
+        e = flk.desc(flk.K, 8, 128)
+        setattr(e, field, bad)
+        assert L.flk_desc_check(ctypes.byref(e)) == 4, field
+    for H, D in [(0, 128), (8, 0), (8, 4), (8, 100), (8, 520), (-1, 64)]:
+        assert L.flk_desc_check(ctypes.byref(flk.desc(flk.V, H, D))) == 2, (H, D)
+    assert flk.codes_bytes(flk.K, 8, 100, 10) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced (validation fails first)
+MIS = ctypes.c_void_p((1 << 20) + 2)     # misaligned
+
+
+def _encode_base(d, x, T, codes, params, recon):
+    return flk.lib().flk_encode_base(ctypes.byref(d), x, T, codes, params, recon, None, None)
+
+
+def test_encode_base_validation():
+    d = flk.desc(flk.K, 2, 64)
+    assert _encode_base(d, None, 16, FAKE, FAKE, FAKE) == 1
+    assert _encode_base(d, FAKE, 16, None, FAKE, FAKE) == 1
+    assert _encode_base(d, FAKE, 16, FAKE, FAKE, None) == 1
+    assert _encode_base(d, FAKE, 0, FAKE, FAKE, FAKE) == 2
+    assert _encode_base(d, MIS, 16, FAKE, FAKE, FAKE) == 3
+    assert _encode_base(d, FAKE, 16, FAKE, MIS, FAKE) == 3
+    bad = flk.desc(flk.K, 2, 64)
+    bad.group = 128
+    assert _encode_base(bad, FAKE, 16, FAKE, FAKE, FAKE) == 4
+
+
+def test_encode_residual_validation():
+    L = flk.lib()
+    d = flk.desc(flk.V, 2, 64)
+
+    def call(x, rows, n, T, recon=FAKE, codes=FAKE, params=FAKE):
+        return L.flk_encode_residual(ctypes.byref(d), x, rows, n, T, recon, codes, params, None, None)
+    assert call(FAKE, None, 10, 16) == 2            # dense needs n == T
+    assert call(FAKE, FAKE, 17, 16) == 2            # n > T
+    assert call(FAKE, FAKE, -1, 16) == 2
+    assert call(None, FAKE, 4, 16) == 1
+    assert call(FAKE, FAKE, 4, 16, recon=None) == 1
+    assert call(FAKE, ctypes.c_void_p((1 << 20) + 1), 4, 16) == 3
+    # an empty residual loop is valid and enqueues nothing
+    assert call(None, FAKE, 0, 16, codes=None, params=None) == 0
+
+
+def test_reconstruct_validation():
+    L = flk.lib()
+    d = flk.desc(flk.K, 2, 64)
+    S = flk.StreamC
+
+    def call(chain, n_loops, T=64, out=FAKE):
+        arr = (S * max(1, len(chain)))(*chain) if chain else None
+        return L.flk_reconstruct(ctypes.byref(d), T, arr, n_loops, out, None)
+    base = S(64, 0, None, FAKE.value, FAKE.value)
+    assert call([], 1) == 1
+    assert call([base], 0) == 2
+    assert call([base] * 9, 9) == 2
+    assert call([S(32, 0, None, FAKE.value, FAKE.value)], 1) == 2      # base must be dense n == T
+    assert call([S(64, 0, FAKE.value, FAKE.value, FAKE.value)], 1) == 2
+    assert call([base, S(65, 0, FAKE.value, FAKE.value, FAKE.value)], 2) == 2
+    assert call([base, S(10, 0, None, FAKE.value, FAKE.value)], 2) == 2
+    assert call([base, S(10, 7, FAKE.value, FAKE.value, FAKE.value)], 2) == 4
+    assert call([base, S(10, 0, FAKE.value, None, FAKE.value)], 2) == 1
+    assert call([base, S(10, 0, FAKE.value, MIS.value, FAKE.value)], 2) == 3
+    assert call([base], 1, out=None) == 1
+    assert call([base], 1, out=MIS) == 3
+
+
+def test_attention_validation():
+    L = flk.lib()
+    kd, vd = flk.desc(flk.K, 8, 128), flk.desc(flk.V, 8, 128)
+    S = flk.StreamC
+    T = 256
+    chain = (S * 1)(S(T, 0, None, FAKE.value, FAKE.value))
+    ws = flk.attn_workspace_bytes(8, 128, T, 32)
+    assert ws > 0
+
+    def call(kd=kd, vd=vd, q=FAKE, hq=32, out=FAKE, w=FAKE, wb=ws, n_loops=1):
+        return L.flk_decode_attn_packed(ctypes.byref(kd), ctypes.byref(vd), T, q, hq, chain, chain, n_loops,
+                                        0.088, out, w, wb, None)
+    assert call(kd=vd, vd=kd) == 4
+    assert call(q=None) == 1
+    assert call(hq=30) == 2
+    assert call(wb=ws - 1) == 6
+    assert call(w=None) == 6
+    assert call(hq=8 * 17) == 5
+    d64k, d64v = flk.desc(flk.K, 8, 64), flk.desc(flk.V, 8, 64)
+    assert call(kd=d64k, vd=d64v) == 5
+    assert call(n_loops=0) == 2
+
+
+def test_status_strings():
+    L = flk.lib()
+    for s in range(8):
+        assert L.flk_status_string(s)
