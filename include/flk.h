@@ -41,10 +41,17 @@
  *          K: [ceil(n/64)][H][D]  (group g of channel (h, c) covers compact rows 64g..64g+63).
  *          V: [n][H][ceil(D/64)]  (group g of (row, h) covers channels 64g..64g+63).
  *          The last group along the axis may be partial (statistics over its real elements).
- *  rows    int32 [n], ascending logical positions of the compact rows (the RFC's explicit
- *          logical-position-to-compact-row map); NULL for a dense stream (n == T).  A
- *          position a residual stream does not list inherits its predecessor (an absent
- *          residual is not a code-0 residual, RFC section 3.3).
+ *  rows    int32 [n], ascending logical positions of the compact rows (compact row ->
+ *          logical position); NULL for a dense stream (n == T).  A position a residual
+ *          stream does not list inherits its predecessor (an absent residual is not a
+ *          code-0 residual, RFC section 3.3).
+ *  tile_start  int32 [ceil(T/64) + 1], the inverse map at 64-position granularity:
+ *          tile_start[t] = number of rows < 64*t, so the compact rows of positions
+ *          [64t, 64t+64) are tile_start[t] .. tile_start[t+1]-1 (and tile_start[last] = n).
+ *          Compact streams only (NULL for dense).  Together with rows it is the RFC's
+ *          explicit logical-position <-> compact-row mapping (section 3.3); readers use it
+ *          instead of searching rows.  flk_encode_residual writes it; it depends on rows and
+ *          T alone, so the K and V streams of one loop may share one array.
  *  Codes and params for a group are computed with the FP16-rounded minimum and scale:
  *    scale32 = (max - min) / 15 (binary32), min16 = fp16(min), scale16 = fp16(scale32),
  *    code = clamp(round_half_even((x - min16) / scale16), 0, 15), or 0 when scale16 == 0
@@ -111,6 +118,7 @@ typedef struct flk_stream {
     const int32_t* rows;    /* device, n ascending positions in [0, T), or NULL = dense    */
     const uint8_t* codes;   /* device, flk_codes_bytes(desc, n) bytes, 16-byte aligned     */
     const uint32_t* params; /* device, flk_params_bytes(desc, n) bytes, 16-byte aligned    */
+    const int32_t* tile_start; /* device, flk_tile_index_bytes(T) bytes; NULL = dense      */
 } flk_stream;
 /* A stream with n_rows == 0 (an empty loop) contributes nothing; its pointers are ignored. */
 
@@ -127,6 +135,7 @@ flk_status flk_desc_check(const flk_desc* d);
 size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows);   /* n*H*D/2                    */
 size_t flk_params_bytes(const flk_desc* d, int32_t n_rows);  /* 4 * number of groups       */
 size_t flk_rows_bytes(int32_t n_rows, int sparse);            /* 4*n if sparse, else 0      */
+size_t flk_tile_index_bytes(int32_t T);                       /* 4*(ceil(T/64) + 1)         */
 
 /* Workspace of flk_decode_attn_packed for a T-token cache and n_q_heads query heads (other
  * calls need none).  0 for malformed arguments. */
@@ -152,13 +161,16 @@ flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t*
  * x_rows: BF16 [n_rows, H, D], X[r] at the active positions only (input).
  * rows: device int32 [n_rows] ascending positions, or NULL for a dense loop (n_rows == T).
  * recon: BF16 [T, H, D], X_hat[r-1] on entry, X_hat[r] on exit (updated in place).
- * codes/params: the residual stream (outputs).  n_rows == 0 (an empty loop) is allowed,
- * ignores x_rows, rows, codes and params, and writes nothing.
+ * codes/params: the residual stream (outputs).  tile_start: output, required when rows is
+ * not NULL (flk_tile_index_bytes(T) bytes, 4-byte aligned), ignored for a dense loop.
+ * n_rows == 0 (an empty loop) is allowed, ignores x_rows, rows, codes, params and
+ * tile_start, and writes nothing.
  * Errors: as flk_encode_base, plus FLK_E_SHAPE when n_rows > T or rows == NULL with
  * n_rows != T.                                                                            */
 flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int32_t* rows,
                                int32_t n_rows, int32_t T, void* recon, uint8_t* codes,
-                               uint32_t* params, uint32_t* dev_status, void* stream);
+                               uint32_t* params, int32_t* tile_start, uint32_t* dev_status,
+                               void* stream);
 
 /* Rebuild X_hat[n_loops] from the packed chain alone (RFC section 3.3: a loop-4 read of t1
  * resolves to base + delta2, of t2 to base + delta2 + delta3, of t4 to the full chain).

@@ -387,6 +387,21 @@ int orc_reconstruct(int kind, int H, int D, int T, int n_loops, const int32_t* n
     return ORC_OK;
 }
 
+/* The inverse position map at 64-position granularity (RFC section 3.3: explicit
+ * logical-position-to-compact-row mappings): out[t] = number of rows < 64*t, for
+ * t = 0 .. ceil(T/64).  Written as the definition, a count per tile. */
+int orc_tile_index(const int32_t* rows, int n, int T, int32_t* out) {
+    if (n < 0 || T < 1) return ORC_E_ARG;
+    int ntiles = (T + ORC_GROUP - 1) / ORC_GROUP;
+    for (int t = 0; t <= ntiles; ++t) {
+        int32_t count = 0;
+        for (int j = 0; j < n; ++j)
+            if (rows[j] < (int64_t)ORC_GROUP * t) ++count;
+        out[t] = count;
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Decode attention over reconstructed K/V (the consumer the RFC describes in section     */
 /* 3.3's last paragraph and section 3.2: historical K/V "at the requested depth,          */

@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.orc_encode_residual.argtypes = [i, i, i, i, i, P, P, P, P, P, i]
         L.orc_reconstruct.restype = i
         L.orc_reconstruct.argtypes = [i, i, i, i, i, P, P, P, P, P]
+        L.orc_tile_index.restype = i
+        L.orc_tile_index.argtypes = [P, i, i, P]
         L.orc_decode_attn.restype = i
         L.orc_decode_attn.argtypes = [i, i, i, i, P, P, P, ctypes.c_double, P]
     return _lib
@@ -245,6 +247,14 @@ def encode_chain(kind: int, xs: Sequence[np.ndarray], rows_list: Sequence[Option
     for x, rows in zip(xs[1:], rows_list[1:]):
         chain.append(encode_residual(kind, x, rows, recon, f32_params))
     return chain, recon
+
+
+def tile_index(rows: np.ndarray, T: int) -> np.ndarray:
+    """out[t] = number of rows < 64*t for t = 0 .. ceil(T/64)."""
+    rows = _c(rows, np.int32)
+    out = np.zeros((T + GROUP - 1) // GROUP + 1, np.int32)
+    _check(lib().orc_tile_index(_p(rows), rows.size, T, _p(out)), "tile_index")
+    return out
 
 
 def decode_attn(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, softmax_scale: float) -> np.ndarray:

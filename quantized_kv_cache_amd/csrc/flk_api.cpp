@@ -47,8 +47,10 @@ flk_status load_chain(const flk_desc* d, int32_t T, const flk_stream* chain, int
     if (s.rows == nullptr && s.n_rows != T) return FLK_E_SHAPE;
     flk_status st = check_stream_ptrs(s.codes, s.params);
     if (st != FLK_OK) return st;
-    if (s.rows && !aligned(s.rows, 4)) return FLK_E_ALIGN;
+    if (s.rows && !s.tile_start) return FLK_E_NULL;      // compact loops carry their index
+    if (s.rows && (!aligned(s.rows, 4) || !aligned(s.tile_start, 4))) return FLK_E_ALIGN;
     out->s[kept].rows = s.rows;
+    out->s[kept].tile_start = s.rows ? s.tile_start : nullptr;
     out->s[kept].codes = s.codes;
     out->s[kept].params = s.params;
     out->s[kept].n = s.n_rows;
@@ -102,6 +104,11 @@ size_t flk_rows_bytes(int32_t n_rows, int sparse) {
   return sparse ? 4 * size_t(n_rows) : 0;
 }
 
+size_t flk_tile_index_bytes(int32_t T) {
+  if (T < 1) return 0;
+  return 4 * (size_t((T + FLK_GROUP - 1) / FLK_GROUP) + 1);
+}
+
 size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads) {
   if (flk_desc_check(k_desc) != FLK_OK || T < 1 || n_q_heads < 1) return 0;
   return flk::attn_workspace_bytes(T, k_desc->n_heads, n_q_heads);
@@ -133,13 +140,14 @@ flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t*
   if (st != FLK_OK) return st;
   if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
   return to_status(flk::launch_encode(d->kind, false, x, nullptr, T, T, d->n_heads, d->head_dim,
-                                      recon, codes, params, dev_status,
+                                      recon, codes, params, nullptr, dev_status,
                                       static_cast<hipStream_t>(stream)));
 }
 
 flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int32_t* rows,
                                int32_t n_rows, int32_t T, void* recon, uint8_t* codes,
-                               uint32_t* params, uint32_t* dev_status, void* stream) {
+                               uint32_t* params, int32_t* tile_start, uint32_t* dev_status,
+                               void* stream) {
   flk_status st = flk_desc_check(d);
   if (st != FLK_OK) return st;
   if (!recon) return FLK_E_NULL;
@@ -150,10 +158,12 @@ flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int3
   if (!x_rows) return FLK_E_NULL;
   st = check_stream_ptrs(codes, params);
   if (st != FLK_OK) return st;
-  if (!aligned(x_rows, 16) || (rows && !aligned(rows, 4))) return FLK_E_ALIGN;
+  if (rows && !tile_start) return FLK_E_NULL;
+  if (!aligned(x_rows, 16) || (rows && (!aligned(rows, 4) || !aligned(tile_start, 4))))
+    return FLK_E_ALIGN;
   return to_status(flk::launch_encode(d->kind, true, x_rows, rows, n_rows, T, d->n_heads,
-                                      d->head_dim, recon, codes, params, dev_status,
-                                      static_cast<hipStream_t>(stream)));
+                                      d->head_dim, recon, codes, params, rows ? tile_start : nullptr,
+                                      dev_status, static_cast<hipStream_t>(stream)));
 }
 
 flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain, int32_t n_loops,

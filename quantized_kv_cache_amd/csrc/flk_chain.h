@@ -23,6 +23,167 @@ __device__ __forceinline__ int32_t lower_bound_rows(const int32_t* __restrict__ 
   return lo;
 }
 
+// lower_bound over an ascending array, computed by a whole 256-thread block in
+// ceil(log256(n)) rounds of one parallel probe each (instead of log2(n) dependent loads):
+// each round probes 256 evenly spaced entries of the current bracket and keeps the one
+// stride that contains the first entry >= key.  Every thread returns the same value.
+// Contains __syncthreads_count(); call from all threads of the block.
+__device__ __forceinline__ int32_t block_lower_bound(const int32_t* __restrict__ rows, int32_t n,
+                                                     int32_t key) {
+  int32_t a = 0, b = n;                    // the answer lies in [a, b]
+  while (a < b) {
+    const int32_t s = (b - a + 255) / 256;
+    const int32_t idx = a + int32_t(threadIdx.x) * s;
+    const bool pred = idx < b && rows[idx] < key;
+    const int32_t c = __syncthreads_count(pred);
+    if (c == 0) return a;
+    const int32_t na = a + (c - 1) * s + 1;
+    const int32_t nb = min(a + c * s, b);
+    if (s == 1) return nb;
+    a = na;
+    b = nb;
+  }
+  return a;
+}
+
+// lower_bound of `key` in every compact loop of a chain at once (dense loops give 0): the
+// probes of all loops share each round, so the block waits ceil(log256(n)) load latencies
+// in total rather than per loop.  Uniform control flow; call from all threads.
+template <int NL>
+__device__ __forceinline__ void chain_lower_bounds(const ChainArgs& chain, int32_t key,
+                                                   int32_t lo[NL]) {
+  int32_t a[NL], b[NL];
+  bool done[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    a[l] = 0;
+    b[l] = chain.s[l].rows ? chain.s[l].n : 0;
+    done[l] = chain.s[l].rows == nullptr || b[l] == 0;
+    lo[l] = 0;
+  }
+  for (int round = 0; round < 4; ++round) {
+    bool any = false;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) any |= !done[l];
+    if (!any) break;
+    bool pred[NL];
+    int32_t st[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      st[l] = (b[l] - a[l] + 255) / 256;
+      const int32_t idx = a[l] + int32_t(threadIdx.x) * st[l];
+      pred[l] = !done[l] && idx < b[l] && chain.s[l].rows[idx] < key;
+    }
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      if (done[l]) continue;
+      const int32_t c = __syncthreads_count(pred[l]);
+      if (c == 0) { lo[l] = a[l]; done[l] = true; continue; }
+      const int32_t na = a[l] + (c - 1) * st[l] + 1;
+      const int32_t nb = min(a[l] + c * st[l], b[l]);
+      if (st[l] == 1 || na >= nb) { lo[l] = nb; done[l] = true; continue; }
+      a[l] = na;
+      b[l] = nb;
+    }
+  }
+}
+
+// lower_bound of key0 and of key1 in every compact loop of a chain (dense loops give 0),
+// all probes sharing each round: ceil(log256(n)) load latencies in total.
+template <int NL>
+__device__ __forceinline__ void chain_bounds(const ChainArgs& chain, int32_t key0, int32_t key1,
+                                             int32_t lo[NL], int32_t hi[NL]) {
+  int32_t a[2][NL], b[2][NL];
+  bool done[2][NL];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      a[k][l] = 0;
+      b[k][l] = chain.s[l].rows ? chain.s[l].n : 0;
+      done[k][l] = chain.s[l].rows == nullptr || b[k][l] == 0;
+      (k ? hi : lo)[l] = 0;
+    }
+  for (int round = 0; round < 4; ++round) {
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int l = 0; l < NL; ++l) any |= !done[k][l];
+    if (!any) break;
+    bool pred[2][NL];
+    int32_t st[2][NL];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        st[k][l] = (b[k][l] - a[k][l] + 255) / 256;
+        const int32_t idx = a[k][l] + int32_t(threadIdx.x) * st[k][l];
+        pred[k][l] = !done[k][l] && idx < b[k][l] && chain.s[l].rows[idx] < (k ? key1 : key0);
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        if (done[k][l]) continue;
+        int32_t* res = k ? hi : lo;
+        const int32_t c = __syncthreads_count(pred[k][l]);
+        if (c == 0) { res[l] = a[k][l]; done[k][l] = true; continue; }
+        const int32_t na = a[k][l] + (c - 1) * st[k][l] + 1;
+        const int32_t nb = min(a[k][l] + c * st[k][l], b[k][l]);
+        if (st[k][l] == 1 || na >= nb) { res[l] = nb; done[k][l] = true; continue; }
+        a[k][l] = na;
+        b[k][l] = nb;
+      }
+  }
+}
+
+// lower_bound of `key` in every compact loop of a chain, computed by one wave alone (no
+// block barrier): each round probes 64 evenly spaced entries of every open bracket and keeps
+// the stride holding the first entry >= key, so a loop of n rows needs ceil(log64(n)) rounds
+// and all loops share them.  Returns wave-uniform values; dense loops give 0.
+template <int NL>
+__device__ __forceinline__ void wave_chain_lower_bounds(const ChainArgs& chain, int32_t key,
+                                                        int32_t lo[NL]) {
+  const int lane = threadIdx.x & 63;
+  int32_t a[NL], b[NL];
+  bool done[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    a[l] = 0;
+    b[l] = chain.s[l].rows ? chain.s[l].n : 0;
+    done[l] = chain.s[l].rows == nullptr || b[l] == 0;
+    lo[l] = 0;
+  }
+  for (int round = 0; round < 6; ++round) {
+    bool any = false;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) any |= !done[l];
+    if (!any) break;
+    bool pred[NL];
+    int32_t st[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      st[l] = (b[l] - a[l] + 63) / 64;
+      const int32_t idx = a[l] + lane * st[l];
+      pred[l] = !done[l] && idx < b[l] && chain.s[l].rows[idx] < key;
+    }
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      if (done[l]) continue;
+      const int32_t c = __builtin_popcountll(__ballot(pred[l]));
+      if (c == 0) { lo[l] = a[l]; done[l] = true; continue; }
+      const int32_t na = a[l] + (c - 1) * st[l] + 1;
+      const int32_t nb = min(a[l] + c * st[l], b[l]);
+      if (st[l] == 1 || na >= nb) { lo[l] = nb; done[l] = true; continue; }
+      a[l] = na;
+      b[l] = nb;
+    }
+  }
+#pragma unroll
+  for (int l = 0; l < NL; ++l) lo[l] = uniform(lo[l]);
+}
+
 // Fill s_map[l][i] with the compact row of position t0 + i in loop l (-1 if absent), for
 // every compact loop of the chain.  Contains two __syncthreads(); call from all threads.
 __device__ __forceinline__ void build_tile_maps(const ChainArgs& chain, int32_t t0,

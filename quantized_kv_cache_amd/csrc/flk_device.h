@@ -28,9 +28,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Round to BF16 and widen back: the binary32 value of bf16(x).
+// Round to BF16 and widen back: the binary32 value of bf16(x), in one instruction
+// (v_cvt_pk_bf16_f32 with a zero low half writes bf16(x) << 16, which is that value).
 __device__ __forceinline__ float round_bf16(float x) {
-  return __uint_as_float(uint32_t(__builtin_bit_cast(uint16_t, (__bf16)x)) << 16);
+  return __uint_as_float(pack_bf16x2(0.0f, x));
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
@@ -106,5 +107,130 @@ __device__ __forceinline__ uint32_t pack_codes8(const float c[8]) {
 
 // Nibble i of a packed word as a float.
 __device__ __forceinline__ float nib(uint32_t w, int i) { return float((w >> (4 * i)) & 0xFu); }
+
+// Keeps a value in a register as computed (an empty asm barrier), so the byte-wise
+// conversion below is not re-folded into per-nibble shifts and masks.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The 8 codes of a packed word as floats in channel order: even channels from the low
+// nibbles, odd from the high nibbles, each byte converted with v_cvt_f32_ubyteN.
+__device__ __forceinline__ void codes8_to_f32(uint32_t cw, float c[8]) {
+  const uint32_t lo = opaque(cw & 0x0F0F0F0Fu);
+  const uint32_t hi = opaque((cw >> 4) & 0x0F0F0F0Fu);
+  c[0] = float(lo & 0xFFu);
+  c[2] = float((lo >> 8) & 0xFFu);
+  c[4] = float((lo >> 16) & 0xFFu);
+  c[6] = float(lo >> 24);
+  c[1] = float(hi & 0xFFu);
+  c[3] = float((hi >> 8) & 0xFFu);
+  c[5] = float((hi >> 16) & 0xFFu);
+  c[7] = float(hi >> 24);
+}
+
+// Round 8 binary32 values to BF16 in place, one instruction each; x[] then holds the
+// binary32 values of the rounded numbers.
+__device__ __forceinline__ void round_bf16x8_inplace(float x[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
+}
+
+// Pack 8 binary32 values that are already exactly BF16 (low halves zero): the high halves.
+__device__ __forceinline__ uint4 pack_exact_bf16x8(const float x[8]) {
+  uint4 w;
+  w.x = __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u);
+  w.y = __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u);
+  w.z = __builtin_amdgcn_perm(__float_as_uint(x[5]), __float_as_uint(x[4]), 0x07060302u);
+  w.w = __builtin_amdgcn_perm(__float_as_uint(x[7]), __float_as_uint(x[6]), 0x07060302u);
+  return w;
+}
+
+// Round 8 binary32 values to BF16 in place (pairs through v_cvt_pk_bf16_f32) and return
+// them packed; x[] then holds the binary32 values of the rounded numbers.
+__device__ __forceinline__ uint4 round_bf16x8(float x[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(x[0], x[1]);
+  w.y = pack_bf16x2(x[2], x[3]);
+  w.z = pack_bf16x2(x[4], x[5]);
+  w.w = pack_bf16x2(x[6], x[7]);
+  x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+  x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+  x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xFFFF0000u);
+  x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xFFFF0000u);
+  return w;
+}
+
+// ---- buffer-resource accesses ----------------------------------------------------------------
+// A raw buffer resource holds a scalar base address and a byte range; an access adds a
+// 32-bit per-lane offset (VGPR) and a 32-bit wave-uniform offset (SGPR), so per-row
+// addressing costs no vector instructions.  Lane offsets at or past the range read zero and
+// drop stores.  kBufDword3 is the gfx9-family descriptor word for raw 32-bit access.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kBufDword3 = 0x00020000;
+constexpr int kCacheStream = 2;     // nontemporal: stream past the caches
+
+__device__ __forceinline__ BufRsrc make_buf(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), kBufDword3);
+}
+template <int AUX = 0>
+__device__ __forceinline__ uint32_t buf_ld32(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ uint4 buf_ld128(BufRsrc r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  const v4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_st32(uint32_t w, BufRsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(w, r, int(voff), int(soff), AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_st128(const uint4& w, BufRsrc r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  const v4 v = {w.x, w.y, w.z, w.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(voff), int(soff), AUX);
+}
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ---- nontemporal (streaming) global accesses ----------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, const uint4& w) {
+  const u32x4 v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ uint32_t ld_stream32(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ void st_stream32(void* p, uint32_t w) {
+  __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p));
+}
+
+// ---- inverse map at 64-position granularity ---------------------------------------------
+// tile_start[t] = number of rows < 64t.  Called once per compact row j: it writes the
+// entries of the tiles whose first listed position is rows[j] (the t with
+// rows[j-1] < 64t <= rows[j]), and the row n-1 also writes n for every later tile.  Each
+// entry is written by exactly one row; entries are clamped to the array.
+__device__ __forceinline__ void write_tile_index(const int32_t* __restrict__ rows, int32_t n,
+                                                 int32_t T, int32_t j,
+                                                 int32_t* __restrict__ tile_start) {
+  const int32_t ntiles = (T + kGroup - 1) / kGroup;
+  const int32_t p = rows[j];
+  const int32_t q = j > 0 ? rows[j - 1] : -1;
+  if (p < 0 || p >= T) return;
+  const int32_t t_first = q < 0 ? 0 : min(q / kGroup + 1, ntiles + 1);
+  const int32_t t_last = p / kGroup;
+  for (int32_t t = t_first; t <= t_last; ++t) tile_start[t] = j;
+  if (j == n - 1)
+    for (int32_t t = t_last + 1; t <= ntiles; ++t) tile_start[t] = n;
+}
 
 }  // namespace flk

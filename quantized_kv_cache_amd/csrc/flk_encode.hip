@@ -40,7 +40,7 @@ template <bool RESID, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void encode_k_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
     int32_t W, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes, uint32_t* __restrict__ params,
-    uint32_t* __restrict__ status) {
+    int32_t* __restrict__ tile_start, uint32_t* __restrict__ status) {
   __shared__ float s_min[4][128];
   __shared__ float s_max[4][128];
   __shared__ float s_m[128], s_s[128], s_rs[128];
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
         ract[i] = false;
         bad_row = true;
       } else {
-        xv = *reinterpret_cast<const uint4*>(x + int64_t(j) * W + ch);
+        xv = ld_stream(x + int64_t(j) * W + ch);
         roff[i] = int64_t(p) * W + ch;
         if (RESID) rv[i] = *reinterpret_cast<const uint4*>(recon + roff[i]);
       }
@@ -81,6 +81,13 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
     unpack8(xv, v[i]);
   }
   if (SPARSE && bad_row && status) atomicOr(status, kDevRows);
+  if (SPARSE && blockIdx.y == 0 && cc == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = band * kGroup + rs + 16 * i;
+      if (j < n) write_tile_index(rows, n, T, j, tile_start);
+    }
+  }
   if (RESID) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
     s_s[tid] = p.s;
     s_rs[tid] = p.rs;
     if (chan < W) {
-      params[int64_t(band) * W + chan] = p.packed;
+      st_stream32(params + int64_t(band) * W + chan, p.packed);
       if (p.err && status) atomicOr(status, p.err);
     }
   }
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
     }
-    *reinterpret_cast<uint32_t*>(codes + ((int64_t(j) * W + ch) >> 1)) = pack_codes8(k);
+    st_stream32(codes + ((int64_t(j) * W + ch) >> 1), pack_codes8(k));
     *reinterpret_cast<uint4*>(recon + roff[i]) = pack8(out);
   }
 }
@@ -165,7 +172,7 @@ template <bool RESID, bool SPARSE, int LPH>
 __global__ __launch_bounds__(kThreads) void encode_v_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
     int32_t H, int32_t D, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes,
-    uint32_t* __restrict__ params, uint32_t* __restrict__ status) {
+    uint32_t* __restrict__ params, int32_t* __restrict__ tile_start, uint32_t* __restrict__ status) {
   constexpr int HS = kThreads / LPH;
   constexpr int U = 4;
   const int tid = threadIdx.x;
@@ -198,10 +205,11 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
           act[u] = false;
           if (status) atomicOr(status, kDevRows);
         }
+        if (h == 0 && w == 0) write_tile_index(rows, n, T, int32_t(j), tile_start);
         ro = (int64_t(p) * H + h) * D + w * 8;
       }
       if (act[u]) {
-        xv = *reinterpret_cast<const uint4*>(x + it * D + w * 8);
+        xv = ld_stream(x + it * D + w * 8);
         roff[u] = ro;
         if (RESID) rv[u] = *reinterpret_cast<const uint4*>(recon + ro);
       }
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
     const int64_t it = base + u * HS + hs;
     GroupParams p = make_params(mn, mx);
     if ((w & 7) == 0) {
-      params[it * S + (w >> 3)] = p.packed;
+      st_stream32(params + it * S + (w >> 3), p.packed);
       if (p.err && status) atomicOr(status, p.err);
     }
     float k[8], out[8];
@@ -250,15 +258,15 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
     }
-    *reinterpret_cast<uint32_t*>(codes + ((it * D + w * 8) >> 1)) = pack_codes8(k);
+    st_stream32(codes + ((it * D + w * 8) >> 1), pack_codes8(k));
     *reinterpret_cast<uint4*>(recon + roff[u]) = pack8(out);
   }
 }
 
 template <bool RESID, bool SPARSE>
 static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t H, int32_t D,
-                           void* recon, uint8_t* codes, uint32_t* params, uint32_t* status,
-                           hipStream_t stream) {
+                           void* recon, uint8_t* codes, uint32_t* params, int32_t* tile_start,
+                           uint32_t* status, hipStream_t stream) {
   const int cph = D / 8;
   const int lph = cph <= 8 ? 8 : cph <= 16 ? 16 : cph <= 32 ? 32 : 64;
   const int per_block = (kThreads / lph) * 4;
@@ -268,7 +276,7 @@ static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_
   uint16_t* rp = static_cast<uint16_t*>(recon);
 #define FLK_LAUNCH_V(L)                                                                        \
   hipLaunchKernelGGL((encode_v_kernel<RESID, SPARSE, L>), grid, dim3(kThreads), 0, stream, xp, \
-                     rows, n, T, H, D, rp, codes, params, status)
+                     rows, n, T, H, D, rp, codes, params, tile_start, status)
   switch (lph) {
     case 8: FLK_LAUNCH_V(8); break;
     case 16: FLK_LAUNCH_V(16); break;
@@ -281,29 +289,31 @@ static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_
 
 template <bool RESID, bool SPARSE>
 static hipError_t launch_k(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t W, void* recon,
-                           uint8_t* codes, uint32_t* params, uint32_t* status, hipStream_t stream) {
+                           uint8_t* codes, uint32_t* params, int32_t* tile_start, uint32_t* status,
+                           hipStream_t stream) {
   const int cpr = W / 8;
   const dim3 grid(unsigned((n + kGroup - 1) / kGroup), unsigned((cpr + 15) / 16));
   hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), grid, dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x), rows, n, T, W, static_cast<uint16_t*>(recon),
-                     codes, params, status);
+                     codes, params, tile_start, status);
   return hipGetLastError();
 }
 
 hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* rows, int32_t n,
                          int32_t T, int32_t H, int32_t D, void* recon, uint8_t* codes,
-                         uint32_t* params, uint32_t* status, hipStream_t stream) {
+                         uint32_t* params, int32_t* tile_start, uint32_t* status,
+                         hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const bool sparse = rows != nullptr;
   if (kind == FLK_KIND_K) {
     const int32_t W = H * D;
-    if (!resid) return launch_k<false, false>(x, rows, n, T, W, recon, codes, params, status, stream);
-    if (!sparse) return launch_k<true, false>(x, rows, n, T, W, recon, codes, params, status, stream);
-    return launch_k<true, true>(x, rows, n, T, W, recon, codes, params, status, stream);
+    if (!resid) return launch_k<false, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+    if (!sparse) return launch_k<true, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+    return launch_k<true, true>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
   }
-  if (!resid) return launch_v<false, false>(x, rows, n, T, H, D, recon, codes, params, status, stream);
-  if (!sparse) return launch_v<true, false>(x, rows, n, T, H, D, recon, codes, params, status, stream);
-  return launch_v<true, true>(x, rows, n, T, H, D, recon, codes, params, status, stream);
+  if (!resid) return launch_v<false, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
+  if (!sparse) return launch_v<true, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
+  return launch_v<true, true>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
 }
 
 }  // namespace flk

@@ -11,10 +11,11 @@ namespace flk {
 
 // One loop of the chain as the kernels see it.
 struct StreamArgs {
-  const int32_t* rows;     // nullptr = dense
+  const int32_t* rows;        // nullptr = dense
   const uint8_t* codes;
   const uint32_t* params;
-  int32_t n;               // compact rows
+  const int32_t* tile_start;  // inverse map per 64 positions (compact loops only)
+  int32_t n;                  // compact rows
 };
 
 struct ChainArgs {
@@ -25,7 +26,8 @@ struct ChainArgs {
 // Encode one loop (base when resid == false).  Returns a hipError_t.
 hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* rows, int32_t n,
                          int32_t T, int32_t H, int32_t D, void* recon, uint8_t* codes,
-                         uint32_t* params, uint32_t* status, hipStream_t stream);
+                         uint32_t* params, int32_t* tile_start, uint32_t* status,
+                         hipStream_t stream);
 
 hipError_t launch_reconstruct(int kind, int32_t T, int32_t H, int32_t D, const ChainArgs& chain,
                               void* out, hipStream_t stream);

@@ -42,7 +42,7 @@ class Desc(ctypes.Structure):
 
 class StreamC(ctypes.Structure):
     _fields_ = [("n_rows", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_void_p),
-                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p)]
+                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p), ("tile_start", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.flk_params_bytes.argtypes = [D, i32]
         L.flk_rows_bytes.restype = sz
         L.flk_rows_bytes.argtypes = [i32, ctypes.c_int]
+        L.flk_tile_index_bytes.restype = sz
+        L.flk_tile_index_bytes.argtypes = [i32]
         L.flk_attn_workspace_bytes.restype = sz
         L.flk_attn_workspace_bytes.argtypes = [D, i32, i32]
         L.flk_status_string.restype = ctypes.c_char_p
@@ -77,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.flk_encode_base.restype = ctypes.c_int
         L.flk_encode_base.argtypes = [D, P, i32, P, P, P, P, P]
         L.flk_encode_residual.restype = ctypes.c_int
-        L.flk_encode_residual.argtypes = [D, P, P, i32, i32, P, P, P, P, P]
+        L.flk_encode_residual.argtypes = [D, P, P, i32, i32, P, P, P, P, P, P]
         L.flk_reconstruct.restype = ctypes.c_int
         L.flk_reconstruct.argtypes = [D, i32, S, i32, P, P]
         L.flk_decode_attn_packed.restype = ctypes.c_int
@@ -126,6 +128,10 @@ def rows_bytes(n: int, sparse: bool) -> int:
     return int(lib().flk_rows_bytes(n, 1 if sparse else 0))
 
 
+def tile_index_bytes(T: int) -> int:
+    return int(lib().flk_tile_index_bytes(T))
+
+
 def attn_workspace_bytes(H: int, D: int, T: int, n_q_heads: int) -> int:
     return int(lib().flk_attn_workspace_bytes(ctypes.byref(desc(K, H, D)), T, n_q_heads))
 
@@ -136,22 +142,29 @@ def params_shape(kind: int, H: int, D: int, n: int):
 
 @dataclass
 class Packed:
-    """Device buffers of one encoded loop (caller-owned torch tensors)."""
+    """Device buffers of one encoded loop (caller-owned torch tensors).  Compact loops also
+    carry tile_start, the inverse map per 64 positions that flk_encode_residual writes."""
     n_rows: int
     rows: Optional[torch.Tensor]
     codes: torch.Tensor
     params: torch.Tensor
+    tile_start: Optional[torch.Tensor] = None
 
     @staticmethod
-    def empty(kind: int, H: int, D: int, n: int, rows: Optional[torch.Tensor] = None,
-              device="cuda") -> "Packed":
+    def empty(kind: int, H: int, D: int, n: int, rows: Optional[torch.Tensor] = None, T: int = 0,
+              tile_start: Optional[torch.Tensor] = None, device="cuda") -> "Packed":
         codes = torch.empty((n, H, D // 2), dtype=torch.uint8, device=device)
         params = torch.empty(params_shape(kind, H, D, n), dtype=torch.int32, device=device)
-        return Packed(n, rows, codes, params)
+        if rows is not None and tile_start is None:
+            if T < 1:
+                raise ValueError("a compact loop needs T to size its tile index")
+            tile_start = torch.empty(tile_index_bytes(T) // 4, dtype=torch.int32, device=device)
+        return Packed(n, rows, codes, params, tile_start if rows is not None else None)
 
     def c(self) -> StreamC:
         return StreamC(self.n_rows, 0, None if self.rows is None else self.rows.data_ptr(),
-                       self.codes.data_ptr(), self.params.data_ptr())
+                       self.codes.data_ptr(), self.params.data_ptr(),
+                       None if self.tile_start is None else self.tile_start.data_ptr())
 
     def nbytes(self) -> int:
         return self.codes.numel() + 4 * self.params.numel() + (0 if self.rows is None else 4 * self.rows.numel())
@@ -178,8 +191,8 @@ def encode_residual(kind: int, x_rows: torch.Tensor, rows: Optional[torch.Tensor
     n, H, D = x_rows.shape
     T = recon.shape[0]
     _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D)), _ptr(x_rows), _ptr(rows), n, T,
-                                     _ptr(recon), _ptr(out.codes), _ptr(out.params), _ptr(status),
-                                     _stream(stream)),
+                                     _ptr(recon), _ptr(out.codes), _ptr(out.params), _ptr(out.tile_start),
+                                     _ptr(status), _stream(stream)),
            "flk_encode_residual")
 
 

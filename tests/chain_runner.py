@@ -37,7 +37,7 @@ class GpuChain:
         for loop, (x, r) in enumerate(zip(xs, rows)):
             xd = to_dev_bf16(x)
             rd = to_dev_rows(r)
-            p = flk.Packed.empty(kind, H, D, x.shape[0], rd)
+            p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T)
             if loop == 0:
                 flk.encode_base(kind, xd, p, self.recon, status)
             else:
@@ -93,3 +93,8 @@ def compare_chains(g: GpuChain, o: OracleChain, head_slice: Optional[slice] = No
         assert_same(codes[:, hs], o.streams[loop].codes, f"{tag} codes loop {loop + 1}")
         assert_same(params[:, hs], o.streams[loop].params, f"{tag} params loop {loop + 1}")
         assert_same(g.recons[loop][:, hs], o.recons[loop], f"{tag} recon loop {loop + 1}")
+        r = o.streams[loop].rows
+        if r is not None and len(r):
+            got = g.packed[loop].tile_start.cpu().numpy()
+            assert np.array_equal(got, orc.tile_index(r, g.T)), f"{tag} tile index loop {loop + 1}"
+

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from quantized_kv_cache_amd import flk
@@ -38,6 +39,7 @@ def test_sizes_match_closed_forms(kind, H, D, n):
     groups = -(-n // 64) * H * D if kind == flk.K else n * H * -(-D // 64)
     assert flk.params_bytes(kind, H, D, n) == 4 * groups
     assert flk.rows_bytes(n, True) == 4 * n and flk.rows_bytes(n, False) == 0
+    assert flk.tile_index_bytes(n) == 4 * (-(-n // 64) + 1) == orc.tile_index(np.arange(0), n).nbytes
 
 
 def test_descriptor_checks():
@@ -80,16 +82,18 @@ def test_encode_residual_validation():
     L = flk.lib()
     d = flk.desc(flk.V, 2, 64)
 
-    def call(x, rows, n, T, recon=FAKE, codes=FAKE, params=FAKE):
-        return L.flk_encode_residual(ctypes.byref(d), x, rows, n, T, recon, codes, params, None, None)
+    def call(x, rows, n, T, recon=FAKE, codes=FAKE, params=FAKE, tile=FAKE):
+        return L.flk_encode_residual(ctypes.byref(d), x, rows, n, T, recon, codes, params, tile, None, None)
     assert call(FAKE, None, 10, 16) == 2            # dense needs n == T
     assert call(FAKE, FAKE, 17, 16) == 2            # n > T
     assert call(FAKE, FAKE, -1, 16) == 2
     assert call(None, FAKE, 4, 16) == 1
     assert call(FAKE, FAKE, 4, 16, recon=None) == 1
     assert call(FAKE, ctypes.c_void_p((1 << 20) + 1), 4, 16) == 3
+    assert call(FAKE, FAKE, 4, 16, tile=None) == 1   # a compact loop writes its tile index
+    assert call(FAKE, FAKE, 4, 16, tile=ctypes.c_void_p((1 << 20) + 2)) == 3
     # an empty residual loop is valid and enqueues nothing
-    assert call(None, FAKE, 0, 16, codes=None, params=None) == 0
+    assert call(None, FAKE, 0, 16, codes=None, params=None, tile=None) == 0
 
 
 def test_reconstruct_validation():
@@ -100,17 +104,18 @@ def test_reconstruct_validation():
     def call(chain, n_loops, T=64, out=FAKE):
         arr = (S * max(1, len(chain)))(*chain) if chain else None
         return L.flk_reconstruct(ctypes.byref(d), T, arr, n_loops, out, None)
-    base = S(64, 0, None, FAKE.value, FAKE.value)
+    base = S(64, 0, None, FAKE.value, FAKE.value, None)
     assert call([], 1) == 1
     assert call([base], 0) == 2
     assert call([base] * 9, 9) == 2
-    assert call([S(32, 0, None, FAKE.value, FAKE.value)], 1) == 2      # base must be dense n == T
-    assert call([S(64, 0, FAKE.value, FAKE.value, FAKE.value)], 1) == 2
-    assert call([base, S(65, 0, FAKE.value, FAKE.value, FAKE.value)], 2) == 2
-    assert call([base, S(10, 0, None, FAKE.value, FAKE.value)], 2) == 2
-    assert call([base, S(10, 7, FAKE.value, FAKE.value, FAKE.value)], 2) == 4
-    assert call([base, S(10, 0, FAKE.value, None, FAKE.value)], 2) == 1
-    assert call([base, S(10, 0, FAKE.value, MIS.value, FAKE.value)], 2) == 3
+    assert call([S(32, 0, None, FAKE.value, FAKE.value, None)], 1) == 2      # base must be dense n == T
+    assert call([S(64, 0, FAKE.value, FAKE.value, FAKE.value, FAKE.value)], 1) == 2
+    assert call([base, S(65, 0, FAKE.value, FAKE.value, FAKE.value, FAKE.value)], 2) == 2
+    assert call([base, S(10, 0, None, FAKE.value, FAKE.value, None)], 2) == 2
+    assert call([base, S(10, 7, FAKE.value, FAKE.value, FAKE.value, FAKE.value)], 2) == 4
+    assert call([base, S(10, 0, FAKE.value, None, FAKE.value, FAKE.value)], 2) == 1
+    assert call([base, S(10, 0, FAKE.value, MIS.value, FAKE.value, FAKE.value)], 2) == 3
+    assert call([base, S(10, 0, FAKE.value, FAKE.value, FAKE.value, None)], 2) == 1   # no tile index
     assert call([base], 1, out=None) == 1
     assert call([base], 1, out=MIS) == 3
 
@@ -120,7 +125,7 @@ def test_attention_validation():
     kd, vd = flk.desc(flk.K, 8, 128), flk.desc(flk.V, 8, 128)
     S = flk.StreamC
     T = 256
-    chain = (S * 1)(S(T, 0, None, FAKE.value, FAKE.value))
+    chain = (S * 1)(S(T, 0, None, FAKE.value, FAKE.value, None))
     ws = flk.attn_workspace_bytes(8, 128, T, 32)
     assert ws > 0
 

@@ -177,8 +177,10 @@ def test_determinism_and_no_stray_writes():
                 pb_n = flk.params_bytes(kind, H, D, n) // 4
                 pb = torch.full((pb_n + pad,), 0x3C3C3C3C, dtype=torch.int32, device="cuda")
                 rd = None if r is None else torch.from_numpy(r).cuda()
+                ts = None if r is None else torch.empty(flk.tile_index_bytes(T) // 4, dtype=torch.int32,
+                                                         device="cuda")
                 p = flk.Packed(n, rd, cb[: n * H * D // 2].view(n, H, D // 2),
-                               pb[:pb_n].view(flk.params_shape(kind, H, D, n)))
+                               pb[:pb_n].view(flk.params_shape(kind, H, D, n)), ts)
                 xd = to_dev_bf16(x)
                 if loop == 0:
                     flk.encode_base(kind, xd, p, recon)

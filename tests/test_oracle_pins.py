@@ -531,3 +531,14 @@ def test_decode_attention_matches_torch_float64():
     zq = bf16(np.zeros((Hq, D), np.float32))
     mean = orc.decode_attn(zq, k, v, scale)
     assert np.allclose(mean, np.repeat(f32(v).astype(np.float64).mean(axis=0), Hq // Hkv, axis=0), rtol=1e-12)
+
+
+def test_tile_index_definition():
+    """tile_index[t] counts the rows before position 64t; spot values checked by hand."""
+    rows = np.array([0, 5, 63, 64, 200, 511], np.int32)
+    ti = orc.tile_index(rows, 600)
+    assert list(ti) == [0, 3, 4, 4, 5, 5, 5, 5, 6, 6, 6]
+    assert list(orc.tile_index(np.array([], np.int32), 130)) == [0, 0, 0, 0]
+    g = np.random.default_rng(20)
+    r = np.sort(g.choice(5000, 777, replace=False)).astype(np.int32)
+    assert np.array_equal(orc.tile_index(r, 5000), np.searchsorted(r, 64 * np.arange(-(-5000 // 64) + 1)))
