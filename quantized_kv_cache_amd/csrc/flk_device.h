@@ -66,7 +66,7 @@ __device__ __forceinline__ GroupParams make_params(float mn, float mx) {
   p.packed = uint32_t(m16) | (uint32_t(s16) << 16);
   p.m = f16_bits_to_f32(m16);
   p.s = f16_bits_to_f32(s16);
-  p.rs = __builtin_amdgcn_rcpf(p.s);
+  p.rs = p.s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(p.s);   // constant group: every q is 0
   uint32_t e = 0;
   // Inf/NaN anywhere in the group make the extremes (or their difference) non-finite.
   if (!(__builtin_isfinite(mn) && __builtin_isfinite(mx))) e |= 1u;
@@ -93,9 +93,46 @@ __device__ __forceinline__ float code_of(float v, const GroupParams& p) {
   return (p.s == 0.0f) ? 0.0f : k;
 }
 
+// Codes of n values against one group's params, as floats 0..15.  The fast path rounds
+// q' = RN(y * rs) clamped to [0, 15]; it can differ from the exact rule only where q' lies
+// within 2^-15 of a half-integer (see code_of), and one test over all n values sends the
+// lane to the correctly rounded division in that case.  Clamping before rounding equals
+// rounding before clamping, and a clamped value (0 or 15) is never near a half-integer.
+template <int N>
+__device__ __forceinline__ void codes_of(const float v[N], const GroupParams& p, float k[N]) {
+  float y[N], dev = 0.0f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    y[e] = v[e] - p.m;
+    const float qc = __builtin_amdgcn_fmed3f(y[e] * p.rs, 0.0f, 15.0f);
+    k[e] = __builtin_rintf(qc);
+    dev = __builtin_fmaxf(dev, __builtin_fabsf(qc - k[e]));
+  }
+  if (__builtin_expect(dev > 0.5f - 0x1p-15f, 0)) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) k[e] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[e] / p.s, 0.0f, 15.0f));
+  }
+}
+
 // decode: min + scale * code in binary32; the product is exact (4-bit code times an 11-bit
 // significand), so the fused form rounds once exactly like the separate multiply and add.
 __device__ __forceinline__ float decode(float code, float m, float s) { return __builtin_fmaf(code, s, m); }
+
+// Pack 8 codes (floats 0..15, exact integers) into a uint32 with v_cvt_pk_u8_f32: the even
+// channels fill the bytes of one word, the odd channels another, shifted into the high
+// nibbles.
+__device__ __forceinline__ uint32_t pack_codes8_u8(const float c[8]) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(c[0], 0, lo);
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(c[2], 1, lo);
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(c[4], 2, lo);
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(c[6], 3, lo);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(c[1], 0, hi);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(c[3], 1, hi);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(c[5], 2, hi);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(c[7], 3, hi);
+  return lo | (hi << 4);
+}
 
 // Pack 8 codes (floats 0..15) into a uint32, channel 2j in the low nibble of byte j.
 __device__ __forceinline__ uint32_t pack_codes8(const float c[8]) {
@@ -171,30 +208,48 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 constexpr int kBufDword3 = 0x00020000;
 constexpr int kCacheStream = 2;     // nontemporal: stream past the caches
 
+// The row offset must be wave-uniform; readfirstlane states it so the compiler never builds
+// a per-lane loop around an access (it is free when the value already is a scalar).
+__device__ __forceinline__ int soffset(uint32_t soff) { return __builtin_amdgcn_readfirstlane(int(soff)); }
+
 __device__ __forceinline__ BufRsrc make_buf(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), kBufDword3);
 }
 template <int AUX = 0>
 __device__ __forceinline__ uint32_t buf_ld32(BufRsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), AUX);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), soffset(soff), AUX);
 }
 template <int AUX = 0>
 __device__ __forceinline__ uint4 buf_ld128(BufRsrc r, uint32_t voff, uint32_t soff) {
   typedef uint32_t v4 __attribute__((ext_vector_type(4)));
-  const v4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), AUX);
+  const v4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), soffset(soff), AUX);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 template <int AUX = 0>
 __device__ __forceinline__ void buf_st32(uint32_t w, BufRsrc r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b32(w, r, int(voff), int(soff), AUX);
+  __builtin_amdgcn_raw_buffer_store_b32(w, r, int(voff), soffset(soff), AUX);
 }
 template <int AUX = 0>
 __device__ __forceinline__ void buf_st128(const uint4& w, BufRsrc r, uint32_t voff, uint32_t soff) {
   typedef uint32_t v4 __attribute__((ext_vector_type(4)));
   const v4 v = {w.x, w.y, w.z, w.w};
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(voff), int(soff), AUX);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(voff), soffset(soff), AUX);
 }
 __device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+template <int AUX = 0>
+__device__ __forceinline__ void buf_st64(uint32_t lo, uint32_t hi, BufRsrc r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t v2 __attribute__((ext_vector_type(2)));
+  const v2 v = {lo, hi};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, int(voff), soffset(soff), AUX);
+}
+
+// ---- quad-lane exchanges through DPP (no LDS traffic) ----------------------------------------
+__device__ __forceinline__ float dpp_xor1(float v) {   // quad_perm [1,0,3,2]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {   // quad_perm [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
 
 // ---- nontemporal (streaming) global accesses ----------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -5,12 +5,18 @@
 // reduces group extremes, derives FP16 params, writes nibble-packed codes and params, and
 // writes the updated reconstruction back in place.  The method is the FlashLoop RFC
 // (vllm-rlt #156) section 3.3; group axes and storage follow vllm-rlt PR #166 "Purpose".
+#include <type_traits>
+
 #include "flk_device.h"
 #include "flk_internal.h"
 
 namespace flk {
 
 constexpr int kThreads = 256;
+#ifndef FLK_VWIDE_WAVES
+#define FLK_VWIDE_WAVES 32768
+#endif
+constexpr int kVWideWaves = FLK_VWIDE_WAVES;
 constexpr uint32_t kDevRows = FLK_DEV_ROWS;
 
 __device__ __forceinline__ void unpack8(const uint4& w, float v[8]) {
@@ -263,6 +269,116 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// V, wide rows (D % 64 == 0, H*D % 1024 == 0): a strip is 1024 channels, 64 lanes x 16
+// channels, so a 64-channel group is 4 consecutive lanes and its extremes take two DPP quad
+// exchanges.  Each wave walks its own run of compact rows one row at a time; the row index,
+// rows[j] and every row offset are scalars, every access is a buffer access, and the next
+// row's loads are issued before the current row is processed.
+// ---------------------------------------------------------------------------------------
+template <bool RESID, bool SPARSE>
+__global__ __launch_bounds__(kThreads) void encode_v_wide_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
+    int32_t W, int32_t rows_per_wave, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes,
+    uint32_t* __restrict__ params, int32_t* __restrict__ tile_start, uint32_t* __restrict__ status) {
+  constexpr int kCh = 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int32_t j0 = (int32_t(blockIdx.x) * (kThreads / 64) + wave) * rows_per_wave;
+  if (j0 >= n) return;
+  const int32_t j1 = min(j0 + rows_per_wave, n);
+  const uint32_t ch = uint32_t(blockIdx.y) * 1024u + uint32_t(lane) * kCh;
+  const uint32_t xrow = uint32_t(W) * 2u, crow = uint32_t(W) / 2u, prow = uint32_t(W) / 16u;
+  const BufRsrc xrs = make_buf(x, uint32_t(n) * xrow);
+  const BufRsrc rrs = make_buf(recon, uint32_t(T) * xrow);
+  const BufRsrc crs = make_buf(codes, uint32_t(n) * crow);
+  const BufRsrc prs = make_buf(params, uint32_t(n) * prow);
+  const uint32_t xv = ch * 2u, cv = ch / 2u, pv = (ch / 64u) * 4u;
+
+  // Two register sets, used alternately; the loop is unrolled by two so every set index is
+  // a compile-time constant (a runtime index would put the sets in scratch memory).
+  uint4 xa[2], xb[2], ra[2], rb[2];
+  int32_t pos[2];
+  auto issue = [&](int32_t j, auto B) {
+    constexpr int b = decltype(B)::value;
+    int32_t p = SPARSE ? uniform(rows[j]) : j;
+    if (SPARSE && uint32_t(p) >= uint32_t(T)) p = -1;       // malformed map: skip the row
+    pos[b] = p;
+    const uint32_t pr = uint32_t(max(p, 0));
+    xa[b] = buf_ld128<kCacheStream>(xrs, xv, uint32_t(j) * xrow);
+    xb[b] = buf_ld128<kCacheStream>(xrs, xv + 16u, uint32_t(j) * xrow);
+    if (RESID) {
+      ra[b] = buf_ld128(rrs, xv, pr * xrow);
+      rb[b] = buf_ld128(rrs, xv + 16u, pr * xrow);
+    }
+  };
+  uint32_t err = 0;
+  auto process = [&](int32_t j, auto B) {
+    constexpr int b = decltype(B)::value;
+    if (SPARSE && lane == 0 && blockIdx.y == 0) write_tile_index(rows, n, T, j, tile_start);
+    const int32_t p = pos[b];
+    if (SPARSE && p < 0) { err |= kDevRows; return; }
+    float v[kCh], r[kCh];
+    unpack8(xa[b], v);
+    unpack8(xb[b], v + 8);
+    if (RESID) {
+      unpack8(ra[b], r);
+      unpack8(rb[b], r + 8);
+#pragma unroll
+      for (int e = 0; e < kCh; ++e) v[e] = round_bf16(v[e] - r[e]);
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int e = 1; e < kCh; ++e) { mn = tmin(mn, v[e]); mx = tmax(mx, v[e]); }
+    mn = tmin(mn, dpp_xor1(mn));
+    mx = tmax(mx, dpp_xor1(mx));
+    mn = tmin(mn, dpp_xor2(mn));
+    mx = tmax(mx, dpp_xor2(mx));
+    const GroupParams gp = make_params(mn, mx);
+    err |= gp.err;
+    float k[kCh];
+    codes_of<kCh>(v, gp, k);
+    buf_st64<kCacheStream>(pack_codes8_u8(k), pack_codes8_u8(k + 8), crs, cv, uint32_t(j) * crow);
+    if ((lane & 3) == 0) buf_st32<kCacheStream>(gp.packed, prs, pv, uint32_t(j) * prow);
+    float o[kCh];
+#pragma unroll
+    for (int e = 0; e < kCh; ++e) {
+      o[e] = decode(k[e], gp.m, gp.s);
+      if (RESID) o[e] = r[e] + round_bf16(o[e]);
+    }
+    buf_st128(pack8(o), rrs, xv, uint32_t(p) * xrow);
+    buf_st128(pack8(o + 8), rrs, xv + 16u, uint32_t(p) * xrow);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  issue(j0, B0{});
+  for (int32_t j = j0; j < j1; j += 2) {
+    if (j + 1 < j1) issue(j + 1, B1{});
+    process(j, B0{});
+    if (j + 1 >= j1) break;
+    if (j + 2 < j1) issue(j + 2, B0{});
+    process(j + 1, B1{});
+  }
+  if (err && status) atomicOr(status, err);
+}
+
+template <bool RESID, bool SPARSE>
+static hipError_t launch_v_wide(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t W,
+                                void* recon, uint8_t* codes, uint32_t* params, int32_t* tile_start,
+                                uint32_t* status, hipStream_t stream) {
+  const int32_t strips = W / 1024;
+  // about kVWideWaves waves per launch: many short waves (one or two rows each) keep the
+  // most loads in flight and let the wave scheduler hide their latency
+  const int64_t per_wave = (int64_t(n) * strips + kVWideWaves - 1) / kVWideWaves;
+  const int32_t rpw = int32_t(per_wave < 1 ? 1 : per_wave);
+  const int32_t waves = (n + rpw - 1) / rpw;
+  const dim3 grid(unsigned((waves + 3) / 4), unsigned(strips));
+  hipLaunchKernelGGL((encode_v_wide_kernel<RESID, SPARSE>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), rows, n, T, W, rpw,
+                     static_cast<uint16_t*>(recon), codes, params, tile_start, status);
+  return hipGetLastError();
+}
+
 template <bool RESID, bool SPARSE>
 static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t H, int32_t D,
                            void* recon, uint8_t* codes, uint32_t* params, int32_t* tile_start,
@@ -310,6 +426,12 @@ hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* row
     if (!resid) return launch_k<false, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
     if (!sparse) return launch_k<true, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
     return launch_k<true, true>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+  }
+  if (D % 64 == 0 && (H * D) % 1024 == 0) {
+    const int32_t W = H * D;
+    if (!resid) return launch_v_wide<false, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+    if (!sparse) return launch_v_wide<true, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+    return launch_v_wide<true, true>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
   }
   if (!resid) return launch_v<false, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
   if (!sparse) return launch_v<true, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);

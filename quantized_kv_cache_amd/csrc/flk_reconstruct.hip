@@ -20,6 +20,10 @@ namespace flk {
 constexpr int kRThreads = 256;
 constexpr int kTile = 64;                 // tokens per block, narrow rows
 constexpr int kBatch = FLK_RECON_BATCH;   // tokens whose loads a wave issues together
+#ifndef FLK_RECON_TPW
+#define FLK_RECON_TPW 4
+#endif
+constexpr int kWideTokPerWave = FLK_RECON_TPW;  // tokens per wave, wide rows (divides 64)
 constexpr int kMaxStripCh = 512;
 
 template <int KIND, int NL>
@@ -156,21 +160,21 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_kernel(ChainArgs chain,
   }
 }
 
-// Wide rows (H*D >= 512 channels): a strip is 512 channels, 64 lanes x 8 channels, and
-// every wave works alone on 16 consecutive tokens with no block barrier: it finds its
-// tokens' compact rows with a wave-level search and a wave-private LDS table, then
-// reconstructs one token at a time, so a token's compact row is a scalar.  Every access is
-// a buffer access (row offset scalar, lane offset vector).  A token a compact loop does not
-// list reads through a zero-length descriptor, chosen with scalar selects, so its load
-// returns zero with no branch and no memory traffic; only that loop's arithmetic is skipped
-// (a scalar branch; the value is inherited bit for bit).  Params stay packed FP16 pairs and
-// feed v_fma_mix_f32 directly.  SPARSE has bit l set when loop l is compact; with RT the
-// pattern is read from the chain at run time instead (chains longer than 4 loops).
+// Wide rows (H*D >= 512 channels): a strip is 512 channels, 64 lanes x 8 channels, and every
+// wave works alone on kWideTokPerWave consecutive tokens with no block barrier.  It reads its
+// tile's slice of each compact loop's tile index, scatters those rows into a wave-private LDS
+// table indexed by position, and then reconstructs one token at a time, so a token's compact
+// row is a scalar (readlane) and every access is a buffer access with a scalar row offset.
+// Many short waves keep more loads in flight than a few long ones.  A token that a compact
+// loop does not list loads row 0 (a cache hit) and skips that loop's arithmetic: its value is
+// inherited bit for bit.  Params stay packed FP16 pairs and feed v_fma_mix_f32 directly.
+// SPARSE has bit l set when loop l is compact; with RT the pattern is read from the chain at
+// run time instead (chains longer than 4 loops).
 template <int KIND, int NL, uint32_t SPARSE, bool RT>
 __global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs chain, int32_t T,
                                                                       int32_t H, int32_t D,
                                                                       uint16_t* __restrict__ out) {
-  constexpr int kTokPerWave = 16;
+  constexpr int kTokPerWave = kWideTokPerWave;
   __shared__ int32_t s_map[kRThreads / 64][NL][kTokPerWave];
   auto is_sparse = [&](int l) -> bool {
     return RT ? chain.s[l].rows != nullptr : ((SPARSE >> l) & 1u) != 0;
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs c
 
   // ---- this wave's position -> compact row table (wave-private; no block barrier) ----
   // The tile index gives the compact rows of the wave's 64-position tile; lane L looks at
-  // the tile's L-th compact row and records it if it falls in the wave's 16 positions.
+  // the tile's L-th compact row and records it if it falls in the wave's own positions.
   const int32_t tile = tw / kGroup;
   int32_t lo[NL], hi[NL];
 #pragma unroll
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs c
   const uint32_t o_voff = uint32_t(ch) * 2u;
   const uint32_t orow_bytes = uint32_t(W) * 2u;
 
-  // K params: one resident rowgroup per loop.  A dense loop's 16 tokens lie in one rowgroup;
+  // K params: one resident rowgroup per loop.  A dense loop's tokens lie in one rowgroup;
   // a compact loop's rows for them span at most two, so the set is reloaded at most once.
   uint4 kreg[NL][2];
   int32_t krg[NL];
@@ -322,7 +326,8 @@ template <int KIND>
 static void launch_kind(dim3 grid, const ChainArgs& chain, int32_t T, int32_t H, int32_t D,
                         int32_t lpt_log2, uint16_t* out, hipStream_t stream) {
   if (lpt_log2 == 6) {
-    const dim3 wgrid(unsigned((T + 63) / 64), grid.y);
+    constexpr int kTokPerBlock = kWideTokPerWave * (kRThreads / 64);
+    const dim3 wgrid(unsigned((T + kTokPerBlock - 1) / kTokPerBlock), grid.y);
     uint32_t mask = 0;
     for (int l = 0; l < chain.n_loops; ++l) mask |= (chain.s[l].rows != nullptr ? 1u : 0u) << l;
 #define FLK_W(NLV, M)                                                                              \
