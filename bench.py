@@ -5,7 +5,8 @@ Workload (long prompt layer): one request/layer, K and V each [T=32768, H=8, D=1
 active sets), K Student-t(3) with per-channel multipliers, V N(0,1), loop deltas N(0,0.05).
 
 One step = for K and for V: flk_encode_base, flk_encode_residual x 3, flk_reconstruct of the
-final depth.  `value` = algorithmic bytes of the step (each input read once, each output
+final depth; the K chain and the V chain are independent and run on two streams (--streams 1
+puts both on one).  `value` = algorithmic bytes of the step (each input read once, each output
 written once) / wall time per step, inputs already resident in HBM.  Steps rotate over
 several independent buffer sets (> 1 GB in total) so the 256 MB MALL holds no timed data.
 
@@ -15,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -62,15 +64,28 @@ def call_bytes(kind, H, D, T, rows_list):
     return out
 
 
-def kernel_symbol(kind, call, D):
-    lph = 8 if D // 8 <= 8 else 16 if D // 8 <= 16 else 32 if D // 8 <= 32 else 64
+def kernel_symbol(kind, call, H, D, rows_list):
+    """Name of the kernel (as the profiler prints it, without namespace and arguments) that the
+    library launches for one call; mirrors the routing in csrc/flk_encode.hip and
+    csrc/flk_reconstruct.hip."""
+    W = H * D
     if call == "reconstruct":
-        return f"reconstruct_kernel<{kind}>"
-    resid = call != "base"
-    sparse = call == "sparse_residual"
+        n_loops = len(rows_list)
+        if W // 8 >= 64:
+            if n_loops <= 4:
+                mask = sum(1 << l for l, r in enumerate(rows_list) if r is not None)
+                return f"reconstruct_wide_kernel<{kind}, {n_loops}, {mask}u, false>"
+            return f"reconstruct_wide_kernel<{kind}, {n_loops}, 0u, true>"
+        return f"reconstruct_kernel<{kind}, {n_loops}>"
+    resid = str(call != "base").lower()
+    sparse = str(call == "sparse_residual").lower()
     if kind == flk.K:
-        return f"encode_k_kernel<{str(resid).lower()}, {str(sparse).lower()}>"
-    return f"encode_v_kernel<{str(resid).lower()}, {str(sparse).lower()}, {lph}>"
+        return f"encode_k_kernel<{resid}, {sparse}>"
+    if D % 64 == 0 and W % 1024 == 0:
+        return f"encode_v_wide_kernel<{resid}, {sparse}>"
+    cph = D // 8
+    lph = 8 if cph <= 8 else 16 if cph <= 16 else 32 if cph <= 32 else 64
+    return f"encode_v_kernel<{resid}, {sparse}, {lph}>"
 
 
 # ----------------------------------------------------------------------------- device state
@@ -116,15 +131,18 @@ class ChainSet:
             self.calls.append(("reconstruct", kind, L.flk_reconstruct,
                                (dp, w.T, arr, len(packed), P(out.data_ptr()))))
 
-    def run(self, stream, ev=None):
+    def run(self, streams, ev=None):
+        """Issue one step: every call on the stream of its tensor (streams[kind]); ev[i], when
+        given, is a pair of events recorded around call i on that same stream."""
         for i, (name, kind, fn, args) in enumerate(self.calls):
+            ts, sp = streams[kind]
             if ev is not None and ev[i] is not None:
-                ev[i][0].record()
-            st = fn(*args, stream)
+                ev[i][0].record(ts)
+            st = fn(*args, sp)
             if st != 0:
                 raise flk.FlkError(st, name)
             if ev is not None and ev[i] is not None:
-                ev[i][1].record()
+                ev[i][1].record(ts)
 
 
 # ----------------------------------------------------------------------------- cpu baseline
@@ -148,6 +166,103 @@ def cpu_baseline(w, host, sets, heads=(0, 1)):
                       f"C oracle on the host"}
 
 
+# ----------------------------------------------------------------------------- HBM traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prompt.txt")
+COPY_PROBE_BYTES = 1 << 29     # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE (2x the MALL)
+
+
+def source_digest():
+    """sha256 over the library's kernel and host sources: a traffic figure taken from an older
+    source tree is not reported."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def copy_probe():
+    """Plain copies of COPY_PROBE_BYTES (read once, written once) by an elementwise kernel whose
+    name contains 'bitwise_not'; the counter runs divide its FETCH_SIZE / WRITE_SIZE into the
+    known size to get the scale applied to the codec kernels.  Returns the copy's GB/s."""
+    src = torch.zeros(COPY_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.bitwise_not(src, out=dst)
+    ev[0].record()
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return 2 * COPY_PROBE_BYTES * 3 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+
+
+def _short_name(kernel_name):
+    n = kernel_name.split("(")[0].strip()
+    for pre in ("void ", "flk::"):
+        if n.startswith(pre):
+            n = n[len(pre):]
+    return n
+
+
+def summarize_pmc(dirs):
+    """Turn rocprofv3 --pmc counter CSVs (one run with FETCH_SIZE, one with WRITE_SIZE, each of
+    `bench.py --copy-probe`) into the per-launch HBM traffic table that bench.py reports."""
+    import csv
+    import glob
+    vals = {}                                   # (counter, kernel) -> [per-dispatch values]
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                key = (r["Counter_Name"], _short_name(r["Kernel_Name"]))
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    w = synth.WORKLOADS[3]
+    sets = synth.active_sets(w, w.T)
+    algo = {}
+    for kind in (flk.K, flk.V):
+        for name, b in call_bytes(kind, w.H, w.D, w.T, sets):
+            algo.setdefault(kernel_symbol(kind, name, w.H, w.D, sets), []).append(b)
+
+    def mean(counter, pred):
+        xs = [v for (c, k), vs in vals.items() if c == counter and pred(k) for v in vs]
+        return (sum(xs) / len(xs), len(xs)) if xs else (float("nan"), 0)
+    probe_kib = COPY_PROBE_BYTES / 1024
+    fetch_copy, nf = mean("FETCH_SIZE", lambda k: "bitwise_not" in k)
+    write_copy, nw = mean("WRITE_SIZE", lambda k: "bitwise_not" in k)
+    fs, ws_ = probe_kib / fetch_copy, probe_kib / write_copy
+    lines = [f"source_sha256 {source_digest()}",
+             f"copy_probe bytes {COPY_PROBE_BYTES} fetch_kib {fetch_copy:.1f} write_kib {write_copy:.1f} "
+             f"fetch_scale {fs:.4f} write_scale {ws_:.4f} dispatches {nf}/{nw}"]
+    for sym, bs in algo.items():
+        f, n1 = mean("FETCH_SIZE", lambda k, s=sym: k == s)
+        wr, n2 = mean("WRITE_SIZE", lambda k, s=sym: k == s)
+        traffic = (f * fs + wr * ws_) * 1024
+        a = sum(bs) / len(bs)
+        lines.append(f"kernel {sym} | dispatches {n1}/{n2} | fetch_kib {f:.1f} | write_kib {wr:.1f} | "
+                     f"traffic_bytes {traffic:.0f} | algorithmic_bytes {a:.0f} | ratio {traffic / a:.4f}")
+    return "\n".join(lines)
+
+
+def read_traffic(symbol):
+    """Per-launch HBM bytes of `symbol` from the committed counter summary, or None when there is
+    none or it was taken from other sources than the ones built now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest, found = None, None
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("source_sha256 "):
+            digest = line.split()[1]
+        elif line.startswith("kernel ") and line.split("|")[0][len("kernel "):].strip() == symbol:
+            for field in line.split("|"):
+                kv = field.split()
+                if kv and kv[0] == "traffic_bytes":
+                    found = float(kv[1])
+    return found if digest == source_digest() else None
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -156,14 +271,24 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled across steps")
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                    help="2: the K chain and the V chain on two streams; 1: both on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a plain copy of known size first (calibrates the HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print the traffic table from rocprofv3 counter output and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the codec runs per request/layer on a single device); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     flk.lib()
+    copy_gbs = copy_probe() if args.copy_probe else None
 
     w = synth.WORKLOADS[3]
     log(f"generating workload {w.name}: T={w.T} H={w.H} D={w.D}")
@@ -177,33 +302,37 @@ def main():
     for kind in (flk.K, flk.V):
         per_call += [(kind, name, b) for name, b in call_bytes(kind, w.H, w.D, w.T, sets)]
     step_bytes = sum(b for _, _, b in per_call)
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
+    # default-priority streams only; K chain and V chain are independent and overlap
+    ts = [torch.cuda.Stream(), torch.cuda.Stream()] if args.streams == 2 else [torch.cuda.Stream()] * 2
+    streams = {k: (ts[i], ctypes.c_void_p(ts[i].cuda_stream)) for i, k in enumerate((flk.K, flk.V))}
 
-    # warmup, and find the kernel with the largest share of the step
+    # warmup (each call timed on its stream), and find the kernel with the largest share of the step
     n_calls = len(chain_sets[0].calls)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
     times = np.zeros(n_calls)
+    counted = 0
     for i in range(max(args.warmup, 1)):
-        chain_sets[i % args.rotate].run(sp, ev)
+        chain_sets[i % args.rotate].run(streams, ev)
         torch.cuda.synchronize()
         if i >= 1 or args.warmup <= 1:
             times += np.array([a.elapsed_time(b) for a, b in ev])
-    symbols = [kernel_symbol(kind, name, w.D) for kind, name, _ in per_call]
+            counted += 1
+    symbols = [kernel_symbol(kind, name, w.H, w.D, sets) for kind, name, _ in per_call]
     sym_time = {}
-    for s, t in zip(symbols, times):
-        sym_time[s] = sym_time.get(s, 0.0) + t
+    for sy, t in zip(symbols, times):
+        sym_time[sy] = sym_time.get(sy, 0.0) + t
     dominant = max(sym_time, key=sym_time.get)
-    dom_idx = [i for i, s in enumerate(symbols) if s == dominant]
-    log("warmup per-call ms: " + ", ".join(f"{s}={t / max(args.warmup - 1, 1):.4f}" for s, t in zip(symbols, times)))
+    dom_idx = [i for i, sy in enumerate(symbols) if sy == dominant]
+    log("warmup per-call us: " + ", ".join(f"{sy}={t / counted * 1e3:.1f}" for sy, t in zip(symbols, times)))
 
-    # timed region: exactly `steps` steps; events only around the dominant kernel's launches
+    # timed region: exactly `steps` steps; events only around the dominant kernel's launches,
+    # recorded on the stream that launches it
     dom_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                if i in dom_idx else None for i in range(n_calls)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        chain_sets[k % args.rotate].run(sp, dom_ev[k])
+        chain_sets[k % args.rotate].run(streams, dom_ev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -213,8 +342,11 @@ def main():
     dom_bytes = float(np.mean([per_call[i][2] for i in dom_idx]))
     dom_avg_ms = float(np.mean(dom_ms))
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic(dominant)
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else int(traffic),
+                "traffic_unit": "bytes per launch", "launches_per_step": len(dom_idx),
                 "launch_avg_us": round(dom_avg_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(dom_bytes)}
 
     result = {
@@ -224,9 +356,11 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "config": {"workload": "long_prompt", "T": w.T, "H": w.H, "D": w.D, "loops": w.n_loops,
                    "budgets_pct": list(w.budgets), "tensors": "K+V", "step_bytes": int(step_bytes),
-                   "rotate_sets": args.rotate},
+                   "rotate_sets": args.rotate, "streams": args.streams},
         "roofline": roofline,
     }
+    if copy_gbs is not None:
+        result["copy_probe_gbs"] = round(copy_gbs, 1)
     if not args.no_cpu_baseline:
         log("timing the oracle on a head sample ...")
         result["cpu_baseline"] = cpu_baseline(w, host, sets)
