@@ -26,7 +26,8 @@
  *    explicit incompatible choices fail clearly).  No C++ exception crosses the ABI.
  *  - BF16 tensors are [rows, H, D] row-major with channels contiguous.  Element (r, h, c) is
  *    at index (r*H + h)*D + c.  BF16 data, codes and params must be 16-byte aligned, rows
- *    4-byte aligned.
+ *    4-byte aligned.  Every BF16 tensor a call describes stays below 4 GiB
+ *    (T*H*D < 2^31 elements); larger sizes are FLK_E_SHAPE.
  *  - Preconditions not checked on the host: `rows` arrays strictly ascending with values in
  *    [0, T); inputs finite.  Non-finite inputs, FP16 overflow of a group's minimum or scale
  *    and rows entries outside [0, T) are reported through the optional device status word

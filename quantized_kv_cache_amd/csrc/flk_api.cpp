@@ -26,9 +26,11 @@ size_t n_groups(const flk_desc* d, int64_t n) {
   return size_t(n) * size_t(d->n_heads) * size_t((d->head_dim + FLK_GROUP - 1) / FLK_GROUP);
 }
 
-// Largest element count a launch indexes; the kernels index in 64-bit, but flattened
-// (row, head) items are divided in 32-bit, so n*H must stay below 2^31.
-bool rows_fit(const flk_desc* d, int64_t n) { return n * int64_t(d->n_heads) < (int64_t(1) << 31); }
+// Every BF16 tensor of a call stays below 4 GiB (n*H*D < 2^31 elements): the kernels address
+// rows through buffer descriptors with 32-bit byte offsets.
+bool rows_fit(const flk_desc* d, int64_t n) {
+  return n * int64_t(d->n_heads) * int64_t(d->head_dim) < (int64_t(1) << 31);
+}
 
 flk_status to_status(hipError_t e) { return e == hipSuccess ? FLK_OK : FLK_E_LAUNCH; }
 

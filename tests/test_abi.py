@@ -71,6 +71,8 @@ def test_encode_base_validation():
     assert _encode_base(d, FAKE, 16, None, FAKE, FAKE) == 1
     assert _encode_base(d, FAKE, 16, FAKE, FAKE, None) == 1
     assert _encode_base(d, FAKE, 0, FAKE, FAKE, FAKE) == 2
+    big = flk.desc(flk.K, 16, 512)                      # T*H*D = 2^31 elements: a 4 GiB tensor
+    assert _encode_base(big, FAKE, 1 << 18, FAKE, FAKE, FAKE) == 2
     assert _encode_base(d, MIS, 16, FAKE, FAKE, FAKE) == 3
     assert _encode_base(d, FAKE, 16, FAKE, MIS, FAKE) == 3
     bad = flk.desc(flk.K, 2, 64)
