@@ -166,6 +166,62 @@ def cpu_baseline(w, host, sets, heads=(0, 1)):
                       f"C oracle on the host"}
 
 
+# ----------------------------------------------------------------------------- decode attention
+
+def attention_leg(reps=20):
+    """Time flk_decode_attn_packed, the chains' consumer, on the decode workload (T=131072,
+    8 KV heads, 32 query heads, D=128, chains at 100/100/50/25%), with the chains encoded by
+    the library from the seeded inputs.  Each timed call is preceded by a 512 MiB write so the
+    MALL holds none of the packed chains; the figure is the median of `reps` calls."""
+    w = synth.WORKLOADS[5]
+    T, H, D, Hq = w.T, w.H, w.D, w.Hq
+    sets = synth.active_sets(w, T)
+    chains, packed_bytes = {}, 0
+    for kind, tensor in ((flk.K, synth.K_TENSOR), (flk.V, synth.V_TENSOR)):
+        c = synth.make_chain(w, tensor, sets=sets)
+        recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+        packs = []
+        for l, (x, r) in enumerate(zip(c.xs, c.rows)):
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            rd = None if r is None else torch.from_numpy(r).cuda()
+            p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T)
+            if l == 0:
+                flk.encode_base(kind, xd, p, recon)
+            else:
+                flk.encode_residual(kind, xd, rd, recon, p)
+            packs.append(p)
+            packed_bytes += flk.codes_bytes(kind, H, D, p.n_rows) + flk.params_bytes(kind, H, D, p.n_rows)
+        chains[kind] = packs
+        del recon
+    packed_bytes += sum(4 * len(r) for r in sets if r is not None)      # one rows array per loop
+    q = torch.from_numpy(synth.make_query(w).view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(flk.attn_workspace_bytes(H, D, T, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    algo = packed_bytes + 2 * Hq * D * 2                                # + q read + out write
+    for _ in range(3):
+        flk.decode_attn_packed(q, chains[flk.K], chains[flk.V], T, H, scale, out, ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flk.decode_attn_packed(q, chains[flk.K], chains[flk.V], T, H, scale, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times))
+    rta = packed_bytes + 4 * 2 * T * H * D        # reconstruct K, V (write) then attend (read them)
+    return {"workload": "decode_attn", "T": T, "Hkv": H, "Hq": Hq, "D": D, "loops": w.n_loops,
+            "budgets_pct": list(w.budgets), "median_us": round(us, 2),
+            "p10_us": round(float(np.percentile(times, 10)), 2), "p90_us": round(float(np.percentile(times, 90)), 2),
+            "algorithmic_bytes": int(algo), "gbs": round(algo / us / 1e3, 1),
+            "hbm_frac": round(algo / us / 1e3 / HBM_PEAK_GBS, 4),
+            "reconstruct_then_attend_bytes": int(rta)}
+
+
 # ----------------------------------------------------------------------------- HBM traffic
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prompt.txt")
@@ -274,6 +330,7 @@ def main():
     ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
                     help="2: the K chain and the V chain on two streams; 1: both on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -361,6 +418,9 @@ def main():
     }
     if copy_gbs is not None:
         result["copy_probe_gbs"] = round(copy_gbs, 1)
+    if not args.no_attention:
+        log("decode attention over the packed chains ...")
+        result["decode_attention"] = attention_leg()
     if not args.no_cpu_baseline:
         log("timing the oracle on a head sample ...")
         result["cpu_baseline"] = cpu_baseline(w, host, sets)
