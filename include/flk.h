@@ -200,6 +200,60 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
                                   float softmax_scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Batched calls.  A serving step encodes or rebuilds many tensors at once -- every layer's K
+ * and V of a request, or of many requests -- and one kernel launch covering them avoids a
+ * launch (and a ramp-up and drain of the GPU) per tensor; the RFC, section 6.2, asks for the
+ * codec to join the runtime's batched submissions.  Each unit is one (request, layer, K or V)
+ * tensor; units are independent and may differ in T, n_rows and kind.  The results are
+ * exactly those of the single call applied to each unit.  No two units may write the same
+ * buffer, except that units whose rows arrays are equal may share one tile_start array.
+ * k_desc / v_desc describe every K / V unit (either may be NULL when no unit has that kind).
+ * The unit tables are host memory; every unit is validated on the host before anything is
+ * launched, so on an error nothing has been written.  n_units == 0 is a no-op.
+ * --------------------------------------------------------------------------------------- */
+
+/* One tensor of a batched encode; the pointers are device addresses as in the single calls. */
+typedef struct flk_unit {
+  const void* x;            /* BF16 [n_rows, H, D]: X[1] (base) or X[r] at the active rows    */
+  const int32_t* rows;      /* ascending positions of a compact loop, NULL for a dense one     */
+  void* recon;              /* BF16 [T, H, D]: written by a base, updated by a residual        */
+  uint8_t* codes;           /* output stream of this loop                                     */
+  uint32_t* params;
+  int32_t* tile_start;      /* output tile index of a compact loop, else NULL                 */
+  int32_t n_rows;           /* == T for a base or dense loop; 0 = an empty residual loop      */
+  int32_t T;
+  int32_t kind;             /* FLK_KIND_K or FLK_KIND_V                                       */
+  int32_t reserved;         /* must be 0                                                      */
+} flk_unit;
+
+/* flk_encode_base for every unit (rows must be NULL and n_rows == T).
+ * Errors: those of flk_encode_base for any unit, FLK_E_NULL for a NULL table or a missing
+ * descriptor, FLK_E_DESC for a bad kind or reserved field, FLK_E_SHAPE for n_units < 0.     */
+flk_status flk_encode_base_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_unit* units,
+                                 int32_t n_units, uint32_t* dev_status, void* stream);
+
+/* flk_encode_residual for every unit (dense and compact units may be mixed).
+ * Errors: those of flk_encode_residual for any unit, plus those of flk_encode_base_batch.   */
+flk_status flk_encode_residual_batch(const flk_desc* k_desc, const flk_desc* v_desc,
+                                     const flk_unit* units, int32_t n_units, uint32_t* dev_status,
+                                     void* stream);
+
+/* One tensor of a batched reconstruct. */
+typedef struct flk_recon_unit {
+  const flk_stream* chain;  /* host array of n_loops streams, chain[0] the dense base         */
+  void* out;                /* BF16 [T, H, D] output                                          */
+  int32_t T;
+  int32_t n_loops;
+  int32_t kind;             /* FLK_KIND_K or FLK_KIND_V                                       */
+  int32_t reserved;         /* must be 0                                                      */
+} flk_recon_unit;
+
+/* flk_reconstruct for every unit.
+ * Errors: those of flk_reconstruct for any unit, plus those of flk_encode_base_batch.       */
+flk_status flk_reconstruct_batch(const flk_desc* k_desc, const flk_desc* v_desc,
+                                 const flk_recon_unit* units, int32_t n_units, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

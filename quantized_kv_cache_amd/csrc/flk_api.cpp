@@ -6,7 +6,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
+#include <utility>
+#include <vector>
 
 #include "../../include/flk.h"
 #include "flk_internal.h"
@@ -208,6 +211,152 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
   return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc,
                                            softmax_scale, out, workspace,
                                            static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+const flk_desc* unit_desc(const flk_desc* kd, const flk_desc* vd, int32_t kind) {
+  return kind == FLK_KIND_K ? kd : kind == FLK_KIND_V ? vd : nullptr;
+}
+
+flk_status check_pair(const flk_desc* kd, const flk_desc* vd) {
+  if (kd) {
+    const flk_status st = flk_desc_check(kd);
+    if (st != FLK_OK) return st;
+    if (kd->kind != FLK_KIND_K) return FLK_E_DESC;
+  }
+  if (vd) {
+    const flk_status st = flk_desc_check(vd);
+    if (st != FLK_OK) return st;
+    if (vd->kind != FLK_KIND_V) return FLK_E_DESC;
+  }
+  return FLK_OK;
+}
+
+// The checks of flk_encode_base / flk_encode_residual for one unit; *skip marks an empty loop.
+flk_status check_encode_unit(const flk_desc* d, bool resid, const flk_unit& u, flk::EncArgs* a, bool* skip) {
+  *skip = false;
+  if (u.reserved != 0) return FLK_E_DESC;
+  if (!u.recon) return FLK_E_NULL;
+  if (u.T < 1 || u.n_rows < 0 || u.n_rows > u.T || !rows_fit(d, u.T)) return FLK_E_SHAPE;
+  if (!aligned(u.recon, 16)) return FLK_E_ALIGN;
+  if (!resid && (u.rows != nullptr || u.n_rows != u.T)) return FLK_E_SHAPE;
+  if (u.n_rows == 0) {
+    *skip = true;
+    return FLK_OK;
+  }
+  if (u.rows == nullptr && u.n_rows != u.T) return FLK_E_SHAPE;
+  if (!u.x) return FLK_E_NULL;
+  const flk_status st = check_stream_ptrs(u.codes, u.params);
+  if (st != FLK_OK) return st;
+  if (u.rows && !u.tile_start) return FLK_E_NULL;
+  if (!aligned(u.x, 16) || (u.rows && (!aligned(u.rows, 4) || !aligned(u.tile_start, 4)))) return FLK_E_ALIGN;
+  *a = flk::EncArgs{static_cast<const uint16_t*>(u.x), u.rows, static_cast<uint16_t*>(u.recon), u.codes, u.params,
+                    u.rows ? u.tile_start : nullptr, nullptr, u.n_rows, u.T, d->n_heads * d->head_dim};
+  return FLK_OK;
+}
+
+flk_status encode_batch(bool resid, const flk_desc* kd, const flk_desc* vd, const flk_unit* units, int32_t n_units,
+                        uint32_t* dev_status, void* stream) {
+  if (n_units < 0) return FLK_E_SHAPE;
+  if (n_units == 0) return FLK_OK;
+  if (!units) return FLK_E_NULL;
+  flk_status st = check_pair(kd, vd);
+  if (st != FLK_OK) return st;
+  if (dev_status && !aligned(dev_status, 4)) return FLK_E_ALIGN;
+  std::vector<flk::EncArgs> batch[2];       // [0] dense (or base), [1] compact
+  std::vector<int> kinds[2];
+  std::vector<std::pair<int, flk::EncArgs>> singles;
+  for (int32_t i = 0; i < n_units; ++i) {
+    const flk_unit& u = units[i];
+    const flk_desc* d = unit_desc(kd, vd, u.kind);
+    if (u.kind != FLK_KIND_K && u.kind != FLK_KIND_V) return FLK_E_DESC;
+    if (!d) return FLK_E_NULL;
+    flk::EncArgs a;
+    bool skip;
+    st = check_encode_unit(d, resid, u, &a, &skip);
+    if (st != FLK_OK) return st;
+    if (skip) continue;
+    a.status = dev_status;
+    if (flk::encode_batchable(u.kind, d->n_heads, d->head_dim)) {
+      batch[u.rows ? 1 : 0].push_back(a);
+      kinds[u.rows ? 1 : 0].push_back(u.kind);
+    } else {
+      singles.emplace_back(i, a);
+    }
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int g = 0; g < 2; ++g) {
+    if (batch[g].empty()) continue;
+    const hipError_t e = flk::launch_encode_batch(resid, g == 1, batch[g].data(), kinds[g].data(),
+                                                  int(batch[g].size()), s);
+    if (e != hipSuccess) return FLK_E_LAUNCH;
+  }
+  for (const auto& [i, a] : singles) {
+    const flk_desc* d = unit_desc(kd, vd, units[i].kind);
+    const hipError_t e = flk::launch_encode(units[i].kind, resid, a.x, a.rows, a.n, a.T, d->n_heads, d->head_dim,
+                                            a.recon, a.codes, a.params, a.tile_start, a.status, s);
+    if (e != hipSuccess) return FLK_E_LAUNCH;
+  }
+  return FLK_OK;
+}
+
+uint32_t pattern_key(const flk::ChainArgs& c) {
+  uint32_t m = uint32_t(c.n_loops) << 16;
+  for (int l = 0; l < c.n_loops; ++l) m |= (c.s[l].rows ? 1u : 0u) << l;
+  return m;
+}
+
+}  // namespace
+
+flk_status flk_encode_base_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_unit* units,
+                                 int32_t n_units, uint32_t* dev_status, void* stream) {
+  return encode_batch(false, k_desc, v_desc, units, n_units, dev_status, stream);
+}
+
+flk_status flk_encode_residual_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_unit* units,
+                                     int32_t n_units, uint32_t* dev_status, void* stream) {
+  return encode_batch(true, k_desc, v_desc, units, n_units, dev_status, stream);
+}
+
+flk_status flk_reconstruct_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_recon_unit* units,
+                                 int32_t n_units, void* stream) {
+  if (n_units < 0) return FLK_E_SHAPE;
+  if (n_units == 0) return FLK_OK;
+  if (!units) return FLK_E_NULL;
+  flk_status st = check_pair(k_desc, v_desc);
+  if (st != FLK_OK) return st;
+  std::vector<flk::RecArgs> batch;
+  std::vector<flk::RecArgs> singles;
+  for (int32_t i = 0; i < n_units; ++i) {
+    const flk_recon_unit& u = units[i];
+    if (u.kind != FLK_KIND_K && u.kind != FLK_KIND_V) return FLK_E_DESC;
+    if (u.reserved != 0) return FLK_E_DESC;
+    const flk_desc* d = unit_desc(k_desc, v_desc, u.kind);
+    if (!d) return FLK_E_NULL;
+    if (!u.out) return FLK_E_NULL;
+    if (u.T < 1 || !rows_fit(d, u.T)) return FLK_E_SHAPE;
+    flk::RecArgs a;
+    st = load_chain(d, u.T, u.chain, u.n_loops, &a.chain);
+    if (st != FLK_OK) return st;
+    if (!aligned(u.out, 16)) return FLK_E_ALIGN;
+    a.out = u.out;
+    a.T = u.T;
+    a.H = d->n_heads;
+    a.D = d->head_dim;
+    a.kind = u.kind;
+    (flk::reconstruct_batchable(a.H, a.D) ? batch : singles).push_back(a);
+  }
+  // units with the same loop count and compact pattern share launches
+  std::stable_sort(batch.begin(), batch.end(), [](const flk::RecArgs& a, const flk::RecArgs& b) {
+    return pattern_key(a.chain) < pattern_key(b.chain);
+  });
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!batch.empty() && flk::launch_reconstruct_batch(batch.data(), int(batch.size()), s) != hipSuccess)
+    return FLK_E_LAUNCH;
+  for (const auto& a : singles)
+    if (flk::launch_reconstruct(a.kind, a.T, a.H, a.D, a.chain, a.out, s) != hipSuccess) return FLK_E_LAUNCH;
+  return FLK_OK;
 }
 
 }  // extern "C"

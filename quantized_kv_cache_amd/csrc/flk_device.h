@@ -243,6 +243,24 @@ __device__ __forceinline__ void buf_st64(uint32_t lo, uint32_t hi, BufRsrc r, ui
   __builtin_amdgcn_raw_buffer_store_b64(v, r, int(voff), soffset(soff), AUX);
 }
 
+// ---- XCD-aware block order --------------------------------------------------------------
+// The dispatcher hands consecutive workgroups of a launch to the 8 XCDs in turn, and each XCD
+// has its own L2.  Renumbering so that XCD x runs a contiguous range of logical blocks, in
+// order, keeps neighbouring blocks (which share parameter rows) on one L2.  Returns the
+// logical (x, y) of this block in a 2-D grid; blocks past the largest multiple of 8 keep
+// their own index.  Correct for any mapping; only the locality assumes 8 XCDs.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t n) {
+  const uint32_t per = n / kXcds;
+  return lin < per * kXcds ? (lin % kXcds) * per + lin / kXcds : lin;
+}
+__device__ __forceinline__ void xcd_block(uint32_t& bx, uint32_t& by) {
+  const uint32_t gx = gridDim.x;
+  const uint32_t lin = xcd_remap(blockIdx.x + blockIdx.y * gx, gx * gridDim.y);
+  by = lin / gx;
+  bx = lin - by * gx;
+}
+
 // ---- quad-lane exchanges through DPP (no LDS traffic) ----------------------------------------
 __device__ __forceinline__ float dpp_xor1(float v) {   // quad_perm [1,0,3,2]
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));

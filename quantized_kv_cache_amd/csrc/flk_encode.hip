@@ -43,10 +43,15 @@ __device__ __forceinline__ uint4 pack8(const float v[8]) {
 // across the 4 waves through LDS; one thread per channel then derives the params.
 // ---------------------------------------------------------------------------------------
 template <bool RESID, bool SPARSE>
-__global__ __launch_bounds__(kThreads) void encode_k_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
-    int32_t W, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes, uint32_t* __restrict__ params,
-    int32_t* __restrict__ tile_start, uint32_t* __restrict__ status) {
+__device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t bx, uint32_t by) {
+  const uint16_t* __restrict__ x = a.x;
+  const int32_t* __restrict__ rows = a.rows;
+  uint16_t* __restrict__ recon = a.recon;
+  uint8_t* __restrict__ codes = a.codes;
+  uint32_t* __restrict__ params = a.params;
+  int32_t* __restrict__ tile_start = a.tile_start;
+  uint32_t* __restrict__ status = a.status;
+  const int32_t n = a.n, T = a.T, W = a.W;
   __shared__ float s_min[4][128];
   __shared__ float s_max[4][128];
   __shared__ float s_m[128], s_s[128], s_rs[128];
@@ -56,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
   const int rs = tid >> 4;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int band = blockIdx.x;
-  const int chunk = blockIdx.y * 16 + cc;
+  const int band = int(bx);
+  const int chunk = int(by) * 16 + cc;
   const bool cact = chunk < (W >> 3);
   const int64_t ch = int64_t(chunk) * 8;
 
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
     unpack8(xv, v[i]);
   }
   if (SPARSE && bad_row && status) atomicOr(status, kDevRows);
-  if (SPARSE && blockIdx.y == 0 && cc == 0) {
+  if (SPARSE && by == 0 && cc == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = band * kGroup + rs + 16 * i;
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
   if (tid < 128) {
     const float a = tmin(tmin(s_min[0][tid], s_min[1][tid]), tmin(s_min[2][tid], s_min[3][tid]));
     const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
-    const int64_t chan = int64_t(blockIdx.y) * 128 + tid;
+    const int64_t chan = int64_t(by) * 128 + tid;
     GroupParams p = make_params(a, b);
     s_m[tid] = p.m;
     s_s[tid] = p.s;
@@ -166,6 +171,11 @@ __global__ __launch_bounds__(kThreads) void encode_k_kernel(
     st_stream32(codes + ((int64_t(j) * W + ch) >> 1), pack_codes8(k));
     *reinterpret_cast<uint4*>(recon + roff[i]) = pack8(out);
   }
+}
+
+template <bool RESID, bool SPARSE>
+__global__ __launch_bounds__(kThreads) void encode_k_kernel(EncArgs a) {
+  encode_k_body<RESID, SPARSE>(a, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -277,17 +287,23 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
 // row's loads are issued before the current row is processed.
 // ---------------------------------------------------------------------------------------
 template <bool RESID, bool SPARSE>
-__global__ __launch_bounds__(kThreads) void encode_v_wide_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
-    int32_t W, int32_t rows_per_wave, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes,
-    uint32_t* __restrict__ params, int32_t* __restrict__ tile_start, uint32_t* __restrict__ status) {
+__device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t rows_per_wave, uint32_t bx,
+                                                   uint32_t by) {
+  const uint16_t* __restrict__ x = a.x;
+  const int32_t* __restrict__ rows = a.rows;
+  uint16_t* __restrict__ recon = a.recon;
+  uint8_t* __restrict__ codes = a.codes;
+  uint32_t* __restrict__ params = a.params;
+  int32_t* __restrict__ tile_start = a.tile_start;
+  uint32_t* __restrict__ status = a.status;
+  const int32_t n = a.n, T = a.T, W = a.W;
   constexpr int kCh = 16;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  const int32_t j0 = (int32_t(blockIdx.x) * (kThreads / 64) + wave) * rows_per_wave;
+  const int32_t j0 = (int32_t(bx) * (kThreads / 64) + wave) * rows_per_wave;
   if (j0 >= n) return;
   const int32_t j1 = min(j0 + rows_per_wave, n);
-  const uint32_t ch = uint32_t(blockIdx.y) * 1024u + uint32_t(lane) * kCh;
+  const uint32_t ch = by * 1024u + uint32_t(lane) * kCh;
   const uint32_t xrow = uint32_t(W) * 2u, crow = uint32_t(W) / 2u, prow = uint32_t(W) / 16u;
   const BufRsrc xrs = make_buf(x, uint32_t(n) * xrow);
   const BufRsrc rrs = make_buf(recon, uint32_t(T) * xrow);
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void encode_v_wide_kernel(
   uint32_t err = 0;
   auto process = [&](int32_t j, auto B) {
     constexpr int b = decltype(B)::value;
-    if (SPARSE && lane == 0 && blockIdx.y == 0) write_tile_index(rows, n, T, j, tile_start);
+    if (SPARSE && lane == 0 && by == 0) write_tile_index(rows, n, T, j, tile_start);
     const int32_t p = pos[b];
     if (SPARSE && p < 0) { err |= kDevRows; return; }
     float v[kCh], r[kCh];
@@ -363,19 +379,32 @@ __global__ __launch_bounds__(kThreads) void encode_v_wide_kernel(
 }
 
 template <bool RESID, bool SPARSE>
-static hipError_t launch_v_wide(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t W,
-                                void* recon, uint8_t* codes, uint32_t* params, int32_t* tile_start,
-                                uint32_t* status, hipStream_t stream) {
-  const int32_t strips = W / 1024;
-  // about kVWideWaves waves per launch: many short waves (one or two rows each) keep the
-  // most loads in flight and let the wave scheduler hide their latency
-  const int64_t per_wave = (int64_t(n) * strips + kVWideWaves - 1) / kVWideWaves;
-  const int32_t rpw = int32_t(per_wave < 1 ? 1 : per_wave);
+__global__ __launch_bounds__(kThreads) void encode_v_wide_kernel(EncArgs a, int32_t rows_per_wave) {
+  encode_v_wide_body<RESID, SPARSE>(a, rows_per_wave, blockIdx.x, blockIdx.y);
+}
+
+static bool v_wide_ok(int32_t H, int32_t D) { return D % 64 == 0 && (H * D) % 1024 == 0; }
+
+// Rows per wave of the wide V encoder: about kVWideWaves waves per launch -- many short waves
+// (one or two rows each) keep the most loads in flight and let the wave scheduler hide their
+// latency.
+static int32_t v_wide_rpw(int32_t n, int32_t W) {
+  const int64_t per_wave = (int64_t(n) * (W / 1024) + kVWideWaves - 1) / kVWideWaves;
+  return int32_t(per_wave < 1 ? 1 : per_wave);
+}
+static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) {
   const int32_t waves = (n + rpw - 1) / rpw;
-  const dim3 grid(unsigned((waves + 3) / 4), unsigned(strips));
-  hipLaunchKernelGGL((encode_v_wide_kernel<RESID, SPARSE>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), rows, n, T, W, rpw,
-                     static_cast<uint16_t*>(recon), codes, params, tile_start, status);
+  return dim3(unsigned((waves + 3) / 4), unsigned(W / 1024));
+}
+static dim3 k_grid(int32_t n, int32_t W) {
+  return dim3(unsigned((n + kGroup - 1) / kGroup), unsigned((W / 8 + 15) / 16));
+}
+
+template <bool RESID, bool SPARSE>
+static hipError_t launch_v_wide(const EncArgs& a, hipStream_t stream) {
+  const int32_t rpw = v_wide_rpw(a.n, a.W);
+  hipLaunchKernelGGL((encode_v_wide_kernel<RESID, SPARSE>), v_wide_grid(a.n, a.W, rpw), dim3(kThreads), 0,
+                     stream, a, rpw);
   return hipGetLastError();
 }
 
@@ -404,14 +433,8 @@ static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_
 }
 
 template <bool RESID, bool SPARSE>
-static hipError_t launch_k(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t W, void* recon,
-                           uint8_t* codes, uint32_t* params, int32_t* tile_start, uint32_t* status,
-                           hipStream_t stream) {
-  const int cpr = W / 8;
-  const dim3 grid(unsigned((n + kGroup - 1) / kGroup), unsigned((cpr + 15) / 16));
-  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), rows, n, T, W, static_cast<uint16_t*>(recon),
-                     codes, params, tile_start, status);
+static hipError_t launch_k(const EncArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a.n, a.W), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -421,21 +444,92 @@ hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* row
                          hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const bool sparse = rows != nullptr;
+  const EncArgs a{static_cast<const uint16_t*>(x), rows, static_cast<uint16_t*>(recon), codes, params,
+                  tile_start, status, n, T, H * D};
   if (kind == FLK_KIND_K) {
-    const int32_t W = H * D;
-    if (!resid) return launch_k<false, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
-    if (!sparse) return launch_k<true, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
-    return launch_k<true, true>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+    if (!resid) return launch_k<false, false>(a, stream);
+    if (!sparse) return launch_k<true, false>(a, stream);
+    return launch_k<true, true>(a, stream);
   }
-  if (D % 64 == 0 && (H * D) % 1024 == 0) {
-    const int32_t W = H * D;
-    if (!resid) return launch_v_wide<false, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
-    if (!sparse) return launch_v_wide<true, false>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
-    return launch_v_wide<true, true>(x, rows, n, T, W, recon, codes, params, tile_start, status, stream);
+  if (v_wide_ok(H, D)) {
+    if (!resid) return launch_v_wide<false, false>(a, stream);
+    if (!sparse) return launch_v_wide<true, false>(a, stream);
+    return launch_v_wide<true, true>(a, stream);
   }
   if (!resid) return launch_v<false, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
   if (!sparse) return launch_v<true, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
   return launch_v<true, true>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// Batched encode: one launch runs the same loop type (base, dense residual or compact
+// residual) for up to kEncBatch tensors, K and V mixed.  Blocks are numbered unit after unit;
+// a block finds its unit with a scan of the (scalar) block offsets and runs that kind's body.
+// V tensors take the wide body only, so a V unit needs D % 64 == 0 and H*D % 1024 == 0.
+// ---------------------------------------------------------------------------------------
+struct EncUnit {
+  EncArgs a;
+  int32_t kind;
+  uint32_t gx;        // blocks along the unit's first grid axis
+  int32_t rpw;        // V: rows per wave
+  uint32_t block0;    // first block of the unit in the launch
+};
+struct EncBatch {
+  EncUnit u[kEncBatch];
+  int32_t n_units;
+};
+
+static_assert(sizeof(EncBatch) <= 4096, "a batch travels as kernel arguments (4 KiB at most)");
+
+template <bool RESID, bool SPARSE>
+__global__ __launch_bounds__(kThreads) void encode_batch_kernel(EncBatch b) {
+  const uint32_t bid = blockIdx.x;
+  int ui = 0;
+#pragma unroll
+  for (int i = 1; i < kEncBatch; ++i)
+    if (i < b.n_units && bid >= b.u[i].block0) ui = i;
+  const EncUnit& u = b.u[ui];
+  const uint32_t lb = bid - u.block0;
+  const uint32_t by = lb / u.gx, bx = lb - by * u.gx;
+  if (u.kind == FLK_KIND_K) encode_k_body<RESID, SPARSE>(u.a, bx, by);
+  else encode_v_wide_body<RESID, SPARSE>(u.a, u.rpw, bx, by);
+}
+
+bool encode_batchable(int kind, int32_t H, int32_t D) { return kind == FLK_KIND_K || v_wide_ok(H, D); }
+
+hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, const int* kinds, int n_units,
+                               hipStream_t stream) {
+  for (int u0 = 0; u0 < n_units; u0 += kEncBatch) {
+    EncBatch b{};
+    uint32_t blocks = 0;
+    for (int i = u0; i < n_units && i < u0 + kEncBatch; ++i) {
+      if (args[i].n <= 0) continue;
+      EncUnit& e = b.u[b.n_units++];
+      e.a = args[i];
+      e.kind = kinds[i];
+      dim3 g;
+      if (kinds[i] == FLK_KIND_K) {
+        g = k_grid(args[i].n, args[i].W);
+        e.rpw = 0;
+      } else {
+        e.rpw = v_wide_rpw(args[i].n, args[i].W);
+        g = v_wide_grid(args[i].n, args[i].W, e.rpw);
+      }
+      e.gx = g.x;
+      e.block0 = blocks;
+      blocks += g.x * g.y;
+    }
+    if (blocks == 0) continue;
+    if (!resid)
+      hipLaunchKernelGGL((encode_batch_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
+    else if (!sparse)
+      hipLaunchKernelGGL((encode_batch_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
+    else
+      hipLaunchKernelGGL((encode_batch_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, stream, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace flk

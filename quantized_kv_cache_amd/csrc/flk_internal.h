@@ -23,14 +23,53 @@ struct ChainArgs {
   int32_t n_loops;
 };
 
+// One encode of one tensor as a kernel sees it (single and batched calls alike).
+struct EncArgs {
+  const uint16_t* x;       // input rows [n][H][D]
+  const int32_t* rows;     // compact positions (compact loops only)
+  uint16_t* recon;         // X_hat [T][H][D]
+  uint8_t* codes;
+  uint32_t* params;
+  int32_t* tile_start;     // compact loops only
+  uint32_t* status;        // optional device status word
+  int32_t n, T, W;         // rows, positions, channels per row (H*D)
+};
+
+// Largest number of tensors one batched launch covers.
+constexpr int kEncBatch = 16;
+
 // Encode one loop (base when resid == false).  Returns a hipError_t.
 hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* rows, int32_t n,
                          int32_t T, int32_t H, int32_t D, void* recon, uint8_t* codes,
                          uint32_t* params, int32_t* tile_start, uint32_t* status,
                          hipStream_t stream);
 
+// Whether a tensor of this kind and shape can join a batched encode launch; the others are
+// encoded one launch each.
+bool encode_batchable(int kind, int32_t H, int32_t D);
+
+// The same loop type for n_units tensors, K and V mixed (kinds[i]), in launches of up to
+// kEncBatch tensors.  Every tensor must be encode_batchable.
+hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, const int* kinds, int n_units,
+                               hipStream_t stream);
+
 hipError_t launch_reconstruct(int kind, int32_t T, int32_t H, int32_t D, const ChainArgs& chain,
                               void* out, hipStream_t stream);
+
+// One reconstruct of a batched call.
+struct RecArgs {
+  ChainArgs chain;
+  void* out;
+  int32_t T, H, D, kind;
+};
+constexpr int kRecBatch = 8;
+
+// Whether a tensor of this shape can join a batched reconstruct launch.
+bool reconstruct_batchable(int32_t H, int32_t D);
+
+// Rebuild n_units tensors (all reconstruct_batchable), K and V mixed: each run of consecutive
+// units whose chains share loop count and compact pattern goes in launches of up to kRecBatch.
+hipError_t launch_reconstruct_batch(const RecArgs* units, int n_units, hipStream_t stream);
 
 size_t attn_workspace_bytes(int32_t T, int32_t H, int32_t Hq);
 

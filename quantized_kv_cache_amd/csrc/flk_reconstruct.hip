@@ -171,9 +171,8 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_kernel(ChainArgs chain,
 // SPARSE has bit l set when loop l is compact; with RT the pattern is read from the chain at
 // run time instead (chains longer than 4 loops).
 template <int KIND, int NL, uint32_t SPARSE, bool RT>
-__global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs chain, int32_t T,
-                                                                      int32_t H, int32_t D,
-                                                                      uint16_t* __restrict__ out) {
+__device__ __forceinline__ void reconstruct_wide_body(const ChainArgs& chain, int32_t T, int32_t H, int32_t D,
+                                                      uint16_t* __restrict__ out, uint32_t bx, uint32_t by) {
   constexpr int kTokPerWave = kWideTokPerWave;
   __shared__ int32_t s_map[kRThreads / 64][NL][kTokPerWave];
   auto is_sparse = [&](int l) -> bool {
@@ -184,9 +183,9 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs c
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int32_t W = H * D;
-  const int32_t chunk = int32_t(blockIdx.y) * 64 + lane;
+  const int32_t chunk = int32_t(by) * 64 + lane;
   const int32_t ch = chunk * 8;
-  const int32_t tw = int32_t(blockIdx.x) * (kTokPerWave * (kRThreads / 64)) + wave * kTokPerWave;
+  const int32_t tw = int32_t(bx) * (kTokPerWave * (kRThreads / 64)) + wave * kTokPerWave;
   if (tw >= T) return;                                   // wave-uniform, no barrier follows
 
   // ---- this wave's position -> compact row table (wave-private; no block barrier) ----
@@ -322,6 +321,14 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs c
   }
 }
 
+template <int KIND, int NL, uint32_t SPARSE, bool RT>
+__global__ __launch_bounds__(kRThreads) void reconstruct_wide_kernel(ChainArgs chain, int32_t T, int32_t H,
+                                                                      int32_t D, uint16_t* __restrict__ out) {
+  uint32_t bx, by;
+  xcd_block(bx, by);                                     // the 4 blocks of a tile share K params
+  reconstruct_wide_body<KIND, NL, SPARSE, RT>(chain, T, H, D, out, bx, by);
+}
+
 template <int KIND>
 static void launch_kind(dim3 grid, const ChainArgs& chain, int32_t T, int32_t H, int32_t D,
                         int32_t lpt_log2, uint16_t* out, hipStream_t stream) {
@@ -376,6 +383,98 @@ hipError_t launch_reconstruct(int kind, int32_t T, int32_t H, int32_t D, const C
   if (kind == FLK_KIND_K) launch_kind<FLK_KIND_K>(grid, chain, T, H, D, lpt_log2, o, stream);
   else launch_kind<FLK_KIND_V>(grid, chain, T, H, D, lpt_log2, o, stream);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Batched reconstruct: one launch rebuilds up to kRecBatch tensors (K and V mixed) whose chains
+// share the loop count and compact pattern, all with rows of at least 512 channels.  Blocks are
+// numbered unit after unit (in XCD order, as above) and each runs its unit's kind of body.
+// ---------------------------------------------------------------------------------------
+struct RecUnit {
+  ChainArgs c;
+  uint16_t* out;
+  int32_t T, H, D, kind;
+  uint32_t gx, block0;
+};
+struct RecBatch {
+  RecUnit u[kRecBatch];
+  int32_t n_units;
+};
+
+static_assert(sizeof(RecBatch) <= 4096, "a batch travels as kernel arguments (4 KiB at most)");
+
+template <int NL, uint32_t SPARSE, bool RT>
+__global__ __launch_bounds__(kRThreads) void reconstruct_batch_kernel(RecBatch b) {
+  const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  int ui = 0;
+#pragma unroll
+  for (int i = 1; i < kRecBatch; ++i)
+    if (i < b.n_units && lin >= b.u[i].block0) ui = i;
+  const RecUnit& u = b.u[ui];
+  const uint32_t lb = lin - u.block0;
+  const uint32_t by = lb / u.gx, bx = lb - by * u.gx;
+  if (u.kind == FLK_KIND_K) reconstruct_wide_body<FLK_KIND_K, NL, SPARSE, RT>(u.c, u.T, u.H, u.D, u.out, bx, by);
+  else reconstruct_wide_body<FLK_KIND_V, NL, SPARSE, RT>(u.c, u.T, u.H, u.D, u.out, bx, by);
+}
+
+static uint32_t chain_mask(const ChainArgs& c) {
+  uint32_t m = 0;
+  for (int l = 0; l < c.n_loops; ++l) m |= (c.s[l].rows != nullptr ? 1u : 0u) << l;
+  return m;
+}
+
+bool reconstruct_batchable(int32_t H, int32_t D) { return H * D >= 512; }
+
+static hipError_t launch_rec_batch(const RecBatch& b, uint32_t blocks, int nl, uint32_t mask, hipStream_t stream) {
+#define FLK_RB(NLV, M)                                                                                 \
+  if (nl == NLV && mask == M) {                                                                        \
+    hipLaunchKernelGGL((reconstruct_batch_kernel<NLV, M, false>), dim3(blocks), dim3(kRThreads), 0, stream, b); \
+    return hipGetLastError();                                                                          \
+  }
+  FLK_RB(1, 0)
+  FLK_RB(2, 0) FLK_RB(2, 2)
+  FLK_RB(3, 0) FLK_RB(3, 2) FLK_RB(3, 4) FLK_RB(3, 6)
+  FLK_RB(4, 0) FLK_RB(4, 2) FLK_RB(4, 4) FLK_RB(4, 6) FLK_RB(4, 8) FLK_RB(4, 10) FLK_RB(4, 12) FLK_RB(4, 14)
+#undef FLK_RB
+#define FLK_RB(NLV)                                                                                    \
+  case NLV:                                                                                            \
+    hipLaunchKernelGGL((reconstruct_batch_kernel<NLV, 0, true>), dim3(blocks), dim3(kRThreads), 0, stream, b); \
+    return hipGetLastError();
+  switch (nl) {
+    FLK_RB(5) FLK_RB(6) FLK_RB(7) FLK_RB(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef FLK_RB
+}
+
+hipError_t launch_reconstruct_batch(const RecArgs* units, int n_units, hipStream_t stream) {
+  constexpr int kTokPerBlock = kWideTokPerWave * (kRThreads / 64);
+  int i = 0;
+  while (i < n_units) {
+    // a run of units with the same loop count and compact pattern, at most kRecBatch long
+    const int nl = units[i].chain.n_loops;
+    const uint32_t mask = chain_mask(units[i].chain);
+    RecBatch b{};
+    uint32_t blocks = 0;
+    while (i < n_units && b.n_units < kRecBatch && units[i].chain.n_loops == nl &&
+           chain_mask(units[i].chain) == mask) {
+      const RecArgs& a = units[i];
+      RecUnit& r = b.u[b.n_units++];
+      r.c = a.chain;
+      r.out = static_cast<uint16_t*>(a.out);
+      r.T = a.T;
+      r.H = a.H;
+      r.D = a.D;
+      r.kind = a.kind;
+      r.gx = uint32_t((a.T + kTokPerBlock - 1) / kTokPerBlock);
+      r.block0 = blocks;
+      blocks += r.gx * uint32_t((a.H * a.D / 8 + 63) / 64);
+      ++i;
+    }
+    const hipError_t e = launch_rec_batch(b, blocks, nl, mask, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace flk

@@ -45,6 +45,18 @@ class StreamC(ctypes.Structure):
                 ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p), ("tile_start", ctypes.c_void_p)]
 
 
+class UnitC(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_void_p), ("recon", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p), ("tile_start", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int32), ("T", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ReconUnitC(ctypes.Structure):
+    _fields_ = [("chain", ctypes.POINTER(StreamC)), ("out", ctypes.c_void_p), ("T", ctypes.c_int32),
+                ("n_loops", ctypes.c_int32), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -82,6 +94,13 @@ def lib() -> ctypes.CDLL:
         L.flk_encode_residual.argtypes = [D, P, P, i32, i32, P, P, P, P, P, P]
         L.flk_reconstruct.restype = ctypes.c_int
         L.flk_reconstruct.argtypes = [D, i32, S, i32, P, P]
+        U = ctypes.POINTER(UnitC)
+        for name in ("flk_encode_base_batch", "flk_encode_residual_batch"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [D, D, U, i32, P, P]
+        L.flk_reconstruct_batch.restype = ctypes.c_int
+        L.flk_reconstruct_batch.argtypes = [D, D, ctypes.POINTER(ReconUnitC), i32, P]
         L.flk_decode_attn_packed.restype = ctypes.c_int
         L.flk_decode_attn_packed.argtypes = [D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P, sz, P]
         _lib = L
@@ -220,3 +239,49 @@ def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequ
                                         Hq, ka, va, len(k_chain), float(softmax_scale), _ptr(out),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)), "flk_decode_attn_packed")
+
+
+# ----------------------------------------------------------------------------- batched calls
+
+def _unit(kind: int, x: Optional[torch.Tensor], rows: Optional[torch.Tensor], recon: torch.Tensor,
+          out: "Packed") -> UnitC:
+    if x is not None:
+        _need(x, torch.bfloat16, "x")
+    _need(recon, torch.bfloat16, "recon")
+    if rows is not None:
+        _need(rows, torch.int32, "rows")
+    n = out.n_rows
+    return UnitC(None if x is None else x.data_ptr(), None if rows is None else rows.data_ptr(), recon.data_ptr(),
+                 out.codes.data_ptr(), out.params.data_ptr(),
+                 None if out.tile_start is None else out.tile_start.data_ptr(), n, recon.shape[0], kind, 0)
+
+
+def encode_base_batch(items, H: int, D: int, status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """items: (kind, x [T, H, D], recon [T, H, D], out Packed) per tensor; one call for all."""
+    units = [_unit(kind, x, None, recon, out) for kind, x, recon, out in items]
+    arr = (UnitC * max(1, len(units)))(*units)
+    _check(lib().flk_encode_base_batch(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), arr, len(units),
+                                       _ptr(status), _stream(stream)), "flk_encode_base_batch")
+
+
+def encode_residual_batch(items, H: int, D: int, status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """items: (kind, x_rows [n, H, D], rows or None, recon [T, H, D], out Packed) per tensor."""
+    units = [_unit(kind, x, rows, recon, out) for kind, x, rows, recon, out in items]
+    arr = (UnitC * max(1, len(units)))(*units)
+    _check(lib().flk_encode_residual_batch(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), arr,
+                                           len(units), _ptr(status), _stream(stream)), "flk_encode_residual_batch")
+
+
+def reconstruct_batch(items, H: int, D: int, stream=None) -> None:
+    """items: (kind, chain [Packed, ...], out [T, H, D]) per tensor."""
+    keep, units = [], []
+    for kind, chain, out in items:
+        _need(out, torch.bfloat16, "out")
+        arr = _chain(chain)
+        keep.append(arr)
+        units.append(ReconUnitC(ctypes.cast(arr, ctypes.POINTER(StreamC)), out.data_ptr(), out.shape[0], len(chain),
+                                kind, 0))
+    tab = (ReconUnitC * max(1, len(units)))(*units)
+    _check(lib().flk_reconstruct_batch(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), tab, len(units),
+                                       _stream(stream)), "flk_reconstruct_batch")
+

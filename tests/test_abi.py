@@ -149,3 +149,53 @@ def test_status_strings():
     L = flk.lib()
     for s in range(8):
         assert L.flk_status_string(s)
+
+
+def test_batch_validation():
+    L = flk.lib()
+    kd, vd = flk.desc(flk.K, 2, 64), flk.desc(flk.V, 2, 64)
+    U = flk.UnitC
+
+    def unit(kind=flk.K, x=FAKE.value, rows=None, recon=FAKE.value, n=16, T=16, tile=None, reserved=0):
+        return U(x, rows, recon, FAKE.value, FAKE.value, tile, n, T, kind, reserved)
+
+    def base(units, k=kd, v=vd, n=None):
+        arr = (U * max(1, len(units)))(*units) if units else None
+        return L.flk_encode_base_batch(ctypes.byref(k) if k else None, ctypes.byref(v) if v else None, arr,
+                                       len(units) if n is None else n, None, None)
+
+    def resid(units, k=kd, v=vd):
+        arr = (U * len(units))(*units)
+        return L.flk_encode_residual_batch(ctypes.byref(k), ctypes.byref(v), arr, len(units), None, None)
+    assert base([]) == 0                                     # nothing to do
+    assert base([], n=-1) == 2
+    assert base([], n=3) == 1                                # NULL table
+    assert base([unit(kind=2)]) == 4
+    assert base([unit(reserved=1)]) == 4
+    assert base([unit(kind=flk.V)], v=None) == 1             # no descriptor for a V unit
+    assert base([unit()], k=vd) == 4                         # k_desc must describe K
+    assert base([unit(rows=FAKE.value, tile=FAKE.value)]) == 2   # a base is dense
+    assert base([unit(n=8)]) == 2
+    # a valid unit followed by a bad one: validation fails before anything is launched
+    assert base([unit(), unit(kind=flk.V, x=MIS.value)]) == 3
+    assert base([unit(), unit(kind=flk.V, recon=None)]) == 1
+    assert resid([unit(rows=FAKE.value, n=4, tile=None)]) == 1   # compact needs its tile index
+    assert resid([unit(rows=None, n=4)]) == 2                    # dense needs n == T
+    assert resid([unit(n=17)]) == 2
+    big = flk.desc(flk.K, 16, 512)
+    assert base([unit(n=1 << 18, T=1 << 18)], k=big) == 2    # a 4 GiB tensor
+
+    R = flk.ReconUnitC
+    chain = (flk.StreamC * 1)(flk.StreamC(64, 0, None, FAKE.value, FAKE.value, None))
+
+    def rec(units, k=kd, v=vd):
+        arr = (R * len(units))(*units)
+        return L.flk_reconstruct_batch(ctypes.byref(k), ctypes.byref(v), arr, len(units), None)
+    good = ctypes.cast(chain, ctypes.POINTER(flk.StreamC))
+    assert rec([R(None, FAKE.value, 64, 1, flk.K, 0)]) == 1
+    assert rec([R(good, FAKE.value, 64, 0, flk.K, 0)]) == 2
+    assert rec([R(good, MIS.value, 64, 1, flk.V, 0)]) == 3
+    assert rec([R(good, FAKE.value, 64, 1, 5, 0)]) == 4
+    assert rec([R(good, FAKE.value, 64, 1, flk.K, 3)]) == 4
+    assert rec([R(good, None, 64, 1, flk.K, 0)]) == 1
+    assert rec([R(good, FAKE.value, 65, 1, flk.K, 0)]) == 2      # base must have n == T
