@@ -4,9 +4,14 @@ Workload (long prompt layer): one request/layer, K and V each [T=32768, H=8, D=1
 4 loops with retention budgets 100/100/50/25% (loops 3 and 4 compact-sparse over nested
 active sets), K Student-t(3) with per-channel multipliers, V N(0,1), loop deltas N(0,0.05).
 
-One step = for K and for V: flk_encode_base, flk_encode_residual x 3, flk_reconstruct of the
-final depth; the K chain and the V chain are independent and run on two streams (--streams 1
-puts both on one).  `value` = algorithmic bytes of the step (each input read once, each output
+One step = for K and for V: encode the base, encode the residuals of loops 2..4, rebuild the
+final depth.  By default the single calls run with the K chain and the V chain on two streams
+(flk_encode_base, flk_encode_residual x 3, flk_reconstruct each; the chains are independent,
+so one chain's next loop overlaps the other's ramp and drain); --mode batched issues one
+batched call per loop covering both tensors (flk_encode_base_batch, flk_encode_residual_batch
+x 3, flk_reconstruct_batch) on one stream, and --mode serial the single calls on one stream.
+After the timed region every call is also timed alone (one stream, nothing overlapping) and
+reported per call, with the dominant kernel's roofline at that isolated duration.  `value` = algorithmic bytes of the step (each input read once, each output
 written once) / wall time per step, inputs already resident in HBM.  Steps rotate over
 several independent buffer sets (> 1 GB in total) so the 256 MB MALL holds no timed data.
 
@@ -64,6 +69,21 @@ def call_bytes(kind, H, D, T, rows_list):
     return out
 
 
+KV = -1    # a batched call covering the K and the V tensor
+
+
+def batched_symbol(call, rows_list):
+    """Kernel a batched call launches for the long-prompt shapes (K and V both take the batched
+    kernels there); mirrors csrc/flk_encode.hip and csrc/flk_reconstruct.hip."""
+    if call == "reconstruct":
+        n_loops = len(rows_list)
+        if n_loops <= 4:
+            mask = sum(1 << l for l, r in enumerate(rows_list) if r is not None)
+            return f"reconstruct_batch_kernel<{n_loops}, {mask}u, false>"
+        return f"reconstruct_batch_kernel<{n_loops}, 0u, true>"
+    return f"encode_batch_kernel<{str(call != 'base').lower()}, {str(call == 'sparse_residual').lower()}>"
+
+
 def kernel_symbol(kind, call, H, D, rows_list):
     """Name of the kernel (as the profiler prints it, without namespace and arguments) that the
     library launches for one call; mirrors the routing in csrc/flk_encode.hip and
@@ -93,8 +113,9 @@ def kernel_symbol(kind, call, H, D, rows_list):
 class ChainSet:
     """One independent set of device buffers for the K and V chains."""
 
-    def __init__(self, w, host, sets):
+    def __init__(self, w, host, sets, batched=True):
         self.tensors = []
+        self.batched = batched
         H, D, T = w.H, w.D, w.T
         for kind in (flk.K, flk.V):
             xs = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in host[kind].xs]
@@ -106,15 +127,44 @@ class ChainSet:
         self._prepare(w)
 
     def _prepare(self, w):
-        """Marshal every call's arguments once, so a step only issues the C calls."""
+        """Marshal every call's arguments once, so a step only issues the C calls.  Batched:
+        one call per loop (and one reconstruct) covers K and V; else one call per tensor."""
         L = flk.lib()
-        self.calls = []     # (name, kind, fn, args)
+        self.calls = []     # (name, kind or KV, fn, args)
         self._keep = []
+        P = ctypes.c_void_p
+        if self.batched:
+            kd, vd = flk.desc(flk.K, w.H, w.D), flk.desc(flk.V, w.H, w.D)
+            self._keep += [kd, vd]
+            n_loops = len(self.tensors[0][1])
+            for l in range(n_loops):
+                units = []
+                for kind, xs, rows, recon, out, packed in self.tensors:
+                    r = rows[l]
+                    units.append(flk.UnitC(xs[l].data_ptr(), None if r is None else r.data_ptr(), recon.data_ptr(),
+                                           packed[l].codes.data_ptr(), packed[l].params.data_ptr(),
+                                           None if r is None else packed[l].tile_start.data_ptr(),
+                                           xs[l].shape[0], w.T, kind, 0))
+                arr = (flk.UnitC * len(units))(*units)
+                self._keep.append(arr)
+                name = "base" if l == 0 else ("sparse_residual" if rows[l] is not None else "dense_residual")
+                fn = L.flk_encode_base_batch if l == 0 else L.flk_encode_residual_batch
+                self.calls.append((name, KV, fn, (ctypes.byref(kd), ctypes.byref(vd), arr, len(units), None)))
+            runits = []
+            for kind, xs, rows, recon, out, packed in self.tensors:
+                chain = (flk.StreamC * len(packed))(*[p.c() for p in packed])
+                self._keep.append(chain)
+                runits.append(flk.ReconUnitC(ctypes.cast(chain, ctypes.POINTER(flk.StreamC)), out.data_ptr(), w.T,
+                                             len(packed), kind, 0))
+            rarr = (flk.ReconUnitC * len(runits))(*runits)
+            self._keep.append(rarr)
+            self.calls.append(("reconstruct", KV, L.flk_reconstruct_batch,
+                               (ctypes.byref(kd), ctypes.byref(vd), rarr, len(runits))))
+            return
         for kind, xs, rows, recon, out, packed in self.tensors:
             d = flk.desc(kind, w.H, w.D)
             self._keep.append(d)
             dp = ctypes.byref(d)
-            P = ctypes.c_void_p
             self.calls.append(("base", kind, L.flk_encode_base,
                                (dp, P(xs[0].data_ptr()), w.T, P(packed[0].codes.data_ptr()),
                                 P(packed[0].params.data_ptr()), P(recon.data_ptr()), None)))
@@ -135,7 +185,7 @@ class ChainSet:
         """Issue one step: every call on the stream of its tensor (streams[kind]); ev[i], when
         given, is a pair of events recorded around call i on that same stream."""
         for i, (name, kind, fn, args) in enumerate(self.calls):
-            ts, sp = streams[kind]
+            ts, sp = streams[flk.K if kind == KV else kind]
             if ev is not None and ev[i] is not None:
                 ev[i][0].record(ts)
             st = fn(*args, sp)
@@ -229,12 +279,13 @@ COPY_PROBE_BYTES = 1 << 29     # plain copy used to calibrate FETCH_SIZE / WRITE
 
 
 def source_digest():
-    """sha256 over the library's kernel and host sources: a traffic figure taken from an older
-    source tree is not reported."""
+    """sha256 over the sources of the codec kernels and their launches (everything in csrc/ but
+    the host-side validation and the attention kernels): a traffic figure taken from other
+    kernel sources than the ones built now is not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and name not in ("flk_api.cpp", "flk_attn.hip"):
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
@@ -327,8 +378,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled across steps")
-    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
-                    help="2: the K chain and the V chain on two streams; 1: both on one stream")
+    ap.add_argument("--mode", default="streams", choices=("batched", "streams", "serial"),
+                    help="batched: one batched call per loop covers K and V (one stream); streams: "
+                         "single calls, the K chain and the V chain on two streams; serial: single calls "
+                         "on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
     ap.add_argument("--copy-probe", action="store_true",
@@ -352,15 +405,21 @@ def main():
     sets = synth.active_sets(w, w.T)
     host = {flk.K: synth.make_chain(w, synth.K_TENSOR, sets=sets),
             flk.V: synth.make_chain(w, synth.V_TENSOR, sets=sets)}
-    chain_sets = [ChainSet(w, host, sets) for _ in range(args.rotate)]
+    batched = args.mode == "batched"
+    chain_sets = [ChainSet(w, host, sets, batched=batched) for _ in range(args.rotate)]
     torch.cuda.synchronize()
 
     per_call = []
-    for kind in (flk.K, flk.V):
-        per_call += [(kind, name, b) for name, b in call_bytes(kind, w.H, w.D, w.T, sets)]
+    if batched:
+        kb = call_bytes(flk.K, w.H, w.D, w.T, sets)
+        vb = call_bytes(flk.V, w.H, w.D, w.T, sets)
+        per_call = [(KV, name, b + b2) for (name, b), (_, b2) in zip(kb, vb)]
+    else:
+        for kind in (flk.K, flk.V):
+            per_call += [(kind, name, b) for name, b in call_bytes(kind, w.H, w.D, w.T, sets)]
     step_bytes = sum(b for _, _, b in per_call)
-    # default-priority streams only; K chain and V chain are independent and overlap
-    ts = [torch.cuda.Stream(), torch.cuda.Stream()] if args.streams == 2 else [torch.cuda.Stream()] * 2
+    # default-priority streams only; in "streams" mode the K chain and the V chain overlap
+    ts = [torch.cuda.Stream(), torch.cuda.Stream()] if args.mode == "streams" else [torch.cuda.Stream()] * 2
     streams = {k: (ts[i], ctypes.c_void_p(ts[i].cuda_stream)) for i, k in enumerate((flk.K, flk.V))}
 
     # warmup (each call timed on its stream), and find the kernel with the largest share of the step
@@ -374,7 +433,8 @@ def main():
         if i >= 1 or args.warmup <= 1:
             times += np.array([a.elapsed_time(b) for a, b in ev])
             counted += 1
-    symbols = [kernel_symbol(kind, name, w.H, w.D, sets) for kind, name, _ in per_call]
+    symbols = [batched_symbol(name, sets) if kind == KV else kernel_symbol(kind, name, w.H, w.D, sets)
+               for kind, name, _ in per_call]
     sym_time = {}
     for sy, t in zip(symbols, times):
         sym_time[sy] = sym_time.get(sy, 0.0) + t
@@ -395,6 +455,20 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # each call alone: one stream, events around every call, nothing overlapping
+    iso_stream = torch.cuda.Stream()
+    iso_streams = {k: (iso_stream, ctypes.c_void_p(iso_stream.cuda_stream)) for k in (flk.K, flk.V)}
+    iso = np.zeros(n_calls)
+    n_iso = 10
+    for k in range(n_iso):
+        chain_sets[k % args.rotate].run(iso_streams, ev)
+        torch.cuda.synchronize()
+        iso += np.array([a.elapsed_time(b) for a, b in ev])
+    iso_us = iso / n_iso * 1e3
+    per_call_iso = [{"tensor": {flk.K: "K", flk.V: "V", KV: "K+V"}[kind], "call": name, "kernel": sy,
+                     "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
+                    for (kind, name, b), sy, t in zip(per_call, symbols, iso_us)]
+
     dom_ms = [dom_ev[k][i][0].elapsed_time(dom_ev[k][i][1]) for k in range(args.steps) for i in dom_idx]
     dom_bytes = float(np.mean([per_call[i][2] for i in dom_idx]))
     dom_avg_ms = float(np.mean(dom_ms))
@@ -413,9 +487,16 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "config": {"workload": "long_prompt", "T": w.T, "H": w.H, "D": w.D, "loops": w.n_loops,
                    "budgets_pct": list(w.budgets), "tensors": "K+V", "step_bytes": int(step_bytes),
-                   "rotate_sets": args.rotate, "streams": args.streams},
+                   "rotate_sets": args.rotate, "mode": args.mode},
         "roofline": roofline,
     }
+    dom_iso_us = float(np.mean([iso_us[i] for i in dom_idx]))
+    result["roofline_isolated"] = {"bound": "hbm", "kernel": dominant, "achieved": round(dom_bytes / dom_iso_us / 1e3, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(dom_bytes / dom_iso_us / 1e3 / HBM_PEAK_GBS, 4),
+                                   "launch_avg_us": round(dom_iso_us, 2)}
+    result["per_call_isolated"] = per_call_iso
+    result["isolated_step_us"] = round(float(iso_us.sum()), 2)
     if copy_gbs is not None:
         result["copy_probe_gbs"] = round(copy_gbs, 1)
     if not args.no_attention:

@@ -306,23 +306,51 @@ __global__ __launch_bounds__(kAThreads) void attn_tile_kernel(ChainArgs kc, Chai
   }
 }
 
-__global__ __launch_bounds__(kAttnD) void attn_combine_kernel(int32_t splits, int32_t Hq,
-                                                              const float* __restrict__ ws_ml,
-                                                              const float* __restrict__ ws_o,
-                                                              uint16_t* __restrict__ out) {
+// Merge the per-block partials of one query head (blockIdx.x).  Thread (c = tid % 128,
+// g = tid / 128) takes channel c of every kCombGroups-th split from g on, with independent
+// loads in flight; the groups then merge through LDS.
+constexpr int kCombGroups = 8;
+__global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int32_t splits, int32_t Hq,
+                                                                            const float* __restrict__ ws_ml,
+                                                                            const float* __restrict__ ws_o,
+                                                                            uint16_t* __restrict__ out) {
+  __shared__ float s_red[kCombGroups * kAttnD];
+  __shared__ float s_l[kCombGroups * kAttnD];
   const int i = blockIdx.x;
-  const int c = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int c = tid % kAttnD, g = tid / kAttnD;
+  // global maximum of the partial maxima
   float M = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_ml[2 * (int64_t(s) * Hq + i)]);
+  for (int s = tid; s < splits; s += kAttnD * kCombGroups) M = fmaxf(M, ws_ml[2 * (int64_t(s) * Hq + i)]);
+  s_red[tid] = M;
+  __syncthreads();
+  for (int w = kAttnD * kCombGroups / 2; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+    __syncthreads();
+  }
+  M = s_red[0];
+  __syncthreads();
   float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < splits; ++s) {
+#pragma unroll 8
+  for (int s = g; s < splits; s += kCombGroups) {
     const int64_t qi = int64_t(s) * Hq + i;
     const float m = ws_ml[2 * qi];
     const float w = m == -__builtin_inff() ? 0.0f : __expf(m - M);
     L = __builtin_fmaf(ws_ml[2 * qi + 1], w, L);
     O = __builtin_fmaf(ws_o[qi * kAttnD + c], w, O);
   }
-  out[int64_t(i) * kAttnD + c] = __builtin_bit_cast(uint16_t, (__bf16)(O / L));
+  s_red[tid] = O;
+  s_l[tid] = L;
+  __syncthreads();
+  if (g == 0) {
+    float Ot = 0.0f, Lt = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCombGroups; ++k) {
+      Ot += s_red[k * kAttnD + c];
+      Lt += s_l[k * kAttnD + c];
+    }
+    out[int64_t(i) * kAttnD + c] = __builtin_bit_cast(uint16_t, (__bf16)(Ot / Lt));
+  }
 }
 
 hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
@@ -349,8 +377,8 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
 #undef FLK_A
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD), 0, stream, splits, Hq, ws_ml, ws_o,
-                     static_cast<uint16_t*>(out));
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, splits, Hq, ws_ml,
+                     ws_o, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
