@@ -2,18 +2,20 @@
 // chains (FlashLoop RFC, vllm-rlt #156, section 3.3: optimized readers consume the packed
 // base/residual tiles during QK and PV instead of keeping a BF16 shadow cache).
 //
-// A block owns one KV head and a run of 64-token tiles.  For each tile it
-//   1. decodes K_hat and V_hat of the tile into LDS, bit for bit as the encoder left them:
-//      the leading dense loops accumulate in registers (one thread per token x 8 channels),
-//      every later loop reads only the rows it lists (compact rows of the tile, found with the
-//      tile index) and updates LDS in place, so an absent token costs nothing;
-//   2. computes the G query heads' scores for its 64 tokens with MFMA, as S^T = K_hat Q^T
-//      (v_mfma_f32_16x16x32_bf16, one 16-token slice per wave);
-//   3. keeps an online softmax per (wave, query head) in binary32 and accumulates
-//      O^T += V_hat^T P^T with v_mfma_f32_16x16x16_bf16 -- the score tile's register layout is
-//      exactly the P^T operand's, so probabilities never leave registers.
-// At the end the 4 waves' (m, l, O) merge through LDS into one partial per (block, query head);
-// a second kernel merges the partials of all blocks.
+// Every wave works alone on a run of 64-token tiles of one KV head, 16 tokens (one MFMA
+// slice) at a time, with no block barrier until the end:
+//   1. per tile it scatters each compact loop's rows of the tile (found with the tile index)
+//      into a wave-private position -> compact-row map, and stages the tile's K parameter rows
+//      in wave-private LDS;
+//   2. it decodes K_hat of the slice bit for bit as the encoder left it, straight into the A
+//      operand registers of S^T = K_hat Q^T (v_mfma_f32_16x16x32_bf16): a lane's A operand is
+//      8 consecutive channels of one token, which is exactly one decode item;
+//   3. it keeps an online softmax per query head in binary32;
+//   4. it decodes V_hat of the slice into a wave-private LDS tile and accumulates
+//      O^T += V_hat^T P^T with v_mfma_f32_16x16x16_bf16, whose P^T operand layout is the score
+//      tile's register layout, so probabilities never leave registers.
+// At the end the block's 4 waves merge their (m, l, O) through LDS into one partial per
+// (block, query head); a second kernel merges the partials of all blocks.
 #include "flk_device.h"
 #include "flk_internal.h"
 
@@ -23,24 +25,29 @@ constexpr int kAThreads = 256;
 constexpr int kAttnD = 128;
 constexpr int kMaxG = 16;
 constexpr int kLdsRow = kAttnD + 8;         // BF16 per LDS row: 272 bytes keep MFMA reads conflict-free
-#ifndef FLK_ATTN_BLOCKS
-#define FLK_ATTN_BLOCKS 2048
+#ifndef FLK_ATTN_WAVES
+#define FLK_ATTN_WAVES 4096
 #endif
-constexpr int kAttnBlocks = FLK_ATTN_BLOCKS;  // aim for about this many blocks per launch
+constexpr int kAttnWaves = FLK_ATTN_WAVES;    // aim for about this many waves per launch
+#ifndef FLK_ATTN_OCC
+#define FLK_ATTN_OCC 2   // waves per SIMD the register budget must allow
+#endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-static int32_t tiles_per_split(int32_t T, int32_t H) {
+// Tiles per wave: about kAttnWaves waves per launch.  A block of 4 waves covers 4*tpw tiles
+// and writes one partial per query head.
+static int32_t tiles_per_wave(int32_t T, int32_t H) {
   const int64_t tiles = (int64_t(T) + kGroup - 1) / kGroup;
-  const int64_t per = (tiles * H + kAttnBlocks - 1) / kAttnBlocks;
+  const int64_t per = (tiles * H + kAttnWaves - 1) / kAttnWaves;
   return int32_t(per < 1 ? 1 : per);
 }
 static int32_t n_splits(int32_t T, int32_t H) {
   const int32_t tiles = (T + kGroup - 1) / kGroup;
-  const int32_t tps = tiles_per_split(T, H);
-  return (tiles + tps - 1) / tps;
+  const int32_t per_block = 4 * tiles_per_wave(T, H);
+  return (tiles + per_block - 1) / per_block;
 }
 
 size_t attn_workspace_bytes(int32_t T, int32_t H, int32_t Hq) {
@@ -69,147 +76,138 @@ __device__ __forceinline__ void load_bf16x8(const uint16_t* src, float v[8]) {
   v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xFFFF0000u);
 }
 
-// Decode one chain's tile (64 tokens from t0, KV head h, all 128 channels) into s[64][kLdsRow].
-// Thread (ts = tid >> 4, oc = tid & 15) owns channels 8*oc..8*oc+7 of tokens ts + 16*i.
-// kp is LDS scratch for K parameter rows: [NL][2][128].  Contains barriers; all threads call.
-template <int KIND, int NL>
-__device__ __forceinline__ void decode_tile(const ChainArgs& c, int32_t tile, int32_t T, int32_t H,
-                                            int32_t h, uint16_t (*s)[kLdsRow], uint32_t (*kp)[2][kAttnD]) {
-  const int tid = threadIdx.x;
-  const int oc = tid & 15, ts = tid >> 4;
-  const int32_t t0 = tile * kGroup;
-  const int nl = c.n_loops;
+constexpr int kAWaves = kAThreads / 64;
 
-  // compact row range of every loop for this tile (dense loops: the tile's positions)
+// One wave's LDS: the V_hat slice, the tile's K parameter rows and the compact-row maps.
+template <int NL>
+struct WaveLds {
+  uint16_t v[16][kLdsRow];                 // V_hat of the current slice, [token][channel]
+  uint32_t kp[NL][2][kAttnD];              // K parameter rows of the tile (two rowgroups)
+  int32_t map[2][NL][kGroup];              // [K|V][loop][position in tile] -> compact row, -1 absent
+};
+constexpr size_t kMergeBytes = size_t(kAWaves) * kMaxG * (2 + kAttnD) * sizeof(float);
+template <int NL>
+constexpr size_t attn_lds_bytes() {
+  return kAWaves * sizeof(WaveLds<NL>) > kMergeBytes ? kAWaves * sizeof(WaveLds<NL>) : kMergeBytes;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per chain and loop: the rows of the tile [lo, hi) and whether the loop is dense.
+template <int NL>
+struct TileRows {
   int32_t lo[NL], hi[NL];
   bool dense[NL];
+};
+
+template <int NL>
+__device__ __forceinline__ TileRows<NL> tile_rows(const ChainArgs& c, int32_t tile, int32_t T) {
+  TileRows<NL> r;
+  const int32_t t0 = tile * kGroup;
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
-    dense[l] = l >= nl || c.s[l].rows == nullptr;
-    lo[l] = dense[l] ? t0 : uniform(c.s[l].tile_start[tile]);
-    hi[l] = dense[l] ? min(t0 + kGroup, T) : uniform(c.s[l].tile_start[tile + 1]);
+    r.dense[l] = l >= c.n_loops || c.s[l].rows == nullptr;
+    r.lo[l] = r.dense[l] ? t0 : uniform(c.s[l].tile_start[tile]);
+    r.hi[l] = r.dense[l] ? min(t0 + kGroup, T) : uniform(c.s[l].tile_start[tile + 1]);
   }
-  int dp = 0;                                             // leading dense loops
+  return r;
+}
+
+// Scatter the tile's compact rows of every compact loop into map[l][position - t0].
+template <int NL>
+__device__ __forceinline__ void build_maps(const ChainArgs& c, const TileRows<NL>& r, int32_t t0,
+                                           int32_t (*map)[kGroup], int lane) {
 #pragma unroll
   for (int l = 0; l < NL; ++l)
-    if (l < nl && dense[l] && dp == l) dp = l + 1;
-
-  // K: stage the parameter rows the tile needs (rowgroups lo/64 and lo/64 + 1 per loop)
-  if (KIND == FLK_KIND_K) {
+    if (l < c.n_loops && !r.dense[l]) map[l][lane] = -1;
+  wave_sync();
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      if (l >= nl) continue;
-      const int32_t rg = lo[l] / kGroup + (tid >> 7);     // a dense loop needs only the first
-      const int32_t nrg = (c.s[l].n + kGroup - 1) / kGroup;
-      if (rg < nrg && !(dense[l] && (tid >> 7)))
-        kp[l][tid >> 7][tid & 127] = c.s[l].params[(int64_t(rg) * H + h) * kAttnD + (tid & 127)];
+  for (int l = 0; l < NL; ++l) {
+    if (l >= c.n_loops || r.dense[l]) continue;
+    const int32_t j = r.lo[l] + lane;
+    if (j < r.hi[l]) {
+      const uint32_t p = uint32_t(c.s[l].rows[j] - t0);
+      if (p < uint32_t(kGroup)) map[l][p] = j;         // a malformed entry outside the tile is dropped
     }
   }
+}
 
-  // issue every item's code word (and V parameter, and compact position) up front
+// Decode 4 items (token tk of the tile, octets oc[i]) of one chain; out[i] receives item i's
+// 8 channels as packed BF16 (zeros for an absent or out-of-range token).  Every code word is
+// requested first; then one item at a time is decoded, so only one item's binary32 values
+// are live.  K: parameters from the staged rows; V: one parameter per item.
+template <int KIND, int NL>
+__device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<NL>& r, int32_t t0, int32_t T,
+                                             int32_t H, int32_t h, int tk, const int oc[4],
+                                             const int32_t (*map)[kGroup], const uint32_t (*kp)[2][kAttnD],
+                                             uint4 out[4]) {
+  const int nl = c.n_loops;
+  const int32_t t = t0 + tk;
+  int32_t j[NL];
   uint32_t cw[NL][4], vp[NL][4];
-  int32_t pos[NL][4];
 #pragma unroll
-  for (int l = 0; l < NL; ++l)
+  for (int l = 0; l < NL; ++l) {
+    j[l] = -1;
+    if (l < nl) j[l] = r.dense[l] ? (t < T ? t : -1) : map[l][tk];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int32_t j = lo[l] + ts + 16 * i;               // row of the stream
-      const bool ok = l < nl && j < hi[l];
       cw[l][i] = 0;
       vp[l][i] = 0;
-      pos[l][i] = -1;
-      if (ok) {
-        cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (int64_t(j) * H + h) * (kAttnD / 2) + oc * 4);
-        if (KIND == FLK_KIND_V) vp[l][i] = c.s[l].params[(int64_t(j) * H + h) * 2 + (oc >> 3)];
-        pos[l][i] = dense[l] ? j - t0 : c.s[l].rows[j] - t0;
+      if (j[l] >= 0) {
+        const int64_t item = int64_t(j[l]) * H + h;
+        cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + item * (kAttnD / 2) + oc[i] * 4);
+        if (KIND == FLK_KIND_V) vp[l][i] = c.s[l].params[item * 2 + (oc[i] >> 3)];
       }
     }
-  if (KIND == FLK_KIND_K) __syncthreads();                // staged parameter rows visible
-
-  auto params_of = [&](int l, int32_t j, uint32_t p[8]) {
-    if (KIND == FLK_KIND_K) {
-      const int r = j / kGroup - lo[l] / kGroup;
-      const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][r][oc * 8]);
-      const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][r][oc * 8 + 4]);
-      p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
-    } else {
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = 0;
-    }
-  };
-
-  // leading dense loops in registers; tokens past T stay zero
-  float acc[4][8];
+  for (int i = 0; i < 4; ++i) {
+    float acc[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
-#pragma unroll
-  for (int l = 0; l < NL; ++l) {
-    if (l >= dp) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (pos[l][i] < 0) continue;
+    for (int l = 0; l < NL; ++l) {
+      if (j[l] < 0) continue;
       uint32_t p[8];
-      params_of(l, lo[l] + ts + 16 * i, p);
-      if (KIND == FLK_KIND_V) {
+      if (KIND == FLK_KIND_K) {
+        const int rg = r.dense[l] ? 0 : j[l] / kGroup - r.lo[l] / kGroup;
+        const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
+        p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+      } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = vp[l][i];
       }
       float d[8];
       decode_item(cw[l][i], p, d);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] = l == 0 ? d[e] : round_bf16(acc[i][e] + d[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
     }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) store_bf16x8(&s[ts + 16 * i][oc * 8], acc[i]);
-  __syncthreads();
-
-  // every later loop: read-modify-write of the rows it lists
-#pragma unroll
-  for (int l = 0; l < NL; ++l) {
-    if (l < dp || l >= nl) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t pl = uint32_t(pos[l][i]);
-      if (pl >= uint32_t(kGroup)) continue;               // no row, or a map entry outside the tile
-      uint32_t p[8];
-      params_of(l, lo[l] + ts + 16 * i, p);
-      if (KIND == FLK_KIND_V) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = vp[l][i];
-      }
-      float d[8], v[8];
-      decode_item(cw[l][i], p, d);
-      load_bf16x8(&s[pl][oc * 8], v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e] + d[e]);
-      store_bf16x8(&s[pl][oc * 8], v);
-    }
-    __syncthreads();
+    out[i] = pack_exact_bf16x8(acc);
   }
 }
 
 template <int NL>
-__global__ __launch_bounds__(kAThreads) void attn_tile_kernel(ChainArgs kc, ChainArgs vc, int32_t T, int32_t H,
+__global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(ChainArgs kc, ChainArgs vc, int32_t T, int32_t H,
                                                               int32_t G, const uint16_t* __restrict__ q,
-                                                              float scale, int32_t tps,
+                                                              float scale, int32_t tpw,
                                                               float* __restrict__ ws_ml, float* __restrict__ ws_o) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_kv[2][kGroup][kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint32_t s_kp[NL][2][kAttnD];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int n = lane & 15;                                // query head of this lane (MFMA column)
-  const int kb = lane >> 4;                               // k-block / row block of this lane
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[attn_lds_bytes<NL>()];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15;                                // MFMA column: query head / token / channel
+  const int kb = lane >> 4;                               // MFMA k-block / row block
   const int32_t split = blockIdx.x;
   const int32_t h = blockIdx.y;
   const int32_t Hq = H * G;
   const int32_t tiles = (T + kGroup - 1) / kGroup;
-  const int32_t tile0 = split * tps;
-  const int32_t tile1 = min(tiles, tile0 + tps);
+  const int32_t tile0 = (split * kAWaves + wave) * tpw;
+  const int32_t tile1 = min(tiles, tile0 + tpw);
+  WaveLds<NL>& L = reinterpret_cast<WaveLds<NL>*>(s_raw)[wave];
 
   // Q^T as the B operand of S^T = K_hat Q^T: lane holds Q[n][32*ks + 8*kb + j], zero past G
   bf16x8_t qb[4];
@@ -219,6 +217,10 @@ __global__ __launch_bounds__(kAThreads) void attn_tile_kernel(ChainArgs kc, Chai
     if (n < G) w = *reinterpret_cast<const uint4*>(q + int64_t(h * G + n) * kAttnD + 32 * ks + 8 * kb);
     qb[ks] = __builtin_bit_cast(bf16x8_t, w);
   }
+  // decode items of this lane: token n of the slice, octets 4*i + kb (the K A-operand layout)
+  int oc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oc[i] = 4 * i + kb;
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   float4_t o[8];
@@ -226,58 +228,85 @@ __global__ __launch_bounds__(kAThreads) void attn_tile_kernel(ChainArgs kc, Chai
   for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int32_t tile = tile0; tile < tile1; ++tile) {
-    decode_tile<FLK_KIND_K, NL>(kc, tile, T, H, h, s_kv[0], s_kp);
-    decode_tile<FLK_KIND_V, NL>(vc, tile, T, H, h, s_kv[1], s_kp);
+    const int32_t t0 = tile * kGroup;
+    const TileRows<NL> rk = tile_rows<NL>(kc, tile, T);
+    const TileRows<NL> rv = tile_rows<NL>(vc, tile, T);
+    wave_sync();                                          // the previous tile's LDS reads are done
+    build_maps<NL>(kc, rk, t0, L.map[0], lane);
+    build_maps<NL>(vc, rv, t0, L.map[1], lane);
+    // K parameter rows of the tile: rowgroup lo/64 (and lo/64 + 1 for a compact loop)
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      if (l >= kc.n_loops) continue;
+      const int32_t nrg = (kc.s[l].n + kGroup - 1) / kGroup;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int32_t rg = rk.lo[l] / kGroup + r;
+        if ((r == 1 && rk.dense[l]) || rg >= nrg) continue;
+        const uint2 w = *reinterpret_cast<const uint2*>(kc.s[l].params + (int64_t(rg) * H + h) * kAttnD + 2 * lane);
+        *reinterpret_cast<uint2*>(&L.kp[l][r][2 * lane]) = w;
+      }
+    }
+    wave_sync();
 
-    // scores of this wave's 16 tokens: S^T[token][head], lane holds tokens 4*kb + i of head n
-    float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sl = 0; sl < kGroup / 16; ++sl) {
+      const int tk = 16 * sl + n;
+      // K_hat of the slice straight into the A operands
+      uint4 item[4];
+      decode_items<FLK_KIND_K, NL>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, item);
+      float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&s_kv[0][16 * wave + n][32 * ks + 8 * kb]);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], sacc, 0, 0, 0);
-    }
-    float sc[4];
-    float mx = -__builtin_inff();
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item[ks]), qb[ks], sacc, 0, 0, 0);
+      // online softmax; lane holds the scores of tokens 4*kb + i of the slice for head n
+      float sc[4];
+      float mx = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t t = tile * kGroup + 16 * wave + 4 * kb + i;
-      sc[i] = t < T ? sacc[i] * scale : -__builtin_inff();
-      mx = fmaxf(mx, sc[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    float p[4], psum = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int32_t t = t0 + 16 * sl + 4 * kb + i;
+        sc[i] = t < T ? sacc[i] * scale : -__builtin_inff();
+        mx = fmaxf(mx, sc[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      float p[4], psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = m_new == -__builtin_inff() ? 0.0f : __expf(sc[i] - m_new);
-      psum += p[i];
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    const float corr = m_run == -__builtin_inff() ? 0.0f : __expf(m_run - m_new);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
+      for (int i = 0; i < 4; ++i) {
+        p[i] = m_new == -__builtin_inff() ? 0.0f : __expf(sc[i] - m_new);
+        psum += p[i];
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      const float corr = m_run == -__builtin_inff() ? 0.0f : __expf(m_run - m_new);
+      l_run = l_run * corr + psum;
+      m_run = m_new;
 
-    // O^T[ch][head] += V_hat^T[ch][token] P^T[token][head]; lane: channel 16*mt + n, tokens 4*kb + j
-    short4_t pb;
+      // V_hat of the slice into LDS, then O^T += V_hat^T P^T
+      decode_items<FLK_KIND_V, NL>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, item);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pb[j] = short(__builtin_bit_cast(uint16_t, (__bf16)p[j]));
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.v[n][oc[i] * 8]) = item[i];
+      wave_sync();
+      short4_t pb;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      short4_t a;
+      for (int j = 0; j < 4; ++j) pb[j] = short(__builtin_bit_cast(uint16_t, (__bf16)p[j]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = short(s_kv[1][16 * wave + 4 * kb + j][16 * mt + n]);
-      o[mt] = o[mt] * corr;
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
+      for (int mt = 0; mt < 8; ++mt) {
+        short4_t a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = short(L.v[4 * kb + j][16 * mt + n]);
+        o[mt] = o[mt] * corr;
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
+      }
+      wave_sync();                                        // the slice's V reads before the next writes
     }
-    __syncthreads();                                      // LDS tiles are rewritten next
   }
 
   // merge the 4 waves: (m, l) per head and O^T per (head, channel) through LDS
-  float* s_m = reinterpret_cast<float*>(&s_kv[0][0][0]);  // [4][16]
-  float* s_l = s_m + 4 * kMaxG;                           // [4][16]
-  float* s_o = s_l + 4 * kMaxG;                           // [4][16][128]
+  __syncthreads();
+  float* s_m = reinterpret_cast<float*>(s_raw);           // [4][16]
+  float* s_l = s_m + kAWaves * kMaxG;                     // [4][16]
+  float* s_o = s_l + kAWaves * kMaxG;                     // [4][16][128]
   if (kb == 0) {
     s_m[wave * kMaxG + n] = m_run;
     s_l[wave * kMaxG + n] = l_run;
@@ -287,21 +316,21 @@ __global__ __launch_bounds__(kAThreads) void attn_tile_kernel(ChainArgs kc, Chai
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_o[(wave * kMaxG + n) * kAttnD + 16 * mt + 4 * kb + i] = o[mt][i];
   __syncthreads();
-  for (int idx = tid; idx < G * kAttnD; idx += kAThreads) {
+  for (int idx = threadIdx.x; idx < G * kAttnD; idx += kAThreads) {
     const int g = idx / kAttnD, ch = idx % kAttnD;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w * kMaxG + g]);
-    float L = 0.0f, O = 0.0f;
+    for (int w = 0; w < kAWaves; ++w) M = fmaxf(M, s_m[w * kMaxG + g]);
+    float Ls = 0.0f, O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kAWaves; ++w) {
       const float mw = s_m[w * kMaxG + g];
       const float f = mw == -__builtin_inff() ? 0.0f : __expf(mw - M);
-      L += s_l[w * kMaxG + g] * f;
+      Ls += s_l[w * kMaxG + g] * f;
       O += s_o[(w * kMaxG + g) * kAttnD + ch] * f;
     }
     const int64_t qi = int64_t(split) * Hq + h * G + g;
-    if (ch == 0) { ws_ml[2 * qi] = M; ws_ml[2 * qi + 1] = L; }
+    if (ch == 0) { ws_ml[2 * qi] = M; ws_ml[2 * qi + 1] = Ls; }
     ws_o[qi * kAttnD + ch] = O;
   }
 }
@@ -357,7 +386,7 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
                               const ChainArgs& kc, const ChainArgs& vc, float scale, void* out,
                               void* ws, hipStream_t stream) {
   (void)D;
-  const int32_t tps = tiles_per_split(T, H);
+  const int32_t tpw = tiles_per_wave(T, H);
   const int32_t splits = n_splits(T, H);
   const int32_t G = Hq / H;
   float* ws_ml = static_cast<float*>(ws);
@@ -367,8 +396,8 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
   const uint16_t* qp = static_cast<const uint16_t*>(q);
 #define FLK_A(NLV)                                                                                      \
   case NLV:                                                                                             \
-    hipLaunchKernelGGL((attn_tile_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
-                       scale, tps, ws_ml, ws_o);                                                        \
+    hipLaunchKernelGGL((attn_wave_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
+                       scale, tpw, ws_ml, ws_o);                                                        \
     break;
   switch (nl) {
     FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
