@@ -84,6 +84,7 @@ struct WaveLds {
   uint16_t v[16][kLdsRow];                 // V_hat of the current slice, [token][channel]
   uint32_t kp[NL][2][kAttnD];              // K parameter rows of the tile (two rowgroups)
   int32_t map[2][NL][kGroup];              // [K|V][loop][position in tile] -> compact row, -1 absent
+  int32_t perm[kGroup];                    // tile positions grouped by which loops list them
 };
 constexpr size_t kMergeBytes = size_t(kAWaves) * kMaxG * (2 + kAttnD) * sizeof(float);
 template <int NL>
@@ -247,10 +248,37 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
         *reinterpret_cast<uint2*>(&L.kp[l][r][2 * lane]) = w;
       }
     }
+    // Order the tile's positions so that positions listed by the same loops sit together (the
+    // softmax sum does not depend on the order): a 16-token slice then mostly holds one loop
+    // pattern, and a loop none of its tokens has is skipped by the whole wave.  Positions past
+    // T go last.  Groups are ranked in order of first occurrence.
+    const int32_t n_valid = min(kGroup, T - t0);
+    {
+      uint32_t key = 0;
+#pragma unroll
+      for (int l = 1; l < NL; ++l) {
+        if (l < kc.n_loops && !rk.dense[l] && L.map[0][l][lane] >= 0) key |= 1u << l;
+        if (l < vc.n_loops && !rv.dense[l] && L.map[1][l][lane] >= 0) key |= 1u << (NL + l);
+      }
+      const bool valid = lane < n_valid;
+      const uint64_t below = (uint64_t(1) << lane) - 1;
+      uint64_t remaining = __ballot(valid);
+      int base = 0, rank = 0;
+      while (remaining) {
+        const int leader = __builtin_ctzll(remaining);
+        const uint32_t k = __builtin_amdgcn_readlane(key, leader);
+        const uint64_t grp = __ballot(valid && key == k);
+        if (valid && key == k) rank = base + __builtin_popcountll(grp & below);
+        base += __builtin_popcountll(grp);
+        remaining &= ~grp;
+      }
+      if (!valid) rank = lane;                              // the invalid tail keeps its order
+      L.perm[rank] = lane;
+    }
     wave_sync();
 
     for (int sl = 0; sl < kGroup / 16; ++sl) {
-      const int tk = 16 * sl + n;
+      const int tk = L.perm[16 * sl + n];
       // K_hat of the slice straight into the A operands
       uint4 item[4];
       decode_items<FLK_KIND_K, NL>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, item);
@@ -263,8 +291,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       float mx = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int32_t t = t0 + 16 * sl + 4 * kb + i;
-        sc[i] = t < T ? sacc[i] * scale : -__builtin_inff();
+        sc[i] = 16 * sl + 4 * kb + i < n_valid ? sacc[i] * scale : -__builtin_inff();
         mx = fmaxf(mx, sc[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
