@@ -159,9 +159,10 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
       cw[l][i] = 0;
       vp[l][i] = 0;
       if (j[l] >= 0) {
-        const int64_t item = int64_t(j[l]) * H + h;
-        cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + item * (kAttnD / 2) + oc[i] * 4);
-        if (KIND == FLK_KIND_V) vp[l][i] = c.s[l].params[item * 2 + (oc[i] >> 3)];
+        // uniform base + 32-bit offset: one saddr load, no 64-bit address arithmetic per lane
+        const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
+        cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (item * (kAttnD / 2) + uint32_t(oc[i]) * 4u));
+        if (KIND == FLK_KIND_V) vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
       }
     }
   }
@@ -175,7 +176,7 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
       if (j[l] < 0) continue;
       uint32_t p[8];
       if (KIND == FLK_KIND_K) {
-        const int rg = r.dense[l] ? 0 : j[l] / kGroup - r.lo[l] / kGroup;
+        const int rg = (j[l] / kGroup) & 1;               // staged by rowgroup parity
         const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
         const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
         p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
@@ -235,7 +236,8 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     wave_sync();                                          // the previous tile's LDS reads are done
     build_maps<NL>(kc, rk, t0, L.map[0], lane);
     build_maps<NL>(vc, rv, t0, L.map[1], lane);
-    // K parameter rows of the tile: rowgroup lo/64 (and lo/64 + 1 for a compact loop)
+    // K parameter rows of the tile: rowgroup lo/64 (and lo/64 + 1 for a compact loop), each in
+    // the slot of its parity, so a row j finds its parameters in slot (j/64) & 1
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
       if (l >= kc.n_loops) continue;
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       for (int r = 0; r < 2; ++r) {
         const int32_t rg = rk.lo[l] / kGroup + r;
         if ((r == 1 && rk.dense[l]) || rg >= nrg) continue;
-        const uint2 w = *reinterpret_cast<const uint2*>(kc.s[l].params + (int64_t(rg) * H + h) * kAttnD + 2 * lane);
-        *reinterpret_cast<uint2*>(&L.kp[l][r][2 * lane]) = w;
+        const uint2 w = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(rg) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
+        *reinterpret_cast<uint2*>(&L.kp[l][rg & 1][2 * lane]) = w;
       }
     }
     // Order the tile's positions so that positions listed by the same loops sit together (the
