@@ -26,7 +26,7 @@ constexpr int kAttnD = 128;
 constexpr int kMaxG = 16;
 constexpr int kLdsRow = kAttnD + 8;         // BF16 per LDS row: 272 bytes keep MFMA reads conflict-free
 #ifndef FLK_ATTN_WAVES
-#define FLK_ATTN_WAVES 4096
+#define FLK_ATTN_WAVES 8192
 #endif
 constexpr int kAttnWaves = FLK_ATTN_WAVES;    // aim for about this many waves per launch
 #ifndef FLK_ATTN_OCC
