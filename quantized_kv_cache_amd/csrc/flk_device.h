@@ -268,6 +268,11 @@ __device__ __forceinline__ float dpp_xor1(float v) {   // quad_perm [1,0,3,2]
 __device__ __forceinline__ float dpp_xor2(float v) {   // quad_perm [2,3,0,1]
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
+// row_half_mirror: lane i of each group of 8 reads lane 7 - i, in the other quad; after the two
+// quad exchanges it completes a reduction over 8 consecutive lanes.
+__device__ __forceinline__ float dpp_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
 
 // ---- nontemporal (streaming) global accesses ----------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -17,6 +17,7 @@ constexpr int kThreads = 256;
 #define FLK_VWIDE_WAVES 32768
 #endif
 constexpr int kVWideWaves = FLK_VWIDE_WAVES;
+
 constexpr uint32_t kDevRows = FLK_DEV_ROWS;
 
 __device__ __forceinline__ void unpack8(const uint4& w, float v[8]) {
@@ -37,13 +38,13 @@ __device__ __forceinline__ uint4 pack8(const float v[8]) {
 
 // ---------------------------------------------------------------------------------------
 // K: groups run down 64 compact rows of one (head, channel).  A block owns one 64-row band
-// (blockIdx.x) of a 128-channel strip (blockIdx.y) of the flattened H*D channel axis.
+// of a 128-channel strip of the flattened H*D channel axis.
 // Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs+16, rs+32, rs+48.
 // Extremes: in registers over 4 rows, across the 4 row slots of a wave with lane shuffles,
 // across the 4 waves through LDS; one thread per channel then derives the params.
 // ---------------------------------------------------------------------------------------
 template <bool RESID, bool SPARSE>
-__device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t bx, uint32_t by) {
+__device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, uint32_t band_) {
   const uint16_t* __restrict__ x = a.x;
   const int32_t* __restrict__ rows = a.rows;
   uint16_t* __restrict__ recon = a.recon;
@@ -61,8 +62,8 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t bx, uin
   const int rs = tid >> 4;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int band = int(bx);
-  const int chunk = int(by) * 16 + cc;
+  const int band = int(band_);
+  const int chunk = int(strip) * 16 + cc;
   const bool cact = chunk < (W >> 3);
   const int64_t ch = int64_t(chunk) * 8;
 
@@ -92,7 +93,7 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t bx, uin
     unpack8(xv, v[i]);
   }
   if (SPARSE && bad_row && status) atomicOr(status, kDevRows);
-  if (SPARSE && by == 0 && cc == 0) {
+  if (SPARSE && strip == 0 && cc == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = band * kGroup + rs + 16 * i;
@@ -133,7 +134,7 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t bx, uin
   if (tid < 128) {
     const float a = tmin(tmin(s_min[0][tid], s_min[1][tid]), tmin(s_min[2][tid], s_min[3][tid]));
     const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
-    const int64_t chan = int64_t(by) * 128 + tid;
+    const int64_t chan = int64_t(strip) * 128 + tid;
     GroupParams p = make_params(a, b);
     s_m[tid] = p.m;
     s_s[tid] = p.s;
@@ -173,9 +174,13 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t bx, uin
   }
 }
 
+// Blocks run strip-fastest in XCD order: the neighbouring strips of a band write the two halves
+// of the same 128-byte code lines, and so meet in one L2.
 template <bool RESID, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void encode_k_kernel(EncArgs a) {
-  encode_k_body<RESID, SPARSE>(a, blockIdx.x, blockIdx.y);
+  uint32_t strip, band;
+  xcd_block(strip, band);
+  encode_k_body<RESID, SPARSE>(a, strip, band);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -280,9 +285,10 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// V, wide rows (D % 64 == 0, H*D % 1024 == 0): a strip is 1024 channels, 64 lanes x 16
-// channels, so a 64-channel group is 4 consecutive lanes and its extremes take two DPP quad
-// exchanges.  Each wave walks its own run of compact rows one row at a time; the row index,
+// V, wide rows (D % 64 == 0, H*D % 1024 == 0): a strip is 1024 channels, two halves of 64
+// lanes x 8 channels, so a 64-channel group is 8 consecutive lanes and its extremes take two
+// DPP quad exchanges and a half-row mirror.  Each wave walks its own run of compact rows one
+// row at a time; the row index,
 // rows[j] and every row offset are scalars, every access is a buffer access, and the next
 // row's loads are issued before the current row is processed.
 // ---------------------------------------------------------------------------------------
@@ -303,7 +309,11 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
   const int32_t j0 = (int32_t(bx) * (kThreads / 64) + wave) * rows_per_wave;
   if (j0 >= n) return;
   const int32_t j1 = min(j0 + rows_per_wave, n);
-  const uint32_t ch = by * 1024u + uint32_t(lane) * kCh;
+  // lane l owns channels 8l..8l+7 of each 512-channel half of the strip, so every load and
+  // store instruction covers one contiguous kilobyte (a lane owning 16 adjacent channels
+  // would split every cache line between two instructions, measurably slower)
+  const uint32_t ch = by * 1024u + uint32_t(lane) * 8u;
+  constexpr uint32_t hoff = 512u;                          // channels between the two halves
   const uint32_t xrow = uint32_t(W) * 2u, crow = uint32_t(W) / 2u, prow = uint32_t(W) / 16u;
   const BufRsrc xrs = make_buf(x, uint32_t(n) * xrow);
   const BufRsrc rrs = make_buf(recon, uint32_t(T) * xrow);
@@ -322,10 +332,10 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
     pos[b] = p;
     const uint32_t pr = uint32_t(max(p, 0));
     xa[b] = buf_ld128<kCacheStream>(xrs, xv, uint32_t(j) * xrow);
-    xb[b] = buf_ld128<kCacheStream>(xrs, xv + 16u, uint32_t(j) * xrow);
+    xb[b] = buf_ld128<kCacheStream>(xrs, xv + 2u * hoff, uint32_t(j) * xrow);
     if (RESID) {
       ra[b] = buf_ld128(rrs, xv, pr * xrow);
-      rb[b] = buf_ld128(rrs, xv + 16u, pr * xrow);
+      rb[b] = buf_ld128(rrs, xv + 2u * hoff, pr * xrow);
     }
   };
   uint32_t err = 0;
@@ -343,27 +353,34 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
 #pragma unroll
       for (int e = 0; e < kCh; ++e) v[e] = round_bf16(v[e] - r[e]);
     }
-    float mn = v[0], mx = v[0];
+    // two groups per lane (one per half), each spread over 8 consecutive lanes
+    float k[kCh], o[kCh];
 #pragma unroll
-    for (int e = 1; e < kCh; ++e) { mn = tmin(mn, v[e]); mx = tmax(mx, v[e]); }
-    mn = tmin(mn, dpp_xor1(mn));
-    mx = tmax(mx, dpp_xor1(mx));
-    mn = tmin(mn, dpp_xor2(mn));
-    mx = tmax(mx, dpp_xor2(mx));
-    const GroupParams gp = make_params(mn, mx);
-    err |= gp.err;
-    float k[kCh];
-    codes_of<kCh>(v, gp, k);
-    buf_st64<kCacheStream>(pack_codes8_u8(k), pack_codes8_u8(k + 8), crs, cv, uint32_t(j) * crow);
-    if ((lane & 3) == 0) buf_st32<kCacheStream>(gp.packed, prs, pv, uint32_t(j) * prow);
-    float o[kCh];
+    for (int hh = 0; hh < 2; ++hh) {
+      const float* vh = v + 8 * hh;
+      float mn = vh[0], mx = vh[0];
 #pragma unroll
-    for (int e = 0; e < kCh; ++e) {
-      o[e] = decode(k[e], gp.m, gp.s);
-      if (RESID) o[e] = r[e] + round_bf16(o[e]);
+      for (int e = 1; e < 8; ++e) { mn = tmin(mn, vh[e]); mx = tmax(mx, vh[e]); }
+      mn = tmin(mn, dpp_xor1(mn));
+      mx = tmax(mx, dpp_xor1(mx));
+      mn = tmin(mn, dpp_xor2(mn));
+      mx = tmax(mx, dpp_xor2(mx));
+      mn = tmin(mn, dpp_half_mirror(mn));
+      mx = tmax(mx, dpp_half_mirror(mx));
+      const GroupParams gp = make_params(mn, mx);
+      err |= gp.err;
+      codes_of<8>(vh, gp, k + 8 * hh);
+      if ((lane & 7) == 0) buf_st32<kCacheStream>(gp.packed, prs, pv + hh * (hoff / 64u) * 4u, uint32_t(j) * prow);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[8 * hh + e] = decode(k[8 * hh + e], gp.m, gp.s);
+        if (RESID) o[8 * hh + e] = r[8 * hh + e] + round_bf16(o[8 * hh + e]);
+      }
     }
+    buf_st32<kCacheStream>(pack_codes8_u8(k), crs, cv, uint32_t(j) * crow);
+    buf_st32<kCacheStream>(pack_codes8_u8(k + 8), crs, cv + hoff / 2u, uint32_t(j) * crow);
     buf_st128(pack8(o), rrs, xv, uint32_t(p) * xrow);
-    buf_st128(pack8(o + 8), rrs, xv + 16u, uint32_t(p) * xrow);
+    buf_st128(pack8(o + 8), rrs, xv + 2u * hoff, uint32_t(p) * xrow);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -396,8 +413,8 @@ static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) {
   const int32_t waves = (n + rpw - 1) / rpw;
   return dim3(unsigned((waves + 3) / 4), unsigned(W / 1024));
 }
-static dim3 k_grid(int32_t n, int32_t W) {
-  return dim3(unsigned((n + kGroup - 1) / kGroup), unsigned((W / 8 + 15) / 16));
+static dim3 k_grid(int32_t n, int32_t W) {          // x: 128-channel strips, y: 64-row bands
+  return dim3(unsigned((W / 8 + 15) / 16), unsigned((n + kGroup - 1) / kGroup));
 }
 
 template <bool RESID, bool SPARSE>
@@ -483,7 +500,7 @@ static_assert(sizeof(EncBatch) <= 4096, "a batch travels as kernel arguments (4 
 
 template <bool RESID, bool SPARSE>
 __global__ __launch_bounds__(kThreads) void encode_batch_kernel(EncBatch b) {
-  const uint32_t bid = blockIdx.x;
+  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   int ui = 0;
 #pragma unroll
   for (int i = 1; i < kEncBatch; ++i)
