@@ -353,6 +353,31 @@ def summarize_pmc(dirs):
     return "\n".join(lines)
 
 
+def summarize_trace(trace_dir, warmup, steps, isolated=10):
+    """Per-kernel average durations from a rocprofv3 kernel trace of `bench.py` (default mode):
+    over all calls, and over the calls of the timed region alone (the codec kernels run a fixed
+    number of times per step, so the timed calls are a contiguous slice in dispatch order)."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    per = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            per.setdefault(_short_name(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    total_steps = warmup + steps + isolated
+    lines = [f"{'kernel':52s} {'calls':>6s} {'all_avg_us':>11s} {'timed_avg_us':>13s}"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        v.sort()
+        d = np.array([x for _, x in v])
+        c = len(d) // total_steps               # calls per step; the attention leg's own encodes
+        timed = ""                                # come after the timed region
+        if c >= 1 and len(d) - c * total_steps <= c:
+            timed = f"{d[warmup * c:(warmup + steps) * c].mean():13.2f}"
+        lines.append(f"{name[:52]:52s} {len(d):6d} {d.mean():11.2f} {timed:>13s}")
+    return "\n".join(lines)
+
+
 def read_traffic(symbol):
     """Per-launch HBM bytes of `symbol` from the committed counter summary, or None when there is
     none or it was taken from other sources than the ones built now."""
@@ -390,9 +415,15 @@ def main():
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="print the traffic table from rocprofv3 counter output and exit (no GPU)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel durations (all calls, timed region) from a rocprofv3 kernel trace "
+                         "of a run with the same --warmup/--steps, and exit (no GPU)")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the codec runs per request/layer on a single device); "
