@@ -17,6 +17,11 @@ constexpr int kThreads = 256;
 #define FLK_VWIDE_WAVES 32768
 #endif
 constexpr int kVWideWaves = FLK_VWIDE_WAVES;
+// K block width: compact loops run one or two rounds of blocks, so they take narrower blocks
+// (twice as many, 2 rows per thread) to overlap their load-reduce-store chains; base and dense
+// loops keep 128 channels.
+template <bool SPARSE>
+constexpr int k_block_channels() { return SPARSE ? 64 : 128; }
 
 constexpr uint32_t kDevRows = FLK_DEV_ROWS;
 
@@ -38,13 +43,18 @@ __device__ __forceinline__ uint4 pack8(const float v[8]) {
 
 // ---------------------------------------------------------------------------------------
 // K: groups run down 64 compact rows of one (head, channel).  A block owns one 64-row band
-// of a 128-channel strip of the flattened H*D channel axis.
-// Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs+16, rs+32, rs+48.
-// Extremes: in registers over 4 rows, across the 4 row slots of a wave with lane shuffles,
-// across the 4 waves through LDS; one thread per channel then derives the params.
+// of a 128-channel (64 for compact loops) strip of the flattened H*D channel axis.
+// Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs + slots, ... (4 rows each
+// at 128 channels, 2 at 64).  Extremes: in registers over its rows, across the row slots of a
+// wave with lane shuffles, across the 4 waves through LDS; one thread per channel then derives
+// the params.
 // ---------------------------------------------------------------------------------------
 template <bool RESID, bool SPARSE>
 __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, uint32_t band_) {
+  constexpr int kKCW = k_block_channels<SPARSE>();  // channels per block
+  constexpr int kKChunks = kKCW / 8;                // 8-channel chunks per block row
+  constexpr int kKSlots = kThreads / kKChunks;      // row slots per block
+  constexpr int kKRows = kGroup / kKSlots;          // rows per thread
   const uint16_t* __restrict__ x = a.x;
   const int32_t* __restrict__ rows = a.rows;
   uint16_t* __restrict__ recon = a.recon;
@@ -53,28 +63,28 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   int32_t* __restrict__ tile_start = a.tile_start;
   uint32_t* __restrict__ status = a.status;
   const int32_t n = a.n, T = a.T, W = a.W;
-  __shared__ float s_min[4][128];
-  __shared__ float s_max[4][128];
-  __shared__ float s_m[128], s_s[128], s_rs[128];
+  __shared__ float s_min[4][kKCW];
+  __shared__ float s_max[4][kKCW];
+  __shared__ float s_m[kKCW], s_s[kKCW], s_rs[kKCW];
 
   const int tid = threadIdx.x;
-  const int cc = tid & 15;
-  const int rs = tid >> 4;
+  const int cc = tid % kKChunks;
+  const int rs = tid / kKChunks;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int band = int(band_);
-  const int chunk = int(strip) * 16 + cc;
+  const int chunk = int(strip) * kKChunks + cc;
   const bool cact = chunk < (W >> 3);
   const int64_t ch = int64_t(chunk) * 8;
 
-  float v[4][8];
-  uint4 rv[4];
-  int64_t roff[4];
-  bool ract[4];
+  float v[kKRows][8];
+  uint4 rv[kKRows];
+  int64_t roff[kKRows];
+  bool ract[kKRows];
   bool bad_row = false;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = band * kGroup + rs + 16 * i;
+  for (int i = 0; i < kKRows; ++i) {
+    const int j = band * kGroup + rs + kKSlots * i;
     ract[i] = cact && j < n;
     rv[i] = make_uint4(0, 0, 0, 0);
     roff[i] = 0;
@@ -95,14 +105,14 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   if (SPARSE && bad_row && status) atomicOr(status, kDevRows);
   if (SPARSE && strip == 0 && cc == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = band * kGroup + rs + 16 * i;
+    for (int i = 0; i < kKRows; ++i) {
+      const int j = band * kGroup + rs + kKSlots * i;
       if (j < n) write_tile_index(rows, n, T, j, tile_start);
     }
   }
   if (RESID) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKRows; ++i) {
       float r[8];
       unpack8(rv[i], r);
 #pragma unroll
@@ -114,27 +124,28 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
 #pragma unroll
   for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kKRows; ++i)
     if (ract[i]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) { mn[e] = tmin(mn[e], v[i][e]); mx[e] = tmax(mx[e], v[i][e]); }
     }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mn[e] = tmin(mn[e], __shfl_xor(mn[e], 16));
-    mx[e] = tmax(mx[e], __shfl_xor(mx[e], 16));
-    mn[e] = tmin(mn[e], __shfl_xor(mn[e], 32));
-    mx[e] = tmax(mx[e], __shfl_xor(mx[e], 32));
+  for (int off = kKChunks; off < 64; off *= 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = tmin(mn[e], __shfl_xor(mn[e], off));
+      mx[e] = tmax(mx[e], __shfl_xor(mx[e], off));
+    }
   }
-  if (lane < 16) {
+  if (lane < kKChunks) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) { s_min[wave][cc * 8 + e] = mn[e]; s_max[wave][cc * 8 + e] = mx[e]; }
   }
   __syncthreads();
-  if (tid < 128) {
+  if (tid < kKCW) {
     const float a = tmin(tmin(s_min[0][tid], s_min[1][tid]), tmin(s_min[2][tid], s_min[3][tid]));
     const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
-    const int64_t chan = int64_t(strip) * 128 + tid;
+    const int64_t chan = int64_t(strip) * kKCW + tid;
     GroupParams p = make_params(a, b);
     s_m[tid] = p.m;
     s_s[tid] = p.s;
@@ -154,9 +165,9 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
     gp[e].rs = s_rs[cc * 8 + e];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kKRows; ++i) {
     if (!ract[i]) continue;
-    const int j = band * kGroup + rs + 16 * i;
+    const int j = band * kGroup + rs + kKSlots * i;
     float k[8], out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -413,8 +424,9 @@ static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) {
   const int32_t waves = (n + rpw - 1) / rpw;
   return dim3(unsigned((waves + 3) / 4), unsigned(W / 1024));
 }
-static dim3 k_grid(int32_t n, int32_t W) {          // x: 128-channel strips, y: 64-row bands
-  return dim3(unsigned((W / 8 + 15) / 16), unsigned((n + kGroup - 1) / kGroup));
+static dim3 k_grid(int32_t n, int32_t W, bool sparse) {  // x: channel strips, y: 64-row bands
+  const int chunks = (sparse ? k_block_channels<true>() : k_block_channels<false>()) / 8;
+  return dim3(unsigned((W / 8 + chunks - 1) / chunks), unsigned((n + kGroup - 1) / kGroup));
 }
 
 template <bool RESID, bool SPARSE>
@@ -451,7 +463,7 @@ static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_
 
 template <bool RESID, bool SPARSE>
 static hipError_t launch_k(const EncArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a.n, a.W), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a.n, a.W, SPARSE), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -526,7 +538,7 @@ hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, con
       e.kind = kinds[i];
       dim3 g;
       if (kinds[i] == FLK_KIND_K) {
-        g = k_grid(args[i].n, args[i].W);
+        g = k_grid(args[i].n, args[i].W, sparse);
         e.rpw = 0;
       } else {
         e.rpw = v_wide_rpw(args[i].n, args[i].W);
