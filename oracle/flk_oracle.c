@@ -23,8 +23,15 @@
  *   - group size 64.  K ("kind" 0): a group is up to 64 consecutive compact rows of one
  *     (head, channel).  V ("kind" 1): a group is up to 64 consecutive channels of one
  *     (row, head).  The last group along the axis may be shorter;
+ *   - K group ownership has two forms.  Compact-row groups (the default): up to 64
+ *     consecutive compact rows.  Tile groups ("page-local", asked for by the PR review's
+ *     item 3, "Group ownership vs 16-token pages"): the compact rows whose positions lie in
+ *     one 64-position tile [64t, 64t+64), 0 to 64 of them.  Dense streams are the same in
+ *     both forms;
  *   - params are one uint32 per group: FP16 minimum in the low half, FP16 scale in the
- *     high half.  K params are laid out [ceil(n/64)][H][D], V params [n][H][ceil(D/64)];
+ *     high half.  K params are laid out [ceil(n/64)][H][D] (compact-row groups) or
+ *     [ceil(T/64)][H][D] (tile groups; an empty tile's params are 0), V params
+ *     [n][H][ceil(D/64)];
  *   - codes are two per byte, [row][H][D/2]; byte j of (row, head) holds the code of
  *     channel 2j in its low nibble and channel 2j+1 in its high nibble.
  *
@@ -289,16 +296,107 @@ int orc_dequantize(int kind, int H, int D, int n, const uint8_t* codes, const ui
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* Page-local K groups (PR review, item 3 "Group ownership vs 16-token pages": a K group   */
+/* that follows compact-row order can mix rows of distant positions, so a page cannot be   */
+/* freed, moved or shared alone; the review points to grouping that never merges rows of   */
+/* different logical 64-token groups).  Group t of (head, channel) holds exactly the       */
+/* compact rows whose logical positions lie in [64t, 64t+64).                              */
+/* ------------------------------------------------------------------------------------ */
+
+/* Logical position of compact row j (rows == NULL: the dense identity). */
+static int32_t position_of(const int32_t* rows, int j) { return rows ? rows[j] : j; }
+
+static int check_rows(const int32_t* rows, int n, int T) {
+    if (n < 0 || n > T || (rows == NULL && n != T)) return ORC_E_ARG;
+    for (int j = 0; rows && j < n; ++j)
+        if (rows[j] < 0 || rows[j] >= T || (j > 0 && rows[j] <= rows[j - 1])) return ORC_E_ARG;
+    return ORC_OK;
+}
+
+size_t orc_k_tile_params_bytes(int H, int D, int T) {
+    return 4 * ceil_div((size_t)T, ORC_GROUP) * (size_t)H * (size_t)D;
+}
+
+/* Quantize K rows x [n, H, D] (compact row j at position rows[j]) with tile groups.
+ * params: [ceil(T/64)][H][D]; an empty tile gets params 0 (no group to describe).      */
+int orc_quantize_k_tiles(int H, int D, int T, int n, const int32_t* rows, const uint16_t* x,
+                         uint8_t* codes, uint32_t* params, int f32_params) {
+    int st = check_shape(0, H, D, n);
+    if (st) return st;
+    if (T < 1) return ORC_E_ARG;
+    st = check_rows(rows, n, T);
+    if (st) return st;
+    int ntiles = (T + ORC_GROUP - 1) / ORC_GROUP;
+    int members[ORC_GROUP];
+    float vals[ORC_GROUP];
+    uint8_t gc[ORC_GROUP];
+    memset(codes, 0, orc_codes_bytes(H, D, n));
+    for (int t = 0; t < ntiles; ++t) {
+        /* the group's members: every compact row whose position falls in tile t */
+        int len = 0;
+        for (int j = 0; j < n; ++j)
+            if (position_of(rows, j) / ORC_GROUP == t) members[len++] = j;
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < D; ++c) {
+                size_t pi = ((size_t)t * (size_t)H + (size_t)h) * (size_t)D + (size_t)c;
+                if (len == 0) { params[pi] = 0; continue; }
+                for (int i = 0; i < len; ++i) vals[i] = orc_f32_from_bf16(x[xidx(H, D, members[i], h, c)]);
+                uint16_t m16, s16;
+                st = quantize_group(vals, len, f32_params, &m16, &s16, gc);
+                if (st) return st;
+                params[pi] = (uint32_t)m16 | ((uint32_t)s16 << 16);
+                for (int i = 0; i < len; ++i) put_code(codes, H, D, members[i], h, c, gc[i]);
+            }
+    }
+    return ORC_OK;
+}
+
+/* Dequantize tile-grouped K: row j reads the params of the tile holding its position. */
+int orc_dequantize_k_tiles(int H, int D, int T, int n, const int32_t* rows, const uint8_t* codes,
+                           const uint32_t* params, uint16_t* xhat) {
+    int st = check_shape(0, H, D, n);
+    if (st) return st;
+    if (T < 1) return ORC_E_ARG;
+    st = check_rows(rows, n, T);
+    if (st) return st;
+    for (int j = 0; j < n; ++j) {
+        size_t t = (size_t)(position_of(rows, j) / ORC_GROUP);
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < D; ++c)
+                xhat[xidx(H, D, j, h, c)] =
+                    dequant_one(params[(t * (size_t)H + (size_t)h) * (size_t)D + (size_t)c],
+                                get_code(codes, H, D, j, h, c));
+    }
+    return ORC_OK;
+}
+
+/* The quantizer and dequantizer of a stream: K with tile groups when k_tiles != 0, else the
+ * grouping of `kind` over the compact rows. */
+static int quantize_stream(int kind, int k_tiles, int H, int D, int T, int n, const int32_t* rows,
+                           const uint16_t* x, uint8_t* codes, uint32_t* params, int f32_params) {
+    if (kind == 0 && k_tiles) return orc_quantize_k_tiles(H, D, T, n, rows, x, codes, params, f32_params);
+    return orc_quantize(kind, H, D, n, x, codes, params, f32_params);
+}
+
+static int dequantize_stream(int kind, int k_tiles, int H, int D, int T, int n, const int32_t* rows,
+                             const uint8_t* codes, const uint32_t* params, uint16_t* xhat) {
+    if (kind == 0 && k_tiles) return orc_dequantize_k_tiles(H, D, T, n, rows, codes, params, xhat);
+    return orc_dequantize(kind, H, D, n, codes, params, xhat);
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* Base and cross-loop residuals (RFC section 3.3).                                      */
 /* ------------------------------------------------------------------------------------ */
 
 /* X_hat[1] = dequantize(quantize(X[1])) over all T positions (loop 1 is always dense,
- * RFC section 3.1).  Writes the packed base and recon = X_hat[1]. */
+ * RFC section 3.1).  Writes the packed base and recon = X_hat[1].  k_tiles selects tile
+ * groups for K (a dense stream's tile groups are its compact-row groups). */
 int orc_encode_base(int kind, int H, int D, int T, const uint16_t* x, uint8_t* codes,
-                    uint32_t* params, uint16_t* recon, int f32_params) {
-    int st = orc_quantize(kind, H, D, T, x, codes, params, f32_params);
+                    uint32_t* params, uint16_t* recon, int f32_params, int k_tiles) {
+    if (T < 1) return ORC_E_ARG;
+    int st = quantize_stream(kind, k_tiles, H, D, T, T, NULL, x, codes, params, f32_params);
     if (st) return st;
-    return orc_dequantize(kind, H, D, T, codes, params, recon);
+    return dequantize_stream(kind, k_tiles, H, D, T, T, NULL, codes, params, recon);
 }
 
 /* Loop r >= 2.  rows == NULL means dense (n == T, compact row j is position j); otherwise
@@ -306,21 +404,19 @@ int orc_encode_base(int kind, int H, int D, int T, const uint16_t* x, uint8_t* c
  * row map), and x_rows holds X[r] at those positions only.
  *   delta[j]          = bf16(X[r][j] - X_hat[r-1][rows[j]])      (subtract the RECONSTRUCTED
  *                                                                  predecessor)
- *   delta_hat         = dequantize(quantize(delta))               (K groups over compact j)
+ *   delta_hat         = dequantize(quantize(delta))               (K groups over compact j,
+ *                                                                  or per tile if k_tiles)
  *   X_hat[r][rows[j]] = bf16(X_hat[r-1][rows[j]] + delta_hat[j])
  *   X_hat[r][p]       = X_hat[r-1][p] for every p not in rows      (absent = inherit)
  * recon holds X_hat[r-1] on entry and X_hat[r] on return.  Subtraction and addition are
  * carried out in binary32 and rounded to BF16, the compute dtype (PR #166 "Purpose").  */
 int orc_encode_residual(int kind, int H, int D, int T, int n, const int32_t* rows,
                         const uint16_t* x_rows, uint16_t* recon, uint8_t* codes, uint32_t* params,
-                        int f32_params) {
+                        int f32_params, int k_tiles) {
     int st = check_shape(kind, H, D, n);
     if (st) return st;
-    if (n > T || (rows == NULL && n != T)) return ORC_E_ARG;
-    for (int j = 0; j < n; ++j) {
-        if (rows == NULL) break;
-        if (rows[j] < 0 || rows[j] >= T || (j > 0 && rows[j] <= rows[j - 1])) return ORC_E_ARG;
-    }
+    st = check_rows(rows, n, T);
+    if (st) return st;
     size_t W = (size_t)H * (size_t)D;
     uint16_t* delta = (uint16_t*)malloc(((size_t)n * W + 1) * sizeof(uint16_t));
     uint16_t* dhat = (uint16_t*)malloc(((size_t)n * W + 1) * sizeof(uint16_t));
@@ -334,8 +430,8 @@ int orc_encode_residual(int kind, int H, int D, int T, int n, const int32_t* row
             delta[(size_t)j * W + e] = orc_bf16_from_f32(d);
         }
     }
-    st = orc_quantize(kind, H, D, n, delta, codes, params, f32_params);
-    if (!st) st = orc_dequantize(kind, H, D, n, codes, params, dhat);
+    st = quantize_stream(kind, k_tiles, H, D, T, n, rows, delta, codes, params, f32_params);
+    if (!st) st = dequantize_stream(kind, k_tiles, H, D, T, n, rows, codes, params, dhat);
     if (!st) {
         for (int j = 0; j < n; ++j) {
             int p = rows ? rows[j] : j;
@@ -359,20 +455,22 @@ int orc_encode_residual(int kind, int H, int D, int T, int n, const int32_t* row
  * Stream l (0 = base) has n_rows[l] rows, rows_list[l] (NULL = dense), codes and params. */
 int orc_reconstruct(int kind, int H, int D, int T, int n_loops, const int32_t* n_rows,
                     const int32_t* const* rows_list, const uint8_t* const* codes_list,
-                    const uint32_t* const* params_list, uint16_t* out) {
+                    const uint32_t* const* params_list, uint16_t* out, int k_tiles) {
     int st = check_shape(kind, H, D, T);
     if (st) return st;
-    if (n_loops < 1 || n_rows[0] != T || rows_list[0] != NULL) return ORC_E_ARG;
+    if (T < 1 || n_loops < 1 || n_rows[0] != T || rows_list[0] != NULL) return ORC_E_ARG;
     size_t W = (size_t)H * (size_t)D;
-    st = orc_dequantize(kind, H, D, T, codes_list[0], params_list[0], out);
+    st = dequantize_stream(kind, k_tiles, H, D, T, T, NULL, codes_list[0], params_list[0], out);
     if (st) return st;
     for (int l = 1; l < n_loops; ++l) {
         int n = n_rows[l];
         const int32_t* rows = rows_list[l];
-        if (n > T || (rows == NULL && n != T)) return ORC_E_ARG;
+        st = check_rows(rows, n, T);
+        if (st) return st;
         uint16_t* dhat = (uint16_t*)malloc(((size_t)n * W + 1) * sizeof(uint16_t));
         if (!dhat) return ORC_E_ARG;
-        orc_dequantize(kind, H, D, n, codes_list[l], params_list[l], dhat);
+        st = dequantize_stream(kind, k_tiles, H, D, T, n, rows, codes_list[l], params_list[l], dhat);
+        if (st) { free(dhat); return st; }
         for (int j = 0; j < n; ++j) {
             int p = rows ? rows[j] : j;
             for (size_t e = 0; e < W; ++e) {

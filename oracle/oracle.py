@@ -10,8 +10,9 @@ section 3.3, and in vllm-rlt pull request #166 ("Purpose" and the review's forma
 
 Array conventions: BF16 tensors are numpy ``uint16`` arrays of bit patterns shaped
 ``[rows, H, D]``; codes are ``uint8`` ``[rows, H, D//2]``; params are ``uint32`` (FP16
-minimum in the low half, FP16 scale in the high half), ``[ceil(rows/64), H, D]`` for K and
-``[rows, H, ceil(D/64)]`` for V; ``rows`` are ascending ``int32`` positions or ``None``.
+minimum in the low half, FP16 scale in the high half), ``[ceil(rows/64), H, D]`` for K,
+``[ceil(T/64), H, D]`` for K with tile (page-local) groups and ``[rows, H, ceil(D/64)]``
+for V; ``rows`` are ascending ``int32`` positions or ``None``.
 """
 from __future__ import annotations
 
@@ -89,11 +90,17 @@ def lib() -> ctypes.CDLL:
         L.orc_dequantize.restype = i
         L.orc_dequantize.argtypes = [i, i, i, i, P, P, P]
         L.orc_encode_base.restype = i
-        L.orc_encode_base.argtypes = [i, i, i, i, P, P, P, P, i]
+        L.orc_encode_base.argtypes = [i, i, i, i, P, P, P, P, i, i]
         L.orc_encode_residual.restype = i
-        L.orc_encode_residual.argtypes = [i, i, i, i, i, P, P, P, P, P, i]
+        L.orc_encode_residual.argtypes = [i, i, i, i, i, P, P, P, P, P, i, i]
         L.orc_reconstruct.restype = i
-        L.orc_reconstruct.argtypes = [i, i, i, i, i, P, P, P, P, P]
+        L.orc_reconstruct.argtypes = [i, i, i, i, i, P, P, P, P, P, i]
+        L.orc_quantize_k_tiles.restype = i
+        L.orc_quantize_k_tiles.argtypes = [i, i, i, i, P, P, P, P, i]
+        L.orc_dequantize_k_tiles.restype = i
+        L.orc_dequantize_k_tiles.argtypes = [i, i, i, i, P, P, P, P]
+        L.orc_k_tile_params_bytes.restype = sz
+        L.orc_k_tile_params_bytes.argtypes = [i, i, i]
         L.orc_tile_index.restype = i
         L.orc_tile_index.argtypes = [P, i, i, P]
         L.orc_decode_attn.restype = i
@@ -155,8 +162,15 @@ def rows_bytes(n: int, sparse: bool) -> int:
     return int(lib().orc_rows_bytes(n, 1 if sparse else 0))
 
 
-def params_shape(kind: int, H: int, D: int, n: int):
+def params_shape(kind: int, H: int, D: int, n: int, T: Optional[int] = None, k_tiles: bool = False):
+    """K with tile groups has one parameter row per 64-position tile of the T positions."""
+    if kind == K and k_tiles:
+        return ((T + GROUP - 1) // GROUP, H, D)
     return ((n + GROUP - 1) // GROUP, H, D) if kind == K else (n, H, (D + GROUP - 1) // GROUP)
+
+
+def k_tile_params_bytes(H: int, D: int, T: int) -> int:
+    return int(lib().orc_k_tile_params_bytes(H, D, T))
 
 
 # ----------------------------------------------------------------------------- codec
@@ -196,20 +210,45 @@ def dequantize(kind: int, codes: np.ndarray, params: np.ndarray, D: int) -> np.n
     return out
 
 
-def encode_base(kind: int, x: np.ndarray, f32_params: bool = False):
+def quantize_k_tiles(x: np.ndarray, rows: Optional[np.ndarray], T: int, f32_params: bool = False):
+    """K rows x [n, H, D] at positions rows (None = 0..n-1) with tile groups: one group per
+    (64-position tile, head, channel).  Returns codes [n, H, D//2], params [ceil(T/64), H, D]."""
+    x = _c(x, np.uint16)
+    n, H, D = x.shape
+    rows_c = None if rows is None else _c(rows, np.int32)
+    codes = np.zeros((n, H, D // 2), np.uint8)
+    params = np.zeros(params_shape(K, H, D, n, T, True), np.uint32)
+    _check(lib().orc_quantize_k_tiles(H, D, T, n, _p(rows_c), _p(x), _p(codes), _p(params), int(f32_params)),
+           "quantize_k_tiles")
+    return codes, params
+
+
+def dequantize_k_tiles(codes: np.ndarray, params: np.ndarray, rows: Optional[np.ndarray], T: int,
+                       D: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    params = _c(params, np.uint32)
+    n, H = codes.shape[0], codes.shape[1]
+    rows_c = None if rows is None else _c(rows, np.int32)
+    out = np.zeros((n, H, D), np.uint16)
+    _check(lib().orc_dequantize_k_tiles(H, D, T, n, _p(rows_c), _p(codes), _p(params), _p(out)),
+           "dequantize_k_tiles")
+    return out
+
+
+def encode_base(kind: int, x: np.ndarray, f32_params: bool = False, k_tiles: bool = False):
     """Returns (Stream, recon) with recon = X_hat[1] as BF16 bits."""
     x = _c(x, np.uint16)
     T, H, D = x.shape
     codes = np.zeros((T, H, D // 2), np.uint8)
-    params = np.zeros(params_shape(kind, H, D, T), np.uint32)
+    params = np.zeros(params_shape(kind, H, D, T, T, k_tiles), np.uint32)
     recon = np.zeros_like(x)
-    _check(lib().orc_encode_base(kind, H, D, T, _p(x), _p(codes), _p(params), _p(recon), int(f32_params)),
-           "encode_base")
+    _check(lib().orc_encode_base(kind, H, D, T, _p(x), _p(codes), _p(params), _p(recon), int(f32_params),
+                                 int(k_tiles)), "encode_base")
     return Stream(T, None, codes, params), recon
 
 
 def encode_residual(kind: int, x_rows: np.ndarray, rows: Optional[np.ndarray], recon: np.ndarray,
-                    f32_params: bool = False) -> Stream:
+                    f32_params: bool = False, k_tiles: bool = False) -> Stream:
     """Encode one residual loop; `recon` (X_hat[r-1]) is updated in place to X_hat[r]."""
     x_rows = _c(x_rows, np.uint16)
     assert recon.dtype == np.uint16 and recon.flags.c_contiguous
@@ -217,13 +256,13 @@ def encode_residual(kind: int, x_rows: np.ndarray, rows: Optional[np.ndarray], r
     T = recon.shape[0]
     rows_c = None if rows is None else _c(rows, np.int32)
     codes = np.zeros((n, H, D // 2), np.uint8)
-    params = np.zeros(params_shape(kind, H, D, n), np.uint32)
+    params = np.zeros(params_shape(kind, H, D, n, T, k_tiles), np.uint32)
     _check(lib().orc_encode_residual(kind, H, D, T, n, _p(rows_c), _p(x_rows), _p(recon), _p(codes),
-                                     _p(params), int(f32_params)), "encode_residual")
+                                     _p(params), int(f32_params), int(k_tiles)), "encode_residual")
     return Stream(n, rows_c, codes, params)
 
 
-def reconstruct(kind: int, chain: Sequence[Stream], T: int, H: int, D: int) -> np.ndarray:
+def reconstruct(kind: int, chain: Sequence[Stream], T: int, H: int, D: int, k_tiles: bool = False) -> np.ndarray:
     n_loops = len(chain)
     n_rows = np.array([s.n_rows for s in chain], np.int32)
     keep = [(s.rows, _c(s.codes, np.uint8), _c(s.params, np.uint32)) for s in chain]
@@ -233,19 +272,19 @@ def reconstruct(kind: int, chain: Sequence[Stream], T: int, H: int, D: int) -> n
     params_arr = (P * n_loops)(*[_p(p).value for _, _, p in keep])
     out = np.zeros((T, H, D), np.uint16)
     _check(lib().orc_reconstruct(kind, H, D, T, n_loops, _p(n_rows), rows_arr, codes_arr, params_arr,
-                                 _p(out)), "reconstruct")
+                                 _p(out), int(k_tiles)), "reconstruct")
     return out
 
 
 def encode_chain(kind: int, xs: Sequence[np.ndarray], rows_list: Sequence[Optional[np.ndarray]],
-                 f32_params: bool = False):
+                 f32_params: bool = False, k_tiles: bool = False):
     """Encode a full loop chain.  xs[0] is X[1] over all T rows; xs[r] (r >= 1) holds X[r+1]
     at the positions rows_list[r] (all T rows when that entry is None).  Returns the list of
     Streams and the final in-place reconstruction X_hat[R]."""
-    base, recon = encode_base(kind, xs[0], f32_params)
+    base, recon = encode_base(kind, xs[0], f32_params, k_tiles)
     chain: List[Stream] = [base]
     for x, rows in zip(xs[1:], rows_list[1:]):
-        chain.append(encode_residual(kind, x, rows, recon, f32_params))
+        chain.append(encode_residual(kind, x, rows, recon, f32_params, k_tiles))
     return chain, recon
 
 
@@ -268,3 +307,28 @@ def decode_attn(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, softmax_scale
     _check(lib().orc_decode_attn(Hq, Hkv, D, T, _p(q), _p(khat), _p(vhat), float(softmax_scale), _p(out)),
            "decode_attn")
     return out
+
+
+# ----------------------------------------------------------------------------- rolling tail
+
+def rolling_prefix(n_tokens: int) -> int:
+    """Positions a rolling cache of n_tokens holds packed; the rest stay in the BF16 tail.
+
+    RFC section 3.3 (last paragraph): the rolling tail keeps at least 64 recent tokens and
+    flushes whole 64-token groups, so after a step it holds 64 to 127 tokens.  Written as the
+    rule itself: the packed prefix is the largest whole number of 64-token groups that still
+    leaves 64 tokens in the tail (none while fewer than 128 tokens exist)."""
+    prefix = 0
+    while n_tokens - (prefix + GROUP) >= GROUP:
+        prefix += GROUP
+    return prefix
+
+
+def decode_attn_rolling(q: np.ndarray, khat_prefix: np.ndarray, vhat_prefix: np.ndarray,
+                        k_tail: np.ndarray, v_tail: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Attention of one query over a rolling cache: the packed prefix's reconstruction
+    followed by the BF16 tail (RFC section 3.3: the recent BF16 tail stays part of the
+    cache).  Plain concatenation of the two token ranges, then textbook attention."""
+    khat = np.concatenate([khat_prefix, k_tail], axis=0)
+    vhat = np.concatenate([vhat_prefix, v_tail], axis=0)
+    return decode_attn(q, khat, vhat, softmax_scale)
