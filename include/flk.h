@@ -39,7 +39,11 @@
  *  codes   uint8 [n][H][D/2]: byte j of (row, head) holds channel 2j in its low nibble and
  *          channel 2j+1 in its high nibble (PR #166 lists nibble order among its tests).
  *  params  uint32, one per group: FP16 minimum in bits 0..15, FP16 scale in bits 16..31.
- *          K: [ceil(n/64)][H][D]  (group g of channel (h, c) covers compact rows 64g..64g+63).
+ *          K, compact-row groups (FLK_KGROUP_ROWS): [ceil(n/64)][H][D], group g of channel
+ *          (h, c) covers compact rows 64g..64g+63.
+ *          K, tile groups (FLK_KGROUP_TILE): [ceil(T/64)][H][D], group t of channel (h, c)
+ *          covers the compact rows whose positions lie in [64t, 64t+64) (0 to 64 rows; an
+ *          empty tile's params are 0).  A dense stream is the same in both forms.
  *          V: [n][H][ceil(D/64)]  (group g of (row, h) covers channels 64g..64g+63).
  *          The last group along the axis may be partial (statistics over its real elements).
  *  rows    int32 [n], ascending logical positions of the compact rows (compact row ->
@@ -69,7 +73,7 @@
 extern "C" {
 #endif
 
-#define FLK_ABI_VERSION 1
+#define FLK_ABI_VERSION 2
 #define FLK_GROUP 64       /* group size (PR #166 "Purpose": default group size 64)        */
 #define FLK_MAX_LOOPS 8    /* longest chain (base + residuals) one call accepts             */
 #define FLK_MAX_HEAD_DIM 512
@@ -92,6 +96,17 @@ enum { FLK_FMT_INT4_AFFINE = 1 };
 enum { FLK_PARAM_FP16_MIN_SCALE = 1 };
 enum { FLK_NIBBLE_LOW_EVEN = 1 };
 
+/* Who owns a K group (the PR #166 review, item 3 "Group ownership vs 16-token pages": K
+ * groups that follow compact-row order can put rows of distant positions, on different
+ * pages, under one minimum and scale, so no page can be freed, offloaded, transferred or
+ * shared without re-encoding its group).
+ *   FLK_KGROUP_ROWS  64 consecutive compact rows (the default; the fewest groups).
+ *   FLK_KGROUP_TILE  the compact rows of one 64-position tile, i.e. of four whole 16-token
+ *                    pages: a tile's codes and params depend on that tile's tokens alone,
+ *                    and whole tiles can be appended to a stream (flk_append_residual).
+ * V groups lie within one token row, so they are page-local in either form. */
+enum { FLK_KGROUP_ROWS = 0, FLK_KGROUP_TILE = 1 };
+
 /* Bits of the optional device status word (a uint32 in device memory the caller zeroes).
  * Encode kernels OR these in with a device atomic; they never clear it. */
 #define FLK_DEV_NONFINITE 1u  /* a group held an Inf or NaN value                           */
@@ -109,6 +124,8 @@ typedef struct flk_desc {
     uint8_t nibble_order;   /* FLK_NIBBLE_LOW_EVEN                                         */
     int32_t n_heads;        /* H >= 1                                                      */
     int32_t head_dim;       /* D: 8 <= D <= FLK_MAX_HEAD_DIM, D % 8 == 0                   */
+    uint8_t k_grouping;     /* FLK_KGROUP_ROWS or FLK_KGROUP_TILE (no effect on V)         */
+    uint8_t reserved[3];    /* must be 0                                                   */
 } flk_desc;
 
 /* One encoded loop of one tensor, as the host describes it to the library.  The struct is
@@ -125,7 +142,8 @@ typedef struct flk_stream {
 
 /* ---------------------------------------------------------------- host-only helpers --- */
 
-/* Fill a descriptor with the only format this ABI version defines. */
+/* Fill a descriptor with the only format this ABI version defines and compact-row K groups
+ * (set k_grouping afterwards to choose tile groups). */
 void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
 /* FLK_OK if the descriptor is well formed, else FLK_E_NULL / FLK_E_DESC / FLK_E_SHAPE. */
@@ -134,12 +152,26 @@ flk_status flk_desc_check(const flk_desc* d);
 /* Storage of one stream with n compact rows (the RFC, section 7.4: the allocator budgets
  * payload, quantization parameters and maps).  0 for a malformed descriptor or n < 0.   */
 size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows);   /* n*H*D/2                    */
-size_t flk_params_bytes(const flk_desc* d, int32_t n_rows);  /* 4 * number of groups       */
+size_t flk_params_bytes(const flk_desc* d, int32_t n_rows, int32_t T); /* 4 * groups; T is
+                                       the stream's positions (read for tile-grouped K only) */
 size_t flk_rows_bytes(int32_t n_rows, int sparse);            /* 4*n if sparse, else 0      */
 size_t flk_tile_index_bytes(int32_t T);                       /* 4*(ceil(T/64) + 1)         */
+/* Everything one stream stores: codes + params + rows + tile index (sparse streams), with
+ * the padding of partially filled groups and, for tile-grouped K, one parameter row per
+ * tile whatever its occupancy (the RFC, section 7.4: small residual streams pay for their
+ * partially filled groups; resource queries report the format's actual cost). */
+size_t flk_stream_bytes(const flk_desc* d, int32_t n_rows, int32_t T, int sparse);
 
-/* Workspace of flk_decode_attn_packed for a T-token cache and n_q_heads query heads (other
- * calls need none).  0 for malformed arguments. */
+/* Rolling BF16 tail (the RFC, section 3.3, last paragraph: the tail keeps at least 64 recent
+ * tokens and flushes whole 64-token groups, so it holds 64 to 127 tokens after a step).
+ * Returns how many leading positions of an n_tokens sequence a rolling cache keeps packed:
+ * the largest multiple of 64 that leaves at least 64 tokens in the tail (0 below 128
+ * tokens, and 0 for n_tokens < 0).  Positions [prefix, n_tokens) stay in BF16. */
+int32_t flk_rolling_prefix(int32_t n_tokens);
+
+/* Workspace of flk_decode_attn_packed and flk_decode_attn_rolling for a cache of T packed
+ * tokens (T >= 0) and n_q_heads query heads (other calls need none).  0 for malformed
+ * arguments. */
 size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads);
 
 const char* flk_status_string(flk_status s);
@@ -199,6 +231,59 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
                                   const flk_stream* v_chain, int32_t n_loops,
                                   float softmax_scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Appending whole tiles: the flush of a rolling BF16 tail (the RFC, section 3.3, last
+ * paragraph).  Decode-time tokens stay in BF16 until a whole 64-token group can leave the
+ * tail; the flush encodes positions [p0, p0 + n_pos) of every loop and appends them to
+ * streams that already hold positions [0, p0).  Because groups never straddle a tile (V
+ * groups lie in one row; K groups are tile groups, or dense), the streams afterwards are
+ * exactly those of encoding [0, p0 + n_pos) in one call, and the bytes already written are
+ * never touched.
+ * Common rules: p0 and n_pos are multiples of 64, n_pos >= 64, and (p0 + n_pos)*H*D < 2^31.
+ * codes / params / tile_start point at the START of the stream's buffers, which must hold
+ * the stream after the append (flk_codes_bytes(d, rows_before + n_rows), flk_params_bytes(
+ * d, rows_before + n_rows, p0 + n_pos), flk_tile_index_bytes(p0 + n_pos)); the call writes
+ * only the window's part of them.  recon is the window's own reconstruction, BF16
+ * [n_pos, H, D]: row i is position p0 + i.
+ * --------------------------------------------------------------------------------------- */
+
+/* Loop 1 of the window: x is X[1] at positions [p0, p0 + n_pos), BF16 [n_pos, H, D]; recon
+ * receives X_hat[1] of the window.  Writes codes rows p0.. and the window's params.
+ * Errors: those of flk_encode_base, plus FLK_E_SHAPE for p0 or n_pos not as above.      */
+flk_status flk_append_base(const flk_desc* d, const void* x, int32_t p0, int32_t n_pos, uint8_t* codes,
+                           uint32_t* params, void* recon, uint32_t* dev_status, void* stream);
+
+/* Loop r >= 2 of the window.  rows: device int32 [n_rows], the stream's row entries for the
+ * window -- ascending absolute positions in [p0, p0 + n_pos) -- or NULL for a dense loop
+ * (n_rows == n_pos, rows_before == p0).  rows_before: the stream's compact rows at
+ * positions < p0 (rows_before <= p0).  x_rows: BF16 [n_rows, H, D], X[r] at those rows.
+ * recon: X_hat[r-1] of the window on entry, X_hat[r] on exit.  A compact loop writes
+ * codes rows rows_before.., its tile parameters (tile-grouped K) or row parameters (V), and
+ * tile_start[p0/64 .. (p0+n_pos)/64] = rows_before + (rows of the window below each tile).
+ * n_rows == 0 writes only those tile_start entries and, for K, zero params of the window's
+ * tiles.  Compact K loops need k_grouping == FLK_KGROUP_TILE (compact-row groups would
+ * have to merge with the stream's last, partially filled group): FLK_E_UNSUPPORTED
+ * otherwise.
+ * Errors: those of flk_encode_residual, plus FLK_E_SHAPE for a window or rows_before out
+ * of range, FLK_E_UNSUPPORTED as above.                                                  */
+flk_status flk_append_residual(const flk_desc* d, const void* x_rows, const int32_t* rows, int32_t n_rows,
+                               int32_t p0, int32_t n_pos, int32_t rows_before, void* recon, uint8_t* codes,
+                               uint32_t* params, int32_t* tile_start, uint32_t* dev_status, void* stream);
+
+/* Decode attention over a rolling cache: the packed chains hold positions [0, T) (T may be
+ * 0, then the chains are not read) and the BF16 tail holds positions [T, T + tail_len)
+ * (RFC section 3.3: the recent BF16 tail is part of the cache).  k_tail / v_tail: BF16
+ * [tail_len, H, D] at the final depth (each token's last-exited version).  Otherwise as
+ * flk_decode_attn_packed; T + tail_len >= 1; workspace >= flk_attn_workspace_bytes(k_desc,
+ * T, n_q_heads).
+ * Errors: those of flk_decode_attn_packed, plus FLK_E_NULL for a missing tail with
+ * tail_len > 0.                                                                            */
+flk_status flk_decode_attn_rolling(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T, const void* q,
+                                   int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                   int32_t n_loops, const void* k_tail, const void* v_tail, int32_t tail_len,
+                                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Batched calls.  A serving step encodes or rebuilds many tensors at once -- every layer's K

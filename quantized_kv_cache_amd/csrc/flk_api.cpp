@@ -24,9 +24,33 @@ flk_status check_stream_ptrs(const void* codes, const void* params) {
   return FLK_OK;
 }
 
-size_t n_groups(const flk_desc* d, int64_t n) {
-  if (d->kind == FLK_KIND_K) return size_t((n + FLK_GROUP - 1) / FLK_GROUP) * size_t(d->n_heads) * size_t(d->head_dim);
+bool k_tiles(const flk_desc* d) { return d->kind == FLK_KIND_K && d->k_grouping == FLK_KGROUP_TILE; }
+
+// Groups of a stream of n compact rows over T positions: K has one parameter row per 64
+// compact rows, or per 64-position tile with tile groups; V one per (row, head, 64 channels).
+size_t n_groups(const flk_desc* d, int64_t n, int64_t T) {
+  const size_t W = size_t(d->n_heads) * size_t(d->head_dim);
+  if (k_tiles(d)) return T < 1 ? 0 : size_t((T + FLK_GROUP - 1) / FLK_GROUP) * W;
+  if (d->kind == FLK_KIND_K) return size_t((n + FLK_GROUP - 1) / FLK_GROUP) * W;
   return size_t(n) * size_t(d->n_heads) * size_t((d->head_dim + FLK_GROUP - 1) / FLK_GROUP);
+}
+
+// The window part of a stream's buffers: codes and params of the rows (and, for tile-grouped
+// K, tiles) before position p0, which hold rows_before compact rows.
+size_t codes_offset(const flk_desc* d, int64_t rows_before) {
+  return size_t(rows_before) * size_t(d->n_heads) * size_t(d->head_dim) / 2;
+}
+size_t params_offset(const flk_desc* d, int64_t rows_before, int64_t p0) {
+  const size_t W = size_t(d->n_heads) * size_t(d->head_dim);
+  if (d->kind == FLK_KIND_K) return k_tiles(d) ? size_t(p0 / FLK_GROUP) * W : size_t(rows_before / FLK_GROUP) * W;
+  return size_t(rows_before) * size_t(d->n_heads) * size_t((d->head_dim + FLK_GROUP - 1) / FLK_GROUP);
+}
+
+flk::EncArgs enc_args(const flk_desc* d, const void* x, const int32_t* rows, int32_t n, int32_t T, void* recon,
+                      uint8_t* codes, uint32_t* params, int32_t* tile_start, uint32_t* status) {
+  return flk::EncArgs{static_cast<const uint16_t*>(x), rows, static_cast<uint16_t*>(recon), codes, params,
+                      rows ? tile_start : nullptr, status, n, T, d->n_heads * d->head_dim, 0, 0,
+                      k_tiles(d) ? 1 : 0};
 }
 
 // Every BF16 tensor of a call stays below 4 GiB (n*H*D < 2^31 elements): the kernels address
@@ -62,6 +86,7 @@ flk_status load_chain(const flk_desc* d, int32_t T, const flk_stream* chain, int
     ++kept;
   }
   out->n_loops = kept;
+  out->ktile = k_tiles(d) ? 1 : 0;
   return FLK_OK;
 }
 
@@ -80,13 +105,16 @@ void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim) {
   d->nibble_order = FLK_NIBBLE_LOW_EVEN;
   d->n_heads = n_heads;
   d->head_dim = head_dim;
+  d->k_grouping = FLK_KGROUP_ROWS;
 }
 
 flk_status flk_desc_check(const flk_desc* d) {
   if (!d) return FLK_E_NULL;
   if (d->abi_version != FLK_ABI_VERSION || d->format != FLK_FMT_INT4_AFFINE ||
       (d->kind != FLK_KIND_K && d->kind != FLK_KIND_V) || d->group != FLK_GROUP ||
-      d->param_dtype != FLK_PARAM_FP16_MIN_SCALE || d->nibble_order != FLK_NIBBLE_LOW_EVEN)
+      d->param_dtype != FLK_PARAM_FP16_MIN_SCALE || d->nibble_order != FLK_NIBBLE_LOW_EVEN ||
+      (d->k_grouping != FLK_KGROUP_ROWS && d->k_grouping != FLK_KGROUP_TILE) || d->reserved[0] != 0 ||
+      d->reserved[1] != 0 || d->reserved[2] != 0)
     return FLK_E_DESC;
   if (d->n_heads < 1 || d->head_dim < 8 || d->head_dim > FLK_MAX_HEAD_DIM || d->head_dim % 8 != 0)
     return FLK_E_SHAPE;
@@ -99,9 +127,9 @@ size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows) {
   return size_t(n_rows) * size_t(d->n_heads) * size_t(d->head_dim) / 2;
 }
 
-size_t flk_params_bytes(const flk_desc* d, int32_t n_rows) {
+size_t flk_params_bytes(const flk_desc* d, int32_t n_rows, int32_t T) {
   if (flk_desc_check(d) != FLK_OK || n_rows < 0) return 0;
-  return 4 * n_groups(d, n_rows);
+  return 4 * n_groups(d, n_rows, T);
 }
 
 size_t flk_rows_bytes(int32_t n_rows, int sparse) {
@@ -114,8 +142,19 @@ size_t flk_tile_index_bytes(int32_t T) {
   return 4 * (size_t((T + FLK_GROUP - 1) / FLK_GROUP) + 1);
 }
 
+size_t flk_stream_bytes(const flk_desc* d, int32_t n_rows, int32_t T, int sparse) {
+  if (flk_desc_check(d) != FLK_OK || n_rows < 0 || T < 1 || n_rows > T) return 0;
+  return flk_codes_bytes(d, n_rows) + flk_params_bytes(d, n_rows, T) +
+         (sparse ? flk_rows_bytes(n_rows, 1) + flk_tile_index_bytes(T) : 0);
+}
+
+int32_t flk_rolling_prefix(int32_t n_tokens) {
+  if (n_tokens < 2 * FLK_GROUP) return 0;
+  return ((n_tokens - FLK_GROUP) / FLK_GROUP) * FLK_GROUP;
+}
+
 size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads) {
-  if (flk_desc_check(k_desc) != FLK_OK || T < 1 || n_q_heads < 1) return 0;
+  if (flk_desc_check(k_desc) != FLK_OK || T < 0 || n_q_heads < 1) return 0;
   return flk::attn_workspace_bytes(T, k_desc->n_heads, n_q_heads);
 }
 
@@ -144,9 +183,9 @@ flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t*
   st = check_stream_ptrs(codes, params);
   if (st != FLK_OK) return st;
   if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
-  return to_status(flk::launch_encode(d->kind, false, x, nullptr, T, T, d->n_heads, d->head_dim,
-                                      recon, codes, params, nullptr, dev_status,
-                                      static_cast<hipStream_t>(stream)));
+  return to_status(flk::launch_encode(d->kind, false,
+                                      enc_args(d, x, nullptr, T, T, recon, codes, params, nullptr, dev_status),
+                                      d->n_heads, d->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int32_t* rows,
@@ -166,9 +205,10 @@ flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int3
   if (rows && !tile_start) return FLK_E_NULL;
   if (!aligned(x_rows, 16) || (rows && (!aligned(rows, 4) || !aligned(tile_start, 4))))
     return FLK_E_ALIGN;
-  return to_status(flk::launch_encode(d->kind, true, x_rows, rows, n_rows, T, d->n_heads,
-                                      d->head_dim, recon, codes, params, rows ? tile_start : nullptr,
-                                      dev_status, static_cast<hipStream_t>(stream)));
+  return to_status(flk::launch_encode(d->kind, true,
+                                      enc_args(d, x_rows, rows, n_rows, T, recon, codes, params, tile_start,
+                                               dev_status),
+                                      d->n_heads, d->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain, int32_t n_loops,
@@ -208,8 +248,113 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
   const size_t need = flk::attn_workspace_bytes(T, kd->n_heads, n_q_heads);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FLK_E_WORKSPACE;
   if (workspace && !aligned(workspace, 16)) return FLK_E_ALIGN;
-  return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc,
-                                           softmax_scale, out, workspace,
+  return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc, nullptr,
+                                           nullptr, 0, softmax_scale, out, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+// ---- appending whole tiles (rolling-tail flush) --------------------------------------------
+
+namespace {
+
+// The window rules shared by both append calls.
+flk_status check_window(const flk_desc* d, int32_t p0, int32_t n_pos) {
+  if (p0 < 0 || n_pos < FLK_GROUP || p0 % FLK_GROUP != 0 || n_pos % FLK_GROUP != 0) return FLK_E_SHAPE;
+  if (!rows_fit(d, int64_t(p0) + n_pos)) return FLK_E_SHAPE;
+  return FLK_OK;
+}
+
+}  // namespace
+
+flk_status flk_append_base(const flk_desc* d, const void* x, int32_t p0, int32_t n_pos, uint8_t* codes,
+                           uint32_t* params, void* recon, uint32_t* dev_status, void* stream) {
+  flk_status st = flk_desc_check(d);
+  if (st != FLK_OK) return st;
+  if (!x || !recon) return FLK_E_NULL;
+  st = check_window(d, p0, n_pos);
+  if (st != FLK_OK) return st;
+  st = check_stream_ptrs(codes, params);
+  if (st != FLK_OK) return st;
+  if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
+  const flk::EncArgs a = enc_args(d, x, nullptr, n_pos, n_pos, recon, codes + codes_offset(d, p0),
+                                  params + params_offset(d, p0, p0), nullptr, dev_status);
+  return to_status(flk::launch_encode(d->kind, false, a, d->n_heads, d->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_append_residual(const flk_desc* d, const void* x_rows, const int32_t* rows, int32_t n_rows,
+                               int32_t p0, int32_t n_pos, int32_t rows_before, void* recon, uint8_t* codes,
+                               uint32_t* params, int32_t* tile_start, uint32_t* dev_status, void* stream) {
+  flk_status st = flk_desc_check(d);
+  if (st != FLK_OK) return st;
+  if (!recon) return FLK_E_NULL;
+  st = check_window(d, p0, n_pos);
+  if (st != FLK_OK) return st;
+  if (n_rows < 0 || n_rows > n_pos || rows_before < 0 || rows_before > p0) return FLK_E_SHAPE;
+  const bool dense = rows == nullptr && n_rows > 0;
+  if (dense && (n_rows != n_pos || rows_before != p0)) return FLK_E_SHAPE;
+  if (!dense && d->kind == FLK_KIND_K && !k_tiles(d)) return FLK_E_UNSUPPORTED;
+  if (n_rows > 0 && !x_rows) return FLK_E_NULL;
+  if (!dense && !tile_start) return FLK_E_NULL;
+  if (n_rows > 0 || k_tiles(d)) {
+    st = check_stream_ptrs(codes, params);
+    if (st != FLK_OK) return st;
+  }
+  if (!aligned(recon, 16) || (dev_status && !aligned(dev_status, 4)) || (x_rows && !aligned(x_rows, 16)) ||
+      (rows && !aligned(rows, 4)) || (tile_start && !aligned(tile_start, 4)))
+    return FLK_E_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_rows == 0) {
+    // an empty window of a compact stream: its tile index entries, and zero tile params for K
+    const int32_t t0 = p0 / FLK_GROUP, nt = n_pos / FLK_GROUP;
+    if (flk::launch_fill_u32(reinterpret_cast<uint32_t*>(tile_start + t0), nt + 1, uint32_t(rows_before), s) !=
+        hipSuccess)
+      return FLK_E_LAUNCH;
+    if (k_tiles(d)) {
+      const int64_t W = int64_t(d->n_heads) * d->head_dim;
+      if (flk::launch_fill_u32(params + params_offset(d, rows_before, p0), int64_t(nt) * W, 0u, s) != hipSuccess)
+        return FLK_E_LAUNCH;
+    }
+    return FLK_OK;
+  }
+  flk::EncArgs a = enc_args(d, x_rows, rows, n_rows, n_pos, recon, codes + codes_offset(d, rows_before),
+                            params + params_offset(d, rows_before, p0),
+                            rows ? tile_start + p0 / FLK_GROUP : nullptr, dev_status);
+  a.pos0 = rows ? p0 : 0;
+  a.row0 = rows_before;
+  return to_status(flk::launch_encode(d->kind, true, a, d->n_heads, d->head_dim, s));
+}
+
+flk_status flk_decode_attn_rolling(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                                   int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                   int32_t n_loops, const void* k_tail, const void* v_tail, int32_t tail_len,
+                                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  flk_status st = flk_desc_check(kd);
+  if (st != FLK_OK) return st;
+  st = flk_desc_check(vd);
+  if (st != FLK_OK) return st;
+  if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
+  if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
+  if (!q || !out) return FLK_E_NULL;
+  if (T < 0 || tail_len < 0 || int64_t(T) + tail_len < 1 || !rows_fit(kd, T) || !rows_fit(kd, tail_len) ||
+      n_q_heads < 1 || n_q_heads % kd->n_heads != 0)
+    return FLK_E_SHAPE;
+  if (kd->head_dim != 128 || n_q_heads / kd->n_heads > 16) return FLK_E_UNSUPPORTED;
+  if (tail_len > 0 && (!k_tail || !v_tail)) return FLK_E_NULL;
+  flk::ChainArgs kc{}, vc{};
+  if (T > 0) {
+    st = load_chain(kd, T, k_chain, n_loops, &kc);
+    if (st != FLK_OK) return st;
+    st = load_chain(vd, T, v_chain, n_loops, &vc);
+    if (st != FLK_OK) return st;
+  }
+  if (!aligned(q, 16) || !aligned(out, 16) || (tail_len > 0 && (!aligned(k_tail, 16) || !aligned(v_tail, 16))))
+    return FLK_E_ALIGN;
+  const size_t need = flk::attn_workspace_bytes(T, kd->n_heads, n_q_heads);
+  if (!workspace || workspace_bytes < need) return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 16)) return FLK_E_ALIGN;
+  return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc, k_tail, v_tail,
+                                           tail_len, softmax_scale, out, workspace,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -251,8 +396,7 @@ flk_status check_encode_unit(const flk_desc* d, bool resid, const flk_unit& u, f
   if (st != FLK_OK) return st;
   if (u.rows && !u.tile_start) return FLK_E_NULL;
   if (!aligned(u.x, 16) || (u.rows && (!aligned(u.rows, 4) || !aligned(u.tile_start, 4)))) return FLK_E_ALIGN;
-  *a = flk::EncArgs{static_cast<const uint16_t*>(u.x), u.rows, static_cast<uint16_t*>(u.recon), u.codes, u.params,
-                    u.rows ? u.tile_start : nullptr, nullptr, u.n_rows, u.T, d->n_heads * d->head_dim};
+  *a = enc_args(d, u.x, u.rows, u.n_rows, u.T, u.recon, u.codes, u.params, u.tile_start, nullptr);
   return FLK_OK;
 }
 
@@ -294,8 +438,7 @@ flk_status encode_batch(bool resid, const flk_desc* kd, const flk_desc* vd, cons
   }
   for (const auto& [i, a] : singles) {
     const flk_desc* d = unit_desc(kd, vd, units[i].kind);
-    const hipError_t e = flk::launch_encode(units[i].kind, resid, a.x, a.rows, a.n, a.T, d->n_heads, d->head_dim,
-                                            a.recon, a.codes, a.params, a.tile_start, a.status, s);
+    const hipError_t e = flk::launch_encode(units[i].kind, resid, a, d->n_heads, d->head_dim, s);
     if (e != hipSuccess) return FLK_E_LAUNCH;
   }
   return FLK_OK;

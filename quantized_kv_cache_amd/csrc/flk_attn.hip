@@ -50,8 +50,11 @@ static int32_t n_splits(int32_t T, int32_t H) {
   return (tiles + per_block - 1) / per_block;
 }
 
+// One partial (m, l, O) per query head for every split of the packed tokens, plus one for a
+// BF16 tail.
 size_t attn_workspace_bytes(int32_t T, int32_t H, int32_t Hq) {
-  return size_t(n_splits(T, H)) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
+  const int32_t splits = T > 0 ? n_splits(T, H) : 0;
+  return size_t(splits + 1) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
 }
 
 // Decode loop l's 8 channels of one item into d[] (binary32 values that are exactly BF16).
@@ -176,7 +179,7 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
       if (j[l] < 0) continue;
       uint32_t p[8];
       if (KIND == FLK_KIND_K) {
-        const int rg = (j[l] / kGroup) & 1;               // staged by rowgroup parity
+        const int rg = c.ktile ? 0 : (j[l] / kGroup) & 1;  // staged by rowgroup parity
         const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
         const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
         p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
@@ -237,10 +240,18 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     build_maps<NL>(kc, rk, t0, L.map[0], lane);
     build_maps<NL>(vc, rv, t0, L.map[1], lane);
     // K parameter rows of the tile: rowgroup lo/64 (and lo/64 + 1 for a compact loop), each in
-    // the slot of its parity, so a row j finds its parameters in slot (j/64) & 1
+    // the slot of its parity, so a row j finds its parameters in slot (j/64) & 1; with tile
+    // groups, the tile's own row in slot 0
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
       if (l >= kc.n_loops) continue;
+      if (kc.ktile) {
+        if (rk.hi[l] > rk.lo[l]) {
+          const uint2 w = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(tile) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
+          *reinterpret_cast<uint2*>(&L.kp[l][0][2 * lane]) = w;
+        }
+        continue;
+      }
       const int32_t nrg = (kc.s[l].n + kGroup - 1) / kGroup;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
@@ -364,6 +375,102 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// The BF16 tail of a rolling cache: one block per KV head writes the partial (m, l, O) of its
+// G query heads over the tail's tokens, in the workspace slot after the packed splits.  The
+// tail holds at most a few hundred tokens, so the block walks them in chunks of 256: one
+// token per thread for the scores, then one (head, channel) pair per thread for P V.
+// ---------------------------------------------------------------------------------------
+constexpr int kTailChunk = kAThreads;
+__global__ __launch_bounds__(kAThreads) void attn_tail_kernel(const uint16_t* __restrict__ kt,
+                                                              const uint16_t* __restrict__ vt, int32_t tail_len,
+                                                              int32_t H, int32_t G, const uint16_t* __restrict__ q,
+                                                              float scale, int32_t slot,
+                                                              float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+  __shared__ float s_q[kMaxG][kAttnD];
+  __shared__ float s_p[kMaxG][kTailChunk];
+  __shared__ float s_m[kMaxG], s_l[kMaxG], s_corr[kMaxG];
+  const int tid = threadIdx.x;
+  const int32_t h = blockIdx.x;
+  const int32_t Hq = H * G;
+  for (int idx = tid; idx < G * kAttnD; idx += kAThreads) {
+    const int g = idx / kAttnD, c = idx % kAttnD;
+    s_q[g][c] = bf16_lo(q[int64_t(h * G + g) * kAttnD + c]);
+  }
+  if (tid < kMaxG) { s_m[tid] = -__builtin_inff(); s_l[tid] = 0.0f; }
+  // (head, channel) pairs of this thread for P V: idx = tid + 256 k
+  constexpr int kPairs = kMaxG * kAttnD / kAThreads;
+  float o[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) o[k] = 0.0f;
+  __syncthreads();
+  const int64_t row = int64_t(H) * kAttnD;
+  for (int32_t c0 = 0; c0 < tail_len; c0 += kTailChunk) {
+    // scores of token c0 + tid for every head
+    const int32_t t = c0 + tid;
+    if (t < tail_len) {
+      float kv[kAttnD];
+      const uint4* kp = reinterpret_cast<const uint4*>(kt + t * row + int64_t(h) * kAttnD);
+#pragma unroll
+      for (int i = 0; i < kAttnD / 8; ++i) {
+        const uint4 w = kp[i];
+        kv[8 * i + 0] = bf16_lo(w.x); kv[8 * i + 1] = bf16_hi(w.x);
+        kv[8 * i + 2] = bf16_lo(w.y); kv[8 * i + 3] = bf16_hi(w.y);
+        kv[8 * i + 4] = bf16_lo(w.z); kv[8 * i + 5] = bf16_hi(w.z);
+        kv[8 * i + 6] = bf16_lo(w.w); kv[8 * i + 7] = bf16_hi(w.w);
+      }
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kAttnD; ++c) acc = __builtin_fmaf(s_q[g][c], kv[c], acc);
+        s_p[g][tid] = acc * scale;
+      }
+    } else {
+      for (int g = 0; g < G; ++g) s_p[g][tid] = -__builtin_inff();
+    }
+    __syncthreads();
+    // per head: the chunk's maximum, the rescale of the running sums, the probabilities
+    if (tid < G) {
+      const int g = tid;
+      float mx = -__builtin_inff();
+      for (int i = 0; i < kTailChunk; ++i) mx = fmaxf(mx, s_p[g][i]);
+      const float m_new = fmaxf(s_m[g], mx);
+      const float corr = s_m[g] == -__builtin_inff() ? 0.0f : __expf(s_m[g] - m_new);
+      float sum = 0.0f;
+      for (int i = 0; i < kTailChunk; ++i) {
+        const float p = s_p[g][i] == -__builtin_inff() ? 0.0f : __expf(s_p[g][i] - m_new);
+        s_p[g][i] = p;
+        sum += p;
+      }
+      s_l[g] = s_l[g] * corr + sum;
+      s_m[g] = m_new;
+      s_corr[g] = corr;
+    }
+    __syncthreads();
+    const int32_t nt = min(kTailChunk, tail_len - c0);
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int idx = tid + kAThreads * k;
+      const int g = idx / kAttnD, c = idx % kAttnD;
+      if (g >= G) continue;
+      float acc = o[k] * s_corr[g];
+      for (int32_t i = 0; i < nt; ++i)
+        acc = __builtin_fmaf(s_p[g][i], bf16_lo(vt[(c0 + i) * row + int64_t(h) * kAttnD + c]), acc);
+      o[k] = acc;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int idx = tid + kAThreads * k;
+    const int g = idx / kAttnD, c = idx % kAttnD;
+    if (g >= G) continue;
+    const int64_t qi = int64_t(slot) * Hq + h * G + g;
+    if (c == 0) { ws_ml[2 * qi] = s_m[g]; ws_ml[2 * qi + 1] = s_l[g]; }
+    ws_o[qi * kAttnD + c] = o[k];
+  }
+}
+
 // Merge the per-block partials of one query head (blockIdx.x).  Thread (c = tid % 128,
 // g = tid / 128) takes channel c of every kCombGroups-th split from g on, with independent
 // loads in flight; the groups then merge through LDS.
@@ -412,30 +519,41 @@ __global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int3
 }
 
 hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
-                              const ChainArgs& kc, const ChainArgs& vc, float scale, void* out,
+                              const ChainArgs& kc, const ChainArgs& vc, const void* k_tail,
+                              const void* v_tail, int32_t tail_len, float scale, void* out,
                               void* ws, hipStream_t stream) {
   (void)D;
-  const int32_t tpw = tiles_per_wave(T, H);
-  const int32_t splits = n_splits(T, H);
+  const int32_t tpw = T > 0 ? tiles_per_wave(T, H) : 0;
+  const int32_t splits = T > 0 ? n_splits(T, H) : 0;
+  const int32_t slots = splits + (tail_len > 0 ? 1 : 0);
   const int32_t G = Hq / H;
   float* ws_ml = static_cast<float*>(ws);
-  float* ws_o = ws_ml + size_t(splits) * Hq * 2;
-  const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
-  const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
+  float* ws_o = ws_ml + size_t(slots) * Hq * 2;
   const uint16_t* qp = static_cast<const uint16_t*>(q);
+  if (splits > 0) {
+    const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
+    const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
 #define FLK_A(NLV)                                                                                      \
   case NLV:                                                                                             \
     hipLaunchKernelGGL((attn_wave_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
                        scale, tpw, ws_ml, ws_o);                                                        \
     break;
-  switch (nl) {
-    FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
-    default: return hipErrorInvalidValue;
-  }
+    switch (nl) {
+      FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
+      default: return hipErrorInvalidValue;
+    }
 #undef FLK_A
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, splits, Hq, ws_ml,
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (tail_len > 0) {
+    hipLaunchKernelGGL(attn_tail_kernel, dim3(unsigned(H)), dim3(kAThreads), 0, stream,
+                       static_cast<const uint16_t*>(k_tail), static_cast<const uint16_t*>(v_tail), tail_len, H, G,
+                       qp, scale, splits, ws_ml, ws_o);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, slots, Hq, ws_ml,
                      ws_o, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }

@@ -297,18 +297,33 @@ __device__ __forceinline__ void st_stream32(void* p, uint32_t w) {
 // entries of the tiles whose first listed position is rows[j] (the t with
 // rows[j-1] < 64t <= rows[j]), and the row n-1 also writes n for every later tile.  Each
 // entry is written by exactly one row; entries are clamped to the array.
+// A window of an appended stream covers positions [pos0, pos0 + T): rows hold absolute
+// positions, tile t of the window is entry t of tile_start (the caller offsets it), and the
+// stream already holds row0 rows before the window, so every entry is offset by row0.
 __device__ __forceinline__ void write_tile_index(const int32_t* __restrict__ rows, int32_t n,
                                                  int32_t T, int32_t j,
-                                                 int32_t* __restrict__ tile_start) {
+                                                 int32_t* __restrict__ tile_start,
+                                                 int32_t pos0, int32_t row0) {
   const int32_t ntiles = (T + kGroup - 1) / kGroup;
-  const int32_t p = rows[j];
-  const int32_t q = j > 0 ? rows[j - 1] : -1;
+  const int32_t p = rows[j] - pos0;
+  const int32_t q = j > 0 ? rows[j - 1] - pos0 : -1;
   if (p < 0 || p >= T) return;
   const int32_t t_first = q < 0 ? 0 : min(q / kGroup + 1, ntiles + 1);
   const int32_t t_last = p / kGroup;
-  for (int32_t t = t_first; t <= t_last; ++t) tile_start[t] = j;
+  for (int32_t t = t_first; t <= t_last; ++t) tile_start[t] = row0 + j;
   if (j == n - 1)
-    for (int32_t t = t_last + 1; t <= ntiles; ++t) tile_start[t] = n;
+    for (int32_t t = t_last + 1; t <= ntiles; ++t) tile_start[t] = row0 + n;
+}
+
+// First index of the ascending rows[0..n) whose value is >= key.
+__device__ __forceinline__ int32_t lower_bound_rows(const int32_t* __restrict__ rows, int32_t n,
+                                                    int32_t key) {
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (rows[mid] < key) lo = mid + 1; else hi = mid;
+  }
+  return lo;
 }
 
 }  // namespace flk

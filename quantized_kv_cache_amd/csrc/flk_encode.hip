@@ -43,7 +43,9 @@ __device__ __forceinline__ uint4 pack8(const float v[8]) {
 
 // ---------------------------------------------------------------------------------------
 // K: groups run down 64 compact rows of one (head, channel).  A block owns one 64-row band
-// of a 128-channel (64 for compact loops) strip of the flattened H*D channel axis.
+// of a 128-channel (64 for compact loops) strip of the flattened H*D channel axis.  With
+// tile groups (page-local, a.ktile) a compact loop's band is instead the rows of one
+// 64-position tile, 0 to 64 of them, found by binary search in rows.
 // Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs + slots, ... (4 rows each
 // at 128 channels, 2 at 64).  Extremes: in registers over its rows, across the row slots of a
 // wave with lane shuffles, across the 4 waves through LDS; one thread per channel then derives
@@ -62,7 +64,7 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   uint32_t* __restrict__ params = a.params;
   int32_t* __restrict__ tile_start = a.tile_start;
   uint32_t* __restrict__ status = a.status;
-  const int32_t n = a.n, T = a.T, W = a.W;
+  const int32_t n = a.n, T = a.T, W = a.W, pos0 = a.pos0;
   __shared__ float s_min[4][kKCW];
   __shared__ float s_max[4][kKCW];
   __shared__ float s_m[kKCW], s_s[kKCW], s_rs[kKCW];
@@ -76,6 +78,13 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   const int chunk = int(strip) * kKChunks + cc;
   const bool cact = chunk < (W >> 3);
   const int64_t ch = int64_t(chunk) * 8;
+  // the band's compact rows [jbeg, jend)
+  int32_t jbeg = band * kGroup, jend = min(n, jbeg + kGroup);
+  if (SPARSE && a.ktile) {
+    const int32_t key = pos0 + band * kGroup;
+    jbeg = uniform(lower_bound_rows(rows, n, key));
+    jend = uniform(min(lower_bound_rows(rows, n, key + kGroup), jbeg + kGroup));
+  }
 
   float v[kKRows][8];
   uint4 rv[kKRows];
@@ -84,13 +93,13 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   bool bad_row = false;
 #pragma unroll
   for (int i = 0; i < kKRows; ++i) {
-    const int j = band * kGroup + rs + kKSlots * i;
-    ract[i] = cact && j < n;
+    const int j = jbeg + rs + kKSlots * i;
+    ract[i] = cact && j < jend;
     rv[i] = make_uint4(0, 0, 0, 0);
     roff[i] = 0;
     uint4 xv = make_uint4(0, 0, 0, 0);
     if (ract[i]) {
-      const int32_t p = SPARSE ? rows[j] : j;
+      const int32_t p = SPARSE ? rows[j] - pos0 : j;
       if (SPARSE && uint32_t(p) >= uint32_t(T)) {   // malformed map: never address outside recon
         ract[i] = false;
         bad_row = true;
@@ -106,8 +115,8 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   if (SPARSE && strip == 0 && cc == 0) {
 #pragma unroll
     for (int i = 0; i < kKRows; ++i) {
-      const int j = band * kGroup + rs + kKSlots * i;
-      if (j < n) write_tile_index(rows, n, T, j, tile_start);
+      const int j = jbeg + rs + kKSlots * i;
+      if (j < jend) write_tile_index(rows, n, T, j, tile_start, pos0, a.row0);
     }
   }
   if (RESID) {
@@ -147,6 +156,10 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
     const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
     const int64_t chan = int64_t(strip) * kKCW + tid;
     GroupParams p = make_params(a, b);
+    if (jend <= jbeg) {                      // an empty tile: no group, params 0
+      p.packed = 0;
+      p.err = 0;
+    }
     s_m[tid] = p.m;
     s_s[tid] = p.s;
     s_rs[tid] = p.rs;
@@ -167,7 +180,7 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
 #pragma unroll
   for (int i = 0; i < kKRows; ++i) {
     if (!ract[i]) continue;
-    const int j = band * kGroup + rs + kKSlots * i;
+    const int j = jbeg + rs + kKSlots * i;
     float k[8], out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -204,7 +217,8 @@ template <bool RESID, bool SPARSE, int LPH>
 __global__ __launch_bounds__(kThreads) void encode_v_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ rows, int32_t n, int32_t T,
     int32_t H, int32_t D, uint16_t* __restrict__ recon, uint8_t* __restrict__ codes,
-    uint32_t* __restrict__ params, int32_t* __restrict__ tile_start, uint32_t* __restrict__ status) {
+    uint32_t* __restrict__ params, int32_t* __restrict__ tile_start, uint32_t* __restrict__ status,
+    int32_t pos0, int32_t row0) {
   constexpr int HS = kThreads / LPH;
   constexpr int U = 4;
   const int tid = threadIdx.x;
@@ -232,12 +246,12 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
       if (SPARSE) {
         const uint32_t j = uint32_t(it) / uint32_t(H);   // n*H < 2^31 (checked on the host)
         const int64_t h = it - int64_t(j) * H;
-        const int32_t p = rows[j];
+        const int32_t p = rows[j] - pos0;
         if (uint32_t(p) >= uint32_t(T)) {              // malformed map: never address outside recon
           act[u] = false;
           if (status) atomicOr(status, kDevRows);
         }
-        if (h == 0 && w == 0) write_tile_index(rows, n, T, int32_t(j), tile_start);
+        if (h == 0 && w == 0) write_tile_index(rows, n, T, int32_t(j), tile_start, pos0, row0);
         ro = (int64_t(p) * H + h) * D + w * 8;
       }
       if (act[u]) {
@@ -338,7 +352,7 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
   int32_t pos[2];
   auto issue = [&](int32_t j, auto B) {
     constexpr int b = decltype(B)::value;
-    int32_t p = SPARSE ? uniform(rows[j]) : j;
+    int32_t p = SPARSE ? uniform(rows[j]) - a.pos0 : j;
     if (SPARSE && uint32_t(p) >= uint32_t(T)) p = -1;       // malformed map: skip the row
     pos[b] = p;
     const uint32_t pr = uint32_t(max(p, 0));
@@ -352,7 +366,7 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
   uint32_t err = 0;
   auto process = [&](int32_t j, auto B) {
     constexpr int b = decltype(B)::value;
-    if (SPARSE && lane == 0 && by == 0) write_tile_index(rows, n, T, j, tile_start);
+    if (SPARSE && lane == 0 && by == 0) write_tile_index(rows, n, T, j, tile_start, a.pos0, a.row0);
     const int32_t p = pos[b];
     if (SPARSE && p < 0) { err |= kDevRows; return; }
     float v[kCh], r[kCh];
@@ -424,9 +438,11 @@ static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) {
   const int32_t waves = (n + rpw - 1) / rpw;
   return dim3(unsigned((waves + 3) / 4), unsigned(W / 1024));
 }
-static dim3 k_grid(int32_t n, int32_t W, bool sparse) {  // x: channel strips, y: 64-row bands
+// x: channel strips; y: 64-row bands, or the window's 64-position tiles for tile groups
+static dim3 k_grid(const EncArgs& a, bool sparse) {
   const int chunks = (sparse ? k_block_channels<true>() : k_block_channels<false>()) / 8;
-  return dim3(unsigned((W / 8 + chunks - 1) / chunks), unsigned((n + kGroup - 1) / kGroup));
+  const int32_t bands = sparse && a.ktile ? a.T : a.n;
+  return dim3(unsigned((a.W / 8 + chunks - 1) / chunks), unsigned((bands + kGroup - 1) / kGroup));
 }
 
 template <bool RESID, bool SPARSE>
@@ -438,19 +454,16 @@ static hipError_t launch_v_wide(const EncArgs& a, hipStream_t stream) {
 }
 
 template <bool RESID, bool SPARSE>
-static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t H, int32_t D,
-                           void* recon, uint8_t* codes, uint32_t* params, int32_t* tile_start,
-                           uint32_t* status, hipStream_t stream) {
+static hipError_t launch_v(const EncArgs& a, int32_t H, int32_t D, hipStream_t stream) {
   const int cph = D / 8;
   const int lph = cph <= 8 ? 8 : cph <= 16 ? 16 : cph <= 32 ? 32 : 64;
   const int per_block = (kThreads / lph) * 4;
-  const int64_t items = int64_t(n) * H;
+  const int64_t items = int64_t(a.n) * H;
   const dim3 grid(unsigned((items + per_block - 1) / per_block));
-  const uint16_t* xp = static_cast<const uint16_t*>(x);
-  uint16_t* rp = static_cast<uint16_t*>(recon);
-#define FLK_LAUNCH_V(L)                                                                        \
-  hipLaunchKernelGGL((encode_v_kernel<RESID, SPARSE, L>), grid, dim3(kThreads), 0, stream, xp, \
-                     rows, n, T, H, D, rp, codes, params, tile_start, status)
+#define FLK_LAUNCH_V(L)                                                                          \
+  hipLaunchKernelGGL((encode_v_kernel<RESID, SPARSE, L>), grid, dim3(kThreads), 0, stream, a.x,   \
+                     a.rows, a.n, a.T, H, D, a.recon, a.codes, a.params, a.tile_start, a.status, \
+                     a.pos0, a.row0)
   switch (lph) {
     case 8: FLK_LAUNCH_V(8); break;
     case 16: FLK_LAUNCH_V(16); break;
@@ -463,18 +476,13 @@ static hipError_t launch_v(const void* x, const int32_t* rows, int32_t n, int32_
 
 template <bool RESID, bool SPARSE>
 static hipError_t launch_k(const EncArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a.n, a.W, SPARSE), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a, SPARSE), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* rows, int32_t n,
-                         int32_t T, int32_t H, int32_t D, void* recon, uint8_t* codes,
-                         uint32_t* params, int32_t* tile_start, uint32_t* status,
-                         hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const bool sparse = rows != nullptr;
-  const EncArgs a{static_cast<const uint16_t*>(x), rows, static_cast<uint16_t*>(recon), codes, params,
-                  tile_start, status, n, T, H * D};
+hipError_t launch_encode(int kind, bool resid, const EncArgs& a, int32_t H, int32_t D, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  const bool sparse = a.rows != nullptr;
   if (kind == FLK_KIND_K) {
     if (!resid) return launch_k<false, false>(a, stream);
     if (!sparse) return launch_k<true, false>(a, stream);
@@ -485,9 +493,21 @@ hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* row
     if (!sparse) return launch_v_wide<true, false>(a, stream);
     return launch_v_wide<true, true>(a, stream);
   }
-  if (!resid) return launch_v<false, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
-  if (!sparse) return launch_v<true, false>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
-  return launch_v<true, true>(x, rows, n, T, H, D, recon, codes, params, tile_start, status, stream);
+  if (!resid) return launch_v<false, false>(a, H, D, stream);
+  if (!sparse) return launch_v<true, false>(a, H, D, stream);
+  return launch_v<true, true>(a, H, D, stream);
+}
+
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count, uint32_t value) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < count) p[i] = value;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(unsigned((count + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     p, count, value);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -538,7 +558,7 @@ hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, con
       e.kind = kinds[i];
       dim3 g;
       if (kinds[i] == FLK_KIND_K) {
-        g = k_grid(args[i].n, args[i].W, sparse);
+        g = k_grid(args[i], sparse);
         e.rpw = 0;
       } else {
         e.rpw = v_wide_rpw(args[i].n, args[i].W);

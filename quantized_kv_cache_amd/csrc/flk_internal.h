@@ -21,6 +21,7 @@ struct StreamArgs {
 struct ChainArgs {
   StreamArgs s[FLK_MAX_LOOPS];
   int32_t n_loops;
+  int32_t ktile;              // K parameter rows per 64-position tile (else per 64 compact rows)
 };
 
 // One encode of one tensor as a kernel sees it (single and batched calls alike).
@@ -33,16 +34,20 @@ struct EncArgs {
   int32_t* tile_start;     // compact loops only
   uint32_t* status;        // optional device status word
   int32_t n, T, W;         // rows, positions, channels per row (H*D)
+  int32_t pos0;            // first position of the window (rows hold absolute positions)
+  int32_t row0;            // rows of the stream before the window (offsets tile_start values)
+  int32_t ktile;           // K groups per 64-position tile instead of per 64 compact rows
 };
 
 // Largest number of tensors one batched launch covers.
 constexpr int kEncBatch = 16;
 
-// Encode one loop (base when resid == false).  Returns a hipError_t.
-hipError_t launch_encode(int kind, bool resid, const void* x, const int32_t* rows, int32_t n,
-                         int32_t T, int32_t H, int32_t D, void* recon, uint8_t* codes,
-                         uint32_t* params, int32_t* tile_start, uint32_t* status,
-                         hipStream_t stream);
+// Encode one loop (base when resid == false); a.rows == nullptr is a dense loop.  The
+// pointers are already offset to the window (codes, params, tile_start).
+hipError_t launch_encode(int kind, bool resid, const EncArgs& a, int32_t H, int32_t D, hipStream_t stream);
+
+// p[0 .. count) = value (small fills of tile index entries and empty-tile parameters).
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t stream);
 
 // Whether a tensor of this kind and shape can join a batched encode launch; the others are
 // encoded one launch each.
@@ -73,8 +78,10 @@ hipError_t launch_reconstruct_batch(const RecArgs* units, int n_units, hipStream
 
 size_t attn_workspace_bytes(int32_t T, int32_t H, int32_t Hq);
 
+// Packed positions [0, T) (T may be 0) plus an optional BF16 tail of tail_len positions.
 hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
-                              const ChainArgs& kc, const ChainArgs& vc, float scale, void* out,
+                              const ChainArgs& kc, const ChainArgs& vc, const void* k_tail,
+                              const void* v_tail, int32_t tail_len, float scale, void* out,
                               void* ws, hipStream_t stream);
 
 }  // namespace flk

@@ -6,13 +6,39 @@
 // is 512 channels wide), so whether a compact loop lists a token is uniform across the wave
 // and absent positions cost no arithmetic.  Per compact loop the block finds the tile's
 // compact rows with a parallel lower_bound and an LDS position -> row table; K params
-// (one per channel and 64 compact rows) are staged in LDS as binary32 pairs.  Each element
+// (one per channel and 64 compact rows, or per tile with tile groups) are staged in LDS as
+// binary32 pairs.  Each element
 // walks base -> delta2 -> ... with the encoder's BF16 rounding after every step
 // (FlashLoop RFC, vllm-rlt #156, section 3.3: t1 reads base + delta2, t2 adds delta3, t4
 // adds delta4; an absent residual means inheritance).
-#include "flk_chain.h"
+#include "flk_device.h"
+#include "flk_internal.h"
 
 namespace flk {
+
+// lower_bound over an ascending array, computed by a whole 256-thread block in
+// ceil(log256(n)) rounds of one parallel probe each (instead of log2(n) dependent loads):
+// each round probes 256 evenly spaced entries of the current bracket and keeps the one
+// stride that contains the first entry >= key.  Every thread returns the same value.
+// Contains __syncthreads_count(); call from all threads of the block.
+__device__ __forceinline__ int32_t block_lower_bound(const int32_t* __restrict__ rows, int32_t n,
+                                                     int32_t key) {
+  int32_t a = 0, b = n;                    // the answer lies in [a, b]
+  while (a < b) {
+    const int32_t s = (b - a + 255) / 256;
+    const int32_t idx = a + int32_t(threadIdx.x) * s;
+    const bool pred = idx < b && rows[idx] < key;
+    const int32_t c = __syncthreads_count(pred);
+    if (c == 0) return a;
+    const int32_t na = a + (c - 1) * s + 1;
+    const int32_t nb = min(a + c * s, b);
+    if (s == 1) return nb;
+    a = na;
+    b = nb;
+  }
+  return a;
+}
+
 
 #ifndef FLK_RECON_BATCH
 #define FLK_RECON_BATCH 4
@@ -66,8 +92,9 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_kernel(ChainArgs chain,
         }
       }
       const int32_t cnt = __syncthreads_count(found);
-      rg0 = lo / kGroup;
-      nrg = cnt == 0 ? 0 : ((lo + cnt - 1) / kGroup - rg0 + 1);
+      // the rowgroups holding the tile's rows (at most 2), or with tile groups the tile's own
+      rg0 = chain.ktile ? int32_t(blockIdx.x) : lo / kGroup;
+      nrg = cnt == 0 ? 0 : chain.ktile ? 1 : ((lo + cnt - 1) / kGroup - rg0 + 1);
     }
     if (KIND == FLK_KIND_K) {
       // stage (min, scale) of rowgroups rg0 .. rg0 + nrg - 1 (at most 2) for this strip
@@ -129,7 +156,7 @@ __global__ __launch_bounds__(kRThreads) void reconstruct_kernel(ChainArgs chain,
         float c[8], m[8], s[8];
         codes8_to_f32(cw[i][l], c);
         if (KIND == FLK_KIND_K) {
-          const int slot = (j >> 6) - s_rg0[l];
+          const int slot = chain.ktile ? 0 : (j >> 6) - s_rg0[l];
           const float4* kp = reinterpret_cast<const float4*>(&s_kp[l][slot][cl * 8]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -230,8 +257,8 @@ __device__ __forceinline__ void reconstruct_wide_body(const ChainArgs& chain, in
   for (int l = 0; l < NL; ++l) {
     const uint32_t n = uint32_t(chain.s[l].n);
     crs[l] = make_buf(chain.s[l].codes, n * crow_bytes);
-    prs[l] = make_buf(chain.s[l].params, KIND == FLK_KIND_K ? ((n + kGroup - 1) / kGroup) * krow_bytes
-                                                            : n * vrow_bytes);
+    const uint32_t krows = chain.ktile ? (uint32_t(T) + kGroup - 1) / kGroup : (n + kGroup - 1) / kGroup;
+    prs[l] = make_buf(chain.s[l].params, KIND == FLK_KIND_K ? krows * krow_bytes : n * vrow_bytes);
   }
   const BufRsrc ors = make_buf(out, uint32_t(T) * uint32_t(W) * 2u);
   const uint32_t o_voff = uint32_t(ch) * 2u;
@@ -239,12 +266,13 @@ __device__ __forceinline__ void reconstruct_wide_body(const ChainArgs& chain, in
 
   // K params: one resident rowgroup per loop.  A dense loop's tokens lie in one rowgroup;
   // a compact loop's rows for them span at most two, so the set is reloaded at most once.
+  // With tile groups every loop's parameter row is the tile's own.
   uint4 kreg[NL][2];
   int32_t krg[NL];
   if (KIND == FLK_KIND_K) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      krg[l] = (is_sparse(l) ? lo[l] : tw) / kGroup;
+      krg[l] = chain.ktile ? tile : (is_sparse(l) ? lo[l] : tw) / kGroup;
       const uint32_t soff = uint32_t(krg[l]) * krow_bytes;
       kreg[l][0] = buf_ld128(prs[l], k_voff, soff);
       kreg[l][1] = buf_ld128(prs[l], k_voff + 16u, soff);
@@ -290,7 +318,7 @@ __device__ __forceinline__ void reconstruct_wide_body(const ChainArgs& chain, in
         codes8_to_f32(cw[cur][i][l], c);
         uint32_t pw[8];
         if (KIND == FLK_KIND_K) {
-          if (is_sparse(l) && (j / kGroup) != krg[l]) {   // crossed into the next rowgroup
+          if (is_sparse(l) && !chain.ktile && (j / kGroup) != krg[l]) {   // crossed into the next rowgroup
             krg[l] = j / kGroup;
             const uint32_t soff = uint32_t(krg[l]) * krow_bytes;
             kreg[l][0] = buf_ld128(prs[l], k_voff, soff);

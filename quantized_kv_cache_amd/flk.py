@@ -6,8 +6,8 @@ library is missing or cannot load, every call raises.
 
 Tensors: BF16 data are torch.bfloat16 [rows, H, D] (contiguous, on the GPU); codes are
 torch.uint8 [n, H, D//2]; params torch.int32 (FP16 min | FP16 scale << 16, bit pattern),
-shaped [ceil(n/64), H, D] for K and [n, H, ceil(D/64)] for V; rows are torch.int32 [n]
-ascending positions or None (dense).
+shaped [ceil(n/64), H, D] for K, [ceil(T/64), H, D] for K with tile (page-local) groups and
+[n, H, ceil(D/64)] for V; rows are torch.int32 [n] ascending positions or None (dense).
 """
 from __future__ import annotations
 
@@ -22,6 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libflk.so")
 
 K, V = 0, 1
+KGROUP_ROWS, KGROUP_TILE = 0, 1
 GROUP = 64
 MAX_LOOPS = 8
 DEV_NONFINITE, DEV_RANGE = 1, 2
@@ -37,7 +38,8 @@ class FlkError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint16), ("format", ctypes.c_uint8), ("kind", ctypes.c_uint8),
                 ("group", ctypes.c_uint16), ("param_dtype", ctypes.c_uint8), ("nibble_order", ctypes.c_uint8),
-                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("k_grouping", ctypes.c_uint8),
+                ("reserved", ctypes.c_uint8 * 3)]
 
 
 class StreamC(ctypes.Structure):
@@ -77,7 +79,17 @@ def lib() -> ctypes.CDLL:
         L.flk_codes_bytes.restype = sz
         L.flk_codes_bytes.argtypes = [D, i32]
         L.flk_params_bytes.restype = sz
-        L.flk_params_bytes.argtypes = [D, i32]
+        L.flk_params_bytes.argtypes = [D, i32, i32]
+        L.flk_stream_bytes.restype = sz
+        L.flk_stream_bytes.argtypes = [D, i32, i32, ctypes.c_int]
+        L.flk_rolling_prefix.restype = i32
+        L.flk_rolling_prefix.argtypes = [i32]
+        L.flk_append_base.restype = ctypes.c_int
+        L.flk_append_base.argtypes = [D, P, i32, i32, P, P, P, P, P]
+        L.flk_append_residual.restype = ctypes.c_int
+        L.flk_append_residual.argtypes = [D, P, P, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.flk_decode_attn_rolling.restype = ctypes.c_int
+        L.flk_decode_attn_rolling.argtypes = [D, D, i32, P, i32, S, S, i32, P, P, i32, ctypes.c_float, P, P, sz, P]
         L.flk_rows_bytes.restype = sz
         L.flk_rows_bytes.argtypes = [i32, ctypes.c_int]
         L.flk_tile_index_bytes.restype = sz
@@ -107,9 +119,11 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def desc(kind: int, H: int, D: int) -> Desc:
+def desc(kind: int, H: int, D: int, k_tiles: bool = False) -> Desc:
+    """k_tiles: K groups per 64-position tile (page-local) instead of per 64 compact rows."""
     d = Desc()
     lib().flk_desc_init(ctypes.byref(d), kind, H, D)
+    d.k_grouping = KGROUP_TILE if k_tiles else KGROUP_ROWS
     return d
 
 
@@ -139,8 +153,16 @@ def codes_bytes(kind: int, H: int, D: int, n: int) -> int:
     return int(lib().flk_codes_bytes(ctypes.byref(desc(kind, H, D)), n))
 
 
-def params_bytes(kind: int, H: int, D: int, n: int) -> int:
-    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D)), n))
+def params_bytes(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = False) -> int:
+    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D, k_tiles)), n, T))
+
+
+def stream_bytes(kind: int, H: int, D: int, n: int, T: int, sparse: bool, k_tiles: bool = False) -> int:
+    return int(lib().flk_stream_bytes(ctypes.byref(desc(kind, H, D, k_tiles)), n, T, 1 if sparse else 0))
+
+
+def rolling_prefix(n_tokens: int) -> int:
+    return int(lib().flk_rolling_prefix(n_tokens))
 
 
 def rows_bytes(n: int, sparse: bool) -> int:
@@ -155,30 +177,39 @@ def attn_workspace_bytes(H: int, D: int, T: int, n_q_heads: int) -> int:
     return int(lib().flk_attn_workspace_bytes(ctypes.byref(desc(K, H, D)), T, n_q_heads))
 
 
-def params_shape(kind: int, H: int, D: int, n: int):
+def params_shape(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = False):
+    if kind == K and k_tiles:
+        return ((T + GROUP - 1) // GROUP, H, D)
     return ((n + GROUP - 1) // GROUP, H, D) if kind == K else (n, H, (D + GROUP - 1) // GROUP)
 
 
 @dataclass
 class Packed:
     """Device buffers of one encoded loop (caller-owned torch tensors).  Compact loops also
-    carry tile_start, the inverse map per 64 positions that flk_encode_residual writes."""
+    carry tile_start, the inverse map per 64 positions that flk_encode_residual writes.
+    k_tiles marks K streams with tile (page-local) groups; it selects the descriptor."""
     n_rows: int
     rows: Optional[torch.Tensor]
     codes: torch.Tensor
     params: torch.Tensor
     tile_start: Optional[torch.Tensor] = None
+    k_tiles: bool = False
 
     @staticmethod
     def empty(kind: int, H: int, D: int, n: int, rows: Optional[torch.Tensor] = None, T: int = 0,
-              tile_start: Optional[torch.Tensor] = None, device="cuda") -> "Packed":
+              tile_start: Optional[torch.Tensor] = None, device="cuda", k_tiles: bool = False,
+              compact: Optional[bool] = None) -> "Packed":
+        """compact: the stream has a tile index (default: when rows is given)."""
+        if k_tiles and kind == K and T < 1:
+            raise ValueError("tile-grouped K needs T to size its params")
+        compact = rows is not None if compact is None else compact
         codes = torch.empty((n, H, D // 2), dtype=torch.uint8, device=device)
-        params = torch.empty(params_shape(kind, H, D, n), dtype=torch.int32, device=device)
-        if rows is not None and tile_start is None:
+        params = torch.empty(params_shape(kind, H, D, n, T, k_tiles), dtype=torch.int32, device=device)
+        if compact and tile_start is None:
             if T < 1:
                 raise ValueError("a compact loop needs T to size its tile index")
             tile_start = torch.empty(tile_index_bytes(T) // 4, dtype=torch.int32, device=device)
-        return Packed(n, rows, codes, params, tile_start if rows is not None else None)
+        return Packed(n, rows, codes, params, tile_start if compact else None, k_tiles and kind == K)
 
     def c(self) -> StreamC:
         return StreamC(self.n_rows, 0, None if self.rows is None else self.rows.data_ptr(),
@@ -196,7 +227,7 @@ def encode_base(kind: int, x: torch.Tensor, out: Packed, recon: torch.Tensor,
     _need(x, torch.bfloat16, "x")
     _need(recon, torch.bfloat16, "recon")
     T, H, D = x.shape
-    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D)), _ptr(x), T, _ptr(out.codes),
+    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D, out.k_tiles)), _ptr(x), T, _ptr(out.codes),
                                  _ptr(out.params), _ptr(recon), _ptr(status), _stream(stream)),
            "flk_encode_base")
 
@@ -209,7 +240,7 @@ def encode_residual(kind: int, x_rows: torch.Tensor, rows: Optional[torch.Tensor
         _need(rows, torch.int32, "rows")
     n, H, D = x_rows.shape
     T = recon.shape[0]
-    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D)), _ptr(x_rows), _ptr(rows), n, T,
+    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D, out.k_tiles)), _ptr(x_rows), _ptr(rows), n, T,
                                      _ptr(recon), _ptr(out.codes), _ptr(out.params), _ptr(out.tile_start),
                                      _ptr(status), _stream(stream)),
            "flk_encode_residual")
@@ -224,7 +255,7 @@ def reconstruct(kind: int, chain: Sequence[Packed], out: torch.Tensor, stream=No
     _need(out, torch.bfloat16, "out")
     T, H, D = out.shape
     arr = _chain(chain)
-    _check(lib().flk_reconstruct(ctypes.byref(desc(kind, H, D)), T, arr, len(chain), _ptr(out),
+    _check(lib().flk_reconstruct(ctypes.byref(desc(kind, H, D, chain[0].k_tiles)), T, arr, len(chain), _ptr(out),
                                  _stream(stream)), "flk_reconstruct")
 
 
@@ -235,13 +266,72 @@ def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequ
     _need(out, torch.bfloat16, "out")
     Hq, D = q.shape
     ka, va = _chain(k_chain), _chain(v_chain)
-    _check(lib().flk_decode_attn_packed(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), T, _ptr(q),
+    _check(lib().flk_decode_attn_packed(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles)), ctypes.byref(desc(V, H, D)),
+                                        T, _ptr(q),
                                         Hq, ka, va, len(k_chain), float(softmax_scale), _ptr(out),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)), "flk_decode_attn_packed")
 
 
+# ----------------------------------------------------------------------------- rolling tail
+
+def append_base(kind: int, x: torch.Tensor, p0: int, out: Packed, recon: torch.Tensor,
+                status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Encode loop 1 of positions [p0, p0 + len(x)) into the stream `out` (its full buffers);
+    recon [len(x), H, D] receives the window's X_hat[1]."""
+    _need(x, torch.bfloat16, "x")
+    _need(recon, torch.bfloat16, "recon")
+    n_pos, H, D = x.shape
+    _check(lib().flk_append_base(ctypes.byref(desc(kind, H, D, out.k_tiles)), _ptr(x), p0, n_pos, _ptr(out.codes),
+                                 _ptr(out.params), _ptr(recon), _ptr(status), _stream(stream)), "flk_append_base")
+
+
+def append_residual(kind: int, x_rows: Optional[torch.Tensor], rows: Optional[torch.Tensor], n_rows: int, p0: int,
+                    n_pos: int, rows_before: int, recon: torch.Tensor, out: Packed,
+                    status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Encode loop r >= 2 of positions [p0, p0 + n_pos) and append it to `out`.  rows: the
+    window's entries of the stream's rows (absolute positions), None for a dense loop;
+    recon [n_pos, H, D]: the window's X_hat[r-1], updated to X_hat[r]."""
+    _need(recon, torch.bfloat16, "recon")
+    if x_rows is not None:
+        _need(x_rows, torch.bfloat16, "x_rows")
+    if rows is not None:
+        _need(rows, torch.int32, "rows")
+    H, D = recon.shape[1], recon.shape[2]
+    _check(lib().flk_append_residual(ctypes.byref(desc(kind, H, D, out.k_tiles)), _ptr(x_rows), _ptr(rows), n_rows,
+                                     p0, n_pos, rows_before, _ptr(recon), _ptr(out.codes), _ptr(out.params),
+                                     _ptr(out.tile_start), _ptr(status), _stream(stream)), "flk_append_residual")
+
+
+def decode_attn_rolling(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int, H: int,
+                        k_tail: Optional[torch.Tensor], v_tail: Optional[torch.Tensor], softmax_scale: float,
+                        out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """Attention over packed positions [0, T) plus the BF16 tail [tail_len, H, D]."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    tail_len = 0
+    if k_tail is not None:
+        _need(k_tail, torch.bfloat16, "k_tail")
+        _need(v_tail, torch.bfloat16, "v_tail")
+        tail_len = k_tail.shape[0]
+    Hq, D = q.shape
+    kt = bool(k_chain) and k_chain[0].k_tiles
+    ka, va = _chain(k_chain), _chain(v_chain)
+    _check(lib().flk_decode_attn_rolling(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), T, _ptr(q),
+                                         Hq, ka, va, len(k_chain), _ptr(k_tail), _ptr(v_tail), tail_len,
+                                         float(softmax_scale), _ptr(out), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "flk_decode_attn_rolling")
+
+
 # ----------------------------------------------------------------------------- batched calls
+
+def _k_tiles(flags) -> bool:
+    """One K descriptor covers every K unit of a batched call, so their groupings must agree."""
+    flags = set(flags)
+    if len(flags) > 1:
+        raise ValueError("the K units of one batched call must share their K grouping")
+    return bool(flags and flags.pop())
 
 def _unit(kind: int, x: Optional[torch.Tensor], rows: Optional[torch.Tensor], recon: torch.Tensor,
           out: "Packed") -> UnitC:
@@ -260,7 +350,8 @@ def encode_base_batch(items, H: int, D: int, status: Optional[torch.Tensor] = No
     """items: (kind, x [T, H, D], recon [T, H, D], out Packed) per tensor; one call for all."""
     units = [_unit(kind, x, None, recon, out) for kind, x, recon, out in items]
     arr = (UnitC * max(1, len(units)))(*units)
-    _check(lib().flk_encode_base_batch(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), arr, len(units),
+    kt = _k_tiles(out.k_tiles for kind, _, _, out in items if kind == K)
+    _check(lib().flk_encode_base_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), arr, len(units),
                                        _ptr(status), _stream(stream)), "flk_encode_base_batch")
 
 
@@ -268,7 +359,8 @@ def encode_residual_batch(items, H: int, D: int, status: Optional[torch.Tensor] 
     """items: (kind, x_rows [n, H, D], rows or None, recon [T, H, D], out Packed) per tensor."""
     units = [_unit(kind, x, rows, recon, out) for kind, x, rows, recon, out in items]
     arr = (UnitC * max(1, len(units)))(*units)
-    _check(lib().flk_encode_residual_batch(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), arr,
+    kt = _k_tiles(out.k_tiles for kind, _, _, _, out in items if kind == K)
+    _check(lib().flk_encode_residual_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), arr,
                                            len(units), _ptr(status), _stream(stream)), "flk_encode_residual_batch")
 
 
@@ -282,6 +374,7 @@ def reconstruct_batch(items, H: int, D: int, stream=None) -> None:
         units.append(ReconUnitC(ctypes.cast(arr, ctypes.POINTER(StreamC)), out.data_ptr(), out.shape[0], len(chain),
                                 kind, 0))
     tab = (ReconUnitC * max(1, len(units)))(*units)
-    _check(lib().flk_reconstruct_batch(ctypes.byref(desc(K, H, D)), ctypes.byref(desc(V, H, D)), tab, len(units),
+    kt = _k_tiles(chain[0].k_tiles for kind, chain, _ in items if kind == K)
+    _check(lib().flk_reconstruct_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), tab, len(units),
                                        _stream(stream)), "flk_reconstruct_batch")
 

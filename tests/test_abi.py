@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert "flk_encode_base" in names and "flk_decode_attn_packed" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.flk_abi_version() == 1
+    assert L.flk_abi_version() == 2
 
 
 @pytest.mark.parametrize("kind", [flk.K, flk.V])
@@ -42,16 +42,42 @@ def test_sizes_match_closed_forms(kind, H, D, n):
     assert flk.tile_index_bytes(n) == 4 * (-(-n // 64) + 1) == orc.tile_index(np.arange(0), n).nbytes
 
 
+@pytest.mark.parametrize("H,D,n,T", [(1, 8, 1, 1), (2, 64, 100, 256), (8, 96, 500, 1000), (8, 128, 8192, 32768),
+                                     (3, 24, 0, 65)])
+def test_tile_grouped_sizes(H, D, n, T):
+    """Tile-grouped K stores one parameter row per 64-position tile, whatever the stream's
+    row count; V and dense K are unchanged; stream_bytes adds rows and the tile index."""
+    assert flk.params_bytes(flk.K, H, D, n, T, k_tiles=True) == orc.k_tile_params_bytes(H, D, T)
+    assert flk.params_bytes(flk.K, H, D, T, T, k_tiles=True) == flk.params_bytes(flk.K, H, D, T)
+    assert flk.params_bytes(flk.V, H, D, n, T, k_tiles=True) == orc.params_bytes(flk.V, H, D, n)
+    for kind in (flk.K, flk.V):
+        for kt in (False, True):
+            want = (orc.codes_bytes(H, D, n) + flk.params_bytes(kind, H, D, n, T, kt) + 4 * n +
+                    4 * (-(-T // 64) + 1))
+            assert flk.stream_bytes(kind, H, D, n, T, True, kt) == want
+    assert flk.stream_bytes(flk.K, H, D, T, T, False) == orc.codes_bytes(H, D, T) + orc.params_bytes(flk.K, H, D, T)
+
+
+def test_rolling_prefix_matches_oracle():
+    for n in list(range(-3, 1200)) + [32767, 131072, 131072 + 127, 2**31 - 1]:
+        assert flk.rolling_prefix(n) == (orc.rolling_prefix(n) if n >= 0 and n < 10**6 else
+                                         (0 if n < 128 else ((n - 64) // 64) * 64)), n
+
+
 def test_descriptor_checks():
     L = flk.lib()
     d = flk.desc(flk.K, 8, 128)
     assert L.flk_desc_check(ctypes.byref(d)) == 0
     assert L.flk_desc_check(None) == 1
-    for field, bad in [("abi_version", 2), ("format", 0), ("kind", 2), ("group", 32), ("param_dtype", 0),
-                       ("nibble_order", 2)]:
+    for field, bad in [("abi_version", 1), ("format", 0), ("kind", 2), ("group", 32), ("param_dtype", 0),
+                       ("nibble_order", 2), ("k_grouping", 2)]:
         e = flk.desc(flk.K, 8, 128)
         setattr(e, field, bad)
         assert L.flk_desc_check(ctypes.byref(e)) == 4, field
+    e = flk.desc(flk.K, 8, 128, k_tiles=True)
+    assert L.flk_desc_check(ctypes.byref(e)) == 0
+    e.reserved[1] = 1
+    assert L.flk_desc_check(ctypes.byref(e)) == 4
     for H, D in [(0, 128), (8, 0), (8, 4), (8, 100), (8, 520), (-1, 64)]:
         assert L.flk_desc_check(ctypes.byref(flk.desc(flk.V, H, D))) == 2, (H, D)
     assert flk.codes_bytes(flk.K, 8, 100, 10) == 0
@@ -199,3 +225,60 @@ def test_batch_validation():
     assert rec([R(good, FAKE.value, 64, 1, flk.K, 3)]) == 4
     assert rec([R(good, None, 64, 1, flk.K, 0)]) == 1
     assert rec([R(good, FAKE.value, 65, 1, flk.K, 0)]) == 2      # base must have n == T
+
+
+def test_append_validation():
+    L = flk.lib()
+    kt = flk.desc(flk.K, 2, 64, k_tiles=True)
+    kr = flk.desc(flk.K, 2, 64)
+    vd = flk.desc(flk.V, 2, 64)
+
+    def base(d, p0=64, n_pos=128, x=FAKE, codes=FAKE, recon=FAKE):
+        return L.flk_append_base(ctypes.byref(d), x, p0, n_pos, codes, FAKE, recon, None, None)
+    assert base(kt, p0=32) == 2
+    assert base(kt, n_pos=100) == 2
+    assert base(kt, n_pos=0) == 2
+    assert base(kt, p0=-64) == 2
+    assert base(kt, x=None) == 1
+    assert base(kt, codes=MIS) == 3
+    big = flk.desc(flk.K, 16, 512)
+    assert base(big, p0=1 << 18, n_pos=64) == 2
+
+    def resid(d, rows=FAKE, n=10, p0=64, n_pos=128, before=20, x=FAKE, tile=FAKE, recon=FAKE):
+        return L.flk_append_residual(ctypes.byref(d), x, rows, n, p0, n_pos, before, recon, FAKE, FAKE, tile,
+                                     None, None)
+    assert resid(kr) == 5                       # compact K needs tile groups
+    assert resid(kt, n=129) == 2
+    assert resid(kt, before=65) == 2            # more rows before p0 than positions
+    assert resid(kt, before=-1) == 2
+    assert resid(kt, p0=65) == 2
+    assert resid(kt, rows=None, n=100) == 2     # dense needs n == n_pos
+    assert resid(kt, rows=None, n=128, before=10) == 2   # and rows_before == p0
+    assert resid(kt, tile=None) == 1
+    assert resid(vd, tile=None) == 1
+    assert resid(kt, x=None) == 1
+    assert resid(kt, recon=None) == 1
+    assert resid(kt, rows=MIS) == 3
+    assert resid(vd, x=MIS) == 3
+
+
+def test_rolling_attention_validation():
+    L = flk.lib()
+    kd, vd = flk.desc(flk.K, 8, 128), flk.desc(flk.V, 8, 128)
+    S = flk.StreamC
+    T = 256
+    chain = (S * 1)(S(T, 0, None, FAKE.value, FAKE.value, None))
+    ws = flk.attn_workspace_bytes(8, 128, T, 32)
+    assert flk.attn_workspace_bytes(8, 128, 0, 32) == 32 * 130 * 4     # the tail's partial alone
+
+    def call(T=T, tail=FAKE, tl=100, w=FAKE, wb=ws, n_loops=1, q=FAKE):
+        return L.flk_decode_attn_rolling(ctypes.byref(kd), ctypes.byref(vd), T, q, 32, chain, chain, n_loops,
+                                         tail, tail, tl, 0.088, FAKE, w, wb, None)
+    assert call(T=0, tl=0) == 2                 # nothing to attend to
+    assert call(T=-1) == 2
+    assert call(tl=-1) == 2
+    assert call(tail=None) == 1
+    assert call(tail=MIS) == 3
+    assert call(wb=ws - 1) == 6
+    assert call(q=None) == 1
+    assert call(n_loops=0) == 2
