@@ -47,24 +47,27 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- bytes
 
-def stream_bytes(kind, H, D, n, sparse):
-    return flk.codes_bytes(kind, H, D, n) + flk.params_bytes(kind, H, D, n) + flk.rows_bytes(n, sparse)
+def stream_bytes(kind, H, D, n, T, sparse, k_tiles=False):
+    return flk.codes_bytes(kind, H, D, n) + flk.params_bytes(kind, H, D, n, T, k_tiles) + flk.rows_bytes(n, sparse)
 
 
-def call_bytes(kind, H, D, T, rows_list):
-    """Algorithmic bytes of each call of one tensor's chain, in launch order."""
+def call_bytes(kind, H, D, T, rows_list, k_tiles=False):
+    """Algorithmic bytes of each call of one tensor's chain, in launch order.  With tile
+    (page-local) K groups a compact loop's params are one row per tile."""
     e = 2  # BF16
     W = H * D
     # base: read X, write codes + params, write recon
-    out = [("base", e * T * W + flk.codes_bytes(kind, H, D, T) + flk.params_bytes(kind, H, D, T) + e * T * W)]
+    out = [("base", e * T * W + flk.codes_bytes(kind, H, D, T) + flk.params_bytes(kind, H, D, T, T, k_tiles)
+            + e * T * W)]
     for rows in rows_list[1:]:
         n = T if rows is None else len(rows)
         sparse = rows is not None
         # read X_r rows, read recon at rows, write codes + params, write recon at rows, read rows
-        b = e * n * W + e * n * W + flk.codes_bytes(kind, H, D, n) + flk.params_bytes(kind, H, D, n) \
+        b = e * n * W + e * n * W + flk.codes_bytes(kind, H, D, n) + flk.params_bytes(kind, H, D, n, T, k_tiles) \
             + e * n * W + flk.rows_bytes(n, sparse)
         out.append(("dense_residual" if not sparse else "sparse_residual", b))
-    rec = sum(stream_bytes(kind, H, D, T if r is None else len(r), r is not None) for r in rows_list) + e * T * W
+    rec = sum(stream_bytes(kind, H, D, T if r is None else len(r), T, r is not None, k_tiles) for r in rows_list) \
+        + e * T * W
     out.append(("reconstruct", rec))
     return out
 
@@ -113,16 +116,17 @@ def kernel_symbol(kind, call, H, D, rows_list):
 class ChainSet:
     """One independent set of device buffers for the K and V chains."""
 
-    def __init__(self, w, host, sets, batched=True):
+    def __init__(self, w, host, sets, batched=True, k_tiles=False):
         self.tensors = []
         self.batched = batched
+        self.k_tiles = k_tiles
         H, D, T = w.H, w.D, w.T
         for kind in (flk.K, flk.V):
             xs = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in host[kind].xs]
             rows = [None if r is None else torch.from_numpy(r).cuda() for r in sets]
             recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
             out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
-            packed = [flk.Packed.empty(kind, H, D, x.shape[0], r, T=T) for x, r in zip(xs, rows)]
+            packed = [flk.Packed.empty(kind, H, D, x.shape[0], r, T=T, k_tiles=k_tiles) for x, r in zip(xs, rows)]
             self.tensors.append((kind, xs, rows, recon, out, packed))
         self._prepare(w)
 
@@ -134,7 +138,7 @@ class ChainSet:
         self._keep = []
         P = ctypes.c_void_p
         if self.batched:
-            kd, vd = flk.desc(flk.K, w.H, w.D), flk.desc(flk.V, w.H, w.D)
+            kd, vd = flk.desc(flk.K, w.H, w.D, self.k_tiles), flk.desc(flk.V, w.H, w.D)
             self._keep += [kd, vd]
             n_loops = len(self.tensors[0][1])
             for l in range(n_loops):
@@ -162,7 +166,7 @@ class ChainSet:
                                (ctypes.byref(kd), ctypes.byref(vd), rarr, len(runits))))
             return
         for kind, xs, rows, recon, out, packed in self.tensors:
-            d = flk.desc(kind, w.H, w.D)
+            d = flk.desc(kind, w.H, w.D, self.k_tiles)
             self._keep.append(d)
             dp = ctypes.byref(d)
             self.calls.append(("base", kind, L.flk_encode_base,
@@ -193,6 +197,49 @@ class ChainSet:
                 raise flk.FlkError(st, name)
             if ev is not None and ev[i] is not None:
                 ev[i][1].record(ts)
+
+
+# ----------------------------------------------------------------------------- page-local K groups
+
+def page_local_leg(w, host, sets, streams, steps, warmup, rotate):
+    """The same step with tile (page-local) K groups: every K group owns the compact rows of one
+    64-position tile, so a page's metadata never mixes with distant positions.  Same timing
+    procedure as the headline (continuous warmup, then `steps` steps between synchronizations);
+    its bytes count one K parameter row per tile for the compact loops.  Also each K call timed
+    alone."""
+    cs = [ChainSet(w, host, sets, batched=False, k_tiles=True) for _ in range(rotate)]
+    per_call = []
+    for kind in (flk.K, flk.V):
+        per_call += [(kind, name, b) for name, b in call_bytes(kind, w.H, w.D, w.T, sets, k_tiles=kind == flk.K)]
+    step_bytes = sum(b for _, _, b in per_call)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        cs[i % rotate].run(streams)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        cs[k % rotate].run(streams)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    iso_stream = torch.cuda.Stream()
+    iso_streams = {k: (iso_stream, ctypes.c_void_p(iso_stream.cuda_stream)) for k in (flk.K, flk.V)}
+    n_calls = len(cs[0].calls)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    iso = np.zeros(n_calls)
+    for k in range(10):
+        cs[k % rotate].run(iso_streams, ev)
+        torch.cuda.synchronize()
+        iso += np.array([a.elapsed_time(b) for a, b in ev])
+    iso_us = iso / 10 * 1e3
+    k_calls = [{"call": name, "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
+               for (kind, name, b), t in zip(per_call, iso_us) if kind == flk.K]
+    rows_k = call_bytes(flk.K, w.H, w.D, w.T, sets)
+    return {"k_grouping": "tile", "value": round(step_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_bytes": int(step_bytes), "steps": steps, "warmup": warmup,
+            "extra_param_bytes_vs_rows": int(sum(b for _, b in call_bytes(flk.K, w.H, w.D, w.T, sets, True))
+                                             - sum(b for _, b in rows_k)),
+            "k_calls_isolated": k_calls}
 
 
 # ----------------------------------------------------------------------------- cpu baseline
@@ -411,6 +458,7 @@ def main():
                          "on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
+    ap.add_argument("--no-page-local", action="store_true", help="skip the page-local K grouping leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -536,6 +584,9 @@ def main():
     result["isolated_step_us"] = round(float(iso_us.sum()), 2)
     if copy_gbs is not None:
         result["copy_probe_gbs"] = round(copy_gbs, 1)
+    if not args.no_page_local and args.mode != "batched":
+        log("the same step with page-local K groups ...")
+        result["page_local"] = page_local_leg(w, host, sets, streams, args.steps, args.warmup, args.rotate)
     if not args.no_attention:
         log("decode attention over the packed chains ...")
         result["decode_attention"] = attention_leg()

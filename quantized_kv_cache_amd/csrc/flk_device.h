@@ -274,6 +274,11 @@ __device__ __forceinline__ float dpp_half_mirror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
 }
 
+// row_ror:8: lane i of each row of 16 reads lane (i + 8) mod 16, i.e. lane i ^ 8.
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
 // ---- nontemporal (streaming) global accesses ----------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -315,15 +320,28 @@ __device__ __forceinline__ void write_tile_index(const int32_t* __restrict__ row
     for (int32_t t = t_last + 1; t <= ntiles; ++t) tile_start[t] = row0 + n;
 }
 
-// First index of the ascending rows[0..n) whose value is >= key.
-__device__ __forceinline__ int32_t lower_bound_rows(const int32_t* __restrict__ rows, int32_t n,
-                                                    int32_t key) {
-  int32_t lo = 0, hi = n;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (rows[mid] < key) lo = mid + 1; else hi = mid;
+// lower_bound over an ascending array, computed by a whole 256-thread block in
+// ceil(log256(n)) rounds of one parallel probe each (instead of log2(n) dependent loads):
+// each round probes 256 evenly spaced entries of the current bracket and keeps the one
+// stride that contains the first entry >= key.  Every thread returns the same value.
+// Contains __syncthreads_count(); call from all threads of the block.
+__device__ __forceinline__ int32_t block_lower_bound(const int32_t* __restrict__ rows, int32_t n,
+                                                     int32_t key) {
+  int32_t a = 0, b = n;                    // the answer lies in [a, b]
+  while (a < b) {
+    const int32_t s = (b - a + 255) / 256;
+    const int32_t idx = a + int32_t(threadIdx.x) * s;
+    const bool pred = idx < b && rows[idx] < key;
+    const int32_t c = __syncthreads_count(pred);
+    if (c == 0) return a;
+    const int32_t na = a + (c - 1) * s + 1;
+    const int32_t nb = min(a + c * s, b);
+    if (s == 1) return nb;
+    a = na;
+    b = nb;
   }
-  return lo;
+  return a;
 }
+
 
 }  // namespace flk

@@ -42,10 +42,173 @@ __device__ __forceinline__ uint4 pack8(const float v[8]) {
 }
 
 // ---------------------------------------------------------------------------------------
+// K, tile (page-local) groups, compact loops: a wave owns the compact rows of one
+// 64-position tile (0 to 64 of them) for 64 channels, and the 4 waves of a block take
+// neighbouring channel strips.  Lane (rs, cc) = (lane >> 3, lane & 7) holds 8 channels of
+// octet cc for rows rs, rs + 8, ... of the tile: 8 consecutive lanes cover one row's 128
+// bytes, so every load and store merges like a row-major access.  A group's extremes take
+// a reduce-scatter across the row-slot lanes (two cross-row shuffles and a DPP rotation,
+// halving the channels each step) -- no LDS, no barrier -- after which each lane derives
+// and writes the params of one channel of its octet (one 256-byte store per wave) and the
+// octet exchanges them.  A tile holds few rows
+// at low retention, so many independent short waves hide the load latency better than a
+// block reduction would.  The tile's row range comes from the tile index, which
+// tile_index_kernel writes first (a search per wave would put several dependent loads in
+// front of every wave's data loads).
+// ---------------------------------------------------------------------------------------
+template <bool RESID>
+__device__ __forceinline__ void encode_k_tile_body(const EncArgs& a, uint32_t item) {
+  const int32_t* __restrict__ rows = a.rows;
+  uint16_t* __restrict__ recon = a.recon;
+  const int32_t n = a.n, T = a.T, W = a.W, pos0 = a.pos0;
+  const int lane = threadIdx.x & 63;
+  const uint32_t nstrips = (uint32_t(W >> 3) + 7u) / 8u;
+  const int32_t tile = int32_t(item / nstrips);
+  const uint32_t strip = item - uint32_t(tile) * nstrips;
+  if (tile >= (T + kGroup - 1) / kGroup) return;          // wave-uniform
+  const int cc = lane & 7, rs = lane >> 3;
+  const int32_t chunk = int32_t(strip) * 8 + cc;
+  const bool cact = chunk < (W >> 3);
+  const int64_t ch = int64_t(chunk) * 8;
+
+  // the tile's compact rows [jbeg, jend), from the tile index tile_index_kernel wrote (its
+  // entries count the stream's rows before the window too); clamped so a malformed map
+  // never addresses outside the rows
+  const int32_t jbeg = min(max(uniform(a.tile_start[tile]) - a.row0, 0), n);
+  const int32_t jend = min(max(uniform(a.tile_start[tile + 1]) - a.row0, jbeg), min(n, jbeg + kGroup));
+
+  // per row: the residual (or value) as 8 packed BF16 and its position.  The predecessor row
+  // is read again for the final add (an L2 hit) instead of being held in registers: the
+  // register budget decides how many of these latency-bound waves a SIMD keeps in flight.
+  constexpr int kR = kGroup / 8;                           // rows per lane at most
+  uint4 dv[kR];
+  int32_t pos[kR];
+  bool bad_row = false;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int32_t j = jbeg + rs + 8 * i;
+    pos[i] = -1;
+    dv[i] = make_uint4(0, 0, 0, 0);
+    if (cact && j < jend) {
+      const int32_t p = rows[j] - pos0;
+      if (uint32_t(p) >= uint32_t(T)) bad_row = true;      // malformed map: never address outside recon
+      else pos[i] = p;
+    }
+  }
+  uint4 rv[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    rv[i] = make_uint4(0, 0, 0, 0);
+    if (pos[i] >= 0) {
+      dv[i] = ld_stream(a.x + int64_t(jbeg + rs + 8 * i) * W + ch);
+      if (RESID) rv[i] = *reinterpret_cast<const uint4*>(recon + int64_t(pos[i]) * W + ch);
+    }
+  }
+  if (bad_row && a.status) atomicOr(a.status, kDevRows);
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    if (pos[i] < 0) continue;
+    float v[8];
+    unpack8(dv[i], v);
+    if (RESID) {
+      float r[8];
+      unpack8(rv[i], r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e] - r[e]);
+      dv[i] = pack8(v);                                     // exact: the values are BF16
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { mn[e] = tmin(mn[e], v[e]); mx[e] = tmax(mx[e], v[e]); }
+  }
+  // Reduce-scatter over the 8 row-slot lanes of each octet (lane bits 5, 4, 3): every step
+  // halves the channels a lane carries, so lane (rs, cc) ends with the extremes of channel
+  // rs of its octet; it derives that channel's params alone and the octet shares them.
+  const bool b2 = (rs & 4) != 0, b1 = (rs & 2) != 0, b0 = (rs & 1) != 0;
+  float mn4[4], mx4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {                            // keep channels 4*b2 + q
+    const float smn = b2 ? mn[q] : mn[q + 4], smx = b2 ? mx[q] : mx[q + 4];
+    const float kmn = b2 ? mn[q + 4] : mn[q], kmx = b2 ? mx[q + 4] : mx[q];
+    mn4[q] = tmin(kmn, __shfl_xor(smn, 32));
+    mx4[q] = tmax(kmx, __shfl_xor(smx, 32));
+  }
+  float mn2[2], mx2[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {                            // keep channels 4*b2 + 2*b1 + q
+    const float smn = b1 ? mn4[q] : mn4[q + 2], smx = b1 ? mx4[q] : mx4[q + 2];
+    const float kmn = b1 ? mn4[q + 2] : mn4[q], kmx = b1 ? mx4[q + 2] : mx4[q];
+    mn2[q] = tmin(kmn, __shfl_xor(smn, 16));
+    mx2[q] = tmax(kmx, __shfl_xor(smx, 16));
+  }
+  // keep channel 4*b2 + 2*b1 + b0 = rs
+  const float smn = b0 ? mn2[0] : mn2[1], smx = b0 ? mx2[0] : mx2[1];
+  const float gmn = tmin(b0 ? mn2[1] : mn2[0], dpp_ror8(smn));
+  const float gmx = tmax(b0 ? mx2[1] : mx2[0], dpp_ror8(smx));
+  const bool empty = jend <= jbeg;
+  const GroupParams own = make_params(gmn, gmx);
+  const uint32_t mine = empty ? 0u : own.packed;
+  if (cact) {
+    st_stream32(a.params + int64_t(tile) * W + ch + rs, mine);
+    if (!empty && own.err && a.status) atomicOr(a.status, own.err);
+  }
+  // the octet's 8 params (lane e*8 + cc holds channel e)
+  float gm[8], gs[8], grs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = uint32_t(__shfl(int(mine), e * 8 + cc));
+    gm[e] = f16_bits_to_f32(w & 0xFFFFu);
+    gs[e] = f16_bits_to_f32(w >> 16);
+    grs[e] = gs[e] == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(gs[e]);
+  }
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    if (pos[i] < 0) continue;
+    const int32_t j = jbeg + rs + 8 * i;
+    uint16_t* rp = recon + int64_t(pos[i]) * W + ch;
+    float v[8], k[8], out[8];
+    unpack8(dv[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      GroupParams g;
+      g.m = gm[e];
+      g.s = gs[e];
+      g.rs = grs[e];
+      k[e] = code_of(v[e], g);
+      out[e] = decode(k[e], gm[e], gs[e]);
+    }
+    if (RESID) {
+      float r[8];
+      unpack8(*reinterpret_cast<const uint4*>(rp), r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
+    }
+    st_stream32(a.codes + ((int64_t(j) * W + ch) >> 1), pack_codes8(k));
+    *reinterpret_cast<uint4*>(rp) = pack8(out);
+  }
+}
+
+// The tile index of a compact loop (one thread per compact row), written before the
+// tile-grouped K encoder runs, which reads each tile's row range from it.
+__device__ __forceinline__ void tile_index_body(const EncArgs& a, uint32_t blk) {
+  const int64_t j = int64_t(blk) * kThreads + threadIdx.x;
+  if (j < a.n) write_tile_index(a.rows, a.n, a.T, int32_t(j), a.tile_start, a.pos0, a.row0);
+}
+__global__ __launch_bounds__(kThreads) void tile_index_kernel(EncArgs a) { tile_index_body(a, blockIdx.x); }
+
+// Tile-grouped compact K loops: 4 waves per block, each on its own (tile, strip) item.
+template <bool RESID>
+__global__ __launch_bounds__(kThreads) void encode_k_tile_kernel(EncArgs a) {
+  const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
+  encode_k_tile_body<RESID>(a, blk * (kThreads / 64) + (threadIdx.x >> 6));
+}
+
+// ---------------------------------------------------------------------------------------
 // K: groups run down 64 compact rows of one (head, channel).  A block owns one 64-row band
 // of a 128-channel (64 for compact loops) strip of the flattened H*D channel axis.  With
-// tile groups (page-local, a.ktile) a compact loop's band is instead the rows of one
-// 64-position tile, 0 to 64 of them, found by binary search in rows.
+// tile groups (page-local, a.ktile) compact loops run encode_k_tile_body instead.
 // Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs + slots, ... (4 rows each
 // at 128 channels, 2 at 64).  Extremes: in registers over its rows, across the row slots of a
 // wave with lane shuffles, across the 4 waves through LDS; one thread per channel then derives
@@ -79,12 +242,7 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
   const bool cact = chunk < (W >> 3);
   const int64_t ch = int64_t(chunk) * 8;
   // the band's compact rows [jbeg, jend)
-  int32_t jbeg = band * kGroup, jend = min(n, jbeg + kGroup);
-  if (SPARSE && a.ktile) {
-    const int32_t key = pos0 + band * kGroup;
-    jbeg = uniform(lower_bound_rows(rows, n, key));
-    jend = uniform(min(lower_bound_rows(rows, n, key + kGroup), jbeg + kGroup));
-  }
+  const int32_t jbeg = band * kGroup, jend = min(n, jbeg + kGroup);
 
   float v[kKRows][8];
   uint4 rv[kKRows];
@@ -156,10 +314,6 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
     const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
     const int64_t chan = int64_t(strip) * kKCW + tid;
     GroupParams p = make_params(a, b);
-    if (jend <= jbeg) {                      // an empty tile: no group, params 0
-      p.packed = 0;
-      p.err = 0;
-    }
     s_m[tid] = p.m;
     s_s[tid] = p.s;
     s_rs[tid] = p.rs;
@@ -438,11 +592,15 @@ static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) {
   const int32_t waves = (n + rpw - 1) / rpw;
   return dim3(unsigned((waves + 3) / 4), unsigned(W / 1024));
 }
-// x: channel strips; y: 64-row bands, or the window's 64-position tiles for tile groups
+// x: channel strips, y: 64-row bands; tile groups of a compact loop: one wave per (tile,
+// 64-channel strip), 4 waves per block along x
 static dim3 k_grid(const EncArgs& a, bool sparse) {
+  if (sparse && a.ktile) {
+    const int64_t waves = int64_t((a.W / 8 + 7) / 8) * ((a.T + kGroup - 1) / kGroup);
+    return dim3(unsigned((waves + 3) / 4), 1);
+  }
   const int chunks = (sparse ? k_block_channels<true>() : k_block_channels<false>()) / 8;
-  const int32_t bands = sparse && a.ktile ? a.T : a.n;
-  return dim3(unsigned((a.W / 8 + chunks - 1) / chunks), unsigned((bands + kGroup - 1) / kGroup));
+  return dim3(unsigned((a.W / 8 + chunks - 1) / chunks), unsigned((a.n + kGroup - 1) / kGroup));
 }
 
 template <bool RESID, bool SPARSE>
@@ -476,7 +634,12 @@ static hipError_t launch_v(const EncArgs& a, int32_t H, int32_t D, hipStream_t s
 
 template <bool RESID, bool SPARSE>
 static hipError_t launch_k(const EncArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a, SPARSE), dim3(kThreads), 0, stream, a);
+  if (SPARSE && a.ktile) {
+    hipLaunchKernelGGL(tile_index_kernel, dim3(unsigned((a.n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL((encode_k_tile_kernel<RESID>), k_grid(a, SPARSE), dim3(kThreads), 0, stream, a);
+  } else
+    hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a, SPARSE), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -530,7 +693,7 @@ struct EncBatch {
 
 static_assert(sizeof(EncBatch) <= 4096, "a batch travels as kernel arguments (4 KiB at most)");
 
-template <bool RESID, bool SPARSE>
+template <bool RESID, bool SPARSE, bool KTILE>
 __global__ __launch_bounds__(kThreads) void encode_batch_kernel(EncBatch b) {
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
   int ui = 0;
@@ -540,8 +703,21 @@ __global__ __launch_bounds__(kThreads) void encode_batch_kernel(EncBatch b) {
   const EncUnit& u = b.u[ui];
   const uint32_t lb = bid - u.block0;
   const uint32_t by = lb / u.gx, bx = lb - by * u.gx;
-  if (u.kind == FLK_KIND_K) encode_k_body<RESID, SPARSE>(u.a, bx, by);
-  else encode_v_wide_body<RESID, SPARSE>(u.a, u.rpw, bx, by);
+  if (u.kind == FLK_KIND_K) {
+    if (SPARSE && KTILE) encode_k_tile_body<RESID>(u.a, bx * (kThreads / 64) + (threadIdx.x >> 6));
+    else encode_k_body<RESID, SPARSE>(u.a, bx, by);
+  } else {
+    encode_v_wide_body<RESID, SPARSE>(u.a, u.rpw, bx, by);
+  }
+}
+
+// The tile indexes of a batch's tile-grouped compact K units, before their encode.
+__global__ __launch_bounds__(kThreads) void tile_index_batch_kernel(EncBatch b) {
+  int ui = 0;
+#pragma unroll
+  for (int i = 1; i < kEncBatch; ++i)
+    if (i < b.n_units && blockIdx.x >= b.u[i].block0) ui = i;
+  tile_index_body(b.u[ui].a, blockIdx.x - b.u[ui].block0);
 }
 
 bool encode_batchable(int kind, int32_t H, int32_t D) { return kind == FLK_KIND_K || v_wide_ok(H, D); }
@@ -551,8 +727,10 @@ hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, con
   for (int u0 = 0; u0 < n_units; u0 += kEncBatch) {
     EncBatch b{};
     uint32_t blocks = 0;
+    bool ktile = false;                         // the K units' grouping (one K descriptor per call)
     for (int i = u0; i < n_units && i < u0 + kEncBatch; ++i) {
       if (args[i].n <= 0) continue;
+      if (kinds[i] == FLK_KIND_K && args[i].ktile) ktile = true;
       EncUnit& e = b.u[b.n_units++];
       e.a = args[i];
       e.kind = kinds[i];
@@ -569,12 +747,27 @@ hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, con
       blocks += g.x * g.y;
     }
     if (blocks == 0) continue;
+    if (sparse && ktile) {
+      EncBatch tb{};
+      uint32_t tblocks = 0;
+      for (int i = 0; i < b.n_units; ++i) {
+        if (b.u[i].kind != FLK_KIND_K) continue;
+        EncUnit& e = tb.u[tb.n_units++];
+        e = b.u[i];
+        e.block0 = tblocks;
+        tblocks += uint32_t((e.a.n + kThreads - 1) / kThreads);
+      }
+      if (tblocks > 0)
+        hipLaunchKernelGGL(tile_index_batch_kernel, dim3(tblocks), dim3(kThreads), 0, stream, tb);
+    }
     if (!resid)
-      hipLaunchKernelGGL((encode_batch_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
+      hipLaunchKernelGGL((encode_batch_kernel<false, false, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
     else if (!sparse)
-      hipLaunchKernelGGL((encode_batch_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
+      hipLaunchKernelGGL((encode_batch_kernel<true, false, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
+    else if (!ktile)
+      hipLaunchKernelGGL((encode_batch_kernel<true, true, false>), dim3(blocks), dim3(kThreads), 0, stream, b);
     else
-      hipLaunchKernelGGL((encode_batch_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, stream, b);
+      hipLaunchKernelGGL((encode_batch_kernel<true, true, true>), dim3(blocks), dim3(kThreads), 0, stream, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

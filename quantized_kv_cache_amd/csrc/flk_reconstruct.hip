@@ -16,30 +16,6 @@
 
 namespace flk {
 
-// lower_bound over an ascending array, computed by a whole 256-thread block in
-// ceil(log256(n)) rounds of one parallel probe each (instead of log2(n) dependent loads):
-// each round probes 256 evenly spaced entries of the current bracket and keeps the one
-// stride that contains the first entry >= key.  Every thread returns the same value.
-// Contains __syncthreads_count(); call from all threads of the block.
-__device__ __forceinline__ int32_t block_lower_bound(const int32_t* __restrict__ rows, int32_t n,
-                                                     int32_t key) {
-  int32_t a = 0, b = n;                    // the answer lies in [a, b]
-  while (a < b) {
-    const int32_t s = (b - a + 255) / 256;
-    const int32_t idx = a + int32_t(threadIdx.x) * s;
-    const bool pred = idx < b && rows[idx] < key;
-    const int32_t c = __syncthreads_count(pred);
-    if (c == 0) return a;
-    const int32_t na = a + (c - 1) * s + 1;
-    const int32_t nb = min(a + c * s, b);
-    if (s == 1) return nb;
-    a = na;
-    b = nb;
-  }
-  return a;
-}
-
-
 #ifndef FLK_RECON_BATCH
 #define FLK_RECON_BATCH 4
 #endif
