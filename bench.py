@@ -319,6 +319,154 @@ def attention_leg(reps=20):
             "reconstruct_then_attend_bytes": int(rta)}
 
 
+# ----------------------------------------------------------------------------- rolling tail
+
+def _timed_us(fn, reps, flush=None):
+    """Median of `reps` calls of fn (HIP events on the current stream); `flush`, when given, is
+    written before each call so the MALL holds none of fn's data."""
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(times))
+
+
+def rolling_leg(reps=50):
+    """The rolling BF16 tail (RFC section 3.3): decode tokens wait in BF16 until a whole
+    64-token group can be flushed into the packed streams, whose K groups are tile-local.
+
+    flush: one decode step's flush for a request of the batched-cache shape (24 layers, K and V,
+    16 KV heads, D=128, 4 loops): the 64-position window [4096, 4160) appended to every
+    layer's streams -- loops 1-2 dense, loops 3/4 over the window's tokens that ran that deep
+    (seeded exit depths: a half reach loop 3, a quarter loop 4).  Timed as 4 batched calls
+    (flk_append_base_batch + 3 x flk_append_residual_batch, 48 tensors each) and as 192
+    one-tensor calls, back to back with the unit tables prepared once.  attention: flk_decode_attn_rolling over the decode workload's 131072 packed
+    tokens (tile-grouped K) plus a 127-token BF16 tail, next to flk_decode_attn_packed over
+    the same packed tokens alone."""
+    out = {}
+    H, D, layers, p0, win = 16, 128, 24, 4096, 64
+    rng = np.random.default_rng(20261202)
+    u = rng.random(win)
+    depth = np.where(u < 0.25, 4, np.where(u < 0.5, 3, 2))
+    rows_w = [None, None, (p0 + np.nonzero(depth >= 3)[0]).astype(np.int32),
+              (p0 + np.nonzero(depth >= 4)[0]).astype(np.int32)]
+    before = [p0, p0, p0 // 2, p0 // 4]                # compact rows already in the streams
+    T_cap = p0 + win
+    units = []
+    for layer in range(layers):
+        for kind in (flk.K, flk.V):
+            xs = [torch.randn((win if r is None else len(r), H, D), device="cuda").to(torch.bfloat16)
+                  for r in rows_w]
+            recon = torch.empty((win, H, D), dtype=torch.bfloat16, device="cuda")
+            packs = []
+            for l, r in enumerate(rows_w):
+                n_cap = before[l] + (win if r is None else len(r))
+                rows = None
+                if r is not None:
+                    rows = torch.empty(n_cap, dtype=torch.int32, device="cuda")
+                    rows[before[l]:].copy_(torch.from_numpy(r))
+                packs.append(flk.Packed.empty(kind, H, D, n_cap, rows, T=T_cap, k_tiles=True,
+                                              compact=r is not None))
+            units.append((kind, xs, recon, packs))
+
+    def items(l):
+        if l == 0:
+            return [(k, xs[0], p0, rec, pk[0]) for k, xs, rec, pk in units]
+        r = rows_w[l]
+        return [(k, xs[l], None if r is None else pk[l].rows[before[l]:], win if r is None else len(r), p0, win,
+                 before[l], rec, pk[l]) for k, xs, rec, pk in units]
+    # unit tables marshalled once, as a serving loop would keep them: a flush is 4 C calls
+    L = flk.lib()
+    kd, vd = flk.desc(flk.K, H, D, True), flk.desc(flk.V, H, D)
+    tables = []
+    for l in range(4):
+        its = items(l)
+        us_ = [flk._append_unit(k, x, None, x.shape[0], q0, x.shape[0], q0, rec, pk) for k, x, q0, rec, pk in its] \
+            if l == 0 else [flk._append_unit(*it) for it in its]
+        tables.append((flk.AppendUnitC * len(us_))(*us_))
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def flush_batched():
+        assert L.flk_append_base_batch(ctypes.byref(kd), ctypes.byref(vd), tables[0], len(tables[0]), None, sp) == 0
+        for l in range(1, 4):
+            assert L.flk_append_residual_batch(ctypes.byref(kd), ctypes.byref(vd), tables[l], len(tables[l]), None,
+                                               sp) == 0
+
+    def flush_single():
+        for l in range(4):
+            for u in tables[l]:
+                one = (flk.AppendUnitC * 1)(u)
+                f = L.flk_append_base_batch if l == 0 else L.flk_append_residual_batch
+                assert f(ctypes.byref(kd), ctypes.byref(vd), one, 1, None, sp) == 0
+
+    def back_to_back(fn, n=50):
+        return lambda: [fn() for _ in range(n)]
+
+    for _ in range(5):
+        flush_batched()
+        flush_single()
+    torch.cuda.synchronize()
+    nb = 0
+    for kind in (flk.K, flk.V):
+        calls = call_bytes(kind, H, D, win, [None if r is None else r - p0 for r in rows_w], k_tiles=kind == flk.K)
+        nb += layers * sum(b for name, b in calls if name != "reconstruct")
+    us_b = _timed_us(back_to_back(flush_batched), 5) / 50
+    us_s = _timed_us(back_to_back(flush_single, 10), 3) / 10
+    out["flush"] = {"workload": "decode_flush", "tensors": 2 * layers, "H": H, "D": D, "window": win,
+                    "window_rows": [win, win, len(rows_w[2]), len(rows_w[3])], "algorithmic_bytes": int(nb),
+                    "batched_us": round(us_b, 2), "batched_gbs": round(nb / us_b / 1e3, 1),
+                    "single_calls_us": round(us_s, 2), "calls_batched": 4, "calls_single": 8 * layers,
+                    "timing": "wall per flush over back-to-back flushes, unit tables prepared once"}
+    del units, tables
+    torch.cuda.empty_cache()
+
+    # attention over 131072 packed tokens (tile-grouped K) + a 127-token BF16 tail
+    w = synth.WORKLOADS[5]
+    T, Hk, Dk, Hq = w.T, w.H, w.D, w.Hq
+    sets = synth.active_sets(w, T)
+    chains = {}
+    for kind, tensor in ((flk.K, synth.K_TENSOR), (flk.V, synth.V_TENSOR)):
+        c = synth.make_chain(w, tensor, sets=sets)
+        recon = torch.empty((T, Hk, Dk), dtype=torch.bfloat16, device="cuda")
+        packs = []
+        for l, (x, r) in enumerate(zip(c.xs, c.rows)):
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            rd = None if r is None else torch.from_numpy(r).cuda()
+            p = flk.Packed.empty(kind, Hk, Dk, x.shape[0], rd, T=T, k_tiles=True)
+            if l == 0:
+                flk.encode_base(kind, xd, p, recon)
+            else:
+                flk.encode_residual(kind, xd, rd, recon, p)
+            packs.append(p)
+        chains[kind] = packs
+        del recon
+    tail = 127
+    assert flk.rolling_prefix(T + tail) == T
+    kt = torch.randn((tail, Hk, Dk), device="cuda").to(torch.bfloat16)
+    vt = torch.randn((tail, Hk, Dk), device="cuda").to(torch.bfloat16)
+    q = torch.from_numpy(synth.make_query(w).view(np.int16)).cuda().view(torch.bfloat16)
+    o = torch.empty((Hq, Dk), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(flk.attn_workspace_bytes(Hk, Dk, T + tail, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(Dk)
+    roll = lambda: flk.decode_attn_rolling(q, chains[flk.K], chains[flk.V], T, Hk, kt, vt, scale, o, ws)
+    packed = lambda: flk.decode_attn_packed(q, chains[flk.K], chains[flk.V], T, Hk, scale, o, ws)
+    for _ in range(3):
+        roll()
+        packed()
+    torch.cuda.synchronize()
+    out["attention"] = {"workload": "decode_attn", "T_packed": T, "tail": tail, "Hkv": Hk, "Hq": Hq, "D": Dk,
+                        "k_grouping": "tile", "rolling_us": round(_timed_us(roll, 20, flush), 2),
+                        "packed_only_us": round(_timed_us(packed, 20, flush), 2)}
+    return out
+
+
 # ----------------------------------------------------------------------------- HBM traffic
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prompt.txt")
@@ -459,6 +607,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
     ap.add_argument("--no-page-local", action="store_true", help="skip the page-local K grouping leg")
+    ap.add_argument("--no-rolling", action="store_true", help="skip the rolling-tail flush and attention leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -590,6 +739,9 @@ def main():
     if not args.no_attention:
         log("decode attention over the packed chains ...")
         result["decode_attention"] = attention_leg()
+    if not args.no_rolling:
+        log("rolling tail: flush and attention ...")
+        result["rolling"] = rolling_leg()
     if not args.no_cpu_baseline:
         log("timing the oracle on a head sample ...")
         result["cpu_baseline"] = cpu_baseline(w, host, sets)

@@ -169,9 +169,10 @@ size_t flk_stream_bytes(const flk_desc* d, int32_t n_rows, int32_t T, int sparse
  * tokens, and 0 for n_tokens < 0).  Positions [prefix, n_tokens) stay in BF16. */
 int32_t flk_rolling_prefix(int32_t n_tokens);
 
-/* Workspace of flk_decode_attn_packed and flk_decode_attn_rolling for a cache of T packed
- * tokens (T >= 0) and n_q_heads query heads (other calls need none).  0 for malformed
- * arguments. */
+/* Workspace of flk_decode_attn_packed and flk_decode_attn_rolling: enough for every call over
+ * at most T attended tokens in all (packed plus BF16 tail, T >= 0) with n_q_heads query heads
+ * (other calls need none); non-decreasing in T, so a buffer sized for the longest context
+ * serves every shorter one.  0 for malformed arguments. */
 size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads);
 
 const char* flk_status_string(flk_status s);
@@ -274,9 +275,10 @@ flk_status flk_append_residual(const flk_desc* d, const void* x_rows, const int3
 /* Decode attention over a rolling cache: the packed chains hold positions [0, T) (T may be
  * 0, then the chains are not read) and the BF16 tail holds positions [T, T + tail_len)
  * (RFC section 3.3: the recent BF16 tail is part of the cache).  k_tail / v_tail: BF16
- * [tail_len, H, D] at the final depth (each token's last-exited version).  Otherwise as
+ * [tail_len, H, D] at the final depth (each token's last-exited version); its tiles are
+ * read as stored, in the same launch as the packed tiles.  Otherwise as
  * flk_decode_attn_packed; T + tail_len >= 1; workspace >= flk_attn_workspace_bytes(k_desc,
- * T, n_q_heads).
+ * T + tail_len, n_q_heads).
  * Errors: those of flk_decode_attn_packed, plus FLK_E_NULL for a missing tail with
  * tail_len > 0.                                                                            */
 flk_status flk_decode_attn_rolling(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T, const void* q,
@@ -338,6 +340,33 @@ typedef struct flk_recon_unit {
  * Errors: those of flk_reconstruct for any unit, plus those of flk_encode_base_batch.       */
 flk_status flk_reconstruct_batch(const flk_desc* k_desc, const flk_desc* v_desc,
                                  const flk_recon_unit* units, int32_t n_units, void* stream);
+
+/* One window of a batched append (the arguments of flk_append_base / flk_append_residual).
+ * Loop 1 (flk_append_base_batch): rows NULL, n_rows == n_pos, rows_before == p0. */
+typedef struct flk_append_unit {
+  const void* x;            /* BF16 [n_rows, H, D]: X[1] of the window, or X[r] at its rows     */
+  const int32_t* rows;      /* the window's row entries (absolute positions), NULL when dense   */
+  void* recon;              /* BF16 [n_pos, H, D]: the window's reconstruction                  */
+  uint8_t* codes;           /* the stream's buffers, at their start                             */
+  uint32_t* params;
+  int32_t* tile_start;      /* compact loops (and empty compact windows), else NULL             */
+  int32_t n_rows;
+  int32_t p0;               /* first position of the window, a multiple of 64                   */
+  int32_t n_pos;            /* positions in the window, a multiple of 64                        */
+  int32_t rows_before;      /* the stream's compact rows at positions < p0                      */
+  int32_t kind;             /* FLK_KIND_K or FLK_KIND_V                                         */
+  int32_t reserved;         /* must be 0                                                        */
+} flk_append_unit;
+
+/* The flush of a decode step that fills whole tiles of many tensors at once (every layer's
+ * K and V of a request, or of several requests): flk_append_base / flk_append_residual for
+ * every unit, in one launch per loop type where the shapes allow.
+ * Errors: those of the single calls for any unit, plus those of flk_encode_base_batch.     */
+flk_status flk_append_base_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_append_unit* units,
+                                 int32_t n_units, uint32_t* dev_status, void* stream);
+flk_status flk_append_residual_batch(const flk_desc* k_desc, const flk_desc* v_desc,
+                                     const flk_append_unit* units, int32_t n_units, uint32_t* dev_status,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

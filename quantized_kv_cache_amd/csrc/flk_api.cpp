@@ -245,11 +245,12 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
   st = load_chain(vd, T, v_chain, n_loops, &vc);
   if (st != FLK_OK) return st;
   if (!aligned(q, 16) || !aligned(out, 16)) return FLK_E_ALIGN;
-  const size_t need = flk::attn_workspace_bytes(T, kd->n_heads, n_q_heads);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return FLK_E_WORKSPACE;
-  if (workspace && !aligned(workspace, 16)) return FLK_E_ALIGN;
+  // the exact need of this launch (flk_attn_workspace_bytes is a bound on it)
+  const size_t need = flk::attn_workspace_need(T, 0, kd->n_heads, n_q_heads);
+  if (!workspace || workspace_bytes < need) return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 16)) return FLK_E_ALIGN;
   return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc, nullptr,
-                                           nullptr, 0, softmax_scale, out, workspace,
+                                           nullptr, 0, softmax_scale, out, workspace, workspace_bytes,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -257,11 +258,48 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
 
 namespace {
 
-// The window rules shared by both append calls.
-flk_status check_window(const flk_desc* d, int32_t p0, int32_t n_pos) {
-  if (p0 < 0 || n_pos < FLK_GROUP || p0 % FLK_GROUP != 0 || n_pos % FLK_GROUP != 0) return FLK_E_SHAPE;
-  if (!rows_fit(d, int64_t(p0) + n_pos)) return FLK_E_SHAPE;
+// The checks of flk_append_base / flk_append_residual for one window.  On FLK_OK, *a is the
+// window's encode (pointers offset into the streams) or, when *empty is set, an empty compact
+// window whose tile index entries (and zero K tile params) still have to be written.
+flk_status check_append(const flk_desc* d, bool resid, const flk_append_unit& u, flk::EncArgs* a, bool* empty) {
+  *empty = false;
+  if (u.reserved != 0) return FLK_E_DESC;
+  if (!u.recon) return FLK_E_NULL;
+  if (u.p0 < 0 || u.n_pos < FLK_GROUP || u.p0 % FLK_GROUP != 0 || u.n_pos % FLK_GROUP != 0) return FLK_E_SHAPE;
+  if (!rows_fit(d, int64_t(u.p0) + u.n_pos)) return FLK_E_SHAPE;
+  if (u.n_rows < 0 || u.n_rows > u.n_pos || u.rows_before < 0 || u.rows_before > u.p0) return FLK_E_SHAPE;
+  const bool dense = u.rows == nullptr && u.n_rows > 0;
+  if (!resid && !dense) return FLK_E_SHAPE;                       // loop 1 covers every position
+  if (dense && (u.n_rows != u.n_pos || u.rows_before != u.p0)) return FLK_E_SHAPE;
+  if (!dense && d->kind == FLK_KIND_K && !k_tiles(d)) return FLK_E_UNSUPPORTED;
+  if (u.n_rows > 0 && !u.x) return FLK_E_NULL;
+  if (!dense && !u.tile_start) return FLK_E_NULL;
+  if (u.n_rows > 0 || k_tiles(d)) {
+    const flk_status st = check_stream_ptrs(u.codes, u.params);
+    if (st != FLK_OK) return st;
+  }
+  if (!aligned(u.recon, 16) || (u.x && !aligned(u.x, 16)) || (u.rows && !aligned(u.rows, 4)) ||
+      (u.tile_start && !aligned(u.tile_start, 4)))
+    return FLK_E_ALIGN;
+  *a = enc_args(d, u.x, u.rows, u.n_rows, u.n_pos, u.recon, u.codes + codes_offset(d, u.rows_before),
+                u.params + params_offset(d, u.rows_before, u.p0), nullptr, nullptr);
+  // a compact window writes its tile index entries, also when it has no rows (and so may come
+  // with rows == NULL): enc_args keeps the index only for a non-NULL rows pointer
+  a->tile_start = dense ? nullptr : u.tile_start + u.p0 / FLK_GROUP;
+  a->pos0 = u.rows ? u.p0 : 0;
+  a->row0 = u.rows_before;
+  *empty = u.n_rows == 0;
   return FLK_OK;
+}
+
+// An empty compact window: tile_start[p0/64 .. (p0+n_pos)/64] = rows_before, and zero params
+// for the window's tiles of a tile-grouped K stream.
+hipError_t fill_empty_window(const flk_desc* d, const flk::EncArgs& a, hipStream_t s) {
+  if (!a.tile_start || !a.params) return hipErrorInvalidValue;
+  const int32_t nt = a.T / FLK_GROUP;
+  hipError_t e = flk::launch_fill_u32(reinterpret_cast<uint32_t*>(a.tile_start), nt + 1, uint32_t(a.row0), s);
+  if (e == hipSuccess && k_tiles(d)) e = flk::launch_fill_u32(a.params, int64_t(nt) * a.W, 0u, s);
+  return e;
 }
 
 }  // namespace
@@ -270,14 +308,14 @@ flk_status flk_append_base(const flk_desc* d, const void* x, int32_t p0, int32_t
                            uint32_t* params, void* recon, uint32_t* dev_status, void* stream) {
   flk_status st = flk_desc_check(d);
   if (st != FLK_OK) return st;
-  if (!x || !recon) return FLK_E_NULL;
-  st = check_window(d, p0, n_pos);
+  if (!x) return FLK_E_NULL;
+  if (dev_status && !aligned(dev_status, 4)) return FLK_E_ALIGN;
+  const flk_append_unit u{x, nullptr, recon, codes, params, nullptr, n_pos, p0, n_pos, p0, d->kind, 0};
+  flk::EncArgs a;
+  bool empty;
+  st = check_append(d, false, u, &a, &empty);
   if (st != FLK_OK) return st;
-  st = check_stream_ptrs(codes, params);
-  if (st != FLK_OK) return st;
-  if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
-  const flk::EncArgs a = enc_args(d, x, nullptr, n_pos, n_pos, recon, codes + codes_offset(d, p0),
-                                  params + params_offset(d, p0, p0), nullptr, dev_status);
+  a.status = dev_status;
   return to_status(flk::launch_encode(d->kind, false, a, d->n_heads, d->head_dim, static_cast<hipStream_t>(stream)));
 }
 
@@ -286,41 +324,15 @@ flk_status flk_append_residual(const flk_desc* d, const void* x_rows, const int3
                                uint32_t* params, int32_t* tile_start, uint32_t* dev_status, void* stream) {
   flk_status st = flk_desc_check(d);
   if (st != FLK_OK) return st;
-  if (!recon) return FLK_E_NULL;
-  st = check_window(d, p0, n_pos);
+  if (dev_status && !aligned(dev_status, 4)) return FLK_E_ALIGN;
+  const flk_append_unit u{x_rows, rows, recon, codes, params, tile_start, n_rows, p0, n_pos, rows_before, d->kind, 0};
+  flk::EncArgs a;
+  bool empty;
+  st = check_append(d, true, u, &a, &empty);
   if (st != FLK_OK) return st;
-  if (n_rows < 0 || n_rows > n_pos || rows_before < 0 || rows_before > p0) return FLK_E_SHAPE;
-  const bool dense = rows == nullptr && n_rows > 0;
-  if (dense && (n_rows != n_pos || rows_before != p0)) return FLK_E_SHAPE;
-  if (!dense && d->kind == FLK_KIND_K && !k_tiles(d)) return FLK_E_UNSUPPORTED;
-  if (n_rows > 0 && !x_rows) return FLK_E_NULL;
-  if (!dense && !tile_start) return FLK_E_NULL;
-  if (n_rows > 0 || k_tiles(d)) {
-    st = check_stream_ptrs(codes, params);
-    if (st != FLK_OK) return st;
-  }
-  if (!aligned(recon, 16) || (dev_status && !aligned(dev_status, 4)) || (x_rows && !aligned(x_rows, 16)) ||
-      (rows && !aligned(rows, 4)) || (tile_start && !aligned(tile_start, 4)))
-    return FLK_E_ALIGN;
+  a.status = dev_status;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (n_rows == 0) {
-    // an empty window of a compact stream: its tile index entries, and zero tile params for K
-    const int32_t t0 = p0 / FLK_GROUP, nt = n_pos / FLK_GROUP;
-    if (flk::launch_fill_u32(reinterpret_cast<uint32_t*>(tile_start + t0), nt + 1, uint32_t(rows_before), s) !=
-        hipSuccess)
-      return FLK_E_LAUNCH;
-    if (k_tiles(d)) {
-      const int64_t W = int64_t(d->n_heads) * d->head_dim;
-      if (flk::launch_fill_u32(params + params_offset(d, rows_before, p0), int64_t(nt) * W, 0u, s) != hipSuccess)
-        return FLK_E_LAUNCH;
-    }
-    return FLK_OK;
-  }
-  flk::EncArgs a = enc_args(d, x_rows, rows, n_rows, n_pos, recon, codes + codes_offset(d, rows_before),
-                            params + params_offset(d, rows_before, p0),
-                            rows ? tile_start + p0 / FLK_GROUP : nullptr, dev_status);
-  a.pos0 = rows ? p0 : 0;
-  a.row0 = rows_before;
+  if (empty) return to_status(fill_empty_window(d, a, s));
   return to_status(flk::launch_encode(d->kind, true, a, d->n_heads, d->head_dim, s));
 }
 
@@ -350,11 +362,12 @@ flk_status flk_decode_attn_rolling(const flk_desc* kd, const flk_desc* vd, int32
   }
   if (!aligned(q, 16) || !aligned(out, 16) || (tail_len > 0 && (!aligned(k_tail, 16) || !aligned(v_tail, 16))))
     return FLK_E_ALIGN;
-  const size_t need = flk::attn_workspace_bytes(T, kd->n_heads, n_q_heads);
+  // the exact need of this launch (flk_attn_workspace_bytes is a bound on it)
+  const size_t need = flk::attn_workspace_need(T, tail_len, kd->n_heads, n_q_heads);
   if (!workspace || workspace_bytes < need) return FLK_E_WORKSPACE;
   if (!aligned(workspace, 16)) return FLK_E_ALIGN;
   return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc, k_tail, v_tail,
-                                           tail_len, softmax_scale, out, workspace,
+                                           tail_len, softmax_scale, out, workspace, workspace_bytes,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -460,6 +473,66 @@ flk_status flk_encode_base_batch(const flk_desc* k_desc, const flk_desc* v_desc,
 flk_status flk_encode_residual_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_unit* units,
                                      int32_t n_units, uint32_t* dev_status, void* stream) {
   return encode_batch(true, k_desc, v_desc, units, n_units, dev_status, stream);
+}
+
+namespace {
+
+flk_status append_batch(bool resid, const flk_desc* kd, const flk_desc* vd, const flk_append_unit* units,
+                        int32_t n_units, uint32_t* dev_status, void* stream) {
+  if (n_units < 0) return FLK_E_SHAPE;
+  if (n_units == 0) return FLK_OK;
+  if (!units) return FLK_E_NULL;
+  flk_status st = check_pair(kd, vd);
+  if (st != FLK_OK) return st;
+  if (dev_status && !aligned(dev_status, 4)) return FLK_E_ALIGN;
+  std::vector<flk::EncArgs> batch[2];       // [0] dense (or loop 1), [1] compact
+  std::vector<int> kinds[2];
+  std::vector<std::pair<int, flk::EncArgs>> singles, empties;
+  for (int32_t i = 0; i < n_units; ++i) {
+    const flk_append_unit& u = units[i];
+    if (u.kind != FLK_KIND_K && u.kind != FLK_KIND_V) return FLK_E_DESC;
+    const flk_desc* d = unit_desc(kd, vd, u.kind);
+    if (!d) return FLK_E_NULL;
+    flk::EncArgs a;
+    bool empty;
+    st = check_append(d, resid, u, &a, &empty);
+    if (st != FLK_OK) return st;
+    a.status = dev_status;
+    if (empty) {
+      empties.emplace_back(i, a);
+    } else if (flk::encode_batchable(u.kind, d->n_heads, d->head_dim)) {
+      batch[u.rows ? 1 : 0].push_back(a);
+      kinds[u.rows ? 1 : 0].push_back(u.kind);
+    } else {
+      singles.emplace_back(i, a);
+    }
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int g = 0; g < 2; ++g) {
+    if (batch[g].empty()) continue;
+    if (flk::launch_encode_batch(resid, g == 1, batch[g].data(), kinds[g].data(), int(batch[g].size()), s) !=
+        hipSuccess)
+      return FLK_E_LAUNCH;
+  }
+  for (const auto& [i, a] : singles) {
+    const flk_desc* d = unit_desc(kd, vd, units[i].kind);
+    if (flk::launch_encode(units[i].kind, resid, a, d->n_heads, d->head_dim, s) != hipSuccess) return FLK_E_LAUNCH;
+  }
+  for (const auto& [i, a] : empties)
+    if (fill_empty_window(unit_desc(kd, vd, units[i].kind), a, s) != hipSuccess) return FLK_E_LAUNCH;
+  return FLK_OK;
+}
+
+}  // namespace
+
+flk_status flk_append_base_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_append_unit* units,
+                                 int32_t n_units, uint32_t* dev_status, void* stream) {
+  return append_batch(false, k_desc, v_desc, units, n_units, dev_status, stream);
+}
+
+flk_status flk_append_residual_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_append_unit* units,
+                                     int32_t n_units, uint32_t* dev_status, void* stream) {
+  return append_batch(true, k_desc, v_desc, units, n_units, dev_status, stream);
 }
 
 flk_status flk_reconstruct_batch(const flk_desc* k_desc, const flk_desc* v_desc, const flk_recon_unit* units,

@@ -15,7 +15,8 @@
 //      O^T += V_hat^T P^T with v_mfma_f32_16x16x16_bf16, whose P^T operand layout is the score
 //      tile's register layout, so probabilities never leave registers.
 // At the end the block's 4 waves merge their (m, l, O) through LDS into one partial per
-// (block, query head); a second kernel merges the partials of all blocks.
+// (block, query head); a second kernel merges the partials of all blocks.  A BF16 tail (a
+// rolling cache's recent tokens) is read as stored, 16 tokens per wave.
 #include "flk_device.h"
 #include "flk_internal.h"
 
@@ -37,24 +38,35 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// Tiles per wave: about kAttnWaves waves per launch.  A block of 4 waves covers 4*tpw tiles
-// and writes one partial per query head.
-static int32_t tiles_per_wave(int32_t T, int32_t H) {
-  const int64_t tiles = (int64_t(T) + kGroup - 1) / kGroup;
-  const int64_t per = (tiles * H + kAttnWaves - 1) / kAttnWaves;
-  return int32_t(per < 1 ? 1 : per);
+// Waves per KV head: about kAttnWaves waves per launch, never more than one per tile.  The
+// waves of a head share its tiles with counts that differ by at most one (the first waves take
+// the extra ones), so a few extra tiles (a BF16 tail) lengthen a few early waves instead of
+// adding blocks.  A block
+// of 4 waves writes one partial per query head.  `tiles` counts the packed tiles and the
+// tiles of a BF16 tail together.
+static int32_t waves_per_head(int32_t tiles, int32_t H) {
+  const int32_t cap = kAttnWaves / H > 0 ? kAttnWaves / H : 1;
+  return tiles < cap ? (tiles > 0 ? tiles : 1) : cap;
 }
-static int32_t n_splits(int32_t T, int32_t H) {
-  const int32_t tiles = (T + kGroup - 1) / kGroup;
-  const int32_t per_block = 4 * tiles_per_wave(T, H);
-  return (tiles + per_block - 1) / per_block;
+static int32_t n_splits(int32_t tiles, int32_t H) { return (waves_per_head(tiles, H) + 3) / 4; }
+
+static int32_t attn_tiles(int32_t T, int32_t tail_len) {
+  return (T + kGroup - 1) / kGroup + (tail_len + kGroup - 1) / kGroup;
 }
 
-// One partial (m, l, O) per query head for every split of the packed tokens, plus one for a
-// BF16 tail.
-size_t attn_workspace_bytes(int32_t T, int32_t H, int32_t Hq) {
-  const int32_t splits = T > 0 ? n_splits(T, H) : 0;
-  return size_t(splits + 1) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
+// The workspace a call over T packed tokens and a tail of tail_len tokens uses: one partial
+// (m, l, O) per query head and split.
+size_t attn_workspace_need(int32_t T, int32_t tail_len, int32_t H, int32_t Hq) {
+  return size_t(n_splits(attn_tiles(T, tail_len), H)) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
+}
+
+// A bound on attn_workspace_need for every call over at most T_total tokens: such a call has at
+// most ceil(T_total/64) + 1 tiles (a packed prefix and a tail may each end in a partial tile),
+// and the split count does not decrease with the tile count.
+size_t attn_workspace_bytes(int32_t T_total, int32_t H, int32_t Hq) {
+  const int64_t tiles = (int64_t(T_total) + kGroup - 1) / kGroup + 1;
+  const int32_t s = n_splits(int32_t(tiles < INT32_MAX ? tiles : INT32_MAX), H);
+  return size_t(s) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
 }
 
 // Decode loop l's 8 channels of one item into d[] (binary32 values that are exactly BF16).
@@ -199,7 +211,9 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
 template <int NL>
 __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(ChainArgs kc, ChainArgs vc, int32_t T, int32_t H,
                                                               int32_t G, const uint16_t* __restrict__ q,
-                                                              float scale, int32_t tpw,
+                                                              const uint16_t* __restrict__ kt,
+                                                              const uint16_t* __restrict__ vt, int32_t tail_len,
+                                                              float scale, int32_t wph,
                                                               float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[attn_lds_bytes<NL>()];
   const int lane = threadIdx.x & 63;
@@ -209,9 +223,12 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   const int32_t split = blockIdx.x;
   const int32_t h = blockIdx.y;
   const int32_t Hq = H * G;
-  const int32_t tiles = (T + kGroup - 1) / kGroup;
-  const int32_t tile0 = (split * kAWaves + wave) * tpw;
-  const int32_t tile1 = min(tiles, tile0 + tpw);
+  const int32_t ptiles = (T + kGroup - 1) / kGroup;       // packed tiles
+  // the head's packed tiles, ptiles / wph per wave and one more for the first ptiles % wph
+  const int32_t w = split * kAWaves + wave;               // this wave's index within its head
+  const int32_t base = ptiles / wph, extra = ptiles - base * wph;
+  const int32_t tile0 = w < wph ? w * base + min(w, extra) : ptiles;
+  const int32_t tile1 = w < wph ? tile0 + base + (w < extra ? 1 : 0) : ptiles;
   WaveLds<NL>& L = reinterpret_cast<WaveLds<NL>*>(s_raw)[wave];
 
   // Q^T as the B operand of S^T = K_hat Q^T: lane holds Q[n][32*ks + 8*kb + j], zero past G
@@ -231,6 +248,74 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   float4_t o[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // One 16-token slice: S^T = K Q^T on the MFMA, the online softmax, then V (from load_v,
+  // called after the softmax so one operand set is live at a time) into LDS and
+  // O^T += V^T P^T.  Slots 16*sl + 4*kb + i at or past n_valid are masked.
+  auto attend_slice = [&](const uint4 (&kitem)[4], int sl, int32_t n_valid, auto&& load_v) {
+    float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kitem[ks]), qb[ks], sacc, 0, 0, 0);
+    // online softmax; lane holds the scores of tokens 4*kb + i of the slice for head n
+    float sc[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = 16 * sl + 4 * kb + i < n_valid ? sacc[i] * scale : -__builtin_inff();
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    float p[4], psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = m_new == -__builtin_inff() ? 0.0f : __expf(sc[i] - m_new);
+      psum += p[i];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    const float corr = m_run == -__builtin_inff() ? 0.0f : __expf(m_run - m_new);
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+
+    uint4 vitem[4];
+    load_v(vitem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.v[n][oc[i] * 8]) = vitem[i];
+    wave_sync();
+    short4_t pb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb[j] = short(__builtin_bit_cast(uint16_t, (__bf16)p[j]));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      short4_t a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = short(L.v[4 * kb + j][16 * mt + n]);
+      o[mt] = o[mt] * corr;
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
+    }
+    wave_sync();                                          // the slice's V reads before the next writes
+  };
+
+  // The BF16 tail, read as stored, in 16-token slices: slice s goes to waves s, s + wph, ...
+  // of every head, a small addition to many waves rather than whole tiles for a few.
+  const int32_t tail_slices = (tail_len + 15) / 16;
+  for (int32_t ts = w; w < wph && ts < tail_slices; ts += wph) {
+    const int32_t n_valid = min(16, tail_len - 16 * ts);
+    const bool ok = n < n_valid;
+    const int64_t base = (int64_t(16 * ts + n) * H + h) * kAttnD;
+    uint4 item[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      item[i] = ok ? *reinterpret_cast<const uint4*>(kt + base + oc[i] * 8) : make_uint4(0, 0, 0, 0);
+    attend_slice(item, 0, n_valid, [&](uint4 (&v)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = ok ? *reinterpret_cast<const uint4*>(vt + base + oc[i] * 8) : make_uint4(0, 0, 0, 0);
+    });
+  }
 
   for (int32_t tile = tile0; tile < tile1; ++tile) {
     const int32_t t0 = tile * kGroup;
@@ -295,50 +380,9 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       // K_hat of the slice straight into the A operands
       uint4 item[4];
       decode_items<FLK_KIND_K, NL>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, item);
-      float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item[ks]), qb[ks], sacc, 0, 0, 0);
-      // online softmax; lane holds the scores of tokens 4*kb + i of the slice for head n
-      float sc[4];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] = 16 * sl + 4 * kb + i < n_valid ? sacc[i] * scale : -__builtin_inff();
-        mx = fmaxf(mx, sc[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      float p[4], psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = m_new == -__builtin_inff() ? 0.0f : __expf(sc[i] - m_new);
-        psum += p[i];
-      }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      const float corr = m_run == -__builtin_inff() ? 0.0f : __expf(m_run - m_new);
-      l_run = l_run * corr + psum;
-      m_run = m_new;
-
-      // V_hat of the slice into LDS, then O^T += V_hat^T P^T
-      decode_items<FLK_KIND_V, NL>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, item);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.v[n][oc[i] * 8]) = item[i];
-      wave_sync();
-      short4_t pb;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pb[j] = short(__builtin_bit_cast(uint16_t, (__bf16)p[j]));
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        short4_t a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = short(L.v[4 * kb + j][16 * mt + n]);
-        o[mt] = o[mt] * corr;
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
-      }
-      wave_sync();                                        // the slice's V reads before the next writes
+      attend_slice(item, sl, n_valid, [&](uint4 (&v)[4]) {
+        decode_items<FLK_KIND_V, NL>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, v);
+      });
     }
   }
 
@@ -372,102 +416,6 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     const int64_t qi = int64_t(split) * Hq + h * G + g;
     if (ch == 0) { ws_ml[2 * qi] = M; ws_ml[2 * qi + 1] = Ls; }
     ws_o[qi * kAttnD + ch] = O;
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// The BF16 tail of a rolling cache: one block per KV head writes the partial (m, l, O) of its
-// G query heads over the tail's tokens, in the workspace slot after the packed splits.  The
-// tail holds at most a few hundred tokens, so the block walks them in chunks of 256: one
-// token per thread for the scores, then one (head, channel) pair per thread for P V.
-// ---------------------------------------------------------------------------------------
-constexpr int kTailChunk = kAThreads;
-__global__ __launch_bounds__(kAThreads) void attn_tail_kernel(const uint16_t* __restrict__ kt,
-                                                              const uint16_t* __restrict__ vt, int32_t tail_len,
-                                                              int32_t H, int32_t G, const uint16_t* __restrict__ q,
-                                                              float scale, int32_t slot,
-                                                              float* __restrict__ ws_ml, float* __restrict__ ws_o) {
-  __shared__ float s_q[kMaxG][kAttnD];
-  __shared__ float s_p[kMaxG][kTailChunk];
-  __shared__ float s_m[kMaxG], s_l[kMaxG], s_corr[kMaxG];
-  const int tid = threadIdx.x;
-  const int32_t h = blockIdx.x;
-  const int32_t Hq = H * G;
-  for (int idx = tid; idx < G * kAttnD; idx += kAThreads) {
-    const int g = idx / kAttnD, c = idx % kAttnD;
-    s_q[g][c] = bf16_lo(q[int64_t(h * G + g) * kAttnD + c]);
-  }
-  if (tid < kMaxG) { s_m[tid] = -__builtin_inff(); s_l[tid] = 0.0f; }
-  // (head, channel) pairs of this thread for P V: idx = tid + 256 k
-  constexpr int kPairs = kMaxG * kAttnD / kAThreads;
-  float o[kPairs];
-#pragma unroll
-  for (int k = 0; k < kPairs; ++k) o[k] = 0.0f;
-  __syncthreads();
-  const int64_t row = int64_t(H) * kAttnD;
-  for (int32_t c0 = 0; c0 < tail_len; c0 += kTailChunk) {
-    // scores of token c0 + tid for every head
-    const int32_t t = c0 + tid;
-    if (t < tail_len) {
-      float kv[kAttnD];
-      const uint4* kp = reinterpret_cast<const uint4*>(kt + t * row + int64_t(h) * kAttnD);
-#pragma unroll
-      for (int i = 0; i < kAttnD / 8; ++i) {
-        const uint4 w = kp[i];
-        kv[8 * i + 0] = bf16_lo(w.x); kv[8 * i + 1] = bf16_hi(w.x);
-        kv[8 * i + 2] = bf16_lo(w.y); kv[8 * i + 3] = bf16_hi(w.y);
-        kv[8 * i + 4] = bf16_lo(w.z); kv[8 * i + 5] = bf16_hi(w.z);
-        kv[8 * i + 6] = bf16_lo(w.w); kv[8 * i + 7] = bf16_hi(w.w);
-      }
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < kAttnD; ++c) acc = __builtin_fmaf(s_q[g][c], kv[c], acc);
-        s_p[g][tid] = acc * scale;
-      }
-    } else {
-      for (int g = 0; g < G; ++g) s_p[g][tid] = -__builtin_inff();
-    }
-    __syncthreads();
-    // per head: the chunk's maximum, the rescale of the running sums, the probabilities
-    if (tid < G) {
-      const int g = tid;
-      float mx = -__builtin_inff();
-      for (int i = 0; i < kTailChunk; ++i) mx = fmaxf(mx, s_p[g][i]);
-      const float m_new = fmaxf(s_m[g], mx);
-      const float corr = s_m[g] == -__builtin_inff() ? 0.0f : __expf(s_m[g] - m_new);
-      float sum = 0.0f;
-      for (int i = 0; i < kTailChunk; ++i) {
-        const float p = s_p[g][i] == -__builtin_inff() ? 0.0f : __expf(s_p[g][i] - m_new);
-        s_p[g][i] = p;
-        sum += p;
-      }
-      s_l[g] = s_l[g] * corr + sum;
-      s_m[g] = m_new;
-      s_corr[g] = corr;
-    }
-    __syncthreads();
-    const int32_t nt = min(kTailChunk, tail_len - c0);
-#pragma unroll
-    for (int k = 0; k < kPairs; ++k) {
-      const int idx = tid + kAThreads * k;
-      const int g = idx / kAttnD, c = idx % kAttnD;
-      if (g >= G) continue;
-      float acc = o[k] * s_corr[g];
-      for (int32_t i = 0; i < nt; ++i)
-        acc = __builtin_fmaf(s_p[g][i], bf16_lo(vt[(c0 + i) * row + int64_t(h) * kAttnD + c]), acc);
-      o[k] = acc;
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < kPairs; ++k) {
-    const int idx = tid + kAThreads * k;
-    const int g = idx / kAttnD, c = idx % kAttnD;
-    if (g >= G) continue;
-    const int64_t qi = int64_t(slot) * Hq + h * G + g;
-    if (c == 0) { ws_ml[2 * qi] = s_m[g]; ws_ml[2 * qi + 1] = s_l[g]; }
-    ws_o[qi * kAttnD + c] = o[k];
   }
 }
 
@@ -521,39 +469,34 @@ __global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int3
 hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
                               const ChainArgs& kc, const ChainArgs& vc, const void* k_tail,
                               const void* v_tail, int32_t tail_len, float scale, void* out,
-                              void* ws, hipStream_t stream) {
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
   (void)D;
-  const int32_t tpw = T > 0 ? tiles_per_wave(T, H) : 0;
-  const int32_t splits = T > 0 ? n_splits(T, H) : 0;
-  const int32_t slots = splits + (tail_len > 0 ? 1 : 0);
+  if (ws == nullptr || ws_bytes < attn_workspace_need(T, tail_len, H, Hq)) return hipErrorInvalidValue;
+  const int32_t tiles = attn_tiles(T, tail_len);
+  const int32_t wph = waves_per_head(tiles, H);
+  const int32_t splits = n_splits(tiles, H);
   const int32_t G = Hq / H;
   float* ws_ml = static_cast<float*>(ws);
-  float* ws_o = ws_ml + size_t(slots) * Hq * 2;
+  float* ws_o = ws_ml + size_t(splits) * Hq * 2;
   const uint16_t* qp = static_cast<const uint16_t*>(q);
-  if (splits > 0) {
-    const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
-    const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
+  const uint16_t* ktp = static_cast<const uint16_t*>(k_tail);
+  const uint16_t* vtp = static_cast<const uint16_t*>(v_tail);
+  int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
+  if (nl < 1) nl = 1;                              // no packed tokens: only the tail's tiles run
+  const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
 #define FLK_A(NLV)                                                                                      \
   case NLV:                                                                                             \
     hipLaunchKernelGGL((attn_wave_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
-                       scale, tpw, ws_ml, ws_o);                                                        \
+                       ktp, vtp, tail_len, scale, wph, ws_ml, ws_o);                                    \
     break;
-    switch (nl) {
-      FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
-      default: return hipErrorInvalidValue;
-    }
+  switch (nl) {
+    FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
+    default: return hipErrorInvalidValue;
+  }
 #undef FLK_A
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (tail_len > 0) {
-    hipLaunchKernelGGL(attn_tail_kernel, dim3(unsigned(H)), dim3(kAThreads), 0, stream,
-                       static_cast<const uint16_t*>(k_tail), static_cast<const uint16_t*>(v_tail), tail_len, H, G,
-                       qp, scale, splits, ws_ml, ws_o);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, slots, Hq, ws_ml,
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, splits, Hq, ws_ml,
                      ws_o, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }

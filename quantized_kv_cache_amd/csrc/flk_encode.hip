@@ -41,6 +41,33 @@ __device__ __forceinline__ uint4 pack8(const float v[8]) {
   return w;
 }
 
+// First index of the ascending rows[0..n) whose value is >= key, found by one wave in rounds
+// of 64 parallel probes (ceil(log64(n)) dependent loads).  Every lane returns the same value;
+// call with the whole wave active.
+__device__ __forceinline__ int32_t wave_lower_bound(const int32_t* __restrict__ rows, int32_t n, int32_t key,
+                                                    int lane) {
+  int32_t a = 0, b = n;                    // the answer lies in [a, b]
+  while (a < b) {
+    const int32_t s = (b - a + 63) / 64;
+    const int32_t idx = a + lane * s;
+    const bool pred = idx < b && rows[idx] < key;
+    const int32_t c = __builtin_popcountll(__ballot(pred));
+    if (c == 0) return a;
+    const int32_t na = a + (c - 1) * s + 1;
+    const int32_t nb = min(a + c * s, b);
+    if (s == 1) return nb;
+    a = na;
+    b = nb;
+  }
+  return a;
+}
+
+// Compact loops of at most this many rows (a rolling-tail flush, a short request) find each
+// tile's rows with an in-wave search and write the tile index themselves; longer ones read
+// the index that tile_index_kernel writes first (one load instead of a search in front of
+// every wave's data loads).
+constexpr int32_t kTileSearchRows = 4096;
+
 // ---------------------------------------------------------------------------------------
 // K, tile (page-local) groups, compact loops: a wave owns the compact rows of one
 // 64-position tile (0 to 64 of them) for 64 channels, and the 4 waves of a block take
@@ -71,11 +98,21 @@ __device__ __forceinline__ void encode_k_tile_body(const EncArgs& a, uint32_t it
   const bool cact = chunk < (W >> 3);
   const int64_t ch = int64_t(chunk) * 8;
 
-  // the tile's compact rows [jbeg, jend), from the tile index tile_index_kernel wrote (its
-  // entries count the stream's rows before the window too); clamped so a malformed map
-  // never addresses outside the rows
-  const int32_t jbeg = min(max(uniform(a.tile_start[tile]) - a.row0, 0), n);
-  const int32_t jend = min(max(uniform(a.tile_start[tile + 1]) - a.row0, jbeg), min(n, jbeg + kGroup));
+  // the tile's compact rows [jbeg, jend): searched in rows for a short loop, else from the tile
+  // index tile_index_kernel wrote (its entries count the stream's rows before the window
+  // too), clamped so a malformed map never addresses outside the rows
+  const bool search = n <= kTileSearchRows;
+  int32_t jbeg, jend;
+  if (search) {
+    const int32_t key = pos0 + tile * kGroup;
+    jend = uniform(wave_lower_bound(rows, n, key + kGroup, lane));
+    const int32_t b0 = max(0, jend - kGroup);             // positions are distinct
+    const bool below = b0 + lane < jend && rows[b0 + lane] < key;
+    jbeg = uniform(b0 + int32_t(__builtin_popcountll(__ballot(below))));
+  } else {
+    jbeg = min(max(uniform(a.tile_start[tile]) - a.row0, 0), n);
+    jend = min(max(uniform(a.tile_start[tile + 1]) - a.row0, jbeg), min(n, jbeg + kGroup));
+  }
 
   // per row: the residual (or value) as 8 packed BF16 and its position.  The predecessor row
   // is read again for the final add (an L2 hit) instead of being held in registers: the
@@ -105,6 +142,13 @@ __device__ __forceinline__ void encode_k_tile_body(const EncArgs& a, uint32_t it
     }
   }
   if (bad_row && a.status) atomicOr(a.status, kDevRows);
+  if (search && strip == 0 && cc == 0) {
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int32_t j = jbeg + rs + 8 * i;
+      if (j < jend) write_tile_index(rows, n, T, j, a.tile_start, pos0, a.row0);
+    }
+  }
   float mn[8], mx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
@@ -635,8 +679,9 @@ static hipError_t launch_v(const EncArgs& a, int32_t H, int32_t D, hipStream_t s
 template <bool RESID, bool SPARSE>
 static hipError_t launch_k(const EncArgs& a, hipStream_t stream) {
   if (SPARSE && a.ktile) {
-    hipLaunchKernelGGL(tile_index_kernel, dim3(unsigned((a.n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, a);
+    if (a.n > kTileSearchRows)
+      hipLaunchKernelGGL(tile_index_kernel, dim3(unsigned((a.n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                         stream, a);
     hipLaunchKernelGGL((encode_k_tile_kernel<RESID>), k_grid(a, SPARSE), dim3(kThreads), 0, stream, a);
   } else
     hipLaunchKernelGGL((encode_k_kernel<RESID, SPARSE>), k_grid(a, SPARSE), dim3(kThreads), 0, stream, a);
@@ -668,6 +713,7 @@ __global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* __restrict
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
+  if (p == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(unsigned((count + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
                      p, count, value);
   return hipGetLastError();
@@ -751,7 +797,7 @@ hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, con
       EncBatch tb{};
       uint32_t tblocks = 0;
       for (int i = 0; i < b.n_units; ++i) {
-        if (b.u[i].kind != FLK_KIND_K) continue;
+        if (b.u[i].kind != FLK_KIND_K || b.u[i].a.n <= kTileSearchRows) continue;
         EncUnit& e = tb.u[tb.n_units++];
         e = b.u[i];
         e.block0 = tblocks;

@@ -39,8 +39,9 @@ struct EncArgs {
   int32_t ktile;           // K groups per 64-position tile instead of per 64 compact rows
 };
 
-// Largest number of tensors one batched launch covers.
-constexpr int kEncBatch = 16;
+// Largest number of tensors one batched launch covers (the unit table travels as kernel
+// arguments, at most 4 KiB).
+constexpr int kEncBatch = 40;
 
 // Encode one loop (base when resid == false); a.rows == nullptr is a dense loop.  The
 // pointers are already offset to the window (codes, params, tile_start).
@@ -76,12 +77,16 @@ bool reconstruct_batchable(int32_t H, int32_t D);
 // units whose chains share loop count and compact pattern goes in launches of up to kRecBatch.
 hipError_t launch_reconstruct_batch(const RecArgs* units, int n_units, hipStream_t stream);
 
-size_t attn_workspace_bytes(int32_t T, int32_t H, int32_t Hq);
+// Workspace of an attention call: exactly what a call over T packed tokens and a tail of
+// tail_len tokens uses, and a bound for every split of T_total tokens into the two.
+size_t attn_workspace_need(int32_t T, int32_t tail_len, int32_t H, int32_t Hq);
+size_t attn_workspace_bytes(int32_t T_total, int32_t H, int32_t Hq);
 
 // Packed positions [0, T) (T may be 0) plus an optional BF16 tail of tail_len positions.
+// Returns hipErrorInvalidValue without launching when ws_bytes is below the need.
 hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
                               const ChainArgs& kc, const ChainArgs& vc, const void* k_tail,
                               const void* v_tail, int32_t tail_len, float scale, void* out,
-                              void* ws, hipStream_t stream);
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace flk

@@ -54,6 +54,13 @@ class UnitC(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class AppendUnitC(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_void_p), ("recon", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("params", ctypes.c_void_p), ("tile_start", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int32), ("p0", ctypes.c_int32), ("n_pos", ctypes.c_int32),
+                ("rows_before", ctypes.c_int32), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class ReconUnitC(ctypes.Structure):
     _fields_ = [("chain", ctypes.POINTER(StreamC)), ("out", ctypes.c_void_p), ("T", ctypes.c_int32),
                 ("n_loops", ctypes.c_int32), ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
@@ -111,6 +118,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [D, D, U, i32, P, P]
+        for name in ("flk_append_base_batch", "flk_append_residual_batch"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [D, D, ctypes.POINTER(AppendUnitC), i32, P, P]
         L.flk_reconstruct_batch.restype = ctypes.c_int
         L.flk_reconstruct_batch.argtypes = [D, D, ctypes.POINTER(ReconUnitC), i32, P]
         L.flk_decode_attn_packed.restype = ctypes.c_int
@@ -378,3 +389,34 @@ def reconstruct_batch(items, H: int, D: int, stream=None) -> None:
     _check(lib().flk_reconstruct_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), tab, len(units),
                                        _stream(stream)), "flk_reconstruct_batch")
 
+
+
+def _append_unit(kind, x, rows, n_rows, p0, n_pos, rows_before, recon, out: "Packed") -> AppendUnitC:
+    _need(recon, torch.bfloat16, "recon")
+    if x is not None:
+        _need(x, torch.bfloat16, "x")
+    if rows is not None:
+        _need(rows, torch.int32, "rows")
+    return AppendUnitC(None if x is None else x.data_ptr(), None if rows is None else rows.data_ptr(),
+                       recon.data_ptr(), out.codes.data_ptr(), out.params.data_ptr(),
+                       None if out.tile_start is None else out.tile_start.data_ptr(),
+                       n_rows, p0, n_pos, rows_before, kind, 0)
+
+
+def append_base_batch(items, H: int, D: int, status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """items: (kind, x [n_pos, H, D], p0, recon [n_pos, H, D], out Packed) per tensor."""
+    units = [_append_unit(kind, x, None, x.shape[0], p0, x.shape[0], p0, recon, out)
+             for kind, x, p0, recon, out in items]
+    arr = (AppendUnitC * max(1, len(units)))(*units)
+    kt = _k_tiles(out.k_tiles for kind, _, _, _, out in items if kind == K)
+    _check(lib().flk_append_base_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), arr,
+                                       len(units), _ptr(status), _stream(stream)), "flk_append_base_batch")
+
+
+def append_residual_batch(items, H: int, D: int, status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """items: (kind, x_rows or None, rows or None, n_rows, p0, n_pos, rows_before, recon, out Packed)."""
+    units = [_append_unit(*it) for it in items]
+    arr = (AppendUnitC * max(1, len(units)))(*units)
+    kt = _k_tiles(it[-1].k_tiles for it in items if it[0] == K)
+    _check(lib().flk_append_residual_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), arr,
+                                           len(units), _ptr(status), _stream(stream)), "flk_append_residual_batch")

@@ -159,13 +159,17 @@ def test_tile_groups_attention(T, H, Hq, sizes):
 
 
 def test_tile_groups_batched_calls():
-    """Tile-grouped K units in the batched calls write exactly what the single calls write."""
+    """Tile-grouped K units in the batched calls write exactly what the single calls write, for
+    compact loops short enough to search their tiles in-kernel and long ones that take the
+    tile index pass."""
     rng = np.random.default_rng(44)
     H, D = 8, 128
     units = []
     for i in range(6):
         T = int(rng.integers(64, 3000))
         n3 = int(rng.integers(0, T + 1))
+        if i < 2:                                    # compact loops long enough for the tile index pass
+            T, n3 = 9000 + 500 * i, 6000
         xs, rows = _random_chain(rng, T, H, D, [None, None, n3, n3 // 3])
         units.append((flk.K if i % 2 == 0 else flk.V, xs, rows))
     dev = []
@@ -370,7 +374,7 @@ def test_rolling_decode_simulation(H, Hq, prompt, steps):
     # attention over packed prefix + BF16 tail
     q = synth.to_bf16_bits(rng.standard_normal((Hq, D)).astype(np.float32))
     k_tail, v_tail = np.ascontiguousarray(fk[P:]), np.ascontiguousarray(fv[P:])
-    ws = torch.empty(flk.attn_workspace_bytes(H, D, P, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(flk.attn_workspace_bytes(H, D, n_tok, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
     out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
     kc = streams[flk.K].chain(P) if P else []
@@ -387,13 +391,14 @@ def test_rolling_decode_simulation(H, Hq, prompt, steps):
 
 @pytest.mark.parametrize("tail_len", [1, 127, 300])
 def test_rolling_attention_tail_only_and_long_tail(tail_len):
-    """No packed prefix (T = 0), and tails longer than one 256-token chunk."""
+    """No packed prefix (T = 0): a single token, a rolling tail and a tail of several tiles
+    ending in a partial one."""
     H, Hq, D = 8, 32, 128
     rng = np.random.default_rng(tail_len)
     kt = synth.to_bf16_bits((2 * rng.standard_normal((tail_len, H, D))).astype(np.float32))
     vt = synth.to_bf16_bits(rng.standard_normal((tail_len, H, D)).astype(np.float32))
     q = synth.to_bf16_bits(rng.standard_normal((Hq, D)).astype(np.float32))
-    ws = torch.empty(flk.attn_workspace_bytes(H, D, 0, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(flk.attn_workspace_bytes(H, D, tail_len, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
     out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
     flk.decode_attn_rolling(to_dev_bf16(q), [], [], 0, H, to_dev_bf16(kt), to_dev_bf16(vt), scale, out, ws)
@@ -401,3 +406,65 @@ def test_rolling_attention_tail_only_and_long_tail(tail_len):
     ref = orc.decode_attn(q, kt, vt, scale)
     rel = _rel_err(out.float().cpu().numpy(), ref)
     assert np.all(rel <= 2e-2), rel
+
+
+@pytest.mark.parametrize("H,D", [(8, 128), (3, 64)])
+def test_batched_appends_equal_single_appends(H, D):
+    """A flush of many tensors through flk_append_*_batch writes exactly what the single
+    append calls write: K and V mixed, windows of 192/64/256 positions, one compact window
+    with no rows, streams at different lengths."""
+    rng = np.random.default_rng(H * 7 + D)
+    n_tok = 512
+    bounds = [0, 192, 256, 512]
+    tensors = []
+    for i in range(6):
+        kind = flk.K if i % 2 == 0 else flk.V
+        _, rows = _decode_depths(rng, n_tok)
+        if i == 2:                                   # no loop-3/4 rows in [192, 256)
+            rows[2] = rows[2][(rows[2] < 192) | (rows[2] >= 256)]
+            rows[3] = np.intersect1d(rows[3], rows[2]).astype(np.int32)
+        X = _decode_values(rng, np.full(n_tok, 4), H, D, 1.0)[0]
+        tensors.append((kind, X, rows))
+    single, batched = [], []
+    for kind, X, rows in tensors:
+        cap = [n_tok, n_tok, rows[2].size, rows[3].size]
+        single.append(RollingStreams(kind, H, D, n_tok, cap, [True, True, False, False]))
+        batched.append(RollingStreams(kind, H, D, n_tok, cap, [True, True, False, False]))
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        say(f"batched appends H={H} D={D} window [{lo}, {hi})")
+        wins = [_window_inputs(X, rows, lo, hi) for _, X, rows in tensors]
+        rec_s = [rs.append(xw, rw, lo, hi - lo) for rs, (xw, rw) in zip(single, wins)]
+        rec_b = [torch.empty((hi - lo, H, D), dtype=torch.bfloat16, device="cuda") for _ in tensors]
+        keep = []
+        for l in range(4):
+            items = []
+            for rs, (xw, rw), rec in zip(batched, wins, rec_b):
+                p = rs.packs[l]
+                xd = None if xw[l] is None else to_dev_bf16(xw[l])
+                keep.append(xd)
+                if l == 0:
+                    items.append((rs.kind, xd, lo, rec, p))
+                elif rs.dense[l]:
+                    items.append((rs.kind, xd, None, hi - lo, lo, hi - lo, lo, rec, p))
+                else:
+                    n_w = 0 if xw[l] is None else xw[l].shape[0]
+                    rd = None
+                    if n_w:
+                        p.rows[rs.n[l]:rs.n[l] + n_w].copy_(torch.from_numpy(rw[l]))
+                        rd = p.rows[rs.n[l]:rs.n[l] + n_w]
+                    items.append((rs.kind, xd, rd, n_w, lo, hi - lo, rs.n[l], rec, p))
+            if l == 0:
+                flk.append_base_batch(items, H, D)
+            else:
+                flk.append_residual_batch(items, H, D)
+            for rs, (xw, rw) in zip(batched, wins):
+                rs.n[l] += (hi - lo) if rs.dense[l] else (0 if xw[l] is None else xw[l].shape[0])
+        torch.cuda.synchronize()
+        for ti, (a, b, ra, rb) in enumerate(zip(single, batched, rec_s, rec_b)):
+            assert_same(to_host_u16(rb), to_host_u16(ra), f"t{ti} window recon [{lo},{hi})")
+            for l, (ca, cb) in enumerate(zip(a.chain(hi), b.chain(hi))):
+                assert ca.n_rows == cb.n_rows
+                assert_same(cb.codes.cpu().numpy(), ca.codes.cpu().numpy(), f"t{ti} codes loop {l}")
+                assert_same(cb.params.cpu().numpy(), ca.params.cpu().numpy(), f"t{ti} params loop {l}")
+                if ca.tile_start is not None:
+                    assert torch.equal(ca.tile_start, cb.tile_start), f"t{ti} tile index loop {l}"
