@@ -527,6 +527,10 @@ def summarize_pmc(dirs):
     for kind in (flk.K, flk.V):
         for name, b in call_bytes(kind, w.H, w.D, w.T, sets):
             algo.setdefault(kernel_symbol(kind, name, w.H, w.D, sets), []).append(b)
+    # the page-local leg's tile-grouped compact K loops (its other kernels are the headline's)
+    for name, b in call_bytes(flk.K, w.H, w.D, w.T, sets, k_tiles=True):
+        if name == "sparse_residual":
+            algo.setdefault("encode_k_tile_kernel<true>", []).append(b)
 
     def mean(counter, pred):
         xs = [v for (c, k), vs in vals.items() if c == counter and pred(k) for v in vs]
