@@ -536,3 +536,160 @@ int orc_decode_attn(int Hq, int Hkv, int D, int T, const uint16_t* q, const uint
     free(s);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* Sparse decode attention (RFC section 3.2 "Sparse decode attention").  Loop 2 is the    */
+/* reference: full attention over the keys at that depth, keeping per query head the     */
+/* selected positions S (the k highest reference probabilities), their mass m, the full   */
+/* output O_ref and the selected keys' weighted value sum C_ref.  A later loop r attends  */
+/* to the keys of S alone at depth r and corrects the reference output:                  */
+/*   p_local = softmax(scale * q_r . K_r[S]),  C_new = m * (p_local . V_r[S]),            */
+/*   O_r = O_ref - C_ref + C_new.                                                          */
+/* Everything here is binary64.  Selection orders keys by reference score (the            */
+/* probabilities are a monotone function of it), higher first, equal scores by the lower  */
+/* position; S is returned in ascending position order.                                   */
+/* ------------------------------------------------------------------------------------ */
+
+static const double* g_sort_scores;   /* qsort has no context argument */
+
+static int by_score_then_position(const void* a, const void* b) {
+    int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+    double si = g_sort_scores[i], sj = g_sort_scores[j];
+    if (si > sj) return -1;
+    if (si < sj) return 1;
+    return (i < j) ? -1 : (i > j);
+}
+
+static int by_position(const void* a, const void* b) {
+    int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+    return (i < j) ? -1 : (i > j);
+}
+
+/* The reference statistics from probabilities p [T] and values v [T, D] (rows of one head):
+ * O_ref = sum_t p_t v_t, and over the selected positions sel [k]: m = sum p_t,
+ * C_ref = sum p_t v_t. */
+int orc_sparse_stats(int T, int D, const double* p, const double* v, int k, const int32_t* sel, double* m,
+                     double* o_ref, double* c_ref) {
+    if (T <= 0 || D <= 0 || k < 1 || k > T) return ORC_E_ARG;
+    for (int c = 0; c < D; ++c) {
+        double acc = 0.0;
+        for (int t = 0; t < T; ++t) acc += p[t] * v[(size_t)t * D + c];
+        o_ref[c] = acc;
+        c_ref[c] = 0.0;
+    }
+    double mm = 0.0;
+    for (int r = 0; r < k; ++r) {
+        int t = sel[r];
+        if (t < 0 || t >= T) return ORC_E_ARG;
+        mm += p[t];
+        for (int c = 0; c < D; ++c) c_ref[c] += p[t] * v[(size_t)t * D + c];
+    }
+    *m = mm;
+    return ORC_OK;
+}
+
+/* The correction of a later loop from its probabilities over the selected keys p_local [k]
+ * and their values v_sel [k, D]: out = O_ref - C_ref + m * sum_r p_local_r v_sel_r. */
+int orc_sparse_correct(int k, int D, const double* p_local, const double* v_sel, double m, const double* o_ref,
+                       const double* c_ref, double* out) {
+    if (k < 1 || D <= 0) return ORC_E_ARG;
+    for (int c = 0; c < D; ++c) {
+        double acc = 0.0;
+        for (int r = 0; r < k; ++r) acc += p_local[r] * v_sel[(size_t)r * D + c];
+        out[c] = o_ref[c] - c_ref[c] + m * acc;
+    }
+    return ORC_OK;
+}
+
+/* Scaled scores of one query head against every key of its KV head, and their softmax. */
+static void head_softmax(int Hkv, int D, const uint16_t* qi, const uint16_t* khat, int h, double scale,
+                         const int32_t* keys, int n, double* sc, double* p) {
+    double smax = -INFINITY;
+    for (int r = 0; r < n; ++r) {
+        int t = keys ? keys[r] : r;
+        double acc = 0.0;
+        for (int c = 0; c < D; ++c)
+            acc += (double)orc_f32_from_bf16(qi[c]) * (double)orc_f32_from_bf16(khat[xidx(Hkv, D, t, h, c)]);
+        sc[r] = scale * acc;
+        if (sc[r] > smax) smax = sc[r];
+    }
+    double denom = 0.0;
+    for (int r = 0; r < n; ++r) { p[r] = exp(sc[r] - smax); denom += p[r]; }
+    for (int r = 0; r < n; ++r) p[r] /= denom;
+}
+
+/* Values of the given keys of one KV head as binary64 rows [n, D]. */
+static void head_values(int Hkv, int D, const uint16_t* vhat, int h, const int32_t* keys, int n, double* out) {
+    for (int r = 0; r < n; ++r) {
+        int t = keys ? keys[r] : r;
+        for (int c = 0; c < D; ++c) out[(size_t)r * D + c] = (double)orc_f32_from_bf16(vhat[xidx(Hkv, D, t, h, c)]);
+    }
+}
+
+/* The k keys with the highest scores, equal scores by the lower position, in position order. */
+int orc_topk_positions(int T, const double* scores, int k, int32_t* sel) {
+    if (T <= 0 || k < 1 || k > T) return ORC_E_ARG;
+    int32_t* order = (int32_t*)malloc((size_t)T * sizeof(int32_t));
+    if (!order) return ORC_E_ARG;
+    for (int t = 0; t < T; ++t) order[t] = t;
+    g_sort_scores = scores;
+    qsort(order, (size_t)T, sizeof(int32_t), by_score_then_position);
+    qsort(order, (size_t)k, sizeof(int32_t), by_position);
+    memcpy(sel, order, (size_t)k * sizeof(int32_t));
+    free(order);
+    return ORC_OK;
+}
+
+/* Reference loop.  q: [Hq, D] BF16; khat, vhat: [T, Hkv, D] BF16 at the reference depth; k keys
+ * kept per query head (1 <= k <= T).  Outputs: sel [Hq, k] ascending positions, mass [Hq],
+ * o_ref [Hq, D], c_ref [Hq, D]. */
+int orc_sparse_reference(int Hq, int Hkv, int D, int T, const uint16_t* q, const uint16_t* khat,
+                         const uint16_t* vhat, double scale, int k, int32_t* sel, double* mass,
+                         double* o_ref, double* c_ref) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || T <= 0 || D <= 0 || k < 1 || k > T) return ORC_E_ARG;
+    int group = Hq / Hkv, st = ORC_OK;
+    double* sc = (double*)malloc((size_t)T * sizeof(double));
+    double* p = (double*)malloc((size_t)T * sizeof(double));
+    double* v = (double*)malloc((size_t)T * (size_t)D * sizeof(double));
+    if (!sc || !p || !v) st = ORC_E_ARG;
+    for (int i = 0; i < Hq && st == ORC_OK; ++i) {
+        int h = i / group;
+        head_softmax(Hkv, D, q + (size_t)i * D, khat, h, scale, NULL, T, sc, p);
+        head_values(Hkv, D, vhat, h, NULL, T, v);
+        st = orc_topk_positions(T, sc, k, sel + (size_t)i * k);
+        if (st == ORC_OK)
+            st = orc_sparse_stats(T, D, p, v, k, sel + (size_t)i * k, mass + i, o_ref + (size_t)i * D,
+                                  c_ref + (size_t)i * D);
+    }
+    free(sc);
+    free(p);
+    free(v);
+    return st;
+}
+
+/* A later loop: q [Hq, D] BF16 of that loop, khat / vhat [T, Hkv, D] at its depth; sel, mass,
+ * o_ref, c_ref from the reference loop.  out [Hq, D] binary64. */
+int orc_sparse_loop(int Hq, int Hkv, int D, int T, const uint16_t* q, const uint16_t* khat,
+                    const uint16_t* vhat, double scale, int k, const int32_t* sel, const double* mass,
+                    const double* o_ref, const double* c_ref, double* out) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || T <= 0 || D <= 0 || k < 1 || k > T) return ORC_E_ARG;
+    for (size_t r = 0; r < (size_t)Hq * (size_t)k; ++r)
+        if (sel[r] < 0 || sel[r] >= T) return ORC_E_ARG;
+    int group = Hq / Hkv, st = ORC_OK;
+    double* sc = (double*)malloc((size_t)k * sizeof(double));
+    double* p = (double*)malloc((size_t)k * sizeof(double));
+    double* v = (double*)malloc((size_t)k * (size_t)D * sizeof(double));
+    if (!sc || !p || !v) st = ORC_E_ARG;
+    for (int i = 0; i < Hq && st == ORC_OK; ++i) {
+        int h = i / group;
+        const int32_t* keys = sel + (size_t)i * k;
+        head_softmax(Hkv, D, q + (size_t)i * D, khat, h, scale, keys, k, sc, p);
+        head_values(Hkv, D, vhat, h, keys, k, v);
+        st = orc_sparse_correct(k, D, p, v, mass[i], o_ref + (size_t)i * D, c_ref + (size_t)i * D,
+                                out + (size_t)i * D);
+    }
+    free(sc);
+    free(p);
+    free(v);
+    return st;
+}

@@ -105,6 +105,16 @@ def lib() -> ctypes.CDLL:
         L.orc_tile_index.argtypes = [P, i, i, P]
         L.orc_decode_attn.restype = i
         L.orc_decode_attn.argtypes = [i, i, i, i, P, P, P, ctypes.c_double, P]
+        L.orc_sparse_reference.restype = i
+        L.orc_sparse_reference.argtypes = [i, i, i, i, P, P, P, ctypes.c_double, i, P, P, P, P]
+        L.orc_sparse_loop.restype = i
+        L.orc_sparse_loop.argtypes = [i, i, i, i, P, P, P, ctypes.c_double, i, P, P, P, P, P]
+        L.orc_sparse_stats.restype = i
+        L.orc_sparse_stats.argtypes = [i, i, P, P, i, P, P, P, P]
+        L.orc_sparse_correct.restype = i
+        L.orc_sparse_correct.argtypes = [i, i, P, P, ctypes.c_double, P, P, P]
+        L.orc_topk_positions.restype = i
+        L.orc_topk_positions.argtypes = [i, P, i, P]
     return _lib
 
 
@@ -332,3 +342,66 @@ def decode_attn_rolling(q: np.ndarray, khat_prefix: np.ndarray, vhat_prefix: np.
     khat = np.concatenate([khat_prefix, k_tail], axis=0)
     vhat = np.concatenate([vhat_prefix, v_tail], axis=0)
     return decode_attn(q, khat, vhat, softmax_scale)
+
+
+# ----------------------------------------------------------------------------- sparse decode attention
+
+@dataclass
+class SparseRef:
+    """Reference-loop state per query head (RFC section 3.2): selected positions (ascending),
+    their reference mass, the full reference output and the selected keys' contribution."""
+    sel: np.ndarray      # int32 [Hq, k]
+    mass: np.ndarray     # float64 [Hq]
+    o_ref: np.ndarray    # float64 [Hq, D]
+    c_ref: np.ndarray    # float64 [Hq, D]
+
+
+def sparse_reference(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, softmax_scale: float, k: int) -> SparseRef:
+    q, khat, vhat = _c(q, np.uint16), _c(khat, np.uint16), _c(vhat, np.uint16)
+    Hq, D = q.shape
+    T, Hkv, _ = khat.shape
+    sel = np.zeros((Hq, k), np.int32)
+    mass = np.zeros(Hq, np.float64)
+    o_ref = np.zeros((Hq, D), np.float64)
+    c_ref = np.zeros((Hq, D), np.float64)
+    _check(lib().orc_sparse_reference(Hq, Hkv, D, T, _p(q), _p(khat), _p(vhat), float(softmax_scale), k, _p(sel),
+                                      _p(mass), _p(o_ref), _p(c_ref)), "sparse_reference")
+    return SparseRef(sel, mass, o_ref, c_ref)
+
+
+def sparse_loop(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, softmax_scale: float, ref: SparseRef) -> np.ndarray:
+    q, khat, vhat = _c(q, np.uint16), _c(khat, np.uint16), _c(vhat, np.uint16)
+    Hq, D = q.shape
+    T, Hkv, _ = khat.shape
+    k = ref.sel.shape[1]
+    out = np.zeros((Hq, D), np.float64)
+    _check(lib().orc_sparse_loop(Hq, Hkv, D, T, _p(q), _p(khat), _p(vhat), float(softmax_scale), k,
+                                 _p(_c(ref.sel, np.int32)), _p(_c(ref.mass, np.float64)),
+                                 _p(_c(ref.o_ref, np.float64)), _p(_c(ref.c_ref, np.float64)), _p(out)), "sparse_loop")
+    return out
+
+
+def sparse_stats(p: np.ndarray, v: np.ndarray, sel: np.ndarray):
+    """(m, O_ref, C_ref) of one head from its reference probabilities p [T] and values v [T, D]."""
+    p, v, sel = _c(p, np.float64), _c(v, np.float64), _c(sel, np.int32)
+    T, D = v.shape
+    m = np.zeros(1, np.float64)
+    o_ref, c_ref = np.zeros(D, np.float64), np.zeros(D, np.float64)
+    _check(lib().orc_sparse_stats(T, D, _p(p), _p(v), sel.size, _p(sel), _p(m), _p(o_ref), _p(c_ref)), "sparse_stats")
+    return float(m[0]), o_ref, c_ref
+
+
+def sparse_correct(p_local: np.ndarray, v_sel: np.ndarray, m: float, o_ref: np.ndarray, c_ref: np.ndarray):
+    p_local, v_sel = _c(p_local, np.float64), _c(v_sel, np.float64)
+    k, D = v_sel.shape
+    out = np.zeros(D, np.float64)
+    _check(lib().orc_sparse_correct(k, D, _p(p_local), _p(v_sel), float(m), _p(_c(o_ref, np.float64)),
+                                    _p(_c(c_ref, np.float64)), _p(out)), "sparse_correct")
+    return out
+
+
+def topk_positions(scores: np.ndarray, k: int) -> np.ndarray:
+    scores = _c(scores, np.float64)
+    sel = np.zeros(k, np.int32)
+    _check(lib().orc_topk_positions(scores.size, _p(scores), k, _p(sel)), "topk_positions")
+    return sel
