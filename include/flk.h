@@ -288,6 +288,45 @@ flk_status flk_decode_attn_rolling(const flk_desc* k_desc, const flk_desc* v_des
                                    void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Sparse decode attention (RFC section 3.2).  Loop 2 is the reference: it runs full attention
+ * and keeps, per query head, the k keys with the highest reference probabilities (S, equal
+ * scores by the lower position), their probability mass m, the full output O_ref and the
+ * selected keys' weighted value sum C_ref.  A later loop r attends to the keys of S alone, read
+ * from the packed chains at depth r, and corrects the reference output:
+ *   p_local = softmax(scale * q_r . K_hat_r[S]),  O_r = O_ref - C_ref + m * (p_local . V_hat_r[S]).
+ * Mass and accumulation are binary32 (RFC section 5).  Shapes as flk_decode_attn_packed (D ==
+ * 128, n_q_heads / H <= 16); 1 <= k <= T; both calls take the packed chains of positions
+ * [0, T) without a BF16 tail.
+ * --------------------------------------------------------------------------------------- */
+
+/* Workspace of both sparse calls for T packed tokens, n_q_heads query heads, k keys per head
+ * and chains of at most n_loops loops (the reference call's scores take 4*T*n_q_heads bytes).
+ * 0 for malformed arguments. */
+size_t flk_sparse_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads, int32_t k, int32_t n_loops);
+
+/* The reference loop over chains of n_loops loops (the reference depth).
+ * q: BF16 [n_q_heads, D].  out: BF16 [n_q_heads, D], the reference loop's attention output.
+ * sel: device int32 [n_q_heads, k], S in ascending position order.  mass: device float
+ * [n_q_heads].  o_ref, c_ref: device float [n_q_heads, D].  All outputs.
+ * Errors: those of flk_decode_attn_packed, plus FLK_E_SHAPE for k out of range.            */
+flk_status flk_sparse_attn_reference(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T, const void* q,
+                                     int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                     int32_t n_loops, int32_t k, float softmax_scale, void* out, int32_t* sel,
+                                     float* mass, float* o_ref, float* c_ref, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* A later loop over chains of n_loops loops (its depth).  q: BF16 [n_q_heads, D] of this loop;
+ * sel, mass, o_ref, c_ref: the reference call's outputs (inputs here); out: BF16
+ * [n_q_heads, D].  Entries of sel outside [0, T) are a precondition violation: they are
+ * skipped.
+ * Errors: those of flk_sparse_attn_reference.                                              */
+flk_status flk_sparse_attn_loop(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T, const void* q,
+                                int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                int32_t n_loops, int32_t k, float softmax_scale, const int32_t* sel,
+                                const float* mass, const float* o_ref, const float* c_ref, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Batched calls.  A serving step encodes or rebuilds many tensors at once -- every layer's K
  * and V of a request, or of many requests -- and one kernel launch covering them avoids a
  * launch (and a ramp-up and drain of the GPU) per tensor; the RFC, section 6.2, asks for the

@@ -693,3 +693,40 @@ int orc_sparse_loop(int Hq, int Hkv, int D, int T, const uint16_t* q, const uint
     free(v);
     return st;
 }
+
+/* Scaled scores of every query head against every key of its KV head: out [Hq, T]. */
+int orc_attn_scores(int Hq, int Hkv, int D, int T, const uint16_t* q, const uint16_t* khat, double scale,
+                    double* out) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || T <= 0 || D <= 0) return ORC_E_ARG;
+    int group = Hq / Hkv;
+    double* p = (double*)malloc((size_t)T * sizeof(double));
+    if (!p) return ORC_E_ARG;
+    for (int i = 0; i < Hq; ++i)
+        head_softmax(Hkv, D, q + (size_t)i * D, khat, i / group, scale, NULL, T, out + (size_t)i * T, p);
+    free(p);
+    return ORC_OK;
+}
+
+/* The reference statistics for a given selection sel [Hq, k] (parity checks of a selection
+ * made elsewhere): mass [Hq], o_ref [Hq, D], c_ref [Hq, D]. */
+int orc_sparse_reference_given(int Hq, int Hkv, int D, int T, const uint16_t* q, const uint16_t* khat,
+                               const uint16_t* vhat, double scale, int k, const int32_t* sel, double* mass,
+                               double* o_ref, double* c_ref) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || T <= 0 || D <= 0 || k < 1 || k > T) return ORC_E_ARG;
+    int group = Hq / Hkv, st = ORC_OK;
+    double* sc = (double*)malloc((size_t)T * sizeof(double));
+    double* p = (double*)malloc((size_t)T * sizeof(double));
+    double* v = (double*)malloc((size_t)T * (size_t)D * sizeof(double));
+    if (!sc || !p || !v) st = ORC_E_ARG;
+    for (int i = 0; i < Hq && st == ORC_OK; ++i) {
+        int h = i / group;
+        head_softmax(Hkv, D, q + (size_t)i * D, khat, h, scale, NULL, T, sc, p);
+        head_values(Hkv, D, vhat, h, NULL, T, v);
+        st = orc_sparse_stats(T, D, p, v, k, sel + (size_t)i * k, mass + i, o_ref + (size_t)i * D,
+                              c_ref + (size_t)i * D);
+    }
+    free(sc);
+    free(p);
+    free(v);
+    return st;
+}

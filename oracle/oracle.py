@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
         L.orc_sparse_correct.argtypes = [i, i, P, P, ctypes.c_double, P, P, P]
         L.orc_topk_positions.restype = i
         L.orc_topk_positions.argtypes = [i, P, i, P]
+        L.orc_attn_scores.restype = i
+        L.orc_attn_scores.argtypes = [i, i, i, i, P, P, ctypes.c_double, P]
+        L.orc_sparse_reference_given.restype = i
+        L.orc_sparse_reference_given.argtypes = [i, i, i, i, P, P, P, ctypes.c_double, i, P, P, P, P]
     return _lib
 
 
@@ -405,3 +409,29 @@ def topk_positions(scores: np.ndarray, k: int) -> np.ndarray:
     sel = np.zeros(k, np.int32)
     _check(lib().orc_topk_positions(scores.size, _p(scores), k, _p(sel)), "topk_positions")
     return sel
+
+
+def attn_scores(q: np.ndarray, khat: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Binary64 scaled scores [Hq, T] of BF16 queries [Hq, D] against BF16 keys [T, Hkv, D]."""
+    q, khat = _c(q, np.uint16), _c(khat, np.uint16)
+    Hq, D = q.shape
+    T, Hkv, _ = khat.shape
+    out = np.zeros((Hq, T), np.float64)
+    _check(lib().orc_attn_scores(Hq, Hkv, D, T, _p(q), _p(khat), float(softmax_scale), _p(out)), "attn_scores")
+    return out
+
+
+def sparse_reference_given(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, softmax_scale: float,
+                           sel: np.ndarray) -> SparseRef:
+    """The reference statistics for the selection sel [Hq, k] (made elsewhere)."""
+    q, khat, vhat = _c(q, np.uint16), _c(khat, np.uint16), _c(vhat, np.uint16)
+    sel = _c(sel, np.int32)
+    Hq, D = q.shape
+    T, Hkv, _ = khat.shape
+    k = sel.shape[1]
+    mass = np.zeros(Hq, np.float64)
+    o_ref = np.zeros((Hq, D), np.float64)
+    c_ref = np.zeros((Hq, D), np.float64)
+    _check(lib().orc_sparse_reference_given(Hq, Hkv, D, T, _p(q), _p(khat), _p(vhat), float(softmax_scale), k,
+                                            _p(sel), _p(mass), _p(o_ref), _p(c_ref)), "sparse_reference_given")
+    return SparseRef(sel, mass, o_ref, c_ref)

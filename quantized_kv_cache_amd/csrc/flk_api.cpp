@@ -254,6 +254,80 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
                                            static_cast<hipStream_t>(stream)));
 }
 
+// ---- sparse decode attention ----------------------------------------------------------------
+
+namespace {
+
+// The shape and pointer checks shared by both sparse calls (those of flk_decode_attn_packed).
+flk_status check_sparse(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q, int32_t n_q_heads,
+                        const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops, int32_t k,
+                        const void* out, const int32_t* sel, const float* mass, const float* o_ref,
+                        const float* c_ref, flk::ChainArgs* kc, flk::ChainArgs* vc) {
+  flk_status st = flk_desc_check(kd);
+  if (st != FLK_OK) return st;
+  st = flk_desc_check(vd);
+  if (st != FLK_OK) return st;
+  if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
+  if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
+  if (!q || !out || !sel || !mass || !o_ref || !c_ref) return FLK_E_NULL;
+  if (T < 1 || !rows_fit(kd, T) || n_q_heads < 1 || n_q_heads % kd->n_heads != 0) return FLK_E_SHAPE;
+  if (int64_t(T) * n_q_heads >= (int64_t(1) << 31)) return FLK_E_SHAPE;   // the scores of one call
+  if (k < 1 || k > T) return FLK_E_SHAPE;
+  if (kd->head_dim != 128 || n_q_heads / kd->n_heads > 16) return FLK_E_UNSUPPORTED;
+  st = load_chain(kd, T, k_chain, n_loops, kc);
+  if (st != FLK_OK) return st;
+  st = load_chain(vd, T, v_chain, n_loops, vc);
+  if (st != FLK_OK) return st;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(sel, 4) || !aligned(mass, 4) || !aligned(o_ref, 16) ||
+      !aligned(c_ref, 16))
+    return FLK_E_ALIGN;
+  return FLK_OK;
+}
+
+}  // namespace
+
+size_t flk_sparse_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads, int32_t k, int32_t n_loops) {
+  if (flk_desc_check(k_desc) != FLK_OK || T < 1 || n_q_heads < 1 || k < 1 || k > T || n_loops < 1 ||
+      n_loops > FLK_MAX_LOOPS)
+    return 0;
+  return flk::sparse_workspace_bytes(T, k_desc->n_heads, n_q_heads, k, n_loops);
+}
+
+flk_status flk_sparse_attn_reference(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                                     int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                     int32_t n_loops, int32_t k, float softmax_scale, void* out, int32_t* sel,
+                                     float* mass, float* o_ref, float* c_ref, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  flk::ChainArgs kc, vc;
+  flk_status st = check_sparse(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, out, sel, mass, o_ref, c_ref,
+                               &kc, &vc);
+  if (st != FLK_OK) return st;
+  const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
+  if (!workspace || workspace_bytes < flk::sparse_workspace_bytes(T, kd->n_heads, n_q_heads, k, nl))
+    return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return FLK_E_ALIGN;
+  return to_status(flk::launch_sparse_reference(T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, out, sel,
+                                                mass, o_ref, c_ref, workspace, workspace_bytes,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_sparse_attn_loop(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q, int32_t n_q_heads,
+                                const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops, int32_t k,
+                                float softmax_scale, const int32_t* sel, const float* mass, const float* o_ref,
+                                const float* c_ref, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  flk::ChainArgs kc, vc;
+  flk_status st = check_sparse(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, out, sel, mass, o_ref, c_ref,
+                               &kc, &vc);
+  if (st != FLK_OK) return st;
+  const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
+  if (!workspace || workspace_bytes < flk::sparse_workspace_bytes(T, kd->n_heads, n_q_heads, k, nl))
+    return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return FLK_E_ALIGN;
+  return to_status(flk::launch_sparse_loop(T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, sel, mass, o_ref,
+                                           c_ref, out, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
 // ---- appending whole tiles (rolling-tail flush) --------------------------------------------
 
 namespace {

@@ -208,13 +208,16 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
   }
 }
 
-template <int NL>
+// SC: also write every (query head, packed token) scaled score to scores[head][position] (the
+// reference loop of sparse decode attention selects keys from them).
+template <int NL, bool SC>
 __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(ChainArgs kc, ChainArgs vc, int32_t T, int32_t H,
                                                               int32_t G, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ kt,
                                                               const uint16_t* __restrict__ vt, int32_t tail_len,
                                                               float scale, int32_t wph,
-                                                              float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+                                                              float* __restrict__ ws_ml, float* __restrict__ ws_o,
+                                                              float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[attn_lds_bytes<NL>()];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   // One 16-token slice: S^T = K Q^T on the MFMA, the online softmax, then V (from load_v,
   // called after the softmax so one operand set is live at a time) into LDS and
   // O^T += V^T P^T.  Slots 16*sl + 4*kb + i at or past n_valid are masked.
-  auto attend_slice = [&](const uint4 (&kitem)[4], int sl, int32_t n_valid, auto&& load_v) {
+  auto attend_slice = [&](const uint4 (&kitem)[4], int sl, int32_t n_valid, auto&& load_v, auto&& emit) {
     float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -265,6 +268,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       sc[i] = 16 * sl + 4 * kb + i < n_valid ? sacc[i] * scale : -__builtin_inff();
       mx = fmaxf(mx, sc[i]);
     }
+    emit(sc);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         v[i] = ok ? *reinterpret_cast<const uint4*>(vt + base + oc[i] * 8) : make_uint4(0, 0, 0, 0);
-    });
+    }, [](const float (&)[4]) {});
   }
 
   for (int32_t tile = tile0; tile < tile1; ++tile) {
@@ -382,6 +386,17 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       decode_items<FLK_KIND_K, NL>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, item);
       attend_slice(item, sl, n_valid, [&](uint4 (&v)[4]) {
         decode_items<FLK_KIND_V, NL>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, v);
+      }, [&](const float (&sc)[4]) {
+        if constexpr (SC) {
+          if (n < G) {
+            float* row = scores + int64_t(h * G + n) * T + t0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int slot = 16 * sl + 4 * kb + i;
+              if (slot < n_valid) row[L.perm[slot]] = sc[i];
+            }
+          }
+        }
       });
     }
   }
@@ -426,7 +441,9 @@ constexpr int kCombGroups = 8;
 __global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int32_t splits, int32_t Hq,
                                                                             const float* __restrict__ ws_ml,
                                                                             const float* __restrict__ ws_o,
-                                                                            uint16_t* __restrict__ out) {
+                                                                            uint16_t* __restrict__ out,
+                                                                            float* __restrict__ out32,
+                                                                            float* __restrict__ ml_out) {
   __shared__ float s_red[kCombGroups * kAttnD];
   __shared__ float s_l[kCombGroups * kAttnD];
   const int i = blockIdx.x;
@@ -463,14 +480,19 @@ __global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int3
       Lt += s_l[k * kAttnD + c];
     }
     out[int64_t(i) * kAttnD + c] = __builtin_bit_cast(uint16_t, (__bf16)(Ot / Lt));
+    if (out32) out32[int64_t(i) * kAttnD + c] = Ot / Lt;     // the sparse reference's O_ref
+    if (ml_out && c == 0) {                                   // and its softmax max and denominator
+      ml_out[2 * i] = M;
+      ml_out[2 * i + 1] = Lt;
+    }
   }
 }
 
-hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
-                              const ChainArgs& kc, const ChainArgs& vc, const void* k_tail,
-                              const void* v_tail, int32_t tail_len, float scale, void* out,
-                              void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)D;
+template <bool SC>
+static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+                              const ChainArgs& vc, const void* k_tail, const void* v_tail, int32_t tail_len,
+                              float scale, void* out, float* out32, float* ml_out, float* scores, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   if (ws == nullptr || ws_bytes < attn_workspace_need(T, tail_len, H, Hq)) return hipErrorInvalidValue;
   const int32_t tiles = attn_tiles(T, tail_len);
   const int32_t wph = waves_per_head(tiles, H);
@@ -484,10 +506,10 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
   int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
   if (nl < 1) nl = 1;                              // no packed tokens: only the tail's tiles run
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
-#define FLK_A(NLV)                                                                                      \
-  case NLV:                                                                                             \
-    hipLaunchKernelGGL((attn_wave_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
-                       ktp, vtp, tail_len, scale, wph, ws_ml, ws_o);                                    \
+#define FLK_A(NLV)                                                                                          \
+  case NLV:                                                                                                 \
+    hipLaunchKernelGGL((attn_wave_kernel<NLV, SC>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
+                       ktp, vtp, tail_len, scale, wph, ws_ml, ws_o, scores);                                \
     break;
   switch (nl) {
     FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
@@ -497,8 +519,24 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, splits, Hq, ws_ml,
-                     ws_o, static_cast<uint16_t*>(out));
+                     ws_o, static_cast<uint16_t*>(out), out32, ml_out);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q,
+                              const ChainArgs& kc, const ChainArgs& vc, const void* k_tail,
+                              const void* v_tail, int32_t tail_len, float scale, void* out,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)D;
+  return launch_attn<false>(T, H, Hq, q, kc, vc, k_tail, v_tail, tail_len, scale, out, nullptr, nullptr, nullptr,
+                            ws, ws_bytes, stream);
+}
+
+hipError_t launch_attn_reference(int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+                                 const ChainArgs& vc, float scale, void* out, float* o_ref, float* ml,
+                                 float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return launch_attn<true>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, o_ref, ml, scores, ws, ws_bytes,
+                           stream);
 }
 
 }  // namespace flk

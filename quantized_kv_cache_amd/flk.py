@@ -124,6 +124,13 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [D, D, ctypes.POINTER(AppendUnitC), i32, P, P]
         L.flk_reconstruct_batch.restype = ctypes.c_int
         L.flk_reconstruct_batch.argtypes = [D, D, ctypes.POINTER(ReconUnitC), i32, P]
+        L.flk_sparse_workspace_bytes.restype = sz
+        L.flk_sparse_workspace_bytes.argtypes = [D, i32, i32, i32, i32]
+        L.flk_sparse_attn_reference.restype = ctypes.c_int
+        L.flk_sparse_attn_reference.argtypes = [D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P, P, P,
+                                                sz, P]
+        L.flk_sparse_attn_loop.restype = ctypes.c_int
+        L.flk_sparse_attn_loop.argtypes = [D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P, P, P, sz, P]
         L.flk_decode_attn_packed.restype = ctypes.c_int
         L.flk_decode_attn_packed.argtypes = [D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P, sz, P]
         _lib = L
@@ -420,3 +427,54 @@ def append_residual_batch(items, H: int, D: int, status: Optional[torch.Tensor] 
     kt = _k_tiles(it[-1].k_tiles for it in items if it[0] == K)
     _check(lib().flk_append_residual_batch(ctypes.byref(desc(K, H, D, kt)), ctypes.byref(desc(V, H, D)), arr,
                                            len(units), _ptr(status), _stream(stream)), "flk_append_residual_batch")
+
+
+# ----------------------------------------------------------------------------- sparse decode attention
+
+def sparse_workspace_bytes(H: int, D: int, T: int, n_q_heads: int, k: int, n_loops: int) -> int:
+    return int(lib().flk_sparse_workspace_bytes(ctypes.byref(desc(K, H, D)), T, n_q_heads, k, n_loops))
+
+
+@dataclass
+class SparseState:
+    """Reference-loop state per query head (device tensors): S [Hq, k] int32 ascending
+    positions, mass [Hq], o_ref and c_ref [Hq, D] float32."""
+    sel: torch.Tensor
+    mass: torch.Tensor
+    o_ref: torch.Tensor
+    c_ref: torch.Tensor
+
+    @staticmethod
+    def empty(n_q_heads: int, D: int, k: int, device="cuda") -> "SparseState":
+        return SparseState(torch.empty((n_q_heads, k), dtype=torch.int32, device=device),
+                           torch.empty(n_q_heads, dtype=torch.float32, device=device),
+                           torch.empty((n_q_heads, D), dtype=torch.float32, device=device),
+                           torch.empty((n_q_heads, D), dtype=torch.float32, device=device))
+
+
+def sparse_attn_reference(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int, H: int,
+                          k: int, softmax_scale: float, out: torch.Tensor, state: SparseState,
+                          workspace: torch.Tensor, stream=None) -> None:
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    Hq, D = q.shape
+    ka, va = _chain(k_chain), _chain(v_chain)
+    _check(lib().flk_sparse_attn_reference(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles)), ctypes.byref(desc(V, H, D)),
+                                           T, _ptr(q), Hq, ka, va, len(k_chain), k, float(softmax_scale), _ptr(out),
+                                           _ptr(state.sel), _ptr(state.mass), _ptr(state.o_ref), _ptr(state.c_ref),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)), "flk_sparse_attn_reference")
+
+
+def sparse_attn_loop(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int, H: int, k: int,
+                     softmax_scale: float, state: SparseState, out: torch.Tensor, workspace: torch.Tensor,
+                     stream=None) -> None:
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    Hq, D = q.shape
+    ka, va = _chain(k_chain), _chain(v_chain)
+    _check(lib().flk_sparse_attn_loop(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles)), ctypes.byref(desc(V, H, D)), T,
+                                      _ptr(q), Hq, ka, va, len(k_chain), k, float(softmax_scale), _ptr(state.sel),
+                                      _ptr(state.mass), _ptr(state.o_ref), _ptr(state.c_ref), _ptr(out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "flk_sparse_attn_loop")

@@ -308,3 +308,40 @@ def test_batched_append_validation():
     assert call([unit()], resid=False) == 2             # loop 1 is dense
     # every unit is checked before anything launches: a bad last unit fails the call
     assert call([unit(kind=flk.V), unit(n=65)]) == 2
+
+
+def test_sparse_attention_validation():
+    L = flk.lib()
+    kd, vd = flk.desc(flk.K, 8, 128), flk.desc(flk.V, 8, 128)
+    S = flk.StreamC
+    T = 256
+    chain = (S * 1)(S(T, 0, None, FAKE.value, FAKE.value, None))
+    ws = flk.sparse_workspace_bytes(8, 128, T, 32, 16, 1)
+    assert ws > 32 * T * 4                       # holds the reference scores
+    assert flk.sparse_workspace_bytes(8, 128, T, 32, T + 1, 1) == 0
+    assert flk.sparse_workspace_bytes(8, 128, T, 32, 16, 0) == 0
+
+    def ref(k=16, q=FAKE, sel=FAKE, w=FAKE, wb=ws, n_loops=1, hq=32, kd=kd, vd=vd, c=FAKE):
+        return L.flk_sparse_attn_reference(ctypes.byref(kd), ctypes.byref(vd), T, q, hq, chain, chain, n_loops, k,
+                                           0.088, FAKE, sel, FAKE, FAKE, c, w, wb, None)
+
+    def loop(k=16, sel=FAKE, wb=ws, c=FAKE):
+        return L.flk_sparse_attn_loop(ctypes.byref(kd), ctypes.byref(vd), T, FAKE, 32, chain, chain, 1, k, 0.088,
+                                      sel, FAKE, FAKE, c, FAKE, FAKE, wb, None)
+    assert ref(kd=vd, vd=kd) == 4
+    assert ref(q=None) == 1
+    assert ref(sel=None) == 1
+    assert ref(k=0) == 2
+    assert ref(k=T + 1) == 2
+    assert ref(hq=30) == 2
+    assert ref(hq=8 * 17) == 5
+    assert ref(n_loops=0) == 2
+    assert ref(sel=MIS) == 3
+    assert ref(c=MIS) == 3
+    assert ref(wb=64) == 6
+    assert ref(w=None) == 6
+    assert ref(w=ctypes.c_void_p((1 << 20) + 16)) == 3   # the workspace is 256-byte aligned
+    assert loop(k=0) == 2
+    assert loop(sel=None) == 1
+    assert loop(wb=64) == 6
+    assert loop(c=MIS) == 3

@@ -105,3 +105,16 @@ def test_unchanged_loop_reproduces_the_reference_output():
     ref = orc.sparse_reference(q, k2, v2, 0.2, k)
     assert np.all(ref.mass < 1.0)
     assert np.allclose(orc.sparse_loop(q, k2, v2, 0.2, ref), ref.o_ref, atol=1e-12)
+
+
+def test_given_selection_and_scores_agree_with_the_reference():
+    rng = np.random.default_rng(4)
+    T, H, Hq, D, k = 150, 2, 4, 8, 20
+    k2, v2 = _random_kv(rng, T, H, D, 2.0)
+    q = orc.bf16_from_f32(rng.standard_normal((Hq, D)).astype(np.float32))
+    ref = orc.sparse_reference(q, k2, v2, 0.4, k)
+    given = orc.sparse_reference_given(q, k2, v2, 0.4, ref.sel)
+    assert np.allclose(given.mass, ref.mass, atol=1e-15) and np.allclose(given.c_ref, ref.c_ref, atol=1e-13)
+    s = orc.attn_scores(q, k2, 0.4)
+    for i in range(Hq):
+        assert np.array_equal(orc.topk_positions(s[i], k), ref.sel[i])
