@@ -337,6 +337,71 @@ def _timed_us(fn, reps, flush=None):
     return float(np.median(times))
 
 
+def decode_chains(w, k_tiles):
+    """The decode workload's K and V chains, encoded by the library from the seeded inputs."""
+    T, H, D = w.T, w.H, w.D
+    sets = synth.active_sets(w, T)
+    chains = {}
+    for kind, tensor in ((flk.K, synth.K_TENSOR), (flk.V, synth.V_TENSOR)):
+        c = synth.make_chain(w, tensor, sets=sets)
+        recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+        packs = []
+        for l, (x, r) in enumerate(zip(c.xs, c.rows)):
+            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+            rd = None if r is None else torch.from_numpy(r).cuda()
+            p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T, k_tiles=k_tiles)
+            if l == 0:
+                flk.encode_base(kind, xd, p, recon)
+            else:
+                flk.encode_residual(kind, xd, rd, recon, p)
+            packs.append(p)
+        chains[kind] = packs
+        del recon
+    return chains
+
+
+def sparse_leg(k=4096, reps=20):
+    """Sparse decode attention (RFC section 3.2) on the decode workload (131072 packed tokens,
+    8 KV heads, 32 query heads, D=128, chains at 100/100/50/25% with tile-grouped K), k keys
+    per query head: the reference call at loop 2 (full attention writing the scores, the top-k
+    selection, the selected keys' mass and C_ref), the loop calls at loops 3 and 4 (only the
+    selected keys, read through the chains at depth 3 and 4), next to dense packed attention
+    at the same depths.  Each call is timed with a cold MALL (a 512 MiB write before it)."""
+    w = synth.WORKLOADS[5]
+    T, H, D, Hq = w.T, w.H, w.D, w.Hq
+    chains = decode_chains(w, k_tiles=True)
+    rng = np.random.default_rng(7)
+    qs = {d: torch.randn((Hq, D), device="cuda").to(torch.bfloat16) for d in (2, 3, 4)}
+    del rng
+    scale = 1.0 / math.sqrt(D)
+    ws = torch.empty(max(flk.sparse_workspace_bytes(H, D, T, Hq, k, 4), flk.attn_workspace_bytes(H, D, T, Hq)) // 4
+                     + 64, dtype=torch.float32, device="cuda")
+    ws = ws[(-ws.data_ptr() // 4) % 64:]
+    st = flk.SparseState.empty(Hq, D, k)
+    out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    K, V = chains[flk.K], chains[flk.V]
+    ref = lambda: flk.sparse_attn_reference(qs[2], K[:2], V[:2], T, H, k, scale, out, st, ws)
+    loop = {d: (lambda d=d: flk.sparse_attn_loop(qs[d], K[:d], V[:d], T, H, k, scale, st, out, ws)) for d in (3, 4)}
+    dense = {d: (lambda d=d: flk.decode_attn_packed(qs[d], K[:d], V[:d], T, H, scale, out, ws)) for d in (2, 3, 4)}
+    for _ in range(3):
+        ref()
+        for d in (3, 4):
+            loop[d]()
+        for d in (2, 3, 4):
+            dense[d]()
+    torch.cuda.synchronize()
+    res = {"workload": "decode_attn", "T": T, "Hkv": H, "Hq": Hq, "D": D, "k": k, "k_grouping": "tile",
+           "reference_us": round(_timed_us(ref, reps, flush), 2)}
+    for d in (3, 4):
+        res[f"loop{d}_us"] = round(_timed_us(loop[d], reps, flush), 2)
+    for d in (2, 3, 4):
+        res[f"dense_depth{d}_us"] = round(_timed_us(dense[d], reps, flush), 2)
+    res["sparse_loops_3_4_us"] = round(res["loop3_us"] + res["loop4_us"], 2)
+    res["dense_loops_3_4_us"] = round(res["dense_depth3_us"] + res["dense_depth4_us"], 2)
+    return res
+
+
 def rolling_leg(reps=50):
     """The rolling BF16 tail (RFC section 3.3): decode tokens wait in BF16 until a whole
     64-token group can be flushed into the packed streams, whose K groups are tile-local.
@@ -429,23 +494,7 @@ def rolling_leg(reps=50):
     # attention over 131072 packed tokens (tile-grouped K) + a 127-token BF16 tail
     w = synth.WORKLOADS[5]
     T, Hk, Dk, Hq = w.T, w.H, w.D, w.Hq
-    sets = synth.active_sets(w, T)
-    chains = {}
-    for kind, tensor in ((flk.K, synth.K_TENSOR), (flk.V, synth.V_TENSOR)):
-        c = synth.make_chain(w, tensor, sets=sets)
-        recon = torch.empty((T, Hk, Dk), dtype=torch.bfloat16, device="cuda")
-        packs = []
-        for l, (x, r) in enumerate(zip(c.xs, c.rows)):
-            xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
-            rd = None if r is None else torch.from_numpy(r).cuda()
-            p = flk.Packed.empty(kind, Hk, Dk, x.shape[0], rd, T=T, k_tiles=True)
-            if l == 0:
-                flk.encode_base(kind, xd, p, recon)
-            else:
-                flk.encode_residual(kind, xd, rd, recon, p)
-            packs.append(p)
-        chains[kind] = packs
-        del recon
+    chains = decode_chains(w, k_tiles=True)
     tail = 127
     assert flk.rolling_prefix(T + tail) == T
     kt = torch.randn((tail, Hk, Dk), device="cuda").to(torch.bfloat16)
@@ -612,6 +661,7 @@ def main():
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
     ap.add_argument("--no-page-local", action="store_true", help="skip the page-local K grouping leg")
     ap.add_argument("--no-rolling", action="store_true", help="skip the rolling-tail flush and attention leg")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the sparse decode attention leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -746,6 +796,9 @@ def main():
     if not args.no_rolling:
         log("rolling tail: flush and attention ...")
         result["rolling"] = rolling_leg()
+    if not args.no_sparse:
+        log("sparse decode attention ...")
+        result["sparse_attention"] = sparse_leg()
     if not args.no_cpu_baseline:
         log("timing the oracle on a head sample ...")
         result["cpu_baseline"] = cpu_baseline(w, host, sets)

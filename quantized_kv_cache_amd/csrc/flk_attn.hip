@@ -208,8 +208,8 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
   }
 }
 
-// SC: also write every (query head, packed token) scaled score to scores[head][position] (the
-// reference loop of sparse decode attention selects keys from them).
+// SC: also write every (query head, packed token) scaled score to scores[head][position], rows
+// of ceil(T/4)*4 floats (the reference loop of sparse decode attention selects keys from them).
 template <int NL, bool SC>
 __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(ChainArgs kc, ChainArgs vc, int32_t T, int32_t H,
                                                               int32_t G, const uint16_t* __restrict__ q,
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       }, [&](const float (&sc)[4]) {
         if constexpr (SC) {
           if (n < G) {
-            float* row = scores + int64_t(h * G + n) * T + t0;
+            float* row = scores + int64_t(h * G + n) * ((int64_t(T) + 3) & ~int64_t(3)) + t0;  // rows padded to 16 B
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int slot = 16 * sl + 4 * kb + i;

@@ -25,85 +25,170 @@ constexpr int kKeysPerBlock = kKeysPerWave * kSWaves;
 constexpr int kTopThreads = 1024;
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// Floats between two query heads' rows of reference scores (16-byte aligned rows).
+__host__ __device__ __forceinline__ int64_t score_stride(int32_t T) { return (int64_t(T) + 3) & ~int64_t(3); }
 
 // ---------------------------------------------------------------------------------------
 // Top-k per query head.  Scores map to unsigned keys whose order is the scores' order; a
 // radix select over three digits (bits 31..21, 20..10, 9..0) finds the k-th largest key tau
 // and how many keys equal to tau belong to S (the lowest positions among them); a final pass
-// writes S in position order (a block-wide scan of each thread's counts over its contiguous
-// chunk).
+// writes S in position order, each wave over a contiguous segment, counting with ballots 64
+// coalesced values at a time.  Every pass keeps kTopBatch loads in flight per thread: with one
+// block per head nothing else hides the memory latency.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t u = __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan of one value per thread across the block (Hillis-Steele in LDS).
-__device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* buf) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTopThreads; off <<= 1) {
-    const uint32_t add = tid >= off ? buf[tid - off] : 0u;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+constexpr int kTopWaves = kTopThreads / 64;
+constexpr int kTopBatch = 8;                 // 16-byte score loads in flight per thread
+
+// Four consecutive scores t..t+3 of a row as keys (t a multiple of 4); positions at or past T
+// give key 0, below every real score's key.
+__device__ __forceinline__ void keys4(const float* __restrict__ sc, int32_t t, int32_t T, uint32_t k[4]) {
+  if (t + 3 < T) {
+    const float4 v = *reinterpret_cast<const float4*>(sc + t);
+    k[0] = order_key(v.x); k[1] = order_key(v.y); k[2] = order_key(v.z); k[3] = order_key(v.w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k[e] = t + e < T ? order_key(sc[t + e]) : 0u;
   }
-  const uint32_t r = buf[tid];
-  __syncthreads();
+}
+
+// Sum over the lanes below this one of a per-lane count 0..7, from three ballots of its bits.
+__device__ __forceinline__ uint32_t lanes_below_sum(uint32_t c, uint64_t below) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int b = 0; b < 3; ++b) r += uint32_t(__builtin_popcountll(__ballot((c >> b) & 1u) & below)) << b;
+  return r;
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t c) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int b = 0; b < 3; ++b) r += uint32_t(__builtin_popcountll(__ballot((c >> b) & 1u))) << b;
   return r;
 }
 
+// Rows of scores are ceil(T/4)*4 floats apart (16-byte aligned) and read 4 at a time.
 __global__ __launch_bounds__(kTopThreads) void topk_kernel(const float* __restrict__ scores, int32_t T, int32_t k,
                                                            int32_t* __restrict__ sel) {
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t buf[kTopThreads];
+  __shared__ uint32_t s_cnt[kTopWaves][2];
   __shared__ uint32_t s_digit, s_above;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
   const int32_t qh = blockIdx.x;
-  const float* sc = scores + int64_t(qh) * T;
+  const float* sc = scores + int64_t(qh) * score_stride(T);
   uint32_t prefix = 0, pmask = 0, need = uint32_t(k);
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
     const uint32_t nb = pass == 2 ? 1024u : 2048u;
     for (int b = tid; b < 2048; b += kTopThreads) hist[b] = 0;
     __syncthreads();
-    for (int32_t t = tid; t < T; t += kTopThreads) {
-      const uint32_t key = order_key(sc[t]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+    for (int32_t t0 = 0; t0 < T; t0 += 4 * kTopThreads * kTopBatch) {
+      uint32_t key[kTopBatch][4];
+#pragma unroll
+      for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 4 * (i * kTopThreads + tid), T, key[i]);
+#pragma unroll
+      for (int i = 0; i < kTopBatch; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int32_t t = t0 + 4 * (i * kTopThreads + tid) + e;
+          if (t < T && (key[i][e] & pmask) == prefix) atomicAdd(&hist[(key[i][e] >> shift) & (nb - 1)], 1u);
+        }
     }
     __syncthreads();
-    // counts from the top digit down: thread t owns digits nb-1-2t and nb-2-2t
-    const int32_t d0 = int32_t(nb) - 1 - 2 * tid, d1 = d0 - 1;
-    const uint32_t c0 = d0 >= 0 ? hist[d0] : 0u, c1 = d1 >= 0 ? hist[d1] : 0u;
-    const uint32_t incl = block_scan_incl(c0 + c1, buf);
-    const uint32_t before0 = incl - c0 - c1, before1 = before0 + c0;
-    if (d0 >= 0 && before0 < need && need <= before0 + c0) { s_digit = uint32_t(d0); s_above = before0; }
-    if (d1 >= 0 && before1 < need && need <= before1 + c1) { s_digit = uint32_t(d1); s_above = before1; }
+    if (wave == 0) {                                       // from the top digit down to the k-th key
+      // lane l holds digits [nb - 32(l+1), nb - 32l); counts above it by a prefix over lanes
+      const int32_t d_hi = int32_t(nb) - 32 * lane;         // exclusive
+      uint32_t c = 0;
+      if (d_hi > 0)
+        for (int i = 1; i <= 32; ++i) c += hist[d_hi - i];
+      uint32_t before = c;                                   // inclusive prefix over lanes 0..l
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(before, off);
+        if (lane >= off) before += o;
+      }
+      before -= c;
+      if (d_hi > 0 && before < need && need <= before + c) {
+        uint32_t above = before;
+        for (int i = 1; i <= 32; ++i) {
+          const uint32_t h = hist[d_hi - i];
+          if (above + h >= need) { s_digit = uint32_t(d_hi - i); s_above = above; break; }
+          above += h;
+        }
+      }
+    }
     __syncthreads();
     prefix |= s_digit << shift;
     pmask |= (nb - 1) << shift;
     need -= s_above;
     __syncthreads();
   }
-  // prefix is tau; `need` keys equal to tau are selected, the lowest positions first
-  const int32_t chunk = (T + kTopThreads - 1) / kTopThreads;
-  const int32_t c_lo = min(T, tid * chunk), c_hi = min(T, c_lo + chunk);
+  // prefix is tau; `need` keys equal to tau are selected, the lowest positions first.  Wave w
+  // owns the contiguous segment [w*seg, (w+1)*seg) of positions, 256 of them per step (lane l
+  // holds positions 4l..4l+3 of the step).
+  const int32_t seg = ((T + kTopWaves - 1) / kTopWaves + 255) & ~255;
+  const int32_t lo = min(T, wave * seg), hi = min(T, lo + seg);
   uint32_t gt = 0, eq = 0;
-  for (int32_t t = c_lo; t < c_hi; ++t) {
-    const uint32_t key = order_key(sc[t]);
-    gt += key > prefix;
-    eq += key == prefix;
+  for (int32_t t0 = lo; t0 < hi; t0 += 256 * kTopBatch) {
+    uint32_t key[kTopBatch][4];
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 256 * i + 4 * lane, hi, key[i]);
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) {
+      uint32_t g = 0, q = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = t0 + 256 * i + 4 * lane + e < hi;
+        g += in && key[i][e] > prefix;
+        q += in && key[i][e] == prefix;
+      }
+      gt += wave_sum(g);
+      eq += wave_sum(q);
+    }
   }
-  const uint32_t g0 = block_scan_incl(gt, buf) - gt;
-  const uint32_t e0 = block_scan_incl(eq, buf) - eq;
-  uint32_t out = g0 + min(e0, need), e = e0;
+  if (lane == 0) { s_cnt[wave][0] = gt; s_cnt[wave][1] = eq; }
+  __syncthreads();
+  uint32_t g0 = 0, e0 = 0;
+  for (int w = 0; w < wave; ++w) { g0 += s_cnt[w][0]; e0 += s_cnt[w][1]; }
   int32_t* dst = sel + int64_t(qh) * k;
-  for (int32_t t = c_lo; t < c_hi; ++t) {
-    const uint32_t key = order_key(sc[t]);
-    bool take = key > prefix;
-    if (key == prefix) take = e++ < need;
-    if (take && out < uint32_t(k)) dst[out++] = t;
+  uint32_t out = g0 + min(e0, need), e_seen = e0;
+  for (int32_t t0 = lo; t0 < hi; t0 += 256 * kTopBatch) {
+    uint32_t key[kTopBatch][4];
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 256 * i + 4 * lane, hi, key[i]);
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) {
+      const int32_t tb = t0 + 256 * i + 4 * lane;
+      bool is_eq[4];
+      uint32_t q = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        is_eq[e] = tb + e < hi && key[i][e] == prefix;
+        q += is_eq[e];
+      }
+      uint32_t eq_rank = e_seen + lanes_below_sum(q, below);   // equal keys before this lane's
+      bool take[4];
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        take[e] = (tb + e < hi && key[i][e] > prefix) || (is_eq[e] && eq_rank < need);
+        eq_rank += is_eq[e];
+        c += take[e];
+      }
+      uint32_t slot = out + lanes_below_sum(c, below);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (take[e]) {
+          if (slot < uint32_t(k)) dst[slot] = tb + e;
+          ++slot;
+        }
+      out += wave_sum(c);
+      e_seen += wave_sum(q);
+    }
   }
 }
 
@@ -291,7 +376,7 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
         }
       }
     } else {
-      const float w = p >= 0 ? __expf(g.scores[int64_t(qh) * g.T + p] - M) * Linv : 0.0f;
+      const float w = p >= 0 ? __expf(g.scores[int64_t(qh) * score_stride(g.T) + p] - M) * Linv : 0.0f;
       m_run += sum16(w);
       if (p >= 0) {
 #pragma unroll
@@ -360,6 +445,7 @@ __global__ __launch_bounds__(kSD) void sparse_combine_kernel(const float* __rest
   const float* pp = part + int64_t(qh) * nblk * (2 + kSD);
   if (MODE == 0) {
     float m = 0.0f, O = 0.0f;
+#pragma unroll 8
     for (int32_t b = 0; b < nblk; ++b) {
       m += pp[b * (2 + kSD)];
       O += pp[b * (2 + kSD) + 2 + c];
@@ -368,8 +454,10 @@ __global__ __launch_bounds__(kSD) void sparse_combine_kernel(const float* __rest
     if (c == 0) mass_out[qh] = m;
   } else {
     float Mx = -__builtin_inff();
+#pragma unroll 8
     for (int32_t b = 0; b < nblk; ++b) Mx = fmaxf(Mx, pp[b * (2 + kSD)]);
     float L = 0.0f, O = 0.0f;
+#pragma unroll 8
     for (int32_t b = 0; b < nblk; ++b) {
       const float mb = pp[b * (2 + kSD)];
       const float f = mb == -__builtin_inff() ? 0.0f : __expf(mb - Mx);
@@ -399,7 +487,7 @@ static SparseLayout sparse_layout(int32_t T, int32_t H, int32_t Hq, int32_t k, i
   L.vmaps = off; off += map_bytes;
   L.part = off; off += align256(size_t(Hq) * gather_blocks(k) * (2 + kSD) * sizeof(float));
   L.attn = off; off += align256(attn_workspace_bytes(T, H, Hq));
-  L.scores = off; off += align256(size_t(Hq) * size_t(T) * sizeof(float));
+  L.scores = off; off += align256(size_t(Hq) * size_t(score_stride(T)) * sizeof(float));
   L.ml = off; off += align256(size_t(Hq) * 2 * sizeof(float));
   L.total = off;
   return L;
