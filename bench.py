@@ -522,16 +522,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prompt.txt")
 COPY_PROBE_BYTES = 1 << 29     # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE (2x the MALL)
 
 
+# The sources the codec kernels (encode, residual encode, reconstruct) are compiled from.
+CODEC_SOURCES = ("flk_device.h", "flk_encode.hip", "flk_internal.h", "flk_reconstruct.hip")
+
+
 def source_digest():
-    """sha256 over the sources of the codec kernels and their launches (everything in csrc/ but
-    the host-side validation and the attention kernels): a traffic figure taken from other
-    kernel sources than the ones built now is not reported."""
+    """sha256 over CODEC_SOURCES: a traffic figure taken from other kernel sources than the ones
+    built now is not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")) and name not in ("flk_api.cpp", "flk_attn.hip"):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in CODEC_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 

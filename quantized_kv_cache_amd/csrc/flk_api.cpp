@@ -13,6 +13,7 @@
 
 #include "../../include/flk.h"
 #include "flk_internal.h"
+#include "flk_readers.h"
 
 namespace {
 

@@ -19,6 +19,7 @@
 // rolling cache's recent tokens) is read as stored, 16 tokens per wave.
 #include "flk_device.h"
 #include "flk_internal.h"
+#include "flk_readers.h"
 
 namespace flk {
 

@@ -14,6 +14,7 @@
 // entry per loop instead of searching.
 #include "flk_device.h"
 #include "flk_internal.h"
+#include "flk_readers.h"
 
 namespace flk {
 
