@@ -302,7 +302,7 @@ def attention_leg(reps=20):
     torch.cuda.synchronize()
     times = []
     for _ in range(reps):
-        flush.fill_(1)
+        flush.view(torch.int64).sum()                                  # clean MALL (see _timed_us)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         flk.decode_attn_packed(q, chains[flk.K], chains[flk.V], T, H, scale, out, ws)
@@ -323,11 +323,12 @@ def attention_leg(reps=20):
 
 def _timed_us(fn, reps, flush=None):
     """Median of `reps` calls of fn (HIP events on the current stream); `flush`, when given, is
-    written before each call so the MALL holds none of fn's data."""
+    read before each call so the MALL holds none of fn's data.  Reading leaves clean lines: a
+    flush by writing would leave dirty lines whose write-back then falls inside fn's time."""
     times = []
     for _ in range(reps):
         if flush is not None:
-            flush.fill_(1)
+            flush.view(torch.int64).sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
@@ -370,9 +371,9 @@ def sparse_leg(k=4096, reps=20):
     w = synth.WORKLOADS[5]
     T, H, D, Hq = w.T, w.H, w.D, w.Hq
     chains = decode_chains(w, k_tiles=True)
-    rng = np.random.default_rng(7)
-    qs = {d: torch.randn((Hq, D), device="cuda").to(torch.bfloat16) for d in (2, 3, 4)}
-    del rng
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    qs = {d: torch.randn((Hq, D), device="cuda", generator=g).to(torch.bfloat16) for d in (2, 3, 4)}
     scale = 1.0 / math.sqrt(D)
     ws = torch.empty(max(flk.sparse_workspace_bytes(H, D, T, Hq, k, 4), flk.attn_workspace_bytes(H, D, T, Hq)) // 4
                      + 64, dtype=torch.float32, device="cuda")
@@ -399,6 +400,47 @@ def sparse_leg(k=4096, reps=20):
         res[f"dense_depth{d}_us"] = round(_timed_us(dense[d], reps, flush), 2)
     res["sparse_loops_3_4_us"] = round(res["loop3_us"] + res["loop4_us"], 2)
     res["dense_loops_3_4_us"] = round(res["dense_depth3_us"] + res["dense_depth4_us"], 2)
+    return res
+
+
+def selection_leg(reps=20):
+    """Token selection for sparse prefill (RFC section 3.1) on the long prompt: T=32768 tokens,
+    hidden width d=4096, selection windows of 2048 tokens; loop 3 keeps 50 % of a dense loop 2,
+    loop 4 keeps 25 % of each window's length from loop 3's tokens.  The hidden states follow
+    the recipe of synth.hidden_states, drawn on the GPU from a seeded generator.  A call reads
+    the eligible rows of H[r-1] and H[r-2] once (512 MiB at loop 3, 256 MiB at loop 4) and
+    writes the scores, the selected positions and the slot map."""
+    T, d, W = 32768, 4096, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261203)
+    mag = torch.exp(torch.empty((T, 1), device="cuda").uniform_(math.log(0.5), math.log(2.0), generator=g))
+    y = torch.randn((T, d), device="cuda", generator=g) * mag
+    hs = [y.to(torch.bfloat16)]
+    for _ in range(2):
+        size = torch.exp(torch.empty((T, 1), device="cuda").uniform_(math.log(0.01), 0.0, generator=g))
+        y = y + torch.randn((T, d), device="cuda", generator=g) * size
+        hs.append(y.to(torch.bfloat16))
+    del y, mag, size
+    n3, n4 = flk.select_count(T, W, [50]), flk.select_count(T, W, [50, 25])
+    i32 = dict(dtype=torch.int32, device="cuda")
+    scores = torch.empty(T, dtype=torch.float32, device="cuda")
+    rows3, rows4, slot = torch.empty(n3, **i32), torch.empty(n4, **i32), torch.empty(T, **i32)
+    ws = torch.empty(flk.select_workspace_bytes(T, W) // 4, **i32)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    l3 = lambda: flk.select_rows(hs[1], hs[0], None, W, 50, 1e-6, scores, rows3, ws, slot)
+    l4 = lambda: flk.select_rows(hs[2], hs[1], rows3, W, 25, 1e-6, scores, rows4, ws, slot)
+    for _ in range(3):
+        l3()
+        l4()
+    torch.cuda.synchronize()
+    res = {"workload": "token_selection", "T": T, "d": d, "window": W, "budgets_pct": [50, 25]}
+    # scoring reads both hidden rows (and the eligible list) and writes a score; the top-k
+    # reads the scores (and the list), writes the positions and the slot map
+    for name, fn, n_prev, n_out, compact in (("loop3", l3, T, n3, False), ("loop4", l4, n3, n4, True)):
+        us = _timed_us(fn, reps, flush)
+        b = 2 * n_prev * d * 2 + 4 * n_prev + 4 * n_prev + 4 * n_out + 4 * T + (8 * n_prev if compact else 0)
+        res[f"{name}_us"] = round(us, 2)
+        res[f"{name}_gbs"] = round(b / us / 1e3, 1)
     return res
 
 
@@ -664,6 +706,7 @@ def main():
     ap.add_argument("--no-page-local", action="store_true", help="skip the page-local K grouping leg")
     ap.add_argument("--no-rolling", action="store_true", help="skip the rolling-tail flush and attention leg")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse decode attention leg")
+    ap.add_argument("--no-selection", action="store_true", help="skip the token selection leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -801,6 +844,9 @@ def main():
     if not args.no_sparse:
         log("sparse decode attention ...")
         result["sparse_attention"] = sparse_leg()
+    if not args.no_selection:
+        log("token selection ...")
+        result["token_selection"] = selection_leg()
     if not args.no_cpu_baseline:
         log("timing the oracle on a head sample ...")
         result["cpu_baseline"] = cpu_baseline(w, host, sets)

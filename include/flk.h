@@ -112,6 +112,9 @@ enum { FLK_KGROUP_ROWS = 0, FLK_KGROUP_TILE = 1 };
 #define FLK_DEV_NONFINITE 1u  /* a group held an Inf or NaN value                           */
 #define FLK_DEV_RANGE 2u      /* a group's minimum or scale overflowed FP16                 */
 #define FLK_DEV_ROWS 4u       /* a rows entry lay outside [0, T); that row was skipped      */
+#define FLK_DEV_COUNT 8u      /* token selection: the windows' budgets do not add up to n_out */
+#define FLK_DEV_CLASS 16u     /* row partition: a class value other than FLK_ROW_*; the row
+                                 was left out as inactive                                  */
 
 /* Versioned encoding descriptor (the RFC, section 6.5: bit width, group axes and sizes and
  * depth representation travel with the data).  Fill with flk_desc_init(). */
@@ -325,6 +328,79 @@ flk_status flk_sparse_attn_loop(const flk_desc* k_desc, const flk_desc* v_desc, 
                                 int32_t n_loops, int32_t k, float softmax_scale, const int32_t* sel,
                                 const float* mass, const float* o_ref, const float* c_ref, void* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Token selection for sparse prefill (RFC section 3.1, "Token-sparse prefill", and its fixed
+ * selection windows; section 6.2 for the row partition).  Loops 1 and 2 run densely; before
+ * loop r >= 3 every token active at loop r-1 gets the change score
+ *   score = ||H[r-1] - H[r-2]|| / max(||H[r-1]||, eps)
+ * and each selection window keeps its highest-scoring tokens, equal scores by the lower
+ * position.  Windows are [w*window, min((w+1)*window, T)); a window's budget is
+ * ceil(pct * len / 100) for its own length len (budgets refer to the original window, not to
+ * the tokens still active), and never more than its tokens still active, so active sets are
+ * nested.  The score is binary32: each difference, square, addition, the square roots and the
+ * quotient are rounded once, and each sum of squares is taken in pairwise order (the complete
+ * binary tree over the channel index, zero-padded to a power of two), so a score depends on
+ * its row alone: not on the batch, the packing or the launch.  Nothing is read back to the host;
+ * the counts the caller needs follow from T, window and the budgets (flk_select_count).
+ * --------------------------------------------------------------------------------------- */
+
+/* Tokens active after the budgets pct[0..n_budgets) are applied in turn, from a dense loop, to
+ * every window (the n_out of the last of them).  -1 for a malformed argument (T < 0,
+ * window < 1, a pct outside [0, 100], n_budgets < 0 or pct NULL with n_budgets > 0). */
+int32_t flk_select_count(int32_t T, int32_t window, const int32_t* pct, int32_t n_budgets);
+
+/* Workspace of flk_select_rows: 4 * (ceil(T / window) + 1) bytes rounded up to 256; 0 for a
+ * malformed argument. */
+size_t flk_select_workspace_bytes(int32_t T, int32_t window);
+
+/* Loop r's active set from H[r-1] and H[r-2].
+ * h_prev:    device BF16 [T, d], H[r-1] indexed by position; 16-byte aligned.
+ * h_prev2:   device BF16 [T, d], H[r-2] (the rows active at loop r-1 kept from before that loop
+ *            overwrote them; RFC: two aliases of one tensor give no change score); 16-byte
+ *            aligned, not the same buffer as h_prev.
+ * rows_prev: device int32 [n_prev], the positions active at loop r-1, strictly ascending in
+ *            [0, T); NULL when loop r-1 was dense (then n_prev == T) or selected nothing
+ *            (n_prev == 0).
+ * window, pct: the selection window length (>= 1) and loop r's budget in percent (0..100).
+ * eps:       a positive finite binary32.
+ * scores:    device float [n_prev], written with the score of rows_prev[j] (or of position j)
+ *            when 0 < pct < 100; pct 0 and 100 select without scores (the RFC asks that 100 %
+ *            retention and all-off skip the selection work) and leave it untouched.
+ * rows_out:  device int32 [n_out], written: loop r's active positions, ascending (may be NULL
+ *            when n_out == 0).
+ * n_out:     flk_select_count for this loop's budgets; if the windows' budgets add up to
+ *            another number (rows_prev not made by the same budgets), FLK_DEV_COUNT is set and
+ *            no entry at or past n_out is written.
+ * slot:      optional device int32 [T], written: slot[p] = index of p in rows_out, else -1.
+ * workspace: device, at least flk_select_workspace_bytes(T, window) bytes, 4-byte aligned.
+ * dev_status: optional device uint32: FLK_DEV_NONFINITE when a score is not finite (inputs
+ *            whose squares overflow), FLK_DEV_COUNT as above.
+ * Errors: FLK_E_NULL, FLK_E_SHAPE (T < 1, d < 8, d % 8 != 0, d > 16384, T * d >= 2^31,
+ * n_prev outside [0, T] or not 0 or T without rows_prev, window < 1, pct outside [0, 100],
+ * n_out outside [0, n_prev], eps not positive and finite, h_prev == h_prev2), FLK_E_ALIGN,
+ * FLK_E_WORKSPACE, FLK_E_LAUNCH.                                                           */
+flk_status flk_select_rows(const void* h_prev, const void* h_prev2, int32_t T, int32_t d, const int32_t* rows_prev,
+                           int32_t n_prev, int32_t window, int32_t pct, float eps, float* scores,
+                           int32_t* rows_out, int32_t n_out, int32_t* slot, void* workspace,
+                           size_t workspace_bytes, uint32_t* dev_status, void* stream);
+
+/* Classes of a submission's execution rows for flk_partition_rows. */
+enum { FLK_ROW_INACTIVE = 0, FLK_ROW_ACTIVE = 1, FLK_ROW_DECODE = 2 };
+
+/* Gather indices of a mixed submission by stable partition (RFC section 6.2): the decode rows
+ * in their order, then the active prefill rows in their order; inactive prefill rows are left
+ * out (they keep their state).  E.g. [P0, D0, P1, P2, D1, P3] with P1 and P3 active gives
+ * [D0, D1 | P1, P3] and the split offset 2.
+ * cls:     device uint8 [n], FLK_ROW_* per row; another value counts as inactive and sets
+ *          FLK_DEV_CLASS.
+ * gather:  device int32 [n], written: entries [0, counts[1]) are row indices, the rest -1.
+ * scatter: device int32 [n], written: the index of row i in gather, or -1.
+ * counts:  device int32 [2], written: {decode rows (the split offset), gathered rows}.
+ * One workgroup scans the rows, sized for a submission's rows (tens of thousands).
+ * Errors: FLK_E_NULL, FLK_E_SHAPE (n < 0), FLK_E_LAUNCH.                                    */
+flk_status flk_partition_rows(const uint8_t* cls, int32_t n, int32_t* gather, int32_t* scatter, int32_t* counts,
+                              uint32_t* dev_status, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Batched calls.  A serving step encodes or rebuilds many tensors at once -- every layer's K

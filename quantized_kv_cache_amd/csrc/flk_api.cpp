@@ -14,6 +14,7 @@
 #include "../../include/flk.h"
 #include "flk_internal.h"
 #include "flk_readers.h"
+#include "flk_select.h"
 
 namespace {
 
@@ -327,6 +328,62 @@ flk_status flk_sparse_attn_loop(const flk_desc* kd, const flk_desc* vd, int32_t 
   if (!aligned(workspace, 256)) return FLK_E_ALIGN;
   return to_status(flk::launch_sparse_loop(T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, sel, mass, o_ref,
                                            c_ref, out, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+// ---- token selection and row partition -----------------------------------------------------
+
+int32_t flk_select_count(int32_t T, int32_t window, const int32_t* pct, int32_t n_budgets) {
+  if (T < 0 || window < 1 || n_budgets < 0 || (n_budgets > 0 && !pct)) return -1;
+  for (int32_t i = 0; i < n_budgets; ++i)
+    if (pct[i] < 0 || pct[i] > 100) return -1;
+  int64_t total = 0;
+  for (int64_t w0 = 0; w0 < T; w0 += window) {
+    const int64_t len = std::min<int64_t>(window, T - w0);
+    int64_t n = len;
+    for (int32_t i = 0; i < n_budgets; ++i) n = std::min<int64_t>(n, (int64_t(pct[i]) * len + 99) / 100);
+    total += n;
+  }
+  return int32_t(total);
+}
+
+size_t flk_select_workspace_bytes(int32_t T, int32_t window) {
+  if (T < 1 || window < 1) return 0;
+  return flk::select_workspace_bytes(T, window);
+}
+
+flk_status flk_select_rows(const void* h_prev, const void* h_prev2, int32_t T, int32_t d, const int32_t* rows_prev,
+                           int32_t n_prev, int32_t window, int32_t pct, float eps, float* scores,
+                           int32_t* rows_out, int32_t n_out, int32_t* slot, void* workspace,
+                           size_t workspace_bytes, uint32_t* dev_status, void* stream) {
+  if (!h_prev || !h_prev2 || (n_out > 0 && !rows_out)) return FLK_E_NULL;
+  if (T < 1 || d < 8 || d % 8 != 0 || d > 16384 || int64_t(T) * d >= (int64_t(1) << 31)) return FLK_E_SHAPE;
+  if (n_prev < 0 || n_prev > T || (!rows_prev && n_prev != T && n_prev != 0)) return FLK_E_SHAPE;
+  if (window < 1 || pct < 0 || pct > 100 || n_out < 0 || n_out > n_prev) return FLK_E_SHAPE;
+  if (!(eps > 0.0f) || !(eps <= 3.4028234663852886e38f)) return FLK_E_SHAPE;
+  if (h_prev == h_prev2) return FLK_E_SHAPE;
+  if (pct > 0 && pct < 100 && n_prev > 0 && !scores) return FLK_E_NULL;
+  if (!aligned(h_prev, 16) || !aligned(h_prev2, 16) || (rows_prev && !aligned(rows_prev, 4)) ||
+      (scores && !aligned(scores, 4)) || !aligned(rows_out, 4) || (slot && !aligned(slot, 4)) ||
+      (dev_status && !aligned(dev_status, 4)))
+    return FLK_E_ALIGN;
+  if (!workspace || workspace_bytes < flk::select_workspace_bytes(T, window)) return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 4)) return FLK_E_ALIGN;
+  // An empty previous set: the kernels see a list of zero positions, which they never read.
+  if (n_prev == 0) rows_prev = static_cast<const int32_t*>(workspace);
+  return to_status(flk::launch_select_rows(h_prev, h_prev2, T, d, rows_prev, n_prev, window, pct, eps, scores,
+                                           rows_out, n_out, slot, workspace, workspace_bytes, dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_partition_rows(const uint8_t* cls, int32_t n, int32_t* gather, int32_t* scatter, int32_t* counts,
+                              uint32_t* dev_status, void* stream) {
+  if (!counts || (n > 0 && (!cls || !gather || !scatter))) return FLK_E_NULL;
+  if (n < 0) return FLK_E_SHAPE;
+  if ((gather && !aligned(gather, 4)) || (scatter && !aligned(scatter, 4)) || !aligned(counts, 4) ||
+      (dev_status && !aligned(dev_status, 4)))
+    return FLK_E_ALIGN;
+  return to_status(flk::launch_partition_rows(cls, n, gather, scatter, counts, dev_status,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 // ---- appending whole tiles (rolling-tail flush) --------------------------------------------

@@ -131,6 +131,14 @@ def lib() -> ctypes.CDLL:
                                                 sz, P]
         L.flk_sparse_attn_loop.restype = ctypes.c_int
         L.flk_sparse_attn_loop.argtypes = [D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P, P, P, sz, P]
+        L.flk_select_count.restype = i32
+        L.flk_select_count.argtypes = [i32, i32, P, i32]
+        L.flk_select_workspace_bytes.restype = sz
+        L.flk_select_workspace_bytes.argtypes = [i32, i32]
+        L.flk_select_rows.restype = ctypes.c_int
+        L.flk_select_rows.argtypes = [P, P, i32, i32, P, i32, i32, i32, ctypes.c_float, P, P, i32, P, P, sz, P, P]
+        L.flk_partition_rows.restype = ctypes.c_int
+        L.flk_partition_rows.argtypes = [P, i32, P, P, P, P, P]
         L.flk_decode_attn_packed.restype = ctypes.c_int
         L.flk_decode_attn_packed.argtypes = [D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P, sz, P]
         _lib = L
@@ -478,3 +486,67 @@ def sparse_attn_loop(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequen
                                       _ptr(state.mass), _ptr(state.o_ref), _ptr(state.c_ref), _ptr(out),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "flk_sparse_attn_loop")
+
+
+# ----------------------------------------------------------------------------- token selection
+
+ROW_INACTIVE, ROW_ACTIVE, ROW_DECODE = 0, 1, 2
+
+
+def select_count(T: int, window: int, pcts: Sequence[int]) -> int:
+    """Active tokens after the budgets pcts (percent) are applied in turn to a dense loop's
+    selection windows."""
+    arr = (ctypes.c_int32 * max(1, len(pcts)))(*pcts)
+    n = int(lib().flk_select_count(T, window, arr, len(pcts)))
+    if n < 0:
+        raise ValueError(f"select_count: bad arguments T={T} window={window} pcts={list(pcts)}")
+    return n
+
+
+def select_workspace_bytes(T: int, window: int) -> int:
+    return int(lib().flk_select_workspace_bytes(T, window))
+
+
+def select_rows(h_prev: torch.Tensor, h_prev2: torch.Tensor, rows_prev: Optional[torch.Tensor], window: int,
+                pct: int, eps: float, scores: Optional[torch.Tensor], rows_out: torch.Tensor,
+                workspace: torch.Tensor, slot: Optional[torch.Tensor] = None,
+                status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Loop r's active positions (rows_out, ascending) from H[r-1] = h_prev and H[r-2] = h_prev2
+    (BF16 [T, d]) and loop r-1's active positions (None = all); scores gets the change score of
+    each eligible token when 0 < pct < 100; slot (optional, int32 [T]) the index of each position
+    in rows_out or -1."""
+    _need(h_prev, torch.bfloat16, "h_prev")
+    _need(h_prev2, torch.bfloat16, "h_prev2")
+    _need(rows_out, torch.int32, "rows_out")
+    T, d = h_prev.shape
+    if tuple(h_prev2.shape) != (T, d):
+        raise ValueError("h_prev2: shape differs from h_prev")
+    n_prev = T if rows_prev is None else rows_prev.numel()
+    if rows_prev is not None:
+        _need(rows_prev, torch.int32, "rows_prev")
+    if scores is not None:
+        _need(scores, torch.float32, "scores")
+        if scores.numel() < n_prev:
+            raise ValueError("scores: fewer entries than eligible tokens")
+    if slot is not None:
+        _need(slot, torch.int32, "slot")
+        if slot.numel() < T:
+            raise ValueError("slot: fewer than T entries")
+    _check(lib().flk_select_rows(_ptr(h_prev), _ptr(h_prev2), T, d, _ptr(rows_prev), n_prev, window, pct,
+                                 float(eps), _ptr(scores), _ptr(rows_out), rows_out.numel(), _ptr(slot),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(status),
+                                 _stream(stream)), "flk_select_rows")
+
+
+def partition_rows(cls: torch.Tensor, gather: torch.Tensor, scatter: torch.Tensor, counts: torch.Tensor,
+                   status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Decode rows, then active prefill rows, each in order (gather); the position of every row
+    in gather or -1 (scatter); counts = [decode rows, gathered rows]."""
+    _need(cls, torch.uint8, "cls")
+    for t, name in ((gather, "gather"), (scatter, "scatter"), (counts, "counts")):
+        _need(t, torch.int32, name)
+    n = cls.numel()
+    if gather.numel() < n or scatter.numel() < n or counts.numel() < 2:
+        raise ValueError("partition_rows: output buffers too small")
+    _check(lib().flk_partition_rows(_ptr(cls), n, _ptr(gather), _ptr(scatter), _ptr(counts), _ptr(status),
+                                    _stream(stream)), "flk_partition_rows")

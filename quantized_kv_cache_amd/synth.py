@@ -22,6 +22,13 @@ Workloads (sizes fixed by the benchmark definition):
                    per-(head, channel) multiplier exp(U(ln 0.1, ln 10)); V ~ N(0,1); sigma 0.05
   4 batched        64 requests x 24 layers, lengths U{512..8192}, H 16, D 128, budgets as 3
   5 decode_attn    T 131072, Hkv 8, Hq 32, D 128, budgets as 3; q ~ N(0,1) BF16
+
+Hidden states for token selection (hidden_states): H[1] = a per-token magnitude exp(U(ln 0.5,
+ln 2)) times N(0,1) per element; H[r] = H[r-1] + s[t, r] * N(0,1) per element, with a change
+size s[t, r] = exp(U(ln 0.01, ln 1)) per (token, loop), so that change scores spread over two
+decades; every H[r] is rounded to BF16.  The long-prompt selection workload uses T = 32768 and
+a hidden width d = 4096 (32 query heads x 128, the decode workload's attention width),
+windows of 2048 tokens and budgets 50 % then 25 %.
 """
 from __future__ import annotations
 
@@ -33,7 +40,7 @@ import numpy as np
 import torch
 
 K_TENSOR, V_TENSOR = 0, 1
-P_VALUES, P_DELTA, P_SCORES, P_MULT, P_QUERY, P_LENGTHS = range(6)
+P_VALUES, P_DELTA, P_SCORES, P_MULT, P_QUERY, P_LENGTHS, P_HIDDEN, P_HSTEP = range(8)
 
 
 def rng(workload: int, request: int, layer: int, tensor: int, loop: int, purpose: int) -> np.random.Generator:
@@ -157,3 +164,17 @@ def make_query(w: Workload) -> np.ndarray:
 def batched_lengths(n_requests: int = 64, lo: int = 512, hi: int = 8192) -> np.ndarray:
     g = rng(4, 0, 0, 0, 0, P_LENGTHS)
     return g.integers(lo, hi + 1, size=n_requests).astype(np.int64)
+
+
+def hidden_states(T: int, d: int, n_states: int, workload: int = 3, request: int = 0, layer: int = 0) -> List[np.ndarray]:
+    """BF16 bit patterns [T, d] of H[1] .. H[n_states] (recipe in the module docstring)."""
+    g = rng(workload, request, layer, 0, 0, P_HIDDEN)
+    mag = np.exp(g.uniform(math.log(0.5), math.log(2.0), (T, 1))).astype(np.float32)
+    y = g.standard_normal((T, d), dtype=np.float32) * mag
+    out = [to_bf16_bits(y)]
+    for r in range(1, n_states):
+        gs = rng(workload, request, layer, 0, r, P_HSTEP)
+        size = np.exp(gs.uniform(math.log(0.01), 0.0, (T, 1))).astype(np.float32)
+        y = y + gs.standard_normal((T, d), dtype=np.float32) * size
+        out.append(to_bf16_bits(y))
+    return out

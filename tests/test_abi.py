@@ -345,3 +345,61 @@ def test_sparse_attention_validation():
     assert loop(sel=None) == 1
     assert loop(wb=64) == 6
     assert loop(c=MIS) == 3
+
+
+def test_select_count_matches_oracle():
+    from oracle import selection as osel
+    for T, W, p in [(32768, 2048, [50]), (32768, 2048, [50, 25]), (1000, 7, [33, 10]), (20, 30, [50, 50]),
+                    (33, 1, [100, 0]), (5, 8, []), (0, 4, [50])]:
+        assert flk.select_count(T, W, p) == osel.select_count(T, W, p)
+    L = flk.lib()
+    arr = (ctypes.c_int32 * 1)(101)
+    assert L.flk_select_count(10, 4, arr, 1) == -1
+    assert L.flk_select_count(10, 0, arr, 0) == -1
+    assert L.flk_select_count(10, 4, None, 1) == -1
+    assert flk.select_workspace_bytes(32768, 2048) == 256
+    assert flk.select_workspace_bytes(100000, 1) == (4 * 100001 + 255) // 256 * 256
+    assert flk.select_workspace_bytes(0, 8) == 0
+
+
+def test_select_rows_validation():
+    L = flk.lib()
+    T, d, W = 100, 64, 16
+    ws = flk.select_workspace_bytes(T, W)
+    H2 = ctypes.c_void_p((1 << 21))
+
+    def call(h1=FAKE, h2=H2, T=T, d=d, rows=None, n_prev=T, W=W, pct=50, eps=1e-6, sc=FAKE, out=FAKE, n_out=56,
+             w=FAKE, wb=ws):
+        return L.flk_select_rows(h1, h2, T, d, rows, n_prev, W, pct, eps, sc, out, n_out, None, w, wb, None, None)
+    assert call(h1=None) == 1
+    assert call(out=None) == 1
+    assert call(sc=None) == 1                            # 0 < pct < 100 writes scores
+    assert call(T=0) == 2
+    assert call(d=12) == 2
+    assert call(d=16392) == 2
+    assert call(n_prev=50) == 2                          # dense needs n_prev == T
+    assert call(rows=FAKE, n_prev=T + 1) == 2
+    assert call(W=0) == 2
+    assert call(pct=101) == 2
+    assert call(pct=-1) == 2
+    assert call(n_out=T + 1) == 2
+    assert call(eps=0.0) == 2
+    assert call(eps=float("inf")) == 2
+    assert call(h2=FAKE) == 2                            # the two hidden states alias
+    assert call(h1=ctypes.c_void_p((1 << 20) + 8)) == 3
+    assert call(rows=ctypes.c_void_p((1 << 20) + 2), n_prev=50, n_out=25) == 3
+    assert call(wb=ws - 4) == 6
+    assert call(w=None) == 6
+    assert call(w=ctypes.c_void_p((1 << 20) + 2)) == 3
+
+
+def test_partition_rows_validation():
+    L = flk.lib()
+
+    def call(cls=FAKE, n=10, g=FAKE, s=FAKE, c=FAKE):
+        return L.flk_partition_rows(cls, n, g, s, c, None, None)
+    assert call(c=None) == 1
+    assert call(cls=None) == 1
+    assert call(g=None) == 1
+    assert call(n=-1) == 2
+    assert call(g=ctypes.c_void_p((1 << 20) + 2)) == 3
