@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kCountThreads) void window_count_kernel(const int32
 // by two searches (block_lower_bound probes with the first 256 threads of the block).
 // ---------------------------------------------------------------------------------------
 constexpr int kWinThreads = 1024;
+constexpr int kCacheKeys = 4;                // keys per thread kept in registers
 
 __device__ __forceinline__ uint32_t sel_key(float s) {
   const uint32_t u = __float_as_uint(s);
@@ -310,6 +311,17 @@ __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* _
   }
   if (k <= 0) return;
   const bool all = k >= hi - lo;
+  // A run of at most kCacheKeys * kWinThreads keys is read once into registers (key r of a
+  // thread is element lo + r * kWinThreads + tid); a longer one is re-read from memory.
+  const bool cached = hi - lo <= kCacheKeys * kWinThreads;
+  uint32_t kreg[kCacheKeys];
+  if (cached && !all) {
+#pragma unroll
+    for (int r = 0; r < kCacheKeys; ++r) {
+      const int32_t i = lo + r * kWinThreads + tid;
+      kreg[r] = i < hi ? sel_key(scores[i]) : 0u;
+    }
+  }
   uint32_t tau = 0, need = 0;
   if (!all) {
     uint32_t prefix = 0, pmask = 0;
@@ -319,9 +331,16 @@ __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* _
       const uint32_t nb = pass == 2 ? 1024u : 2048u;
       for (int b = tid; b < 2048; b += kWinThreads) hist[b] = 0;
       __syncthreads();
-      for (int32_t i = lo + tid; i < hi; i += kWinThreads) {
-        const uint32_t key = sel_key(scores[i]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+      if (cached) {
+#pragma unroll
+        for (int r = 0; r < kCacheKeys; ++r)
+          if (lo + r * kWinThreads + tid < hi && (kreg[r] & pmask) == prefix)
+            atomicAdd(&hist[(kreg[r] >> shift) & (nb - 1)], 1u);
+      } else {
+        for (int32_t i = lo + tid; i < hi; i += kWinThreads) {
+          const uint32_t key = sel_key(scores[i]);
+          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+        }
       }
       __syncthreads();
       if (wave == 0) {                                 // lane l: digits [nb - 32(l+1), nb - 32l)
@@ -352,22 +371,11 @@ __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* _
     }
     tau = prefix;
   }
-  // Position-ordered pass: element i of the run is taken if all, or its key is above tau, or it
-  // is among the first `need` keys equal to tau.
+  // Position-ordered pass, a block's width of elements per step: element i of the run is taken
+  // if all, or its key is above tau, or it is among the first `need` keys equal to tau.
   const uint64_t below = (uint64_t(1) << lane) - 1;
   int32_t taken = 0, eq_seen = 0;
-  for (int32_t base = lo; base < hi; base += kWinThreads) {
-    const int32_t i = base + tid;
-    bool gt = false, eq = false;
-    if (i < hi) {
-      if (all) {
-        gt = true;
-      } else {
-        const uint32_t key = sel_key(scores[i]);
-        gt = key > tau;
-        eq = key == tau;
-      }
-    }
+  auto step = [&](int32_t i, bool gt, bool eq) {
     const uint64_t bg = __ballot(gt), be = __ballot(eq);
     if (lane == 0) { s_wave[wave][0] = __builtin_popcountll(bg); s_wave[wave][1] = __builtin_popcountll(be); }
     __syncthreads();
@@ -379,8 +387,7 @@ __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* _
       e_all += s_wave[v][1];
     }
     const int32_t e_rank = eq_seen + e_before + __builtin_popcountll(be & below);
-    const bool take = gt || (eq && e_rank < int32_t(need));
-    if (take) {
+    if (gt || (eq && e_rank < int32_t(need))) {
       // selected before this element in the run: those of earlier steps, the greater keys
       // before it in this step, and the equal keys before it that are among the first `need`
       const int32_t gt_before = g_before + __builtin_popcountll(bg & below);
@@ -394,6 +401,30 @@ __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* _
     taken += g_all + min(eq_seen + e_all, int32_t(need)) - min(eq_seen, int32_t(need));
     eq_seen += e_all;
     __syncthreads();
+  };
+  if (cached && !all) {
+#pragma unroll
+    for (int r = 0; r < kCacheKeys; ++r) {
+      const int32_t base = lo + r * kWinThreads;
+      if (base >= hi) break;                           // uniform over the block
+      const bool in = base + tid < hi;
+      step(base + tid, in && kreg[r] > tau, in && kreg[r] == tau);
+    }
+  } else {
+    for (int32_t base = lo; base < hi; base += kWinThreads) {
+      const int32_t i = base + tid;
+      bool gt = false, eq = false;
+      if (i < hi) {
+        if (all) {
+          gt = true;
+        } else {
+          const uint32_t key = sel_key(scores[i]);
+          gt = key > tau;
+          eq = key == tau;
+        }
+      }
+      step(i, gt, eq);
+    }
   }
 }
 
