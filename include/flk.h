@@ -92,9 +92,27 @@ typedef enum flk_status {
 /* Which tensor a stream encodes; it selects the group axis and is recorded in the
  * descriptor (the PR #166 review asks for format, axis and group size in the descriptor). */
 enum { FLK_KIND_K = 0, FLK_KIND_V = 1 };
-enum { FLK_FMT_INT4_AFFINE = 1 };
-enum { FLK_PARAM_FP16_MIN_SCALE = 1 };
+enum { FLK_FMT_INT4_AFFINE = 1, FLK_FMT_NVFP4 = 2 };
+enum { FLK_PARAM_FP16_MIN_SCALE = 1, FLK_PARAM_E4M3_BLOCK_F32_STREAM = 2 };
 enum { FLK_NIBBLE_LOW_EVEN = 1 };
+
+/* The NVFP4 variant (PR #166 review, item 2: E2M1 codes, one E4M3 scale per 16 elements and
+ * one FP32 scale per tensor, about 4.5 bits per element, symmetric).  Descriptor: format
+ * FLK_FMT_NVFP4, group FLK_FP4_BLOCK, param_dtype FLK_PARAM_E4M3_BLOCK_F32_STREAM,
+ * k_grouping FLK_KGROUP_ROWS, D % 16 == 0.  Blocks run along the 16 consecutive channels of one
+ * (row, head) for K and V alike.  Per stream of n rows:
+ *   codes   [n][H][D/2] bytes, low nibble = even channel; a nibble is sign (bit 3) and the
+ *           E2M1 magnitude 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7)
+ *   params  a 16-byte header {s_g, amax, 0, 0} (binary32) then the E4M3 block scales
+ *           [n][H][D/16] bytes (flk_params_bytes = 16 + n*H*D/16)
+ * The stream scale is s_g = RN32(amax / 2688) over the magnitudes the stream encodes (X for a
+ * base loop, the BF16 residual for a residual loop), or 1 when amax is 0.  A block's scale is
+ * E4M3(RN32(amax_b / RN32(6 * s_g))), nearest-even and saturated at 448, and its binary32 value
+ * bs = RN32(e4m3 * s_g).  Each code is the E2M1 value nearest (ties to even) to RN32(x / bs),
+ * saturated at 6; a value that rounds to zero keeps its sign; a block with bs == 0 has codes
+ * +0.  Decoding gives RN32(e2m1 * bs), rounded to BF16.  The residual chain is the INT4 one:
+ * residuals are rounded to BF16 before encoding and added in binary32, rounded to BF16. */
+#define FLK_FP4_BLOCK 16
 
 /* Who owns a K group (the PR #166 review, item 3 "Group ownership vs 16-token pages": K
  * groups that follow compact-row order can put rows of distant positions, on different
@@ -120,10 +138,10 @@ enum { FLK_KGROUP_ROWS = 0, FLK_KGROUP_TILE = 1 };
  * depth representation travel with the data).  Fill with flk_desc_init(). */
 typedef struct flk_desc {
     uint16_t abi_version;   /* FLK_ABI_VERSION                                             */
-    uint8_t format;         /* FLK_FMT_INT4_AFFINE                                         */
+    uint8_t format;         /* FLK_FMT_INT4_AFFINE or FLK_FMT_NVFP4                        */
     uint8_t kind;           /* FLK_KIND_K or FLK_KIND_V                                    */
-    uint16_t group;         /* FLK_GROUP (64); no other size is accepted                   */
-    uint8_t param_dtype;    /* FLK_PARAM_FP16_MIN_SCALE                                    */
+    uint16_t group;         /* FLK_GROUP (64) for INT4, FLK_FP4_BLOCK (16) for NVFP4       */
+    uint8_t param_dtype;    /* FLK_PARAM_FP16_MIN_SCALE (INT4), FLK_PARAM_E4M3_BLOCK_F32_STREAM */
     uint8_t nibble_order;   /* FLK_NIBBLE_LOW_EVEN                                         */
     int32_t n_heads;        /* H >= 1                                                      */
     int32_t head_dim;       /* D: 8 <= D <= FLK_MAX_HEAD_DIM, D % 8 == 0                   */
@@ -149,6 +167,11 @@ typedef struct flk_stream {
  * (set k_grouping afterwards to choose tile groups). */
 void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
+/* Fill a descriptor for NVFP4 streams.  NVFP4 descriptors are accepted by flk_desc_check, the
+ * size functions, flk_encode_base, flk_encode_residual, flk_reconstruct and
+ * flk_reconstruct_mixed; every other entry point answers FLK_E_UNSUPPORTED. */
+void flk_desc_init_nvfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
+
 /* FLK_OK if the descriptor is well formed, else FLK_E_NULL / FLK_E_DESC / FLK_E_SHAPE. */
 flk_status flk_desc_check(const flk_desc* d);
 
@@ -156,7 +179,8 @@ flk_status flk_desc_check(const flk_desc* d);
  * payload, quantization parameters and maps).  0 for a malformed descriptor or n < 0.   */
 size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows);   /* n*H*D/2                    */
 size_t flk_params_bytes(const flk_desc* d, int32_t n_rows, int32_t T); /* 4 * groups; T is
-                                       the stream's positions (read for tile-grouped K only) */
+                                       the stream's positions (read for tile-grouped K only);
+                                       NVFP4: 16 + n*H*D/16                                 */
 size_t flk_rows_bytes(int32_t n_rows, int sparse);            /* 4*n if sparse, else 0      */
 size_t flk_tile_index_bytes(int32_t T);                       /* 4*(ceil(T/64) + 1)         */
 /* Everything one stream stores: codes + params + rows + tile index (sparse streams), with
@@ -218,6 +242,14 @@ flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int3
  * Errors: FLK_E_NULL, FLK_E_DESC, FLK_E_SHAPE, FLK_E_ALIGN, FLK_E_LAUNCH.                */
 flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain,
                            int32_t n_loops, void* out, void* stream);
+
+/* flk_reconstruct for a chain whose base (chain[0]) is described by base_desc and whose
+ * residual loops by resid_desc: an INT4 base with NVFP4 residuals (the PR #166 review's
+ * "INT4 base plus NVFP4 residuals"), NVFP4 throughout, or INT4 throughout.  Both descriptors
+ * must agree on kind, H and D.  An NVFP4 base with INT4 residuals is FLK_E_UNSUPPORTED.
+ * Errors: those of flk_reconstruct, plus FLK_E_DESC when the descriptors disagree. */
+flk_status flk_reconstruct_mixed(const flk_desc* base_desc, const flk_desc* resid_desc, int32_t T,
+                                 const flk_stream* chain, int32_t n_loops, void* out, void* stream);
 
 /* Single-token decode attention read directly from the packed chains (RFC section 3.3:
  * optimized readers consume packed base/residual tiles during QK/PV instead of building a

@@ -14,6 +14,7 @@
 #include "../../include/flk.h"
 #include "flk_internal.h"
 #include "flk_readers.h"
+#include "flk_fp4.h"
 #include "flk_select.h"
 
 namespace {
@@ -63,6 +64,16 @@ bool rows_fit(const flk_desc* d, int64_t n) {
 
 flk_status to_status(hipError_t e) { return e == hipSuccess ? FLK_OK : FLK_E_LAUNCH; }
 
+bool is_fp4(const flk_desc* d) { return d->format == FLK_FMT_NVFP4; }
+
+// The check of the entry points that implement INT4 streams only: a well-formed NVFP4
+// descriptor is a valid request they do not implement.
+flk_status int4_desc(const flk_desc* d) {
+  const flk_status st = flk_desc_check(d);
+  if (st != FLK_OK) return st;
+  return is_fp4(d) ? FLK_E_UNSUPPORTED : FLK_OK;
+}
+
 flk_status load_chain(const flk_desc* d, int32_t T, const flk_stream* chain, int32_t n_loops,
                       flk::ChainArgs* out) {
   if (!chain) return FLK_E_NULL;
@@ -110,16 +121,27 @@ void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim) {
   d->k_grouping = FLK_KGROUP_ROWS;
 }
 
+void flk_desc_init_nvfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim) {
+  flk_desc_init(d, kind, n_heads, head_dim);
+  if (!d) return;
+  d->format = FLK_FMT_NVFP4;
+  d->group = FLK_FP4_BLOCK;
+  d->param_dtype = FLK_PARAM_E4M3_BLOCK_F32_STREAM;
+}
+
 flk_status flk_desc_check(const flk_desc* d) {
   if (!d) return FLK_E_NULL;
-  if (d->abi_version != FLK_ABI_VERSION || d->format != FLK_FMT_INT4_AFFINE ||
-      (d->kind != FLK_KIND_K && d->kind != FLK_KIND_V) || d->group != FLK_GROUP ||
-      d->param_dtype != FLK_PARAM_FP16_MIN_SCALE || d->nibble_order != FLK_NIBBLE_LOW_EVEN ||
-      (d->k_grouping != FLK_KGROUP_ROWS && d->k_grouping != FLK_KGROUP_TILE) || d->reserved[0] != 0 ||
-      d->reserved[1] != 0 || d->reserved[2] != 0)
+  const bool int4 = d->format == FLK_FMT_INT4_AFFINE && d->group == FLK_GROUP &&
+                    d->param_dtype == FLK_PARAM_FP16_MIN_SCALE &&
+                    (d->k_grouping == FLK_KGROUP_ROWS || d->k_grouping == FLK_KGROUP_TILE);
+  const bool fp4 = d->format == FLK_FMT_NVFP4 && d->group == FLK_FP4_BLOCK &&
+                   d->param_dtype == FLK_PARAM_E4M3_BLOCK_F32_STREAM && d->k_grouping == FLK_KGROUP_ROWS;
+  if (d->abi_version != FLK_ABI_VERSION || !(int4 || fp4) || (d->kind != FLK_KIND_K && d->kind != FLK_KIND_V) ||
+      d->nibble_order != FLK_NIBBLE_LOW_EVEN || d->reserved[0] != 0 || d->reserved[1] != 0 || d->reserved[2] != 0)
     return FLK_E_DESC;
   if (d->n_heads < 1 || d->head_dim < 8 || d->head_dim > FLK_MAX_HEAD_DIM || d->head_dim % 8 != 0)
     return FLK_E_SHAPE;
+  if (fp4 && d->head_dim % FLK_FP4_BLOCK != 0) return FLK_E_SHAPE;
   if (int64_t(d->n_heads) * d->head_dim > (int64_t(1) << 20)) return FLK_E_SHAPE;
   return FLK_OK;
 }
@@ -131,6 +153,8 @@ size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows) {
 
 size_t flk_params_bytes(const flk_desc* d, int32_t n_rows, int32_t T) {
   if (flk_desc_check(d) != FLK_OK || n_rows < 0) return 0;
+  if (is_fp4(d))                                  // header, then one E4M3 byte per 16 elements
+    return 16 + size_t(n_rows) * size_t(d->n_heads) * size_t(d->head_dim) / FLK_FP4_BLOCK;
   return 4 * n_groups(d, n_rows, T);
 }
 
@@ -156,7 +180,7 @@ int32_t flk_rolling_prefix(int32_t n_tokens) {
 }
 
 size_t flk_attn_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads) {
-  if (flk_desc_check(k_desc) != FLK_OK || T < 0 || n_q_heads < 1) return 0;
+  if (int4_desc(k_desc) != FLK_OK || T < 0 || n_q_heads < 1) return 0;
   return flk::attn_workspace_bytes(T, k_desc->n_heads, n_q_heads);
 }
 
@@ -185,6 +209,9 @@ flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t*
   st = check_stream_ptrs(codes, params);
   if (st != FLK_OK) return st;
   if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
+  if (is_fp4(d))
+    return to_status(flk::launch_fp4_encode(false, x, nullptr, T, T, d->n_heads, d->head_dim, recon, codes, params,
+                                            nullptr, dev_status, static_cast<hipStream_t>(stream)));
   return to_status(flk::launch_encode(d->kind, false,
                                       enc_args(d, x, nullptr, T, T, recon, codes, params, nullptr, dev_status),
                                       d->n_heads, d->head_dim, static_cast<hipStream_t>(stream)));
@@ -207,6 +234,10 @@ flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int3
   if (rows && !tile_start) return FLK_E_NULL;
   if (!aligned(x_rows, 16) || (rows && (!aligned(rows, 4) || !aligned(tile_start, 4))))
     return FLK_E_ALIGN;
+  if (is_fp4(d))
+    return to_status(flk::launch_fp4_encode(true, x_rows, rows, n_rows, T, d->n_heads, d->head_dim, recon, codes,
+                                            params, rows ? tile_start : nullptr, dev_status,
+                                            static_cast<hipStream_t>(stream)));
   return to_status(flk::launch_encode(d->kind, true,
                                       enc_args(d, x_rows, rows, n_rows, T, recon, codes, params, tile_start,
                                                dev_status),
@@ -223,8 +254,32 @@ flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain
   st = load_chain(d, T, chain, n_loops, &ca);
   if (st != FLK_OK) return st;
   if (!aligned(out, 16)) return FLK_E_ALIGN;
+  if (is_fp4(d))
+    return to_status(flk::launch_fp4_reconstruct(ca, true, d->kind, T, d->n_heads, d->head_dim, out,
+                                                 static_cast<hipStream_t>(stream)));
   return to_status(flk::launch_reconstruct(d->kind, T, d->n_heads, d->head_dim, ca, out,
                                            static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_reconstruct_mixed(const flk_desc* bd, const flk_desc* rd, int32_t T, const flk_stream* chain,
+                                 int32_t n_loops, void* out, void* stream) {
+  flk_status st = flk_desc_check(bd);
+  if (st != FLK_OK) return st;
+  if ((st = flk_desc_check(rd)) != FLK_OK) return st;
+  if (bd->kind != rd->kind || bd->n_heads != rd->n_heads || bd->head_dim != rd->head_dim) return FLK_E_DESC;
+  if (!is_fp4(rd)) {
+    if (is_fp4(bd)) return FLK_E_UNSUPPORTED;                 // NVFP4 base, INT4 residuals
+    return flk_reconstruct(bd, T, chain, n_loops, out, stream);
+  }
+  if (!out) return FLK_E_NULL;
+  if (T < 1 || !rows_fit(bd, T)) return FLK_E_SHAPE;
+  if (rd->head_dim % FLK_FP4_BLOCK != 0) return FLK_E_SHAPE;
+  flk::ChainArgs ca;
+  st = load_chain(bd, T, chain, n_loops, &ca);
+  if (st != FLK_OK) return st;
+  if (!aligned(out, 16)) return FLK_E_ALIGN;
+  return to_status(flk::launch_fp4_reconstruct(ca, is_fp4(bd), bd->kind, T, bd->n_heads, bd->head_dim, out,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
@@ -232,9 +287,9 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
                                   const flk_stream* v_chain, int32_t n_loops, float softmax_scale,
                                   void* out, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  flk_status st = flk_desc_check(kd);
+  flk_status st = int4_desc(kd);
   if (st != FLK_OK) return st;
-  st = flk_desc_check(vd);
+  st = int4_desc(vd);
   if (st != FLK_OK) return st;
   if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
   if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
@@ -265,9 +320,9 @@ flk_status check_sparse(const flk_desc* kd, const flk_desc* vd, int32_t T, const
                         const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops, int32_t k,
                         const void* out, const int32_t* sel, const float* mass, const float* o_ref,
                         const float* c_ref, flk::ChainArgs* kc, flk::ChainArgs* vc) {
-  flk_status st = flk_desc_check(kd);
+  flk_status st = int4_desc(kd);
   if (st != FLK_OK) return st;
-  st = flk_desc_check(vd);
+  st = int4_desc(vd);
   if (st != FLK_OK) return st;
   if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
   if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
@@ -289,7 +344,7 @@ flk_status check_sparse(const flk_desc* kd, const flk_desc* vd, int32_t T, const
 }  // namespace
 
 size_t flk_sparse_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q_heads, int32_t k, int32_t n_loops) {
-  if (flk_desc_check(k_desc) != FLK_OK || T < 1 || n_q_heads < 1 || k < 1 || k > T || n_loops < 1 ||
+  if (int4_desc(k_desc) != FLK_OK || T < 1 || n_q_heads < 1 || k < 1 || k > T || n_loops < 1 ||
       n_loops > FLK_MAX_LOOPS)
     return 0;
   return flk::sparse_workspace_bytes(T, k_desc->n_heads, n_q_heads, k, n_loops);
@@ -438,7 +493,7 @@ hipError_t fill_empty_window(const flk_desc* d, const flk::EncArgs& a, hipStream
 
 flk_status flk_append_base(const flk_desc* d, const void* x, int32_t p0, int32_t n_pos, uint8_t* codes,
                            uint32_t* params, void* recon, uint32_t* dev_status, void* stream) {
-  flk_status st = flk_desc_check(d);
+  flk_status st = int4_desc(d);
   if (st != FLK_OK) return st;
   if (!x) return FLK_E_NULL;
   if (dev_status && !aligned(dev_status, 4)) return FLK_E_ALIGN;
@@ -454,7 +509,7 @@ flk_status flk_append_base(const flk_desc* d, const void* x, int32_t p0, int32_t
 flk_status flk_append_residual(const flk_desc* d, const void* x_rows, const int32_t* rows, int32_t n_rows,
                                int32_t p0, int32_t n_pos, int32_t rows_before, void* recon, uint8_t* codes,
                                uint32_t* params, int32_t* tile_start, uint32_t* dev_status, void* stream) {
-  flk_status st = flk_desc_check(d);
+  flk_status st = int4_desc(d);
   if (st != FLK_OK) return st;
   if (dev_status && !aligned(dev_status, 4)) return FLK_E_ALIGN;
   const flk_append_unit u{x_rows, rows, recon, codes, params, tile_start, n_rows, p0, n_pos, rows_before, d->kind, 0};
@@ -473,9 +528,9 @@ flk_status flk_decode_attn_rolling(const flk_desc* kd, const flk_desc* vd, int32
                                    int32_t n_loops, const void* k_tail, const void* v_tail, int32_t tail_len,
                                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  flk_status st = flk_desc_check(kd);
+  flk_status st = int4_desc(kd);
   if (st != FLK_OK) return st;
-  st = flk_desc_check(vd);
+  st = int4_desc(vd);
   if (st != FLK_OK) return st;
   if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
   if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
@@ -511,12 +566,12 @@ const flk_desc* unit_desc(const flk_desc* kd, const flk_desc* vd, int32_t kind) 
 
 flk_status check_pair(const flk_desc* kd, const flk_desc* vd) {
   if (kd) {
-    const flk_status st = flk_desc_check(kd);
+    const flk_status st = int4_desc(kd);
     if (st != FLK_OK) return st;
     if (kd->kind != FLK_KIND_K) return FLK_E_DESC;
   }
   if (vd) {
-    const flk_status st = flk_desc_check(vd);
+    const flk_status st = int4_desc(vd);
     if (st != FLK_OK) return st;
     if (vd->kind != FLK_KIND_V) return FLK_E_DESC;
   }

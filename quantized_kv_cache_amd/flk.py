@@ -131,6 +131,10 @@ def lib() -> ctypes.CDLL:
                                                 sz, P]
         L.flk_sparse_attn_loop.restype = ctypes.c_int
         L.flk_sparse_attn_loop.argtypes = [D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P, P, P, sz, P]
+        L.flk_desc_init_nvfp4.restype = None
+        L.flk_desc_init_nvfp4.argtypes = [D, ctypes.c_int, i32, i32]
+        L.flk_reconstruct_mixed.restype = ctypes.c_int
+        L.flk_reconstruct_mixed.argtypes = [D, D, i32, S, i32, P, P]
         L.flk_select_count.restype = i32
         L.flk_select_count.argtypes = [i32, i32, P, i32]
         L.flk_select_workspace_bytes.restype = sz
@@ -145,9 +149,13 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def desc(kind: int, H: int, D: int, k_tiles: bool = False) -> Desc:
-    """k_tiles: K groups per 64-position tile (page-local) instead of per 64 compact rows."""
+def desc(kind: int, H: int, D: int, k_tiles: bool = False, nvfp4: bool = False) -> Desc:
+    """k_tiles: K groups per 64-position tile (page-local) instead of per 64 compact rows;
+    nvfp4: the NVFP4 format (E2M1 codes, E4M3 scales per 16 channels, one FP32 stream scale)."""
     d = Desc()
+    if nvfp4:
+        lib().flk_desc_init_nvfp4(ctypes.byref(d), kind, H, D)
+        return d
     lib().flk_desc_init(ctypes.byref(d), kind, H, D)
     d.k_grouping = KGROUP_TILE if k_tiles else KGROUP_ROWS
     return d
@@ -179,12 +187,13 @@ def codes_bytes(kind: int, H: int, D: int, n: int) -> int:
     return int(lib().flk_codes_bytes(ctypes.byref(desc(kind, H, D)), n))
 
 
-def params_bytes(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = False) -> int:
-    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D, k_tiles)), n, T))
+def params_bytes(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = False, nvfp4: bool = False) -> int:
+    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D, k_tiles, nvfp4)), n, T))
 
 
-def stream_bytes(kind: int, H: int, D: int, n: int, T: int, sparse: bool, k_tiles: bool = False) -> int:
-    return int(lib().flk_stream_bytes(ctypes.byref(desc(kind, H, D, k_tiles)), n, T, 1 if sparse else 0))
+def stream_bytes(kind: int, H: int, D: int, n: int, T: int, sparse: bool, k_tiles: bool = False,
+                 nvfp4: bool = False) -> int:
+    return int(lib().flk_stream_bytes(ctypes.byref(desc(kind, H, D, k_tiles, nvfp4)), n, T, 1 if sparse else 0))
 
 
 def rolling_prefix(n_tokens: int) -> int:
@@ -220,22 +229,29 @@ class Packed:
     params: torch.Tensor
     tile_start: Optional[torch.Tensor] = None
     k_tiles: bool = False
+    nvfp4: bool = False
 
     @staticmethod
     def empty(kind: int, H: int, D: int, n: int, rows: Optional[torch.Tensor] = None, T: int = 0,
               tile_start: Optional[torch.Tensor] = None, device="cuda", k_tiles: bool = False,
-              compact: Optional[bool] = None) -> "Packed":
-        """compact: the stream has a tile index (default: when rows is given)."""
+              compact: Optional[bool] = None, nvfp4: bool = False) -> "Packed":
+        """compact: the stream has a tile index (default: when rows is given).  nvfp4: an NVFP4
+        stream (params: a 16-byte header, then one E4M3 byte per 16 elements)."""
         if k_tiles and kind == K and T < 1:
             raise ValueError("tile-grouped K needs T to size its params")
+        if nvfp4 and k_tiles:
+            raise ValueError("NVFP4 blocks run along channels; there are no tile groups")
         compact = rows is not None if compact is None else compact
         codes = torch.empty((n, H, D // 2), dtype=torch.uint8, device=device)
-        params = torch.empty(params_shape(kind, H, D, n, T, k_tiles), dtype=torch.int32, device=device)
+        if nvfp4:
+            params = torch.empty((params_bytes(kind, H, D, n, nvfp4=True) + 3) // 4, dtype=torch.int32, device=device)
+        else:
+            params = torch.empty(params_shape(kind, H, D, n, T, k_tiles), dtype=torch.int32, device=device)
         if compact and tile_start is None:
             if T < 1:
                 raise ValueError("a compact loop needs T to size its tile index")
             tile_start = torch.empty(tile_index_bytes(T) // 4, dtype=torch.int32, device=device)
-        return Packed(n, rows, codes, params, tile_start if compact else None, k_tiles and kind == K)
+        return Packed(n, rows, codes, params, tile_start if compact else None, k_tiles and kind == K, nvfp4)
 
     def c(self) -> StreamC:
         return StreamC(self.n_rows, 0, None if self.rows is None else self.rows.data_ptr(),
@@ -253,7 +269,7 @@ def encode_base(kind: int, x: torch.Tensor, out: Packed, recon: torch.Tensor,
     _need(x, torch.bfloat16, "x")
     _need(recon, torch.bfloat16, "recon")
     T, H, D = x.shape
-    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D, out.k_tiles)), _ptr(x), T, _ptr(out.codes),
+    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D, out.k_tiles, out.nvfp4)), _ptr(x), T, _ptr(out.codes),
                                  _ptr(out.params), _ptr(recon), _ptr(status), _stream(stream)),
            "flk_encode_base")
 
@@ -266,7 +282,7 @@ def encode_residual(kind: int, x_rows: torch.Tensor, rows: Optional[torch.Tensor
         _need(rows, torch.int32, "rows")
     n, H, D = x_rows.shape
     T = recon.shape[0]
-    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D, out.k_tiles)), _ptr(x_rows), _ptr(rows), n, T,
+    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D, out.k_tiles, out.nvfp4)), _ptr(x_rows), _ptr(rows), n, T,
                                      _ptr(recon), _ptr(out.codes), _ptr(out.params), _ptr(out.tile_start),
                                      _ptr(status), _stream(stream)),
            "flk_encode_residual")
@@ -278,11 +294,22 @@ def _chain(chain: Sequence[Packed]):
 
 
 def reconstruct(kind: int, chain: Sequence[Packed], out: torch.Tensor, stream=None) -> None:
+    """X_hat of the chain; an INT4 or NVFP4 base, INT4 or NVFP4 residual loops (one format for
+    all of them)."""
     _need(out, torch.bfloat16, "out")
     T, H, D = out.shape
     arr = _chain(chain)
-    _check(lib().flk_reconstruct(ctypes.byref(desc(kind, H, D, chain[0].k_tiles)), T, arr, len(chain), _ptr(out),
-                                 _stream(stream)), "flk_reconstruct")
+    resid_fp4 = {p.nvfp4 for p in chain[1:]}
+    if len(resid_fp4) > 1:
+        raise ValueError("the residual loops of one chain share one format")
+    rf = resid_fp4.pop() if resid_fp4 else chain[0].nvfp4
+    if not chain[0].nvfp4 and not rf:
+        _check(lib().flk_reconstruct(ctypes.byref(desc(kind, H, D, chain[0].k_tiles)), T, arr, len(chain), _ptr(out),
+                                     _stream(stream)), "flk_reconstruct")
+        return
+    _check(lib().flk_reconstruct_mixed(ctypes.byref(desc(kind, H, D, chain[0].k_tiles, chain[0].nvfp4)),
+                                       ctypes.byref(desc(kind, H, D, nvfp4=rf)), T, arr, len(chain), _ptr(out),
+                                       _stream(stream)), "flk_reconstruct_mixed")
 
 
 def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int,

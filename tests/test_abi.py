@@ -403,3 +403,50 @@ def test_partition_rows_validation():
     assert call(g=None) == 1
     assert call(n=-1) == 2
     assert call(g=ctypes.c_void_p((1 << 20) + 2)) == 3
+
+
+def test_nvfp4_descriptor_sizes_and_unsupported_entry_points():
+    L = flk.lib()
+    d = flk.desc(flk.K, 8, 128, nvfp4=True)
+    assert L.flk_desc_check(ctypes.byref(d)) == 0
+    assert (d.format, d.group, d.param_dtype, d.k_grouping) == (2, 16, 2, 0)
+    assert flk.codes_bytes(flk.K, 8, 128, 100) == 100 * 8 * 64
+    assert flk.params_bytes(flk.K, 8, 128, 100, nvfp4=True) == 16 + 100 * 8 * 8
+    assert flk.stream_bytes(flk.V, 8, 128, 100, 1000, True, nvfp4=True) == \
+        100 * 8 * 64 + 16 + 100 * 64 + 400 + flk.tile_index_bytes(1000)
+    bad = flk.desc(flk.K, 8, 120, nvfp4=True)           # D % 16 != 0
+    assert L.flk_desc_check(ctypes.byref(bad)) == 2
+    tiles = flk.desc(flk.K, 8, 128, nvfp4=True)
+    tiles.k_grouping = 1                                  # NVFP4 has no tile groups
+    assert L.flk_desc_check(ctypes.byref(tiles)) == 4
+    mixed = flk.desc(flk.K, 8, 128)
+    mixed.group = 16                                      # INT4 with an NVFP4 block size
+    assert L.flk_desc_check(ctypes.byref(mixed)) == 4
+    # INT4-only entry points answer "unsupported" for a well-formed NVFP4 descriptor
+    vd = flk.desc(flk.V, 8, 128)
+    S = flk.StreamC
+    chain = (S * 1)(S(256, 0, None, FAKE.value, FAKE.value, None))
+    assert L.flk_decode_attn_packed(ctypes.byref(d), ctypes.byref(vd), 256, FAKE, 32, chain, chain, 1, 0.088, FAKE,
+                                    FAKE, 1 << 24, None) == 5
+    assert L.flk_attn_workspace_bytes(ctypes.byref(d), 256, 32) == 0
+    assert L.flk_sparse_workspace_bytes(ctypes.byref(d), 256, 32, 16, 1) == 0
+
+
+def test_reconstruct_mixed_validation():
+    L = flk.lib()
+    S = flk.StreamC
+    T = 256
+    base = S(T, 0, None, FAKE.value, FAKE.value, None)
+    chain = (S * 2)(base, S(T, 0, None, FAKE.value, FAKE.value, None))
+    i4, f4 = flk.desc(flk.K, 8, 128), flk.desc(flk.K, 8, 128, nvfp4=True)
+    f4v, f4h = flk.desc(flk.V, 8, 128, nvfp4=True), flk.desc(flk.K, 4, 128, nvfp4=True)
+
+    def call(bd, rd, out=FAKE, n=2, T=T):
+        return L.flk_reconstruct_mixed(ctypes.byref(bd), ctypes.byref(rd), T, chain, n, out, None)
+    assert call(i4, f4v) == 4                             # kinds disagree
+    assert call(i4, f4h) == 4                             # head counts disagree
+    assert call(f4, i4) == 5                              # NVFP4 base, INT4 residuals
+    assert call(i4, f4, out=None) == 1
+    assert call(i4, f4, T=0) == 2
+    assert call(i4, f4, n=0) == 2
+    assert call(i4, f4, out=MIS) == 3
