@@ -444,6 +444,137 @@ def selection_leg(reps=20):
     return res
 
 
+def _format_calls(kind, w, xs, rows, recon, out, packed, base_fp4, resid_fp4):
+    """Prepared C calls of one tensor's chain in a format: base, residual loops, reconstruct."""
+    L = flk.lib()
+    P = ctypes.c_void_p
+    bd = flk.desc(kind, w.H, w.D, nvfp4=base_fp4)
+    rd = flk.desc(kind, w.H, w.D, nvfp4=resid_fp4)
+    keep = [bd, rd]
+    calls = [(L.flk_encode_base, (ctypes.byref(bd), P(xs[0].data_ptr()), w.T, P(packed[0].codes.data_ptr()),
+                                  P(packed[0].params.data_ptr()), P(recon.data_ptr()), None))]
+    for l in range(1, len(xs)):
+        r = rows[l]
+        calls.append((L.flk_encode_residual,
+                      (ctypes.byref(rd), P(xs[l].data_ptr()), None if r is None else P(r.data_ptr()), xs[l].shape[0],
+                       w.T, P(recon.data_ptr()), P(packed[l].codes.data_ptr()), P(packed[l].params.data_ptr()),
+                       None if r is None else P(packed[l].tile_start.data_ptr()), None)))
+    arr = (flk.StreamC * len(packed))(*[p.c() for p in packed])
+    keep.append(arr)
+    calls.append((L.flk_reconstruct_mixed, (ctypes.byref(bd), ctypes.byref(rd), w.T, arr, len(packed),
+                                            P(out.data_ptr()))))
+    return calls, keep
+
+
+def _format_bytes(kind, w, sets, base_fp4, resid_fp4):
+    """Algorithmic bytes of one tensor's chain (each input read once, each output written once);
+    the stream-amax pass of an NVFP4 loop re-reads its input and is not counted."""
+    H, D, T = w.H, w.D, w.T
+    W = H * D
+
+    def stream(n, fp4, sparse):
+        return flk.stream_bytes(kind, H, D, n, T, sparse, nvfp4=fp4) - (flk.tile_index_bytes(T) if sparse else 0)
+    b = 2 * T * W + stream(T, base_fp4, False) + 2 * T * W
+    total_streams = stream(T, base_fp4, False)
+    for r in sets[1:]:
+        n = T if r is None else len(r)
+        st = stream(n, resid_fp4, r is not None)
+        b += 6 * n * W + st
+        total_streams += st
+    return b + total_streams + 2 * T * W, total_streams
+
+
+def fp4_leg(w, host, sets, reps=30, rotate=2):
+    """The NVFP4 variant (PR #166 review item 2) on the long prompt, K and V chains of 4 loops
+    (100/100/50/25 %), against INT4 at the same ~4.5 bits per element: INT4 throughout, NVFP4
+    throughout, INT4 base + NVFP4 residuals.  Per format: the chain step (encode base, three
+    residual encodes, reconstruct, for K and V; events around the step, `rotate` buffer sets),
+    the stored bytes, and the accuracy of the depth-4 reconstruction X_hat against the BF16
+    inputs: relative Frobenius error per tensor, and decode attention (32 query heads over the
+    8 KV heads, binary32 on the GPU) from X_hat against attention from the inputs."""
+    H, D, T = w.H, w.D, w.T
+    dev = {}
+    for kind in (flk.K, flk.V):
+        xs = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in host[kind].xs]
+        rows = [None if r is None else torch.from_numpy(r).cuda() for r in sets]
+        truth = xs[0].clone()                                  # the logical BF16 tensor after loop 4
+        for x, r in zip(xs[1:], rows[1:]):
+            if r is None:
+                truth.copy_(x)
+            else:
+                truth[r.long()] = x
+        dev[kind] = (xs, rows, truth)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    Hq = 32
+    q = torch.randn((Hq, D), device="cuda", generator=g).to(torch.bfloat16).float()
+
+    def attend(kt, vt):
+        kf = kt.float().permute(1, 2, 0).contiguous()          # [H, D, T]
+        vf = vt.float().permute(1, 0, 2).contiguous()          # [H, T, D]
+        qh = q.view(H, Hq // H, D)
+        p = torch.softmax(torch.bmm(qh, kf) / math.sqrt(D), dim=-1)
+        return torch.bmm(p, vf).reshape(Hq, D)
+
+    ref_out = attend(dev[flk.K][2], dev[flk.V][2])
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    res = {"workload": "long_prompt", "T": T, "H": H, "D": D, "budgets_pct": list(w.budgets), "formats": {}}
+    for name, base_fp4, resid_fp4 in (("int4", False, False), ("nvfp4", True, True),
+                                      ("int4_base_nvfp4_residuals", False, True)):
+        sets_dev, keep, outs = [], [], {}
+        for _ in range(rotate):
+            calls = []
+            for kind in (flk.K, flk.V):
+                xs, rows, _ = dev[kind]
+                recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+                out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+                packed = [flk.Packed.empty(kind, H, D, x.shape[0], r, T=T, nvfp4=base_fp4 if l == 0 else resid_fp4)
+                          for l, (x, r) in enumerate(zip(xs, rows))]
+                c, k = _format_calls(kind, w, xs, rows, recon, out, packed, base_fp4, resid_fp4)
+                calls += c
+                keep += [k, packed, recon, out]
+                outs.setdefault(kind, out)
+            sets_dev.append(calls)
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def step(i):
+            for fn, args in sets_dev[i % rotate]:
+                st = fn(*args, sp)
+                if st != 0:
+                    raise flk.FlkError(st, name)
+        for i in range(5):
+            step(i)
+        torch.cuda.synchronize()
+        times = []
+        for i in range(reps):
+            flush.view(torch.int64).sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(i)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        step(0)                                                # outs[] hold set 0's reconstruction
+        torch.cuda.synchronize()
+        us = float(np.median(times))
+        b_k, s_k = _format_bytes(flk.K, w, sets, base_fp4, resid_fp4)
+        b_v, s_v = _format_bytes(flk.V, w, sets, base_fp4, resid_fp4)
+        acc = {}
+        for kind, tag in ((flk.K, "k"), (flk.V, "v")):
+            t = dev[kind][2].float()
+            acc[f"{tag}_rel_fro_err"] = float((outs[kind].float() - t).norm() / t.norm())
+        o = attend(outs[flk.K], outs[flk.V])
+        rel = ((o - ref_out).abs().amax(dim=1) / ref_out.abs().amax(dim=1)).cpu().numpy()
+        res["formats"][name] = {
+            "step_us": round(us, 2), "step_bytes": int(b_k + b_v), "gbs": round((b_k + b_v) / us / 1e3, 1),
+            "stored_bytes": int(s_k + s_v),
+            "bits_per_element": round(8 * (s_k + s_v) / (2 * sum((T if r is None else len(r)) for r in sets) * H * D), 4),
+            **{k: round(v, 6) for k, v in acc.items()},
+            "attn_rel_err_max": round(float(rel.max()), 6), "attn_rel_err_mean": round(float(rel.mean()), 6)}
+        del sets_dev, keep, outs
+    return res
+
+
 def rolling_leg(reps=50):
     """The rolling BF16 tail (RFC section 3.3): decode tokens wait in BF16 until a whole
     64-token group can be flushed into the packed streams, whose K groups are tile-local.
@@ -707,6 +838,7 @@ def main():
     ap.add_argument("--no-rolling", action="store_true", help="skip the rolling-tail flush and attention leg")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse decode attention leg")
     ap.add_argument("--no-selection", action="store_true", help="skip the token selection leg")
+    ap.add_argument("--no-fp4", action="store_true", help="skip the NVFP4 variant leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -844,6 +976,9 @@ def main():
     if not args.no_sparse:
         log("sparse decode attention ...")
         result["sparse_attention"] = sparse_leg()
+    if not args.no_fp4:
+        log("NVFP4 variant against INT4 ...")
+        result["nvfp4"] = fp4_leg(w, host, sets)
     if not args.no_selection:
         log("token selection ...")
         result["token_selection"] = selection_leg()

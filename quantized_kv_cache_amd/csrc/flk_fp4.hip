@@ -2,8 +2,10 @@
 // E2M1 codes, one E4M3 scale per 16 elements, one FP32 scale per tensor; an INT4 base with
 // NVFP4 residuals allowed), on the residual chain of the FlashLoop RFC (section 3.3).
 //
-//   fp4_amax_kernel<RESID>   the stream's largest magnitude (X, or the BF16 residual against
-//                            the reconstruction) into the params header, one atomic per block
+//   fp4_amax_kernel<RESID>   per-block maxima of the stream's magnitudes (X, or the BF16 residual
+//                            against the reconstruction), parked in the stream's codes buffer,
+//                            which the encoder overwrites afterwards
+//   fp4_amax_fold_kernel     their maximum into the params header
 //   fp4_encode_kernel<RESID> one thread per 16-channel block: block scale, codes, the decoded
 //                            values into the reconstruction, and (compact loops) the tile index
 //   fp4_reconstruct_kernel   X_hat from a chain whose base is INT4 or NVFP4 and whose residual
@@ -25,6 +27,7 @@ namespace {
 
 constexpr int kFp4Threads = 256;
 constexpr int kAmaxBlocks = 1024;
+constexpr int kAmaxUnroll = 4;
 constexpr int kRecItemsPerThread = 4;
 
 // ---- element formats ------------------------------------------------------------------------
@@ -51,42 +54,74 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return e == 0 ? float(m) * 0x1p-9f : __builtin_ldexpf(1.0f + float(m) * 0.125f, int(e) - 7);
 }
 
-// E2M1 magnitude 0..7 -> value.
-__device__ __forceinline__ float e2m1_value(uint32_t mag) {
-  return mag < 2 ? 0.5f * float(mag) : __uint_as_float((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22));
-}
-
-// Magnitude code of the nearest-even E2M1 value to |y| = a, saturated at 6; the grid step is
-// 0.5 below 2, 1 below 4, 2 above, so a / step is exact and rint picks the even neighbour.
-__device__ __forceinline__ float e2m1_steps(float a, float& step) {
-  step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
-  return a * (1.0f / step);
-}
-__device__ __forceinline__ uint32_t e2m1_mag_of(float k, float step) {
-  if (step == 0.5f) return uint32_t(k);                          // 0..4
-  if (step == 1.0f) return uint32_t(k) + 2u;                     // 2..4 -> 4..6
-  return uint32_t(__builtin_fminf(k, 3.0f)) + 4u;                // 2, 3, >= 4 -> 6, 7, 7
-}
-
-// Code (sign in bit 3) of v against the block's scale bs > 0 with rbs ~ 1/bs.  Fast path:
-// q = RN(v * rbs) is within 3 ulp of RN(v / bs); with |v| <= 6.4 bs, |q| / step stays below
-// 13, so its rounding can differ from that of the exact quotient only within 2^-15 of a
-// half-integer, where the correctly rounded division decides (as it does when q is not a
-// finite value below 16 steps, e.g. when a tiny bs has no finite reciprocal).
-__device__ __forceinline__ uint32_t e2m1_code(float v, float bs, float rbs) {
-  float step;
-  float t = e2m1_steps(__builtin_fabsf(v * rbs), step);
-  float k = __builtin_rintf(t);
-  if (__builtin_expect(!(t < 16.0f) || __builtin_fabsf(t - k) > 0.5f - 0x1p-15f, 0)) {
-    t = e2m1_steps(__builtin_fabsf(v / bs), step);
-    k = __builtin_rintf(t);
+// gfx950 converts pairs of binary32 values to E2M1 codes (v_cvt_scalef32_pk_fp4_f32) and back
+// (v_cvt_scalef32_pk_f32_fp4).  With a scale of 1 the conversion to E2M1 is the nearest-even
+// value, saturated at 6, with the sign kept for values that round to zero (zeros and
+// subnormals included), and the conversion back is exact -- checked against the oracle's
+// rounding on ties, their neighbours, saturation, signed zeros and subnormals.  (A scale that
+// is not a power of two contributes only its exponent, so the block scale is divided out
+// beforehand.)  Pair k of a word is byte k; its low nibble is the even element.
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t w, float a, float b, int k) {
+  switch (k) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 3);
   }
-  return e2m1_mag_of(k, step) | (__builtin_signbit(v) ? 8u : 0u);
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 uncvt_pair(uint32_t w, int k) {
+  switch (k) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
 }
 
-__device__ __forceinline__ float e2m1_decode(uint32_t code, float bs) {
-  const float m = e2m1_value(code & 7u) * bs;
-  return (code & 8u) ? -m : m;
+// Codes of 8 values (4 pairs, one word) against the block's scale bs > 0, and their decoded
+// values RN32(e2m1 * bs).  The code of v is the E2M1 rounding of y = RN32(v / bs).  Fast path:
+// q = RN(v * rcp(bs)) lies within 2^-22 (relative) of y for a normal bs, so y lies between
+// q (1 - 2^-21) and q (1 + 2^-21); E2M1 rounding is monotonic, so when both ends give the
+// same codes, y does too.  Otherwise (or for a bs outside the normal range) the correctly
+// rounded division decides.
+__device__ __forceinline__ uint32_t e2m1_encode8(const float v[8], float bs, float dec[8]) {
+  uint32_t cw = 0u;
+  bool exact = !(bs >= 0x1p-126f && bs <= 0x1p125f);
+  if (!exact) {
+    const float rbs = __builtin_amdgcn_rcpf(bs);
+    const float lo = 1.0f - 0x1p-21f, hi = 1.0f + 0x1p-21f;
+    uint32_t clo = 0u, chi = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float q0 = v[2 * k] * rbs, q1 = v[2 * k + 1] * rbs;
+      clo = cvt_pair(clo, q0 * lo, q1 * lo, k);
+      chi = cvt_pair(chi, q0 * hi, q1 * hi, k);
+    }
+    cw = clo;
+    exact = clo != chi;
+  }
+  if (__builtin_expect(exact, 0)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cw = cvt_pair(cw, v[2 * k] / bs, v[2 * k + 1] / bs, k);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 d = uncvt_pair(cw, k);
+    dec[2 * k] = d.x * bs;
+    dec[2 * k + 1] = d.y * bs;
+  }
+  return cw;
+}
+
+// The 8 decoded values of a code word against the block's scale.
+__device__ __forceinline__ void e2m1_decode8(uint32_t cw, float bs, float dec[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 d = uncvt_pair(cw, k);
+    dec[2 * k] = d.x * bs;
+    dec[2 * k + 1] = d.y * bs;
+  }
 }
 
 // Stream scale from the stream's largest magnitude.
@@ -125,20 +160,31 @@ template <bool RESID>
 __global__ __launch_bounds__(kFp4Threads) void fp4_amax_kernel(const uint16_t* __restrict__ x,
                                                                  const int32_t* __restrict__ rows,
                                                                  const uint16_t* __restrict__ recon, int64_t chunks,
-                                                                 int32_t W, uint32_t* __restrict__ amax_word,
+                                                                 int32_t W, float* __restrict__ partial,
                                                                  uint32_t* __restrict__ status) {
   __shared__ float wmax[kFp4Threads / 64];
   float m = 0.0f;
   bool bad = false;
-  for (int64_t c = int64_t(blockIdx.x) * kFp4Threads + threadIdx.x; c < chunks;
-       c += int64_t(gridDim.x) * kFp4Threads) {
-    float v[8];
-    chunk_values<RESID>(x, rows, recon, W, c, v);
+  const int64_t stride = int64_t(gridDim.x) * kFp4Threads;
+  for (int64_t c0 = int64_t(blockIdx.x) * kFp4Threads + threadIdx.x; c0 < chunks; c0 += kAmaxUnroll * stride) {
+    float v[kAmaxUnroll][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      bad |= !__builtin_isfinite(v[i]);
-      m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    for (int u = 0; u < kAmaxUnroll; ++u) {           // kAmaxUnroll chunks in flight per thread
+      const int64_t c = c0 + u * stride;
+      if (c < chunks) {
+        chunk_values<RESID>(x, rows, recon, W, c, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bad |= !__builtin_isfinite(v[u][i]);
+        m = __builtin_fmaxf(m, __builtin_fabsf(v[u][i]));
+      }
   }
   if (bad && status) atomicOr(status, FLK_DEV_NONFINITE);
 #pragma unroll
@@ -147,12 +193,31 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_amax_kernel(const uint16_t* _
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int i = 1; i < kFp4Threads / 64; ++i) m = __builtin_fmaxf(m, wmax[i]);
-    if (m > 0.0f) atomicMax(amax_word, __float_as_uint(m));   // non-negative floats order as integers
+    partial[blockIdx.x] = m;
+  }
+}
+
+// The stream amax from the blocks' maxima, into the header's amax word.
+__global__ __launch_bounds__(kFp4Threads) void fp4_amax_fold_kernel(const float* __restrict__ partial, int32_t nb,
+                                                                     uint32_t* __restrict__ params) {
+  __shared__ float wmax[kFp4Threads / 64];
+  float m = 0.0f;
+  for (int32_t i = threadIdx.x; i < nb; i += kFp4Threads) m = __builtin_fmaxf(m, partial[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kFp4Threads / 64; ++i) m = __builtin_fmaxf(m, wmax[i]);
+    params[1] = __float_as_uint(m);
   }
 }
 
 // ---- encode ----------------------------------------------------------------------------------
 
+// Lane pairs own a 16-channel block: lane 2m holds its channels 0..7, lane 2m+1 channels
+// 8..15 (16 coalesced bytes per lane and tensor), the pair takes the block's amax with one
+// shuffle, and each lane writes its 4 bytes of codes and 16 bytes of reconstruction.
 template <bool RESID>
 __global__ __launch_bounds__(kFp4Threads) void fp4_encode_kernel(const uint16_t* __restrict__ x,
                                                                   const int32_t* __restrict__ rows,
@@ -160,75 +225,73 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_encode_kernel(const uint16_t*
                                                                   int32_t W, uint8_t* __restrict__ codes,
                                                                   uint32_t* __restrict__ params,
                                                                   int32_t* __restrict__ tile_start) {
-  const int32_t bpr = W / 16;                                     // blocks per row
-  const int64_t i = int64_t(blockIdx.x) * kFp4Threads + threadIdx.x;
+  const int64_t c = int64_t(blockIdx.x) * kFp4Threads + threadIdx.x;    // 8-element chunk
   const float s_g = stream_scale(__uint_as_float(params[1]));
-  if (i == 0) {
+  if (c == 0) {
     params[0] = __float_as_uint(s_g);
     params[2] = 0u;
     params[3] = 0u;
   }
-  if (i >= int64_t(n) * bpr) return;
-  const int32_t j = int32_t(i / bpr);
-  const int32_t rem = int32_t(i - int64_t(j) * bpr);
-  if (RESID && rows && rem == 0) write_tile_index(rows, n, T, j, tile_start, 0, 0);
-  float v[16], prev[16];
+  const int64_t chunks = int64_t(n) * (W / 8);
+  const bool live = c < chunks;                        // chunks is even: pairs are whole
+  const int64_t cc = live ? c : 0;
+  const int64_t e0 = 8 * cc;
+  const int32_t j = int32_t(e0 / W);
+  const int64_t within = e0 - int64_t(j) * W;
+  if (RESID && rows && live && within == 0) write_tile_index(rows, n, T, j, tile_start, 0, 0);
+  float v[8], prev[8];
   uint16_t* dst;
   {
-    const uint4 a0 = *reinterpret_cast<const uint4*>(x + 16 * i);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(x + 16 * i + 8);
-    const uint32_t wa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const uint4 a = *reinterpret_cast<const uint4*>(x + e0);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       v[2 * e] = bf16_lo(wa[e]);
       v[2 * e + 1] = bf16_hi(wa[e]);
     }
   }
   if (RESID) {
     const int64_t p = rows ? rows[j] : j;
-    dst = recon + p * W + 16 * rem;
-    const uint4 b0 = *reinterpret_cast<const uint4*>(dst);
-    const uint4 b1 = *reinterpret_cast<const uint4*>(dst + 8);
-    const uint32_t wb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    dst = recon + p * W + within;
+    const uint4 b = *reinterpret_cast<const uint4*>(dst);
+    const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       prev[2 * e] = bf16_lo(wb[e]);
       prev[2 * e + 1] = bf16_hi(wb[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = round_bf16(v[e] - prev[e]);   // the residual, in BF16
+    for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e] - prev[e]);      // the residual, in BF16
   } else {
-    dst = recon + 16 * i;
+    dst = recon + e0;
   }
   float amax_b = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[e]));
+  for (int e = 0; e < 8; ++e) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[e]));
+  amax_b = __builtin_fmaxf(amax_b, __shfl_xor(amax_b, 1));
+  if (!live) return;
   uint32_t sbyte;
   const float e4 = e4m3_round(amax_b / (6.0f * s_g), sbyte);
   const float bs = e4 * s_g;
-  const float rbs = __builtin_amdgcn_rcpf(bs);
-  uint32_t cw[2] = {0u, 0u};
-  float dec[16];
+  uint32_t cw = 0u;
+  float dec[8];
+  if (bs > 0.0f) {
+    cw = e2m1_encode8(v, bs, dec);
+  } else {                                             // a block whose scale is 0: codes +0
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t c = bs > 0.0f ? e2m1_code(v[e], bs, rbs) : 0u;
-    cw[e >> 3] |= c << (4 * (e & 7));
-    dec[e] = e2m1_decode(c, bs);
+    for (int e = 0; e < 8; ++e) dec[e] = 0.0f;
   }
-  *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(cw[0], cw[1]);
-  reinterpret_cast<uint8_t*>(params)[16 + i] = uint8_t(sbyte);
-  uint32_t o[8];
+  *reinterpret_cast<uint32_t*>(codes + 4 * c) = cw;
+  if ((c & 1) == 0) reinterpret_cast<uint8_t*>(params)[16 + (c >> 1)] = uint8_t(sbyte);
+  uint32_t o[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (RESID) {
-      const float d0 = round_bf16(dec[2 * e]), d1 = round_bf16(dec[2 * e + 1]);
-      o[e] = pack_bf16x2(prev[2 * e] + d0, prev[2 * e + 1] + d1);
-    } else {
+  for (int e = 0; e < 4; ++e) {
+    if (RESID)
+      o[e] = pack_bf16x2(prev[2 * e] + round_bf16(dec[2 * e]), prev[2 * e + 1] + round_bf16(dec[2 * e + 1]));
+    else
       o[e] = pack_bf16x2(dec[2 * e], dec[2 * e + 1]);
-    }
   }
   *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-  *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // ---- reconstruct (mixed chains) -------------------------------------------------------------
@@ -275,8 +338,10 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
     if (base_fp4) {
       const float s_g = __uint_as_float(b.params[0]);
       const float bs = e4m3_value(reinterpret_cast<const uint8_t*>(b.params)[16 + int64_t(p) * bpr + blk]) * s_g;
+      e2m1_decode8(bw[0], bs, x);
+      e2m1_decode8(bw[1], bs, x + 8);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = round_bf16(e2m1_decode((bw[e >> 3] >> (4 * (e & 7))) & 15u, bs));
+      for (int e = 0; e < 16; ++e) x[e] = round_bf16(x[e]);
     } else if (kind == FLK_KIND_K) {                            // one (min, scale) per channel of the 64-row group
       const uint32_t* pk = b.params + int64_t(p / kGroup) * W + int64_t(h) * D + c0;
 #pragma unroll
@@ -305,9 +370,11 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
       const uint32_t rw[2] = {rc.x, rc.y};
       const float s_g = __uint_as_float(s.params[0]);
       const float bs = e4m3_value(reinterpret_cast<const uint8_t*>(s.params)[16 + int64_t(j) * bpr + blk]) * s_g;
+      float d[16];
+      e2m1_decode8(rw[0], bs, d);
+      e2m1_decode8(rw[1], bs, d + 8);
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        x[e] = round_bf16(x[e] + round_bf16(e2m1_decode((rw[e >> 3] >> (4 * (e & 7))) & 15u, bs)));
+      for (int e = 0; e < 16; ++e) x[e] = round_bf16(x[e] + round_bf16(d[e]));
     }
     uint16_t* o = out + off;
     *reinterpret_cast<uint4*>(o) = pack_exact_bf16x8(x);
@@ -322,21 +389,24 @@ hipError_t launch_fp4_encode(bool resid, const void* x, const int32_t* rows, int
                              uint32_t* status, hipStream_t stream) {
   const int32_t W = H * D;
   if (D % 16 != 0 || n < 1) return hipErrorInvalidValue;
-  hipError_t e = launch_fill_u32(params + 1, 1, 0u, stream);           // the header's amax word
-  if (e != hipSuccess) return e;
   const int64_t chunks = int64_t(n) * W / 8;
+  // one partial maximum per amax block, parked in the codes buffer (n*W/2 bytes, room for
+  // `chunks` floats), which the encode kernel overwrites after the fold has read it
   const unsigned ab = unsigned(std::min<int64_t>(kAmaxBlocks, (chunks + kFp4Threads - 1) / kFp4Threads));
+  float* partial = reinterpret_cast<float*>(codes);
   const auto* xs = static_cast<const uint16_t*>(x);
   auto* rc = static_cast<uint16_t*>(recon);
-  const unsigned eb = unsigned((int64_t(n) * (W / 16) + kFp4Threads - 1) / kFp4Threads);
+  const unsigned eb = unsigned((int64_t(n) * (W / 8) + kFp4Threads - 1) / kFp4Threads);
   if (resid) {
     hipLaunchKernelGGL(fp4_amax_kernel<true>, dim3(ab), dim3(kFp4Threads), 0, stream, xs, rows, rc, chunks, W,
-                       params + 1, status);
+                       partial, status);
+    hipLaunchKernelGGL(fp4_amax_fold_kernel, dim3(1), dim3(kFp4Threads), 0, stream, partial, int32_t(ab), params);
     hipLaunchKernelGGL(fp4_encode_kernel<true>, dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n, T, W,
                        codes, params, tile_start);
   } else {
     hipLaunchKernelGGL(fp4_amax_kernel<false>, dim3(ab), dim3(kFp4Threads), 0, stream, xs, rows, rc, chunks, W,
-                       params + 1, status);
+                       partial, status);
+    hipLaunchKernelGGL(fp4_amax_fold_kernel, dim3(1), dim3(kFp4Threads), 0, stream, partial, int32_t(ab), params);
     hipLaunchKernelGGL(fp4_encode_kernel<false>, dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n, T, W,
                        codes, params, tile_start);
   }
