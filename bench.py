@@ -27,6 +27,7 @@ import math
 import os
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 import torch
@@ -260,7 +261,54 @@ def cpu_baseline(w, host, sets, heads=(0, 1)):
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"KV heads {list(heads)} of {w.H} for K and V (1/{w.H // len(heads)} of the step's "
                       f"groups), full T={w.T}, same 4-loop chain + reconstruct; {dt:.1f} s single-threaded "
-                      f"C oracle on the host"}
+                      f"C oracle on the host",
+            "rows": cpu_baseline_rows(w, host, sets)}
+
+
+def cpu_baseline_rows(w, host, sets):
+    """The oracle (as it stands, single thread) on bounded samples of the other legs' workloads,
+    each in the unit its leg reports."""
+    from oracle import fp4 as ofp4
+    from oracle import oracle as orc
+    from oracle import selection as osel
+    rows = {}
+    # token selection: loop 3 (50 %) over the first two windows (4096 tokens, d = 4096)
+    T_s, d, W = 4096, 4096, 2048
+    hs = synth.hidden_states(T_s, d, 2)
+    t0 = time.perf_counter()
+    osel.select_rows(hs[1], hs[0], None, W, 50, 1e-6)
+    dt = time.perf_counter() - t0
+    b = 2 * T_s * d * 2 + 4 * T_s
+    rows["token_selection"] = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "sample": f"loop 3 over windows 0-1 ({T_s} of 32768 tokens, d={d}): {dt:.2f} s"}
+    # NVFP4: the long-prompt K chain of KV head 0 (1/8 of the tensor), encode + reconstruct
+    xs = [np.ascontiguousarray(x[:, 0:1]) for x in host[flk.K].xs]
+    t0 = time.perf_counter()
+    _, recon = ofp4.encode_base(xs[0])
+    base = recon.copy()
+    streams = [ofp4.encode_residual(x, r, recon) for x, r in zip(xs[1:], sets[1:])]
+    ofp4.apply_residuals(base, streams)
+    dt = time.perf_counter() - t0
+    b, _ = _format_bytes(flk.K, SimpleNamespace(H=1, D=w.D, T=w.T), sets, True, True)
+    rows["nvfp4"] = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                     "sample": f"K chain of KV head 0 (1/{w.H} of the tensor), 4 loops + reconstruct: {dt:.2f} s"}
+    # sparse decode attention: the reference and one later loop for the 4 query heads of one KV
+    # head over 131072 tokens (BF16 K/V drawn like the decode workload's), k = 4096
+    wd = synth.WORKLOADS[5]
+    g = synth.rng(wd.wid, 0, 0, 0, 0, synth.P_VALUES)
+    kh = synth.to_bf16_bits(g.standard_normal((wd.T, 1, wd.D), dtype=np.float32))
+    vh = synth.to_bf16_bits(g.standard_normal((wd.T, 1, wd.D), dtype=np.float32))
+    q = synth.to_bf16_bits(g.standard_normal((wd.Hq // wd.H, wd.D), dtype=np.float32))
+    t0 = time.perf_counter()
+    ref = orc.sparse_reference(q, kh, vh, 1.0 / math.sqrt(wd.D), 4096)
+    t1 = time.perf_counter()
+    orc.sparse_loop(q, kh, vh, 1.0 / math.sqrt(wd.D), ref)
+    t2 = time.perf_counter()
+    rows["sparse_attention"] = {"value": round((t1 - t0) * 1e6 * wd.H, 1), "unit": "us per reference call",
+                                "loop_us": round((t2 - t1) * 1e6 * wd.H, 1), "cores": 1,
+                                "sample": f"1 of {wd.H} KV heads ({wd.Hq // wd.H} query heads), T={wd.T}, k=4096, "
+                                          f"scaled by {wd.H}: reference {t1 - t0:.2f} s, loop {t2 - t1:.2f} s"}
+    return rows
 
 
 # ----------------------------------------------------------------------------- decode attention
@@ -268,7 +316,7 @@ def cpu_baseline(w, host, sets, heads=(0, 1)):
 def attention_leg(reps=20):
     """Time flk_decode_attn_packed, the chains' consumer, on the decode workload (T=131072,
     8 KV heads, 32 query heads, D=128, chains at 100/100/50/25%), with the chains encoded by
-    the library from the seeded inputs.  Each timed call is preceded by a 512 MiB write so the
+    the library from the seeded inputs.  Each timed call is preceded by a 512 MiB read so the
     MALL holds none of the packed chains; the figure is the median of `reps` calls."""
     w = synth.WORKLOADS[5]
     T, H, D, Hq = w.T, w.H, w.D, w.Hq
