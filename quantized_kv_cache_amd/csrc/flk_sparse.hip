@@ -194,6 +194,238 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------
+// Top-k split over segments, for long rows: one block of 1024 threads per head keeps a single
+// CU busy with three passes of LDS atomics over T keys, so past kSplitMinT each head's row
+// is cut into B segments of S keys (S a multiple of 4).  Per radix pass, topk_seg_hist_kernel
+// builds each segment's digit histogram (of the keys that match the head's prefix so far) and
+// topk_seg_digit_kernel sums a head's segment histograms and advances its state {prefix,
+// mask, need}; then topk_seg_count_kernel counts each segment's keys above and equal to tau,
+// and topk_seg_write_kernel writes the segment's selected positions at offsets taken from the
+// earlier segments' counts.  The selection is exactly the one-block kernel's.
+// ---------------------------------------------------------------------------------------
+constexpr int32_t kSplitMinT = 16384;
+constexpr int32_t kSegKeys = 8192;            // target keys per segment
+constexpr int kSegThreads = 256;
+constexpr int kSegWaves = kSegThreads / 64;
+
+struct SplitTopk {
+  int32_t B, S;                               // segments per head, keys per segment
+};
+__host__ __device__ inline SplitTopk split_topk(int32_t T) {
+  SplitTopk t;
+  t.B = (T + kSegKeys - 1) / kSegKeys;
+  if (t.B > 64) t.B = 64;
+  t.S = (((T + t.B - 1) / t.B) + 3) & ~3;
+  return t;
+}
+
+__device__ __forceinline__ void pass_digits(int pass, int& shift, uint32_t& nb) {
+  shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+  nb = pass == 2 ? 1024u : 2048u;
+}
+
+__global__ __launch_bounds__(kSegThreads) void topk_seg_hist_kernel(const float* __restrict__ scores, int32_t T,
+                                                                     int32_t B, int32_t S, int pass,
+                                                                     const uint32_t* __restrict__ state,
+                                                                     uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t hist[2048];
+  const int tid = threadIdx.x;
+  const int32_t b = blockIdx.x, qh = blockIdx.y;
+  const float* sc = scores + int64_t(qh) * score_stride(T);
+  int shift;
+  uint32_t nb;
+  pass_digits(pass, shift, nb);
+  const uint32_t prefix = pass ? state[4 * qh] : 0u, pmask = pass ? state[4 * qh + 1] : 0u;
+  for (int d = tid; d < 2048; d += kSegThreads) hist[d] = 0;
+  __syncthreads();
+  const int32_t lo = b * S, hi = min(T, lo + S);
+  for (int32_t t0 = lo; t0 < hi; t0 += 4 * kSegThreads * kTopBatch) {
+    uint32_t key[kTopBatch][4];
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 4 * (i * kSegThreads + tid), hi, key[i]);
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t t = t0 + 4 * (i * kSegThreads + tid) + e;
+        if (t < hi && (key[i][e] & pmask) == prefix) atomicAdd(&hist[(key[i][e] >> shift) & (nb - 1)], 1u);
+      }
+  }
+  __syncthreads();
+  uint32_t* dst = ghist + (int64_t(qh) * B + b) * 2048;
+  for (int d = tid; d < int(nb); d += kSegThreads) dst[d] = hist[d];
+}
+
+__global__ __launch_bounds__(kTopThreads) void topk_seg_digit_kernel(int32_t B, int32_t k, int pass,
+                                                                      const uint32_t* __restrict__ ghist,
+                                                                      uint32_t* __restrict__ state) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t s_digit, s_above;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t qh = blockIdx.x;
+  int shift;
+  uint32_t nb;
+  pass_digits(pass, shift, nb);
+  for (int d = tid; d < int(nb); d += kTopThreads) {
+    uint32_t c = 0;
+#pragma unroll 8
+    for (int32_t b = 0; b < B; ++b) c += ghist[(int64_t(qh) * B + b) * 2048 + d];   // 8 loads in flight
+    hist[d] = c;
+  }
+  const uint32_t prefix = pass ? state[4 * qh] : 0u, pmask = pass ? state[4 * qh + 1] : 0u;
+  const uint32_t need = pass ? state[4 * qh + 2] : uint32_t(k);
+  __syncthreads();
+  if (wave == 0) {                                       // lane l: digits [nb - 32(l+1), nb - 32l)
+    const int32_t d_hi = int32_t(nb) - 32 * lane;
+    uint32_t c = 0;
+    if (d_hi > 0)
+      for (int i = 1; i <= 32; ++i) c += hist[d_hi - i];
+    uint32_t before = c;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(before, off);
+      if (lane >= off) before += o;
+    }
+    before -= c;
+    if (d_hi > 0 && before < need && need <= before + c) {
+      uint32_t above = before;
+      for (int i = 1; i <= 32; ++i) {
+        const uint32_t h = hist[d_hi - i];
+        if (above + h >= need) { s_digit = uint32_t(d_hi - i); s_above = above; break; }
+        above += h;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    state[4 * qh] = prefix | (s_digit << shift);
+    state[4 * qh + 1] = pmask | ((nb - 1) << shift);
+    state[4 * qh + 2] = need - s_above;
+  }
+}
+
+// Keys of a segment above tau and equal to tau: cnt[(qh * B + b) * 2 + {0, 1}].
+__global__ __launch_bounds__(kSegThreads) void topk_seg_count_kernel(const float* __restrict__ scores, int32_t T,
+                                                                      int32_t B, int32_t S,
+                                                                      const uint32_t* __restrict__ state,
+                                                                      uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t s_cnt[kSegWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t b = blockIdx.x, qh = blockIdx.y;
+  const float* sc = scores + int64_t(qh) * score_stride(T);
+  const uint32_t tau = state[4 * qh];
+  const int32_t lo = b * S, hi = min(T, lo + S);
+  uint32_t gt = 0, eq = 0;
+  for (int32_t t0 = lo; t0 < hi; t0 += 4 * kSegThreads * kTopBatch) {
+    uint32_t key[kTopBatch][4];
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 4 * (i * kSegThreads + tid), hi, key[i]);
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = t0 + 4 * (i * kSegThreads + tid) + e < hi;
+        gt += in && key[i][e] > tau;
+        eq += in && key[i][e] == tau;
+      }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    gt += __shfl_xor(gt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  if (lane == 0) { s_cnt[wave][0] = gt; s_cnt[wave][1] = eq; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t g = 0, q = 0;
+    for (int w = 0; w < kSegWaves; ++w) { g += s_cnt[w][0]; q += s_cnt[w][1]; }
+    cnt[(int64_t(qh) * B + b) * 2] = g;
+    cnt[(int64_t(qh) * B + b) * 2 + 1] = q;
+  }
+}
+
+// The segment's selected positions in position order: wave w of the block owns the contiguous
+// part [lo + w*seg, lo + (w+1)*seg) of the segment, 256 positions per step (lane l holds
+// positions 4l..4l+3 of the step), ranked with ballots as in topk_kernel.
+__global__ __launch_bounds__(kSegThreads) void topk_seg_write_kernel(const float* __restrict__ scores, int32_t T,
+                                                                      int32_t B, int32_t S, int32_t k,
+                                                                      const uint32_t* __restrict__ state,
+                                                                      const uint32_t* __restrict__ cnt,
+                                                                      int32_t* __restrict__ sel) {
+  __shared__ uint32_t s_cnt[kSegWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  const int32_t b = blockIdx.x, qh = blockIdx.y;
+  const float* sc = scores + int64_t(qh) * score_stride(T);
+  const uint32_t tau = state[4 * qh], need = state[4 * qh + 2];
+  uint32_t g_seg = 0, e_seg = 0;                          // earlier segments of the head
+  for (int32_t c = 0; c < b; ++c) {
+    g_seg += cnt[(int64_t(qh) * B + c) * 2];
+    e_seg += cnt[(int64_t(qh) * B + c) * 2 + 1];
+  }
+  const int32_t seg_lo = b * S, seg_hi = min(T, seg_lo + S);
+  const int32_t part = (((seg_hi - seg_lo) + kSegWaves - 1) / kSegWaves + 255) & ~255;
+  const int32_t lo = min(seg_hi, seg_lo + wave * part), hi = min(seg_hi, lo + part);
+  uint32_t gt = 0, eq = 0;
+  for (int32_t t0 = lo; t0 < hi; t0 += 256 * kTopBatch) {
+    uint32_t key[kTopBatch][4];
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 256 * i + 4 * lane, hi, key[i]);
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) {
+      uint32_t g = 0, q = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = t0 + 256 * i + 4 * lane + e < hi;
+        g += in && key[i][e] > tau;
+        q += in && key[i][e] == tau;
+      }
+      gt += wave_sum(g);
+      eq += wave_sum(q);
+    }
+  }
+  if (lane == 0) { s_cnt[wave][0] = gt; s_cnt[wave][1] = eq; }
+  __syncthreads();
+  uint32_t g0 = g_seg, e0 = e_seg;
+  for (int w = 0; w < wave; ++w) { g0 += s_cnt[w][0]; e0 += s_cnt[w][1]; }
+  int32_t* dst = sel + int64_t(qh) * k;
+  uint32_t out = g0 + min(e0, need), e_seen = e0;
+  for (int32_t t0 = lo; t0 < hi; t0 += 256 * kTopBatch) {
+    uint32_t key[kTopBatch][4];
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) keys4(sc, t0 + 256 * i + 4 * lane, hi, key[i]);
+#pragma unroll
+    for (int i = 0; i < kTopBatch; ++i) {
+      const int32_t tb = t0 + 256 * i + 4 * lane;
+      bool is_eq[4];
+      uint32_t q = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        is_eq[e] = tb + e < hi && key[i][e] == tau;
+        q += is_eq[e];
+      }
+      uint32_t eq_rank = e_seen + lanes_below_sum(q, below);
+      bool take[4];
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        take[e] = (tb + e < hi && key[i][e] > tau) || (is_eq[e] && eq_rank < need);
+        eq_rank += is_eq[e];
+        c += take[e];
+      }
+      uint32_t slot = out + lanes_below_sum(c, below);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (take[e]) {
+          if (slot < uint32_t(k)) dst[slot] = tb + e;
+          ++slot;
+        }
+      out += wave_sum(c);
+      e_seen += wave_sum(q);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Position -> compact row maps of a chain's compact loops.
 // ---------------------------------------------------------------------------------------
 struct MapJob {
@@ -478,7 +710,7 @@ __global__ __launch_bounds__(kSD) void sparse_combine_kernel(const float* __rest
 static int32_t gather_blocks(int32_t k) { return (k + kKeysPerBlock - 1) / kKeysPerBlock; }
 
 struct SparseLayout {
-  size_t kmaps, vmaps, part, attn, scores, ml, total;
+  size_t kmaps, vmaps, part, attn, scores, ml, topk, total;
 };
 static SparseLayout sparse_layout(int32_t T, int32_t H, int32_t Hq, int32_t k, int32_t n_loops) {
   SparseLayout L{};
@@ -490,6 +722,12 @@ static SparseLayout sparse_layout(int32_t T, int32_t H, int32_t Hq, int32_t k, i
   L.attn = off; off += align256(attn_workspace_bytes(T, H, Hq));
   L.scores = off; off += align256(size_t(Hq) * size_t(score_stride(T)) * sizeof(float));
   L.ml = off; off += align256(size_t(Hq) * 2 * sizeof(float));
+  L.topk = off;                                  // split top-k: state, segment counts, histograms
+  if (T > kSplitMinT) {
+    const SplitTopk st = split_topk(T);
+    off += align256(size_t(Hq) * 4 * sizeof(uint32_t)) + align256(size_t(Hq) * st.B * 2 * sizeof(uint32_t)) +
+           align256(size_t(Hq) * st.B * 2048 * sizeof(uint32_t));
+  }
   L.total = off;
   return L;
 }
@@ -543,7 +781,26 @@ hipError_t launch_sparse_reference(int32_t T, int32_t H, int32_t Hq, int32_t k, 
   hipError_t e = launch_attn_reference(T, H, Hq, q, kc, vc, scale, out, o_ref, ml, scores, w + L.attn,
                                        attn_workspace_bytes(T, H, Hq), stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(Hq)), dim3(kTopThreads), 0, stream, scores, T, k, sel);
+  if (T > kSplitMinT) {
+    const SplitTopk st = split_topk(T);
+    uint32_t* state = reinterpret_cast<uint32_t*>(w + L.topk);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(w + L.topk + align256(size_t(Hq) * 4 * sizeof(uint32_t)));
+    uint32_t* ghist = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(cnt) +
+                                                  align256(size_t(Hq) * st.B * 2 * sizeof(uint32_t)));
+    const dim3 sgrid(unsigned(st.B), unsigned(Hq));
+    for (int pass = 0; pass < 3; ++pass) {
+      hipLaunchKernelGGL(topk_seg_hist_kernel, sgrid, dim3(kSegThreads), 0, stream, scores, T, st.B, st.S, pass,
+                         state, ghist);
+      hipLaunchKernelGGL(topk_seg_digit_kernel, dim3(unsigned(Hq)), dim3(kTopThreads), 0, stream, st.B, k, pass,
+                         ghist, state);
+    }
+    hipLaunchKernelGGL(topk_seg_count_kernel, sgrid, dim3(kSegThreads), 0, stream, scores, T, st.B, st.S, state,
+                       cnt);
+    hipLaunchKernelGGL(topk_seg_write_kernel, sgrid, dim3(kSegThreads), 0, stream, scores, T, st.B, st.S, k, state,
+                       cnt, sel);
+  } else {
+    hipLaunchKernelGGL(topk_kernel, dim3(unsigned(Hq)), dim3(kTopThreads), 0, stream, scores, T, k, sel);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   GatherArgs g{};
   g.kc = kc;

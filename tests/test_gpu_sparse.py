@@ -43,12 +43,19 @@ def _round_bound(q, khat, scale, G):
 
 
 def _unique_heads(scores, k, eps):
-    """Heads whose top-k under the oracle's scores cannot change by binary32 rounding."""
+    """Heads whose top-k under the oracle's scores cannot change by binary32 rounding: a gap of
+    more than twice the rounding bound at the k-th key, or an exact tie there whose scores are
+    the only ones within that bound (identical keys score identically on both sides, and the
+    tie goes to the lower positions)."""
     T = scores.shape[1]
     if k == T:
         return np.ones(scores.shape[0], bool)
     part = -np.partition(-scores, (k - 1, k), axis=1)
-    return part[:, k - 1] - part[:, k] > 2 * eps
+    gap = part[:, k - 1] - part[:, k] > 2 * eps
+    kth = part[:, k - 1:k]
+    near = np.abs(scores - kth) <= 2 * eps[:, None]
+    clean_tie = (part[:, k - 1] == part[:, k]) & np.all(~near | (scores == kth), axis=1)
+    return gap | clean_tie
 
 
 def _check_selection(sel, scores, eps, tag):
@@ -184,6 +191,30 @@ def test_sparse_attention_small(T, H, Hq, sizes, k, k_tiles):
         for depth, got in gpu["outs"].items():
             dense = orc.decode_attn(qs[depth], o[flk.K].recons[depth - 1], o[flk.V].recons[depth - 1], scale)
             assert np.all(_rel(got, dense) <= 2e-2)
+
+
+@pytest.mark.parametrize("T,k,tied", [(20000, 777, False), (40000, 3000, True)])
+def test_sparse_attention_split_selection(T, k, tied):
+    """Rows longer than the split threshold take the segmented top-k; with every key identical
+    all scores tie, the selection is the first k positions and need runs through all segments."""
+    H, Hq, D = 1, 4, 128
+    rng = np.random.default_rng(T + k)
+    xs, rows = _chains(rng, T, H, D, [None, None, T // 2])
+    if tied:
+        row = xs[flk.K][0][:1]
+        xs[flk.K] = [np.ascontiguousarray(np.broadcast_to(row, x.shape)) for x in xs[flk.K]]
+    g = {kind: GpuChain(kind, xs[kind], rows, k_tiles=kind == flk.K) for kind in (flk.K, flk.V)}
+    o = {kind: OracleChain(kind, xs[kind], rows, k_tiles=kind == flk.K) for kind in (flk.K, flk.V)}
+    qs = {d: synth.to_bf16_bits(rng.standard_normal((Hq, D)).astype(np.float32)) for d in (2, 3)}
+    scale = 1.0 / math.sqrt(D)
+    say(f"sparse attention split top-k T={T} k={k} tied={tied}")
+    ws = _workspace(T, H, Hq, k, 3)
+    gpu = _gpu_reference(g, T, H, Hq, k, qs, scale, ws)
+    ref = orc.sparse_reference(qs[2], o[flk.K].recons[1], o[flk.V].recons[1], scale, k)
+    fed = _gpu_loops(g, T, H, Hq, k, qs, scale, _state_from([(slice(None), ref)], Hq, k), ws)
+    _compare(gpu, fed, o, qs, scale, H, Hq, k, slice(None), tag=f"split T={T}")
+    if tied:
+        assert np.array_equal(gpu["sel"], np.tile(np.arange(k, dtype=np.int32), (Hq, 1)))
 
 
 def test_sparse_attention_long_context():
