@@ -13,6 +13,7 @@
 
 #include <cstdint>
 
+#include "flk_blockscan.h"
 #include "flk_device.h"
 #include "flk_internal.h"
 #include "flk_select.h"
@@ -229,28 +230,6 @@ __device__ __forceinline__ uint32_t sel_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix of v over the NT threads of the block (and the total); call from all threads.
-template <int NT>
-__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t* tmp, int32_t& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  int32_t before = 0;
-  total = 0;
-  for (int u = 0; u < NT / 64; ++u) {
-    before += u < wave ? tmp[u] : 0;
-    total += tmp[u];
-  }
-  __syncthreads();
-  return before + inc - v;
-}
-
 template <bool OWN>
 __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* __restrict__ scores,
                                                                    const int32_t* __restrict__ rows, int32_t n_prev,
@@ -343,30 +322,11 @@ __global__ __launch_bounds__(kWinThreads) void window_topk_kernel(const float* _
         }
       }
       __syncthreads();
-      if (wave == 0) {                                 // lane l: digits [nb - 32(l+1), nb - 32l)
-        const int32_t d_hi = int32_t(nb) - 32 * lane;
-        uint32_t c = 0;
-        if (d_hi > 0)
-          for (int i = 1; i <= 32; ++i) c += hist[d_hi - i];
-        uint32_t before = c;
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t t = __shfl_up(before, o);
-          if (lane >= o) before += t;
-        }
-        before -= c;
-        if (d_hi > 0 && before < need && need <= before + c) {
-          uint32_t above = before;
-          for (int i = 1; i <= 32; ++i) {
-            const uint32_t h = hist[d_hi - i];
-            if (above + h >= need) { s_digit = uint32_t(d_hi - i); s_above = above; break; }
-            above += h;
-          }
-        }
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
+      uint32_t digit, above;
+      block_find_digit<kWinThreads>(hist, nb, need, &s_wave[0][0], digit, above, &s_digit, &s_above);
+      prefix |= digit << shift;
       pmask |= (nb - 1) << shift;
-      need -= s_above;
+      need -= above;
       __syncthreads();
     }
     tau = prefix;

@@ -12,6 +12,7 @@
 // A selected position's compact row in a compact loop comes from a position -> row map that
 // chain_map_kernel writes per call (one wave per 64-position tile), so a gather reads one map
 // entry per loop instead of searching.
+#include "flk_blockscan.h"
 #include "flk_device.h"
 #include "flk_internal.h"
 #include "flk_readers.h"
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(const float* __restri
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t s_cnt[kTopWaves][2];
   __shared__ uint32_t s_digit, s_above;
+  __shared__ int32_t s_tmp[kTopWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
@@ -101,31 +103,11 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(const float* __restri
         }
     }
     __syncthreads();
-    if (wave == 0) {                                       // from the top digit down to the k-th key
-      // lane l holds digits [nb - 32(l+1), nb - 32l); counts above it by a prefix over lanes
-      const int32_t d_hi = int32_t(nb) - 32 * lane;         // exclusive
-      uint32_t c = 0;
-      if (d_hi > 0)
-        for (int i = 1; i <= 32; ++i) c += hist[d_hi - i];
-      uint32_t before = c;                                   // inclusive prefix over lanes 0..l
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(before, off);
-        if (lane >= off) before += o;
-      }
-      before -= c;
-      if (d_hi > 0 && before < need && need <= before + c) {
-        uint32_t above = before;
-        for (int i = 1; i <= 32; ++i) {
-          const uint32_t h = hist[d_hi - i];
-          if (above + h >= need) { s_digit = uint32_t(d_hi - i); s_above = above; break; }
-          above += h;
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
+    uint32_t digit, above;                                   // from the top digit down to the k-th key
+    block_find_digit<kTopThreads>(hist, nb, need, s_tmp, digit, above, &s_digit, &s_above);
+    prefix |= digit << shift;
     pmask |= (nb - 1) << shift;
-    need -= s_above;
+    need -= above;
     __syncthreads();
   }
   // prefix is tau; `need` keys equal to tau are selected, the lowest positions first.  Wave w
@@ -261,7 +243,8 @@ __global__ __launch_bounds__(kTopThreads) void topk_seg_digit_kernel(int32_t B, 
                                                                       uint32_t* __restrict__ state) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t s_digit, s_above;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int32_t s_tmp[kTopWaves];
+  const int tid = threadIdx.x;
   const int32_t qh = blockIdx.x;
   int shift;
   uint32_t nb;
@@ -275,31 +258,12 @@ __global__ __launch_bounds__(kTopThreads) void topk_seg_digit_kernel(int32_t B, 
   const uint32_t prefix = pass ? state[4 * qh] : 0u, pmask = pass ? state[4 * qh + 1] : 0u;
   const uint32_t need = pass ? state[4 * qh + 2] : uint32_t(k);
   __syncthreads();
-  if (wave == 0) {                                       // lane l: digits [nb - 32(l+1), nb - 32l)
-    const int32_t d_hi = int32_t(nb) - 32 * lane;
-    uint32_t c = 0;
-    if (d_hi > 0)
-      for (int i = 1; i <= 32; ++i) c += hist[d_hi - i];
-    uint32_t before = c;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(before, off);
-      if (lane >= off) before += o;
-    }
-    before -= c;
-    if (d_hi > 0 && before < need && need <= before + c) {
-      uint32_t above = before;
-      for (int i = 1; i <= 32; ++i) {
-        const uint32_t h = hist[d_hi - i];
-        if (above + h >= need) { s_digit = uint32_t(d_hi - i); s_above = above; break; }
-        above += h;
-      }
-    }
-  }
-  __syncthreads();
+  uint32_t digit, above;
+  block_find_digit<kTopThreads>(hist, nb, need, s_tmp, digit, above, &s_digit, &s_above);
   if (tid == 0) {
-    state[4 * qh] = prefix | (s_digit << shift);
+    state[4 * qh] = prefix | (digit << shift);
     state[4 * qh + 1] = pmask | ((nb - 1) << shift);
-    state[4 * qh + 2] = need - s_above;
+    state[4 * qh + 2] = need - above;
   }
 }
 
