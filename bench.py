@@ -514,6 +514,48 @@ def _format_calls(kind, w, xs, rows, recon, out, packed, base_fp4, resid_fp4):
     return calls, keep
 
 
+def fp4_attention_times(flush, reps=20):
+    """Fused decode attention on the decode workload (131072 tokens, 8 KV heads, 32 query heads,
+    chains of 4 loops at 100/100/50/25 %) in each format: median microseconds per call, each
+    after a 512 MiB read that evicts the MALL."""
+    w = synth.WORKLOADS[5]
+    T, H, D, Hq = w.T, w.H, w.D, w.Hq
+    sets = synth.active_sets(w, T)
+    host = {kind: synth.make_chain(w, tensor, sets=sets) for kind, tensor in ((flk.K, synth.K_TENSOR),
+                                                                                (flk.V, synth.V_TENSOR))}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    q = torch.randn((Hq, D), device="cuda", generator=g).to(torch.bfloat16)
+    ws = torch.empty(flk.attn_workspace_bytes(H, D, T, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    times = {}
+    for name, base_fp4, resid_fp4 in (("int4", False, False), ("nvfp4", True, True),
+                                      ("int4_base_nvfp4_residuals", False, True)):
+        chains = {}
+        for kind in (flk.K, flk.V):
+            recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+            packs = []
+            for l, (x, r) in enumerate(zip(host[kind].xs, host[kind].rows)):
+                xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+                rd = None if r is None else torch.from_numpy(r).cuda()
+                p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T, nvfp4=base_fp4 if l == 0 else resid_fp4)
+                if l == 0:
+                    flk.encode_base(kind, xd, p, recon)
+                else:
+                    flk.encode_residual(kind, xd, rd, recon, p)
+                packs.append(p)
+            chains[kind] = packs
+            del recon
+        fn = lambda: flk.decode_attn_mixed(q, chains[flk.K], chains[flk.V], T, H, scale, out, ws)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        times[name] = round(_timed_us(fn, reps, flush), 2)
+        del chains
+    return times
+
+
 def _format_bytes(kind, w, sets, base_fp4, resid_fp4):
     """Algorithmic bytes of one tensor's chain (each input read once, each output written once);
     the stream-amax pass of an NVFP4 loop re-reads its input and is not counted."""
@@ -539,7 +581,8 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
     residual encodes, reconstruct, for K and V; events around the step, `rotate` buffer sets),
     the stored bytes, and the accuracy of the depth-4 reconstruction X_hat against the BF16
     inputs: relative Frobenius error per tensor, and decode attention (32 query heads over the
-    8 KV heads, binary32 on the GPU) from X_hat against attention from the inputs."""
+    8 KV heads, binary32 on the GPU) from X_hat against attention from the inputs.  Also the
+    fused decode attention's time per call on the decode workload in each format."""
     H, D, T = w.H, w.D, w.T
     dev = {}
     for kind in (flk.K, flk.V):
@@ -566,6 +609,7 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
 
     ref_out = attend(dev[flk.K][2], dev[flk.V][2])
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    attn_us = fp4_attention_times(flush)
     res = {"workload": "long_prompt", "T": T, "H": H, "D": D, "budgets_pct": list(w.budgets), "formats": {}}
     for name, base_fp4, resid_fp4 in (("int4", False, False), ("nvfp4", True, True),
                                       ("int4_base_nvfp4_residuals", False, True)):
@@ -614,6 +658,7 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
         o = attend(outs[flk.K], outs[flk.V])
         rel = ((o - ref_out).abs().amax(dim=1) / ref_out.abs().amax(dim=1)).cpu().numpy()
         res["formats"][name] = {
+            "decode_attention_us": attn_us[name],
             "step_us": round(us, 2), "step_bytes": int(b_k + b_v), "gbs": round((b_k + b_v) / us / 1e3, 1),
             "stored_bytes": int(s_k + s_v),
             "bits_per_element": round(8 * (s_k + s_v) / (2 * sum((T if r is None else len(r)) for r in sets) * H * D), 4),

@@ -168,8 +168,8 @@ typedef struct flk_stream {
 void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
 /* Fill a descriptor for NVFP4 streams.  NVFP4 descriptors are accepted by flk_desc_check, the
- * size functions, flk_encode_base, flk_encode_residual, flk_reconstruct and
- * flk_reconstruct_mixed; every other entry point answers FLK_E_UNSUPPORTED. */
+ * size functions, flk_encode_base, flk_encode_residual, flk_reconstruct, flk_reconstruct_mixed
+ * and flk_decode_attn_mixed; every other entry point answers FLK_E_UNSUPPORTED. */
 void flk_desc_init_nvfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
 /* FLK_OK if the descriptor is well formed, else FLK_E_NULL / FLK_E_DESC / FLK_E_SHAPE. */
@@ -267,6 +267,21 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
                                   const flk_stream* v_chain, int32_t n_loops,
                                   float softmax_scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* flk_decode_attn_packed over chains whose streams are INT4 throughout, an INT4 base with NVFP4
+ * residual loops, or NVFP4 throughout (PR #166 review, item 2: the comparison that counts is
+ * speed and accuracy with dequantization and residual reconstruction fused into attention).
+ * The base loop of the K chain is described by kd_base, its residual loops by kd_resid; V
+ * likewise.  K and V must use the same combination; an NVFP4 base with INT4 residuals, and
+ * tile-grouped K with NVFP4 residuals, are FLK_E_UNSUPPORTED.  An NVFP4 value is the E2M1 code
+ * times the block's binary32 scale, rounded to BF16, as flk_reconstruct decodes it.
+ * Errors: those of flk_decode_attn_packed, plus FLK_E_DESC when a descriptor's kind is not the
+ * tensor's. */
+flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
+                                 const flk_desc* vd_resid, int32_t T, const void* q, int32_t n_q_heads,
+                                 const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
+                                 float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Appending whole tiles: the flush of a rolling BF16 tail (the RFC, section 3.3, last

@@ -311,6 +311,42 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
                                            static_cast<hipStream_t>(stream)));
 }
 
+flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
+                                 const flk_desc* vd_resid, int32_t T, const void* q, int32_t n_q_heads,
+                                 const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
+                                 float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  flk_status st;
+  for (const flk_desc* d : {kd_base, kd_resid, vd_base, vd_resid})
+    if ((st = flk_desc_check(d)) != FLK_OK) return st;
+  if (kd_base->kind != FLK_KIND_K || kd_resid->kind != FLK_KIND_K || vd_base->kind != FLK_KIND_V ||
+      vd_resid->kind != FLK_KIND_V)
+    return FLK_E_DESC;
+  for (const flk_desc* d : {kd_resid, vd_base, vd_resid})
+    if (d->n_heads != kd_base->n_heads || d->head_dim != kd_base->head_dim) return FLK_E_SHAPE;
+  // the format combination, the same for K and V: INT4 throughout, INT4 base + NVFP4
+  // residuals, NVFP4 throughout
+  const auto fmt_of = [](const flk_desc* b, const flk_desc* r) { return is_fp4(b) ? (is_fp4(r) ? 2 : -1) : (is_fp4(r) ? 1 : 0); };
+  const int fk = fmt_of(kd_base, kd_resid), fv = fmt_of(vd_base, vd_resid);
+  if (fk < 0 || fk != fv) return FLK_E_UNSUPPORTED;
+  if (fk == 0)
+    return flk_decode_attn_packed(kd_base, vd_base, T, q, n_q_heads, k_chain, v_chain, n_loops, softmax_scale, out,
+                                  workspace, workspace_bytes, stream);
+  if (kd_base->k_grouping != FLK_KGROUP_ROWS) return FLK_E_UNSUPPORTED;
+  if (!q || !out) return FLK_E_NULL;
+  if (T < 1 || !rows_fit(kd_base, T) || n_q_heads < 1 || n_q_heads % kd_base->n_heads != 0) return FLK_E_SHAPE;
+  if (kd_base->head_dim != 128 || n_q_heads / kd_base->n_heads > 16) return FLK_E_UNSUPPORTED;
+  flk::ChainArgs kc, vc;
+  if ((st = load_chain(kd_base, T, k_chain, n_loops, &kc)) != FLK_OK) return st;
+  if ((st = load_chain(vd_base, T, v_chain, n_loops, &vc)) != FLK_OK) return st;
+  if (!aligned(q, 16) || !aligned(out, 16)) return FLK_E_ALIGN;
+  const size_t need = flk::attn_workspace_need(T, 0, kd_base->n_heads, n_q_heads);
+  if (!workspace || workspace_bytes < need) return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 16)) return FLK_E_ALIGN;
+  return to_status(flk::launch_decode_attn_fmt(fk, T, kd_base->n_heads, n_q_heads, q, kc, vc, softmax_scale, out,
+                                               workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
 // ---- sparse decode attention ----------------------------------------------------------------
 
 namespace {

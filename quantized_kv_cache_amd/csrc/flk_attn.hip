@@ -81,6 +81,28 @@ __device__ __forceinline__ void decode_item(uint32_t cw, const uint32_t p[8], fl
   round_bf16x8_inplace(d);
 }
 
+// An NVFP4 item: 8 E2M1 codes times the block's scale bs = RN32(e4m3 * s_g), each product
+// rounded to BF16.  gfx950's v_cvt_scalef32_pk_f32_fp4 with a scale of 1 gives the exact E2M1
+// values (the codec's encoder relies on the same conversion).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void decode_item_fp4(uint32_t cw, float bs, float d[8]) {
+  f32x2_t v;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0); d[0] = v.x * bs; d[1] = v.y * bs;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1); d[2] = v.x * bs; d[3] = v.y * bs;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2); d[4] = v.x * bs; d[5] = v.y * bs;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3); d[6] = v.x * bs; d[7] = v.y * bs;
+  round_bf16x8_inplace(d);
+}
+__device__ __forceinline__ float e4m3_scale(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e == 0 ? float(m) * 0x1p-9f : __builtin_ldexpf(1.0f + float(m) * 0.125f, int(e) - 7);
+}
+
+// Stream formats of a chain: FMT 0 = INT4 throughout, 1 = INT4 base with NVFP4 residual
+// loops, 2 = NVFP4 throughout.
+template <int FMT>
+__device__ __forceinline__ constexpr bool loop_fp4(int l) { return FMT == 2 || (FMT == 1 && l > 0); }
+
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float v[8]) {
   *reinterpret_cast<uint4*>(dst) = pack_exact_bf16x8(v);
 }
@@ -157,11 +179,11 @@ __device__ __forceinline__ void build_maps(const ChainArgs& c, const TileRows<NL
 // 8 channels as packed BF16 (zeros for an absent or out-of-range token).  Every code word is
 // requested first; then one item at a time is decoded, so only one item's binary32 values
 // are live.  K: parameters from the staged rows; V: one parameter per item.
-template <int KIND, int NL>
+template <int KIND, int NL, int FMT = 0>
 __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<NL>& r, int32_t t0, int32_t T,
                                              int32_t H, int32_t h, int tk, const int oc[4],
                                              const int32_t (*map)[kGroup], const uint32_t (*kp)[2][kAttnD],
-                                             uint4 out[4]) {
+                                             const float (&sg)[NL], uint4 out[4]) {
   const int nl = c.n_loops;
   const int32_t t = t0 + tk;
   int32_t j[NL];
@@ -178,7 +200,10 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
         // uniform base + 32-bit offset: one saddr load, no 64-bit address arithmetic per lane
         const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
         cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (item * (kAttnD / 2) + uint32_t(oc[i]) * 4u));
-        if (KIND == FLK_KIND_V) vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
+        if (loop_fp4<FMT>(l))        // the block's E4M3 byte, after the 16-byte header
+          vp[l][i] = reinterpret_cast<const uint8_t*>(c.s[l].params)[16u + item * (kAttnD / 16) + uint32_t(oc[i] >> 1)];
+        else if (KIND == FLK_KIND_V)
+          vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
       }
     }
   }
@@ -190,6 +215,13 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
       if (j[l] < 0) continue;
+      float d[8];
+      if (loop_fp4<FMT>(l)) {
+        decode_item_fp4(cw[l][i], e4m3_scale(vp[l][i]) * sg[l], d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
+        continue;
+      }
       uint32_t p[8];
       if (KIND == FLK_KIND_K) {
         const int rg = c.ktile ? 0 : (j[l] / kGroup) & 1;  // staged by rowgroup parity
@@ -200,7 +232,6 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = vp[l][i];
       }
-      float d[8];
       decode_item(cw[l][i], p, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
@@ -211,7 +242,7 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
 
 // SC: also write every (query head, packed token) scaled score to scores[head][position], rows
 // of ceil(T/4)*4 floats (the reference loop of sparse decode attention selects keys from them).
-template <int NL, bool SC>
+template <int NL, bool SC, int FMT = 0>
 __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(ChainArgs kc, ChainArgs vc, int32_t T, int32_t H,
                                                               int32_t G, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ kt,
@@ -247,6 +278,15 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   int oc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oc[i] = 4 * i + kb;
+
+  // NVFP4 loops: the stream scales, loaded once (kept out of the tile loop, where their scalar
+  // loads would share a wait counter with the LDS reads of the K parameter rows)
+  float sgk[NL], sgv[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    sgk[l] = loop_fp4<FMT>(l) && l < kc.n_loops ? __uint_as_float(kc.s[l].params[0]) : 0.0f;
+    sgv[l] = loop_fp4<FMT>(l) && l < vc.n_loops ? __uint_as_float(vc.s[l].params[0]) : 0.0f;
+  }
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   float4_t o[8];
@@ -334,7 +374,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     // groups, the tile's own row in slot 0
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      if (l >= kc.n_loops) continue;
+      if (l >= kc.n_loops || loop_fp4<FMT>(l)) continue;    // NVFP4 loops carry no K parameter rows
       if (kc.ktile) {
         if (rk.hi[l] > rk.lo[l]) {
           const uint2 w = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(tile) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
@@ -384,9 +424,9 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
       const int tk = L.perm[16 * sl + n];
       // K_hat of the slice straight into the A operands
       uint4 item[4];
-      decode_items<FLK_KIND_K, NL>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, item);
+      decode_items<FLK_KIND_K, NL, FMT>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, sgk, item);
       attend_slice(item, sl, n_valid, [&](uint4 (&v)[4]) {
-        decode_items<FLK_KIND_V, NL>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, v);
+        decode_items<FLK_KIND_V, NL, FMT>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, sgv, v);
       }, [&](const float (&sc)[4]) {
         if constexpr (SC) {
           if (n < G) {
@@ -489,7 +529,7 @@ __global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int3
   }
 }
 
-template <bool SC>
+template <bool SC, int FMT = 0>
 static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
                               const ChainArgs& vc, const void* k_tail, const void* v_tail, int32_t tail_len,
                               float scale, void* out, float* out32, float* ml_out, float* scores, void* ws,
@@ -509,7 +549,7 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
 #define FLK_A(NLV)                                                                                          \
   case NLV:                                                                                                 \
-    hipLaunchKernelGGL((attn_wave_kernel<NLV, SC>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
+    hipLaunchKernelGGL((attn_wave_kernel<NLV, SC, FMT>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
                        ktp, vtp, tail_len, scale, wph, ws_ml, ws_o, scores);                                \
     break;
   switch (nl) {
@@ -531,6 +571,24 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
   (void)D;
   return launch_attn<false>(T, H, Hq, q, kc, vc, k_tail, v_tail, tail_len, scale, out, nullptr, nullptr, nullptr,
                             ws, ws_bytes, stream);
+}
+
+hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+                                  const ChainArgs& vc, float scale, void* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  switch (fmt) {
+    case 0:
+      return launch_attn<false, 0>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, nullptr, nullptr, nullptr, ws,
+                                   ws_bytes, stream);
+    case 1:
+      return launch_attn<false, 1>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, nullptr, nullptr, nullptr, ws,
+                                   ws_bytes, stream);
+    case 2:
+      return launch_attn<false, 2>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, nullptr, nullptr, nullptr, ws,
+                                   ws_bytes, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_reference(int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,

@@ -18,6 +18,12 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
                               const void* v_tail, int32_t tail_len, float scale, void* out,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Decode attention over packed chains whose streams are INT4 throughout (fmt 0), an INT4 base
+// with NVFP4 residual loops (fmt 1) or NVFP4 throughout (fmt 2), K and V alike; no tail.
+hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+                                  const ChainArgs& vc, float scale, void* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 // Full attention over the packed chains (no tail) that also writes every scaled score to
 // scores [Hq][T], the FP32 output to o_ref [Hq][128] and the softmax (max, denominator) to
 // ml [Hq][2]; out gets the BF16 output.

@@ -135,6 +135,8 @@ def lib() -> ctypes.CDLL:
         L.flk_desc_init_nvfp4.argtypes = [D, ctypes.c_int, i32, i32]
         L.flk_reconstruct_mixed.restype = ctypes.c_int
         L.flk_reconstruct_mixed.argtypes = [D, D, i32, S, i32, P, P]
+        L.flk_decode_attn_mixed.restype = ctypes.c_int
+        L.flk_decode_attn_mixed.argtypes = [D, D, D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P, sz, P]
         L.flk_select_count.restype = i32
         L.flk_select_count.argtypes = [i32, i32, P, i32]
         L.flk_select_workspace_bytes.restype = sz
@@ -324,6 +326,32 @@ def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequ
                                         Hq, ka, va, len(k_chain), float(softmax_scale), _ptr(out),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)), "flk_decode_attn_packed")
+
+
+def _chain_formats(chain: Sequence[Packed]):
+    base = chain[0].nvfp4
+    resid = {p.nvfp4 for p in chain[1:]}
+    if len(resid) > 1:
+        raise ValueError("the residual loops of one chain share one format")
+    return base, (resid.pop() if resid else base)
+
+
+def decode_attn_mixed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int,
+                      H: int, softmax_scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                      stream=None) -> None:
+    """Decode attention over chains of INT4 and NVFP4 streams (formats taken from the streams)."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    Hq, D = q.shape
+    kb, kr = _chain_formats(k_chain)
+    vb, vr = _chain_formats(v_chain)
+    ka, va = _chain(k_chain), _chain(v_chain)
+    _check(lib().flk_decode_attn_mixed(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles, kb)),
+                                       ctypes.byref(desc(K, H, D, nvfp4=kr)), ctypes.byref(desc(V, H, D, nvfp4=vb)),
+                                       ctypes.byref(desc(V, H, D, nvfp4=vr)), T, _ptr(q), Hq, ka, va, len(k_chain),
+                                       float(softmax_scale), _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+           "flk_decode_attn_mixed")
 
 
 # ----------------------------------------------------------------------------- rolling tail

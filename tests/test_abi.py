@@ -450,3 +450,25 @@ def test_reconstruct_mixed_validation():
     assert call(i4, f4, T=0) == 2
     assert call(i4, f4, n=0) == 2
     assert call(i4, f4, out=MIS) == 3
+
+
+def test_decode_attn_mixed_validation():
+    L = flk.lib()
+    S = flk.StreamC
+    T = 256
+    chain = (S * 2)(S(T, 0, None, FAKE.value, FAKE.value, None), S(T, 0, None, FAKE.value, FAKE.value, None))
+    ki4, kf4 = flk.desc(flk.K, 8, 128), flk.desc(flk.K, 8, 128, nvfp4=True)
+    vi4, vf4 = flk.desc(flk.V, 8, 128), flk.desc(flk.V, 8, 128, nvfp4=True)
+    ws = flk.attn_workspace_bytes(8, 128, T, 32)
+
+    def call(kb, kr, vb, vr, q=FAKE, hq=32, wb=ws):
+        return L.flk_decode_attn_mixed(ctypes.byref(kb), ctypes.byref(kr), ctypes.byref(vb), ctypes.byref(vr), T, q,
+                                       hq, chain, chain, 2, 0.088, FAKE, FAKE, wb, None)
+    assert call(vi4, kf4, vi4, vf4) == 4                        # a V descriptor for K
+    assert call(ki4, kf4, vi4, vi4) == 5                        # K and V formats differ
+    assert call(kf4, ki4, vf4, vi4) == 5                        # NVFP4 base, INT4 residuals
+    assert call(ki4, kf4, vi4, vf4, q=None) == 1
+    assert call(ki4, kf4, vi4, vf4, hq=30) == 2
+    assert call(ki4, kf4, vi4, vf4, wb=64) == 6
+    kt = flk.desc(flk.K, 8, 128, k_tiles=True)
+    assert call(kt, kf4, vi4, vf4) == 5                         # tile-grouped K with NVFP4 residuals

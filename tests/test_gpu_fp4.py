@@ -1,7 +1,10 @@
 """GPU parity for the NVFP4 codec variant (vllm-rlt PR #166, review item 2) through the C ABI:
 codes, params (header and E4M3 block scales), the tile index of compact loops, every loop's
 reconstruction and the reconstruction from the streams, bit for bit against the oracle, for
-NVFP4 chains and for an INT4 base with NVFP4 residuals."""
+NVFP4 chains and for an INT4 base with NVFP4 residuals; and decode attention fused over such
+chains against exact attention over the oracle's reconstructions (within 2e-2 per head)."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -157,3 +160,38 @@ def test_fp4_long_prompt_k_chain():
     for int4_base in (True, False):
         say(f"nvfp4 long prompt K int4_base={int4_base}")
         _compare(flk.K, c.xs, c.rows, int4_base, f"long prompt K int4_base={int4_base}")
+
+
+def _rel(got, ref):
+    return np.abs(got - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-30)
+
+
+@pytest.mark.parametrize("int4_base", [False, True])
+@pytest.mark.parametrize("T,H,Hq,sizes", [
+    (1000, 2, 8, [None, None, 500, 250]),
+    (700, 1, 16, [None, None, 0, None]),        # an empty loop dropped from the chain, then a dense one
+    (16384, 8, 32, [None, None, 8192, 4096]),   # 8 KV heads, 32 query heads
+])
+def test_fp4_decode_attention(T, H, Hq, sizes, int4_base):
+    """Fused decode attention over NVFP4 (or INT4 base + NVFP4 residual) chains against exact
+    attention over the oracle's reconstructions, within 2e-2 per query head."""
+    D = 128
+    rng = np.random.default_rng(T + H + int(int4_base))
+    xk, rows = _chain_inputs(rng, T, H, D, sizes, scale=2.0)
+    xv, _ = _chain_inputs(np.random.default_rng(T + 7), T, H, D, [None] * len(sizes))
+    xv = [xv[0]] + [x if r is None else np.ascontiguousarray(x[r]) for x, r in zip(xv[1:], rows[1:])]
+    say(f"nvfp4 attention T={T} H={H} Hq={Hq} int4_base={int4_base}")
+    kp, _, _ = _gpu_chain(flk.K, xk, rows, int4_base)
+    vp, _, _ = _gpu_chain(flk.V, xv, rows, int4_base)
+    q = synth.to_bf16_bits(rng.standard_normal((Hq, D)).astype(np.float32))
+    ws = torch.empty(flk.attn_workspace_bytes(H, D, T, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    flk.decode_attn_mixed(to_dev_bf16(q), kp, vp, T, H, scale, out, ws)
+    torch.cuda.synchronize()
+    _, ok = _oracle_chain(flk.K, xk, rows, int4_base)
+    _, ov = _oracle_chain(flk.V, xv, rows, int4_base)
+    ref = orc.decode_attn(q, ok[-1], ov[-1], scale)
+    rel = _rel(out.float().cpu().numpy(), ref)
+    say(f"  max rel err {rel.max():.2e}")
+    assert np.all(rel <= 2e-2), rel
