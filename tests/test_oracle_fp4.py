@@ -158,3 +158,145 @@ def test_chain_reconstructs_from_stored_bytes(int4_base):
     before = recon.copy()
     s = fp4.encode_residual(recon.copy(), None, recon)
     assert s.amax == 0 and np.array_equal(fp4.f32_of_bf16(recon), fp4.f32_of_bf16(before))
+
+
+def test_e2m1_code_against_brute_force():
+    """Each code is the grid value nearest to y (ties to the even magnitude index, i.e. the even
+    mantissa bit), searched over all 16 codes; magnitudes past 6 land on 6; values that round to
+    zero keep their sign."""
+    rng = np.random.default_rng(4)
+    grid = fp4.E2M1_VALUES
+    mids = (grid[1:] + grid[:-1]) / 2
+    y = np.concatenate([rng.uniform(-9, 9, 20000), mids, -mids, grid, -grid, [7.0, -7.0, 1e9]])
+    y = y.astype(np.float32).astype(np.float64)
+    got = fp4.e2m1_code(y)
+    vals = fp4.e2m1_value(np.arange(16))
+    for yi, ci in zip(y, got):
+        d = np.abs(vals - yi)
+        best = np.flatnonzero(d == d.min())
+        mags = {int(b) & 7 for b in best}
+        mag = min(mags) if len(mags) == 1 else [m for m in mags if m % 2 == 0][0]
+        assert int(ci) & 7 == mag, yi
+        assert (int(ci) >> 3) == (1 if np.signbit(yi) else 0), yi
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+def test_e8m0_grid_from_the_bit_layout():
+    """E8M0 is a bare biased exponent: byte b is 2^(b - 127), b = 0 .. 254."""
+    b = np.arange(255)
+    v = fp4.e8m0_value(b)
+    assert v[127] == 1.0 and v[0] == 2.0 ** -127 and v[254] == 2.0 ** 127
+    assert np.all(v[1:] / v[:-1] == 2.0)
+
+
+@pytest.mark.parametrize("amax,byte", [
+    (1.0, 125),            # floor(log2 1) = 0  -> X = 2^-2
+    (6.0, 127),            # floor(log2 6) = 2  -> X = 1: the block's largest value is 6 X
+    (7.0, 127),            # still X = 1: 7 clips to 6
+    (8.0, 128),            # floor(log2 8) = 3  -> X = 2
+    (0.75, 124),           # floor(log2 0.75) = -1 -> X = 2^-3
+    (3.999, 126),          # floor(log2 3.999) = 1 -> X = 2^-1: 3.999 / X = 7.998 clips to 6
+    (0.0, 0),              # a block of zeros: the smallest scale
+    (2.0 ** -130, 0),      # -132 clamps to -127
+    (1.5 * 2.0 ** 127, 252),
+])
+def test_mx_shared_exponent(amax, byte):
+    """OCP MX v1.0: X = 2^(floor(log2 amax) - 2), clamped to E8M0's range."""
+    assert int(fp4.mx_scale_bits(np.array([amax]))[0]) == byte
+
+
+def test_mx_worked_block():
+    """One block worked by hand: amax 7 gives X = 1; 7 and -6.5 clip to +-6, 0.25, 0.75, 2.5
+    and 5 are ties that go to the even mantissa (0, 1, 2, 4), -0.3 (BF16 -0.30078125) is nearer
+    -0.5 than -0; the same block times 2^-10 gives X = 2^-10 and the same codes."""
+    vals = [7.0, 1.0, -0.3, 0.25, 0.75, 2.5, 5.0, -6.5]
+    want_codes = [7, 2, 9, 0, 2, 4, 6, 15]
+    want_dec = [6.0, 1.0, -0.5, 0.0, 1.0, 2.0, 4.0, -6.0]
+    for k in (0, -10):
+        x = np.zeros((1, 1, 32), np.float32)
+        x[0, 0, :8] = np.array(vals, np.float32) * np.float32(2.0 ** k)
+        x = fp4.f32_of_bf16(fp4.bf16_of_f32(x))
+        codes, scales, dec = fp4.mx_encode_values(x)
+        assert int(scales[0, 0, 0]) == 127 + k
+        c4 = np.empty(32, np.uint8)
+        c4[0::2], c4[1::2] = codes[0, 0] & 15, codes[0, 0] >> 4
+        assert list(c4[:8]) == want_codes and not c4[8:].any()
+        assert list(dec[0, 0, :8]) == [v * 2.0 ** k for v in want_dec] and not dec[0, 0, 8:].any()
+
+
+def test_mx_storage_is_four_and_a_quarter_bits():
+    assert fp4.mx_stream_bits_per_element(8, 128, 32768) == 4.25
+
+
+def test_mx_error_bound_and_clipping():
+    """|x - x_hat| <= X * (half the E2M1 step at |x / X|) when |x / X| <= 6; above 6 the value
+    clips to 6 X and the error is below 2 X.  Every block's amax lies in [4 X, 8 X)."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((64, 4, 64)) * np.exp(rng.uniform(-6, 6, (64, 4, 1)))).astype(np.float32)
+    x = fp4.f32_of_bf16(fp4.bf16_of_f32(x))
+    codes, scales, dec = fp4.mx_encode_values(x)
+    X = np.repeat(fp4.e8m0_value(scales), 32, axis=-1)
+    y = np.abs(x / X)
+    amax = np.abs(x).reshape(64, 4, 2, 32).max(-1) / fp4.e8m0_value(scales)
+    assert np.all((amax >= 4) & (amax < 8))
+    err = np.abs(x.astype(np.float64) - dec)
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    inside = y <= 6
+    assert np.all(err[inside] <= X[inside] * step[inside] / 2)
+    assert np.all(err[~inside] == (y[~inside] - 6) * X[~inside]) and np.all(err[~inside] < 2 * X[~inside])
+    assert (~inside).any()                                          # clipping does occur
+
+
+def test_mx_symmetric_and_grid_round_trip():
+    rng = np.random.default_rng(6)
+    x = fp4.f32_of_bf16(fp4.bf16_of_f32(rng.standard_normal((5, 2, 64)).astype(np.float32)))
+    c1, s1, d1 = fp4.mx_encode_values(x)
+    c2, s2, d2 = fp4.mx_encode_values(-x)
+    assert np.array_equal(s1, s2) and np.array_equal(c1 ^ 0x88, c2) and np.array_equal(d1, -d2)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6, 6], np.float32)
+    for k in (-120, -3, 0, 5, 100):
+        g = np.tile(grid, 2).reshape(1, 1, 32) * np.float32(2.0 ** k)
+        *_, dec = fp4.mx_encode_values(g)
+        assert np.array_equal(dec, g)
+
+
+def test_mx_block_is_32_channels():
+    """An outlier changes the scale of its own 32-channel block only."""
+    x = np.tile(np.linspace(-1, 1, 32).astype(np.float32), 3).reshape(1, 1, 96)
+    x = fp4.f32_of_bf16(fp4.bf16_of_f32(x))
+    _, s0, d0 = fp4.mx_encode_values(x)
+    x[0, 0, 40] = 96.0
+    _, s1, d1 = fp4.mx_encode_values(x)
+    assert list(s0[0, 0] != s1[0, 0]) == [False, True, False]
+    assert np.array_equal(d0[0, 0, :32], d1[0, 0, :32]) and np.array_equal(d0[0, 0, 64:], d1[0, 0, 64:])
+
+
+@pytest.mark.parametrize("int4_base", [False, True])
+def test_mx_chain_reconstructs_from_stored_bytes(int4_base):
+    rng = np.random.default_rng(7)
+    T, H, D = 200, 3, 64
+    y = rng.standard_normal((T, H, D)).astype(np.float32)
+    xs, rows = [fp4.bf16_of_f32(y)], [None]
+    prev = np.arange(T, dtype=np.int32)
+    for n in [None, 100, 37]:
+        y = y + (0.05 * rng.standard_normal((T, H, D))).astype(np.float32)
+        if n is not None:
+            prev = np.sort(rng.choice(prev, n, replace=False)).astype(np.int32)
+        sel = None if n is None else prev
+        xb = fp4.bf16_of_f32(y)
+        xs.append(xb if sel is None else xb[sel])
+        rows.append(sel)
+    if int4_base:
+        _, recon = orc.encode_base(orc.V, xs[0])
+    else:
+        base, recon = fp4.encode_base(xs[0], mx=True)
+        assert isinstance(base, fp4.MxStream)
+        assert np.array_equal(fp4.bf16_of_f32(fp4.mx_decode_stream(base)), recon)
+    start = recon.copy()
+    streams = [fp4.encode_residual(x, r, recon, mx=True) for x, r in zip(xs[1:], rows[1:])]
+    assert all(isinstance(s, fp4.MxStream) for s in streams)
+    assert np.array_equal(fp4.apply_residuals(start, streams), recon)
+    # an MXFP4 residual step is closer to X_r than the base alone
+    x4 = fp4.f32_of_bf16(xs[-1])
+    assert np.abs(fp4.f32_of_bf16(recon[rows[-1]]) - x4).mean() < np.abs(fp4.f32_of_bf16(start[rows[-1]]) - x4).mean()
