@@ -92,8 +92,8 @@ typedef enum flk_status {
 /* Which tensor a stream encodes; it selects the group axis and is recorded in the
  * descriptor (the PR #166 review asks for format, axis and group size in the descriptor). */
 enum { FLK_KIND_K = 0, FLK_KIND_V = 1 };
-enum { FLK_FMT_INT4_AFFINE = 1, FLK_FMT_NVFP4 = 2 };
-enum { FLK_PARAM_FP16_MIN_SCALE = 1, FLK_PARAM_E4M3_BLOCK_F32_STREAM = 2 };
+enum { FLK_FMT_INT4_AFFINE = 1, FLK_FMT_NVFP4 = 2, FLK_FMT_MXFP4 = 3 };
+enum { FLK_PARAM_FP16_MIN_SCALE = 1, FLK_PARAM_E4M3_BLOCK_F32_STREAM = 2, FLK_PARAM_E8M0_BLOCK = 3 };
 enum { FLK_NIBBLE_LOW_EVEN = 1 };
 
 /* The NVFP4 variant (PR #166 review, item 2: E2M1 codes, one E4M3 scale per 16 elements and
@@ -113,6 +113,20 @@ enum { FLK_NIBBLE_LOW_EVEN = 1 };
  * +0.  Decoding gives RN32(e2m1 * bs), rounded to BF16.  The residual chain is the INT4 one:
  * residuals are rounded to BF16 before encoding and added in binary32, rounded to BF16. */
 #define FLK_FP4_BLOCK 16
+
+/* The MXFP4 variant (OCP Microscaling Formats specification v1.0, section 6: E2M1 elements
+ * sharing one E8M0 power-of-two scale per block of 32; the pages name NVFP4 only, and MX-scaled
+ * FP4 only as an instruction's name).  Descriptor: format FLK_FMT_MXFP4, group FLK_MX_BLOCK,
+ * param_dtype FLK_PARAM_E8M0_BLOCK, k_grouping FLK_KGROUP_ROWS, D % 32 == 0.  Blocks run along
+ * the 32 consecutive channels of one (row, head) for K and V alike.  Per stream of n rows:
+ *   codes   as NVFP4's: [n][H][D/2] bytes, low nibble = even channel, sign in bit 3
+ *   params  the E8M0 block scales [n][H][D/32] bytes, no header (flk_params_bytes = n*H*D/32)
+ * A block's scale is X = 2^e with e = floor(log2(amax_b)) - 2, clamped to [-127, 127] (-127 for
+ * a block of zeros); its byte is e + 127.  Each code is the E2M1 value nearest (ties to even) to
+ * x / X, saturated at 6 (amax_b / X lies in [4, 8), so values above 6 X are clipped); a value
+ * that rounds to zero keeps its sign.  Decoding gives e2m1 * X, exact in BF16.  4.25 bits per
+ * element.  The residual chain is the INT4 one. */
+#define FLK_MX_BLOCK 32
 
 /* Who owns a K group (the PR #166 review, item 3 "Group ownership vs 16-token pages": K
  * groups that follow compact-row order can put rows of distant positions, on different
@@ -138,10 +152,11 @@ enum { FLK_KGROUP_ROWS = 0, FLK_KGROUP_TILE = 1 };
  * depth representation travel with the data).  Fill with flk_desc_init(). */
 typedef struct flk_desc {
     uint16_t abi_version;   /* FLK_ABI_VERSION                                             */
-    uint8_t format;         /* FLK_FMT_INT4_AFFINE or FLK_FMT_NVFP4                        */
+    uint8_t format;         /* FLK_FMT_INT4_AFFINE, FLK_FMT_NVFP4 or FLK_FMT_MXFP4         */
     uint8_t kind;           /* FLK_KIND_K or FLK_KIND_V                                    */
-    uint16_t group;         /* FLK_GROUP (64) for INT4, FLK_FP4_BLOCK (16) for NVFP4       */
-    uint8_t param_dtype;    /* FLK_PARAM_FP16_MIN_SCALE (INT4), FLK_PARAM_E4M3_BLOCK_F32_STREAM */
+    uint16_t group;         /* FLK_GROUP (64) INT4, FLK_FP4_BLOCK (16) NVFP4, FLK_MX_BLOCK (32) MXFP4 */
+    uint8_t param_dtype;    /* FLK_PARAM_FP16_MIN_SCALE (INT4), FLK_PARAM_E4M3_BLOCK_F32_STREAM
+                               (NVFP4), FLK_PARAM_E8M0_BLOCK (MXFP4)                      */
     uint8_t nibble_order;   /* FLK_NIBBLE_LOW_EVEN                                         */
     int32_t n_heads;        /* H >= 1                                                      */
     int32_t head_dim;       /* D: 8 <= D <= FLK_MAX_HEAD_DIM, D % 8 == 0                   */
@@ -172,6 +187,9 @@ void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
  * and flk_decode_attn_mixed; every other entry point answers FLK_E_UNSUPPORTED. */
 void flk_desc_init_nvfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
+/* Fill a descriptor for MXFP4 streams; accepted by the same entry points as NVFP4's. */
+void flk_desc_init_mxfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
+
 /* FLK_OK if the descriptor is well formed, else FLK_E_NULL / FLK_E_DESC / FLK_E_SHAPE. */
 flk_status flk_desc_check(const flk_desc* d);
 
@@ -180,7 +198,7 @@ flk_status flk_desc_check(const flk_desc* d);
 size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows);   /* n*H*D/2                    */
 size_t flk_params_bytes(const flk_desc* d, int32_t n_rows, int32_t T); /* 4 * groups; T is
                                        the stream's positions (read for tile-grouped K only);
-                                       NVFP4: 16 + n*H*D/16                                 */
+                                       NVFP4: 16 + n*H*D/16; MXFP4: n*H*D/32               */
 size_t flk_rows_bytes(int32_t n_rows, int sparse);            /* 4*n if sparse, else 0      */
 size_t flk_tile_index_bytes(int32_t T);                       /* 4*(ceil(T/64) + 1)         */
 /* Everything one stream stores: codes + params + rows + tile index (sparse streams), with
@@ -244,9 +262,10 @@ flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain
                            int32_t n_loops, void* out, void* stream);
 
 /* flk_reconstruct for a chain whose base (chain[0]) is described by base_desc and whose
- * residual loops by resid_desc: an INT4 base with NVFP4 residuals (the PR #166 review's
- * "INT4 base plus NVFP4 residuals"), NVFP4 throughout, or INT4 throughout.  Both descriptors
- * must agree on kind, H and D.  An NVFP4 base with INT4 residuals is FLK_E_UNSUPPORTED.
+ * residual loops by resid_desc: an INT4 base with FP4 residuals (the PR #166 review's "INT4
+ * base plus NVFP4 residuals", and likewise with MXFP4), NVFP4 or MXFP4 throughout, or INT4
+ * throughout.  Both descriptors must agree on kind, H and D.  An FP4 base with INT4 residuals,
+ * and NVFP4 mixed with MXFP4, are FLK_E_UNSUPPORTED.
  * Errors: those of flk_reconstruct, plus FLK_E_DESC when the descriptors disagree. */
 flk_status flk_reconstruct_mixed(const flk_desc* base_desc, const flk_desc* resid_desc, int32_t T,
                                  const flk_stream* chain, int32_t n_loops, void* out, void* stream);
@@ -268,13 +287,14 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
                                   float softmax_scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-/* flk_decode_attn_packed over chains whose streams are INT4 throughout, an INT4 base with NVFP4
- * residual loops, or NVFP4 throughout (PR #166 review, item 2: the comparison that counts is
- * speed and accuracy with dequantization and residual reconstruction fused into attention).
- * The base loop of the K chain is described by kd_base, its residual loops by kd_resid; V
- * likewise.  K and V must use the same combination; an NVFP4 base with INT4 residuals, and
- * tile-grouped K with NVFP4 residuals, are FLK_E_UNSUPPORTED.  An NVFP4 value is the E2M1 code
- * times the block's binary32 scale, rounded to BF16, as flk_reconstruct decodes it.
+/* flk_decode_attn_packed over chains whose streams are INT4 throughout, an INT4 base with FP4
+ * residual loops, or FP4 throughout, the FP4 loops all NVFP4 or all MXFP4 (PR #166 review,
+ * item 2: the comparison that counts is speed and accuracy with dequantization and residual
+ * reconstruction fused into attention).  The base loop of the K chain is described by kd_base,
+ * its residual loops by kd_resid; V likewise.  K and V must use the same combination; an FP4
+ * base with INT4 residuals, NVFP4 mixed with MXFP4, and tile-grouped K with FP4 residuals are
+ * FLK_E_UNSUPPORTED.  An FP4 value is the E2M1 code times the block's binary32 scale, rounded
+ * to BF16, as flk_reconstruct decodes it.
  * Errors: those of flk_decode_attn_packed, plus FLK_E_DESC when a descriptor's kind is not the
  * tensor's. */
 flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,

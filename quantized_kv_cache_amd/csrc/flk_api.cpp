@@ -64,9 +64,10 @@ bool rows_fit(const flk_desc* d, int64_t n) {
 
 flk_status to_status(hipError_t e) { return e == hipSuccess ? FLK_OK : FLK_E_LAUNCH; }
 
-bool is_fp4(const flk_desc* d) { return d->format == FLK_FMT_NVFP4; }
+bool is_fp4(const flk_desc* d) { return d->format == FLK_FMT_NVFP4 || d->format == FLK_FMT_MXFP4; }
+bool is_mx(const flk_desc* d) { return d->format == FLK_FMT_MXFP4; }
 
-// The check of the entry points that implement INT4 streams only: a well-formed NVFP4
+// The check of the entry points that implement INT4 streams only: a well-formed FP4
 // descriptor is a valid request they do not implement.
 flk_status int4_desc(const flk_desc* d) {
   const flk_status st = flk_desc_check(d);
@@ -129,19 +130,30 @@ void flk_desc_init_nvfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_di
   d->param_dtype = FLK_PARAM_E4M3_BLOCK_F32_STREAM;
 }
 
+void flk_desc_init_mxfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim) {
+  flk_desc_init(d, kind, n_heads, head_dim);
+  if (!d) return;
+  d->format = FLK_FMT_MXFP4;
+  d->group = FLK_MX_BLOCK;
+  d->param_dtype = FLK_PARAM_E8M0_BLOCK;
+}
+
 flk_status flk_desc_check(const flk_desc* d) {
   if (!d) return FLK_E_NULL;
   const bool int4 = d->format == FLK_FMT_INT4_AFFINE && d->group == FLK_GROUP &&
                     d->param_dtype == FLK_PARAM_FP16_MIN_SCALE &&
                     (d->k_grouping == FLK_KGROUP_ROWS || d->k_grouping == FLK_KGROUP_TILE);
-  const bool fp4 = d->format == FLK_FMT_NVFP4 && d->group == FLK_FP4_BLOCK &&
-                   d->param_dtype == FLK_PARAM_E4M3_BLOCK_F32_STREAM && d->k_grouping == FLK_KGROUP_ROWS;
-  if (d->abi_version != FLK_ABI_VERSION || !(int4 || fp4) || (d->kind != FLK_KIND_K && d->kind != FLK_KIND_V) ||
+  const bool nv = d->format == FLK_FMT_NVFP4 && d->group == FLK_FP4_BLOCK &&
+                  d->param_dtype == FLK_PARAM_E4M3_BLOCK_F32_STREAM && d->k_grouping == FLK_KGROUP_ROWS;
+  const bool mx = d->format == FLK_FMT_MXFP4 && d->group == FLK_MX_BLOCK && d->param_dtype == FLK_PARAM_E8M0_BLOCK &&
+                  d->k_grouping == FLK_KGROUP_ROWS;
+  if (d->abi_version != FLK_ABI_VERSION || !(int4 || nv || mx) || (d->kind != FLK_KIND_K && d->kind != FLK_KIND_V) ||
       d->nibble_order != FLK_NIBBLE_LOW_EVEN || d->reserved[0] != 0 || d->reserved[1] != 0 || d->reserved[2] != 0)
     return FLK_E_DESC;
   if (d->n_heads < 1 || d->head_dim < 8 || d->head_dim > FLK_MAX_HEAD_DIM || d->head_dim % 8 != 0)
     return FLK_E_SHAPE;
-  if (fp4 && d->head_dim % FLK_FP4_BLOCK != 0) return FLK_E_SHAPE;
+  if (nv && d->head_dim % FLK_FP4_BLOCK != 0) return FLK_E_SHAPE;
+  if (mx && d->head_dim % FLK_MX_BLOCK != 0) return FLK_E_SHAPE;
   if (int64_t(d->n_heads) * d->head_dim > (int64_t(1) << 20)) return FLK_E_SHAPE;
   return FLK_OK;
 }
@@ -153,6 +165,8 @@ size_t flk_codes_bytes(const flk_desc* d, int32_t n_rows) {
 
 size_t flk_params_bytes(const flk_desc* d, int32_t n_rows, int32_t T) {
   if (flk_desc_check(d) != FLK_OK || n_rows < 0) return 0;
+  if (is_mx(d))                                   // one E8M0 byte per 32 elements
+    return size_t(n_rows) * size_t(d->n_heads) * size_t(d->head_dim) / FLK_MX_BLOCK;
   if (is_fp4(d))                                  // header, then one E4M3 byte per 16 elements
     return 16 + size_t(n_rows) * size_t(d->n_heads) * size_t(d->head_dim) / FLK_FP4_BLOCK;
   return 4 * n_groups(d, n_rows, T);
@@ -210,8 +224,8 @@ flk_status flk_encode_base(const flk_desc* d, const void* x, int32_t T, uint8_t*
   if (st != FLK_OK) return st;
   if (!aligned(x, 16) || !aligned(recon, 16) || (dev_status && !aligned(dev_status, 4))) return FLK_E_ALIGN;
   if (is_fp4(d))
-    return to_status(flk::launch_fp4_encode(false, x, nullptr, T, T, d->n_heads, d->head_dim, recon, codes, params,
-                                            nullptr, dev_status, static_cast<hipStream_t>(stream)));
+    return to_status(flk::launch_fp4_encode(false, is_mx(d), x, nullptr, T, T, d->n_heads, d->head_dim, recon, codes,
+                                            params, nullptr, dev_status, static_cast<hipStream_t>(stream)));
   return to_status(flk::launch_encode(d->kind, false,
                                       enc_args(d, x, nullptr, T, T, recon, codes, params, nullptr, dev_status),
                                       d->n_heads, d->head_dim, static_cast<hipStream_t>(stream)));
@@ -235,8 +249,8 @@ flk_status flk_encode_residual(const flk_desc* d, const void* x_rows, const int3
   if (!aligned(x_rows, 16) || (rows && (!aligned(rows, 4) || !aligned(tile_start, 4))))
     return FLK_E_ALIGN;
   if (is_fp4(d))
-    return to_status(flk::launch_fp4_encode(true, x_rows, rows, n_rows, T, d->n_heads, d->head_dim, recon, codes,
-                                            params, rows ? tile_start : nullptr, dev_status,
+    return to_status(flk::launch_fp4_encode(true, is_mx(d), x_rows, rows, n_rows, T, d->n_heads, d->head_dim, recon,
+                                            codes, params, rows ? tile_start : nullptr, dev_status,
                                             static_cast<hipStream_t>(stream)));
   return to_status(flk::launch_encode(d->kind, true,
                                       enc_args(d, x_rows, rows, n_rows, T, recon, codes, params, tile_start,
@@ -255,7 +269,7 @@ flk_status flk_reconstruct(const flk_desc* d, int32_t T, const flk_stream* chain
   if (st != FLK_OK) return st;
   if (!aligned(out, 16)) return FLK_E_ALIGN;
   if (is_fp4(d))
-    return to_status(flk::launch_fp4_reconstruct(ca, true, d->kind, T, d->n_heads, d->head_dim, out,
+    return to_status(flk::launch_fp4_reconstruct(ca, true, is_mx(d), d->kind, T, d->n_heads, d->head_dim, out,
                                                  static_cast<hipStream_t>(stream)));
   return to_status(flk::launch_reconstruct(d->kind, T, d->n_heads, d->head_dim, ca, out,
                                            static_cast<hipStream_t>(stream)));
@@ -268,17 +282,17 @@ flk_status flk_reconstruct_mixed(const flk_desc* bd, const flk_desc* rd, int32_t
   if ((st = flk_desc_check(rd)) != FLK_OK) return st;
   if (bd->kind != rd->kind || bd->n_heads != rd->n_heads || bd->head_dim != rd->head_dim) return FLK_E_DESC;
   if (!is_fp4(rd)) {
-    if (is_fp4(bd)) return FLK_E_UNSUPPORTED;                 // NVFP4 base, INT4 residuals
+    if (is_fp4(bd)) return FLK_E_UNSUPPORTED;                 // FP4 base, INT4 residuals
     return flk_reconstruct(bd, T, chain, n_loops, out, stream);
   }
+  if (is_fp4(bd) && bd->format != rd->format) return FLK_E_UNSUPPORTED;   // NVFP4 with MXFP4
   if (!out) return FLK_E_NULL;
   if (T < 1 || !rows_fit(bd, T)) return FLK_E_SHAPE;
-  if (rd->head_dim % FLK_FP4_BLOCK != 0) return FLK_E_SHAPE;
   flk::ChainArgs ca;
   st = load_chain(bd, T, chain, n_loops, &ca);
   if (st != FLK_OK) return st;
   if (!aligned(out, 16)) return FLK_E_ALIGN;
-  return to_status(flk::launch_fp4_reconstruct(ca, is_fp4(bd), bd->kind, T, bd->n_heads, bd->head_dim, out,
+  return to_status(flk::launch_fp4_reconstruct(ca, is_fp4(bd), is_mx(rd), bd->kind, T, bd->n_heads, bd->head_dim, out,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -324,9 +338,13 @@ flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_res
     return FLK_E_DESC;
   for (const flk_desc* d : {kd_resid, vd_base, vd_resid})
     if (d->n_heads != kd_base->n_heads || d->head_dim != kd_base->head_dim) return FLK_E_SHAPE;
-  // the format combination, the same for K and V: INT4 throughout, INT4 base + NVFP4
-  // residuals, NVFP4 throughout
-  const auto fmt_of = [](const flk_desc* b, const flk_desc* r) { return is_fp4(b) ? (is_fp4(r) ? 2 : -1) : (is_fp4(r) ? 1 : 0); };
+  // the format combination, the same for K and V: INT4 throughout (0), INT4 base + NVFP4
+  // residuals (1), NVFP4 throughout (2), INT4 base + MXFP4 residuals (3), MXFP4 throughout (4)
+  const auto fmt_of = [](const flk_desc* b, const flk_desc* r) {
+    if (!is_fp4(r)) return is_fp4(b) ? -1 : 0;
+    if (is_fp4(b) && b->format != r->format) return -1;
+    return (is_mx(r) ? 3 : 1) + (is_fp4(b) ? 1 : 0);
+  };
   const int fk = fmt_of(kd_base, kd_resid), fv = fmt_of(vd_base, vd_resid);
   if (fk < 0 || fk != fv) return FLK_E_UNSUPPORTED;
   if (fk == 0)

@@ -98,10 +98,17 @@ __device__ __forceinline__ float e4m3_scale(uint32_t b) {
   return e == 0 ? float(m) * 0x1p-9f : __builtin_ldexpf(1.0f + float(m) * 0.125f, int(e) - 7);
 }
 
+// E8M0 byte b (an MXFP4 block scale) -> 2^(b - 127); byte 0 is 2^-127, a binary32 subnormal.
+__device__ __forceinline__ float e8m0_scale(uint32_t b) { return __uint_as_float(b != 0u ? b << 23 : 0x00400000u); }
+
 // Stream formats of a chain: FMT 0 = INT4 throughout, 1 = INT4 base with NVFP4 residual
-// loops, 2 = NVFP4 throughout.
+// loops, 2 = NVFP4 throughout, 3 = INT4 base with MXFP4 residual loops, 4 = MXFP4 throughout.
 template <int FMT>
-__device__ __forceinline__ constexpr bool loop_fp4(int l) { return FMT == 2 || (FMT == 1 && l > 0); }
+__device__ __forceinline__ constexpr bool loop_nv(int l) { return FMT == 2 || (FMT == 1 && l > 0); }
+template <int FMT>
+__device__ __forceinline__ constexpr bool loop_mx(int l) { return FMT == 4 || (FMT == 3 && l > 0); }
+template <int FMT>
+__device__ __forceinline__ constexpr bool loop_fp4(int l) { return loop_nv<FMT>(l) || loop_mx<FMT>(l); }
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float v[8]) {
   *reinterpret_cast<uint4*>(dst) = pack_exact_bf16x8(v);
@@ -200,7 +207,9 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
         // uniform base + 32-bit offset: one saddr load, no 64-bit address arithmetic per lane
         const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
         cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (item * (kAttnD / 2) + uint32_t(oc[i]) * 4u));
-        if (loop_fp4<FMT>(l))        // the block's E4M3 byte, after the 16-byte header
+        if (loop_mx<FMT>(l))         // the 32-channel block's E8M0 byte
+          vp[l][i] = reinterpret_cast<const uint8_t*>(c.s[l].params)[item * (kAttnD / 32) + uint32_t(oc[i] >> 2)];
+        else if (loop_nv<FMT>(l))    // the 16-channel block's E4M3 byte, after the 16-byte header
           vp[l][i] = reinterpret_cast<const uint8_t*>(c.s[l].params)[16u + item * (kAttnD / 16) + uint32_t(oc[i] >> 1)];
         else if (KIND == FLK_KIND_V)
           vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
@@ -217,7 +226,7 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
       if (j[l] < 0) continue;
       float d[8];
       if (loop_fp4<FMT>(l)) {
-        decode_item_fp4(cw[l][i], e4m3_scale(vp[l][i]) * sg[l], d);
+        decode_item_fp4(cw[l][i], loop_mx<FMT>(l) ? e8m0_scale(vp[l][i]) : e4m3_scale(vp[l][i]) * sg[l], d);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
         continue;
@@ -284,8 +293,8 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   float sgk[NL], sgv[NL];
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
-    sgk[l] = loop_fp4<FMT>(l) && l < kc.n_loops ? __uint_as_float(kc.s[l].params[0]) : 0.0f;
-    sgv[l] = loop_fp4<FMT>(l) && l < vc.n_loops ? __uint_as_float(vc.s[l].params[0]) : 0.0f;
+    sgk[l] = loop_nv<FMT>(l) && l < kc.n_loops ? __uint_as_float(kc.s[l].params[0]) : 0.0f;
+    sgv[l] = loop_nv<FMT>(l) && l < vc.n_loops ? __uint_as_float(vc.s[l].params[0]) : 0.0f;
   }
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     // groups, the tile's own row in slot 0
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      if (l >= kc.n_loops || loop_fp4<FMT>(l)) continue;    // NVFP4 loops carry no K parameter rows
+      if (l >= kc.n_loops || loop_fp4<FMT>(l)) continue;    // FP4 loops carry no K parameter rows
       if (kc.ktile) {
         if (rk.hi[l] > rk.lo[l]) {
           const uint2 w = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(tile) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
@@ -585,6 +594,12 @@ hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, con
                                    ws_bytes, stream);
     case 2:
       return launch_attn<false, 2>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, nullptr, nullptr, nullptr, ws,
+                                   ws_bytes, stream);
+    case 3:
+      return launch_attn<false, 3>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, nullptr, nullptr, nullptr, ws,
+                                   ws_bytes, stream);
+    case 4:
+      return launch_attn<false, 4>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, nullptr, nullptr, nullptr, ws,
                                    ws_bytes, stream);
     default:
       return hipErrorInvalidValue;

@@ -1,18 +1,23 @@
-// flk_fp4.hip -- the NVFP4 variant of the codec (vllm-rlt pull request #166, review item 2:
-// E2M1 codes, one E4M3 scale per 16 elements, one FP32 scale per tensor; an INT4 base with
-// NVFP4 residuals allowed), on the residual chain of the FlashLoop RFC (section 3.3).
+// flk_fp4.hip -- the FP4 variants of the codec on the residual chain of the FlashLoop RFC
+// (section 3.3): NVFP4 (vllm-rlt pull request #166, review item 2: E2M1 codes, one E4M3 scale
+// per 16 elements, one FP32 scale per tensor; an INT4 base with NVFP4 residuals allowed) and
+// MXFP4 (OCP Microscaling Formats v1.0, section 6: E2M1 codes, one E8M0 power-of-two scale per
+// 32 elements, no tensor scale).
 //
-//   fp4_amax_kernel<RESID>   per-block maxima of the stream's magnitudes (X, or the BF16 residual
-//                            against the reconstruction), parked in the stream's codes buffer,
-//                            which the encoder overwrites afterwards
-//   fp4_amax_fold_kernel     their maximum into the params header
-//   fp4_encode_kernel<RESID> one thread per 16-channel block: block scale, codes, the decoded
-//                            values into the reconstruction, and (compact loops) the tile index
-//   fp4_reconstruct_kernel   X_hat from a chain whose base is INT4 or NVFP4 and whose residual
-//                            loops are NVFP4; a block per (64-position tile, slice of blocks)
+//   fp4_amax_kernel<RESID>       NVFP4: per-block maxima of the stream's magnitudes (X, or the
+//                                BF16 residual against the reconstruction), parked in the
+//                                stream's codes buffer, which the encoder overwrites afterwards
+//   fp4_amax_fold_kernel         NVFP4: their maximum into the params header
+//   fp4_encode_kernel<RESID, MX> lanes own 8 channels of a 16-channel (NVFP4) or 32-channel
+//                                (MXFP4) block: block scale, codes, the decoded values into the
+//                                reconstruction, and (compact loops) the tile index
+//   fp4_reconstruct_kernel       X_hat from a chain whose base is INT4 or FP4 and whose residual
+//                                loops are FP4 of one kind; a block per (64-position tile,
+//                                slice of 16-channel items)
 //
 // Element formats: E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7, sign in bit 3);
-// E4M3 bias 7, subnormal below 2^-6 (steps of 2^-9), largest finite 448.
+// E4M3 bias 7, subnormal below 2^-6 (steps of 2^-9), largest finite 448; E8M0 a bare biased
+// exponent, byte b = 2^(b - 127).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -124,6 +129,38 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t cw, float bs, float dec[8]
   }
 }
 
+// E8M0 byte b -> 2^(b - 127); byte 0 is 2^-127, a binary32 subnormal.
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return __uint_as_float(b != 0u ? b << 23 : 0x00400000u);
+}
+
+// MXFP4 shared scale of a block from its largest magnitude: floor(log2 amax) - 2 (E2M1's
+// largest power of two is 2^2), clamped to E8M0's smallest exponent -127; the biased byte is
+// the exponent field of amax less 2, or 0 (amax zero, subnormal, or below 2^-124).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;
+  return ef > 2u ? ef - 2u : 0u;
+}
+
+// Codes of 8 values against an MXFP4 block scale 2^(byte - 127), and their decoded values.
+// The quotient x / X is x times the power of two 2^(127 - byte) (a normal binary32 for every
+// byte up to 252), exact except where it falls below 2^-126, far under the smallest E2M1
+// rounding boundary 0.25, where the code is a signed zero either way.
+__device__ __forceinline__ uint32_t mx_encode8(const float v[8], uint32_t byte, float dec[8]) {
+  const float inv = __uint_as_float((254u - byte) << 23);
+  const float X = e8m0_value(byte);
+  uint32_t cw = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cw = cvt_pair(cw, v[2 * k] * inv, v[2 * k + 1] * inv, k);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 d = uncvt_pair(cw, k);
+    dec[2 * k] = d.x * X;
+    dec[2 * k + 1] = d.y * X;
+  }
+  return cw;
+}
+
 // Stream scale from the stream's largest magnitude.
 __device__ __forceinline__ float stream_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 2688.0f; }
 
@@ -215,19 +252,23 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_amax_fold_kernel(const float*
 
 // ---- encode ----------------------------------------------------------------------------------
 
-// Lane pairs own a 16-channel block: lane 2m holds its channels 0..7, lane 2m+1 channels
-// 8..15 (16 coalesced bytes per lane and tensor), the pair takes the block's amax with one
-// shuffle, and each lane writes its 4 bytes of codes and 16 bytes of reconstruction.
-template <bool RESID>
+// NVFP4: lane pairs own a 16-channel block: lane 2m holds its channels 0..7, lane 2m+1
+// channels 8..15 (16 coalesced bytes per lane and tensor), and the pair takes the block's amax
+// with one shuffle.  MXFP4: lane quads own a 32-channel block, two shuffles.  Each lane writes
+// its 4 bytes of codes and 16 bytes of reconstruction; the block's first lane its scale byte.
+// The NVFP4 amax pass reports non-finite inputs; the MXFP4 encoder, which has no such pass,
+// checks them itself.
+template <bool RESID, bool MX>
 __global__ __launch_bounds__(kFp4Threads) void fp4_encode_kernel(const uint16_t* __restrict__ x,
                                                                   const int32_t* __restrict__ rows,
                                                                   uint16_t* __restrict__ recon, int32_t n, int32_t T,
                                                                   int32_t W, uint8_t* __restrict__ codes,
                                                                   uint32_t* __restrict__ params,
-                                                                  int32_t* __restrict__ tile_start) {
+                                                                  int32_t* __restrict__ tile_start,
+                                                                  uint32_t* __restrict__ status) {
   const int64_t c = int64_t(blockIdx.x) * kFp4Threads + threadIdx.x;    // 8-element chunk
-  const float s_g = stream_scale(__uint_as_float(params[1]));
-  if (c == 0) {
+  const float s_g = MX ? 1.0f : stream_scale(__uint_as_float(params[1]));
+  if (!MX && c == 0) {
     params[0] = __float_as_uint(s_g);
     params[2] = 0u;
     params[3] = 0u;
@@ -269,20 +310,31 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_encode_kernel(const uint16_t*
 #pragma unroll
   for (int e = 0; e < 8; ++e) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(v[e]));
   amax_b = __builtin_fmaxf(amax_b, __shfl_xor(amax_b, 1));
+  if (MX) amax_b = __builtin_fmaxf(amax_b, __shfl_xor(amax_b, 2));
   if (!live) return;
-  uint32_t sbyte;
-  const float e4 = e4m3_round(amax_b / (6.0f * s_g), sbyte);
-  const float bs = e4 * s_g;
   uint32_t cw = 0u;
   float dec[8];
-  if (bs > 0.0f) {
-    cw = e2m1_encode8(v, bs, dec);
-  } else {                                             // a block whose scale is 0: codes +0
+  if (MX) {
+    bool bad = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dec[e] = 0.0f;
+    for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(v[e]);
+    if (bad && status) atomicOr(status, FLK_DEV_NONFINITE);
+    const uint32_t sbyte = mx_scale_byte(amax_b);
+    cw = mx_encode8(v, sbyte, dec);
+    if ((c & 3) == 0) reinterpret_cast<uint8_t*>(params)[c >> 2] = uint8_t(sbyte);
+  } else {
+    uint32_t sbyte;
+    const float e4 = e4m3_round(amax_b / (6.0f * s_g), sbyte);
+    const float bs = e4 * s_g;
+    if (bs > 0.0f) {
+      cw = e2m1_encode8(v, bs, dec);
+    } else {                                           // a block whose scale is 0: codes +0
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dec[e] = 0.0f;
+    }
+    if ((c & 1) == 0) reinterpret_cast<uint8_t*>(params)[16 + (c >> 1)] = uint8_t(sbyte);
   }
   *reinterpret_cast<uint32_t*>(codes + 4 * c) = cw;
-  if ((c & 1) == 0) reinterpret_cast<uint8_t*>(params)[16 + (c >> 1)] = uint8_t(sbyte);
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -296,12 +348,22 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_encode_kernel(const uint16_t*
 
 // ---- reconstruct (mixed chains) -------------------------------------------------------------
 
+// The binary32 scale of the FP4 block holding element offset off (in [n, H, D]) of a stream:
+// MXFP4 its E8M0 byte, at off / 32; NVFP4 its E4M3 byte (after the 16-byte header, at 16 +
+// off / 16) times the stream scale.
+__device__ __forceinline__ float fp4_block_scale(const uint32_t* params, int64_t off, bool mx) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(params);
+  if (mx) return e8m0_value(b[off / 32]);
+  return e4m3_value(b[16 + off / 16]) * __uint_as_float(params[0]);
+}
+
 // Block (tile, part): items part*1024 .. of the tile, item = (position in tile, 16-channel
-// block of the row); thread tid takes items part*1024 + k*256 + tid, k < 4, so consecutive
+// piece of the row); thread tid takes items part*1024 + k*256 + tid, k < 4, so consecutive
 // threads write consecutive 32-byte pieces of a row.  Compact loops map the tile's positions
-// to their compact rows through an LDS table built from the tile index.
-__global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs c, int32_t base_fp4, int32_t kind,
-                                                                       int32_t T, int32_t H, int32_t D,
+// to their compact rows through an LDS table built from the tile index.  mx: the FP4 loops
+// are MXFP4, else NVFP4.
+__global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs c, int32_t base_fp4, int32_t mx,
+                                                                       int32_t kind, int32_t T, int32_t H, int32_t D,
                                                                        uint16_t* __restrict__ out) {
   __shared__ int32_t lmap[FLK_MAX_LOOPS][kGroup];
   const int32_t tile = blockIdx.x;
@@ -336,8 +398,7 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
     const uint2 bc = *reinterpret_cast<const uint2*>(b.codes + off / 2);
     const uint32_t bw[2] = {bc.x, bc.y};
     if (base_fp4) {
-      const float s_g = __uint_as_float(b.params[0]);
-      const float bs = e4m3_value(reinterpret_cast<const uint8_t*>(b.params)[16 + int64_t(p) * bpr + blk]) * s_g;
+      const float bs = fp4_block_scale(b.params, off, mx != 0);
       e2m1_decode8(bw[0], bs, x);
       e2m1_decode8(bw[1], bs, x + 8);
 #pragma unroll
@@ -368,8 +429,7 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
       const int64_t roff = int64_t(j) * W + int64_t(h) * D + c0;
       const uint2 rc = *reinterpret_cast<const uint2*>(s.codes + roff / 2);
       const uint32_t rw[2] = {rc.x, rc.y};
-      const float s_g = __uint_as_float(s.params[0]);
-      const float bs = e4m3_value(reinterpret_cast<const uint8_t*>(s.params)[16 + int64_t(j) * bpr + blk]) * s_g;
+      const float bs = fp4_block_scale(s.params, roff, mx != 0);
       float d[16];
       e2m1_decode8(rw[0], bs, d);
       e2m1_decode8(rw[1], bs, d + 8);
@@ -384,43 +444,52 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
 
 }  // namespace
 
-hipError_t launch_fp4_encode(bool resid, const void* x, const int32_t* rows, int32_t n, int32_t T, int32_t H,
-                             int32_t D, void* recon, uint8_t* codes, uint32_t* params, int32_t* tile_start,
-                             uint32_t* status, hipStream_t stream) {
+hipError_t launch_fp4_encode(bool resid, bool mx, const void* x, const int32_t* rows, int32_t n, int32_t T,
+                             int32_t H, int32_t D, void* recon, uint8_t* codes, uint32_t* params,
+                             int32_t* tile_start, uint32_t* status, hipStream_t stream) {
   const int32_t W = H * D;
-  if (D % 16 != 0 || n < 1) return hipErrorInvalidValue;
+  if (D % (mx ? 32 : 16) != 0 || n < 1) return hipErrorInvalidValue;
   const int64_t chunks = int64_t(n) * W / 8;
+  const auto* xs = static_cast<const uint16_t*>(x);
+  auto* rc = static_cast<uint16_t*>(recon);
+  const unsigned eb = unsigned((chunks + kFp4Threads - 1) / kFp4Threads);
+  if (mx) {                                            // block scales need no stream pass
+    if (resid)
+      hipLaunchKernelGGL((fp4_encode_kernel<true, true>), dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n, T,
+                         W, codes, params, tile_start, status);
+    else
+      hipLaunchKernelGGL((fp4_encode_kernel<false, true>), dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n,
+                         T, W, codes, params, tile_start, status);
+    return hipGetLastError();
+  }
   // one partial maximum per amax block, parked in the codes buffer (n*W/2 bytes, room for
   // `chunks` floats), which the encode kernel overwrites after the fold has read it
   const unsigned ab = unsigned(std::min<int64_t>(kAmaxBlocks, (chunks + kFp4Threads - 1) / kFp4Threads));
   float* partial = reinterpret_cast<float*>(codes);
-  const auto* xs = static_cast<const uint16_t*>(x);
-  auto* rc = static_cast<uint16_t*>(recon);
-  const unsigned eb = unsigned((int64_t(n) * (W / 8) + kFp4Threads - 1) / kFp4Threads);
   if (resid) {
     hipLaunchKernelGGL(fp4_amax_kernel<true>, dim3(ab), dim3(kFp4Threads), 0, stream, xs, rows, rc, chunks, W,
                        partial, status);
     hipLaunchKernelGGL(fp4_amax_fold_kernel, dim3(1), dim3(kFp4Threads), 0, stream, partial, int32_t(ab), params);
-    hipLaunchKernelGGL(fp4_encode_kernel<true>, dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n, T, W,
-                       codes, params, tile_start);
+    hipLaunchKernelGGL((fp4_encode_kernel<true, false>), dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n, T,
+                       W, codes, params, tile_start, nullptr);
   } else {
     hipLaunchKernelGGL(fp4_amax_kernel<false>, dim3(ab), dim3(kFp4Threads), 0, stream, xs, rows, rc, chunks, W,
                        partial, status);
     hipLaunchKernelGGL(fp4_amax_fold_kernel, dim3(1), dim3(kFp4Threads), 0, stream, partial, int32_t(ab), params);
-    hipLaunchKernelGGL(fp4_encode_kernel<false>, dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n, T, W,
-                       codes, params, tile_start);
+    hipLaunchKernelGGL((fp4_encode_kernel<false, false>), dim3(eb), dim3(kFp4Threads), 0, stream, xs, rows, rc, n,
+                       T, W, codes, params, tile_start, nullptr);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fp4_reconstruct(const ChainArgs& chain, bool base_fp4, int kind, int32_t T, int32_t H, int32_t D,
-                                  void* out, hipStream_t stream) {
-  if (D % 16 != 0 || chain.n_loops < 1) return hipErrorInvalidValue;
+hipError_t launch_fp4_reconstruct(const ChainArgs& chain, bool base_fp4, bool mx, int kind, int32_t T, int32_t H,
+                                  int32_t D, void* out, hipStream_t stream) {
+  if (D % (mx ? 32 : 16) != 0 || chain.n_loops < 1) return hipErrorInvalidValue;
   const int32_t items = kGroup * (H * D / 16);
   const unsigned parts = unsigned((items + kRecItemsPerThread * kFp4Threads - 1) / (kRecItemsPerThread * kFp4Threads));
   const dim3 grid(unsigned((T + kGroup - 1) / kGroup), parts);
-  hipLaunchKernelGGL(fp4_reconstruct_kernel, grid, dim3(kFp4Threads), 0, stream, chain, base_fp4 ? 1 : 0, kind, T,
-                     H, D, static_cast<uint16_t*>(out));
+  hipLaunchKernelGGL(fp4_reconstruct_kernel, grid, dim3(kFp4Threads), 0, stream, chain, base_fp4 ? 1 : 0, mx ? 1 : 0,
+                     kind, T, H, D, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Decode attention over packed chains whose streams are INT4 throughout (fmt 0), an INT4 base
-// with NVFP4 residual loops (fmt 1) or NVFP4 throughout (fmt 2), K and V alike; no tail.
+// with NVFP4 residual loops (fmt 1), NVFP4 throughout (fmt 2), an INT4 base with MXFP4 residual
+// loops (fmt 3) or MXFP4 throughout (fmt 4), K and V alike; no tail.
 hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
                                   const ChainArgs& vc, float scale, void* out, void* ws, size_t ws_bytes,
                                   hipStream_t stream);

@@ -131,8 +131,10 @@ def lib() -> ctypes.CDLL:
                                                 sz, P]
         L.flk_sparse_attn_loop.restype = ctypes.c_int
         L.flk_sparse_attn_loop.argtypes = [D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P, P, P, sz, P]
-        L.flk_desc_init_nvfp4.restype = None
-        L.flk_desc_init_nvfp4.argtypes = [D, ctypes.c_int, i32, i32]
+        for name in ("flk_desc_init_nvfp4", "flk_desc_init_mxfp4"):
+            f = getattr(L, name)
+            f.restype = None
+            f.argtypes = [D, ctypes.c_int, i32, i32]
         L.flk_reconstruct_mixed.restype = ctypes.c_int
         L.flk_reconstruct_mixed.argtypes = [D, D, i32, S, i32, P, P]
         L.flk_decode_attn_mixed.restype = ctypes.c_int
@@ -151,12 +153,28 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def desc(kind: int, H: int, D: int, k_tiles: bool = False, nvfp4: bool = False) -> Desc:
+INT4, NVFP4, MXFP4 = "int4", "nvfp4", "mxfp4"
+FORMATS = (INT4, NVFP4, MXFP4)
+
+
+def _fmt(nvfp4: bool, fmt: Optional[str]) -> str:
+    """The stream format from the nvfp4 flag or the format name (int4, nvfp4, mxfp4)."""
+    if fmt is None:
+        return NVFP4 if nvfp4 else INT4
+    if fmt not in FORMATS or (nvfp4 and fmt != NVFP4):
+        raise ValueError(f"unknown or conflicting stream format {fmt!r} (nvfp4={nvfp4})")
+    return fmt
+
+
+def desc(kind: int, H: int, D: int, k_tiles: bool = False, nvfp4: bool = False, fmt: Optional[str] = None) -> Desc:
     """k_tiles: K groups per 64-position tile (page-local) instead of per 64 compact rows;
-    nvfp4: the NVFP4 format (E2M1 codes, E4M3 scales per 16 channels, one FP32 stream scale)."""
+    fmt (or nvfp4=True): NVFP4 (E2M1 codes, E4M3 scales per 16 channels, one FP32 stream
+    scale) or MXFP4 (E2M1 codes, E8M0 scales per 32 channels) instead of INT4."""
+    f = _fmt(nvfp4, fmt)
     d = Desc()
-    if nvfp4:
-        lib().flk_desc_init_nvfp4(ctypes.byref(d), kind, H, D)
+    if f != INT4:
+        init = lib().flk_desc_init_nvfp4 if f == NVFP4 else lib().flk_desc_init_mxfp4
+        init(ctypes.byref(d), kind, H, D)
         return d
     lib().flk_desc_init(ctypes.byref(d), kind, H, D)
     d.k_grouping = KGROUP_TILE if k_tiles else KGROUP_ROWS
@@ -189,13 +207,15 @@ def codes_bytes(kind: int, H: int, D: int, n: int) -> int:
     return int(lib().flk_codes_bytes(ctypes.byref(desc(kind, H, D)), n))
 
 
-def params_bytes(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = False, nvfp4: bool = False) -> int:
-    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D, k_tiles, nvfp4)), n, T))
+def params_bytes(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = False, nvfp4: bool = False,
+                 fmt: Optional[str] = None) -> int:
+    return int(lib().flk_params_bytes(ctypes.byref(desc(kind, H, D, k_tiles, nvfp4, fmt)), n, T))
 
 
 def stream_bytes(kind: int, H: int, D: int, n: int, T: int, sparse: bool, k_tiles: bool = False,
-                 nvfp4: bool = False) -> int:
-    return int(lib().flk_stream_bytes(ctypes.byref(desc(kind, H, D, k_tiles, nvfp4)), n, T, 1 if sparse else 0))
+                 nvfp4: bool = False, fmt: Optional[str] = None) -> int:
+    return int(lib().flk_stream_bytes(ctypes.byref(desc(kind, H, D, k_tiles, nvfp4, fmt)), n, T,
+                                      1 if sparse else 0))
 
 
 def rolling_prefix(n_tokens: int) -> int:
@@ -224,36 +244,42 @@ def params_shape(kind: int, H: int, D: int, n: int, T: int = 0, k_tiles: bool = 
 class Packed:
     """Device buffers of one encoded loop (caller-owned torch tensors).  Compact loops also
     carry tile_start, the inverse map per 64 positions that flk_encode_residual writes.
-    k_tiles marks K streams with tile (page-local) groups; it selects the descriptor."""
+    k_tiles marks K streams with tile (page-local) groups; it and fmt select the descriptor."""
     n_rows: int
     rows: Optional[torch.Tensor]
     codes: torch.Tensor
     params: torch.Tensor
     tile_start: Optional[torch.Tensor] = None
     k_tiles: bool = False
-    nvfp4: bool = False
+    fmt: str = INT4
+
+    @property
+    def nvfp4(self) -> bool:
+        return self.fmt == NVFP4
 
     @staticmethod
     def empty(kind: int, H: int, D: int, n: int, rows: Optional[torch.Tensor] = None, T: int = 0,
               tile_start: Optional[torch.Tensor] = None, device="cuda", k_tiles: bool = False,
-              compact: Optional[bool] = None, nvfp4: bool = False) -> "Packed":
-        """compact: the stream has a tile index (default: when rows is given).  nvfp4: an NVFP4
-        stream (params: a 16-byte header, then one E4M3 byte per 16 elements)."""
+              compact: Optional[bool] = None, nvfp4: bool = False, fmt: Optional[str] = None) -> "Packed":
+        """compact: the stream has a tile index (default: when rows is given).  fmt (or
+        nvfp4=True): an NVFP4 stream (params: a 16-byte header, then one E4M3 byte per 16
+        elements) or an MXFP4 stream (params: one E8M0 byte per 32 elements)."""
+        f = _fmt(nvfp4, fmt)
         if k_tiles and kind == K and T < 1:
             raise ValueError("tile-grouped K needs T to size its params")
-        if nvfp4 and k_tiles:
-            raise ValueError("NVFP4 blocks run along channels; there are no tile groups")
+        if f != INT4 and k_tiles:
+            raise ValueError("FP4 blocks run along channels; there are no tile groups")
         compact = rows is not None if compact is None else compact
         codes = torch.empty((n, H, D // 2), dtype=torch.uint8, device=device)
-        if nvfp4:
-            params = torch.empty((params_bytes(kind, H, D, n, nvfp4=True) + 3) // 4, dtype=torch.int32, device=device)
+        if f != INT4:
+            params = torch.empty((params_bytes(kind, H, D, n, fmt=f) + 3) // 4, dtype=torch.int32, device=device)
         else:
             params = torch.empty(params_shape(kind, H, D, n, T, k_tiles), dtype=torch.int32, device=device)
         if compact and tile_start is None:
             if T < 1:
                 raise ValueError("a compact loop needs T to size its tile index")
             tile_start = torch.empty(tile_index_bytes(T) // 4, dtype=torch.int32, device=device)
-        return Packed(n, rows, codes, params, tile_start if compact else None, k_tiles and kind == K, nvfp4)
+        return Packed(n, rows, codes, params, tile_start if compact else None, k_tiles and kind == K, f)
 
     def c(self) -> StreamC:
         return StreamC(self.n_rows, 0, None if self.rows is None else self.rows.data_ptr(),
@@ -271,7 +297,7 @@ def encode_base(kind: int, x: torch.Tensor, out: Packed, recon: torch.Tensor,
     _need(x, torch.bfloat16, "x")
     _need(recon, torch.bfloat16, "recon")
     T, H, D = x.shape
-    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D, out.k_tiles, out.nvfp4)), _ptr(x), T, _ptr(out.codes),
+    _check(lib().flk_encode_base(ctypes.byref(desc(kind, H, D, out.k_tiles, fmt=out.fmt)), _ptr(x), T, _ptr(out.codes),
                                  _ptr(out.params), _ptr(recon), _ptr(status), _stream(stream)),
            "flk_encode_base")
 
@@ -284,7 +310,7 @@ def encode_residual(kind: int, x_rows: torch.Tensor, rows: Optional[torch.Tensor
         _need(rows, torch.int32, "rows")
     n, H, D = x_rows.shape
     T = recon.shape[0]
-    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D, out.k_tiles, out.nvfp4)), _ptr(x_rows), _ptr(rows), n, T,
+    _check(lib().flk_encode_residual(ctypes.byref(desc(kind, H, D, out.k_tiles, fmt=out.fmt)), _ptr(x_rows), _ptr(rows), n, T,
                                      _ptr(recon), _ptr(out.codes), _ptr(out.params), _ptr(out.tile_start),
                                      _ptr(status), _stream(stream)),
            "flk_encode_residual")
@@ -296,21 +322,18 @@ def _chain(chain: Sequence[Packed]):
 
 
 def reconstruct(kind: int, chain: Sequence[Packed], out: torch.Tensor, stream=None) -> None:
-    """X_hat of the chain; an INT4 or NVFP4 base, INT4 or NVFP4 residual loops (one format for
-    all of them)."""
+    """X_hat of the chain; an INT4 or FP4 base, INT4 or FP4 residual loops (one format for all
+    of them)."""
     _need(out, torch.bfloat16, "out")
     T, H, D = out.shape
     arr = _chain(chain)
-    resid_fp4 = {p.nvfp4 for p in chain[1:]}
-    if len(resid_fp4) > 1:
-        raise ValueError("the residual loops of one chain share one format")
-    rf = resid_fp4.pop() if resid_fp4 else chain[0].nvfp4
-    if not chain[0].nvfp4 and not rf:
+    bf, rf = _chain_formats(chain)
+    if bf == INT4 and rf == INT4:
         _check(lib().flk_reconstruct(ctypes.byref(desc(kind, H, D, chain[0].k_tiles)), T, arr, len(chain), _ptr(out),
                                      _stream(stream)), "flk_reconstruct")
         return
-    _check(lib().flk_reconstruct_mixed(ctypes.byref(desc(kind, H, D, chain[0].k_tiles, chain[0].nvfp4)),
-                                       ctypes.byref(desc(kind, H, D, nvfp4=rf)), T, arr, len(chain), _ptr(out),
+    _check(lib().flk_reconstruct_mixed(ctypes.byref(desc(kind, H, D, chain[0].k_tiles, fmt=bf)),
+                                       ctypes.byref(desc(kind, H, D, fmt=rf)), T, arr, len(chain), _ptr(out),
                                        _stream(stream)), "flk_reconstruct_mixed")
 
 
@@ -329,8 +352,9 @@ def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequ
 
 
 def _chain_formats(chain: Sequence[Packed]):
-    base = chain[0].nvfp4
-    resid = {p.nvfp4 for p in chain[1:]}
+    """(base format, residual format) of a chain; one format for all its residual loops."""
+    base = chain[0].fmt
+    resid = {p.fmt for p in chain[1:]}
     if len(resid) > 1:
         raise ValueError("the residual loops of one chain share one format")
     return base, (resid.pop() if resid else base)
@@ -339,16 +363,16 @@ def _chain_formats(chain: Sequence[Packed]):
 def decode_attn_mixed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int,
                       H: int, softmax_scale: float, out: torch.Tensor, workspace: torch.Tensor,
                       stream=None) -> None:
-    """Decode attention over chains of INT4 and NVFP4 streams (formats taken from the streams)."""
+    """Decode attention over chains of INT4 and FP4 streams (formats taken from the streams)."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.bfloat16, "out")
     Hq, D = q.shape
     kb, kr = _chain_formats(k_chain)
     vb, vr = _chain_formats(v_chain)
     ka, va = _chain(k_chain), _chain(v_chain)
-    _check(lib().flk_decode_attn_mixed(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles, kb)),
-                                       ctypes.byref(desc(K, H, D, nvfp4=kr)), ctypes.byref(desc(V, H, D, nvfp4=vb)),
-                                       ctypes.byref(desc(V, H, D, nvfp4=vr)), T, _ptr(q), Hq, ka, va, len(k_chain),
+    _check(lib().flk_decode_attn_mixed(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles, fmt=kb)),
+                                       ctypes.byref(desc(K, H, D, fmt=kr)), ctypes.byref(desc(V, H, D, fmt=vb)),
+                                       ctypes.byref(desc(V, H, D, fmt=vr)), T, _ptr(q), Hq, ka, va, len(k_chain),
                                        float(softmax_scale), _ptr(out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "flk_decode_attn_mixed")

@@ -432,6 +432,27 @@ def test_nvfp4_descriptor_sizes_and_unsupported_entry_points():
     assert L.flk_sparse_workspace_bytes(ctypes.byref(d), 256, 32, 16, 1) == 0
 
 
+def test_mxfp4_descriptor_and_sizes():
+    L = flk.lib()
+    d = flk.desc(flk.K, 8, 128, fmt="mxfp4")
+    assert L.flk_desc_check(ctypes.byref(d)) == 0
+    assert (d.format, d.group, d.param_dtype, d.k_grouping) == (3, 32, 3, 0)
+    assert flk.params_bytes(flk.K, 8, 128, 100, fmt="mxfp4") == 100 * 8 * 4     # one byte per 32 elements
+    assert flk.stream_bytes(flk.V, 8, 128, 100, 1000, True, fmt="mxfp4") == \
+        100 * 8 * 64 + 100 * 8 * 4 + 400 + flk.tile_index_bytes(1000)
+    assert L.flk_desc_check(ctypes.byref(flk.desc(flk.K, 8, 48, fmt="mxfp4"))) == 2    # D % 32 != 0
+    assert L.flk_desc_check(ctypes.byref(flk.desc(flk.K, 8, 48, fmt="nvfp4"))) == 0    # NVFP4 needs D % 16
+    tiles = flk.desc(flk.K, 8, 128, fmt="mxfp4")
+    tiles.k_grouping = 1
+    assert L.flk_desc_check(ctypes.byref(tiles)) == 4
+    wrong = flk.desc(flk.K, 8, 128, fmt="mxfp4")
+    wrong.param_dtype = 2                                 # MXFP4 blocks with NVFP4 scales
+    assert L.flk_desc_check(ctypes.byref(wrong)) == 4
+    with pytest.raises(ValueError):
+        flk.desc(flk.K, 8, 128, nvfp4=True, fmt="mxfp4")
+    assert L.flk_attn_workspace_bytes(ctypes.byref(d), 256, 32) == 0
+
+
 def test_reconstruct_mixed_validation():
     L = flk.lib()
     S = flk.StreamC
@@ -446,6 +467,8 @@ def test_reconstruct_mixed_validation():
     assert call(i4, f4v) == 4                             # kinds disagree
     assert call(i4, f4h) == 4                             # head counts disagree
     assert call(f4, i4) == 5                              # NVFP4 base, INT4 residuals
+    mx = flk.desc(flk.K, 8, 128, fmt="mxfp4")
+    assert call(f4, mx) == 5 and call(mx, f4) == 5        # NVFP4 mixed with MXFP4
     assert call(i4, f4, out=None) == 1
     assert call(i4, f4, T=0) == 2
     assert call(i4, f4, n=0) == 2
@@ -472,3 +495,7 @@ def test_decode_attn_mixed_validation():
     assert call(ki4, kf4, vi4, vf4, wb=64) == 6
     kt = flk.desc(flk.K, 8, 128, k_tiles=True)
     assert call(kt, kf4, vi4, vf4) == 5                         # tile-grouped K with NVFP4 residuals
+    kmx, vmx = flk.desc(flk.K, 8, 128, fmt="mxfp4"), flk.desc(flk.V, 8, 128, fmt="mxfp4")
+    assert call(kf4, kmx, vf4, vmx) == 5                        # NVFP4 base, MXFP4 residuals
+    assert call(ki4, kmx, vi4, vf4) == 5                        # K MXFP4, V NVFP4 residuals
+    assert call(ki4, kmx, vi4, vmx, hq=30) == 2                 # a valid combination reaches the shape checks
