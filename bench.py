@@ -289,7 +289,7 @@ def cpu_baseline_rows(w, host, sets):
     streams = [ofp4.encode_residual(x, r, recon) for x, r in zip(xs[1:], sets[1:])]
     ofp4.apply_residuals(base, streams)
     dt = time.perf_counter() - t0
-    b, _ = _format_bytes(flk.K, SimpleNamespace(H=1, D=w.D, T=w.T), sets, True, True)
+    b, _ = _format_bytes(flk.K, SimpleNamespace(H=1, D=w.D, T=w.T), sets, "nvfp4", "nvfp4")
     rows["nvfp4"] = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
                      "sample": f"K chain of KV head 0 (1/{w.H} of the tensor), 4 loops + reconstruct: {dt:.2f} s"}
     # sparse decode attention: the reference and one later loop for the 4 query heads of one KV
@@ -492,12 +492,17 @@ def selection_leg(reps=20):
     return res
 
 
-def _format_calls(kind, w, xs, rows, recon, out, packed, base_fp4, resid_fp4):
+# The chain formats the FP4 leg compares: (name, base loop's format, residual loops' format).
+CHAIN_FORMATS = (("int4", "int4", "int4"), ("nvfp4", "nvfp4", "nvfp4"), ("int4_base_nvfp4_residuals", "int4", "nvfp4"),
+                 ("mxfp4", "mxfp4", "mxfp4"), ("int4_base_mxfp4_residuals", "int4", "mxfp4"))
+
+
+def _format_calls(kind, w, xs, rows, recon, out, packed, base_fmt, resid_fmt):
     """Prepared C calls of one tensor's chain in a format: base, residual loops, reconstruct."""
     L = flk.lib()
     P = ctypes.c_void_p
-    bd = flk.desc(kind, w.H, w.D, nvfp4=base_fp4)
-    rd = flk.desc(kind, w.H, w.D, nvfp4=resid_fp4)
+    bd = flk.desc(kind, w.H, w.D, fmt=base_fmt)
+    rd = flk.desc(kind, w.H, w.D, fmt=resid_fmt)
     keep = [bd, rd]
     calls = [(L.flk_encode_base, (ctypes.byref(bd), P(xs[0].data_ptr()), w.T, P(packed[0].codes.data_ptr()),
                                   P(packed[0].params.data_ptr()), P(recon.data_ptr()), None))]
@@ -530,8 +535,7 @@ def fp4_attention_times(flush, reps=20):
     out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
     times = {}
-    for name, base_fp4, resid_fp4 in (("int4", False, False), ("nvfp4", True, True),
-                                      ("int4_base_nvfp4_residuals", False, True)):
+    for name, base_fmt, resid_fmt in CHAIN_FORMATS:
         chains = {}
         for kind in (flk.K, flk.V):
             recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
@@ -539,7 +543,7 @@ def fp4_attention_times(flush, reps=20):
             for l, (x, r) in enumerate(zip(host[kind].xs, host[kind].rows)):
                 xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
                 rd = None if r is None else torch.from_numpy(r).cuda()
-                p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T, nvfp4=base_fp4 if l == 0 else resid_fp4)
+                p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T, fmt=base_fmt if l == 0 else resid_fmt)
                 if l == 0:
                     flk.encode_base(kind, xd, p, recon)
                 else:
@@ -556,28 +560,29 @@ def fp4_attention_times(flush, reps=20):
     return times
 
 
-def _format_bytes(kind, w, sets, base_fp4, resid_fp4):
+def _format_bytes(kind, w, sets, base_fmt, resid_fmt):
     """Algorithmic bytes of one tensor's chain (each input read once, each output written once);
     the stream-amax pass of an NVFP4 loop re-reads its input and is not counted."""
     H, D, T = w.H, w.D, w.T
     W = H * D
 
-    def stream(n, fp4, sparse):
-        return flk.stream_bytes(kind, H, D, n, T, sparse, nvfp4=fp4) - (flk.tile_index_bytes(T) if sparse else 0)
-    b = 2 * T * W + stream(T, base_fp4, False) + 2 * T * W
-    total_streams = stream(T, base_fp4, False)
+    def stream(n, fmt, sparse):
+        return flk.stream_bytes(kind, H, D, n, T, sparse, fmt=fmt) - (flk.tile_index_bytes(T) if sparse else 0)
+    b = 2 * T * W + stream(T, base_fmt, False) + 2 * T * W
+    total_streams = stream(T, base_fmt, False)
     for r in sets[1:]:
         n = T if r is None else len(r)
-        st = stream(n, resid_fp4, r is not None)
+        st = stream(n, resid_fmt, r is not None)
         b += 6 * n * W + st
         total_streams += st
     return b + total_streams + 2 * T * W, total_streams
 
 
 def fp4_leg(w, host, sets, reps=30, rotate=2):
-    """The NVFP4 variant (PR #166 review item 2) on the long prompt, K and V chains of 4 loops
-    (100/100/50/25 %), against INT4 at the same ~4.5 bits per element: INT4 throughout, NVFP4
-    throughout, INT4 base + NVFP4 residuals.  Per format: the chain step (encode base, three
+    """The FP4 variants (NVFP4, PR #166 review item 2; MXFP4, OCP MX v1.0) on the long prompt, K
+    and V chains of 4 loops (100/100/50/25 %), against INT4 at about the same bits per element
+    (4.5; MXFP4 4.25): INT4 throughout, NVFP4 or MXFP4 throughout, INT4 base + NVFP4 or MXFP4
+    residuals.  Per format: the chain step (encode base, three
     residual encodes, reconstruct, for K and V; events around the step, `rotate` buffer sets),
     the stored bytes, and the accuracy of the depth-4 reconstruction X_hat against the BF16
     inputs: relative Frobenius error per tensor, and decode attention (32 query heads over the
@@ -611,8 +616,7 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     attn_us = fp4_attention_times(flush)
     res = {"workload": "long_prompt", "T": T, "H": H, "D": D, "budgets_pct": list(w.budgets), "formats": {}}
-    for name, base_fp4, resid_fp4 in (("int4", False, False), ("nvfp4", True, True),
-                                      ("int4_base_nvfp4_residuals", False, True)):
+    for name, base_fmt, resid_fmt in CHAIN_FORMATS:
         sets_dev, keep, outs = [], [], {}
         for _ in range(rotate):
             calls = []
@@ -620,9 +624,9 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
                 xs, rows, _ = dev[kind]
                 recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
                 out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
-                packed = [flk.Packed.empty(kind, H, D, x.shape[0], r, T=T, nvfp4=base_fp4 if l == 0 else resid_fp4)
+                packed = [flk.Packed.empty(kind, H, D, x.shape[0], r, T=T, fmt=base_fmt if l == 0 else resid_fmt)
                           for l, (x, r) in enumerate(zip(xs, rows))]
-                c, k = _format_calls(kind, w, xs, rows, recon, out, packed, base_fp4, resid_fp4)
+                c, k = _format_calls(kind, w, xs, rows, recon, out, packed, base_fmt, resid_fmt)
                 calls += c
                 keep += [k, packed, recon, out]
                 outs.setdefault(kind, out)
@@ -649,8 +653,8 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
         step(0)                                                # outs[] hold set 0's reconstruction
         torch.cuda.synchronize()
         us = float(np.median(times))
-        b_k, s_k = _format_bytes(flk.K, w, sets, base_fp4, resid_fp4)
-        b_v, s_v = _format_bytes(flk.V, w, sets, base_fp4, resid_fp4)
+        b_k, s_k = _format_bytes(flk.K, w, sets, base_fmt, resid_fmt)
+        b_v, s_v = _format_bytes(flk.V, w, sets, base_fmt, resid_fmt)
         acc = {}
         for kind, tag in ((flk.K, "k"), (flk.V, "v")):
             t = dev[kind][2].float()
@@ -931,7 +935,7 @@ def main():
     ap.add_argument("--no-rolling", action="store_true", help="skip the rolling-tail flush and attention leg")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse decode attention leg")
     ap.add_argument("--no-selection", action="store_true", help="skip the token selection leg")
-    ap.add_argument("--no-fp4", action="store_true", help="skip the NVFP4 variant leg")
+    ap.add_argument("--no-fp4", action="store_true", help="skip the FP4 (NVFP4, MXFP4) variant leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -1070,8 +1074,8 @@ def main():
         log("sparse decode attention ...")
         result["sparse_attention"] = sparse_leg()
     if not args.no_fp4:
-        log("NVFP4 variant against INT4 ...")
-        result["nvfp4"] = fp4_leg(w, host, sets)
+        log("FP4 variants against INT4 ...")
+        result["fp4"] = fp4_leg(w, host, sets)
     if not args.no_selection:
         log("token selection ...")
         result["token_selection"] = selection_leg()
