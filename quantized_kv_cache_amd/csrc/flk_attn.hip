@@ -70,20 +70,20 @@ size_t attn_workspace_bytes(int32_t T_total, int32_t H, int32_t Hq) {
   return size_t(s) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
 }
 
-// Decode loop l's 8 channels of one item into d[] (binary32 values that are exactly BF16).
-// K: params of the 8 channels come from the LDS copy of the item's parameter row; V: one
-// parameter for the item's 64-channel group.
+// Decode loop l's 8 channels of one item into d[], the binary32 values min + scale * code
+// before their BF16 rounding (the caller rounds them where the chain needs it).  K: params of
+// the 8 channels come from the LDS copy of the item's parameter row; V: one parameter for the
+// item's 64-channel group.
 __device__ __forceinline__ void decode_item(uint32_t cw, const uint32_t p[8], float d[8]) {
   float c[8];
   codes8_to_f32(cw, c);
 #pragma unroll
   for (int e = 0; e < 8; ++e) d[e] = decode(c[e], f16_bits_to_f32(p[e] & 0xFFFFu), f16_bits_to_f32(p[e] >> 16));
-  round_bf16x8_inplace(d);
 }
 
-// An NVFP4 item: 8 E2M1 codes times the block's scale bs = RN32(e4m3 * s_g), each product
-// rounded to BF16.  gfx950's v_cvt_scalef32_pk_f32_fp4 with a scale of 1 gives the exact E2M1
-// values (the codec's encoder relies on the same conversion).
+// An FP4 item: 8 E2M1 codes times the block's binary32 scale (NVFP4 RN32(e4m3 * s_g), MXFP4
+// 2^(e8m0 - 127)), before the BF16 rounding.  gfx950's v_cvt_scalef32_pk_f32_fp4 with a scale
+// of 1 gives the exact E2M1 values (the codec's encoder relies on the same conversion).
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void decode_item_fp4(uint32_t cw, float bs, float d[8]) {
   f32x2_t v;
@@ -91,7 +91,6 @@ __device__ __forceinline__ void decode_item_fp4(uint32_t cw, float bs, float d[8
   v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1); d[2] = v.x * bs; d[3] = v.y * bs;
   v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2); d[4] = v.x * bs; d[5] = v.y * bs;
   v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3); d[6] = v.x * bs; d[7] = v.y * bs;
-  round_bf16x8_inplace(d);
 }
 __device__ __forceinline__ float e4m3_scale(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
@@ -216,6 +215,9 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
       }
     }
   }
+  // The chain's roundings are taken lazily: acc holds the running sum before its BF16
+  // rounding, which happens only when another loop adds to it, or in the final pack.  The
+  // result is the encoder's bf16(...bf16(bf16(base) + bf16(d2)) ... + bf16(dR)).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float acc[8];
@@ -227,25 +229,30 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
       float d[8];
       if (loop_fp4<FMT>(l)) {
         decode_item_fp4(cw[l][i], loop_mx<FMT>(l) ? e8m0_scale(vp[l][i]) : e4m3_scale(vp[l][i]) * sg[l], d);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
-        continue;
-      }
-      uint32_t p[8];
-      if (KIND == FLK_KIND_K) {
-        const int rg = c.ktile ? 0 : (j[l] / kGroup) & 1;  // staged by rowgroup parity
-        const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
-        const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
-        p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
       } else {
+        uint32_t p[8];
+        if (KIND == FLK_KIND_K) {
+          const int rg = c.ktile ? 0 : (j[l] / kGroup) & 1;  // staged by rowgroup parity
+          const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
+          const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
+          p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = vp[l][i];
+          for (int e = 0; e < 8; ++e) p[e] = vp[l][i];
+        }
+        decode_item(cw[l][i], p, d);
       }
-      decode_item(cw[l][i], p, d);
+      if (l == 0) {                                      // the dense base: every live token
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = d[e];
+      } else {
+        round_bf16x8_inplace(acc);
+        round_bf16x8_inplace(d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + d[e];
+      }
     }
-    out[i] = pack_exact_bf16x8(acc);
+    out[i] = round_bf16x8(acc);                          // RNE pack of the last sum
   }
 }
 
