@@ -29,6 +29,10 @@ size s[t, r] = exp(U(ln 0.01, ln 1)) per (token, loop), so that change scores sp
 decades; every H[r] is rounded to BF16.  The long-prompt selection workload uses T = 32768 and
 a hidden width d = 4096 (32 query heads x 128, the decode workload's attention width),
 windows of 2048 tokens and budgets 50 % then 25 %.
+
+Inputs too large to draw on the host (device_trajectory, the largest tensor the library
+accepts): the same trajectory recipe with Y[1] ~ N(0,1), drawn on the device by torch's
+generator in row chunks, chunk c of every loop from one generator seeded seed * 2^20 + c.
 """
 from __future__ import annotations
 
@@ -178,3 +182,21 @@ def hidden_states(T: int, d: int, n_states: int, workload: int = 3, request: int
         y = y + gs.standard_normal((T, d), dtype=np.float32) * size
         out.append(to_bf16_bits(y))
     return out
+
+
+def device_trajectory(T: int, H: int, D: int, n_loops: int, seed: int, sigma: float = 0.1,
+                      chunk: int = 1 << 16, device: str = "cuda") -> List[torch.Tensor]:
+    """Dense BF16 inputs X[1..n_loops], each [T, H, D], drawn on the device: Y[1] ~ N(0,1),
+    Y[r] = Y[r-1] + N(0, sigma^2) per element, X[r] = bf16(Y[r]) (round-to-nearest-even)."""
+    xs = [torch.empty((T, H, D), dtype=torch.bfloat16, device=device) for _ in range(n_loops)]
+    g = torch.Generator(device=device)
+    for c, r0 in enumerate(range(0, T, chunk)):
+        r1 = min(T, r0 + chunk)
+        g.manual_seed(seed * (1 << 20) + c)
+        y = torch.randn((r1 - r0, H, D), generator=g, device=device)
+        xs[0][r0:r1] = y.to(torch.bfloat16)
+        for r in range(1, n_loops):
+            y += sigma * torch.randn((r1 - r0, H, D), generator=g, device=device)
+            xs[r][r0:r1] = y.to(torch.bfloat16)
+        del y
+    return xs

@@ -499,3 +499,17 @@ def test_decode_attn_mixed_validation():
     assert call(kf4, kmx, vf4, vmx) == 5                        # NVFP4 base, MXFP4 residuals
     assert call(ki4, kmx, vi4, vf4) == 5                        # K MXFP4, V NVFP4 residuals
     assert call(ki4, kmx, vi4, vmx, hq=30) == 2                 # a valid combination reaches the shape checks
+
+
+def test_largest_tensor_bound():
+    """T*H*D must stay below 2^31 elements (4 GiB of BF16, the kernels' 32-bit byte offsets):
+    one position past the largest accepted T is rejected before anything is launched."""
+    L = flk.lib()
+    H, D = 8, 128
+    T = (1 << 31) // (H * D)                 # 2,097,152: T*H*D == 2^31
+    for kind in (flk.K, flk.V):
+        d = flk.desc(kind, H, D)
+        assert L.flk_encode_base(ctypes.byref(d), FAKE, T, FAKE, FAKE, FAKE, None, None) == 2
+        assert L.flk_encode_residual(ctypes.byref(d), FAKE, None, T, T, FAKE, FAKE, FAKE, None, None, None) == 2
+        chain = (flk.StreamC * 1)(flk.StreamC(T, 0, None, FAKE.value, FAKE.value, None))
+        assert L.flk_reconstruct(ctypes.byref(d), T, chain, 1, FAKE, None) == 2
