@@ -415,7 +415,7 @@ def sparse_leg(k=4096, reps=20):
     per query head: the reference call at loop 2 (full attention writing the scores, the top-k
     selection, the selected keys' mass and C_ref), the loop calls at loops 3 and 4 (only the
     selected keys, read through the chains at depth 3 and 4), next to dense packed attention
-    at the same depths.  Each call is timed with a cold MALL (a 512 MiB write before it)."""
+    at the same depths.  Each call is timed with a cold MALL (a 512 MiB read before it)."""
     w = synth.WORKLOADS[5]
     T, H, D, Hq = w.T, w.H, w.D, w.Hq
     chains = decode_chains(w, k_tiles=True)
@@ -519,10 +519,12 @@ def _format_calls(kind, w, xs, rows, recon, out, packed, base_fmt, resid_fmt):
     return calls, keep
 
 
-def fp4_attention_times(flush, reps=20):
-    """Fused decode attention on the decode workload (131072 tokens, 8 KV heads, 32 query heads,
-    chains of 4 loops at 100/100/50/25 %) in each format: median microseconds per call, each
-    after a 512 MiB read that evicts the MALL."""
+def fp4_attention_times(flush, reps=20, k=4096):
+    """The chains' consumers on the decode workload (131072 tokens, 8 KV heads, 32 query heads,
+    chains of 4 loops at 100/100/50/25 %) in each format: fused decode attention at depth 4, and
+    sparse decode attention with k keys per query head (the reference call at loop 2, the loop
+    calls at depths 3 and 4).  Median microseconds per call, each after a 512 MiB read that
+    evicts the MALL."""
     w = synth.WORKLOADS[5]
     T, H, D, Hq = w.T, w.H, w.D, w.Hq
     sets = synth.active_sets(w, T)
@@ -531,7 +533,10 @@ def fp4_attention_times(flush, reps=20):
     g = torch.Generator(device="cuda")
     g.manual_seed(11)
     q = torch.randn((Hq, D), device="cuda", generator=g).to(torch.bfloat16)
-    ws = torch.empty(flk.attn_workspace_bytes(H, D, T, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(flk.sparse_workspace_bytes(H, D, T, Hq, k, 4), flk.attn_workspace_bytes(H, D, T, Hq)) // 4
+                     + 64, dtype=torch.float32, device="cuda")
+    ws = ws[(-ws.data_ptr() // 4) % 64:]                         # 256-byte aligned
+    st = flk.SparseState.empty(Hq, D, k)
     out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
     times = {}
@@ -551,12 +556,21 @@ def fp4_attention_times(flush, reps=20):
                 packs.append(p)
             chains[kind] = packs
             del recon
-        fn = lambda: flk.decode_attn_mixed(q, chains[flk.K], chains[flk.V], T, H, scale, out, ws)
+        Kc, Vc = chains[flk.K], chains[flk.V]
+        fn = lambda: flk.decode_attn_mixed(q, Kc, Vc, T, H, scale, out, ws)
+        ref = lambda: flk.sparse_attn_reference(q, Kc[:2], Vc[:2], T, H, k, scale, out, st, ws)
+        loop = {d: (lambda d=d: flk.sparse_attn_loop(q, Kc[:d], Vc[:d], T, H, k, scale, st, out, ws)) for d in (3, 4)}
         for _ in range(3):
             fn()
+            ref()
+            loop[3]()
+            loop[4]()
         torch.cuda.synchronize()
-        times[name] = round(_timed_us(fn, reps, flush), 2)
-        del chains
+        times[name] = {"decode_attention_us": round(_timed_us(fn, reps, flush), 2),
+                       "sparse_reference_us": round(_timed_us(ref, reps, flush), 2),
+                       "sparse_loop3_us": round(_timed_us(loop[3], reps, flush), 2),
+                       "sparse_loop4_us": round(_timed_us(loop[4], reps, flush), 2)}
+        del chains, Kc, Vc
     return times
 
 
@@ -587,7 +601,8 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
     the stored bytes, and the accuracy of the depth-4 reconstruction X_hat against the BF16
     inputs: relative Frobenius error per tensor, and decode attention (32 query heads over the
     8 KV heads, binary32 on the GPU) from X_hat against attention from the inputs.  Also the
-    fused decode attention's time per call on the decode workload in each format."""
+    fused decode attention's and the sparse decode attention's times per call on the decode
+    workload in each format."""
     H, D, T = w.H, w.D, w.T
     dev = {}
     for kind in (flk.K, flk.V):
@@ -662,7 +677,7 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
         o = attend(outs[flk.K], outs[flk.V])
         rel = ((o - ref_out).abs().amax(dim=1) / ref_out.abs().amax(dim=1)).cpu().numpy()
         res["formats"][name] = {
-            "decode_attention_us": attn_us[name],
+            **attn_us[name],
             "step_us": round(us, 2), "step_bytes": int(b_k + b_v), "gbs": round((b_k + b_v) / us / 1e3, 1),
             "stored_bytes": int(s_k + s_v),
             "bits_per_element": round(8 * (s_k + s_v) / (2 * sum((T if r is None else len(r)) for r in sets) * H * D), 4),

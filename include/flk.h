@@ -183,8 +183,9 @@ typedef struct flk_stream {
 void flk_desc_init(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
 /* Fill a descriptor for NVFP4 streams.  NVFP4 descriptors are accepted by flk_desc_check, the
- * size functions, flk_encode_base, flk_encode_residual, flk_reconstruct, flk_reconstruct_mixed
- * and flk_decode_attn_mixed; every other entry point answers FLK_E_UNSUPPORTED. */
+ * stream size functions, flk_encode_base, flk_encode_residual, flk_reconstruct,
+ * flk_reconstruct_mixed, flk_decode_attn_mixed and the two sparse *_mixed calls; every other
+ * entry point answers FLK_E_UNSUPPORTED. */
 void flk_desc_init_nvfp4(flk_desc* d, int kind, int32_t n_heads, int32_t head_dim);
 
 /* Fill a descriptor for MXFP4 streams; accepted by the same entry points as NVFP4's. */
@@ -395,6 +396,30 @@ flk_status flk_sparse_attn_loop(const flk_desc* k_desc, const flk_desc* v_desc, 
                                 int32_t n_loops, int32_t k, float softmax_scale, const int32_t* sel,
                                 const float* mass, const float* o_ref, const float* c_ref, void* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* flk_sparse_attn_reference and flk_sparse_attn_loop over chains of FP4 streams (the PR #166
+ * review, item 2, asks for the consumers' speed and accuracy with FP4 residual reconstruction
+ * fused in; RFC section 3.2 for the method): the K chain's base loop is described by kd_base,
+ * its residual loops by kd_resid, V likewise, with the combinations flk_decode_attn_mixed
+ * accepts (INT4 throughout; an INT4 base with NVFP4 or MXFP4 residuals; NVFP4 or MXFP4
+ * throughout; the same for K and V).  The keys the later loops gather are decoded from the
+ * FP4 streams as flk_reconstruct decodes them.  The workspace is flk_sparse_workspace_bytes of
+ * an INT4 descriptor with the same H and D (the size does not depend on the stream format).
+ * Errors: those of the INT4 calls, plus FLK_E_DESC / FLK_E_UNSUPPORTED as for
+ * flk_decode_attn_mixed. */
+flk_status flk_sparse_attn_reference_mixed(const flk_desc* kd_base, const flk_desc* kd_resid,
+                                           const flk_desc* vd_base, const flk_desc* vd_resid, int32_t T,
+                                           const void* q, int32_t n_q_heads, const flk_stream* k_chain,
+                                           const flk_stream* v_chain, int32_t n_loops, int32_t k,
+                                           float softmax_scale, void* out, int32_t* sel, float* mass,
+                                           float* o_ref, float* c_ref, void* workspace, size_t workspace_bytes,
+                                           void* stream);
+flk_status flk_sparse_attn_loop_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
+                                      const flk_desc* vd_resid, int32_t T, const void* q, int32_t n_q_heads,
+                                      const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
+                                      int32_t k, float softmax_scale, const int32_t* sel, const float* mass,
+                                      const float* o_ref, const float* c_ref, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Token selection for sparse prefill (RFC section 3.1, "Token-sparse prefill", and its fixed

@@ -325,11 +325,15 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
                                            static_cast<hipStream_t>(stream)));
 }
 
-flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
-                                 const flk_desc* vd_resid, int32_t T, const void* q, int32_t n_q_heads,
-                                 const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
-                                 float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+namespace {
+
+// The readers' format code of a K and a V chain, each described by its base loop's and its
+// residual loops' descriptors: INT4 throughout (0), INT4 base + NVFP4 residuals (1), NVFP4
+// throughout (2), INT4 base + MXFP4 residuals (3), MXFP4 throughout (4), the same for K and V.
+// An FP4 base with INT4 residuals, NVFP4 with MXFP4, and tile-grouped K with FP4 residuals are
+// FLK_E_UNSUPPORTED.
+flk_status chain_fmt(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
+                     const flk_desc* vd_resid, int* fmt) {
   flk_status st;
   for (const flk_desc* d : {kd_base, kd_resid, vd_base, vd_resid})
     if ((st = flk_desc_check(d)) != FLK_OK) return st;
@@ -338,8 +342,6 @@ flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_res
     return FLK_E_DESC;
   for (const flk_desc* d : {kd_resid, vd_base, vd_resid})
     if (d->n_heads != kd_base->n_heads || d->head_dim != kd_base->head_dim) return FLK_E_SHAPE;
-  // the format combination, the same for K and V: INT4 throughout (0), INT4 base + NVFP4
-  // residuals (1), NVFP4 throughout (2), INT4 base + MXFP4 residuals (3), MXFP4 throughout (4)
   const auto fmt_of = [](const flk_desc* b, const flk_desc* r) {
     if (!is_fp4(r)) return is_fp4(b) ? -1 : 0;
     if (is_fp4(b) && b->format != r->format) return -1;
@@ -347,10 +349,24 @@ flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_res
   };
   const int fk = fmt_of(kd_base, kd_resid), fv = fmt_of(vd_base, vd_resid);
   if (fk < 0 || fk != fv) return FLK_E_UNSUPPORTED;
+  if (fk != 0 && kd_base->k_grouping != FLK_KGROUP_ROWS) return FLK_E_UNSUPPORTED;
+  *fmt = fk;
+  return FLK_OK;
+}
+
+}  // namespace
+
+flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
+                                 const flk_desc* vd_resid, int32_t T, const void* q, int32_t n_q_heads,
+                                 const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
+                                 float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  int fk = 0;
+  flk_status st = chain_fmt(kd_base, kd_resid, vd_base, vd_resid, &fk);
+  if (st != FLK_OK) return st;
   if (fk == 0)
     return flk_decode_attn_packed(kd_base, vd_base, T, q, n_q_heads, k_chain, v_chain, n_loops, softmax_scale, out,
                                   workspace, workspace_bytes, stream);
-  if (kd_base->k_grouping != FLK_KGROUP_ROWS) return FLK_E_UNSUPPORTED;
   if (!q || !out) return FLK_E_NULL;
   if (T < 1 || !rows_fit(kd_base, T) || n_q_heads < 1 || n_q_heads % kd_base->n_heads != 0) return FLK_E_SHAPE;
   if (kd_base->head_dim != 128 || n_q_heads / kd_base->n_heads > 16) return FLK_E_UNSUPPORTED;
@@ -369,15 +385,13 @@ flk_status flk_decode_attn_mixed(const flk_desc* kd_base, const flk_desc* kd_res
 
 namespace {
 
-// The shape and pointer checks shared by both sparse calls (those of flk_decode_attn_packed).
+// The shape and pointer checks shared by the sparse calls (those of flk_decode_attn_packed); kd
+// and vd describe the chains' base loops and are well formed.
 flk_status check_sparse(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q, int32_t n_q_heads,
                         const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops, int32_t k,
                         const void* out, const int32_t* sel, const float* mass, const float* o_ref,
                         const float* c_ref, flk::ChainArgs* kc, flk::ChainArgs* vc) {
-  flk_status st = int4_desc(kd);
-  if (st != FLK_OK) return st;
-  st = int4_desc(vd);
-  if (st != FLK_OK) return st;
+  flk_status st;
   if (kd->kind != FLK_KIND_K || vd->kind != FLK_KIND_V) return FLK_E_DESC;
   if (kd->n_heads != vd->n_heads || kd->head_dim != vd->head_dim) return FLK_E_SHAPE;
   if (!q || !out || !sel || !mass || !o_ref || !c_ref) return FLK_E_NULL;
@@ -404,11 +418,12 @@ size_t flk_sparse_workspace_bytes(const flk_desc* k_desc, int32_t T, int32_t n_q
   return flk::sparse_workspace_bytes(T, k_desc->n_heads, n_q_heads, k, n_loops);
 }
 
-flk_status flk_sparse_attn_reference(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
-                                     int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
-                                     int32_t n_loops, int32_t k, float softmax_scale, void* out, int32_t* sel,
-                                     float* mass, float* o_ref, float* c_ref, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+namespace {
+
+flk_status sparse_reference(int fmt, const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                            int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
+                            int32_t k, float softmax_scale, void* out, int32_t* sel, float* mass, float* o_ref,
+                            float* c_ref, void* workspace, size_t workspace_bytes, void* stream) {
   flk::ChainArgs kc, vc;
   flk_status st = check_sparse(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, out, sel, mass, o_ref, c_ref,
                                &kc, &vc);
@@ -417,9 +432,39 @@ flk_status flk_sparse_attn_reference(const flk_desc* kd, const flk_desc* vd, int
   if (!workspace || workspace_bytes < flk::sparse_workspace_bytes(T, kd->n_heads, n_q_heads, k, nl))
     return FLK_E_WORKSPACE;
   if (!aligned(workspace, 256)) return FLK_E_ALIGN;
-  return to_status(flk::launch_sparse_reference(T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, out, sel,
-                                                mass, o_ref, c_ref, workspace, workspace_bytes,
+  return to_status(flk::launch_sparse_reference(fmt, T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, out,
+                                                sel, mass, o_ref, c_ref, workspace, workspace_bytes,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+flk_status sparse_loop(int fmt, const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q, int32_t n_q_heads,
+                       const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops, int32_t k,
+                       float softmax_scale, const int32_t* sel, const float* mass, const float* o_ref,
+                       const float* c_ref, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  flk::ChainArgs kc, vc;
+  flk_status st = check_sparse(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, out, sel, mass, o_ref, c_ref,
+                               &kc, &vc);
+  if (st != FLK_OK) return st;
+  const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
+  if (!workspace || workspace_bytes < flk::sparse_workspace_bytes(T, kd->n_heads, n_q_heads, k, nl))
+    return FLK_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return FLK_E_ALIGN;
+  return to_status(flk::launch_sparse_loop(fmt, T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, sel, mass,
+                                           o_ref, c_ref, out, workspace, workspace_bytes,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+flk_status flk_sparse_attn_reference(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                                     int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                     int32_t n_loops, int32_t k, float softmax_scale, void* out, int32_t* sel,
+                                     float* mass, float* o_ref, float* c_ref, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  flk_status st;
+  if ((st = int4_desc(kd)) != FLK_OK || (st = int4_desc(vd)) != FLK_OK) return st;
+  return sparse_reference(0, kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, softmax_scale, out, sel, mass,
+                          o_ref, c_ref, workspace, workspace_bytes, stream);
 }
 
 flk_status flk_sparse_attn_loop(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q, int32_t n_q_heads,
@@ -427,16 +472,36 @@ flk_status flk_sparse_attn_loop(const flk_desc* kd, const flk_desc* vd, int32_t 
                                 float softmax_scale, const int32_t* sel, const float* mass, const float* o_ref,
                                 const float* c_ref, void* out, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  flk::ChainArgs kc, vc;
-  flk_status st = check_sparse(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, out, sel, mass, o_ref, c_ref,
-                               &kc, &vc);
+  flk_status st;
+  if ((st = int4_desc(kd)) != FLK_OK || (st = int4_desc(vd)) != FLK_OK) return st;
+  return sparse_loop(0, kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, k, softmax_scale, sel, mass, o_ref, c_ref,
+                     out, workspace, workspace_bytes, stream);
+}
+
+flk_status flk_sparse_attn_reference_mixed(const flk_desc* kd_base, const flk_desc* kd_resid,
+                                           const flk_desc* vd_base, const flk_desc* vd_resid, int32_t T,
+                                           const void* q, int32_t n_q_heads, const flk_stream* k_chain,
+                                           const flk_stream* v_chain, int32_t n_loops, int32_t k,
+                                           float softmax_scale, void* out, int32_t* sel, float* mass, float* o_ref,
+                                           float* c_ref, void* workspace, size_t workspace_bytes, void* stream) {
+  int fmt = 0;
+  flk_status st = chain_fmt(kd_base, kd_resid, vd_base, vd_resid, &fmt);
   if (st != FLK_OK) return st;
-  const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
-  if (!workspace || workspace_bytes < flk::sparse_workspace_bytes(T, kd->n_heads, n_q_heads, k, nl))
-    return FLK_E_WORKSPACE;
-  if (!aligned(workspace, 256)) return FLK_E_ALIGN;
-  return to_status(flk::launch_sparse_loop(T, kd->n_heads, n_q_heads, k, q, kc, vc, softmax_scale, sel, mass, o_ref,
-                                           c_ref, out, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+  return sparse_reference(fmt, kd_base, vd_base, T, q, n_q_heads, k_chain, v_chain, n_loops, k, softmax_scale, out,
+                          sel, mass, o_ref, c_ref, workspace, workspace_bytes, stream);
+}
+
+flk_status flk_sparse_attn_loop_mixed(const flk_desc* kd_base, const flk_desc* kd_resid, const flk_desc* vd_base,
+                                      const flk_desc* vd_resid, int32_t T, const void* q, int32_t n_q_heads,
+                                      const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops,
+                                      int32_t k, float softmax_scale, const int32_t* sel, const float* mass,
+                                      const float* o_ref, const float* c_ref, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  int fmt = 0;
+  flk_status st = chain_fmt(kd_base, kd_resid, vd_base, vd_resid, &fmt);
+  if (st != FLK_OK) return st;
+  return sparse_loop(fmt, kd_base, vd_base, T, q, n_q_heads, k_chain, v_chain, n_loops, k, softmax_scale, sel, mass,
+                     o_ref, c_ref, out, workspace, workspace_bytes, stream);
 }
 
 // ---- token selection and row partition -----------------------------------------------------

@@ -18,6 +18,7 @@
 // (block, query head); a second kernel merges the partials of all blocks.  A BF16 tail (a
 // rolling cache's recent tokens) is read as stored, 16 tokens per wave.
 #include "flk_device.h"
+#include "flk_fp4_device.h"
 #include "flk_internal.h"
 #include "flk_readers.h"
 
@@ -81,33 +82,6 @@ __device__ __forceinline__ void decode_item(uint32_t cw, const uint32_t p[8], fl
   for (int e = 0; e < 8; ++e) d[e] = decode(c[e], f16_bits_to_f32(p[e] & 0xFFFFu), f16_bits_to_f32(p[e] >> 16));
 }
 
-// An FP4 item: 8 E2M1 codes times the block's binary32 scale (NVFP4 RN32(e4m3 * s_g), MXFP4
-// 2^(e8m0 - 127)), before the BF16 rounding.  gfx950's v_cvt_scalef32_pk_f32_fp4 with a scale
-// of 1 gives the exact E2M1 values (the codec's encoder relies on the same conversion).
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void decode_item_fp4(uint32_t cw, float bs, float d[8]) {
-  f32x2_t v;
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0); d[0] = v.x * bs; d[1] = v.y * bs;
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1); d[2] = v.x * bs; d[3] = v.y * bs;
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2); d[4] = v.x * bs; d[5] = v.y * bs;
-  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3); d[6] = v.x * bs; d[7] = v.y * bs;
-}
-__device__ __forceinline__ float e4m3_scale(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  return e == 0 ? float(m) * 0x1p-9f : __builtin_ldexpf(1.0f + float(m) * 0.125f, int(e) - 7);
-}
-
-// E8M0 byte b (an MXFP4 block scale) -> 2^(b - 127); byte 0 is 2^-127, a binary32 subnormal.
-__device__ __forceinline__ float e8m0_scale(uint32_t b) { return __uint_as_float(b != 0u ? b << 23 : 0x00400000u); }
-
-// Stream formats of a chain: FMT 0 = INT4 throughout, 1 = INT4 base with NVFP4 residual
-// loops, 2 = NVFP4 throughout, 3 = INT4 base with MXFP4 residual loops, 4 = MXFP4 throughout.
-template <int FMT>
-__device__ __forceinline__ constexpr bool loop_nv(int l) { return FMT == 2 || (FMT == 1 && l > 0); }
-template <int FMT>
-__device__ __forceinline__ constexpr bool loop_mx(int l) { return FMT == 4 || (FMT == 3 && l > 0); }
-template <int FMT>
-__device__ __forceinline__ constexpr bool loop_fp4(int l) { return loop_nv<FMT>(l) || loop_mx<FMT>(l); }
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float v[8]) {
   *reinterpret_cast<uint4*>(dst) = pack_exact_bf16x8(v);
@@ -193,11 +167,25 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
   const int nl = c.n_loops;
   const int32_t t = t0 + tk;
   int32_t j[NL];
-  uint32_t cw[NL][4], vp[NL][4];
+  uint32_t cw[NL][4], vp[NL][4], sw[NL][2];
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     j[l] = -1;
     if (l < nl) j[l] = r.dense[l] ? (t < T ? t : -1) : map[l][tk];
+    // FP4 loops: the item's block scales in one load -- its 4 E8M0 bytes (MXFP4, one per 32
+    // channels) or its 8 E4M3 bytes after the 16-byte header (NVFP4, one per 16 channels);
+    // the bytes are picked at decode time, so no load waits before the others are issued
+    sw[l][0] = sw[l][1] = 0u;
+    if (loop_fp4<FMT>(l) && j[l] >= 0) {
+      const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
+      if (loop_mx<FMT>(l)) {
+        sw[l][0] = c.s[l].params[item];
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(c.s[l].params + 4u + item * 2u);
+        sw[l][0] = w.x;
+        sw[l][1] = w.y;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       cw[l][i] = 0;
@@ -206,12 +194,7 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
         // uniform base + 32-bit offset: one saddr load, no 64-bit address arithmetic per lane
         const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
         cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (item * (kAttnD / 2) + uint32_t(oc[i]) * 4u));
-        if (loop_mx<FMT>(l))         // the 32-channel block's E8M0 byte
-          vp[l][i] = reinterpret_cast<const uint8_t*>(c.s[l].params)[item * (kAttnD / 32) + uint32_t(oc[i] >> 2)];
-        else if (loop_nv<FMT>(l))    // the 16-channel block's E4M3 byte, after the 16-byte header
-          vp[l][i] = reinterpret_cast<const uint8_t*>(c.s[l].params)[16u + item * (kAttnD / 16) + uint32_t(oc[i] >> 1)];
-        else if (KIND == FLK_KIND_V)
-          vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
+        if (KIND == FLK_KIND_V && !loop_fp4<FMT>(l)) vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
       }
     }
   }
@@ -227,8 +210,10 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
     for (int l = 0; l < NL; ++l) {
       if (j[l] < 0) continue;
       float d[8];
-      if (loop_fp4<FMT>(l)) {
-        decode_item_fp4(cw[l][i], loop_mx<FMT>(l) ? e8m0_scale(vp[l][i]) : e4m3_scale(vp[l][i]) * sg[l], d);
+      if (loop_fp4<FMT>(l)) {          // octet oc's block: byte oc / 4 (MXFP4) or oc / 2 (NVFP4)
+        const uint32_t b = loop_mx<FMT>(l) ? uint32_t(oc[i]) >> 2 : uint32_t(oc[i]) >> 1;
+        const uint32_t sb = (((b & 4u) ? sw[l][1] : sw[l][0]) >> (8u * (b & 3u))) & 0xFFu;
+        fp4_decode8(cw[l][i], loop_mx<FMT>(l) ? fp4_e8m0_value(sb) : fp4_e4m3_value(sb) * sg[l], d);
       } else {
         uint32_t p[8];
         if (KIND == FLK_KIND_K) {
@@ -613,11 +598,18 @@ hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, con
   }
 }
 
-hipError_t launch_attn_reference(int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+hipError_t launch_attn_reference(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
                                  const ChainArgs& vc, float scale, void* out, float* o_ref, float* ml,
                                  float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return launch_attn<true>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, o_ref, ml, scores, ws, ws_bytes,
-                           stream);
+#define FLK_R(F)                                                                                                  \
+  case F:                                                                                                         \
+    return launch_attn<true, F>(T, H, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, o_ref, ml, scores, ws,      \
+                                ws_bytes, stream);
+  switch (fmt) {
+    FLK_R(0) FLK_R(1) FLK_R(2) FLK_R(3) FLK_R(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef FLK_R
 }
 
 }  // namespace flk

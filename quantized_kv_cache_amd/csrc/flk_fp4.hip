@@ -24,6 +24,7 @@
 
 #include "flk_device.h"
 #include "flk_fp4.h"
+#include "flk_fp4_device.h"
 #include "flk_internal.h"
 
 namespace flk {
@@ -54,10 +55,6 @@ __device__ __forceinline__ float e4m3_round(float v, uint32_t& byte) {
   return __builtin_ldexpf(q, e - 3);
 }
 
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  return e == 0 ? float(m) * 0x1p-9f : __builtin_ldexpf(1.0f + float(m) * 0.125f, int(e) - 7);
-}
 
 // gfx950 converts pairs of binary32 values to E2M1 codes (v_cvt_scalef32_pk_fp4_f32) and back
 // (v_cvt_scalef32_pk_f32_fp4).  With a scale of 1 the conversion to E2M1 is the nearest-even
@@ -119,20 +116,6 @@ __device__ __forceinline__ uint32_t e2m1_encode8(const float v[8], float bs, flo
   return cw;
 }
 
-// The 8 decoded values of a code word against the block's scale.
-__device__ __forceinline__ void e2m1_decode8(uint32_t cw, float bs, float dec[8]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x2 d = uncvt_pair(cw, k);
-    dec[2 * k] = d.x * bs;
-    dec[2 * k + 1] = d.y * bs;
-  }
-}
-
-// E8M0 byte b -> 2^(b - 127); byte 0 is 2^-127, a binary32 subnormal.
-__device__ __forceinline__ float e8m0_value(uint32_t b) {
-  return __uint_as_float(b != 0u ? b << 23 : 0x00400000u);
-}
 
 // MXFP4 shared scale of a block from its largest magnitude: floor(log2 amax) - 2 (E2M1's
 // largest power of two is 2^2), clamped to E8M0's smallest exponent -127; the biased byte is
@@ -148,7 +131,7 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
 // rounding boundary 0.25, where the code is a signed zero either way.
 __device__ __forceinline__ uint32_t mx_encode8(const float v[8], uint32_t byte, float dec[8]) {
   const float inv = __uint_as_float((254u - byte) << 23);
-  const float X = e8m0_value(byte);
+  const float X = fp4_e8m0_value(byte);
   uint32_t cw = 0u;
 #pragma unroll
   for (int k = 0; k < 4; ++k) cw = cvt_pair(cw, v[2 * k] * inv, v[2 * k + 1] * inv, k);
@@ -353,8 +336,8 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_encode_kernel(const uint16_t*
 // off / 16) times the stream scale.
 __device__ __forceinline__ float fp4_block_scale(const uint32_t* params, int64_t off, bool mx) {
   const uint8_t* b = reinterpret_cast<const uint8_t*>(params);
-  if (mx) return e8m0_value(b[off / 32]);
-  return e4m3_value(b[16 + off / 16]) * __uint_as_float(params[0]);
+  if (mx) return fp4_e8m0_value(b[off / 32]);
+  return fp4_e4m3_value(b[16 + off / 16]) * __uint_as_float(params[0]);
 }
 
 // Block (tile, part): items part*1024 .. of the tile, item = (position in tile, 16-channel
@@ -399,8 +382,8 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
     const uint32_t bw[2] = {bc.x, bc.y};
     if (base_fp4) {
       const float bs = fp4_block_scale(b.params, off, mx != 0);
-      e2m1_decode8(bw[0], bs, x);
-      e2m1_decode8(bw[1], bs, x + 8);
+      fp4_decode8(bw[0], bs, x);
+      fp4_decode8(bw[1], bs, x + 8);
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[e] = round_bf16(x[e]);
     } else if (kind == FLK_KIND_K) {                            // one (min, scale) per channel of the 64-row group
@@ -431,8 +414,8 @@ __global__ __launch_bounds__(kFp4Threads) void fp4_reconstruct_kernel(ChainArgs 
       const uint32_t rw[2] = {rc.x, rc.y};
       const float bs = fp4_block_scale(s.params, roff, mx != 0);
       float d[16];
-      e2m1_decode8(rw[0], bs, d);
-      e2m1_decode8(rw[1], bs, d + 8);
+      fp4_decode8(rw[0], bs, d);
+      fp4_decode8(rw[1], bs, d + 8);
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[e] = round_bf16(x[e] + round_bf16(d[e]));
     }

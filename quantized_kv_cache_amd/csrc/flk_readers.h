@@ -28,19 +28,20 @@ hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, con
 // Full attention over the packed chains (no tail) that also writes every scaled score to
 // scores [Hq][T], the FP32 output to o_ref [Hq][128] and the softmax (max, denominator) to
 // ml [Hq][2]; out gets the BF16 output.
-hipError_t launch_attn_reference(int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+hipError_t launch_attn_reference(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
                                  const ChainArgs& vc, float scale, void* out, float* o_ref, float* ml,
                                  float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Sparse decode attention: workspace, the reference loop (after launch_attn_reference's
-// attention) and a later loop.
+// attention) and a later loop; fmt as launch_decode_attn_fmt's.
 size_t sparse_workspace_bytes(int32_t T, int32_t H, int32_t Hq, int32_t k, int32_t n_loops);
-hipError_t launch_sparse_reference(int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q, const ChainArgs& kc,
-                                   const ChainArgs& vc, float scale, void* out, int32_t* sel, float* mass,
-                                   float* o_ref, float* c_ref, void* ws, size_t ws_bytes, hipStream_t stream);
-hipError_t launch_sparse_loop(int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q, const ChainArgs& kc,
-                              const ChainArgs& vc, float scale, const int32_t* sel, const float* mass,
-                              const float* o_ref, const float* c_ref, void* out, void* ws, size_t ws_bytes,
-                              hipStream_t stream);
+hipError_t launch_sparse_reference(int fmt, int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q,
+                                   const ChainArgs& kc, const ChainArgs& vc, float scale, void* out, int32_t* sel,
+                                   float* mass, float* o_ref, float* c_ref, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+hipError_t launch_sparse_loop(int fmt, int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q,
+                              const ChainArgs& kc, const ChainArgs& vc, float scale, const int32_t* sel,
+                              const float* mass, const float* o_ref, const float* c_ref, void* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 }  // namespace flk

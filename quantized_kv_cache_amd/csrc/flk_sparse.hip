@@ -14,6 +14,7 @@
 // entry per loop instead of searching.
 #include "flk_blockscan.h"
 #include "flk_device.h"
+#include "flk_fp4_device.h"
 #include "flk_internal.h"
 #include "flk_readers.h"
 
@@ -450,8 +451,9 @@ struct GatherArgs {
 };
 
 // 8 channels (octet oc) of key position p of KV head h at the chain's depth, as binary32 values
-// that are exactly the BF16 reconstruction.
-template <int KIND, int NL>
+// that are exactly the BF16 reconstruction.  FMT: the chain's stream formats (INT4, or FP4 loops
+// as the fused decode attention takes them).
+template <int KIND, int NL, int FMT>
 __device__ __forceinline__ void gather_octet(const ChainArgs& c, const int32_t* const* maps, int32_t p, int32_t H,
                                              int32_t h, int oc, float acc[8]) {
 #pragma unroll
@@ -464,6 +466,15 @@ __device__ __forceinline__ void gather_octet(const ChainArgs& c, const int32_t* 
     if (j < 0) continue;                                     // absent: inherits
     const uint32_t item = uint32_t(j) * uint32_t(H) + uint32_t(h);
     const uint32_t cw = *reinterpret_cast<const uint32_t*>(st.codes + (item * (kSD / 2) + uint32_t(oc) * 4u));
+    float d[8];
+    if (loop_fp4<FMT>(l)) {
+      const uint32_t sb = fp4_scale_byte_128(st.params, item, oc, loop_mx<FMT>(l));
+      fp4_decode8(cw, loop_mx<FMT>(l) ? fp4_e8m0_value(sb) : fp4_e4m3_value(sb) * __uint_as_float(st.params[0]), d);
+      round_bf16x8_inplace(d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
+      continue;
+    }
     uint32_t pw[8];
     if (KIND == FLK_KIND_K) {
       const uint32_t row = c.ktile ? uint32_t(p) / kGroup : uint32_t(j) / kGroup;
@@ -475,7 +486,7 @@ __device__ __forceinline__ void gather_octet(const ChainArgs& c, const int32_t* 
 #pragma unroll
       for (int e = 0; e < 8; ++e) pw[e] = w;
     }
-    float cv[8], d[8];
+    float cv[8];
     codes8_to_f32(cw, cv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) d[e] = decode(cv[e], f16_bits_to_f32(pw[e] & 0xFFFFu), f16_bits_to_f32(pw[e] >> 16));
@@ -502,7 +513,7 @@ __device__ __forceinline__ float max16(float v) {
 
 // MODE 0 (reference statistics): partial (mass, c[128]) of p_t = exp(s_t - M) / L over the keys.
 // MODE 1 (later loop): partial (m, l, o[128]) of the online softmax over the keys.
-template <int NL, int MODE>
+template <int NL, int MODE, int FMT>
 __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) {
   __shared__ float s_m[kSWaves], s_l[kSWaves];
   __shared__ float s_o[kSWaves][kSD];
@@ -548,7 +559,7 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float kv[8];
-          gather_octet<FLK_KIND_K, NL>(g.kc, g.kmap, p, g.H, h, 4 * i + kb, kv);
+          gather_octet<FLK_KIND_K, NL, FMT>(g.kc, g.kmap, p, g.H, h, 4 * i + kb, kv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[8 * i + e], kv[e], s);
         }
@@ -567,7 +578,7 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float vv[8];
-          gather_octet<FLK_KIND_V, NL>(g.vc, g.vmap, p, g.H, h, 4 * i + kb, vv);
+          gather_octet<FLK_KIND_V, NL, FMT>(g.vc, g.vmap, p, g.H, h, 4 * i + kb, vv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[8 * i + e] = __builtin_fmaf(pn, vv[e], o[8 * i + e]);
         }
@@ -579,7 +590,7 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float vv[8];
-          gather_octet<FLK_KIND_V, NL>(g.vc, g.vmap, p, g.H, h, 4 * i + kb, vv);
+          gather_octet<FLK_KIND_V, NL, FMT>(g.vc, g.vmap, p, g.H, h, 4 * i + kb, vv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[8 * i + e] = __builtin_fmaf(w, vv[e], o[8 * i + e]);
         }
@@ -718,12 +729,12 @@ static hipError_t build_maps(const ChainArgs& c, int32_t T, int32_t* base, const
   return hipGetLastError();
 }
 
-template <int MODE>
-static hipError_t launch_gather(const GatherArgs& g, int nl, hipStream_t stream) {
+template <int MODE, int FMT>
+static hipError_t launch_gather_fmt(const GatherArgs& g, int nl, hipStream_t stream) {
   const dim3 grid(unsigned(g.nblk), unsigned(g.H * g.G));
 #define FLK_G(NLV)                                                                                        \
   case NLV:                                                                                               \
-    hipLaunchKernelGGL((sparse_gather_kernel<NLV, MODE>), grid, dim3(kSThreads), 0, stream, g);         \
+    hipLaunchKernelGGL((sparse_gather_kernel<NLV, MODE, FMT>), grid, dim3(kSThreads), 0, stream, g);    \
     break;
   switch (nl) {
     FLK_G(1) FLK_G(2) FLK_G(3) FLK_G(4) FLK_G(5) FLK_G(6) FLK_G(7) FLK_G(8)
@@ -733,16 +744,29 @@ static hipError_t launch_gather(const GatherArgs& g, int nl, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_reference(int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q, const ChainArgs& kc,
-                                   const ChainArgs& vc, float scale, void* out, int32_t* sel, float* mass,
-                                   float* o_ref, float* c_ref, void* ws, size_t ws_bytes, hipStream_t stream) {
+template <int MODE>
+static hipError_t launch_gather(const GatherArgs& g, int nl, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case 0: return launch_gather_fmt<MODE, 0>(g, nl, stream);
+    case 1: return launch_gather_fmt<MODE, 1>(g, nl, stream);
+    case 2: return launch_gather_fmt<MODE, 2>(g, nl, stream);
+    case 3: return launch_gather_fmt<MODE, 3>(g, nl, stream);
+    case 4: return launch_gather_fmt<MODE, 4>(g, nl, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_sparse_reference(int fmt, int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q,
+                                   const ChainArgs& kc, const ChainArgs& vc, float scale, void* out, int32_t* sel,
+                                   float* mass, float* o_ref, float* c_ref, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
   const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
   const SparseLayout L = sparse_layout(T, H, Hq, k, nl);
   if (ws == nullptr || ws_bytes < L.total || k < 1 || k > T) return hipErrorInvalidValue;
   char* w = static_cast<char*>(ws);
   float* scores = reinterpret_cast<float*>(w + L.scores);
   float* ml = reinterpret_cast<float*>(w + L.ml);
-  hipError_t e = launch_attn_reference(T, H, Hq, q, kc, vc, scale, out, o_ref, ml, scores, w + L.attn,
+  hipError_t e = launch_attn_reference(fmt, T, H, Hq, q, kc, vc, scale, out, o_ref, ml, scores, w + L.attn,
                                        attn_workspace_bytes(T, H, Hq), stream);
   if (e != hipSuccess) return e;
   if (T > kSplitMinT) {
@@ -780,16 +804,16 @@ hipError_t launch_sparse_reference(int32_t T, int32_t H, int32_t Hq, int32_t k, 
   g.k = k;
   g.nblk = gather_blocks(k);
   g.scale = scale;
-  if ((e = launch_gather<0>(g, vc.n_loops, stream)) != hipSuccess) return e;
+  if ((e = launch_gather<0>(g, vc.n_loops, fmt, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((sparse_combine_kernel<0>), dim3(unsigned(Hq)), dim3(kSD), 0, stream, g.part, g.nblk, mass,
                      c_ref, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_loop(int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q, const ChainArgs& kc,
-                              const ChainArgs& vc, float scale, const int32_t* sel, const float* mass,
-                              const float* o_ref, const float* c_ref, void* out, void* ws, size_t ws_bytes,
-                              hipStream_t stream) {
+hipError_t launch_sparse_loop(int fmt, int32_t T, int32_t H, int32_t Hq, int32_t k, const void* q,
+                              const ChainArgs& kc, const ChainArgs& vc, float scale, const int32_t* sel,
+                              const float* mass, const float* o_ref, const float* c_ref, void* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   const int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
   const SparseLayout L = sparse_layout(T, H, Hq, k, nl);
   if (ws == nullptr || ws_bytes < L.part + align256(size_t(Hq) * gather_blocks(k) * (2 + kSD) * sizeof(float)) ||
@@ -811,7 +835,7 @@ hipError_t launch_sparse_loop(int32_t T, int32_t H, int32_t Hq, int32_t k, const
   g.k = k;
   g.nblk = gather_blocks(k);
   g.scale = scale;
-  if ((e = launch_gather<1>(g, nl, stream)) != hipSuccess) return e;
+  if ((e = launch_gather<1>(g, nl, fmt, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((sparse_combine_kernel<1>), dim3(unsigned(Hq)), dim3(kSD), 0, stream, g.part, g.nblk, nullptr,
                      nullptr, mass, o_ref, c_ref, static_cast<uint16_t*>(out));
   return hipGetLastError();

@@ -131,6 +131,12 @@ def lib() -> ctypes.CDLL:
                                                 sz, P]
         L.flk_sparse_attn_loop.restype = ctypes.c_int
         L.flk_sparse_attn_loop.argtypes = [D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P, P, P, sz, P]
+        L.flk_sparse_attn_reference_mixed.restype = ctypes.c_int
+        L.flk_sparse_attn_reference_mixed.argtypes = [D, D, D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P,
+                                                      P, P, P, P, sz, P]
+        L.flk_sparse_attn_loop_mixed.restype = ctypes.c_int
+        L.flk_sparse_attn_loop_mixed.argtypes = [D, D, D, D, i32, P, i32, S, S, i32, i32, ctypes.c_float, P, P, P, P,
+                                                 P, P, sz, P]
         for name in ("flk_desc_init_nvfp4", "flk_desc_init_mxfp4"):
             f = getattr(L, name)
             f.restype = None
@@ -539,13 +545,34 @@ class SparseState:
                            torch.empty((n_q_heads, D), dtype=torch.float32, device=device))
 
 
+def _mixed_descs(k_chain: Sequence[Packed], v_chain: Sequence[Packed], H: int, D: int):
+    """The four descriptors of the *_mixed calls, or None when both chains are INT4 throughout."""
+    kb, kr = _chain_formats(k_chain)
+    vb, vr = _chain_formats(v_chain)
+    if {kb, kr, vb, vr} == {INT4}:
+        return None
+    return [desc(K, H, D, k_chain[0].k_tiles, fmt=kb), desc(K, H, D, fmt=kr), desc(V, H, D, fmt=vb),
+            desc(V, H, D, fmt=vr)]
+
+
 def sparse_attn_reference(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int, H: int,
                           k: int, softmax_scale: float, out: torch.Tensor, state: SparseState,
                           workspace: torch.Tensor, stream=None) -> None:
+    """The reference loop over INT4 chains, or (flk_sparse_attn_reference_mixed) chains with FP4
+    streams; formats taken from the streams."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.bfloat16, "out")
     Hq, D = q.shape
     ka, va = _chain(k_chain), _chain(v_chain)
+    mixed = _mixed_descs(k_chain, v_chain, H, D)
+    if mixed is not None:
+        _check(lib().flk_sparse_attn_reference_mixed(*[ctypes.byref(d) for d in mixed], T, _ptr(q), Hq, ka, va,
+                                                     len(k_chain), k, float(softmax_scale), _ptr(out),
+                                                     _ptr(state.sel), _ptr(state.mass), _ptr(state.o_ref),
+                                                     _ptr(state.c_ref), _ptr(workspace),
+                                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+               "flk_sparse_attn_reference_mixed")
+        return
     _check(lib().flk_sparse_attn_reference(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles)), ctypes.byref(desc(V, H, D)),
                                            T, _ptr(q), Hq, ka, va, len(k_chain), k, float(softmax_scale), _ptr(out),
                                            _ptr(state.sel), _ptr(state.mass), _ptr(state.o_ref), _ptr(state.c_ref),
@@ -556,10 +583,19 @@ def sparse_attn_reference(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: S
 def sparse_attn_loop(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int, H: int, k: int,
                      softmax_scale: float, state: SparseState, out: torch.Tensor, workspace: torch.Tensor,
                      stream=None) -> None:
+    """A later loop over INT4 chains, or (flk_sparse_attn_loop_mixed) chains with FP4 streams."""
     _need(q, torch.bfloat16, "q")
     _need(out, torch.bfloat16, "out")
     Hq, D = q.shape
     ka, va = _chain(k_chain), _chain(v_chain)
+    mixed = _mixed_descs(k_chain, v_chain, H, D)
+    if mixed is not None:
+        _check(lib().flk_sparse_attn_loop_mixed(*[ctypes.byref(d) for d in mixed], T, _ptr(q), Hq, ka, va,
+                                                len(k_chain), k, float(softmax_scale), _ptr(state.sel),
+                                                _ptr(state.mass), _ptr(state.o_ref), _ptr(state.c_ref), _ptr(out),
+                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                _stream(stream)), "flk_sparse_attn_loop_mixed")
+        return
     _check(lib().flk_sparse_attn_loop(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles)), ctypes.byref(desc(V, H, D)), T,
                                       _ptr(q), Hq, ka, va, len(k_chain), k, float(softmax_scale), _ptr(state.sel),
                                       _ptr(state.mass), _ptr(state.o_ref), _ptr(state.c_ref), _ptr(out),

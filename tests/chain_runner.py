@@ -28,7 +28,9 @@ class GpuChain:
     a copy of the reconstruction after every loop."""
 
     def __init__(self, kind: int, xs: Sequence[np.ndarray], rows: Sequence[Optional[np.ndarray]],
-                 status: Optional[torch.Tensor] = None, k_tiles: bool = False):
+                 status: Optional[torch.Tensor] = None, k_tiles: bool = False, fmt: str = "int4",
+                 base_fmt: Optional[str] = None):
+        """fmt: the residual loops' stream format; base_fmt: the base loop's (default fmt)."""
         T, H, D = xs[0].shape
         self.kind, self.T, self.H, self.D = kind, T, H, D
         self.recon = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
@@ -37,7 +39,8 @@ class GpuChain:
         for loop, (x, r) in enumerate(zip(xs, rows)):
             xd = to_dev_bf16(x)
             rd = to_dev_rows(r)
-            p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T, k_tiles=k_tiles)
+            f = (base_fmt or fmt) if loop == 0 else fmt
+            p = flk.Packed.empty(kind, H, D, x.shape[0], rd, T=T, k_tiles=k_tiles, fmt=f)
             if loop == 0:
                 flk.encode_base(kind, xd, p, self.recon, status)
             else:

@@ -513,3 +513,39 @@ def test_largest_tensor_bound():
         assert L.flk_encode_residual(ctypes.byref(d), FAKE, None, T, T, FAKE, FAKE, FAKE, None, None, None) == 2
         chain = (flk.StreamC * 1)(flk.StreamC(T, 0, None, FAKE.value, FAKE.value, None))
         assert L.flk_reconstruct(ctypes.byref(d), T, chain, 1, FAKE, None) == 2
+
+
+def test_sparse_mixed_validation():
+    """The sparse *_mixed calls resolve formats as flk_decode_attn_mixed does, then apply the
+    INT4 calls' checks; the INT4 calls still refuse FP4 descriptors."""
+    L = flk.lib()
+    S = flk.StreamC
+    T, Hq, k = 256, 32, 16
+    chain = (S * 2)(S(T, 0, None, FAKE.value, FAKE.value, None), S(T, 0, None, FAKE.value, FAKE.value, None))
+    ki4, kf4, kmx = (flk.desc(flk.K, 8, 128, fmt=f) for f in ("int4", "nvfp4", "mxfp4"))
+    vi4, vf4, vmx = (flk.desc(flk.V, 8, 128, fmt=f) for f in ("int4", "nvfp4", "mxfp4"))
+    ws = flk.sparse_workspace_bytes(8, 128, T, Hq, k, 2)
+
+    def ref(kb, kr, vb, vr, q=FAKE, kk=k, wb=ws):
+        return L.flk_sparse_attn_reference_mixed(ctypes.byref(kb), ctypes.byref(kr), ctypes.byref(vb),
+                                                 ctypes.byref(vr), T, q, Hq, chain, chain, 2, kk, 0.088, FAKE,
+                                                 FAKE, FAKE, FAKE, FAKE, FAKE, wb, None)
+
+    def loop(kb, kr, vb, vr, q=FAKE):
+        return L.flk_sparse_attn_loop_mixed(ctypes.byref(kb), ctypes.byref(kr), ctypes.byref(vb), ctypes.byref(vr),
+                                            T, q, Hq, chain, chain, 2, k, 0.088, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            ws, None)
+    assert ref(vi4, kf4, vi4, vf4) == 4                   # a V descriptor for K
+    assert ref(kf4, kmx, vf4, vmx) == 5                   # NVFP4 base, MXFP4 residuals
+    assert ref(ki4, kf4, vi4, vmx) == 5                   # K and V formats differ
+    assert ref(kf4, ki4, vf4, vi4) == 5                   # FP4 base, INT4 residuals
+    assert ref(ki4, kf4, vi4, vf4, q=None) == 1
+    assert ref(ki4, kmx, vi4, vmx, kk=0) == 2
+    assert ref(ki4, kmx, vi4, vmx, wb=64) == 6
+    assert loop(ki4, kf4, vi4, vf4, q=None) == 1
+    assert loop(kf4, kmx, vf4, vmx) == 5
+    kt = flk.desc(flk.K, 8, 128, k_tiles=True)
+    assert ref(kt, kf4, vi4, vf4) == 5                    # tile-grouped K with FP4 residuals
+    # the INT4-only calls refuse FP4 descriptors
+    assert L.flk_sparse_attn_reference(ctypes.byref(kf4), ctypes.byref(vi4), T, FAKE, Hq, chain, chain, 2, k, 0.088,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 5

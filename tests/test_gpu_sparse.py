@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import fp4 as ofp4
 from oracle import oracle as orc
 from quantized_kv_cache_amd import flk, synth
 
@@ -247,3 +248,45 @@ def test_sparse_attention_long_context():
     fed = _gpu_loops(g, T, H, Hq, k, qs, scale, _state_from(parts, Hq, k), ws)
     for h in (0, 5):
         _compare(gpu, fed, orcs[h], qs, scale, H, Hq, k, slice(h * G, (h + 1) * G), tag=f"kv head {h}")
+
+
+class _Fp4Oracle:
+    """The oracle's reconstructions after every loop of an FP4 chain (NVFP4 or MXFP4 residual
+    loops on an INT4 or same-format base)."""
+
+    def __init__(self, kind, xs, rows, fmt, int4_base):
+        mx = fmt == "mxfp4"
+        _, recon = orc.encode_base(kind, xs[0]) if int4_base else ofp4.encode_base(xs[0], mx=mx)
+        self.recons = [recon.copy()]
+        for x, r in zip(xs[1:], rows[1:]):
+            ofp4.encode_residual(x, r, recon, mx=mx)
+            self.recons.append(recon.copy())
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("int4_base", [False, True])
+@pytest.mark.parametrize("T,H,Hq,sizes,k", [
+    (1000, 2, 8, [None, None, 500, 250], 37),
+    (2049, 4, 64, [None, 2049, 1024, 1], 300),           # G = 16, a 1-row compact loop
+])
+def test_sparse_attention_fp4(T, H, Hq, sizes, k, int4_base, fmt):
+    """The reference and later loops over FP4 chains (keys and values decoded from NVFP4 or MXFP4
+    residual loops, on an INT4 or FP4 base), against the oracle's sparse attention over the FP4
+    oracle's reconstructions."""
+    D = 128
+    rng = np.random.default_rng(T + H + k + 7)
+    xs, rows = _chains(rng, T, H, D, sizes)
+    base = "int4" if int4_base else fmt
+    g = {kind: GpuChain(kind, xs[kind], rows, fmt=fmt, base_fmt=base) for kind in (flk.K, flk.V)}
+    o = {kind: _Fp4Oracle(kind, xs[kind], rows, fmt, int4_base) for kind in (flk.K, flk.V)}
+    for kind in (flk.K, flk.V):                          # the chains themselves agree bit for bit
+        for loop in range(len(sizes)):
+            assert np.array_equal(g[kind].recons[loop], o[kind].recons[loop]), f"{fmt} recon loop {loop + 1}"
+    qs = {d: synth.to_bf16_bits(rng.standard_normal((Hq, D)).astype(np.float32)) for d in range(2, len(sizes) + 1)}
+    scale = 1.0 / math.sqrt(D)
+    say(f"sparse attention {fmt} int4_base={int4_base} T={T} H={H} Hq={Hq} k={k}")
+    ws = _workspace(T, H, Hq, k, len(sizes))
+    gpu = _gpu_reference(g, T, H, Hq, k, qs, scale, ws)
+    ref = orc.sparse_reference(qs[2], o[flk.K].recons[1], o[flk.V].recons[1], scale, k)
+    fed = _gpu_loops(g, T, H, Hq, k, qs, scale, _state_from([(slice(None), ref)], Hq, k), ws)
+    _compare(gpu, fed, o, qs, scale, H, Hq, k, slice(None), tag=f"{fmt} int4_base={int4_base} T={T} k={k}")
