@@ -158,7 +158,7 @@ __device__ __forceinline__ void build_maps(const ChainArgs& c, const TileRows<NL
 // Decode 4 items (token tk of the tile, octets oc[i]) of one chain; out[i] receives item i's
 // 8 channels as packed BF16 (zeros for an absent or out-of-range token).  Every code word is
 // requested first; then one item at a time is decoded, so only one item's binary32 values
-// are live.  K: parameters from the staged rows; V: one parameter per item.
+// are live.  K: parameters from the staged rows; V: the row's two parameter words, one load.
 template <int KIND, int NL, int FMT = 0>
 __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<NL>& r, int32_t t0, int32_t T,
                                              int32_t H, int32_t h, int tk, const int oc[4],
@@ -167,7 +167,7 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
   const int nl = c.n_loops;
   const int32_t t = t0 + tk;
   int32_t j[NL];
-  uint32_t cw[NL][4], vp[NL][4], sw[NL][2];
+  uint32_t cw[NL][4], sw[NL][2];
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     j[l] = -1;
@@ -175,13 +175,14 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
     // FP4 loops: the item's block scales in one load -- its 4 E8M0 bytes (MXFP4, one per 32
     // channels) or its 8 E4M3 bytes after the 16-byte header (NVFP4, one per 16 channels);
     // the bytes are picked at decode time, so no load waits before the others are issued
+    // (INT4 V loops likewise: the item's two (min, scale) words, one per 64 channels)
     sw[l][0] = sw[l][1] = 0u;
-    if (loop_fp4<FMT>(l) && j[l] >= 0) {
+    if ((loop_fp4<FMT>(l) || KIND == FLK_KIND_V) && j[l] >= 0) {
       const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
       if (loop_mx<FMT>(l)) {
         sw[l][0] = c.s[l].params[item];
       } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(c.s[l].params + 4u + item * 2u);
+        const uint2 w = *reinterpret_cast<const uint2*>(c.s[l].params + (loop_nv<FMT>(l) ? 4u : 0u) + item * 2u);
         sw[l][0] = w.x;
         sw[l][1] = w.y;
       }
@@ -189,12 +190,10 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       cw[l][i] = 0;
-      vp[l][i] = 0;
       if (j[l] >= 0) {
         // uniform base + 32-bit offset: one saddr load, no 64-bit address arithmetic per lane
         const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
         cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (item * (kAttnD / 2) + uint32_t(oc[i]) * 4u));
-        if (KIND == FLK_KIND_V && !loop_fp4<FMT>(l)) vp[l][i] = c.s[l].params[item * 2u + uint32_t(oc[i] >> 3)];
       }
     }
   }
@@ -221,9 +220,10 @@ __device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<
           const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
           const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
           p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
-        } else {
+        } else {                                         // V: the octet's 64-channel group
+          const uint32_t w = (oc[i] >> 3) ? sw[l][1] : sw[l][0];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = vp[l][i];
+          for (int e = 0; e < 8; ++e) p[e] = w;
         }
         decode_item(cw[l][i], p, d);
       }
