@@ -226,12 +226,12 @@ def page_local_leg(w, host, sets, streams, steps, warmup, rotate):
     iso_streams = {k: (iso_stream, ctypes.c_void_p(iso_stream.cuda_stream)) for k in (flk.K, flk.V)}
     n_calls = len(cs[0].calls)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
-    iso = np.zeros(n_calls)
+    iso = []
     for k in range(10):
         cs[k % rotate].run(iso_streams, ev)
         torch.cuda.synchronize()
-        iso += np.array([a.elapsed_time(b) for a, b in ev])
-    iso_us = iso / 10 * 1e3
+        iso.append([a.elapsed_time(b) for a, b in ev])
+    iso_us = np.median(np.array(iso), axis=0) * 1e3           # median: one slow launch moves no figure
     k_calls = [{"call": name, "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
                for (kind, name, b), t in zip(per_call, iso_us) if kind == flk.K]
     rows_k = call_bytes(flk.K, w.H, w.D, w.T, sets)
@@ -1035,13 +1035,13 @@ def main():
     # each call alone: one stream, events around every call, nothing overlapping
     iso_stream = torch.cuda.Stream()
     iso_streams = {k: (iso_stream, ctypes.c_void_p(iso_stream.cuda_stream)) for k in (flk.K, flk.V)}
-    iso = np.zeros(n_calls)
+    iso = []
     n_iso = 10
     for k in range(n_iso):
         chain_sets[k % args.rotate].run(iso_streams, ev)
         torch.cuda.synchronize()
-        iso += np.array([a.elapsed_time(b) for a, b in ev])
-    iso_us = iso / n_iso * 1e3
+        iso.append([a.elapsed_time(b) for a, b in ev])
+    iso_us = np.median(np.array(iso), axis=0) * 1e3           # median: one slow launch moves no figure
     per_call_iso = [{"tensor": {flk.K: "K", flk.V: "V", KV: "K+V"}[kind], "call": name, "kernel": sy,
                      "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
                     for (kind, name, b), sy, t in zip(per_call, symbols, iso_us)]
