@@ -292,6 +292,15 @@ def cpu_baseline_rows(w, host, sets):
     b, _ = _format_bytes(flk.K, SimpleNamespace(H=1, D=w.D, T=w.T), sets, "nvfp4", "nvfp4")
     rows["nvfp4"] = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
                      "sample": f"K chain of KV head 0 (1/{w.H} of the tensor), 4 loops + reconstruct: {dt:.2f} s"}
+    t0 = time.perf_counter()
+    _, recon = ofp4.encode_base(xs[0], mx=True)
+    base = recon.copy()
+    streams = [ofp4.encode_residual(x, r, recon, mx=True) for x, r in zip(xs[1:], sets[1:])]
+    ofp4.apply_residuals(base, streams)
+    dt = time.perf_counter() - t0
+    b, _ = _format_bytes(flk.K, SimpleNamespace(H=1, D=w.D, T=w.T), sets, "mxfp4", "mxfp4")
+    rows["mxfp4"] = {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                     "sample": f"K chain of KV head 0 (1/{w.H} of the tensor), 4 loops + reconstruct: {dt:.2f} s"}
     # sparse decode attention: the reference and one later loop for the 4 query heads of one KV
     # head over 131072 tokens (BF16 K/V drawn like the decode workload's), k = 4096
     wd = synth.WORKLOADS[5]
