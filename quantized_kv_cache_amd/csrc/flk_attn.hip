@@ -256,8 +256,13 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   const int wave = uniform(threadIdx.x >> 6);
   const int n = lane & 15;                                // MFMA column: query head / token / channel
   const int kb = lane >> 4;                               // MFMA k-block / row block
-  const int32_t split = blockIdx.x;
-  const int32_t h = blockIdx.y;
+  // Blocks are renumbered split-major, head-minor, and each XCD runs a contiguous range of the
+  // new numbers: the H heads of a token range run together in one L2.  A token's codes of heads
+  // 2m and 2m+1 share a 128-byte line, and a row's V parameters of all heads share one, so
+  // those lines are fetched once instead of once per head.
+  const uint32_t lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int32_t split = int32_t(lin / gridDim.y);
+  const int32_t h = int32_t(lin % gridDim.y);
   const int32_t Hq = H * G;
   const int32_t ptiles = (T + kGroup - 1) / kGroup;       // packed tiles
   // the head's packed tiles, ptiles / wph per wave and one more for the first ptiles % wph
