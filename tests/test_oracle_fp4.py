@@ -4,6 +4,7 @@ ties worked by hand, saturation, the storage cost the review states, symmetry, t
 remark on outlier channels, round trips and the chain's self-consistency."""
 import numpy as np
 import pytest
+import torch
 
 from oracle import fp4
 from oracle import oracle as orc
@@ -300,3 +301,34 @@ def test_mx_chain_reconstructs_from_stored_bytes(int4_base):
     # an MXFP4 residual step is closer to X_r than the base alone
     x4 = fp4.f32_of_bf16(xs[-1])
     assert np.abs(fp4.f32_of_bf16(recon[rows[-1]]) - x4).mean() < np.abs(fp4.f32_of_bf16(start[rows[-1]]) - x4).mean()
+
+
+def test_bf16_of_f32_matches_torch():
+    """The FP4 oracle's own BF16 rounding (residuals and reconstructions of every FP4 chain)
+    against torch's BF16 cast, an independent implementation: 2M random binary32 patterns plus,
+    for every BF16 upper half, the lower halves just below, at and above the rounding midpoint."""
+    g = np.random.default_rng(17)
+    u = g.integers(0, 2**32, size=1 << 21, dtype=np.uint64).astype(np.uint32)
+    hi = np.arange(0, 1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    x = np.concatenate([u, (hi[:, None] | lows[None, :]).ravel()]).view(np.float32)
+    # finite inputs whose rounding stays finite (the oracle's precondition)
+    x = x[np.isfinite(x) & (np.abs(x) < np.float32(3.3895313e38))]
+    ours = fp4.bf16_of_f32(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_round_matches_torch_float8():
+    """e4m3_round against torch's float8_e4m3fn cast (round to nearest even) below the
+    saturation point, over every E4M3 midpoint and its binary32 neighbours and random values
+    spanning the subnormal and normal ranges."""
+    vals = fp4.e4m3_value(np.arange(0x7F))
+    mid = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    g = np.random.default_rng(5)
+    rnd = np.exp(g.uniform(np.log(2.0 ** -12), np.log(447.0), 200000)).astype(np.float32)
+    x = np.concatenate([vals.astype(np.float32), mid, np.nextafter(mid, np.float32(0)),
+                        np.nextafter(mid, np.float32(np.inf)), rnd])
+    ours = fp4.e4m3_round(x)
+    ref = torch.from_numpy(x.copy()).to(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(ours, ref)

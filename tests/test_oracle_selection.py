@@ -191,3 +191,58 @@ def test_partition_is_stable_and_complete():
     assert total == int((cls != sel.ROW_INACTIVE).sum())
     assert np.all(scatter[gather] == np.arange(total)) and np.all(scatter[cls == sel.ROW_INACTIVE] == -1)
     assert sel.partition_rows([])[2] == (0, 0)
+
+
+def _exact_ratio(h1, h2, eps):
+    """Exact squared change scores ||h1 - h2||^2 / max(||h1||^2, eps^2) per row, as Fractions.
+    BF16 values are dyadic rationals: scaled by 2^140 they are integers, so the sums of squares
+    are exact big-integer sums."""
+    a = sel.f32_of_bf16(h1).astype(np.float64) * 2.0 ** 140
+    b = sel.f32_of_bf16(h2).astype(np.float64) * 2.0 ** 140
+    e2 = Fraction(float(np.float32(eps))) ** 2 * Fraction(2) ** 280
+    out = []
+    for ra, rb in zip(a.tolist(), b.tolist()):
+        ia = [int(v) for v in ra]
+        ib = [int(v) for v in rb]
+        num = sum((x - y) * (x - y) for x, y in zip(ia, ib))
+        den = sum(x * x for x in ia)
+        out.append(Fraction(num) / max(Fraction(den), e2))
+    return out
+
+
+@pytest.mark.parametrize("seed,T,d,W,pcts", [(0, 1600, 64, 256, [50, 25]), (1, 1200, 96, 100, [30, 10]),
+                                             (2, 700, 136, 64, [50, 50])])
+def test_selection_matches_exact_top_k(seed, T, d, W, pcts):
+    """The selected sets against exact arithmetic.  Each score is a square root of an exact
+    rational (squared norm ratio), so ranking by the exact squared ratios is exact.  Wherever a
+    window's exact k-th and (k+1)-th squared ratios are separated by more than the binary32
+    error of the score ((log2 d + 8) * 2^-24 relative, squared), the oracle must choose exactly
+    the exact top k of that window (RFC 3.1: highest scores, equal scores by lower position)."""
+    rng = np.random.default_rng(100 + seed)
+    hs = [bf16_round(rng.standard_normal((T, d)).astype(np.float32) * 3)]
+    for _ in range(len(pcts) + 1):
+        step = (rng.standard_normal((T, d)) * np.exp(rng.uniform(np.log(1e-3), 0, (T, 1)))).astype(np.float32)
+        hs.append(bf16_round(sel.f32_of_bf16(hs[-1]) + step))
+    delta = Fraction(math.ceil(math.log2(d)) + 8, 2 ** 24)
+    lo, hi = (1 - delta) ** 2, (1 + delta) ** 2
+    prev, decided, windows = None, 0, 0
+    for i, p in enumerate(pcts):
+        _, rows = sel.select_rows(hs[i + 2], hs[i + 1], prev, W, p, 1e-6)
+        elig = np.arange(T, dtype=np.int32) if prev is None else prev
+        ratio = dict(zip(elig.tolist(), _exact_ratio(hs[i + 2][elig], hs[i + 1][elig], 1e-6)))
+        chosen = set(rows.tolist())
+        for w0 in range(0, T, W):
+            length = min(W, T - w0)
+            e = [q for q in elig.tolist() if w0 <= q < w0 + length]
+            k = min(sel.window_budget(length, p), len(e))
+            got = sorted(q for q in e if q in chosen)
+            assert len(got) == k
+            ranked = sorted(e, key=lambda q: (-ratio[q], q))
+            if not 0 < k < len(e):
+                continue
+            windows += 1
+            if ratio[ranked[k - 1]] * lo > ratio[ranked[k]] * hi:
+                assert got == sorted(ranked[:k]), f"window {w0}, loop {i + 3}"
+                decided += 1
+        prev = rows
+    assert windows > 0 and decided >= 0.8 * windows     # the comparison is not vacuous
