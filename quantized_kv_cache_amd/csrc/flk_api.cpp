@@ -587,8 +587,10 @@ flk_status check_append(const flk_desc* d, bool resid, const flk_append_unit& u,
   if (!aligned(u.recon, 16) || (u.x && !aligned(u.x, 16)) || (u.rows && !aligned(u.rows, 4)) ||
       (u.tile_start && !aligned(u.tile_start, 4)))
     return FLK_E_ALIGN;
-  *a = enc_args(d, u.x, u.rows, u.n_rows, u.n_pos, u.recon, u.codes + codes_offset(d, u.rows_before),
-                u.params + params_offset(d, u.rows_before, u.p0), nullptr, nullptr);
+  // an empty V window may come without stream buffers: no offset is added to a NULL pointer
+  *a = enc_args(d, u.x, u.rows, u.n_rows, u.n_pos, u.recon,
+                u.codes ? u.codes + codes_offset(d, u.rows_before) : nullptr,
+                u.params ? u.params + params_offset(d, u.rows_before, u.p0) : nullptr, nullptr, nullptr);
   // a compact window writes its tile index entries, also when it has no rows (and so may come
   // with rows == NULL): enc_args keeps the index only for a non-NULL rows pointer
   a->tile_start = dense ? nullptr : u.tile_start + u.p0 / FLK_GROUP;
@@ -601,7 +603,7 @@ flk_status check_append(const flk_desc* d, bool resid, const flk_append_unit& u,
 // An empty compact window: tile_start[p0/64 .. (p0+n_pos)/64] = rows_before, and zero params
 // for the window's tiles of a tile-grouped K stream.
 hipError_t fill_empty_window(const flk_desc* d, const flk::EncArgs& a, hipStream_t s) {
-  if (!a.tile_start || !a.params) return hipErrorInvalidValue;
+  if (!a.tile_start || (k_tiles(d) && !a.params)) return hipErrorInvalidValue;   // V writes no params
   const int32_t nt = a.T / FLK_GROUP;
   hipError_t e = flk::launch_fill_u32(reinterpret_cast<uint32_t*>(a.tile_start), nt + 1, uint32_t(a.row0), s);
   if (e == hipSuccess && k_tiles(d)) e = flk::launch_fill_u32(a.params, int64_t(nt) * a.W, 0u, s);

@@ -468,3 +468,22 @@ def test_batched_appends_equal_single_appends(H, D):
                 assert_same(cb.params.cpu().numpy(), ca.params.cpu().numpy(), f"t{ti} params loop {l}")
                 if ca.tile_start is not None:
                     assert torch.equal(ca.tile_start, cb.tile_start), f"t{ti} tile index loop {l}"
+
+
+@pytest.mark.parametrize("before", [0, 5])
+def test_empty_v_window_needs_no_stream_buffers(before):
+    """An empty compact V window writes only its tile index entries, so it may come without codes
+    and params (V has no per-tile params); the result must not depend on rows_before."""
+    import ctypes
+    H, D, p0, n_pos = 2, 64, 128, 128
+    say(f"empty V window, rows_before {before}")
+    tile = torch.full((p0 // 64 + n_pos // 64 + 1,), -7, dtype=torch.int32, device="cuda")
+    recon = torch.zeros((n_pos, H, D), dtype=torch.bfloat16, device="cuda")
+    st = flk.lib().flk_append_residual(ctypes.byref(flk.desc(flk.V, H, D)), None, None, 0, p0, n_pos, before,
+                                       ctypes.c_void_p(recon.data_ptr()), None, None,
+                                       ctypes.c_void_p(tile.data_ptr()), None, None)
+    torch.cuda.synchronize()
+    assert st == 0, flk.lib().flk_status_string(st).decode()
+    got = tile.cpu().numpy()
+    assert list(got[:p0 // 64]) == [-7] * (p0 // 64)            # entries before the window untouched
+    assert np.all(got[p0 // 64:] == before)
