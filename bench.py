@@ -922,6 +922,47 @@ def summarize_trace(trace_dir, warmup, steps, isolated=10):
     return "\n".join(lines)
 
 
+def summarize_counters(dirs, n_cu=256, clock_mhz=2400.0):
+    """Per-kernel instruction and occupancy counters from rocprofv3 --pmc runs (CSV output, one
+    counter set per run; every run over the same command), as a table of per-dispatch medians.
+    Derived columns use the dispatch's duration at the nominal 2.4 GHz clock: VALU issue share
+    (SQ_INSTS_VALU against one VALU wave-instruction per CU per cycle) and mean resident waves
+    per CU (SQ_WAVE_CYCLES counts wave quad-cycles); also VALU instructions per wave."""
+    import csv
+    import glob
+    import statistics
+    vals, dur = {}, {}
+    for d in dirs:
+        seen = set()
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                k = _short_name(r["Kernel_Name"])
+                if not (k.startswith(("encode", "reconstruct", "attn", "sparse", "fp4", "select"))):
+                    continue
+                vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                key = (path, r["Dispatch_Id"])
+                if key not in seen:
+                    seen.add(key)
+                    dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = []
+    for k in sorted(vals, key=lambda k: -statistics.median(dur[k]) * len(dur[k])):
+        med = {c: statistics.median(v) for c, v in vals[k].items()}
+        us = statistics.median(dur[k])
+        lines.append(f"kernel {k} | dispatches {len(dur[k])} | median_us {us:.2f}")
+        lines.append("  " + " | ".join(f"{c} {v:.0f}" for c, v in sorted(med.items())))
+        derived = []
+        cyc = us * clock_mhz
+        if "SQ_INSTS_VALU" in med:
+            derived.append(f"valu_issue_share {med['SQ_INSTS_VALU'] / (n_cu * cyc):.3f}")
+        if "SQ_WAVE_CYCLES" in med:
+            derived.append(f"mean_waves_per_cu {4 * med['SQ_WAVE_CYCLES'] / (n_cu * cyc):.1f}")
+        if "SQ_INSTS_VALU" in med and med.get("SQ_WAVES"):
+            derived.append(f"valu_per_wave {med['SQ_INSTS_VALU'] / med['SQ_WAVES']:.0f}")
+        if derived:
+            lines.append("  derived: " + " | ".join(derived))
+    return "\n".join(lines)
+
+
 def read_traffic(symbol):
     """Per-launch HBM bytes of `symbol` from the committed counter summary, or None when there is
     none or it was taken from other sources than the ones built now."""
@@ -964,12 +1005,18 @@ def main():
                     help="run a plain copy of known size first (calibrates the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="print the traffic table from rocprofv3 counter output and exit (no GPU)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print per-kernel instruction/occupancy counters from rocprofv3 --pmc CSV runs, and exit "
+                         "(no GPU)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel durations (all calls, timed region) from a rocprofv3 kernel trace "
                          "of a run with the same --warmup/--steps, and exit (no GPU)")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
