@@ -288,6 +288,27 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
                                   float softmax_scale, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Largest scratch area flk_decode_attn_packed_noalloc uses: a device array of this many bytes,
+ * one copy per GPU the library runs on, held until the process ends. */
+#define FLK_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* flk_decode_attn_packed without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The per-split partial results go to the library's own device array of
+ * FLK_NOALLOC_SCRATCH_BYTES bytes on the current device (located on the first call on that
+ * device); the call allocates nothing.  Every call on one GPU uses the same array, which keeps
+ * the last call's contents (each call writes every partial it reads): calls that may overlap
+ * in time on one GPU (streams not ordered with each other) race, and their outputs are then
+ * undefined.  Arguments as flk_decode_attn_packed.
+ * Errors: those of flk_decode_attn_packed; FLK_E_WORKSPACE when the call needs more than
+ * FLK_NOALLOC_SCRATCH_BYTES (flk_attn_workspace_bytes(k_desc, T, n_q_heads) bounds the need;
+ * 131072 tokens, 8 KV heads and 32 query heads need about 4.3 MB); FLK_E_LAUNCH when the
+ * array cannot be located on the current device or a launch fails.                         */
+flk_status flk_decode_attn_packed_noalloc(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T,
+                                          const void* q, int32_t n_q_heads, const flk_stream* k_chain,
+                                          const flk_stream* v_chain, int32_t n_loops, float softmax_scale,
+                                          void* out, void* stream);
+
 /* flk_decode_attn_packed over chains whose streams are INT4 throughout, an INT4 base with FP4
  * residual loops, or FP4 throughout, the FP4 loops all NVFP4 or all MXFP4 (PR #166 review,
  * item 2: the comparison that counts is speed and accuracy with dequantization and residual

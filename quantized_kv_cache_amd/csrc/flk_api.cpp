@@ -296,11 +296,13 @@ flk_status flk_reconstruct_mixed(const flk_desc* bd, const flk_desc* rd, int32_t
                                                static_cast<hipStream_t>(stream)));
 }
 
-flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
-                                  int32_t n_q_heads, const flk_stream* k_chain,
-                                  const flk_stream* v_chain, int32_t n_loops, float softmax_scale,
-                                  void* out, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+namespace {
+
+// The checks flk_decode_attn_packed and flk_decode_attn_packed_noalloc share (all but the
+// workspace); on FLK_OK the chains are loaded into kc and vc.
+flk_status check_decode_attn(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q, int32_t n_q_heads,
+                             const flk_stream* k_chain, const flk_stream* v_chain, int32_t n_loops, const void* out,
+                             flk::ChainArgs* kc, flk::ChainArgs* vc) {
   flk_status st = int4_desc(kd);
   if (st != FLK_OK) return st;
   st = int4_desc(vd);
@@ -310,12 +312,24 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
   if (!q || !out) return FLK_E_NULL;
   if (T < 1 || !rows_fit(kd, T) || n_q_heads < 1 || n_q_heads % kd->n_heads != 0) return FLK_E_SHAPE;
   if (kd->head_dim != 128 || n_q_heads / kd->n_heads > 16) return FLK_E_UNSUPPORTED;
-  flk::ChainArgs kc, vc;
-  st = load_chain(kd, T, k_chain, n_loops, &kc);
+  st = load_chain(kd, T, k_chain, n_loops, kc);
   if (st != FLK_OK) return st;
-  st = load_chain(vd, T, v_chain, n_loops, &vc);
+  st = load_chain(vd, T, v_chain, n_loops, vc);
   if (st != FLK_OK) return st;
   if (!aligned(q, 16) || !aligned(out, 16)) return FLK_E_ALIGN;
+  return FLK_OK;
+}
+
+}  // namespace
+
+flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                                  int32_t n_q_heads, const flk_stream* k_chain,
+                                  const flk_stream* v_chain, int32_t n_loops, float softmax_scale,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  flk::ChainArgs kc, vc;
+  const flk_status st = check_decode_attn(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, out, &kc, &vc);
+  if (st != FLK_OK) return st;
   // the exact need of this launch (flk_attn_workspace_bytes is a bound on it)
   const size_t need = flk::attn_workspace_need(T, 0, kd->n_heads, n_q_heads);
   if (!workspace || workspace_bytes < need) return FLK_E_WORKSPACE;
@@ -323,6 +337,18 @@ flk_status flk_decode_attn_packed(const flk_desc* kd, const flk_desc* vd, int32_
   return to_status(flk::launch_decode_attn(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc, nullptr,
                                            nullptr, 0, softmax_scale, out, workspace, workspace_bytes,
                                            static_cast<hipStream_t>(stream)));
+}
+
+flk_status flk_decode_attn_packed_noalloc(const flk_desc* kd, const flk_desc* vd, int32_t T, const void* q,
+                                          int32_t n_q_heads, const flk_stream* k_chain, const flk_stream* v_chain,
+                                          int32_t n_loops, float softmax_scale, void* out, void* stream) {
+  flk::ChainArgs kc, vc;
+  const flk_status st = check_decode_attn(kd, vd, T, q, n_q_heads, k_chain, v_chain, n_loops, out, &kc, &vc);
+  if (st != FLK_OK) return st;
+  if (flk::attn_workspace_need(T, 0, kd->n_heads, n_q_heads) > size_t(FLK_NOALLOC_SCRATCH_BYTES))
+    return FLK_E_WORKSPACE;
+  return to_status(flk::launch_decode_attn_noalloc(T, kd->n_heads, kd->head_dim, n_q_heads, q, kc, vc,
+                                                   softmax_scale, out, static_cast<hipStream_t>(stream)));
 }
 
 namespace {

@@ -17,10 +17,18 @@
 // At the end the block's 4 waves merge their (m, l, O) through LDS into one partial per
 // (block, query head); a second kernel merges the partials of all blocks.  A BF16 tail (a
 // rolling cache's recent tokens) is read as stored, 16 tokens per wave.
+#include <mutex>
+
 #include "flk_device.h"
 #include "flk_fp4_device.h"
 #include "flk_internal.h"
 #include "flk_readers.h"
+
+// The partials buffer of flk_decode_attn_packed_noalloc, for callers that cannot allocate: one
+// copy per GPU, held until the process ends, shared by every such call on that GPU.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for the symbol); it uses
+// the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FLK_NOALLOC_SCRATCH_BYTES];
 
 namespace flk {
 
@@ -577,6 +585,41 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
   (void)D;
   return launch_attn<false>(T, H, Hq, q, kc, vc, k_tail, v_tail, tail_len, scale, out, nullptr, nullptr, nullptr,
                             ws, ws_bytes, stream);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];    // device address of `scratch` per device, found once
+
+// The current device's copy of `scratch`, looked up on the first call on that device.
+hipError_t scratch_address(void** p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *p = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_attn_noalloc(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q, const ChainArgs& kc,
+                                      const ChainArgs& vc, float scale, void* out, hipStream_t stream) {
+  if (attn_workspace_need(T, 0, H, Hq) > size_t(FLK_NOALLOC_SCRATCH_BYTES)) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  // every partial the combine reads is written by the attention kernel first: nothing to clear
+  return launch_decode_attn(T, H, D, Hq, q, kc, vc, nullptr, nullptr, 0, scale, out, ws,
+                            size_t(FLK_NOALLOC_SCRATCH_BYTES), stream);
 }
 
 hipError_t launch_decode_attn_fmt(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,

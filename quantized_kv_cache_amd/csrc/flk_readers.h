@@ -18,6 +18,12 @@ hipError_t launch_decode_attn(int32_t T, int32_t H, int32_t D, int32_t Hq, const
                               const void* v_tail, int32_t tail_len, float scale, void* out,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+// launch_decode_attn over packed positions only, with the library's per-device scratch array as
+// the workspace (no allocation); hipErrorInvalidValue without launching when the call needs
+// more than FLK_NOALLOC_SCRATCH_BYTES.
+hipError_t launch_decode_attn_noalloc(int32_t T, int32_t H, int32_t D, int32_t Hq, const void* q, const ChainArgs& kc,
+                                      const ChainArgs& vc, float scale, void* out, hipStream_t stream);
+
 // Decode attention over packed chains whose streams are INT4 throughout (fmt 0), an INT4 base
 // with NVFP4 residual loops (fmt 1), NVFP4 throughout (fmt 2), an INT4 base with MXFP4 residual
 // loops (fmt 3) or MXFP4 throughout (fmt 4), K and V alike; no tail.

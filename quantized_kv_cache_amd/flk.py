@@ -155,6 +155,8 @@ def lib() -> ctypes.CDLL:
         L.flk_partition_rows.argtypes = [P, i32, P, P, P, P, P]
         L.flk_decode_attn_packed.restype = ctypes.c_int
         L.flk_decode_attn_packed.argtypes = [D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P, sz, P]
+        L.flk_decode_attn_packed_noalloc.restype = ctypes.c_int
+        L.flk_decode_attn_packed_noalloc.argtypes = [D, D, i32, P, i32, S, S, i32, ctypes.c_float, P, P]
         _lib = L
     return _lib
 
@@ -355,6 +357,19 @@ def decode_attn_packed(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequ
                                         Hq, ka, va, len(k_chain), float(softmax_scale), _ptr(out),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)), "flk_decode_attn_packed")
+
+
+def decode_attn_packed_noalloc(q: torch.Tensor, k_chain: Sequence[Packed], v_chain: Sequence[Packed], T: int,
+                               H: int, softmax_scale: float, out: torch.Tensor, stream=None) -> None:
+    """decode_attn_packed with the library's per-device scratch array instead of a workspace."""
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out")
+    Hq, D = q.shape
+    ka, va = _chain(k_chain), _chain(v_chain)
+    _check(lib().flk_decode_attn_packed_noalloc(ctypes.byref(desc(K, H, D, k_chain[0].k_tiles)),
+                                                ctypes.byref(desc(V, H, D)), T, _ptr(q), Hq, ka, va, len(k_chain),
+                                                float(softmax_scale), _ptr(out), _stream(stream)),
+           "flk_decode_attn_packed_noalloc")
 
 
 def _chain_formats(chain: Sequence[Packed]):

@@ -171,6 +171,29 @@ def test_attention_validation():
     assert call(n_loops=0) == 2
 
 
+def test_noalloc_attention_validation():
+    """The allocation-free decode attention validates like flk_decode_attn_packed and rejects a
+    call whose partials would not fit the library's scratch array before touching the device."""
+    L = flk.lib()
+    S = flk.StreamC
+
+    def call(H=8, hq=32, T=256, q=FAKE, n_loops=1, kind_swap=False):
+        kd, vd = flk.desc(flk.K, H, 128), flk.desc(flk.V, H, 128)
+        if kind_swap:
+            kd, vd = vd, kd
+        chain = (S * 1)(S(T, 0, None, FAKE.value, FAKE.value, None))
+        return L.flk_decode_attn_packed_noalloc(ctypes.byref(kd), ctypes.byref(vd), T, q, hq, chain, chain, n_loops,
+                                                0.088, FAKE, None)
+    assert call(kind_swap=True) == 4
+    assert call(q=None) == 1
+    assert call(hq=30) == 2
+    assert call(hq=8 * 17) == 5
+    assert call(n_loops=0) == 2
+    # one KV head with 16 query heads over 2^19 tokens needs more than the scratch array holds
+    assert flk.attn_workspace_bytes(1, 128, 1 << 19, 16) > 16 << 20
+    assert call(H=1, hq=16, T=1 << 19) == 6
+
+
 def test_status_strings():
     L = flk.lib()
     for s in range(8):
