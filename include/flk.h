@@ -290,7 +290,7 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
 
 /* Largest scratch area flk_decode_attn_packed_noalloc uses: a device array of this many bytes,
  * one copy per GPU the library runs on, held until the process ends. */
-#define FLK_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define FLK_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* flk_decode_attn_packed without a workspace argument, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
@@ -302,7 +302,7 @@ flk_status flk_decode_attn_packed(const flk_desc* k_desc, const flk_desc* v_desc
  * undefined.  Arguments as flk_decode_attn_packed.
  * Errors: those of flk_decode_attn_packed; FLK_E_WORKSPACE when the call needs more than
  * FLK_NOALLOC_SCRATCH_BYTES (flk_attn_workspace_bytes(k_desc, T, n_q_heads) bounds the need;
- * 131072 tokens, 8 KV heads and 32 query heads need about 4.3 MB); FLK_E_LAUNCH when the
+ * 131072 tokens, 8 KV heads and 32 query heads need about 21.5 MB); FLK_E_LAUNCH when the
  * array cannot be located on the current device or a launch fails.                         */
 flk_status flk_decode_attn_packed_noalloc(const flk_desc* k_desc, const flk_desc* v_desc, int32_t T,
                                           const void* q, int32_t n_q_heads, const flk_stream* k_chain,

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libflk.so")
-SOURCES = ["flk_api.cpp", "flk_encode.hip", "flk_reconstruct.hip", "flk_attn.hip", "flk_sparse.hip",
+SOURCES = ["flk_api.cpp", "flk_encode.hip", "flk_reconstruct.hip", "flk_attn.hip", "flk_attn_split.hip", "flk_sparse.hip",
            "flk_select.hip", "flk_fp4.hip"]
 ARCH = os.environ.get("FLK_OFFLOAD_ARCH", "gfx950")
 

@@ -19,10 +19,7 @@
 // rolling cache's recent tokens) is read as stored, 16 tokens per wave.
 #include <mutex>
 
-#include "flk_device.h"
-#include "flk_fp4_device.h"
-#include "flk_internal.h"
-#include "flk_readers.h"
+#include "flk_attn_common.h"
 
 // The partials buffer of flk_decode_attn_packed_noalloc, for callers that cannot allocate: one
 // copy per GPU, held until the process ends, shared by every such call on that GPU.  Host code
@@ -32,221 +29,24 @@ static __device__ __align__(256) unsigned char scratch[FLK_NOALLOC_SCRATCH_BYTES
 
 namespace flk {
 
-constexpr int kAThreads = 256;
-constexpr int kAttnD = 128;
-constexpr int kMaxG = 16;
-constexpr int kLdsRow = kAttnD + 8;         // BF16 per LDS row: 272 bytes keep MFMA reads conflict-free
-#ifndef FLK_ATTN_WAVES
-#define FLK_ATTN_WAVES 8192
-#endif
-constexpr int kAttnWaves = FLK_ATTN_WAVES;    // aim for about this many waves per launch
-#ifndef FLK_ATTN_OCC
-#define FLK_ATTN_OCC 2   // waves per SIMD the register budget must allow
-#endif
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
-// Waves per KV head: about kAttnWaves waves per launch, never more than one per tile.  The
-// waves of a head share its tiles with counts that differ by at most one (the first waves take
-// the extra ones), so a few extra tiles (a BF16 tail) lengthen a few early waves instead of
-// adding blocks.  A block
-// of 4 waves writes one partial per query head.  `tiles` counts the packed tiles and the
-// tiles of a BF16 tail together.
-static int32_t waves_per_head(int32_t tiles, int32_t H) {
-  const int32_t cap = kAttnWaves / H > 0 ? kAttnWaves / H : 1;
-  return tiles < cap ? (tiles > 0 ? tiles : 1) : cap;
-}
-static int32_t n_splits(int32_t tiles, int32_t H) { return (waves_per_head(tiles, H) + 3) / 4; }
-
-static int32_t attn_tiles(int32_t T, int32_t tail_len) {
-  return (T + kGroup - 1) / kGroup + (tail_len + kGroup - 1) / kGroup;
-}
-
 // The workspace a call over T packed tokens and a tail of tail_len tokens uses: one partial
-// (m, l, O) per query head and split.
+// (m, l, O) and one block maximum per query head and split, then the two-pass path's scores,
+// one row of ceil(T/4)*4 binary32 per query head.
+static size_t attn_ws_bytes(int32_t splits, int32_t T, int32_t Hq) {
+  return size_t(splits) * size_t(Hq) * (2 + kAttnD + 1) * sizeof(float) +
+         size_t(Hq) * ((size_t(T) + 3) & ~size_t(3)) * sizeof(float);
+}
 size_t attn_workspace_need(int32_t T, int32_t tail_len, int32_t H, int32_t Hq) {
-  return size_t(n_splits(attn_tiles(T, tail_len), H)) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
+  return attn_ws_bytes(n_splits(attn_tiles(T, tail_len), H), T, Hq);
 }
 
 // A bound on attn_workspace_need for every call over at most T_total tokens: such a call has at
 // most ceil(T_total/64) + 1 tiles (a packed prefix and a tail may each end in a partial tile),
-// and the split count does not decrease with the tile count.
+// the split count does not decrease with the tile count, and the packed part is at most T_total.
 size_t attn_workspace_bytes(int32_t T_total, int32_t H, int32_t Hq) {
   const int64_t tiles = (int64_t(T_total) + kGroup - 1) / kGroup + 1;
   const int32_t s = n_splits(int32_t(tiles < INT32_MAX ? tiles : INT32_MAX), H);
-  return size_t(s) * size_t(Hq) * (2 + kAttnD) * sizeof(float);
-}
-
-// Decode loop l's 8 channels of one item into d[], the binary32 values min + scale * code
-// before their BF16 rounding (the caller rounds them where the chain needs it).  K: params of
-// the 8 channels come from the LDS copy of the item's parameter row; V: one parameter for the
-// item's 64-channel group.
-__device__ __forceinline__ void decode_item(uint32_t cw, const uint32_t p[8], float d[8]) {
-  float c[8];
-  codes8_to_f32(cw, c);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) d[e] = decode(c[e], f16_bits_to_f32(p[e] & 0xFFFFu), f16_bits_to_f32(p[e] >> 16));
-}
-
-
-__device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float v[8]) {
-  *reinterpret_cast<uint4*>(dst) = pack_exact_bf16x8(v);
-}
-__device__ __forceinline__ void load_bf16x8(const uint16_t* src, float v[8]) {
-  const uint4 w = *reinterpret_cast<const uint4*>(src);
-  v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xFFFF0000u);
-  v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xFFFF0000u);
-  v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xFFFF0000u);
-  v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xFFFF0000u);
-}
-
-constexpr int kAWaves = kAThreads / 64;
-
-// One wave's LDS: the V_hat slice, the tile's K parameter rows and the compact-row maps.
-template <int NL>
-struct WaveLds {
-  uint16_t v[16][kLdsRow];                 // V_hat of the current slice, [token][channel]
-  uint32_t kp[NL][2][kAttnD];              // K parameter rows of the tile (two rowgroups)
-  int32_t map[2][NL][kGroup];              // [K|V][loop][position in tile] -> compact row, -1 absent
-  int32_t perm[kGroup];                    // tile positions grouped by which loops list them
-};
-constexpr size_t kMergeBytes = size_t(kAWaves) * kMaxG * (2 + kAttnD) * sizeof(float);
-template <int NL>
-constexpr size_t attn_lds_bytes() {
-  return kAWaves * sizeof(WaveLds<NL>) > kMergeBytes ? kAWaves * sizeof(WaveLds<NL>) : kMergeBytes;
-}
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Per chain and loop: the rows of the tile [lo, hi) and whether the loop is dense.
-template <int NL>
-struct TileRows {
-  int32_t lo[NL], hi[NL];
-  bool dense[NL];
-};
-
-template <int NL>
-__device__ __forceinline__ TileRows<NL> tile_rows(const ChainArgs& c, int32_t tile, int32_t T) {
-  TileRows<NL> r;
-  const int32_t t0 = tile * kGroup;
-#pragma unroll
-  for (int l = 0; l < NL; ++l) {
-    r.dense[l] = l >= c.n_loops || c.s[l].rows == nullptr;
-    r.lo[l] = r.dense[l] ? t0 : uniform(c.s[l].tile_start[tile]);
-    r.hi[l] = r.dense[l] ? min(t0 + kGroup, T) : uniform(c.s[l].tile_start[tile + 1]);
-  }
-  return r;
-}
-
-// Scatter the tile's compact rows of every compact loop into map[l][position - t0].
-template <int NL>
-__device__ __forceinline__ void build_maps(const ChainArgs& c, const TileRows<NL>& r, int32_t t0,
-                                           int32_t (*map)[kGroup], int lane) {
-#pragma unroll
-  for (int l = 0; l < NL; ++l)
-    if (l < c.n_loops && !r.dense[l]) map[l][lane] = -1;
-  wave_sync();
-#pragma unroll
-  for (int l = 0; l < NL; ++l) {
-    if (l >= c.n_loops || r.dense[l]) continue;
-    const int32_t j = r.lo[l] + lane;
-    if (j < r.hi[l]) {
-      const uint32_t p = uint32_t(c.s[l].rows[j] - t0);
-      if (p < uint32_t(kGroup)) map[l][p] = j;         // a malformed entry outside the tile is dropped
-    }
-  }
-}
-
-// Decode 4 items (token tk of the tile, octets oc[i]) of one chain; out[i] receives item i's
-// 8 channels as packed BF16 (zeros for an absent or out-of-range token).  Every code word is
-// requested first; then one item at a time is decoded, so only one item's binary32 values
-// are live.  K: parameters from the staged rows; V: the row's two parameter words, one load.
-template <int KIND, int NL, int FMT = 0>
-__device__ __forceinline__ void decode_items(const ChainArgs& c, const TileRows<NL>& r, int32_t t0, int32_t T,
-                                             int32_t H, int32_t h, int tk, const int oc[4],
-                                             const int32_t (*map)[kGroup], const uint32_t (*kp)[2][kAttnD],
-                                             const float (&sg)[NL], uint4 out[4]) {
-  const int nl = c.n_loops;
-  const int32_t t = t0 + tk;
-  int32_t j[NL];
-  uint32_t cw[NL][4], sw[NL][2];
-#pragma unroll
-  for (int l = 0; l < NL; ++l) {
-    j[l] = -1;
-    if (l < nl) j[l] = r.dense[l] ? (t < T ? t : -1) : map[l][tk];
-    // FP4 loops: the item's block scales in one load -- its 4 E8M0 bytes (MXFP4, one per 32
-    // channels) or its 8 E4M3 bytes after the 16-byte header (NVFP4, one per 16 channels);
-    // the bytes are picked at decode time, so no load waits before the others are issued
-    // (INT4 V loops likewise: the item's two (min, scale) words, one per 64 channels)
-    sw[l][0] = sw[l][1] = 0u;
-    if ((loop_fp4<FMT>(l) || KIND == FLK_KIND_V) && j[l] >= 0) {
-      const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
-      if (loop_mx<FMT>(l)) {
-        sw[l][0] = c.s[l].params[item];
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(c.s[l].params + (loop_nv<FMT>(l) ? 4u : 0u) + item * 2u);
-        sw[l][0] = w.x;
-        sw[l][1] = w.y;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      cw[l][i] = 0;
-      if (j[l] >= 0) {
-        // uniform base + 32-bit offset: one saddr load, no 64-bit address arithmetic per lane
-        const uint32_t item = uint32_t(j[l]) * uint32_t(H) + uint32_t(h);
-        cw[l][i] = *reinterpret_cast<const uint32_t*>(c.s[l].codes + (item * (kAttnD / 2) + uint32_t(oc[i]) * 4u));
-      }
-    }
-  }
-  // The chain's roundings are taken lazily: acc holds the running sum before its BF16
-  // rounding, which happens only when another loop adds to it, or in the final pack.  The
-  // result is the encoder's bf16(...bf16(bf16(base) + bf16(d2)) ... + bf16(dR)).
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      if (j[l] < 0) continue;
-      float d[8];
-      if (loop_fp4<FMT>(l)) {          // octet oc's block: byte oc / 4 (MXFP4) or oc / 2 (NVFP4)
-        const uint32_t b = loop_mx<FMT>(l) ? uint32_t(oc[i]) >> 2 : uint32_t(oc[i]) >> 1;
-        const uint32_t sb = (((b & 4u) ? sw[l][1] : sw[l][0]) >> (8u * (b & 3u))) & 0xFFu;
-        fp4_decode8(cw[l][i], loop_mx<FMT>(l) ? fp4_e8m0_value(sb) : fp4_e4m3_value(sb) * sg[l], d);
-      } else {
-        uint32_t p[8];
-        if (KIND == FLK_KIND_K) {
-          const int rg = c.ktile ? 0 : (j[l] / kGroup) & 1;  // staged by rowgroup parity
-          const uint4 a = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8]);
-          const uint4 b = *reinterpret_cast<const uint4*>(&kp[l][rg][oc[i] * 8 + 4]);
-          p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
-        } else {                                         // V: the octet's 64-channel group
-          const uint32_t w = (oc[i] >> 3) ? sw[l][1] : sw[l][0];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = w;
-        }
-        decode_item(cw[l][i], p, d);
-      }
-      if (l == 0) {                                      // the dense base: every live token
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = d[e];
-      } else {
-        round_bf16x8_inplace(acc);
-        round_bf16x8_inplace(d);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + d[e];
-      }
-    }
-    out[i] = round_bf16x8(acc);                          // RNE pack of the last sum
-  }
+  return attn_ws_bytes(s, T_total, Hq);
 }
 
 // SC: also write every (query head, packed token) scaled score to scores[head][position], rows
@@ -306,11 +106,37 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   float4_t o[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // INT4 V loops go to the MFMA as codes (VNIB): the A operand is 1024 + code in binary16, the B
+  // operand p * scale per token and V group, so the products carry 1024 * sum(B) on top of
+  // sum(code * B).  vmin accumulates, per V group, the minimum's share sum(p * min) minus that
+  // 1024 * sum(B) over this lane's tokens; it is added to every channel of the group at the end.
+  // Other formats decode V_hat to BF16 first (exact).
+  constexpr bool VNIB = FMT == 0;
+  float vmin[2] = {0.0f, 0.0f};
 
-  // One 16-token slice: S^T = K Q^T on the MFMA, the online softmax, then V (from load_v,
-  // called after the softmax so one operand set is live at a time) into LDS and
-  // O^T += V^T P^T.  Slots 16*sl + 4*kb + i at or past n_valid are masked.
-  auto attend_slice = [&](const uint4 (&kitem)[4], int sl, int32_t n_valid, auto&& load_v, auto&& emit) {
+  // Exact PV of one slice: V_hat (this lane: token n, octets oc[]) through wave-private LDS into
+  // the A operands, p as BF16.
+  auto pv_exact = [&](const uint4 (&vitem)[4], const float (&p)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.v[n][oc[i] * 8]) = vitem[i];
+    wave_sync();
+    short4_t pb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pb[j] = short(__builtin_bit_cast(uint16_t, (__bf16)p[j]));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      short4_t a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = short(L.v[4 * kb + j][pv_channel(mt, n)]);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
+    }
+    wave_sync();                                          // the slice's V reads before the next writes
+  };
+
+  // One 16-token slice: S^T = K_hat Q^T on the MFMA (kitem: the A operands), one online-softmax
+  // step, then the PV products (vpath, given this lane's 4 probabilities).  Slots 4*kb + i at or
+  // past nv are masked.
+  auto attend_slice = [&](const uint4 (&kitem)[4], int32_t nv, auto&& vpath, auto&& emit) {
     float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -320,7 +146,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sc[i] = 16 * sl + 4 * kb + i < n_valid ? sacc[i] * scale : -__builtin_inff();
+      sc[i] = 4 * kb + i < nv ? sacc[i] * scale : -__builtin_inff();
       mx = fmaxf(mx, sc[i]);
     }
     emit(sc);
@@ -338,41 +164,32 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     const float corr = m_run == -__builtin_inff() ? 0.0f : __expf(m_run - m_new);
     l_run = l_run * corr + psum;
     m_run = m_new;
-
-    uint4 vitem[4];
-    load_v(vitem);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.v[n][oc[i] * 8]) = vitem[i];
-    wave_sync();
-    short4_t pb;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pb[j] = short(__builtin_bit_cast(uint16_t, (__bf16)p[j]));
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      short4_t a;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = short(L.v[4 * kb + j][16 * mt + n]);
-      o[mt] = o[mt] * corr;
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
+    for (int mt = 0; mt < 8; ++mt) o[mt] = o[mt] * corr;
+    if constexpr (VNIB) {
+      vmin[0] *= corr;
+      vmin[1] *= corr;
     }
-    wave_sync();                                          // the slice's V reads before the next writes
+    vpath(p);
   };
 
   // The BF16 tail, read as stored, in 16-token slices: slice s goes to waves s, s + wph, ...
   // of every head, a small addition to many waves rather than whole tiles for a few.
   const int32_t tail_slices = (tail_len + 15) / 16;
   for (int32_t ts = w; w < wph && ts < tail_slices; ts += wph) {
-    const int32_t n_valid = min(16, tail_len - 16 * ts);
-    const bool ok = n < n_valid;
-    const int64_t base = (int64_t(16 * ts + n) * H + h) * kAttnD;
+    const int32_t nv = min(16, tail_len - 16 * ts);
+    const bool ok = n < nv;
+    const int64_t b = (int64_t(16 * ts + n) * H + h) * kAttnD;
     uint4 item[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      item[i] = ok ? *reinterpret_cast<const uint4*>(kt + base + oc[i] * 8) : make_uint4(0, 0, 0, 0);
-    attend_slice(item, 0, n_valid, [&](uint4 (&v)[4]) {
+      item[i] = ok ? *reinterpret_cast<const uint4*>(kt + b + oc[i] * 8) : make_uint4(0, 0, 0, 0);
+    attend_slice(item, nv, [&](const float (&p)[4]) {
+      uint4 v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        v[i] = ok ? *reinterpret_cast<const uint4*>(vt + base + oc[i] * 8) : make_uint4(0, 0, 0, 0);
+        v[i] = ok ? *reinterpret_cast<const uint4*>(vt + b + oc[i] * 8) : make_uint4(0, 0, 0, 0);
+      pv_exact(v, p);
     }, [](const float (&)[4]) {});
   }
 
@@ -434,13 +251,99 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     }
     wave_sync();
 
-    for (int sl = 0; sl < kGroup / 16; ++sl) {
+    for (int sl = 0; sl * 16 < n_valid; ++sl) {
       const int tk = L.perm[16 * sl + n];
+      // VNIB: the slice's INT4 V codes and parameters of every loop are copied into the wave's
+      // LDS staging by buffer loads that write LDS directly (no registers held), issued before
+      // the K decode so their latency hides behind K's.  Lane L copies 16 bytes of code row
+      // L / 4 (chunk vchunk) and, for L < 32, parameter word L % 2 of row L / 2.  A row the loop
+      // does not list (or past T) reads zeros, which contribute nothing; a loop none of the
+      // slice's rows has is skipped.
+      uint32_t vlive = 0;
+      if constexpr (VNIB) {
+        const int crow = lane >> 2, prow = (lane & 31) >> 1;
+        const int cq = (lane & 3) ^ ((crow >> 2) & 3);     // the chunk this lane's slot holds
+        const int ctk = L.perm[16 * sl + crow], ptk = L.perm[16 * sl + prow];
+        wave_sync();                                          // the previous slice's staging is read
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          if (l >= vc.n_loops) continue;
+          const int32_t tc = t0 + ctk, tp = t0 + ptk;
+          const int32_t jc = rv.dense[l] ? (tc < T ? tc : -1) : L.map[1][l][ctk];
+          const int32_t jp = rv.dense[l] ? (tp < T ? tp : -1) : L.map[1][l][ptk];
+          if (__ballot(jc >= 0) == 0) continue;
+          vlive |= 1u << l;
+          const uint32_t nb = uint32_t(vc.s[l].n) * uint32_t(H);
+          const BufRsrc cb = make_buf(vc.s[l].codes, nb * (kAttnD / 2));
+          const BufRsrc pb = make_buf(vc.s[l].params, nb * 8u);
+          const uint32_t co = jc >= 0 ? (uint32_t(jc) * uint32_t(H) + uint32_t(h)) * (kAttnD / 2) + 16u * uint32_t(cq)
+                                      : kOutOfRange;
+          const uint32_t po = lane < 32 && jp >= 0 ? (uint32_t(jp) * uint32_t(H) + uint32_t(h)) * 8u + 4u * uint32_t(lane & 1)
+                                                   : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(cb, (lds_ptr_t)&L.vs.codes[l][0][0], 16, co, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(pb, (lds_ptr_t)&L.vs.params[l][0], 4, po, 0, 0, 0);
+        }
+      }
       // K_hat of the slice straight into the A operands
       uint4 item[4];
       decode_items<FLK_KIND_K, NL, FMT>(kc, rk, t0, T, H, h, tk, oc, L.map[0], L.kp, sgk, item);
-      attend_slice(item, sl, n_valid, [&](uint4 (&v)[4]) {
-        decode_items<FLK_KIND_V, NL, FMT>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, sgv, v);
+      attend_slice(item, n_valid - 16 * sl, [&](const float (&p)[4]) {
+        if constexpr (VNIB) {
+          // B operands: p * scale16 per V group, rows (0, 1) and (2, 3) as binary16 pairs; the
+          // minimum's share p * min16 accumulates in binary32 (dot2).  A operands: output tile
+          // mt takes nibble mt of each row's word, as binary16 1024 + code.
+          const uint32_t pp01 = pack_f16x2(p[0], p[1]), pp23 = pack_f16x2(p[2], p[3]);
+          const f16x2_t m1024 = __builtin_bit_cast(f16x2_t, 0xE400E400u);   // (-1024, -1024)
+          __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): the staging has landed
+          wave_sync();
+#pragma unroll
+          for (int l = 0; l < NL; ++l) {
+            if (!((vlive >> l) & 1u)) continue;
+            // this lane's rows 4*kb + r: the 16-bit words at bytes 2n and 32 + 2n, and the row's
+            // two parameter words
+            uint32_t d[4];
+            uint2 vpw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = 4 * kb + r;
+              const uint16_t* cr = reinterpret_cast<const uint16_t*>(&L.vs.codes[l][row][0]);
+              const uint32_t lo = cr[(16 * vchunk(row, n >> 3) + ((2 * n) & 15)) >> 1];
+              const uint32_t hi = cr[(16 * vchunk(row, 2 + (n >> 3)) + ((2 * n) & 15)) >> 1];
+              d[r] = lo | (hi << 16);
+              vpw[r] = *reinterpret_cast<const uint2*>(&L.vs.params[l][2 * row]);
+            }
+            f16x4_t bg[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const uint32_t w0 = g ? vpw[0].y : vpw[0].x, w1 = g ? vpw[1].y : vpw[1].x;
+              const uint32_t w2 = g ? vpw[2].y : vpw[2].x, w3 = g ? vpw[3].y : vpw[3].x;
+              const uint32_t s01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u), s23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+              const uint32_t m01 = __builtin_amdgcn_perm(w1, w0, 0x05040100u), m23 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+              const f16x2_t b01 = __builtin_bit_cast(f16x2_t, pp01) * __builtin_bit_cast(f16x2_t, s01);
+              const f16x2_t b23 = __builtin_bit_cast(f16x2_t, pp23) * __builtin_bit_cast(f16x2_t, s23);
+              bg[g] = f16x4_of(__builtin_bit_cast(uint32_t, b01), __builtin_bit_cast(uint32_t, b23));
+              vmin[g] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pp01), __builtin_bit_cast(f16x2_t, m01), vmin[g], false);
+              vmin[g] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pp23), __builtin_bit_cast(f16x2_t, m23), vmin[g], false);
+              vmin[g] = __builtin_amdgcn_fdot2(b01, m1024, vmin[g], false);
+              vmin[g] = __builtin_amdgcn_fdot2(b23, m1024, vmin[g], false);
+            }
+            const uint32_t e0 = d[0] >> 4, e1 = d[1] >> 4, e2 = d[2] >> 4, e3 = d[3] >> 4;
+            const uint32_t nib = opaque(0x000F000Fu);           // a VGPR operand: one v_and_or per word
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+              const uint32_t b = uint32_t(mt >> 1);
+              const uint32_t sel = b | 0x0C00u | ((4u + b) << 16) | 0x0C000000u;   // [x0.b, 0, x1.b, 0]
+              const uint32_t x01 = (mt & 1) ? __builtin_amdgcn_perm(e1, e0, sel) : __builtin_amdgcn_perm(d[1], d[0], sel);
+              const uint32_t x23 = (mt & 1) ? __builtin_amdgcn_perm(e3, e2, sel) : __builtin_amdgcn_perm(d[3], d[2], sel);
+              const f16x4_t a = f16x4_of((x01 & nib) | 0x64006400u, (x23 & nib) | 0x64006400u);
+              o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bg[mt >> 2], o[mt], 0, 0, 0);
+            }
+          }
+        } else {
+          uint4 v[4];
+          decode_items<FLK_KIND_V, NL, FMT>(vc, rv, t0, T, H, h, tk, oc, L.map[1], L.kp, sgv, v);
+          pv_exact(v, p);
+        }
       }, [&](const float (&sc)[4]) {
         if constexpr (SC) {
           if (n < G) {
@@ -456,6 +359,20 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
     }
   }
 
+  if constexpr (VNIB) {
+    // the minimum's share and the offset: over the 4 k-blocks, every lane then holds its head's
+    float vm[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      vm[g] = vmin[g] + __shfl_xor(vmin[g], 16);
+      vm[g] += __shfl_xor(vm[g], 32);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[mt][i] += vm[mt >> 2];
+  }
+
   // merge the 4 waves: (m, l) per head and O^T per (head, channel) through LDS
   __syncthreads();
   float* s_m = reinterpret_cast<float*>(s_raw);           // [4][16]
@@ -468,7 +385,7 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[(wave * kMaxG + n) * kAttnD + 16 * mt + 4 * kb + i] = o[mt][i];
+    for (int i = 0; i < 4; ++i) s_o[(wave * kMaxG + n) * kAttnD + pv_channel(mt, 4 * kb + i)] = o[mt][i];
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * kAttnD; idx += kAThreads) {
     const int g = idx / kAttnD, ch = idx % kAttnD;
@@ -489,27 +406,30 @@ __global__ __launch_bounds__(kAThreads, FLK_ATTN_OCC) void attn_wave_kernel(Chai
   }
 }
 
-// Merge the per-block partials of one query head (blockIdx.x).  Thread (c = tid % 128,
-// g = tid / 128) takes channel c of every kCombGroups-th split from g on, with independent
-// loads in flight; the groups then merge through LDS.
-constexpr int kCombGroups = 8;
-__global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int32_t splits, int32_t Hq,
-                                                                            const float* __restrict__ ws_ml,
-                                                                            const float* __restrict__ ws_o,
-                                                                            uint16_t* __restrict__ out,
-                                                                            float* __restrict__ out32,
-                                                                            float* __restrict__ ml_out) {
-  __shared__ float s_red[kCombGroups * kAttnD];
-  __shared__ float s_l[kCombGroups * kAttnD];
+// Merge the per-block partials of one query head over one range of 16 channels: block
+// (blockIdx.x = query head, blockIdx.y = channel range); thread (c = tid % 16, g = tid / 16)
+// takes channel c of every kCombGroups-th split from g on, with independent loads in flight;
+// the groups then merge through LDS.  Every block finds the global maximum itself.
+constexpr int kCombGroups = 16;
+constexpr int kCombChannels = 16;
+constexpr int kCombThreads = kCombGroups * kCombChannels;
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(int32_t splits, int32_t Hq,
+                                                                   const float* __restrict__ ws_ml,
+                                                                   const float* __restrict__ ws_o,
+                                                                   uint16_t* __restrict__ out,
+                                                                   float* __restrict__ out32,
+                                                                   float* __restrict__ ml_out) {
+  __shared__ float s_red[kCombThreads];
+  __shared__ float s_l[kCombThreads];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  const int c = tid % kAttnD, g = tid / kAttnD;
+  const int c = int(blockIdx.y) * kCombChannels + tid % kCombChannels, g = tid / kCombChannels;
   // global maximum of the partial maxima
   float M = -__builtin_inff();
-  for (int s = tid; s < splits; s += kAttnD * kCombGroups) M = fmaxf(M, ws_ml[2 * (int64_t(s) * Hq + i)]);
+  for (int s = tid; s < splits; s += kCombThreads) M = fmaxf(M, ws_ml[2 * (int64_t(s) * Hq + i)]);
   s_red[tid] = M;
   __syncthreads();
-  for (int w = kAttnD * kCombGroups / 2; w > 0; w >>= 1) {
+  for (int w = kCombThreads / 2; w > 0; w >>= 1) {
     if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
     __syncthreads();
   }
@@ -531,8 +451,8 @@ __global__ __launch_bounds__(kAttnD * kCombGroups) void attn_combine_kernel(int3
     float Ot = 0.0f, Lt = 0.0f;
 #pragma unroll
     for (int k = 0; k < kCombGroups; ++k) {
-      Ot += s_red[k * kAttnD + c];
-      Lt += s_l[k * kAttnD + c];
+      Ot += s_red[k * kCombChannels + tid];
+      Lt += s_l[k * kCombChannels + tid];
     }
     out[int64_t(i) * kAttnD + c] = __builtin_bit_cast(uint16_t, (__bf16)(Ot / Lt));
     if (out32) out32[int64_t(i) * kAttnD + c] = Ot / Lt;     // the sparse reference's O_ref
@@ -561,19 +481,28 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
   int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
   if (nl < 1) nl = 1;                              // no packed tokens: only the tail's tiles run
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
+  if (FMT == 0 && tail_len == 0 && T > 0) {
+    // INT4 chains without a tail: the scores of every position, then PV straight from the V codes
+    float* block_max = ws_o + size_t(splits) * Hq * kAttnD;
+    float* sc = SC ? scores : block_max + size_t(splits) * Hq;
+    const hipError_t e = launch_attn_split(0, T, H, Hq, q, kc, vc, scale, wph, splits, sc, block_max, ws_ml, ws_o,
+                                           stream);
+    if (e != hipSuccess) return e;
+  } else {
 #define FLK_A(NLV)                                                                                          \
   case NLV:                                                                                                 \
     hipLaunchKernelGGL((attn_wave_kernel<NLV, SC, FMT>), grid, dim3(kAThreads), 0, stream, kc, vc, T, H, G, qp, \
                        ktp, vtp, tail_len, scale, wph, ws_ml, ws_o, scores);                                \
     break;
-  switch (nl) {
-    FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
-    default: return hipErrorInvalidValue;
-  }
+    switch (nl) {
+      FLK_A(1) FLK_A(2) FLK_A(3) FLK_A(4) FLK_A(5) FLK_A(6) FLK_A(7) FLK_A(8)
+      default: return hipErrorInvalidValue;
+    }
 #undef FLK_A
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq), dim3(kAttnD * kCombGroups), 0, stream, splits, Hq, ws_ml,
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq, kAttnD / kCombChannels), dim3(kCombThreads), 0, stream, splits, Hq, ws_ml,
                      ws_o, static_cast<uint16_t*>(out), out32, ml_out);
   return hipGetLastError();
 }

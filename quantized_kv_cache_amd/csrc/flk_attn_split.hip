@@ -1,0 +1,385 @@
+// flk_attn_split.hip -- decode attention over INT4 packed chains in two passes over the tokens
+// (FlashLoop RFC, vllm-rlt #156, section 3.3: readers consume the packed base/residual tiles
+// directly during QK and PV).
+//
+// Pass 1 (attn_scores_kernel) decodes K_hat bit for bit as the encoder left it -- the BF16
+// rounding after every loop of the chain matters here: a sharp softmax turns a one-ulp change
+// of a key into a visible change of the output -- and writes every scaled score
+// s[head][position] and, per block, each query head's maximum score.
+// Pass 2 (attn_pv_kernel) takes V straight from the codes.  A V loop's contribution is linear
+// in its codes, V_hat_l = min + scale * code per (row, 64-channel group), so
+// sum_t p_t V_l[t] = sum_t p_t min_t + sum_t (p_t scale_t) code_t: the codes go to the MFMA
+// as binary16 1024 + code (a nibble ORed into 0x6400), the B operand is p * scale in
+// binary16, and the minima and the 1024 offset are a per-(head, group) correction accumulated
+// with dot2.  The loops are walked one at a time over their own compact rows, so no row the
+// loop does not list is ever touched.  Leaving out the chain's intermediate BF16 roundings of
+// V_hat changes the output by a few 1e-3 relative (errors average over the tokens), against
+// 1e-1 for K.
+// Both passes use the same blocks (split, KV head), so the block maximum of pass 1 is the
+// reference of pass 2's probabilities and pass 2's partial (max, sum, O) per block merges in
+// the same combine kernel as the fused path.
+#include "flk_attn_common.h"
+
+namespace flk {
+
+// ---- pass 1: scores ------------------------------------------------------------------------
+
+template <int NL>
+struct ScoreLds {
+  uint32_t kp[NL][2][kAttnD];              // K parameter rows of the tile (two rowgroups)
+  int32_t map[NL][kGroup];                 // [loop][position in tile] -> compact row, -1 absent
+  int32_t perm[kGroup];                    // tile positions grouped by which loops list them
+};
+
+template <int NL, int FMT>
+__global__ __launch_bounds__(kAThreads, 4) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
+                                                                   const uint16_t* __restrict__ q, float scale,
+                                                                   int32_t wph, float* __restrict__ scores,
+                                                                   float* __restrict__ block_max) {
+  __shared__ __attribute__((aligned(16))) ScoreLds<NL> s_lds[kAWaves];
+  __shared__ float s_max[kAWaves][kMaxG];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int kb = lane >> 4;
+  // the block order of the fused kernel: split-major, head-minor, contiguous per XCD
+  const uint32_t lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int32_t split = int32_t(lin / gridDim.y);
+  const int32_t h = int32_t(lin % gridDim.y);
+  const int32_t Hq = H * G;
+  const int32_t ptiles = (T + kGroup - 1) / kGroup;
+  const int32_t w = split * kAWaves + wave;
+  const int32_t base = ptiles / wph, extra = ptiles - base * wph;
+  const int32_t tile0 = w < wph ? w * base + min(w, extra) : ptiles;
+  const int32_t tile1 = w < wph ? tile0 + base + (w < extra ? 1 : 0) : ptiles;
+  ScoreLds<NL>& L = s_lds[wave];
+  const int64_t Tpad = (int64_t(T) + 3) & ~int64_t(3);
+
+  bf16x8_t qb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 qw = make_uint4(0, 0, 0, 0);
+    if (n < G) qw = *reinterpret_cast<const uint4*>(q + int64_t(h * G + n) * kAttnD + 32 * ks + 8 * kb);
+    qb[ks] = __builtin_bit_cast(bf16x8_t, qw);
+  }
+  int oc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oc[i] = 4 * i + kb;
+  float sgk[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) sgk[l] = loop_nv<FMT>(l) && l < kc.n_loops ? __uint_as_float(kc.s[l].params[0]) : 0.0f;
+
+  float* srow = scores + int64_t(h * G + (n < G ? n : 0)) * Tpad;
+  float mx = -__builtin_inff();
+  for (int32_t tile = tile0; tile < tile1; ++tile) {
+    const int32_t t0 = tile * kGroup;
+    const TileRows<NL> rk = tile_rows<NL>(kc, tile, T);
+    wave_sync();                                          // the previous tile's LDS reads are done
+    build_maps<NL>(kc, rk, t0, L.map, lane);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      if (l >= kc.n_loops || loop_fp4<FMT>(l)) continue;    // FP4 loops carry no K parameter rows
+      if (kc.ktile) {
+        if (rk.hi[l] > rk.lo[l]) {
+          const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(tile) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
+          *reinterpret_cast<uint2*>(&L.kp[l][0][2 * lane]) = pw;
+        }
+        continue;
+      }
+      const int32_t nrg = (kc.s[l].n + kGroup - 1) / kGroup;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int32_t rg = rk.lo[l] / kGroup + r;
+        if ((r == 1 && rk.dense[l]) || rg >= nrg) continue;
+        const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(rg) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
+        *reinterpret_cast<uint2*>(&L.kp[l][rg & 1][2 * lane]) = pw;
+      }
+    }
+    // positions listed by the same loops sit together, so a loop none of a slice's tokens has
+    // is skipped by the whole wave; positions past T go last
+    const int32_t n_valid = min(kGroup, T - t0);
+    {
+      uint32_t key = 0;
+#pragma unroll
+      for (int l = 1; l < NL; ++l)
+        if (l < kc.n_loops && !rk.dense[l] && L.map[l][lane] >= 0) key |= 1u << l;
+      const bool valid = lane < n_valid;
+      const uint64_t below = (uint64_t(1) << lane) - 1;
+      uint64_t remaining = __ballot(valid);
+      int nb = 0, rank = 0;
+      while (remaining) {
+        const int leader = __builtin_ctzll(remaining);
+        const uint32_t k = __builtin_amdgcn_readlane(key, leader);
+        const uint64_t grp = __ballot(valid && key == k);
+        if (valid && key == k) rank = nb + __builtin_popcountll(grp & below);
+        nb += __builtin_popcountll(grp);
+        remaining &= ~grp;
+      }
+      if (!valid) rank = lane;
+      L.perm[rank] = lane;
+    }
+    wave_sync();
+    // the next slice's code words are requested before this slice is decoded
+    ItemLoads<NL> cur, nxt;
+    issue_items<FLK_KIND_K, NL, FMT>(kc, rk, t0, T, H, h, L.perm[n], oc, L.map, cur);
+    for (int sl = 0; sl * 16 < n_valid; ++sl) {
+      if ((sl + 1) * 16 < n_valid)
+        issue_items<FLK_KIND_K, NL, FMT>(kc, rk, t0, T, H, h, L.perm[16 * (sl + 1) + n], oc, L.map, nxt);
+      uint4 item[4];
+      decode_loaded<FLK_KIND_K, NL, FMT>(kc, cur, oc, L.kp, sgk, item);
+      cur = nxt;
+      float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item[ks]), qb[ks], sacc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 16 * sl + 4 * kb + i;
+        if (slot < n_valid) {
+          const float s = sacc[i] * scale;
+          mx = fmaxf(mx, s);
+          if (n < G) srow[t0 + L.perm[slot]] = s;
+        }
+      }
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (kb == 0) s_max[wave][n] = mx;
+  __syncthreads();
+  if (int(threadIdx.x) < G) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int wv = 0; wv < kAWaves; ++wv) m = fmaxf(m, s_max[wv][threadIdx.x]);
+    block_max[int64_t(split) * Hq + h * G + int(threadIdx.x)] = m;
+  }
+}
+
+// ---- pass 2: PV from the V codes -----------------------------------------------------------
+
+// One wave's staging of a slice: 16 code rows (chunks swizzled, see vchunk) and 16 parameter
+// rows (words 32..63 stay unused).  A wave stages kPvBatch slices at a time.
+struct PvStage {
+  uint8_t codes[16][kAttnD / 2];
+  uint32_t params[64];
+};
+constexpr int kPvBatch = 4;
+union PvLds {
+  PvStage stage[kAWaves][kPvBatch];
+  struct {
+    float o[kAWaves][kMaxG][kAttnD];
+    float l[kAWaves][kMaxG];
+  } merge;
+};
+
+template <int NL>
+__global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int32_t T, int32_t H, int32_t G,
+                                                               const float* __restrict__ scores,
+                                                               const float* __restrict__ block_max, int32_t wph,
+                                                               float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+  __shared__ __attribute__((aligned(16))) PvLds s_lds;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int kb = lane >> 4;
+  const uint32_t lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int32_t split = int32_t(lin / gridDim.y);
+  const int32_t h = int32_t(lin % gridDim.y);
+  const int32_t Hq = H * G;
+  const int32_t ptiles = (T + kGroup - 1) / kGroup;
+  const int32_t w = split * kAWaves + wave;
+  const int32_t base = ptiles / wph, extra = ptiles - base * wph;
+  const int32_t tile0 = w < wph ? w * base + min(w, extra) : ptiles;
+  const int32_t tile1 = w < wph ? tile0 + base + (w < extra ? 1 : 0) : ptiles;
+  PvStage* Sw = s_lds.stage[wave];
+  const int64_t Tpad = (int64_t(T) + 3) & ~int64_t(3);
+  const int32_t P0 = tile0 * kGroup, P1 = min(tile1 * kGroup, T);
+
+  // the block's maximum score of this lane's query head (pass 1); probabilities are relative to it
+  const float m = n < G ? block_max[int64_t(split) * Hq + h * G + n] : 0.0f;
+  const float* srow = scores + int64_t(h * G + (n < G ? n : 0)) * Tpad;
+  const bool head_live = n < G && m != -__builtin_inff();
+
+  float4_t o[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float vmin[2] = {0.0f, 0.0f};   // per V group: sum p * min - 1024 * sum (p * scale) over this lane's rows
+  float lsum = 0.0f;
+  const f16x2_t m1024 = __builtin_bit_cast(f16x2_t, 0xE400E400u);   // (-1024, -1024)
+  const uint32_t nib = opaque(0x000F000Fu);                        // a VGPR operand: one v_and_or per word
+
+  // this lane's staging slots: 16 bytes of code row crow (chunk cq), parameter word of prow
+  const int crow = lane >> 2, prow = (lane & 31) >> 1;
+  const int cq = (lane & 3) ^ ((crow >> 2) & 3);
+
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    if (l >= vc.n_loops || P0 >= P1) continue;
+    const StreamArgs st = vc.s[l];
+    const bool dense = st.rows == nullptr;
+    // the loop's compact rows of positions [P0, P1)
+    const int32_t a = dense ? P0 : uniform(st.tile_start[tile0]);
+    const int32_t b = dense ? P1 : uniform(st.tile_start[tile1]);
+    const uint32_t nbytes = uint32_t(st.n) * uint32_t(H);
+    const BufRsrc cb = make_buf(st.codes, nbytes * (kAttnD / 2));
+    const BufRsrc pb = make_buf(st.params, nbytes * 8u);
+    // batches of kPvBatch 16-row slices: every load of a batch (staging, positions, scores)
+    // goes out before any of it is used, so a batch costs one exposed round trip, not one per slice
+    for (int32_t jb = a; jb < b; jb += 16 * kPvBatch) {
+      wave_sync();                                        // the previous batch's staging is read
+#pragma unroll
+      for (int sb = 0; sb < kPvBatch; ++sb) {
+        const int32_t j0 = jb + 16 * sb;
+        if (j0 >= b) break;
+        const int32_t jc = j0 + crow, jp = j0 + prow;
+        const uint32_t co = jc < b ? (uint32_t(jc) * uint32_t(H) + uint32_t(h)) * (kAttnD / 2) + 16u * uint32_t(cq)
+                                   : kOutOfRange;
+        const uint32_t po = lane < 32 && jp < b ? (uint32_t(jp) * uint32_t(H) + uint32_t(h)) * 8u + 4u * uint32_t(lane & 1)
+                                                : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cb, (lds_ptr_t)&Sw[sb].codes[0][0], 16, co, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pb, (lds_ptr_t)&Sw[sb].params[0], 4, po, 0, 0, 0);
+      }
+      // this lane's rows 4*kb + r of each slice: positions, then scores and probabilities (0 past
+      // the range)
+      int32_t pos[kPvBatch][4];
+#pragma unroll
+      for (int sb = 0; sb < kPvBatch; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t j = jb + 16 * sb + 4 * kb + r;
+          pos[sb][r] = j < b && head_live ? (dense ? j : st.rows[j]) : -1;
+        }
+      float sv[kPvBatch][4];
+#pragma unroll
+      for (int sb = 0; sb < kPvBatch; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[sb][r] = pos[sb][r] >= 0 ? srow[pos[sb][r]] : -__builtin_inff();
+      __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): the staging has landed
+      wave_sync();
+#pragma unroll
+      for (int sb = 0; sb < kPvBatch; ++sb) {
+        if (jb + 16 * sb >= b) break;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = sv[sb][r] == -__builtin_inff() ? 0.0f : __expf(sv[sb][r] - m);
+          if (l == 0) lsum += p[r];                       // the dense base lists every position once
+        }
+        const uint32_t pp01 = pack_f16x2(p[0], p[1]), pp23 = pack_f16x2(p[2], p[3]);
+        const PvStage& S = Sw[sb];
+        uint32_t d[4];
+        uint2 vpw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * kb + r;
+          const uint16_t* cr = reinterpret_cast<const uint16_t*>(&S.codes[row][0]);
+          const uint32_t lo = cr[(16 * vchunk(row, n >> 3) + ((2 * n) & 15)) >> 1];
+          const uint32_t hi = cr[(16 * vchunk(row, 2 + (n >> 3)) + ((2 * n) & 15)) >> 1];
+          d[r] = lo | (hi << 16);
+          vpw[r] = *reinterpret_cast<const uint2*>(&S.params[2 * row]);
+        }
+        f16x4_t bg[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint32_t w0 = g ? vpw[0].y : vpw[0].x, w1 = g ? vpw[1].y : vpw[1].x;
+          const uint32_t w2 = g ? vpw[2].y : vpw[2].x, w3 = g ? vpw[3].y : vpw[3].x;
+          const uint32_t s01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u), s23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+          const uint32_t m01 = __builtin_amdgcn_perm(w1, w0, 0x05040100u), m23 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+          const f16x2_t b01 = __builtin_bit_cast(f16x2_t, pp01) * __builtin_bit_cast(f16x2_t, s01);
+          const f16x2_t b23 = __builtin_bit_cast(f16x2_t, pp23) * __builtin_bit_cast(f16x2_t, s23);
+          bg[g] = f16x4_of(__builtin_bit_cast(uint32_t, b01), __builtin_bit_cast(uint32_t, b23));
+          vmin[g] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pp01), __builtin_bit_cast(f16x2_t, m01), vmin[g], false);
+          vmin[g] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pp23), __builtin_bit_cast(f16x2_t, m23), vmin[g], false);
+          vmin[g] = __builtin_amdgcn_fdot2(b01, m1024, vmin[g], false);
+          vmin[g] = __builtin_amdgcn_fdot2(b23, m1024, vmin[g], false);
+        }
+        // output tile mt takes nibble mt of each row's word, as binary16 1024 + code
+        const uint32_t e0 = d[0] >> 4, e1 = d[1] >> 4, e2 = d[2] >> 4, e3 = d[3] >> 4;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const uint32_t bsel = uint32_t(mt >> 1);
+          const uint32_t sel = bsel | 0x0C00u | ((4u + bsel) << 16) | 0x0C000000u;   // [x0.b, 0, x1.b, 0]
+          const uint32_t x01 = (mt & 1) ? __builtin_amdgcn_perm(e1, e0, sel) : __builtin_amdgcn_perm(d[1], d[0], sel);
+          const uint32_t x23 = (mt & 1) ? __builtin_amdgcn_perm(e3, e2, sel) : __builtin_amdgcn_perm(d[3], d[2], sel);
+          const f16x4_t av = f16x4_of((x01 & nib) | 0x64006400u, (x23 & nib) | 0x64006400u);
+          o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bg[mt >> 2], o[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // per head: the corrections and the probability sums over the 4 k-blocks
+  float vm[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    vm[g] = vmin[g] + __shfl_xor(vmin[g], 16);
+    vm[g] += __shfl_xor(vm[g], 32);
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  // merge the 4 waves (one reference maximum, so plain sums) through LDS
+  __syncthreads();
+  if (kb == 0) s_lds.merge.l[wave][n] = lsum;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_lds.merge.o[wave][n][pv_channel(mt, 4 * kb + i)] = o[mt][i] + vm[mt >> 2];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * kAttnD; idx += kAThreads) {
+    const int g = idx / kAttnD, ch = idx % kAttnD;
+    float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kAWaves; ++wv) {
+      Ls += s_lds.merge.l[wv][g];
+      O += s_lds.merge.o[wv][g][ch];
+    }
+    const int64_t qi = int64_t(split) * Hq + h * G + g;
+    if (ch == 0) {
+      ws_ml[2 * qi] = block_max[qi];
+      ws_ml[2 * qi + 1] = Ls;
+    }
+    ws_o[qi * kAttnD + ch] = O;
+  }
+}
+
+hipError_t launch_attn_split(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
+                             const ChainArgs& vc, float scale, int32_t wph, int32_t splits, float* scores,
+                             float* block_max, float* ws_ml, float* ws_o, hipStream_t stream) {
+  const int32_t G = Hq / H;
+  const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
+  const uint16_t* qp = static_cast<const uint16_t*>(q);
+  const int nlk = kc.n_loops, nlv = vc.n_loops;
+#define FLK_S(NLV, F)                                                                                      \
+  case NLV:                                                                                                \
+    hipLaunchKernelGGL((attn_scores_kernel<NLV, F>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp, scale, \
+                       wph, scores, block_max);                                                            \
+    break;
+#define FLK_SF(F)                                                                                          \
+  case F:                                                                                                  \
+    switch (nlk) {                                                                                         \
+      FLK_S(1, F) FLK_S(2, F) FLK_S(3, F) FLK_S(4, F) FLK_S(5, F) FLK_S(6, F) FLK_S(7, F) FLK_S(8, F)     \
+      default: return hipErrorInvalidValue;                                                                \
+    }                                                                                                      \
+    break;
+  switch (fmt) {
+    FLK_SF(0)
+    default: return hipErrorInvalidValue;
+  }
+#undef FLK_SF
+#undef FLK_S
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define FLK_P(NLV)                                                                                         \
+  case NLV:                                                                                                \
+    hipLaunchKernelGGL((attn_pv_kernel<NLV>), grid, dim3(kAThreads), 0, stream, vc, T, H, G, scores, block_max, \
+                       wph, ws_ml, ws_o);                                                                  \
+    break;
+  switch (nlv) {
+    FLK_P(1) FLK_P(2) FLK_P(3) FLK_P(4) FLK_P(5) FLK_P(6) FLK_P(7) FLK_P(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef FLK_P
+  return hipGetLastError();
+}
+
+}  // namespace flk

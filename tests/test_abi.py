@@ -189,9 +189,9 @@ def test_noalloc_attention_validation():
     assert call(hq=30) == 2
     assert call(hq=8 * 17) == 5
     assert call(n_loops=0) == 2
-    # one KV head with 16 query heads over 2^19 tokens needs more than the scratch array holds
-    assert flk.attn_workspace_bytes(1, 128, 1 << 19, 16) > 16 << 20
-    assert call(H=1, hq=16, T=1 << 19) == 6
+    # one KV head with 16 query heads over 2^21 tokens needs more than the scratch array holds
+    assert flk.attn_workspace_bytes(1, 128, 1 << 21, 16) > 64 << 20
+    assert call(H=1, hq=16, T=1 << 21) == 6
 
 
 def test_status_strings():
