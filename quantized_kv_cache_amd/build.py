@@ -57,5 +57,20 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_check(src: str, verbose: bool = True) -> str:
+    """Compile a standalone gfx950 check program (test infrastructure, not part of the
+    library) next to its source, with the library's flags."""
+    exe = os.path.splitext(src)[0]
+    tmp = exe + ".tmp"
+    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-fPIC", "-ffp-contract=off")], src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n" + (r.stdout + r.stderr))
+    os.replace(tmp, exe)
+    if verbose:
+        print(f"built {exe}")
+    return exe
+
+
 if __name__ == "__main__":
     build()

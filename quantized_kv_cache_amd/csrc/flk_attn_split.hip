@@ -23,16 +23,118 @@
 namespace flk {
 
 // ---- pass 1: scores ------------------------------------------------------------------------
+//
+// A 4-bit code read as a binary16 bit pattern is the denormal code * 2^-24, so v_fma_mix_f32
+// takes it straight from a 16-bit half of the code word, with no conversion instruction.  The
+// scale is staged as the binary32 s * 2^24 (exact: a power-of-two multiple of a binary16
+// value) and the minimum as its binary16 bits; the product is then exactly code * s, and the
+// fma gives RN(code * s + m), the value the encoder's decode gives.
+// A lane's four items are four consecutive octets, 4*kb .. 4*kb+3 (32 channels, one 16-byte
+// code load per loop); the query operand takes the same channels, so the MFMA sums the same
+// products.
 
 template <int NL>
 struct ScoreLds {
-  uint32_t kp[NL][2][kAttnD];              // K parameter rows of the tile (two rowgroups)
+  float ks[NL][2][kAttnD];                 // K scale * 2^24 (binary32) per loop, rowgroup
+                                           // parity and channel
+  uint16_t km[NL][2][kAttnD];              // K minimum, FP16 bits
   int32_t map[NL][kGroup];                 // [loop][position in tile] -> compact row, -1 absent
   int32_t perm[kGroup];                    // tile positions grouped by which loops list them
 };
 
-template <int NL, int FMT>
-__global__ __launch_bounds__(kAThreads, 4) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
+// One slice's loads: per loop the lane's compact row (-1: the loop does not list the token)
+// and its 16 code bytes (octets 4*kb .. 4*kb+3).  Dense loops read position min(t, T - 1): a
+// lane past the end decodes a copy of the last row, whose score goes nowhere (an MFMA output
+// row depends on its own input row only).  A compact loop's absent token reads row 0 and
+// skips the decode.  So every load is unconditional and no register needs a default value.
+template <int NL>
+struct KSliceLoads {
+  int32_t j[NL];
+  uint4 cw[NL];
+};
+
+template <int NL>
+__device__ __forceinline__ void issue_k_slice(const ChainArgs& c, const TileRows<NL>& r, int32_t t, int32_t T,
+                                              int32_t H, int32_t h, int kb, const int32_t (*map)[kGroup],
+                                              int tk, KSliceLoads<NL>& ld) {
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    ld.j[l] = r.dense[l] ? min(t, T - 1) : map[l][tk];
+    const uint32_t item = uint32_t(max(ld.j[l], 0)) * uint32_t(H) + uint32_t(h);
+    ld.cw[l] = *reinterpret_cast<const uint4*>(c.s[l].codes + (item * (kAttnD / 2) + 16u * uint32_t(kb)));
+  }
+}
+
+// binary16 bits -> binary32 (exact; a code nibble gives the denormal code * 2^-24)
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// K_hat of the lane's four items, packed BF16 for the MFMA: the chain's
+// bf16(... bf16(bf16(base) + bf16(d2)) ... + bf16(dR)) with d = RN(code * s + m).
+template <int NL>
+__device__ __forceinline__ void decode_k_slice(const ChainArgs& c, const KSliceLoads<NL>& ld, int kb,
+                                               const ScoreLds<NL>& L, uint32_t ones, uint4 out[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float acc[8];
+    const int ch = 32 * kb + 8 * i;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      if (l > 0 && ld.j[l] < 0) continue;                // the base is dense: every lane decodes it
+      const int rg = c.ktile ? 0 : (ld.j[l] / kGroup) & 1;   // staged by rowgroup parity
+      const float4 s0 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch + 4]);
+      const uint4 mw = *reinterpret_cast<const uint4*>(&L.km[l][rg][ch]);
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const uint32_t mv[4] = {mw.x, mw.y, mw.z, mw.w};
+      const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
+      // code e sits in bits 4e .. 4e+3: word q holds codes q (low half) and q + 4 (high half)
+      uint32_t wq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wq[q] = (cwi >> (4 * q)) & 0x000F000Fu;
+      float d[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        d[q] = __builtin_fmaf(f16lo(wq[q]), sv[q], (q & 1) ? f16hi(mv[q >> 1]) : f16lo(mv[q >> 1]));
+        d[q + 4] = __builtin_fmaf(f16hi(wq[q]), sv[q + 4], (q & 1) ? f16hi(mv[2 + (q >> 1)]) : f16lo(mv[2 + (q >> 1)]));
+      }
+      if (l == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = d[e];
+      } else {
+        add_rounded_bf16x8(acc, d, ones);
+      }
+    }
+    out[i] = round_bf16x8(acc);
+  }
+}
+
+// One slice: decode K_hat, S^T = K_hat Q^T on the MFMA, the scaled scores to their positions'
+// entries of the scores rows and into the running maximum.
+template <int NL>
+__device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoads<NL>& ld, int kb,
+                                            const ScoreLds<NL>& L, uint32_t ones, const bf16x8_t qb[4], int sl,
+                                            int32_t n_valid, int32_t t0, int n, int32_t G, float scale,
+                                            float* srow, float& mx) {
+  uint4 item[4];
+  decode_k_slice<NL>(kc, ld, kb, L, ones, item);
+  float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item[ks]), qb[ks], sacc, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = 16 * sl + 4 * kb + i;
+    if (slot < n_valid) {
+      const float sc = sacc[i] * scale;
+      mx = fmaxf(mx, sc);
+      if (n < G) srow[t0 + L.perm[slot]] = sc;
+    }
+  }
+}
+
+template <int NL>
+__global__ __launch_bounds__(kAThreads, 3) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
                                                                    const uint16_t* __restrict__ q, float scale,
                                                                    int32_t wph, float* __restrict__ scores,
                                                                    float* __restrict__ block_max) {
@@ -54,20 +156,16 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_scores_kernel(ChainArgs kc,
   const int32_t tile1 = w < wph ? tile0 + base + (w < extra ? 1 : 0) : ptiles;
   ScoreLds<NL>& L = s_lds[wave];
   const int64_t Tpad = (int64_t(T) + 3) & ~int64_t(3);
+  const uint32_t ones = bf16_ones();
 
+  // query operand of k-step ks: channels 32*kb + 8*ks .. +7, the channels of the lane's item ks
   bf16x8_t qb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     uint4 qw = make_uint4(0, 0, 0, 0);
-    if (n < G) qw = *reinterpret_cast<const uint4*>(q + int64_t(h * G + n) * kAttnD + 32 * ks + 8 * kb);
+    if (n < G) qw = *reinterpret_cast<const uint4*>(q + int64_t(h * G + n) * kAttnD + 32 * kb + 8 * ks);
     qb[ks] = __builtin_bit_cast(bf16x8_t, qw);
   }
-  int oc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) oc[i] = 4 * i + kb;
-  float sgk[NL];
-#pragma unroll
-  for (int l = 0; l < NL; ++l) sgk[l] = loop_nv<FMT>(l) && l < kc.n_loops ? __uint_as_float(kc.s[l].params[0]) : 0.0f;
 
   float* srow = scores + int64_t(h * G + (n < G ? n : 0)) * Tpad;
   float mx = -__builtin_inff();
@@ -78,21 +176,24 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_scores_kernel(ChainArgs kc,
     build_maps<NL>(kc, rk, t0, L.map, lane);
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      if (l >= kc.n_loops || loop_fp4<FMT>(l)) continue;    // FP4 loops carry no K parameter rows
-      if (kc.ktile) {
-        if (rk.hi[l] > rk.lo[l]) {
-          const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(tile) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
-          *reinterpret_cast<uint2*>(&L.kp[l][0][2 * lane]) = pw;
-        }
-        continue;
-      }
-      const int32_t nrg = (kc.s[l].n + kGroup - 1) / kGroup;
+      if (l >= kc.n_loops) continue;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int32_t rg = rk.lo[l] / kGroup + r;
-        if ((r == 1 && rk.dense[l]) || rg >= nrg) continue;
-        const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(rg) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
-        *reinterpret_cast<uint2*>(&L.kp[l][rg & 1][2 * lane]) = pw;
+        int32_t row;                                      // the parameter row staged in slot r
+        if (kc.ktile) {
+          if (r == 1 || rk.hi[l] <= rk.lo[l]) continue;
+          row = tile;
+        } else {
+          const int32_t nrg = (kc.s[l].n + kGroup - 1) / kGroup;
+          row = rk.lo[l] / kGroup + r;
+          if ((r == 1 && rk.dense[l]) || row >= nrg) continue;
+        }
+        const int slot = kc.ktile ? 0 : (row & 1);
+        const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(row) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
+        // word = (min16, scale16): scale * 2^24 in binary32, the minima as they are
+        *reinterpret_cast<float2*>(&L.ks[l][slot][2 * lane]) = make_float2(f16hi(pw.x) * 16777216.0f,
+                                                                           f16hi(pw.y) * 16777216.0f);
+        *reinterpret_cast<uint32_t*>(&L.km[l][slot][2 * lane]) = __builtin_amdgcn_perm(pw.y, pw.x, 0x05040100u);
       }
     }
     // positions listed by the same loops sit together, so a loop none of a slice's tokens has
@@ -119,28 +220,24 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_scores_kernel(ChainArgs kc,
       L.perm[rank] = lane;
     }
     wave_sync();
-    // the next slice's code words are requested before this slice is decoded
-    ItemLoads<NL> cur, nxt;
-    issue_items<FLK_KIND_K, NL, FMT>(kc, rk, t0, T, H, h, L.perm[n], oc, L.map, cur);
-    for (int sl = 0; sl * 16 < n_valid; ++sl) {
-      if ((sl + 1) * 16 < n_valid)
-        issue_items<FLK_KIND_K, NL, FMT>(kc, rk, t0, T, H, h, L.perm[16 * (sl + 1) + n], oc, L.map, nxt);
-      uint4 item[4];
-      decode_loaded<FLK_KIND_K, NL, FMT>(kc, cur, oc, L.kp, sgk, item);
-      cur = nxt;
-      float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item[ks]), qb[ks], sacc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = 16 * sl + 4 * kb + i;
-        if (slot < n_valid) {
-          const float s = sacc[i] * scale;
-          mx = fmaxf(mx, s);
-          if (n < G) srow[t0 + L.perm[slot]] = s;
-        }
+    // two slices' loads in flight: slice sl + 1 is requested before slice sl is decoded (the
+    // loop takes the slices in pairs, so each slice's loads have fixed registers)
+    KSliceLoads<NL> la, lb;
+    issue_k_slice<NL>(kc, rk, t0 + L.perm[n], T, H, h, kb, L.map, L.perm[n], la);
+#pragma nounroll
+    for (int sl = 0; sl * 16 < n_valid; sl += 2) {
+      const bool second = (sl + 1) * 16 < n_valid;
+      if (second) {
+        const int tk = L.perm[16 * (sl + 1) + n];
+        issue_k_slice<NL>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, lb);
       }
+      score_slice<NL>(kc, la, kb, L, ones, qb, sl, n_valid, t0, n, G, scale, srow, mx);
+      if (!second) break;
+      if ((sl + 2) * 16 < n_valid) {
+        const int tk = L.perm[16 * (sl + 2) + n];
+        issue_k_slice<NL>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, la);
+      }
+      score_slice<NL>(kc, lb, kb, L, ones, qb, sl + 1, n_valid, t0, n, G, scale, srow, mx);
     }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -351,7 +448,7 @@ hipError_t launch_attn_split(int fmt, int32_t T, int32_t H, int32_t Hq, const vo
   const int nlk = kc.n_loops, nlv = vc.n_loops;
 #define FLK_S(NLV, F)                                                                                      \
   case NLV:                                                                                                \
-    hipLaunchKernelGGL((attn_scores_kernel<NLV, F>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp, scale, \
+    hipLaunchKernelGGL((attn_scores_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp, scale,   \
                        wph, scores, block_max);                                                            \
     break;
 #define FLK_SF(F)                                                                                          \
