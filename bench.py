@@ -186,6 +186,13 @@ class ChainSet:
             self.calls.append(("reconstruct", kind, L.flk_reconstruct,
                                (dp, w.T, arr, len(packed), P(out.data_ptr()))))
 
+    def call(self, i, stream_ptr):
+        """Issue call i alone on the stream stream_ptr."""
+        name, _, fn, args = self.calls[i]
+        st = fn(*args, stream_ptr)
+        if st != 0:
+            raise flk.FlkError(st, name)
+
     def run(self, streams, ev=None):
         """Issue one step: every call on the stream of its tensor (streams[kind]); ev[i], when
         given, is a pair of events recorded around call i on that same stream."""
@@ -222,16 +229,7 @@ def page_local_leg(w, host, sets, streams, steps, warmup, rotate):
         cs[k % rotate].run(streams)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    iso_stream = torch.cuda.Stream()
-    iso_streams = {k: (iso_stream, ctypes.c_void_p(iso_stream.cuda_stream)) for k in (flk.K, flk.V)}
-    n_calls = len(cs[0].calls)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
-    iso = []
-    for k in range(10):
-        cs[k % rotate].run(iso_streams, ev)
-        torch.cuda.synchronize()
-        iso.append([a.elapsed_time(b) for a, b in ev])
-    iso_us = np.median(np.array(iso), axis=0) * 1e3           # median: one slow launch moves no figure
+    iso_us = isolated_calls(cs, 10)
     k_calls = [{"call": name, "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
                for (kind, name, b), t in zip(per_call, iso_us) if kind == flk.K]
     rows_k = call_bytes(flk.K, w.H, w.D, w.T, sets)
@@ -243,25 +241,85 @@ def page_local_leg(w, host, sets, streams, steps, warmup, rotate):
             "k_calls_isolated": k_calls}
 
 
+def isolated_calls(chain_sets, reps):
+    """Duration (us) of every call of a step run alone: per call, `reps` launches back to back on
+    one stream (rotating over the buffer sets, so the MALL holds none of a launch's inputs), one
+    pair of events around them, the mean per launch.  A spin kernel queued first keeps the GPU
+    busy while the host issues the launches, so the events see no issue latency, and one event
+    pair per `reps` launches keeps the events' own cost (a cache flush each) out of the figure."""
+    iso_stream = torch.cuda.Stream()
+    sp = ctypes.c_void_p(iso_stream.cuda_stream)
+    n_calls = len(chain_sets[0].calls)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    for i in range(n_calls):
+        with torch.cuda.stream(iso_stream):
+            torch.cuda._sleep(ISO_SPIN_CYCLES)
+        ev[i][0].record(iso_stream)
+        for r in range(reps):
+            chain_sets[r % len(chain_sets)].call(i, sp)
+        ev[i][1].record(iso_stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3 / reps
+
+
+ISO_SPIN_CYCLES = 5_000_000       # about 2 ms at the shader clock: longer than the host's issue of the launches
+
+
 # ----------------------------------------------------------------------------- cpu baseline
 
-def cpu_baseline(w, host, sets, heads=(0, 1)):
-    """Time the oracle (as it stands, single thread) on a head sample of the same workload."""
+def host_threads():
+    """Worker threads for the host baseline: the process's CPU share (OMP_NUM_THREADS where the
+    environment sets it), never more than the CPUs the process may run on."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", avail))
+    except ValueError:
+        share = avail
+    return max(1, min(avail, share))
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_unit(kind, h, host, sets, w):
+    """The oracle's 4-loop chain + reconstruct of one KV head of one tensor (one independent unit:
+    K groups run within a head's channels, V groups within a head's row); returns its bytes."""
     from oracle import oracle as orc
-    total_bytes = 0
+    xs = [np.ascontiguousarray(x[:, h:h + 1]) for x in host[kind].xs]
+    chain, recon = orc.encode_chain(kind, xs, sets)
+    out = orc.reconstruct(kind, chain, w.T, 1, w.D)
+    assert np.array_equal(out, recon)
+    return sum(b for _, b in call_bytes(kind, 1, w.D, w.T, sets))
+
+
+def cpu_baseline(w, host, sets):
+    """Time the oracle (as it stands) on the host: the whole long-prompt step (every KV head of K
+    and V, full T) on a thread pool over the 2 x H independent (tensor, head) units -- the C
+    oracle releases the interpreter lock -- and, single-threaded, the units of KV head 0."""
+    from concurrent.futures import ThreadPoolExecutor
+    units = [(kind, h) for kind in (flk.K, flk.V) for h in range(w.H)]
+    n_threads = min(host_threads(), len(units))
     t0 = time.perf_counter()
-    for kind in (flk.K, flk.V):
-        for h in heads:
-            xs = [np.ascontiguousarray(x[:, h:h + 1]) for x in host[kind].xs]
-            chain, recon = orc.encode_chain(kind, xs, sets)
-            out = orc.reconstruct(kind, chain, w.T, 1, w.D)
-            assert np.array_equal(out, recon)
-            total_bytes += sum(b for _, b in call_bytes(kind, 1, w.D, w.T, sets))
+    with ThreadPoolExecutor(max_workers=n_threads) as ex:
+        total = sum(ex.map(lambda u: _oracle_unit(u[0], u[1], host, sets, w), units))
     dt = time.perf_counter() - t0
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"KV heads {list(heads)} of {w.H} for K and V (1/{w.H // len(heads)} of the step's "
-                      f"groups), full T={w.T}, same 4-loop chain + reconstruct; {dt:.1f} s single-threaded "
-                      f"C oracle on the host",
+    t1 = time.perf_counter()
+    one = sum(_oracle_unit(kind, 0, host, sets, w) for kind in (flk.K, flk.V))
+    dt1 = time.perf_counter() - t1
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"the whole step (K and V, all {w.H} KV heads, T={w.T}, 4-loop chain + reconstruct) as "
+                      f"{len(units)} (tensor, head) units on {n_threads} threads: {dt:.2f} s wall",
+            "single_thread": {"value": round(one / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"KV head 0 of K and V (1/{w.H} of the step): {dt1:.2f} s"},
+            "host": {"cpu_model": host_cpu_model(), "nproc": os.cpu_count(),
+                     "threads_allowed": host_threads()},
             "rows": cpu_baseline_rows(w, host, sets)}
 
 
@@ -367,13 +425,172 @@ def attention_leg(reps=20):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3)
     us = float(np.median(times))
-    rta = packed_bytes + 4 * 2 * T * H * D        # reconstruct K, V (write) then attend (read them)
+    fused = out.float().clone()
+    # the same attention the plain way: rebuild K_hat and V_hat in BF16 (flk_reconstruct), then
+    # attend over the BF16 cache (the BF16-tail reader of flk_decode_attn_rolling, no packed part)
+    kfull = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    vfull = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
+
+    def rta_call():
+        flk.reconstruct(flk.K, chains[flk.K], kfull)
+        flk.reconstruct(flk.V, chains[flk.V], vfull)
+        flk.decode_attn_rolling(q, [], [], 0, H, kfull, vfull, scale, out2, ws)
+    for _ in range(3):
+        rta_call()
+    torch.cuda.synchronize()
+    rta_us = _timed_us(rta_call, reps, flush)
+    o2 = out2.float()
+    rta_diff = float(((fused - o2).abs().amax(dim=1) / o2.abs().amax(dim=1)).max())
+    # bytes of that path: the packed chains read once, K_hat and V_hat written, then read back
+    rta = packed_bytes + 4 * 2 * T * H * D + 2 * Hq * D * 2
     return {"workload": "decode_attn", "T": T, "Hkv": H, "Hq": Hq, "D": D, "loops": w.n_loops,
             "budgets_pct": list(w.budgets), "median_us": round(us, 2),
             "p10_us": round(float(np.percentile(times, 10)), 2), "p90_us": round(float(np.percentile(times, 90)), 2),
             "algorithmic_bytes": int(algo), "gbs": round(algo / us / 1e3, 1),
             "hbm_frac": round(algo / us / 1e3 / HBM_PEAK_GBS, 4),
-            "reconstruct_then_attend_bytes": int(rta)}
+            "reconstruct_then_attend_us": round(rta_us, 2), "reconstruct_then_attend_bytes": int(rta),
+            "reconstruct_then_attend_gbs": round(rta / rta_us / 1e3, 1),
+            "fused_speedup": round(rta_us / us, 3),
+            "fused_vs_reconstruct_max_rel_diff": round(rta_diff, 6)}
+
+
+# ----------------------------------------------------------------------------- batched cache
+
+def _student_t3(shape, g):
+    """Student-t(3) draws on the device: N(0,1) / sqrt(chi2(3) / 3)."""
+    z = torch.randn(shape, device="cuda", generator=g)
+    c = (torch.randn(shape, device="cuda", generator=g) ** 2 + torch.randn(shape, device="cuda", generator=g) ** 2
+         + torch.randn(shape, device="cuda", generator=g) ** 2) / 3.0
+    return z / torch.sqrt(c)
+
+
+def batched_cache_leg(layers=24, requests=64):
+    """The batched cache: 64 requests with seeded lengths L ~ U{512..8192}, 16 KV heads, D = 128,
+    4 loops at 100/100/50/25 % of each request's L (compact loops over nested seeded active sets,
+    per request and layer), K and V of every (request, layer).  The library encodes one layer at
+    a time -- the base of all 128 of the layer's tensors in one flk_encode_base_batch call, then
+    one flk_encode_residual_batch call per loop -- and afterwards rebuilds every tensor of every
+    layer with flk_reconstruct_batch, one call per layer.  `layers` of the 24 layers are run (the
+    request lengths, and so every layer's shapes and bytes, are the same for all 24).  Inputs are
+    drawn on the device per layer (K: Student-t(3) times a per-(head, channel) multiplier
+    exp(U(ln 0.1, ln 10)); V: N(0,1); loop deltas N(0, 0.05)) outside the timed calls; each
+    layer's calls are timed with events, after a 512 MiB read that evicts the MALL.  GB/s from
+    the exact algorithmic bytes of the seeded lengths (each input read once, each output written
+    once)."""
+    w = synth.WORKLOADS[4]
+    H, D = w.H, w.D
+    lengths = [int(x) for x in synth.batched_lengths(requests)]
+    L_tot = sum(lengths)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261204)
+    L = flk.lib()
+    kd, vd = flk.desc(flk.K, H, D), flk.desc(flk.V, H, D)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    recon = {k: torch.empty((L_tot, H, D), dtype=torch.bfloat16, device="cuda") for k in (flk.K, flk.V)}
+    outs = {k: torch.empty((L_tot, H, D), dtype=torch.bfloat16, device="cuda") for k in (flk.K, flk.V)}
+    enc_bytes = rec_bytes = 0
+    enc_us, rec_us = [], []
+    streams = []                     # per layer: (kind, chain) per tensor, kept for the reconstruct
+    keep = []
+    for layer in range(layers):
+        sets = [synth.active_sets(w, Lr, request=r, layer=layer) for r, Lr in enumerate(lengths)]
+        # inputs of the layer: one trajectory per tensor over all requests' rows
+        xs = {}
+        for kind in (flk.K, flk.V):
+            if kind == flk.K:
+                mult = torch.exp(torch.empty((H, D), device="cuda").uniform_(math.log(0.1), math.log(10.0), generator=g))
+                y = _student_t3((L_tot, H, D), g) * mult
+            else:
+                y = torch.randn((L_tot, H, D), device="cuda", generator=g)
+            per_loop = []
+            for loop in range(w.n_loops):
+                if loop:
+                    y.add_(torch.randn((L_tot, H, D), device="cuda", generator=g), alpha=w.sigma)
+                xb = y.to(torch.bfloat16)
+                if sets[0][loop] is None:
+                    per_loop.append([xb[off[r]:off[r + 1]] for r in range(requests)])
+                else:
+                    per_loop.append([xb[off[r]:off[r + 1]][torch.from_numpy(sets[r][loop]).cuda().long()].contiguous()
+                                     for r in range(requests)])
+            xs[kind] = per_loop
+            del y
+        rows = [[None if sets[r][loop] is None else torch.from_numpy(sets[r][loop]).cuda()
+                 for loop in range(w.n_loops)] for r in range(requests)]
+        tables, layer_streams = [], []
+        chains = {}
+        for loop in range(w.n_loops):
+            units = []
+            for r, Lr in enumerate(lengths):
+                for kind in (flk.K, flk.V):
+                    rr = rows[r][loop]
+                    n = Lr if rr is None else len(rr)
+                    pk = flk.Packed.empty(kind, H, D, n, rr, T=Lr)
+                    chains.setdefault((r, kind), []).append(pk)
+                    rec = recon[kind][off[r]:off[r + 1]]
+                    x = xs[kind][loop][r]
+                    units.append(flk.UnitC(x.data_ptr(), None if rr is None else rr.data_ptr(), rec.data_ptr(),
+                                           pk.codes.data_ptr(), pk.params.data_ptr(),
+                                           None if rr is None else pk.tile_start.data_ptr(), n, Lr, kind, 0))
+                    if loop == 0:
+                        enc_bytes += 2 * Lr * H * D * 2 + flk.codes_bytes(kind, H, D, Lr) + \
+                            flk.params_bytes(kind, H, D, Lr, Lr)
+                    else:
+                        enc_bytes += 3 * n * H * D * 2 + flk.codes_bytes(kind, H, D, n) + \
+                            flk.params_bytes(kind, H, D, n, Lr) + flk.rows_bytes(n, rr is not None)
+            tables.append((flk.UnitC * len(units))(*units))
+        runits = []
+        for r, Lr in enumerate(lengths):
+            for kind in (flk.K, flk.V):
+                ch = chains[(r, kind)]
+                arr = (flk.StreamC * len(ch))(*[p.c() for p in ch])
+                keep.append(arr)
+                runits.append(flk.ReconUnitC(ctypes.cast(arr, ctypes.POINTER(flk.StreamC)),
+                                             outs[kind][off[r]:off[r + 1]].data_ptr(), Lr, len(ch), kind, 0))
+                rec_bytes += sum(flk.codes_bytes(kind, H, D, p.n_rows) + flk.params_bytes(kind, H, D, p.n_rows, Lr)
+                                 + flk.rows_bytes(p.n_rows, p.rows is not None) for p in ch) + Lr * H * D * 2
+        rtab = (flk.ReconUnitC * len(runits))(*runits)
+        keep += [tables, rtab, rows, chains]
+        streams.append(rtab)
+        torch.cuda.synchronize()
+        flush.view(torch.int64).sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st = L.flk_encode_base_batch(ctypes.byref(kd), ctypes.byref(vd), tables[0], len(tables[0]), None, sp)
+        for t in tables[1:]:
+            st = st or L.flk_encode_residual_batch(ctypes.byref(kd), ctypes.byref(vd), t, len(t), None, sp)
+        e1.record()
+        torch.cuda.synchronize()
+        if st != 0:
+            raise flk.FlkError(st, "batched encode")
+        enc_us.append(e0.elapsed_time(e1) * 1e3)
+        del xs
+    for layer, rtab in enumerate(streams):
+        flush.view(torch.int64).sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st = L.flk_reconstruct_batch(ctypes.byref(kd), ctypes.byref(vd), rtab, len(rtab), sp)
+        e1.record()
+        torch.cuda.synchronize()
+        if st != 0:
+            raise flk.FlkError(st, "batched reconstruct")
+        rec_us.append(e0.elapsed_time(e1) * 1e3)
+    enc_t, rec_t = sum(enc_us), sum(rec_us)
+    res = {"workload": "batched_cache", "requests": requests, "layers_run": layers, "layers_config": 24,
+           "H": H, "D": D, "tokens_per_layer": L_tot, "budgets_pct": list(w.budgets),
+           "tensors_per_layer": 2 * requests,
+           "encode": {"bytes": int(enc_bytes), "us": round(enc_t, 1), "gbs": round(enc_bytes / enc_t / 1e3, 1),
+                      "hbm_frac": round(enc_bytes / enc_t / 1e3 / HBM_PEAK_GBS, 4),
+                      "per_layer_us": [round(x, 1) for x in enc_us]},
+           "reconstruct": {"bytes": int(rec_bytes), "us": round(rec_t, 1), "gbs": round(rec_bytes / rec_t / 1e3, 1),
+                           "hbm_frac": round(rec_bytes / rec_t / 1e3 / HBM_PEAK_GBS, 4),
+                           "per_layer_us": [round(x, 1) for x in rec_us]},
+           "all_24_layers_estimate_s": round(24 * (enc_t + rec_t) / layers / 1e6, 3)}
+    del keep, streams, recon, outs
+    torch.cuda.empty_cache()
+    return res
 
 
 # ----------------------------------------------------------------------------- rolling tail
@@ -457,7 +674,34 @@ def sparse_leg(k=4096, reps=20):
         res[f"dense_depth{d}_us"] = round(_timed_us(dense[d], reps, flush), 2)
     res["sparse_loops_3_4_us"] = round(res["loop3_us"] + res["loop4_us"], 2)
     res["dense_loops_3_4_us"] = round(res["dense_depth3_us"] + res["dense_depth4_us"], 2)
+    # bytes of a loop call: the packed rows of the selected keys only
+    sel = st.sel.cpu().numpy()
+    sets = synth.active_sets(w, T)
+    for d in (3, 4):
+        b = sparse_loop_bytes(sel, sets[:d], T, H, D, Hq)
+        res[f"loop{d}_algorithmic_bytes"] = int(b)
+        res[f"loop{d}_gbs"] = round(b / res[f"loop{d}_us"] / 1e3, 1)
+        res[f"loop{d}_hbm_frac"] = round(b / res[f"loop{d}_us"] / 1e3 / HBM_PEAK_GBS, 4)
     return res
+
+
+def sparse_loop_bytes(sel, sets, T, H, D, Hq):
+    """Algorithmic bytes of a sparse loop call at depth len(sets) over tile-grouped K: per KV head,
+    the union of its query heads' selected positions; per such position and loop that lists it,
+    the K and V code rows (D/2 bytes each) and the V parameter row (4 bytes per 64 channels); per
+    (loop, 64-position tile) holding such a position, the tile's K parameter row (4 bytes per
+    channel); plus q, the reference state (mass, O_ref, C_ref), the selection and the output."""
+    G = Hq // H
+    total = 0
+    for h in range(H):
+        u = np.unique(sel[h * G:(h + 1) * G].ravel())
+        u = u[(u >= 0) & (u < T)]
+        for rows in sets:
+            listed = u if rows is None else u[np.isin(u, rows)]
+            total += len(listed) * (D // 2 + D // 2 + 4 * ((D + 63) // 64))
+            total += len(np.unique(listed // 64)) * 4 * D
+    total += Hq * D * 2 + Hq * (1 + 2 * D) * 4 + sel.size * 4 + Hq * D * 2
+    return total
 
 
 def selection_leg(reps=20):
@@ -498,6 +742,7 @@ def selection_leg(reps=20):
         b = 2 * n_prev * d * 2 + 4 * n_prev + 4 * n_prev + 4 * n_out + 4 * T + (8 * n_prev if compact else 0)
         res[f"{name}_us"] = round(us, 2)
         res[f"{name}_gbs"] = round(b / us / 1e3, 1)
+        res[f"{name}_hbm_frac"] = round(b / us / 1e3 / HBM_PEAK_GBS, 4)
     return res
 
 
@@ -688,6 +933,7 @@ def fp4_leg(w, host, sets, reps=30, rotate=2):
         res["formats"][name] = {
             **attn_us[name],
             "step_us": round(us, 2), "step_bytes": int(b_k + b_v), "gbs": round((b_k + b_v) / us / 1e3, 1),
+            "hbm_frac": round((b_k + b_v) / us / 1e3 / HBM_PEAK_GBS, 4),
             "stored_bytes": int(s_k + s_v),
             "bits_per_element": round(8 * (s_k + s_v) / (2 * sum((T if r is None else len(r)) for r in sets) * H * D), 4),
             **{k: round(v, 6) for k, v in acc.items()},
@@ -831,20 +1077,29 @@ def source_digest():
     return h.hexdigest()
 
 
-def copy_probe():
-    """Plain copies of COPY_PROBE_BYTES (read once, written once) by an elementwise kernel whose
-    name contains 'bitwise_not'; the counter runs divide its FETCH_SIZE / WRITE_SIZE into the
-    known size to get the scale applied to the codec kernels.  Returns the copy's GB/s."""
+def copy_probe(warm_s=0.3, reps=100):
+    """The practical ceiling: plain copies of COPY_PROBE_BYTES (read once, written once) by an
+    elementwise kernel whose name contains 'bitwise_not', timed at steady clocks -- about warm_s
+    seconds of copies first (the GPU reaches its sustained clocks only after some hundred
+    milliseconds of load), then `reps` copies between two events.  The counter runs also divide
+    its FETCH_SIZE / WRITE_SIZE into the known size to get the scale applied to the codec
+    kernels.  Returns the copy's GB/s (bytes read + written)."""
     src = torch.zeros(COPY_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.bitwise_not(src, out=dst)
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
     ev[0].record()
-    for _ in range(3):
+    for _ in range(reps):
         torch.bitwise_not(src, out=dst)
     ev[1].record()
     torch.cuda.synchronize()
-    return 2 * COPY_PROBE_BYTES * 3 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    gbs = 2 * COPY_PROBE_BYTES * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def _short_name(kernel_name):
@@ -897,10 +1152,24 @@ def summarize_pmc(dirs):
     return "\n".join(lines)
 
 
+def headline_launches():
+    """Kernel symbol -> launches per step of the headline (long-prompt, single calls)."""
+    w = synth.WORKLOADS[3]
+    sets = synth.active_sets(w, w.T)
+    per = {}
+    for kind in (flk.K, flk.V):
+        for name, _ in call_bytes(kind, w.H, w.D, w.T, sets):
+            sym = kernel_symbol(kind, name, w.H, w.D, sets)
+            per[sym] = per.get(sym, 0) + 1
+    return per
+
+
 def summarize_trace(trace_dir, warmup, steps, isolated=10):
-    """Per-kernel average durations from a rocprofv3 kernel trace of `bench.py` (default mode):
-    over all calls, and over the calls of the timed region alone (the codec kernels run a fixed
-    number of times per step, so the timed calls are a contiguous slice in dispatch order)."""
+    """Per-kernel durations from a rocprofv3 kernel trace of `bench.py` (default mode): over all
+    calls, and for the headline's kernels over its timed region and over its isolated launches.
+    A headline kernel runs c times per step and the headline's launches come first in dispatch
+    order (warmup steps, timed steps, then `isolated` launches of each call alone), so its timed
+    calls are launches [c*warmup, c*(warmup+steps)) and its isolated ones the next c*isolated."""
     import csv
     import glob
     paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
@@ -909,17 +1178,34 @@ def summarize_trace(trace_dir, warmup, steps, isolated=10):
         for r in csv.DictReader(open(path)):
             per.setdefault(_short_name(r["Kernel_Name"]), []).append(
                 (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
-    total_steps = warmup + steps + isolated
-    lines = [f"{'kernel':52s} {'calls':>6s} {'all_avg_us':>11s} {'timed_avg_us':>13s}"]
+    head = headline_launches()
+    lines = [f"{'kernel':52s} {'calls':>6s} {'all_avg_us':>11s} {'timed_avg_us':>13s} {'isolated_avg_us':>16s}"]
     for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
         v.sort()
         d = np.array([x for _, x in v])
-        c = len(d) // total_steps               # calls per step; the attention leg's own encodes
-        timed = ""                                # come after the timed region
-        if c >= 1 and len(d) - c * total_steps <= c:
+        timed = iso = ""
+        c = head.get(name, 0)
+        if c and len(d) >= c * (warmup + steps + isolated):
             timed = f"{d[warmup * c:(warmup + steps) * c].mean():13.2f}"
-        lines.append(f"{name[:52]:52s} {len(d):6d} {d.mean():11.2f} {timed:>13s}")
+            iso = f"{d[(warmup + steps) * c:(warmup + steps + isolated) * c].mean():16.2f}"
+        lines.append(f"{name[:52]:52s} {len(d):6d} {d.mean():11.2f} {timed:>13s} {iso:>16s}")
     return "\n".join(lines)
+
+
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_long_prompt.txt")
+
+
+def read_trace(symbol):
+    """(timed-region, isolated-step) average durations (us) of `symbol` in the committed
+    kernel-trace summary of the benchmark command, or (None, None)."""
+    if not os.path.exists(TRACE_FILE):
+        return None, None
+    for line in open(TRACE_FILE):
+        if line[:52].strip() == symbol[:52]:
+            parts = line[52:].split()
+            if len(parts) == 4:
+                return float(parts[2]), float(parts[3])
+    return None, None
 
 
 def summarize_counters(dirs, n_cu=256, clock_mhz=2400.0):
@@ -1001,8 +1287,12 @@ def main():
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse decode attention leg")
     ap.add_argument("--no-selection", action="store_true", help="skip the token selection leg")
     ap.add_argument("--no-fp4", action="store_true", help="skip the FP4 (NVFP4, MXFP4) variant leg")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched-cache leg")
+    ap.add_argument("--batched-layers", type=int, default=24,
+                    help="layers of the batched cache (64 requests each) the batched-cache leg runs (24 = all)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="run a plain copy of known size first (calibrates the HBM byte counters)")
+                    help="accepted for older command lines: the copy of known size (which calibrates the HBM "
+                         "byte counters) now always runs")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="print the traffic table from rocprofv3 counter output and exit (no GPU)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
@@ -1027,7 +1317,6 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     flk.lib()
-    copy_gbs = copy_probe() if args.copy_probe else None
 
     w = synth.WORKLOADS[3]
     log(f"generating workload {w.name}: T={w.T} H={w.H} D={w.D}")
@@ -1047,25 +1336,28 @@ def main():
         for kind in (flk.K, flk.V):
             per_call += [(kind, name, b) for name, b in call_bytes(kind, w.H, w.D, w.T, sets)]
     step_bytes = sum(b for _, _, b in per_call)
+    # the practical ceiling, measured at steady clocks right before the headline (the GPU then
+    # enters the headline's warmup at the clocks sustained load gives it)
+    log("copy ceiling ...")
+    copy_gbs = copy_probe()
     # default-priority streams only; in "streams" mode the K chain and the V chain overlap
     ts = [torch.cuda.Stream(), torch.cuda.Stream()] if args.mode == "streams" else [torch.cuda.Stream()] * 2
     streams = {k: (ts[i], ctypes.c_void_p(ts[i].cuda_stream)) for i, k in enumerate((flk.K, flk.V))}
 
-    # warmup (each call timed on its stream), and find the kernel with the largest share of the step
+    # warmup: every step back to back (no idle gaps while the clocks settle), events around each
+    # call of the last min(10, W) steps on the call's stream; they pick the kernel with the largest
+    # share of the overlapped step
     n_calls = len(chain_sets[0].calls)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
-    times = np.zeros(n_calls)
-    counted = 0
     n_warm = max(args.warmup, 1)
+    n_ev = min(10, n_warm)
+    wev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+           for _ in range(n_ev)]
     for i in range(n_warm):
-        if i < n_warm - 10:                       # continuous load while the clocks settle
-            chain_sets[i % args.rotate].run(streams)
-            continue
-        chain_sets[i % args.rotate].run(streams, ev)
-        torch.cuda.synchronize()
-        if i >= 1 or n_warm <= 1:
-            times += np.array([a.elapsed_time(b) for a, b in ev])
-            counted += 1
+        k = i - (n_warm - n_ev)
+        chain_sets[i % args.rotate].run(streams, wev[k] if k >= 0 else None)
+    torch.cuda.synchronize()
+    times = np.sum([[a.elapsed_time(b) for a, b in e] for e in wev], axis=0)
+    counted = n_ev
     symbols = [batched_symbol(name, sets) if kind == KV else kernel_symbol(kind, name, w.H, w.D, sets)
                for kind, name, _ in per_call]
     sym_time = {}
@@ -1089,55 +1381,70 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # each call alone: one stream, events around every call, nothing overlapping
-    iso_stream = torch.cuda.Stream()
-    iso_streams = {k: (iso_stream, ctypes.c_void_p(iso_stream.cuda_stream)) for k in (flk.K, flk.V)}
-    iso = []
-    n_iso = 10
-    for k in range(n_iso):
-        chain_sets[k % args.rotate].run(iso_streams, ev)
-        torch.cuda.synchronize()
-        iso.append([a.elapsed_time(b) for a, b in ev])
-    iso_us = np.median(np.array(iso), axis=0) * 1e3           # median: one slow launch moves no figure
+    iso_us = isolated_calls(chain_sets, 10)
     per_call_iso = [{"tensor": {flk.K: "K", flk.V: "V", KV: "K+V"}[kind], "call": name, "kernel": sy,
                      "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
                     for (kind, name, b), sy, t in zip(per_call, symbols, iso_us)]
 
+    # the timed region's event durations of the warmup's dominant kernel: with two streams they
+    # include waiting for compute units the other chain holds, so they are reported apart
     dom_ms = [dom_ev[k][i][0].elapsed_time(dom_ev[k][i][1]) for k in range(args.steps) for i in dom_idx]
     dom_bytes = float(np.mean([per_call[i][2] for i in dom_idx]))
     dom_avg_ms = float(np.mean(dom_ms))
-    achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(dominant)
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else int(traffic),
-                "traffic_unit": "bytes per launch", "launches_per_step": len(dom_idx),
-                "launch_avg_us": round(dom_avg_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(dom_bytes)}
+    prof_timed, _ = read_trace(dominant)
+    roofline_overlapped = {"kernel": dominant, "launch_avg_us": round(dom_avg_ms * 1e3, 2),
+                           "achieved": round(dom_bytes / (dom_avg_ms * 1e-3) / 1e9, 1),
+                           "frac": round(dom_bytes / (dom_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "note": "HIP events in the timed region, on the kernel's stream, overlapping the "
+                                   "other chain",
+                           "profile_launch_avg_us": prof_timed}
+
+    # the roofline's kernel: the largest summed time per step with every call timed alone (one
+    # stream, nothing overlapping), its duration the mean of its isolated launches; the committed
+    # kernel trace of this command gives the same launches' duration for comparison
+    iso_sym = {}
+    for sy, t in zip(symbols, iso_us):
+        iso_sym[sy] = iso_sym.get(sy, 0.0) + float(t)
+    rdom = max(iso_sym, key=iso_sym.get)
+    r_idx = [i for i, sy in enumerate(symbols) if sy == rdom]
+    r_bytes = float(np.mean([per_call[i][2] for i in r_idx]))
+    r_us = float(np.mean([iso_us[i] for i in r_idx]))
+    traffic = read_traffic(rdom)
+    _, prof_us = read_trace(rdom)
+    roofline = {"bound": "hbm", "kernel": rdom, "achieved": round(r_bytes / r_us / 1e3, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(r_bytes / r_us / 1e3 / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else int(traffic), "traffic_unit": "bytes per launch",
+                "launches_per_step": len(r_idx), "launch_avg_us": round(r_us, 2),
+                "algorithmic_bytes_per_launch": int(r_bytes),
+                "timing": "HIP events on the kernel's stream around 10 back-to-back launches of its call "
+                          "alone (rotating buffer sets, queued behind a spin kernel), mean per launch",
+                "profile_launch_avg_us": None if prof_us is None else prof_us,
+                "profile_frac": None if prof_us is None else round(r_bytes / prof_us / 1e3 / HBM_PEAK_GBS, 4),
+                "profile": os.path.relpath(TRACE_FILE, ROOT)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "copy_ceiling_gbs": round(copy_gbs, 1), "copy_frac": round(value / copy_gbs, 4),
         "config": {"workload": "long_prompt", "T": w.T, "H": w.H, "D": w.D, "loops": w.n_loops,
                    "budgets_pct": list(w.budgets), "tensors": "K+V", "step_bytes": int(step_bytes),
                    "rotate_sets": args.rotate, "mode": args.mode},
         "roofline": roofline,
+        "roofline_overlapped": roofline_overlapped,
     }
-    dom_iso_us = float(np.mean([iso_us[i] for i in dom_idx]))
-    result["roofline_isolated"] = {"bound": "hbm", "kernel": dominant, "achieved": round(dom_bytes / dom_iso_us / 1e3, 1),
-                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": round(dom_bytes / dom_iso_us / 1e3 / HBM_PEAK_GBS, 4),
-                                   "launch_avg_us": round(dom_iso_us, 2)}
     result["per_call_isolated"] = per_call_iso
     result["isolated_step_us"] = round(float(iso_us.sum()), 2)
-    if copy_gbs is not None:
-        result["copy_probe_gbs"] = round(copy_gbs, 1)
     if not args.no_page_local and args.mode != "batched":
         log("the same step with page-local K groups ...")
         result["page_local"] = page_local_leg(w, host, sets, streams, args.steps, args.warmup, args.rotate)
     if not args.no_attention:
         log("decode attention over the packed chains ...")
         result["decode_attention"] = attention_leg()
+    if not args.no_batched:
+        log(f"batched cache: {args.batched_layers} layers x 64 requests ...")
+        result["batched_cache"] = batched_cache_leg(layers=args.batched_layers)
     if not args.no_rolling:
         log("rolling tail: flush and attention ...")
         result["rolling"] = rolling_leg()

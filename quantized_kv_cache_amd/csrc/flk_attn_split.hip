@@ -65,10 +65,6 @@ __device__ __forceinline__ void issue_k_slice(const ChainArgs& c, const TileRows
   }
 }
 
-// binary16 bits -> binary32 (exact; a code nibble gives the denormal code * 2^-24)
-__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
-__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
-
 // K_hat of the lane's four items, packed BF16 for the MFMA: the chain's
 // bf16(... bf16(bf16(base) + bf16(d2)) ... + bf16(dR)) with d = RN(code * s + m).
 template <int NL>
@@ -88,10 +84,8 @@ __device__ __forceinline__ void decode_k_slice(const ChainArgs& c, const KSliceL
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const uint32_t mv[4] = {mw.x, mw.y, mw.z, mw.w};
       const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
-      // code e sits in bits 4e .. 4e+3: word q holds codes q (low half) and q + 4 (high half)
       uint32_t wq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wq[q] = (cwi >> (4 * q)) & 0x000F000Fu;
+      codes8_to_f16_halves(cwi, wq);
       float d[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -191,8 +185,8 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_scores_kernel(ChainArgs kc,
         const int slot = kc.ktile ? 0 : (row & 1);
         const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(row) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
         // word = (min16, scale16): scale * 2^24 in binary32, the minima as they are
-        *reinterpret_cast<float2*>(&L.ks[l][slot][2 * lane]) = make_float2(f16hi(pw.x) * 16777216.0f,
-                                                                           f16hi(pw.y) * 16777216.0f);
+        *reinterpret_cast<float2*>(&L.ks[l][slot][2 * lane]) = make_float2(f16hi(pw.x) * kCodeScale,
+                                                                           f16hi(pw.y) * kCodeScale);
         *reinterpret_cast<uint32_t*>(&L.km[l][slot][2 * lane]) = __builtin_amdgcn_perm(pw.y, pw.x, 0x05040100u);
       }
     }
@@ -260,7 +254,10 @@ struct PvStage {
   uint8_t codes[16][kAttnD / 2];
   uint32_t params[64];
 };
-constexpr int kPvBatch = 4;
+#ifndef FLK_PV_BATCH
+#define FLK_PV_BATCH 4
+#endif
+constexpr int kPvBatch = FLK_PV_BATCH;
 union PvLds {
   PvStage stage[kAWaves][kPvBatch];
   struct {

@@ -199,6 +199,53 @@ __device__ __forceinline__ uint4 round_bf16x8(float x[8]) {
   return w;
 }
 
+// acc[e] = bf16(acc[e]) + bf16(d[e]) in binary32, for 8 elements: v_cvt_pk_bf16_f32 rounds
+// the two operands into the halves of one word, and v_dot2_f32_bf16 against (1, 1) with a zero
+// addend sums them -- two instructions per element instead of three.  The dot's binary32 sum
+// is not always the correctly rounded one when the exponents are 16 or more apart, but every
+// such sum lies far from a BF16 rounding boundary, and each sum of the chain is rounded to
+// BF16 before it is used, so the BF16 results equal those of v_add_f32 (checked on the GPU
+// for every pair of +0 / finite normal BF16 values).  The eight dots sit in one asm statement
+// followed by the 3 wait states a VALU read of a dot's result needs; the compiler does not
+// know the instructions inside an asm statement and inserts no wait states for them.
+__device__ __forceinline__ void add_rounded_bf16x8(float acc[8], const float d[8], uint32_t ones) {
+  uint32_t p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = pack_bf16x2(acc[e], d[e]);
+  asm("v_dot2_f32_bf16 %0, %8, %16, 0\n\t"
+      "v_dot2_f32_bf16 %1, %9, %16, 0\n\t"
+      "v_dot2_f32_bf16 %2, %10, %16, 0\n\t"
+      "v_dot2_f32_bf16 %3, %11, %16, 0\n\t"
+      "v_dot2_f32_bf16 %4, %12, %16, 0\n\t"
+      "v_dot2_f32_bf16 %5, %13, %16, 0\n\t"
+      "v_dot2_f32_bf16 %6, %14, %16, 0\n\t"
+      "v_dot2_f32_bf16 %7, %15, %16, 0\n\t"
+      "s_nop 2"
+      : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5]),
+        "=&v"(acc[6]), "=&v"(acc[7])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "s"(ones));
+}
+// BF16 1.0 in both halves, in a scalar register (the three-operand dot2 takes no literal)
+__device__ __forceinline__ uint32_t bf16_ones() {
+  uint32_t x;
+  asm volatile("s_mov_b32 %0, 0x3f803f80" : "=s"(x));
+  return x;
+}
+
+// binary16 bits of the low / high half of a word -> binary32 (exact; a 4-bit code as the bit
+// pattern gives the subnormal code * 2^-24)
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// The 8 codes of a code word (code e in bits 4e .. 4e+3) as binary16 subnormals: word q holds
+// code q in its low half and code q + 4 in its high half.
+__device__ __forceinline__ void codes8_to_f16_halves(uint32_t cw, uint32_t wq[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wq[q] = (cw >> (4 * q)) & 0x000F000Fu;
+}
+
+constexpr float kCodeScale = 16777216.0f;   // 2^24: scale * 2^24 times code * 2^-24 is code * scale
+
 // ---- buffer-resource accesses ----------------------------------------------------------------
 // A raw buffer resource holds a scalar base address and a byte range; an access adds a
 // 32-bit per-lane offset (VGPR) and a 32-bit wave-uniform offset (SGPR), so per-row
