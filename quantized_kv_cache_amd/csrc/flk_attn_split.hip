@@ -33,6 +33,10 @@ namespace flk {
 // code load per loop); the query operand takes the same channels, so the MFMA sums the same
 // products.
 
+#ifndef FLK_SCORES_OCC
+#define FLK_SCORES_OCC 4   // waves per SIMD the scores pass's register budget must allow
+#endif
+
 template <int NL>
 struct ScoreLds {
   float ks[NL][2][kAttnD];                 // K scale * 2^24 (binary32) per loop, rowgroup
@@ -65,42 +69,39 @@ __device__ __forceinline__ void issue_k_slice(const ChainArgs& c, const TileRows
   }
 }
 
-// K_hat of the lane's four items, packed BF16 for the MFMA: the chain's
+// K_hat of the lane's item i (8 channels), packed BF16 for the MFMA: the chain's
 // bf16(... bf16(bf16(base) + bf16(d2)) ... + bf16(dR)) with d = RN(code * s + m).
 template <int NL>
-__device__ __forceinline__ void decode_k_slice(const ChainArgs& c, const KSliceLoads<NL>& ld, int kb,
-                                               const ScoreLds<NL>& L, uint32_t ones, uint4 out[4]) {
+__device__ __forceinline__ uint4 decode_k_item(const ChainArgs& c, const KSliceLoads<NL>& ld, int kb, int i,
+                                               const ScoreLds<NL>& L, uint32_t ones) {
+  float acc[8];
+  const int ch = 32 * kb + 8 * i;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float acc[8];
-    const int ch = 32 * kb + 8 * i;
+  for (int l = 0; l < NL; ++l) {
+    if (l > 0 && ld.j[l] < 0) continue;                  // the base is dense: every lane decodes it
+    const int rg = c.ktile ? 0 : (ld.j[l] / kGroup) & 1;   // staged by rowgroup parity
+    const float4 s0 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch]);
+    const float4 s1 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch + 4]);
+    const uint4 mw = *reinterpret_cast<const uint4*>(&L.km[l][rg][ch]);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const uint32_t mv[4] = {mw.x, mw.y, mw.z, mw.w};
+    const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
+    uint32_t wq[4];
+    codes8_to_f16_halves(cwi, wq);
+    float d[8];
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      if (l > 0 && ld.j[l] < 0) continue;                // the base is dense: every lane decodes it
-      const int rg = c.ktile ? 0 : (ld.j[l] / kGroup) & 1;   // staged by rowgroup parity
-      const float4 s0 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch]);
-      const float4 s1 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch + 4]);
-      const uint4 mw = *reinterpret_cast<const uint4*>(&L.km[l][rg][ch]);
-      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      const uint32_t mv[4] = {mw.x, mw.y, mw.z, mw.w};
-      const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
-      uint32_t wq[4];
-      codes8_to_f16_halves(cwi, wq);
-      float d[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        d[q] = __builtin_fmaf(f16lo(wq[q]), sv[q], (q & 1) ? f16hi(mv[q >> 1]) : f16lo(mv[q >> 1]));
-        d[q + 4] = __builtin_fmaf(f16hi(wq[q]), sv[q + 4], (q & 1) ? f16hi(mv[2 + (q >> 1)]) : f16lo(mv[2 + (q >> 1)]));
-      }
-      if (l == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = d[e];
-      } else {
-        add_rounded_bf16x8(acc, d, ones);
-      }
+    for (int q = 0; q < 4; ++q) {
+      d[q] = __builtin_fmaf(f16lo(wq[q]), sv[q], (q & 1) ? f16hi(mv[q >> 1]) : f16lo(mv[q >> 1]));
+      d[q + 4] = __builtin_fmaf(f16hi(wq[q]), sv[q + 4], (q & 1) ? f16hi(mv[2 + (q >> 1)]) : f16lo(mv[2 + (q >> 1)]));
     }
-    out[i] = round_bf16x8(acc);
+    if (l == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = d[e];
+    } else {
+      add_rounded_bf16x8(acc, d, ones);
+    }
   }
+  return round_bf16x8(acc);
 }
 
 // One slice: decode K_hat, S^T = K_hat Q^T on the MFMA, the scaled scores to their positions'
@@ -110,12 +111,13 @@ __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoa
                                             const ScoreLds<NL>& L, uint32_t ones, const bf16x8_t qb[4], int sl,
                                             int32_t n_valid, int32_t t0, int n, int32_t G, float scale,
                                             float* srow, float& mx) {
-  uint4 item[4];
-  decode_k_slice<NL>(kc, ld, kb, L, ones, item);
+  // each item goes to the MFMA as soon as it is decoded, so one item's registers are live
   float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item[ks]), qb[ks], sacc, 0, 0, 0);
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 item = decode_k_item<NL>(kc, ld, kb, ks, L, ones);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item), qb[ks], sacc, 0, 0, 0);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int slot = 16 * sl + 4 * kb + i;
@@ -128,7 +130,7 @@ __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoa
 }
 
 template <int NL>
-__global__ __launch_bounds__(kAThreads, 3) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
+__global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
                                                                    const uint16_t* __restrict__ q, float scale,
                                                                    int32_t wph, float* __restrict__ scores,
                                                                    float* __restrict__ block_max) {
@@ -291,7 +293,9 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
 
   // the block's maximum score of this lane's query head (pass 1); probabilities are relative to it
   const float m = n < G ? block_max[int64_t(split) * Hq + h * G + n] : 0.0f;
-  const float* srow = scores + int64_t(h * G + (n < G ? n : 0)) * Tpad;
+  // the KV head's scores rows, one resource; this lane's row starts srow_off floats in
+  const BufRsrc sb_rsrc = make_buf(scores + int64_t(h) * G * Tpad, uint32_t(int64_t(G) * Tpad * 4));
+  const uint32_t srow_off = uint32_t(n < G ? n : 0) * uint32_t(Tpad);
   const bool head_live = n < G && m != -__builtin_inff();
 
   float4_t o[8];
@@ -317,6 +321,7 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
     const uint32_t nbytes = uint32_t(st.n) * uint32_t(H);
     const BufRsrc cb = make_buf(st.codes, nbytes * (kAttnD / 2));
     const BufRsrc pb = make_buf(st.params, nbytes * 8u);
+    const BufRsrc rb = make_buf(dense ? nullptr : st.rows, dense ? 0u : uint32_t(st.n) * 4u);
     // batches of kPvBatch 16-row slices: every load of a batch (staging, positions, scores)
     // goes out before any of it is used, so a batch costs one exposed round trip, not one per slice
     for (int32_t jb = a; jb < b; jb += 16 * kPvBatch) {
@@ -333,21 +338,25 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
         __builtin_amdgcn_raw_ptr_buffer_load_lds(cb, (lds_ptr_t)&Sw[sb].codes[0][0], 16, co, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(pb, (lds_ptr_t)&Sw[sb].params[0], 4, po, 0, 0, 0);
       }
-      // this lane's rows 4*kb + r of each slice: positions, then scores and probabilities (0 past
-      // the range)
+      // this lane's rows 4*kb + r of each slice: positions, then scores (buffer loads with 32-bit
+      // offsets; a row past the range or of a dead head reads nothing and gets p = 0 below)
       int32_t pos[kPvBatch][4];
 #pragma unroll
       for (int sb = 0; sb < kPvBatch; ++sb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t j = jb + 16 * sb + 4 * kb + r;
-          pos[sb][r] = j < b && head_live ? (dense ? j : st.rows[j]) : -1;
+          pos[sb][r] = dense ? j : int32_t(buf_ld32(rb, j < b ? uint32_t(j) * 4u : kOutOfRange, 0u));
         }
       float sv[kPvBatch][4];
 #pragma unroll
       for (int sb = 0; sb < kPvBatch; ++sb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[sb][r] = pos[sb][r] >= 0 ? srow[pos[sb][r]] : -__builtin_inff();
+        for (int r = 0; r < 4; ++r) {
+          const int32_t j = jb + 16 * sb + 4 * kb + r;
+          const uint32_t so = j < b && head_live ? (srow_off + uint32_t(pos[sb][r])) * 4u : kOutOfRange;
+          sv[sb][r] = __uint_as_float(buf_ld32(sb_rsrc, so, 0u));
+        }
       __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): the staging has landed
       wave_sync();
 #pragma unroll
@@ -356,7 +365,8 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[r] = sv[sb][r] == -__builtin_inff() ? 0.0f : __expf(sv[sb][r] - m);
+          const int32_t j = jb + 16 * sb + 4 * kb + r;
+          p[r] = j < b && head_live ? __expf(sv[sb][r] - m) : 0.0f;
           if (l == 0) lsum += p[r];                       // the dense base lists every position once
         }
         const uint32_t pp01 = pack_f16x2(p[0], p[1]), pp23 = pack_f16x2(p[2], p[3]);
