@@ -1103,7 +1103,12 @@ def copy_probe(warm_s=0.3, reps=100):
 
 
 def _short_name(kernel_name):
-    n = kernel_name.split("(")[0].strip()
+    if "at::native::" in kernel_name:                # torch's kernels: the op's functor name
+        import re
+        m = re.search(r"at::native::(?:[A-Za-z_]\w*::)*?(\w*(?:_kernel_cuda|Functor_\w+|_kernel_impl\w*|reduce_kernel))",
+                      kernel_name)
+        return "torch " + (m.group(1) if m else kernel_name.split("<")[0].split()[-1])
+    n = kernel_name.replace("(anonymous namespace)::", "").split("(")[0].strip()
     for pre in ("void ", "flk::"):
         if n.startswith(pre):
             n = n[len(pre):]
@@ -1189,6 +1194,19 @@ def summarize_trace(trace_dir, warmup, steps, isolated=10):
             timed = f"{d[warmup * c:(warmup + steps) * c].mean():13.2f}"
             iso = f"{d[(warmup + steps) * c:(warmup + steps + isolated) * c].mean():16.2f}"
         lines.append(f"{name[:52]:52s} {len(d):6d} {d.mean():11.2f} {timed:>13s} {iso:>16s}")
+    return "\n".join(lines)
+
+
+def summarize_stats(stats_csv, top=40):
+    """rocprofv3 --stats kernel statistics (kernel_stats.csv) as a short table: per kernel the
+    calls, mean / min / max duration (us) and share of the summed kernel time."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"{'kernel':52s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share_%':>8s}"]
+    for r in rows[:top]:
+        lines.append(f"{_short_name(r['Name'])[:52]:52s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):8.2f}")
     return "\n".join(lines)
 
 
@@ -1298,6 +1316,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="print per-kernel instruction/occupancy counters from rocprofv3 --pmc CSV runs, and exit "
                          "(no GPU)")
+    ap.add_argument("--summarize-stats", metavar="CSV",
+                    help="print a rocprofv3 kernel_stats.csv as a short table and exit")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel durations (all calls, timed region) from a rocprofv3 kernel trace "
                          "of a run with the same --warmup/--steps, and exit (no GPU)")
@@ -1307,6 +1327,9 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
+        return
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
