@@ -37,11 +37,15 @@ namespace flk {
 #define FLK_SCORES_OCC 4   // waves per SIMD the scores pass's register budget must allow
 #endif
 
+constexpr int kKsRow = 36;                 // 32 scales + 4 pad: block b starts at bank 4b
+constexpr int kKmRow = 40;                 // 32 minima + 8 pad: blocks start at banks 0, 20, 8, 28
+
 template <int NL>
 struct ScoreLds {
-  float ks[NL][2][kAttnD];                 // K scale * 2^24 (binary32) per loop, rowgroup
-                                           // parity and channel
-  uint16_t km[NL][2][kAttnD];              // K minimum, FP16 bits
+  // Per loop and rowgroup parity, the 128 channels in 4 blocks of 32 (a lane block's channels),
+  // each block padded so the 4 lane blocks' reads of one instruction hit different banks:
+  float ks[NL][2][4][kKsRow];              // K scale * 2^24 (binary32)
+  uint16_t km[NL][2][4][kKmRow];           // K minimum, FP16 bits
   int32_t map[NL][kGroup];                 // [loop][position in tile] -> compact row, -1 absent
   int32_t perm[kGroup];                    // tile positions grouped by which loops list them
 };
@@ -75,14 +79,13 @@ template <int NL>
 __device__ __forceinline__ uint4 decode_k_item(const ChainArgs& c, const KSliceLoads<NL>& ld, int kb, int i,
                                                const ScoreLds<NL>& L, uint32_t ones) {
   float acc[8];
-  const int ch = 32 * kb + 8 * i;
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     if (l > 0 && ld.j[l] < 0) continue;                  // the base is dense: every lane decodes it
     const int rg = c.ktile ? 0 : (ld.j[l] / kGroup) & 1;   // staged by rowgroup parity
-    const float4 s0 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch]);
-    const float4 s1 = *reinterpret_cast<const float4*>(&L.ks[l][rg][ch + 4]);
-    const uint4 mw = *reinterpret_cast<const uint4*>(&L.km[l][rg][ch]);
+    const float4 s0 = *reinterpret_cast<const float4*>(&L.ks[l][rg][kb][8 * i]);
+    const float4 s1 = *reinterpret_cast<const float4*>(&L.ks[l][rg][kb][8 * i + 4]);
+    const uint4 mw = *reinterpret_cast<const uint4*>(&L.km[l][rg][kb][8 * i]);
     const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     const uint32_t mv[4] = {mw.x, mw.y, mw.z, mw.w};
     const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
@@ -187,9 +190,9 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
         const int slot = kc.ktile ? 0 : (row & 1);
         const uint2 pw = *reinterpret_cast<const uint2*>(kc.s[l].params + (uint32_t(row) * uint32_t(H) + uint32_t(h)) * kAttnD + 2 * lane);
         // word = (min16, scale16): scale * 2^24 in binary32, the minima as they are
-        *reinterpret_cast<float2*>(&L.ks[l][slot][2 * lane]) = make_float2(f16hi(pw.x) * kCodeScale,
+        *reinterpret_cast<float2*>(&L.ks[l][slot][lane >> 4][(2 * lane) & 31]) = make_float2(f16hi(pw.x) * kCodeScale,
                                                                            f16hi(pw.y) * kCodeScale);
-        *reinterpret_cast<uint32_t*>(&L.km[l][slot][2 * lane]) = __builtin_amdgcn_perm(pw.y, pw.x, 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&L.km[l][slot][lane >> 4][(2 * lane) & 31]) = __builtin_amdgcn_perm(pw.y, pw.x, 0x05040100u);
       }
     }
     // positions listed by the same loops sit together, so a loop none of a slice's tokens has
@@ -250,8 +253,15 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
 
 // ---- pass 2: PV from the V codes -----------------------------------------------------------
 
-// One wave's staging of a slice: 16 code rows (chunks swizzled, see vchunk) and 16 parameter
+// One wave's staging of a slice: 16 code rows (chunks swizzled, see pv_chunk) and 16 parameter
 // rows (words 32..63 stay unused).  A wave stages kPvBatch slices at a time.
+//
+// Token k = 4 kb + r of the MFMA (lane block kb, its r-th token) is staged row 4 r + kb, so one
+// read instruction's four rows (kb = 0..3) are consecutive: two even and two odd rows, which
+// lie in the two halves of the LDS banks (64-byte rows).  The two rows of a parity differ in
+// bit 1 of the row index, and pv_chunk moves their 16-byte chunks two places apart, so the 32
+// dwords of an instruction's reads fall in 32 distinct banks.
+__device__ __forceinline__ int pv_chunk(int row, int q) { return q ^ (((row >> 1) & 1) << 1); }
 struct PvStage {
   uint8_t codes[16][kAttnD / 2];
   uint32_t params[64];
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
 
   // this lane's staging slots: 16 bytes of code row crow (chunk cq), parameter word of prow
   const int crow = lane >> 2, prow = (lane & 31) >> 1;
-  const int cq = (lane & 3) ^ ((crow >> 2) & 3);
+  const int cq = pv_chunk(crow, lane & 3);
 
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
@@ -338,14 +348,15 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
         __builtin_amdgcn_raw_ptr_buffer_load_lds(cb, (lds_ptr_t)&Sw[sb].codes[0][0], 16, co, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(pb, (lds_ptr_t)&Sw[sb].params[0], 4, po, 0, 0, 0);
       }
-      // this lane's rows 4*kb + r of each slice: positions, then scores (buffer loads with 32-bit
-      // offsets; a row past the range or of a dead head reads nothing and gets p = 0 below)
+      // this lane's tokens 4 kb + r of each slice (staged rows 4 r + kb): positions, then scores
+      // (buffer loads with 32-bit offsets; a row past the range or of a dead head reads nothing
+      // and gets p = 0 below)
       int32_t pos[kPvBatch][4];
 #pragma unroll
       for (int sb = 0; sb < kPvBatch; ++sb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int32_t j = jb + 16 * sb + 4 * kb + r;
+          const int32_t j = jb + 16 * sb + 4 * r + kb;
           pos[sb][r] = dense ? j : int32_t(buf_ld32(rb, j < b ? uint32_t(j) * 4u : kOutOfRange, 0u));
         }
       float sv[kPvBatch][4];
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
       for (int sb = 0; sb < kPvBatch; ++sb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int32_t j = jb + 16 * sb + 4 * kb + r;
+          const int32_t j = jb + 16 * sb + 4 * r + kb;
           const uint32_t so = j < b && head_live ? (srow_off + uint32_t(pos[sb][r])) * 4u : kOutOfRange;
           sv[sb][r] = __uint_as_float(buf_ld32(sb_rsrc, so, 0u));
         }
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int32_t j = jb + 16 * sb + 4 * kb + r;
+          const int32_t j = jb + 16 * sb + 4 * r + kb;
           p[r] = j < b && head_live ? __expf(sv[sb][r] - m) : 0.0f;
           if (l == 0) lsum += p[r];                       // the dense base lists every position once
         }
@@ -375,10 +386,10 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
         uint2 vpw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 4 * kb + r;
+          const int row = 4 * r + kb;
           const uint16_t* cr = reinterpret_cast<const uint16_t*>(&S.codes[row][0]);
-          const uint32_t lo = cr[(16 * vchunk(row, n >> 3) + ((2 * n) & 15)) >> 1];
-          const uint32_t hi = cr[(16 * vchunk(row, 2 + (n >> 3)) + ((2 * n) & 15)) >> 1];
+          const uint32_t lo = cr[(16 * pv_chunk(row, n >> 3) + ((2 * n) & 15)) >> 1];
+          const uint32_t hi = cr[(16 * pv_chunk(row, 2 + (n >> 3)) + ((2 * n) & 15)) >> 1];
           d[r] = lo | (hi << 16);
           vpw[r] = *reinterpret_cast<const uint2*>(&S.params[2 * row]);
         }
