@@ -23,7 +23,10 @@ namespace flk {
 constexpr int kSD = 128;                     // head dimension
 constexpr int kSThreads = 256;
 constexpr int kSWaves = kSThreads / 64;
-constexpr int kKeysPerWave = 32;             // two 16-key slices per wave
+#ifndef FLK_SPARSE_KPW
+#define FLK_SPARSE_KPW 16
+#endif
+constexpr int kKeysPerWave = FLK_SPARSE_KPW;  // one 16-key slice per wave: more, shorter waves
 constexpr int kKeysPerBlock = kKeysPerWave * kSWaves;
 constexpr int kTopThreads = 1024;
 
@@ -432,10 +435,10 @@ __global__ __launch_bounds__(kSThreads) void chain_map_kernel(MapJobs jobs) {
 
 // ---------------------------------------------------------------------------------------
 // Gather: the selected keys of one query head, read through the chain at the call's depth.
-// A block covers 128 keys of one query head (4 waves x two 16-key slices).  Lane (n, kb) =
-// (lane & 15, lane >> 4) holds key n of the slice, channel octets kb, kb + 4, kb + 8, kb + 12
-// (32 channels); a key's score is summed over its 4 kb lanes, a slice's softmax over the 16 n
-// lanes, and each lane accumulates its own 32 output channels.
+// A block covers 4 waves x kKeysPerWave keys of one query head, in 16-key slices.  Lane (n, kb) =
+// (lane & 15, lane >> 4) holds key n of the slice, channels 32 kb .. 32 kb + 31; a key's score
+// is summed over its 4 kb lanes, a slice's softmax over the 16 n lanes, and each lane
+// accumulates its own 32 output channels.
 // ---------------------------------------------------------------------------------------
 struct GatherArgs {
   ChainArgs kc, vc;
@@ -450,14 +453,15 @@ struct GatherArgs {
   float scale;
 };
 
-// 8 channels (octet oc) of key position p of KV head h at the chain's depth, as binary32 values
-// that are exactly the BF16 reconstruction.  FMT: the chain's stream formats (INT4, or FP4 loops
-// as the fused decode attention takes them).
+// The lane's 32 channels 32 kb .. 32 kb + 31 of key position p of KV head h at the chain's
+// depth, as binary32 values that are exactly the BF16 reconstruction.  One 16-byte code load
+// per loop (the four octets are contiguous); an INT4 V loop's group word is one load (the 32
+// channels lie in one 64-channel group).  The chain's sums bf16(acc) + bf16(d) go through
+// v_dot2_f32_bf16 (add_rounded_bf16x8).  FMT: the chain's stream formats (INT4, or FP4 loops as
+// the fused decode attention takes them).
 template <int KIND, int NL, int FMT>
-__device__ __forceinline__ void gather_octet(const ChainArgs& c, const int32_t* const* maps, int32_t p, int32_t H,
-                                             int32_t h, int oc, float acc[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+__device__ __forceinline__ void gather_row32(const ChainArgs& c, const int32_t* const* maps, int32_t p, int32_t H,
+                                             int32_t h, int kb, uint32_t ones, float acc[32]) {
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     if (l >= c.n_loops) continue;
@@ -465,35 +469,44 @@ __device__ __forceinline__ void gather_octet(const ChainArgs& c, const int32_t* 
     const int32_t j = st.rows == nullptr ? p : maps[l][p];
     if (j < 0) continue;                                     // absent: inherits
     const uint32_t item = uint32_t(j) * uint32_t(H) + uint32_t(h);
-    const uint32_t cw = *reinterpret_cast<const uint32_t*>(st.codes + (item * (kSD / 2) + uint32_t(oc) * 4u));
-    float d[8];
-    if (loop_fp4<FMT>(l)) {
-      const uint32_t sb = fp4_scale_byte_128(st.params, item, oc, loop_mx<FMT>(l));
-      fp4_decode8(cw, loop_mx<FMT>(l) ? fp4_e8m0_value(sb) : fp4_e4m3_value(sb) * __uint_as_float(st.params[0]), d);
-      round_bf16x8_inplace(d);
+    const uint4 cw4 = *reinterpret_cast<const uint4*>(st.codes + (item * (kSD / 2) + 16u * uint32_t(kb)));
+    const uint32_t cws[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
+    uint32_t vw = 0;
+    if (KIND == FLK_KIND_V && !loop_fp4<FMT>(l)) vw = st.params[item * 2u + uint32_t(kb >> 1)];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
-      continue;
+    for (int i = 0; i < 4; ++i) {
+      const int oc = 4 * kb + i;
+      float d[8];
+      if (loop_fp4<FMT>(l)) {
+        const uint32_t sb = fp4_scale_byte_128(st.params, item, oc, loop_mx<FMT>(l));
+        fp4_decode8(cws[i], loop_mx<FMT>(l) ? fp4_e8m0_value(sb) : fp4_e4m3_value(sb) * __uint_as_float(st.params[0]), d);
+      } else {
+        uint32_t pw[8];
+        if (KIND == FLK_KIND_K) {
+          const uint32_t row = c.ktile ? uint32_t(p) / kGroup : uint32_t(j) / kGroup;
+          const uint4* pp = reinterpret_cast<const uint4*>(st.params + (row * uint32_t(H) + uint32_t(h)) * kSD + uint32_t(oc) * 8u);
+          const uint4 a = pp[0], b = pp[1];
+          pw[0] = a.x; pw[1] = a.y; pw[2] = a.z; pw[3] = a.w; pw[4] = b.x; pw[5] = b.y; pw[6] = b.z; pw[7] = b.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pw[e] = vw;
+        }
+        float cv[8];
+        codes8_to_f32(cws[i], cv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = decode(cv[e], f16_bits_to_f32(pw[e] & 0xFFFFu), f16_bits_to_f32(pw[e] >> 16));
+      }
+      float* a8 = acc + 8 * i;
+      if (l == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = d[e];
+      } else {
+        add_rounded_bf16x8(a8, d, ones);
+      }
     }
-    uint32_t pw[8];
-    if (KIND == FLK_KIND_K) {
-      const uint32_t row = c.ktile ? uint32_t(p) / kGroup : uint32_t(j) / kGroup;
-      const uint4* pp = reinterpret_cast<const uint4*>(st.params + (row * uint32_t(H) + uint32_t(h)) * kSD + uint32_t(oc) * 8u);
-      const uint4 a = pp[0], b = pp[1];
-      pw[0] = a.x; pw[1] = a.y; pw[2] = a.z; pw[3] = a.w; pw[4] = b.x; pw[5] = b.y; pw[6] = b.z; pw[7] = b.w;
-    } else {
-      const uint32_t w = st.params[item * 2u + uint32_t(oc >> 3)];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pw[e] = w;
-    }
-    float cv[8];
-    codes8_to_f32(cw, cv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = decode(cv[e], f16_bits_to_f32(pw[e] & 0xFFFFu), f16_bits_to_f32(pw[e] >> 16));
-    round_bf16x8_inplace(d);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = l == 0 ? d[e] : round_bf16(acc[e] + d[e]);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) round_bf16x8(acc + 8 * i);   // the last rounding, in place
 }
 
 __device__ __forceinline__ float sum16(float v) {          // over lane bits 0..3
@@ -524,17 +537,17 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
   const int32_t key0 = int32_t(blockIdx.x) * kKeysPerBlock + wave * kKeysPerWave;
   const int32_t* sel = g.sel + int64_t(qh) * g.k;
 
-  float qv[32];
+  // the query's channels 32 kb .. 32 kb + 31 as BF16 pairs (the score is a sum of dot2 steps)
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  uint32_t qp[16];
   if (MODE == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 w = *reinterpret_cast<const uint4*>(g.q + int64_t(qh) * kSD + (4 * i + kb) * 8);
-      qv[8 * i + 0] = bf16_lo(w.x); qv[8 * i + 1] = bf16_hi(w.x);
-      qv[8 * i + 2] = bf16_lo(w.y); qv[8 * i + 3] = bf16_hi(w.y);
-      qv[8 * i + 4] = bf16_lo(w.z); qv[8 * i + 5] = bf16_hi(w.z);
-      qv[8 * i + 6] = bf16_lo(w.w); qv[8 * i + 7] = bf16_hi(w.w);
+      const uint4 w = *reinterpret_cast<const uint4*>(g.q + int64_t(qh) * kSD + 32 * kb + 8 * i);
+      qp[4 * i + 0] = w.x; qp[4 * i + 1] = w.y; qp[4 * i + 2] = w.z; qp[4 * i + 3] = w.w;
     }
   }
+  const uint32_t ones = bf16_ones();
   float M = 0.0f, Linv = 0.0f;
   if (MODE == 0) {
     M = g.ml[2 * qh];
@@ -556,13 +569,12 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
     if (MODE == 1) {
       float s = 0.0f;
       if (p >= 0) {
+        float kv[32];
+        gather_row32<FLK_KIND_K, NL, FMT>(g.kc, g.kmap, p, g.H, h, kb, ones, kv);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float kv[8];
-          gather_octet<FLK_KIND_K, NL, FMT>(g.kc, g.kmap, p, g.H, h, 4 * i + kb, kv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[8 * i + e], kv[e], s);
-        }
+        for (int c2 = 0; c2 < 16; ++c2)                   // K_hat is exactly BF16: the pairs are exact
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pack_bf16x2(kv[2 * c2], kv[2 * c2 + 1])),
+                                              __builtin_bit_cast(bf16x2v, qp[c2]), s, false);
       }
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
@@ -575,25 +587,19 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
 #pragma unroll
       for (int c = 0; c < 32; ++c) o[c] *= corr;
       if (p >= 0) {
+        float vv[32];
+        gather_row32<FLK_KIND_V, NL, FMT>(g.vc, g.vmap, p, g.H, h, kb, ones, vv);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float vv[8];
-          gather_octet<FLK_KIND_V, NL, FMT>(g.vc, g.vmap, p, g.H, h, 4 * i + kb, vv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[8 * i + e] = __builtin_fmaf(pn, vv[e], o[8 * i + e]);
-        }
+        for (int c2 = 0; c2 < 32; ++c2) o[c2] = __builtin_fmaf(pn, vv[c2], o[c2]);
       }
     } else {
       const float w = p >= 0 ? __expf(g.scores[int64_t(qh) * score_stride(g.T) + p] - M) * Linv : 0.0f;
       m_run += sum16(w);
       if (p >= 0) {
+        float vv[32];
+        gather_row32<FLK_KIND_V, NL, FMT>(g.vc, g.vmap, p, g.H, h, kb, ones, vv);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float vv[8];
-          gather_octet<FLK_KIND_V, NL, FMT>(g.vc, g.vmap, p, g.H, h, 4 * i + kb, vv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[8 * i + e] = __builtin_fmaf(w, vv[e], o[8 * i + e]);
-        }
+        for (int c2 = 0; c2 < 32; ++c2) o[c2] = __builtin_fmaf(w, vv[c2], o[c2]);
       }
     }
   }
@@ -602,9 +608,7 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
   for (int c = 0; c < 32; ++c) o[c] = sum16(o[c]);
   if (n == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][(4 * i + kb) * 8 + e] = o[8 * i + e];
+    for (int c2 = 0; c2 < 32; ++c2) s_o[wave][32 * kb + c2] = o[c2];
     if (kb == 0) {
       s_m[wave] = m_run;
       s_l[wave] = l_run;
