@@ -31,13 +31,13 @@ namespace flk {
 
 // The workspace a call over T packed tokens and a tail of tail_len tokens uses: one partial
 // (m, l, O) and one block maximum per query head and split, then the two-pass path's scores,
-// one row of ceil(T/4)*4 binary32 per query head.
+// one row of ceil(T/4)*4 binary32 per query head (T counting the tail's tokens as well).
 static size_t attn_ws_bytes(int32_t splits, int32_t T, int32_t Hq) {
   return size_t(splits) * size_t(Hq) * (2 + kAttnD + 1) * sizeof(float) +
          size_t(Hq) * ((size_t(T) + 3) & ~size_t(3)) * sizeof(float);
 }
 size_t attn_workspace_need(int32_t T, int32_t tail_len, int32_t H, int32_t Hq) {
-  return attn_ws_bytes(n_splits(attn_tiles(T, tail_len), H), T, Hq);
+  return attn_ws_bytes(n_splits(attn_tiles(T, tail_len), H), T + tail_len, Hq);
 }
 
 // A bound on attn_workspace_need for every call over at most T_total tokens: such a call has at
@@ -481,12 +481,13 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
   int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
   if (nl < 1) nl = 1;                              // no packed tokens: only the tail's tiles run
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
-  if (FMT == 0 && tail_len == 0 && T > 0) {
-    // INT4 chains without a tail: the scores of every position, then PV straight from the V codes
+  if (FMT == 0 && T > 0 && (!SC || tail_len == 0)) {
+    // INT4 chains: the scores of every position (packed, then the BF16 tail), then PV straight
+    // from the V codes (the tail's V as stored)
     float* block_max = ws_o + size_t(splits) * Hq * kAttnD;
     float* sc = SC ? scores : block_max + size_t(splits) * Hq;
-    const hipError_t e = launch_attn_split(0, T, H, Hq, q, kc, vc, scale, wph, splits, sc, block_max, ws_ml, ws_o,
-                                           stream);
+    const hipError_t e = launch_attn_split(0, T, H, Hq, q, kc, vc, k_tail, v_tail, tail_len, scale, wph, splits, sc,
+                                           block_max, ws_ml, ws_o, stream);
     if (e != hipSuccess) return e;
   } else {
 #define FLK_A(NLV)                                                                                          \

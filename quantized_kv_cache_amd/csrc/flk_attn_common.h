@@ -295,11 +295,13 @@ __device__ __forceinline__ const T* opaque_ptr(const T* p) {
 }
 
 
-// The two-pass decode attention over INT4 chains without a tail (flk_attn_split.hip): scores
-// (binary32 rows of ceil(T/4)*4 per query head) and block maxima, then the PV partials (m, l, O)
-// per split and query head that attn_combine_kernel merges.
+// The two-pass decode attention over INT4 chains and an optional BF16 tail (flk_attn_split.hip):
+// scores (binary32 rows of ceil((T + tail_len)/4)*4 per query head, the tail's after the packed
+// positions) and block maxima, then the PV partials (m, l, O) per split and query head that
+// attn_combine_kernel merges.
 hipError_t launch_attn_split(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
-                             const ChainArgs& vc, float scale, int32_t wph, int32_t splits, float* scores,
-                             float* block_max, float* ws_ml, float* ws_o, hipStream_t stream);
+                             const ChainArgs& vc, const void* k_tail, const void* v_tail, int32_t tail_len,
+                             float scale, int32_t wph, int32_t splits, float* scores, float* block_max, float* ws_ml,
+                             float* ws_o, hipStream_t stream);
 
 }  // namespace flk

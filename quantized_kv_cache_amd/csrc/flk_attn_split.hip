@@ -17,7 +17,8 @@
 // 1e-1 for K.
 // Both passes use the same blocks (split, KV head), so the block maximum of pass 1 is the
 // reference of pass 2's probabilities and pass 2's partial (max, sum, O) per block merges in
-// the same combine kernel as the fused path.
+// the same combine kernel as the fused path.  A BF16 tail (a rolling cache's recent tokens)
+// is read as stored, 16 tokens per wave, in both passes; its scores follow the packed ones.
 #include "flk_attn_common.h"
 
 namespace flk {
@@ -132,11 +133,14 @@ __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoa
   }
 }
 
-template <int NL>
+// TAIL: the call has a BF16 tail (an instance of its own, so the packed-only loop keeps its
+// register allocation).
+template <int NL, bool TAIL>
 __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
                                                                    const uint16_t* __restrict__ q, float scale,
                                                                    int32_t wph, float* __restrict__ scores,
-                                                                   float* __restrict__ block_max) {
+                                                                   float* __restrict__ block_max,
+                                                                   const uint16_t* __restrict__ kt, int32_t tail_len) {
   __shared__ __attribute__((aligned(16))) ScoreLds<NL> s_lds[kAWaves];
   __shared__ float s_max[kAWaves][kMaxG];
   const int lane = threadIdx.x & 63;
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
   const int32_t tile0 = w < wph ? w * base + min(w, extra) : ptiles;
   const int32_t tile1 = w < wph ? tile0 + base + (w < extra ? 1 : 0) : ptiles;
   ScoreLds<NL>& L = s_lds[wave];
-  const int64_t Tpad = (int64_t(T) + 3) & ~int64_t(3);
+  const int64_t Tpad = (int64_t(T) + (TAIL ? tail_len : 0) + 3) & ~int64_t(3);   // positions T.. hold the tail
   const uint32_t ones = bf16_ones();
 
   // query operand of k-step ks: channels 32*kb + 8*ks .. +7, the channels of the lane's item ks
@@ -168,6 +172,28 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
 
   float* srow = scores + int64_t(h * G + (n < G ? n : 0)) * Tpad;
   float mx = -__builtin_inff();
+  // The BF16 tail, read as stored, in 16-token slices: slice s goes to waves s, s + wph, ...
+  // of every head (a small addition to many waves); its scores follow the packed positions.
+  const int32_t tail_slices = (tail_len + 15) / 16;
+  for (int32_t ts = w; TAIL && w < wph && ts < tail_slices; ts += wph) {
+    const int32_t nv = min(16, tail_len - 16 * ts);
+    const int64_t b = (int64_t(16 * ts + n) * H + h) * kAttnD + 32 * kb;
+    float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 item = n < nv ? *reinterpret_cast<const uint4*>(kt + b + 8 * ks) : make_uint4(0, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item), qb[ks], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 4 * kb + i;
+      if (slot < nv) {
+        const float sc = sacc[i] * scale;
+        mx = fmaxf(mx, sc);
+        if (n < G) srow[int64_t(T) + 16 * ts + slot] = sc;
+      }
+    }
+  }
   for (int32_t tile = tile0; tile < tile1; ++tile) {
     const int32_t t0 = tile * kGroup;
     const TileRows<NL> rk = tile_rows<NL>(kc, tile, T);
@@ -270,6 +296,7 @@ struct PvStage {
 #define FLK_PV_BATCH 4
 #endif
 constexpr int kPvBatch = FLK_PV_BATCH;
+static_assert(sizeof(PvStage) * kPvBatch >= 16 * kAttnD * sizeof(uint16_t), "a wave's staging holds a BF16 tail slice");
 union PvLds {
   PvStage stage[kAWaves][kPvBatch];
   struct {
@@ -282,7 +309,8 @@ template <int NL>
 __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int32_t T, int32_t H, int32_t G,
                                                                const float* __restrict__ scores,
                                                                const float* __restrict__ block_max, int32_t wph,
-                                                               float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+                                                               float* __restrict__ ws_ml, float* __restrict__ ws_o,
+                                                               const uint16_t* __restrict__ vt, int32_t tail_len) {
   __shared__ __attribute__((aligned(16))) PvLds s_lds;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -298,7 +326,7 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
   const int32_t tile0 = w < wph ? w * base + min(w, extra) : ptiles;
   const int32_t tile1 = w < wph ? tile0 + base + (w < extra ? 1 : 0) : ptiles;
   PvStage* Sw = s_lds.stage[wave];
-  const int64_t Tpad = (int64_t(T) + 3) & ~int64_t(3);
+  const int64_t Tpad = (int64_t(T) + tail_len + 3) & ~int64_t(3);
   const int32_t P0 = tile0 * kGroup, P1 = min(tile1 * kGroup, T);
 
   // the block's maximum score of this lane's query head (pass 1); probabilities are relative to it
@@ -319,6 +347,40 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
   // this lane's staging slots: 16 bytes of code row crow (chunk cq), parameter word of prow
   const int crow = lane >> 2, prow = (lane & 31) >> 1;
   const int cq = pv_chunk(crow, lane & 3);
+
+  // The BF16 tail, as the scores pass split it: per 16-token slice, its V rows through the
+  // wave's staging area in LDS (16 rows of 128 BF16), O^T += V^T P^T on the BF16 MFMA
+  const int32_t tail_slices = (tail_len + 15) / 16;
+  for (int32_t ts = w; w < wph && ts < tail_slices; ts += wph) {
+    const int32_t nv = min(16, tail_len - 16 * ts);
+    uint16_t (*vs)[kAttnD] = reinterpret_cast<uint16_t (*)[kAttnD]>(&Sw[0]);
+    wave_sync();                                          // earlier reads of the staging area are done
+    {
+      const int row = lane >> 2, c0 = 32 * (lane & 3);
+      const int64_t b = (int64_t(16 * ts + row) * H + h) * kAttnD + c0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(&vs[row][c0 + 8 * i]) =
+            row < nv ? *reinterpret_cast<const uint4*>(vt + b + 8 * i) : make_uint4(0, 0, 0, 0);
+    }
+    short4_t pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t k = 4 * kb + r;
+      const float p = k < nv && head_live ? __expf(__uint_as_float(buf_ld32(sb_rsrc, (srow_off + uint32_t(T + 16 * ts + k)) * 4u, 0u)) - m)
+                                          : 0.0f;
+      lsum += p;
+      pb[r] = short(__builtin_bit_cast(uint16_t, (__bf16)p));
+    }
+    wave_sync();
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      short4_t a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = short(vs[4 * kb + r][pv_channel(mt, n)]);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[mt], 0, 0, 0);
+    }
+  }
 
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
@@ -458,36 +520,39 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
 }
 
 hipError_t launch_attn_split(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
-                             const ChainArgs& vc, float scale, int32_t wph, int32_t splits, float* scores,
-                             float* block_max, float* ws_ml, float* ws_o, hipStream_t stream) {
+                             const ChainArgs& vc, const void* k_tail, const void* v_tail, int32_t tail_len,
+                             float scale, int32_t wph, int32_t splits, float* scores, float* block_max, float* ws_ml,
+                             float* ws_o, hipStream_t stream) {
+  const uint16_t* kt = static_cast<const uint16_t*>(k_tail);
+  const uint16_t* vt = static_cast<const uint16_t*>(v_tail);
   const int32_t G = Hq / H;
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const int nlk = kc.n_loops, nlv = vc.n_loops;
-#define FLK_S(NLV, F)                                                                                      \
+  if (fmt != 0) return hipErrorInvalidValue;
+#define FLK_S(NLV, TL)                                                                                     \
   case NLV:                                                                                                \
-    hipLaunchKernelGGL((attn_scores_kernel<NLV>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp, scale,   \
-                       wph, scores, block_max);                                                            \
+    hipLaunchKernelGGL((attn_scores_kernel<NLV, TL>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp,     \
+                       scale, wph, scores, block_max, kt, tail_len);                                       \
     break;
-#define FLK_SF(F)                                                                                          \
-  case F:                                                                                                  \
-    switch (nlk) {                                                                                         \
-      FLK_S(1, F) FLK_S(2, F) FLK_S(3, F) FLK_S(4, F) FLK_S(5, F) FLK_S(6, F) FLK_S(7, F) FLK_S(8, F)     \
-      default: return hipErrorInvalidValue;                                                                \
-    }                                                                                                      \
-    break;
-  switch (fmt) {
-    FLK_SF(0)
-    default: return hipErrorInvalidValue;
+#define FLK_ST(TL)                                                                                         \
+  switch (nlk) {                                                                                           \
+    FLK_S(1, TL) FLK_S(2, TL) FLK_S(3, TL) FLK_S(4, TL) FLK_S(5, TL) FLK_S(6, TL) FLK_S(7, TL) FLK_S(8, TL) \
+    default: return hipErrorInvalidValue;                                                                  \
   }
-#undef FLK_SF
+  if (tail_len > 0) {
+    FLK_ST(true)
+  } else {
+    FLK_ST(false)
+  }
+#undef FLK_ST
 #undef FLK_S
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 #define FLK_P(NLV)                                                                                         \
   case NLV:                                                                                                \
     hipLaunchKernelGGL((attn_pv_kernel<NLV>), grid, dim3(kAThreads), 0, stream, vc, T, H, G, scores, block_max, \
-                       wph, ws_ml, ws_o);                                                                  \
+                       wph, ws_ml, ws_o, vt, tail_len);                                                    \
     break;
   switch (nlv) {
     FLK_P(1) FLK_P(2) FLK_P(3) FLK_P(4) FLK_P(5) FLK_P(6) FLK_P(7) FLK_P(8)

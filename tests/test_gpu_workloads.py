@@ -123,6 +123,52 @@ def test_decode_attention_shapes(T, H, Hq, sizes):
     assert np.all(rel <= 2e-2), rel
 
 
+@pytest.mark.parametrize("T,tail_len,H,Hq,sizes", [
+    (1, 1, 1, 1, [None]),                     # one packed token, one tail token
+    (63, 300, 2, 8, [None, None]),            # a partial tile, a tail of several slices
+    (1025, 17, 4, 16, [None, None, 700, 3]),  # a split boundary; a tail slice plus one token
+    (4096, 127, 8, 128, [None, 4096, 2048, 1]),  # G = 16, a rolling cache's longest tail
+])
+def test_decode_attention_packed_prefix_and_tail(T, tail_len, H, Hq, sizes):
+    """Attention over packed INT4 chains plus a BF16 tail (flk_decode_attn_rolling with T > 0):
+    the tail's scores follow the packed ones in both passes.  Against the oracle's exact
+    attention over the reconstruction followed by the tail, within 2e-2 normwise per head."""
+    D = 128
+    rng = np.random.default_rng(7 * T + tail_len)
+    xs = {flk.K: [], flk.V: []}
+    rows = []
+    prev = np.arange(T, dtype=np.int32)
+    yk = (2.0 * rng.standard_normal((T, H, D))).astype(np.float32)
+    yv = rng.standard_normal((T, H, D)).astype(np.float32)
+    for r, n in enumerate(sizes):
+        if r:
+            yk = yk + (0.05 * rng.standard_normal((T, H, D))).astype(np.float32)
+            yv = yv + (0.05 * rng.standard_normal((T, H, D))).astype(np.float32)
+        if n is not None:
+            prev = np.sort(rng.choice(prev, size=n, replace=False)).astype(np.int32)
+        sel = None if n is None else prev
+        for kind, yy in ((flk.K, yk), (flk.V, yv)):
+            xb = synth.to_bf16_bits(yy)
+            xs[kind].append(xb if sel is None else np.ascontiguousarray(xb[sel]))
+        rows.append(sel)
+    g = {k: GpuChain(k, xs[k], rows) for k in (flk.K, flk.V)}
+    o = {k: OracleChain(k, xs[k], rows) for k in (flk.K, flk.V)}
+    kt = synth.to_bf16_bits((2 * rng.standard_normal((tail_len, H, D))).astype(np.float32))
+    vt = synth.to_bf16_bits(rng.standard_normal((tail_len, H, D)).astype(np.float32))
+    q = synth.to_bf16_bits(rng.standard_normal((Hq, D)).astype(np.float32))
+    ws = torch.empty(flk.attn_workspace_bytes(H, D, T + tail_len, Hq) // 4 + 1, dtype=torch.float32, device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    say(f"attention prefix T={T} tail={tail_len} H={H} Hq={Hq} sizes={sizes}")
+    flk.decode_attn_rolling(to_dev_bf16(q), g[flk.K].packed, g[flk.V].packed, T, H, to_dev_bf16(kt),
+                            to_dev_bf16(vt), scale, out, ws)
+    torch.cuda.synchronize()
+    ref = orc.decode_attn_rolling(q, o[flk.K].recons[-1], o[flk.V].recons[-1], kt, vt, scale)
+    rel = _attn_rel_err(out.float().cpu().numpy(), ref)
+    say(f"  max rel err {rel.max():.2e}")
+    assert np.all(rel <= 2e-2), rel
+
+
 def test_reconstruct_then_attend_matches_oracle():
     """The plain path the fused reader is measured against: rebuild K_hat and V_hat in BF16
     (flk_reconstruct), then attend over the BF16 cache (flk_decode_attn_rolling with no packed
