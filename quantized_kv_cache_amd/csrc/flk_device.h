@@ -56,22 +56,42 @@ struct GroupParams {
   uint32_t err;   // FLK_DEV_* bits for this group
 };
 
+// RN(x / 15), the IEEE quotient, for every binary32 x other than -0 (a range is never -0):
+// q0 = RN(x * RN(1/15)) is within an ulp of x / 15, the remainder x - 15 q0 is exact in an
+// fma, and one fma step from it rounds correctly.  Three instructions where the division
+// takes about ten; checked against the IEEE division for every finite binary32 x >= +0
+// (tests/native/hw_arith_check.hip).  An infinite x gives NaN instead of Inf (an error
+// group either way).
+__device__ __forceinline__ float div15(float x) {
+  constexpr float r = 0x1.111112p-4f;   // RN(1/15)
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, 15.0f, x);
+  return __builtin_fmaf(e, r, q0);
+}
+
 // scale32 = (max - min)/15 with IEEE division, then both rounded to FP16.
 __device__ __forceinline__ GroupParams make_params(float mn, float mx) {
   GroupParams p;
   float range = mx - mn;
-  float scale32 = range / 15.0f;
+  float scale32 = div15(range);
+  // the FP16 scale is the FP16 rounding of the binary32 quotient: without this barrier the
+  // compiler folds the conversion into the last fma (v_fma_mixlo_f16), which rounds the exact
+  // value to FP16 once and differs where the quotient is an FP16 midpoint
+  asm volatile("" : "+v"(scale32));
   uint16_t m16 = f32_to_f16_bits(mn);
   uint16_t s16 = f32_to_f16_bits(scale32);
   p.packed = uint32_t(m16) | (uint32_t(s16) << 16);
   p.m = f16_bits_to_f32(m16);
   p.s = f16_bits_to_f32(s16);
   p.rs = p.s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(p.s);   // constant group: every q is 0
-  uint32_t e = 0;
-  // Inf/NaN anywhere in the group make the extremes (or their difference) non-finite.
-  if (!(__builtin_isfinite(mn) && __builtin_isfinite(mx))) e |= 1u;
-  else if (((m16 & 0x7FFFu) >= 0x7C00u) || ((s16 & 0x7FFFu) >= 0x7C00u)) e |= 2u;
-  p.err = e;
+  // Inf/NaN anywhere in the group make the minimum or the scale Inf/NaN in FP16, and so does
+  // an FP16 overflow: an all-ones exponent in either half of the packed params (adding 1 to
+  // the exponent field carries into the half's sign bit exactly then) flags the group, which
+  // then tells the two cases apart.
+  p.err = 0;
+  const uint32_t ex = p.packed & 0x7C007C00u;
+  if (__builtin_expect(((ex + 0x04000400u) & 0x80008000u) != 0u, 0))
+    p.err = (__builtin_isfinite(mn) && __builtin_isfinite(mx)) ? 2u : 1u;
   return p;
 }
 
@@ -111,6 +131,26 @@ __device__ __forceinline__ void codes_of(const float v[N], const GroupParams& p,
   if (__builtin_expect(dev > 0.5f - 0x1p-15f, 0)) {
 #pragma unroll
     for (int e = 0; e < N; ++e) k[e] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[e] / p.s, 0.0f, 15.0f));
+  }
+}
+
+// Codes of n values, each against its own group's params (K: a group per channel), with the
+// fast path and the single fallback test of codes_of.  A group of scale 0 (its reciprocal is 0,
+// so the fast path gives code 0) keeps code 0 in the fallback too.
+template <int N>
+__device__ __forceinline__ void codes_of_each(const float v[N], const GroupParams (&p)[N], float k[N]) {
+  float y[N], dev = 0.0f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    y[e] = v[e] - p[e].m;
+    const float qc = __builtin_amdgcn_fmed3f(y[e] * p[e].rs, 0.0f, 15.0f);
+    k[e] = __builtin_rintf(qc);
+    dev = __builtin_fmaxf(dev, __builtin_fabsf(qc - k[e]));
+  }
+  if (__builtin_expect(dev > 0.5f - 0x1p-15f, 0)) {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      k[e] = p[e].s == 0.0f ? 0.0f : __builtin_rintf(__builtin_amdgcn_fmed3f(y[e] / p[e].s, 0.0f, 15.0f));
   }
 }
 

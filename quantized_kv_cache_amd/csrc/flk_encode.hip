@@ -199,13 +199,16 @@ __device__ __forceinline__ void encode_k_tile_body(const EncArgs& a, uint32_t it
     if (!empty && own.err && a.status) atomicOr(a.status, own.err);
   }
   // the octet's 8 params (lane e*8 + cc holds channel e)
-  float gm[8], gs[8], grs[8];
+  float gm[8], gs[8];
+  GroupParams g[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t w = uint32_t(__shfl(int(mine), e * 8 + cc));
     gm[e] = f16_bits_to_f32(w & 0xFFFFu);
     gs[e] = f16_bits_to_f32(w >> 16);
-    grs[e] = gs[e] == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(gs[e]);
+    g[e].m = gm[e];
+    g[e].s = gs[e];
+    g[e].rs = gs[e] == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(gs[e]);
   }
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
@@ -214,22 +217,16 @@ __device__ __forceinline__ void encode_k_tile_body(const EncArgs& a, uint32_t it
     uint16_t* rp = recon + int64_t(pos[i]) * W + ch;
     float v[8], k[8], out[8];
     unpack8(dv[i], v);
+    codes_of_each<8>(v, g, k);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      GroupParams g;
-      g.m = gm[e];
-      g.s = gs[e];
-      g.rs = grs[e];
-      k[e] = code_of(v[e], g);
-      out[e] = decode(k[e], gm[e], gs[e]);
-    }
+    for (int e = 0; e < 8; ++e) out[e] = decode(k[e], gm[e], gs[e]);
     if (RESID) {
       float r[8];
       unpack8(*reinterpret_cast<const uint4*>(rp), r);
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
     }
-    st_stream32(a.codes + ((int64_t(j) * W + ch) >> 1), pack_codes8(k));
+    st_stream32(a.codes + ((int64_t(j) * W + ch) >> 1), pack_codes8_u8(k));
     *reinterpret_cast<uint4*>(rp) = pack8(out);
   }
 }
@@ -380,18 +377,16 @@ __device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, 
     if (!ract[i]) continue;
     const int j = jbeg + rs + kKSlots * i;
     float k[8], out[8];
+    codes_of_each<8>(v[i], gp, k);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      k[e] = code_of(v[i][e], gp[e]);
-      out[e] = decode(k[e], gp[e].m, gp[e].s);
-    }
+    for (int e = 0; e < 8; ++e) out[e] = decode(k[e], gp[e].m, gp[e].s);
     if (RESID) {
       float r[8];
       unpack8(rv[i], r);
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
     }
-    st_stream32(codes + ((int64_t(j) * W + ch) >> 1), pack_codes8(k));
+    st_stream32(codes + ((int64_t(j) * W + ch) >> 1), pack_codes8_u8(k));
     *reinterpret_cast<uint4*>(recon + roff[i]) = pack8(out);
   }
 }
@@ -491,18 +486,16 @@ __global__ __launch_bounds__(kThreads) void encode_v_kernel(
       if (p.err && status) atomicOr(status, p.err);
     }
     float k[8], out[8];
+    codes_of<8>(v[u], p, k);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      k[e] = code_of(v[u][e], p);
-      out[e] = decode(k[e], p.m, p.s);
-    }
+    for (int e = 0; e < 8; ++e) out[e] = decode(k[e], p.m, p.s);
     if (RESID) {
       float r[8];
       unpack8(rv[u], r);
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
     }
-    st_stream32(codes + ((it * D + w * 8) >> 1), pack_codes8(k));
+    st_stream32(codes + ((it * D + w * 8) >> 1), pack_codes8_u8(k));
     *reinterpret_cast<uint4*>(recon + roff[u]) = pack8(out);
   }
 }

@@ -1,5 +1,5 @@
-// hw_arith_check.hip -- exhaustive checks of two gfx950 arithmetic facts the exact K decode of the
-// decode-attention scores kernel relies on.  Test infrastructure: built by build(), run by
+// hw_arith_check.hip -- exhaustive checks of gfx950 arithmetic facts the kernels rely on: two for
+// the exact K decode of the decode-attention scores kernel, one for the encoders.  Test infrastructure: built by build(), run by
 // tests/test_gpu_hw_arith.py; the library does not use this file.
 //
 // 1. v_dot2_f32_bf16 (a, b) . (1, 1) + 0, rounded to BF16 by v_cvt_pk_bf16_f32, equals the BF16
@@ -11,9 +11,13 @@
 //    denormal code * 2^-24) times s * 2^24 in binary32 plus a binary16 minimum m equals
 //    fma(code, s, m) in binary32, for every finite non-negative binary16 scale s, every code
 //    and 512 minima (zeros, denormals, both signs, the extremes).
+// 3. The encoders' three-instruction RN(x / 15) (flk::div15) equals the IEEE division for every
+//    finite binary32 x >= +0, denormals included.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cstdio>
+
+#include "../../quantized_kv_cache_amd/csrc/flk_device.h"
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -72,6 +76,23 @@ __global__ void check_fma_mix(const uint16_t* ms, unsigned long long* cnt) {
   if (bad) atomicAdd(&cnt[4], bad);
 }
 
+// grid-stride over every finite binary32 x >= +0: div15 (the params' RN(x / 15)) against the
+// IEEE division
+__global__ void check_div15(unsigned long long* cnt) {
+  unsigned long long bad = 0, tested = 0;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < 0x7F800000u; u += stride) {
+    float x = __uint_as_float(u);
+    asm volatile("" : "+v"(x));                 // a run-time value
+    const float q1 = flk::div15(x);
+    const float q2 = x / 15.0f;
+    ++tested;
+    if (__float_as_uint(q1) != __float_as_uint(q2)) ++bad;
+  }
+  atomicAdd(&cnt[5], tested);
+  if (bad) atomicAdd(&cnt[6], bad);
+}
+
 int main() {
   uint16_t hm[512];
   uint32_t x = 12345u;
@@ -87,19 +108,21 @@ int main() {
   unsigned long long* cnt = nullptr;
   const uint32_t one2 = 0x3F803F80u;
   if (hipMalloc(&ones, 4) != hipSuccess || hipMalloc(&ms, sizeof(hm)) != hipSuccess ||
-      hipMalloc(&cnt, 8 * 5) != hipSuccess || hipMemcpy(ones, &one2, 4, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(ms, hm, sizeof(hm), hipMemcpyHostToDevice) != hipSuccess || hipMemset(cnt, 0, 8 * 5) != hipSuccess) {
+      hipMalloc(&cnt, 8 * 7) != hipSuccess || hipMemcpy(ones, &one2, 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ms, hm, sizeof(hm), hipMemcpyHostToDevice) != hipSuccess || hipMemset(cnt, 0, 8 * 7) != hipSuccess) {
     printf("setup failed\n");
     return 2;
   }
   hipLaunchKernelGGL(check_dot2, dim3(65536), dim3(256), 0, 0, ones, cnt);
   hipLaunchKernelGGL(check_fma_mix, dim3(0x7C00), dim3(512), 0, 0, ms, cnt);
-  unsigned long long c[5] = {0, 0, 0, 0, 0};
-  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(c, cnt, 8 * 5, hipMemcpyDeviceToHost) != hipSuccess) {
+  hipLaunchKernelGGL(check_div15, dim3(65536), dim3(256), 0, 0, cnt);
+  unsigned long long c[7] = {0, 0, 0, 0, 0, 0, 0};
+  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(c, cnt, 8 * 7, hipMemcpyDeviceToHost) != hipSuccess) {
     printf("run failed\n");
     return 2;
   }
   printf("dot2_pairs %llu dot2_bf16_mismatch %llu dot2_inexact_below_16 %llu\n", c[0], c[1], c[2]);
   printf("fma_mix_cases %llu fma_mix_mismatch %llu\n", c[3], c[4]);
-  return (c[1] == 0 && c[4] == 0) ? 0 : 1;
+  printf("div15_cases %llu div15_mismatch %llu\n", c[5], c[6]);
+  return (c[1] == 0 && c[4] == 0 && c[6] == 0) ? 0 : 1;
 }

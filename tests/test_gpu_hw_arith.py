@@ -1,11 +1,13 @@
-"""The two gfx950 arithmetic facts the exact K decode of the decode-attention scores kernel
-rests on, checked exhaustively on the GPU by tests/native/hw_arith_check (built by build()):
+"""The gfx950 arithmetic facts the exact K decode of the decode-attention scores kernel and the
+encoders rest on, checked exhaustively on the GPU by tests/native/hw_arith_check (built by build()):
 
 * a BF16 pair summed by v_dot2_f32_bf16 against (1, 1), then rounded to BF16, equals the BF16
   rounding of the v_add_f32 sum, for every pair of +0 / finite normal BF16 values;
 * v_fma_mix_f32 with the code as a binary16 denormal times s * 2^24 plus the binary16 minimum
   equals fma(code, s, m), for every finite non-negative binary16 scale, every code and 512
-  minima.
+  minima;
+* the encoders' three-instruction RN(x / 15) equals the IEEE division for every finite
+  binary32 x >= +0.
 """
 import os
 import subprocess
@@ -34,3 +36,7 @@ def test_hw_arith_facts():
     assert vals["dot2_bf16_mismatch"] == 0
     assert vals["fma_mix_cases"] == 0x7C00 * 512 * 16
     assert vals["fma_mix_mismatch"] == 0
+    # every finite binary32 x >= +0
+    assert vals["div15_cases"] == 0x7F800000
+    assert vals["div15_mismatch"] == 0
+
