@@ -36,6 +36,7 @@ static size_t attn_ws_bytes(int32_t splits, int32_t T, int32_t Hq) {
   return size_t(splits) * size_t(Hq) * (2 + kAttnD + 1) * sizeof(float) +
          size_t(Hq) * ((size_t(T) + 3) & ~size_t(3)) * sizeof(float);
 }
+// (Sized with the one-pass reader's split count, which the two-pass reader's never exceeds.)
 size_t attn_workspace_need(int32_t T, int32_t tail_len, int32_t H, int32_t Hq) {
   return attn_ws_bytes(n_splits(attn_tiles(T, tail_len), H), T + tail_len, Hq);
 }
@@ -470,8 +471,12 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
                               size_t ws_bytes, hipStream_t stream) {
   if (ws == nullptr || ws_bytes < attn_workspace_need(T, tail_len, H, Hq)) return hipErrorInvalidValue;
   const int32_t tiles = attn_tiles(T, tail_len);
-  const int32_t wph = waves_per_head(tiles, H);
-  const int32_t splits = n_splits(tiles, H);
+  // INT4 chains with packed tokens take the two-pass reader (the score-writing call only
+  // without a tail, whose scores rows count the packed positions alone)
+  const bool two_pass = FMT == 0 && T > 0 && (!SC || tail_len == 0);
+  const int32_t nw = two_pass ? kSplitAttnWaves : kAttnWaves;
+  const int32_t wph = waves_per_head(tiles, H, nw);
+  const int32_t splits = n_splits(tiles, H, nw);
   const int32_t G = Hq / H;
   float* ws_ml = static_cast<float*>(ws);
   float* ws_o = ws_ml + size_t(splits) * Hq * 2;
@@ -481,7 +486,7 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
   int nl = kc.n_loops > vc.n_loops ? kc.n_loops : vc.n_loops;
   if (nl < 1) nl = 1;                              // no packed tokens: only the tail's tiles run
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
-  if (FMT == 0 && T > 0 && (!SC || tail_len == 0)) {
+  if (two_pass) {
     // INT4 chains: the scores of every position (packed, then the BF16 tail), then PV straight
     // from the V codes (the tail's V as stored)
     float* block_max = ws_o + size_t(splits) * Hq * kAttnD;

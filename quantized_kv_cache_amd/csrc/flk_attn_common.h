@@ -19,6 +19,12 @@ constexpr int kLdsRow = kAttnD + 8;         // BF16 per LDS row: 272 bytes keep 
 #define FLK_ATTN_WAVES 8192
 #endif
 constexpr int kAttnWaves = FLK_ATTN_WAVES;    // aim for about this many waves per launch
+// The two-pass reader's launches: one round of 4 waves per SIMD on 256 CUs (4096 waves) beats
+// two rounds (8192) by about 3 %; the one-pass reader keeps 8192 (4096 is 6 % slower there).
+#ifndef FLK_SPLIT_ATTN_WAVES
+#define FLK_SPLIT_ATTN_WAVES 4096
+#endif
+constexpr int kSplitAttnWaves = FLK_SPLIT_ATTN_WAVES;
 #ifndef FLK_ATTN_OCC
 #define FLK_ATTN_OCC 3   // waves per SIMD the register budget must allow
 #endif
@@ -33,11 +39,14 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // adding blocks.  A block
 // of 4 waves writes one partial per query head.  `tiles` counts the packed tiles and the
 // tiles of a BF16 tail together.
-inline int32_t waves_per_head(int32_t tiles, int32_t H) {
-  const int32_t cap = kAttnWaves / H > 0 ? kAttnWaves / H : 1;
+inline int32_t waves_per_head(int32_t tiles, int32_t H, int32_t waves = kAttnWaves) {
+  const int32_t cap = waves / H > 0 ? waves / H : 1;
   return tiles < cap ? (tiles > 0 ? tiles : 1) : cap;
 }
-inline int32_t n_splits(int32_t tiles, int32_t H) { return (waves_per_head(tiles, H) + 3) / 4; }
+inline int32_t n_splits(int32_t tiles, int32_t H, int32_t waves = kAttnWaves) {
+  return (waves_per_head(tiles, H, waves) + 3) / 4;
+}
+static_assert(kSplitAttnWaves <= kAttnWaves, "workspace sizes count the larger split count");
 
 inline int32_t attn_tiles(int32_t T, int32_t tail_len) {
   return (T + kGroup - 1) / kGroup + (tail_len + kGroup - 1) / kGroup;
