@@ -1147,9 +1147,24 @@ def summarize_pmc(dirs):
     lines = [f"source_sha256 {source_digest()}",
              f"copy_probe bytes {COPY_PROBE_BYTES} fetch_kib {fetch_copy:.1f} write_kib {write_copy:.1f} "
              f"fetch_scale {fs:.4f} write_scale {ws_:.4f} dispatches {nf}/{nw}"]
+    # the two-pass decode attention, when the run had the attention leg: pass 1 reads the K
+    # chain (and the loops' rows) and writes the scores rows, pass 2 reads the V chain, the rows
+    # and the scores; the algorithmic bytes count the chains alone, so the scores' round trip
+    # (Hq * T * 4 bytes written, then read) shows in the ratio
+    if any(c == "FETCH_SIZE" and k.startswith("attn_scores_kernel<4") for (c, k) in vals):
+        wa = synth.WORKLOADS[5]
+        sa = synth.active_sets(wa, wa.T)
+        rows_b = sum(4 * len(r) for r in sa if r is not None)
+        chain_b = {kind: sum(flk.codes_bytes(kind, wa.H, wa.D, n) + flk.params_bytes(kind, wa.H, wa.D, n)
+                             for n in (wa.T if r is None else len(r) for r in sa)) + rows_b
+                   for kind in (flk.K, flk.V)}
+        for sym, a in (("attn_scores_kernel<4, false>", chain_b[flk.K]), ("attn_pv_kernel<4>", chain_b[flk.V])):
+            algo[sym] = [a]
     for sym, bs in algo.items():
         f, n1 = mean("FETCH_SIZE", lambda k, s=sym: k == s)
         wr, n2 = mean("WRITE_SIZE", lambda k, s=sym: k == s)
+        if n1 == 0 and n2 == 0:
+            continue
         traffic = (f * fs + wr * ws_) * 1024
         a = sum(bs) / len(bs)
         lines.append(f"kernel {sym} | dispatches {n1}/{n2} | fetch_kib {f:.1f} | write_kib {wr:.1f} | "
@@ -1197,12 +1212,17 @@ def summarize_trace(trace_dir, warmup, steps, isolated=10):
     return "\n".join(lines)
 
 
-def summarize_stats(stats_csv, top=40):
+def summarize_stats(stats_csv, top=40, match=None):
     """rocprofv3 --stats kernel statistics (kernel_stats.csv) as a short table: per kernel the
-    calls, mean / min / max duration (us) and share of the summed kernel time."""
+    calls, mean / min / max duration (us) and share of the summed kernel time; the `top`
+    kernels by summed time, or every kernel whose short name matches the regex `match`."""
     import csv
+    import re
     rows = list(csv.DictReader(open(stats_csv)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    if match:
+        rows = [r for r in rows if re.search(match, _short_name(r["Name"]))]
+        top = len(rows)
     lines = [f"{'kernel':52s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share_%':>8s}"]
     for r in rows[:top]:
         lines.append(f"{_short_name(r['Name'])[:52]:52s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
@@ -1318,6 +1338,8 @@ def main():
                          "(no GPU)")
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="print a rocprofv3 kernel_stats.csv as a short table and exit")
+    ap.add_argument("--stats-match", metavar="REGEX",
+                    help="with --summarize-stats: every kernel whose name matches, instead of the top 40")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel durations (all calls, timed region) from a rocprofv3 kernel trace "
                          "of a run with the same --warmup/--steps, and exit (no GPU)")
@@ -1329,7 +1351,7 @@ def main():
         print(summarize_counters(args.summarize_counters))
         return
     if args.summarize_stats:
-        print(summarize_stats(args.summarize_stats))
+        print(summarize_stats(args.summarize_stats, match=args.stats_match))
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.warmup, args.steps))
