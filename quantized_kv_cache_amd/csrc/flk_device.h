@@ -316,11 +316,17 @@ template <int AUX = 0>
 __device__ __forceinline__ void buf_st32(uint32_t w, BufRsrc r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(w, r, int(voff), soffset(soff), AUX);
 }
+// A store of more than 64 bits reads its data VGPRs after it issues, so a VALU write of them
+// needs a wait state in between.  The compiler inserts it only for a store whose scalar offset
+// is not a register; on gfx950 a store with an SGPR offset showed the same hazard (the last
+// four lanes of each 16-lane row stored the overwritten value of data dwords whose registers
+// the next instruction rewrote).  So the row offset joins the lane offset and the scalar
+// offset is the constant 0, which makes the compiler keep the wait state.
 template <int AUX = 0>
 __device__ __forceinline__ void buf_st128(const uint4& w, BufRsrc r, uint32_t voff, uint32_t soff) {
   typedef uint32_t v4 __attribute__((ext_vector_type(4)));
   const v4 v = {w.x, w.y, w.z, w.w};
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(voff), soffset(soff), AUX);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, int(voff + soff), 0, AUX);
 }
 __device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 template <int AUX = 0>

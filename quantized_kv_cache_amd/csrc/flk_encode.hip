@@ -251,144 +251,195 @@ __global__ __launch_bounds__(kThreads) void encode_k_tile_kernel(EncArgs a) {
 // of a 128-channel (64 for compact loops) strip of the flattened H*D channel axis.  With
 // tile groups (page-local, a.ktile) compact loops run encode_k_tile_body instead.
 // Thread (rs, cc): 8 channels (16 bytes) of chunk cc, rows rs, rs + slots, ... (4 rows each
-// at 128 channels, 2 at 64).  Extremes: in registers over its rows, across the row slots of a
-// wave with lane shuffles, across the 4 waves through LDS; one thread per channel then derives
-// the params.
+// at 128 channels, 2 at 64); the lanes of one row slot cover the strip of one row, so every
+// load and store instruction covers whole rows of the strip.  Extremes: in registers over the
+// thread's rows, then through LDS, where one thread per channel reduces the row slots' partial
+// extremes and derives the channel's params, which every thread reads back.
+// A band whose 64 rows and strip channels are all present (every band but a ragged last one,
+// every strip when H*D is a multiple of the strip width) and, for a compact loop, whose rows
+// all lie in [0, T) runs without per-row predicates -- buffer accesses with scalar row offsets
+// and no selects; other bands take the predicated form.
 // ---------------------------------------------------------------------------------------
-template <bool RESID, bool SPARSE>
-__device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, uint32_t band_) {
-  constexpr int kKCW = k_block_channels<SPARSE>();  // channels per block
-  constexpr int kKChunks = kKCW / 8;                // 8-channel chunks per block row
-  constexpr int kKSlots = kThreads / kKChunks;      // row slots per block
-  constexpr int kKRows = kGroup / kKSlots;          // rows per thread
-  const uint16_t* __restrict__ x = a.x;
-  const int32_t* __restrict__ rows = a.rows;
-  uint16_t* __restrict__ recon = a.recon;
-  uint8_t* __restrict__ codes = a.codes;
-  uint32_t* __restrict__ params = a.params;
-  int32_t* __restrict__ tile_start = a.tile_start;
-  uint32_t* __restrict__ status = a.status;
-  const int32_t n = a.n, T = a.T, W = a.W, pos0 = a.pos0;
-  __shared__ float s_min[4][kKCW];
-  __shared__ float s_max[4][kKCW];
-  __shared__ float s_m[kKCW], s_s[kKCW], s_rs[kKCW];
+template <bool SPARSE>
+struct KShape {
+  static constexpr int kCW = k_block_channels<SPARSE>();  // channels per block
+  static constexpr int kChunks = kCW / 8;                 // 16-byte chunks per block row
+  static constexpr int kSlots = kThreads / kChunks;       // row slots per block
+  static constexpr int kRows = kGroup / kSlots;           // rows per thread
+};
 
+template <bool SPARSE>
+struct KShared {
+  float red[2][KShape<SPARSE>::kSlots][KShape<SPARSE>::kCW];   // partial minima, maxima
+  float par[3][KShape<SPARSE>::kCW];                            // m, s, ~1/s per channel
+};
+
+// pos[i]: the X_hat row of the thread's i-th row (compact loops; -1 = not present).
+template <bool RESID, bool SPARSE, bool FULL>
+__device__ __forceinline__ void encode_k_band(const EncArgs& a, uint32_t strip, int32_t band,
+                                              const int32_t (&pos)[KShape<SPARSE>::kRows],
+                                              KShared<SPARSE>& sh) {
+  using S = KShape<SPARSE>;
   const int tid = threadIdx.x;
-  const int cc = tid % kKChunks;
-  const int rs = tid / kKChunks;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int band = int(band_);
-  const int chunk = int(strip) * kKChunks + cc;
-  const bool cact = chunk < (W >> 3);
-  const int64_t ch = int64_t(chunk) * 8;
-  // the band's compact rows [jbeg, jend)
+  const int cc = tid % S::kChunks;
+  const int rs = tid / S::kChunks;
+  const int32_t n = a.n, T = a.T, W = a.W;
+  const int32_t chunk = int32_t(strip) * S::kChunks + cc;
+  const bool cact = FULL || chunk < (W >> 3);
+  const uint32_t ch = uint32_t(chunk) * 8u;
   const int32_t jbeg = band * kGroup, jend = min(n, jbeg + kGroup);
+  const uint32_t rowb = uint32_t(W) * 2u, crow = uint32_t(W) >> 1;
+  const BufRsrc xrs = make_buf(a.x, uint32_t(n) * rowb);
+  const BufRsrc rrs = make_buf(a.recon, uint32_t(T) * rowb);
+  const BufRsrc crs = make_buf(a.codes, uint32_t(n) * crow);
+  // row j = jbeg + rs + kSlots*i: a lane part (rs, chunk) and a scalar part (jbeg + kSlots*i)
+  const uint32_t xl = uint32_t(rs) * rowb + ch * 2u;
+  const uint32_t cl = uint32_t(rs) * crow + ch / 2u;
+  auto xsoff = [&](int i) { return uint32_t(jbeg + S::kSlots * i) * rowb; };
+  auto rl = [&](int i) { return SPARSE ? uint32_t(max(pos[i], 0)) * rowb + ch * 2u : xl; };
+  auto rsoff = [&](int i) { return SPARSE ? 0u : xsoff(i); };
 
-  float v[kKRows][8];
-  uint4 rv[kKRows];
-  int64_t roff[kKRows];
-  bool ract[kKRows];
-  bool bad_row = false;
+  bool ract[S::kRows];
 #pragma unroll
-  for (int i = 0; i < kKRows; ++i) {
-    const int j = jbeg + rs + kKSlots * i;
-    ract[i] = cact && j < jend;
-    rv[i] = make_uint4(0, 0, 0, 0);
-    roff[i] = 0;
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (ract[i]) {
-      const int32_t p = SPARSE ? rows[j] - pos0 : j;
-      if (SPARSE && uint32_t(p) >= uint32_t(T)) {   // malformed map: never address outside recon
-        ract[i] = false;
-        bad_row = true;
-      } else {
-        xv = ld_stream(x + int64_t(j) * W + ch);
-        roff[i] = int64_t(p) * W + ch;
-        if (RESID) rv[i] = *reinterpret_cast<const uint4*>(recon + roff[i]);
+  for (int i = 0; i < S::kRows; ++i)
+    ract[i] = FULL || (cact && jbeg + rs + S::kSlots * i < jend && (!SPARSE || pos[i] >= 0));
+
+  uint4 xw[S::kRows], rw[S::kRows];
+#pragma unroll
+  for (int i = 0; i < S::kRows; ++i) {
+    if (FULL) {
+      xw[i] = buf_ld128<kCacheStream>(xrs, xl, xsoff(i));
+      if (RESID) rw[i] = buf_ld128(rrs, rl(i), rsoff(i));
+    } else {
+      xw[i] = rw[i] = make_uint4(0, 0, 0, 0);
+      if (ract[i]) {
+        xw[i] = buf_ld128<kCacheStream>(xrs, xl, xsoff(i));
+        if (RESID) rw[i] = buf_ld128(rrs, rl(i), rsoff(i));
       }
     }
-    unpack8(xv, v[i]);
   }
-  if (SPARSE && bad_row && status) atomicOr(status, kDevRows);
-  if (SPARSE && strip == 0 && cc == 0) {
+  float v[S::kRows][8], r[S::kRows][8];
 #pragma unroll
-    for (int i = 0; i < kKRows; ++i) {
-      const int j = jbeg + rs + kKSlots * i;
-      if (j < jend) write_tile_index(rows, n, T, j, tile_start, pos0, a.row0);
-    }
-  }
-  if (RESID) {
+  for (int i = 0; i < S::kRows; ++i) {
+    unpack8(xw[i], v[i]);
+    if (RESID) {
+      unpack8(rw[i], r[i]);
 #pragma unroll
-    for (int i = 0; i < kKRows; ++i) {
-      float r[8];
-      unpack8(rv[i], r);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = round_bf16(v[i][e] - r[e]);
+      for (int e = 0; e < 8; ++e) v[i][e] = round_bf16(v[i][e] - r[i][e]);
     }
   }
 
+  // the thread's extremes per channel, then one thread per channel over the row slots
   float mn[8], mx[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = ract[0] ? v[0][e] : __builtin_inff();
+    mx[e] = ract[0] ? v[0][e] : -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < kKRows; ++i)
-    if (ract[i]) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { mn[e] = tmin(mn[e], v[i][e]); mx[e] = tmax(mx[e], v[i][e]); }
+    for (int i = 1; i < S::kRows; ++i) {
+      mn[e] = tmin(mn[e], ract[i] ? v[i][e] : __builtin_inff());
+      mx[e] = tmax(mx[e], ract[i] ? v[i][e] : -__builtin_inff());
     }
+  }
+  float4* dmn = reinterpret_cast<float4*>(&sh.red[0][rs][cc * 8]);
+  float4* dmx = reinterpret_cast<float4*>(&sh.red[1][rs][cc * 8]);
+  dmn[0] = make_float4(mn[0], mn[1], mn[2], mn[3]);
+  dmn[1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
+  dmx[0] = make_float4(mx[0], mx[1], mx[2], mx[3]);
+  dmx[1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
+  __syncthreads();
+  if (tid < S::kCW) {
+    float lo = sh.red[0][0][tid], hi = sh.red[1][0][tid];
 #pragma unroll
-  for (int off = kKChunks; off < 64; off *= 2) {
+    for (int s = 1; s < S::kSlots; ++s) {
+      lo = tmin(lo, sh.red[0][s][tid]);
+      hi = tmax(hi, sh.red[1][s][tid]);
+    }
+    const int32_t chan = int32_t(strip) * S::kCW + tid;
+    const GroupParams p = make_params(lo, hi);
+    sh.par[0][tid] = p.m;
+    sh.par[1][tid] = p.s;
+    sh.par[2][tid] = p.rs;
+    if (FULL || chan < W) {
+      st_stream32(a.params + int64_t(band) * W + chan, p.packed);
+      if (p.err && a.status) atomicOr(a.status, p.err);
+    }
+  }
+  __syncthreads();
+  GroupParams gp[8];
+  {
+    const float4* pm = reinterpret_cast<const float4*>(&sh.par[0][cc * 8]);
+    const float4* ps = reinterpret_cast<const float4*>(&sh.par[1][cc * 8]);
+    const float4* pr = reinterpret_cast<const float4*>(&sh.par[2][cc * 8]);
+    const float4 m0 = pm[0], m1 = pm[1], s0 = ps[0], s1 = ps[1], r0 = pr[0], r1 = pr[1];
+    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const float rr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      mn[e] = tmin(mn[e], __shfl_xor(mn[e], off));
-      mx[e] = tmax(mx[e], __shfl_xor(mx[e], off));
+      gp[e].m = mm[e];
+      gp[e].s = ss[e];
+      gp[e].rs = rr[e];
     }
   }
-  if (lane < kKChunks) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { s_min[wave][cc * 8 + e] = mn[e]; s_max[wave][cc * 8 + e] = mx[e]; }
-  }
-  __syncthreads();
-  if (tid < kKCW) {
-    const float a = tmin(tmin(s_min[0][tid], s_min[1][tid]), tmin(s_min[2][tid], s_min[3][tid]));
-    const float b = tmax(tmax(s_max[0][tid], s_max[1][tid]), tmax(s_max[2][tid], s_max[3][tid]));
-    const int64_t chan = int64_t(strip) * kKCW + tid;
-    GroupParams p = make_params(a, b);
-    s_m[tid] = p.m;
-    s_s[tid] = p.s;
-    s_rs[tid] = p.rs;
-    if (chan < W) {
-      st_stream32(params + int64_t(band) * W + chan, p.packed);
-      if (p.err && status) atomicOr(status, p.err);
-    }
-  }
-  __syncthreads();
-
-  GroupParams gp[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    gp[e].m = s_m[cc * 8 + e];
-    gp[e].s = s_s[cc * 8 + e];
-    gp[e].rs = s_rs[cc * 8 + e];
-  }
-#pragma unroll
-  for (int i = 0; i < kKRows; ++i) {
-    if (!ract[i]) continue;
-    const int j = jbeg + rs + kKSlots * i;
+  for (int i = 0; i < S::kRows; ++i) {
+    if (!FULL && !ract[i]) continue;
     float k[8], out[8];
     codes_of_each<8>(v[i], gp, k);
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = decode(k[e], gp[e].m, gp[e].s);
     if (RESID) {
-      float r[8];
-      unpack8(rv[i], r);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = r[e] + round_bf16(out[e]);
+      for (int e = 0; e < 8; ++e) out[e] = r[i][e] + round_bf16(out[e]);
     }
-    st_stream32(codes + ((int64_t(j) * W + ch) >> 1), pack_codes8_u8(k));
-    *reinterpret_cast<uint4*>(recon + roff[i]) = pack8(out);
+    buf_st32<kCacheStream>(pack_codes8_u8(k), crs, cl, uint32_t(jbeg + S::kSlots * i) * crow);
+    buf_st128(pack8(out), rrs, rl(i), rsoff(i));
   }
+}
+
+template <bool RESID, bool SPARSE>
+__device__ __forceinline__ void encode_k_body(const EncArgs& a, uint32_t strip, uint32_t band_) {
+  using S = KShape<SPARSE>;
+  __shared__ __align__(16) KShared<SPARSE> sh;
+  const int tid = threadIdx.x;
+  const int cc = tid % S::kChunks;
+  const int rs = tid / S::kChunks;
+  const int32_t n = a.n, T = a.T, W = a.W;
+  const int32_t band = int32_t(band_);
+  const int32_t jbeg = band * kGroup, jend = min(n, jbeg + kGroup);
+  const bool cact = int32_t(strip) * S::kChunks + cc < (W >> 3);
+  bool full = jend - jbeg == kGroup && (int32_t(strip) + 1) * S::kCW <= W;
+  int32_t pos[S::kRows];
+  if (SPARSE) {
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < S::kRows; ++i) {
+      const int32_t j = jbeg + rs + S::kSlots * i;
+      pos[i] = -1;
+      if (cact && j < jend) {
+        const int32_t p = a.rows[j] - a.pos0;
+        if (uint32_t(p) >= uint32_t(T)) bad = true;       // malformed map: never address outside recon
+        else pos[i] = p;
+      }
+    }
+    if (__syncthreads_or(bad)) {
+      full = false;
+      if (bad && a.status) atomicOr(a.status, kDevRows);
+    }
+    if (strip == 0 && cc == 0) {
+#pragma unroll
+      for (int i = 0; i < S::kRows; ++i) {
+        const int32_t j = jbeg + rs + S::kSlots * i;
+        if (j < jend) write_tile_index(a.rows, n, T, j, a.tile_start, a.pos0, a.row0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::kRows; ++i) pos[i] = jbeg + rs + S::kSlots * i;
+  }
+  if (full) encode_k_band<RESID, SPARSE, true>(a, strip, band, pos, sh);
+  else encode_k_band<RESID, SPARSE, false>(a, strip, band, pos, sh);
 }
 
 // Blocks run strip-fastest in XCD order: the neighbouring strips of a band write the two halves
