@@ -10,8 +10,11 @@ final depth.  By default the single calls run with the K chain and the V chain o
 so one chain's next loop overlaps the other's ramp and drain); --mode batched issues one
 batched call per loop covering both tensors (flk_encode_base_batch, flk_encode_residual_batch
 x 3, flk_reconstruct_batch) on one stream, and --mode serial the single calls on one stream.
-After the timed region every call is also timed alone (one stream, nothing overlapping) and
-reported per call, with the dominant kernel's roofline at that isolated duration.  `value` = algorithmic bytes of the step (each input read once, each output
+The timed region holds the steps alone: events around single launches cost about 9 us per step
+(each event record drains its stream and writes back the L2), so the per-launch events of the
+overlapped step run on min(10, steps) further steps after it.  Then every call is also timed
+alone (one stream, nothing overlapping) and reported per call, with the dominant kernel's
+roofline at that isolated duration.  `value` = algorithmic bytes of the step (each input read once, each output
 written once) / wall time per step, inputs already resident in HBM.  Steps rotate over
 several independent buffer sets (> 1 GB in total) so the 256 MB MALL holds no timed data.
 
@@ -263,6 +266,7 @@ def isolated_calls(chain_sets, reps):
 
 
 ISO_SPIN_CYCLES = 5_000_000       # about 2 ms at the shader clock: longer than the host's issue of the launches
+OVERLAP_STEPS = 10                # steps after the timed region that carry per-launch events
 
 
 # ----------------------------------------------------------------------------- cpu baseline
@@ -1188,8 +1192,9 @@ def summarize_trace(trace_dir, warmup, steps, isolated=10):
     """Per-kernel durations from a rocprofv3 kernel trace of `bench.py` (default mode): over all
     calls, and for the headline's kernels over its timed region and over its isolated launches.
     A headline kernel runs c times per step and the headline's launches come first in dispatch
-    order (warmup steps, timed steps, then `isolated` launches of each call alone), so its timed
-    calls are launches [c*warmup, c*(warmup+steps)) and its isolated ones the next c*isolated."""
+    order (warmup steps, timed steps, min(10, steps) steps with per-launch events, then
+    `isolated` launches of each call alone), so its timed calls are launches
+    [c*warmup, c*(warmup+steps)) and its isolated ones the c*isolated after the evented steps."""
     import csv
     import glob
     paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
@@ -1205,9 +1210,10 @@ def summarize_trace(trace_dir, warmup, steps, isolated=10):
         d = np.array([x for _, x in v])
         timed = iso = ""
         c = head.get(name, 0)
-        if c and len(d) >= c * (warmup + steps + isolated):
+        ov = min(OVERLAP_STEPS, steps)
+        if c and len(d) >= c * (warmup + steps + ov + isolated):
             timed = f"{d[warmup * c:(warmup + steps) * c].mean():13.2f}"
-            iso = f"{d[(warmup + steps) * c:(warmup + steps + isolated) * c].mean():16.2f}"
+            iso = f"{d[(warmup + steps + ov) * c:(warmup + steps + ov + isolated) * c].mean():16.2f}"
         lines.append(f"{name[:52]:52s} {len(d):6d} {d.mean():11.2f} {timed:>13s} {iso:>16s}")
     return "\n".join(lines)
 
@@ -1412,18 +1418,25 @@ def main():
     dom_idx = [i for i, sy in enumerate(symbols) if sy == dominant]
     log("warmup per-call us: " + ", ".join(f"{sy}={t / counted * 1e3:.1f}" for sy, t in zip(symbols, times)))
 
-    # timed region: exactly `steps` steps; events only around the dominant kernel's launches,
-    # recorded on the stream that launches it
-    dom_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               if i in dom_idx else None for i in range(n_calls)] for _ in range(args.steps)]
+    # timed region: exactly `steps` steps, nothing else on the streams
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        chain_sets[k % args.rotate].run(streams, dom_ev[k])
+        chain_sets[k % args.rotate].run(streams)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the dominant kernel inside the overlapped step: min(10, steps) further steps, back to back
+    # as in the timed region, with events around that kernel's launches on the stream that
+    # launches it (kept out of the timed region: each event pair drains its stream)
+    n_ov = min(OVERLAP_STEPS, args.steps)
+    dom_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               if i in dom_idx else None for i in range(n_calls)] for _ in range(n_ov)]
+    for k in range(n_ov):
+        chain_sets[(args.steps + k) % args.rotate].run(streams, dom_ev[k])
+    torch.cuda.synchronize()
 
     # each call alone: one stream, events around every call, nothing overlapping
     iso_us = isolated_calls(chain_sets, 10)
@@ -1431,17 +1444,18 @@ def main():
                      "bytes": int(b), "us": round(float(t), 2), "gbs": round(b / t / 1e3, 1)}
                     for (kind, name, b), sy, t in zip(per_call, symbols, iso_us)]
 
-    # the timed region's event durations of the warmup's dominant kernel: with two streams they
+    # the overlapped steps' event durations of the warmup's dominant kernel: with two streams they
     # include waiting for compute units the other chain holds, so they are reported apart
-    dom_ms = [dom_ev[k][i][0].elapsed_time(dom_ev[k][i][1]) for k in range(args.steps) for i in dom_idx]
+    dom_ms = [dom_ev[k][i][0].elapsed_time(dom_ev[k][i][1]) for k in range(n_ov) for i in dom_idx]
     dom_bytes = float(np.mean([per_call[i][2] for i in dom_idx]))
     dom_avg_ms = float(np.mean(dom_ms))
     prof_timed, _ = read_trace(dominant)
     roofline_overlapped = {"kernel": dominant, "launch_avg_us": round(dom_avg_ms * 1e3, 2),
                            "achieved": round(dom_bytes / (dom_avg_ms * 1e-3) / 1e9, 1),
                            "frac": round(dom_bytes / (dom_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "note": "HIP events in the timed region, on the kernel's stream, overlapping the "
-                                   "other chain",
+                           "note": f"HIP events on the kernel's stream around its launches in {n_ov} steps run "
+                                   "right after the timed region as it runs (two streams, overlapping the other "
+                                   "chain)",
                            "profile_launch_avg_us": prof_timed}
 
     # the roofline's kernel: the largest summed time per step with every call timed alone (one

@@ -398,19 +398,23 @@ __device__ __forceinline__ void st_stream32(void* p, uint32_t w) {
 // A window of an appended stream covers positions [pos0, pos0 + T): rows hold absolute
 // positions, tile t of the window is entry t of tile_start (the caller offsets it), and the
 // stream already holds row0 rows before the window, so every entry is offset by row0.
-__device__ __forceinline__ void write_tile_index(const int32_t* __restrict__ rows, int32_t n,
-                                                 int32_t T, int32_t j,
-                                                 int32_t* __restrict__ tile_start,
-                                                 int32_t pos0, int32_t row0) {
+// The same from the window positions p = rows[j] - pos0 and q = rows[j-1] - pos0 (q = -1 for
+// j == 0), for a caller that already holds them.
+__device__ __forceinline__ void write_tile_index_pq(int32_t p, int32_t q, int32_t n, int32_t T, int32_t j,
+                                                    int32_t* __restrict__ tile_start, int32_t row0) {
   const int32_t ntiles = (T + kGroup - 1) / kGroup;
-  const int32_t p = rows[j] - pos0;
-  const int32_t q = j > 0 ? rows[j - 1] - pos0 : -1;
   if (p < 0 || p >= T) return;
   const int32_t t_first = q < 0 ? 0 : min(q / kGroup + 1, ntiles + 1);
   const int32_t t_last = p / kGroup;
   for (int32_t t = t_first; t <= t_last; ++t) tile_start[t] = row0 + j;
   if (j == n - 1)
     for (int32_t t = t_last + 1; t <= ntiles; ++t) tile_start[t] = row0 + n;
+}
+__device__ __forceinline__ void write_tile_index(const int32_t* __restrict__ rows, int32_t n,
+                                                 int32_t T, int32_t j,
+                                                 int32_t* __restrict__ tile_start,
+                                                 int32_t pos0, int32_t row0) {
+  write_tile_index_pq(rows[j] - pos0, j > 0 ? rows[j - 1] - pos0 : -1, n, T, j, tile_start, row0);
 }
 
 // lower_bound over an ascending array, computed by a whole 256-thread block in

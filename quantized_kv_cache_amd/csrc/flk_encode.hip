@@ -594,12 +594,12 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
   int32_t pos[2];
   auto issue = [&](int32_t j, auto B) {
     constexpr int b = decltype(B)::value;
+    xa[b] = buf_ld128<kCacheStream>(xrs, xv, uint32_t(j) * xrow);   // independent of the position
+    xb[b] = buf_ld128<kCacheStream>(xrs, xv + 2u * hoff, uint32_t(j) * xrow);
     int32_t p = SPARSE ? uniform(rows[j]) - a.pos0 : j;
     if (SPARSE && uint32_t(p) >= uint32_t(T)) p = -1;       // malformed map: skip the row
     pos[b] = p;
     const uint32_t pr = uint32_t(max(p, 0));
-    xa[b] = buf_ld128<kCacheStream>(xrs, xv, uint32_t(j) * xrow);
-    xb[b] = buf_ld128<kCacheStream>(xrs, xv + 2u * hoff, uint32_t(j) * xrow);
     if (RESID) {
       ra[b] = buf_ld128(rrs, xv, pr * xrow);
       rb[b] = buf_ld128(rrs, xv + 2u * hoff, pr * xrow);
@@ -608,7 +608,6 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
   uint32_t err = 0;
   auto process = [&](int32_t j, auto B) {
     constexpr int b = decltype(B)::value;
-    if (SPARSE && lane == 0 && by == 0) write_tile_index(rows, n, T, j, tile_start, a.pos0, a.row0);
     const int32_t p = pos[b];
     if (SPARSE && p < 0) { err |= kDevRows; return; }
     float v[kCh], r[kCh];
@@ -652,12 +651,40 @@ __device__ __forceinline__ void encode_v_wide_body(const EncArgs& a, int32_t row
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   issue(j0, B0{});
-  for (int32_t j = j0; j < j1; j += 2) {
-    if (j + 1 < j1) issue(j + 1, B1{});
-    process(j, B0{});
-    if (j + 1 >= j1) break;
-    if (j + 2 < j1) issue(j + 2, B0{});
-    process(j + 1, B1{});
+  if (!SPARSE) {
+    for (int32_t j = j0; j < j1; j += 2) {
+      if (j + 1 < j1) issue(j + 1, B1{});
+      process(j, B0{});
+      if (j + 1 >= j1) break;
+      if (j + 2 < j1) issue(j + 2, B0{});
+      process(j + 1, B1{});
+    }
+  } else {
+    // Compact loops: inside the loop every row is processed with exactly one younger set of
+    // loads in flight, and the last one or two rows take their own code path (a row reached
+    // both with and without a younger set makes the wait before it a wait for every
+    // outstanding load, the prefetch included).
+    int32_t j = j0;
+    for (; j + 2 < j1; j += 2) {
+      issue(j + 1, B1{});
+      process(j, B0{});
+      issue(j + 2, B0{});
+      process(j + 1, B1{});
+    }
+    if (j + 1 < j1) {
+      issue(j + 1, B1{});
+      process(j, B0{});
+      process(j + 1, B1{});
+    } else {
+      process(j, B0{});
+    }
+    // The tile index entries of the wave's rows, once its rows are done: stores of a varying
+    // count inside the row loop would likewise turn the waits there into waits for every
+    // outstanding load.
+    if (by == 0) {
+      for (int32_t jb = j0; jb < j1; jb += 64)
+        if (jb + lane < j1) write_tile_index(rows, n, T, jb + lane, tile_start, a.pos0, a.row0);
+    }
   }
   if (err && status) atomicOr(status, err);
 }
