@@ -25,7 +25,7 @@ K, V = 0, 1
 KGROUP_ROWS, KGROUP_TILE = 0, 1
 GROUP = 64
 MAX_LOOPS = 8
-DEV_NONFINITE, DEV_RANGE = 1, 2
+DEV_NONFINITE, DEV_RANGE, DEV_ROWS = 1, 2, 4
 
 
 class FlkError(RuntimeError):
