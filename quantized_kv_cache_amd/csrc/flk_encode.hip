@@ -699,23 +699,29 @@ static bool v_wide_ok(int32_t H, int32_t D) { return D % 64 == 0 && (H * D) % 10
 // Rows per wave of the wide V encoder: about kVWideWaves waves per launch -- many short waves
 // (one or two rows each) keep the most loads in flight and let the wave scheduler hide their
 // latency.
-static int32_t v_wide_rpw(int32_t n, int32_t W) {
+// (host and device: the batched kernel derives each unit's grid from its sizes)
+__host__ __device__ inline int32_t v_wide_rpw(int32_t n, int32_t W) {
   const int64_t per_wave = (int64_t(n) * (W / 1024) + kVWideWaves - 1) / kVWideWaves;
   return int32_t(per_wave < 1 ? 1 : per_wave);
 }
-static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) {
+__host__ __device__ inline uint32_t v_wide_grid_x(int32_t n, int32_t rpw) {
   const int32_t waves = (n + rpw - 1) / rpw;
-  return dim3(unsigned((waves + 3) / 4), unsigned(W / 1024));
+  return uint32_t((waves + 3) / 4);
 }
+static dim3 v_wide_grid(int32_t n, int32_t W, int32_t rpw) { return dim3(v_wide_grid_x(n, rpw), unsigned(W / 1024)); }
 // x: channel strips, y: 64-row bands; tile groups of a compact loop: one wave per (tile,
 // 64-channel strip), 4 waves per block along x
-static dim3 k_grid(const EncArgs& a, bool sparse) {
-  if (sparse && a.ktile) {
-    const int64_t waves = int64_t((a.W / 8 + 7) / 8) * ((a.T + kGroup - 1) / kGroup);
-    return dim3(unsigned((waves + 3) / 4), 1);
+__host__ __device__ inline uint32_t k_grid_x(int32_t W, int32_t T, bool sparse, bool ktile) {
+  if (sparse && ktile) {
+    const int64_t waves = int64_t((W / 8 + 7) / 8) * ((T + kGroup - 1) / kGroup);
+    return uint32_t((waves + 3) / 4);
   }
   const int chunks = (sparse ? k_block_channels<true>() : k_block_channels<false>()) / 8;
-  return dim3(unsigned((a.W / 8 + chunks - 1) / chunks), unsigned((a.n + kGroup - 1) / kGroup));
+  return uint32_t((W / 8 + chunks - 1) / chunks);
+}
+static dim3 k_grid(const EncArgs& a, bool sparse) {
+  if (sparse && a.ktile) return dim3(k_grid_x(a.W, a.T, true, true), 1);
+  return dim3(k_grid_x(a.W, a.T, sparse, false), unsigned((a.n + kGroup - 1) / kGroup));
 }
 
 template <bool RESID, bool SPARSE>
@@ -796,45 +802,67 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream
 // a block finds its unit with a scan of the (scalar) block offsets and runs that kind's body.
 // V tensors take the wide body only, so a V unit needs D % 64 == 0 and H*D % 1024 == 0.
 // ---------------------------------------------------------------------------------------
+// What a unit's encode needs beyond the batch's shared fields (status word, K grouping),
+// packed so that kEncBatch units fit the kernel-argument space; its kind is a bit of the
+// batch and its grid is derived from its sizes, as the host derived it.
 struct EncUnit {
-  EncArgs a;
-  int32_t kind;
-  uint32_t gx;        // blocks along the unit's first grid axis
-  int32_t rpw;        // V: rows per wave
+  const uint16_t* x;
+  const int32_t* rows;
+  uint16_t* recon;
+  uint8_t* codes;
+  uint32_t* params;
+  int32_t* tile_start;
+  int32_t n, T, W, pos0, row0;
   uint32_t block0;    // first block of the unit in the launch
 };
 struct EncBatch {
-  EncUnit u[kEncBatch];
+  uint32_t* status;
+  uint64_t v_units;   // bit i: unit i is a V tensor
   int32_t n_units;
+  int32_t ktile;      // the K units' grouping (one K descriptor per call)
+  EncUnit u[kEncBatch];
 };
 
+static_assert(kEncBatch <= 64, "one kind bit per unit");
 static_assert(sizeof(EncBatch) <= 4096, "a batch travels as kernel arguments (4 KiB at most)");
 
-template <bool RESID, bool SPARSE, bool KTILE>
-__global__ __launch_bounds__(kThreads) void encode_batch_kernel(EncBatch b) {
-  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ EncArgs unit_args(const EncBatch& b, const EncUnit& u, bool is_v) {
+  return EncArgs{u.x, u.rows, u.recon, u.codes, u.params, u.tile_start, b.status, u.n, u.T, u.W, u.pos0, u.row0,
+                 is_v ? 0 : b.ktile};
+}
+
+// The unit of a block: the last unit whose first block is at or below it (a scan of scalars).
+__device__ __forceinline__ int batch_unit(const EncBatch& b, uint32_t bid) {
   int ui = 0;
 #pragma unroll
   for (int i = 1; i < kEncBatch; ++i)
     if (i < b.n_units && bid >= b.u[i].block0) ui = i;
+  return ui;
+}
+
+template <bool RESID, bool SPARSE, bool KTILE>
+__global__ __launch_bounds__(kThreads) void encode_batch_kernel(EncBatch b) {
+  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ui = batch_unit(b, bid);
   const EncUnit& u = b.u[ui];
+  const bool is_v = ((b.v_units >> ui) & 1u) != 0;
+  const EncArgs a = unit_args(b, u, is_v);
+  const int32_t rpw = is_v ? v_wide_rpw(u.n, u.W) : 0;
+  const uint32_t gx = is_v ? v_wide_grid_x(u.n, rpw) : k_grid_x(u.W, u.T, SPARSE, KTILE);
   const uint32_t lb = bid - u.block0;
-  const uint32_t by = lb / u.gx, bx = lb - by * u.gx;
-  if (u.kind == FLK_KIND_K) {
-    if (SPARSE && KTILE) encode_k_tile_body<RESID>(u.a, bx * (kThreads / 64) + (threadIdx.x >> 6));
-    else encode_k_body<RESID, SPARSE>(u.a, bx, by);
+  const uint32_t by = lb / gx, bx = lb - by * gx;
+  if (!is_v) {
+    if (SPARSE && KTILE) encode_k_tile_body<RESID>(a, bx * (kThreads / 64) + (threadIdx.x >> 6));
+    else encode_k_body<RESID, SPARSE>(a, bx, by);
   } else {
-    encode_v_wide_body<RESID, SPARSE>(u.a, u.rpw, bx, by);
+    encode_v_wide_body<RESID, SPARSE>(a, rpw, bx, by);
   }
 }
 
 // The tile indexes of a batch's tile-grouped compact K units, before their encode.
 __global__ __launch_bounds__(kThreads) void tile_index_batch_kernel(EncBatch b) {
-  int ui = 0;
-#pragma unroll
-  for (int i = 1; i < kEncBatch; ++i)
-    if (i < b.n_units && blockIdx.x >= b.u[i].block0) ui = i;
-  tile_index_body(b.u[ui].a, blockIdx.x - b.u[ui].block0);
+  const int ui = batch_unit(b, blockIdx.x);
+  tile_index_body(unit_args(b, b.u[ui], false), blockIdx.x - b.u[ui].block0);
 }
 
 bool encode_batchable(int kind, int32_t H, int32_t D) { return kind == FLK_KIND_K || v_wide_ok(H, D); }
@@ -846,33 +874,34 @@ hipError_t launch_encode_batch(bool resid, bool sparse, const EncArgs* args, con
     uint32_t blocks = 0;
     bool ktile = false;                         // the K units' grouping (one K descriptor per call)
     for (int i = u0; i < n_units && i < u0 + kEncBatch; ++i) {
-      if (args[i].n <= 0) continue;
-      if (kinds[i] == FLK_KIND_K && args[i].ktile) ktile = true;
-      EncUnit& e = b.u[b.n_units++];
-      e.a = args[i];
-      e.kind = kinds[i];
+      const EncArgs& a = args[i];
+      if (a.n <= 0) continue;
+      if (kinds[i] == FLK_KIND_K && a.ktile) ktile = true;
+      if (a.status) b.status = a.status;        // one status word per call
+      const int k = b.n_units++;
+      b.u[k] = EncUnit{a.x, a.rows, a.recon, a.codes, a.params, a.tile_start, a.n, a.T, a.W, a.pos0, a.row0, blocks};
       dim3 g;
       if (kinds[i] == FLK_KIND_K) {
-        g = k_grid(args[i], sparse);
-        e.rpw = 0;
+        g = k_grid(a, sparse);
       } else {
-        e.rpw = v_wide_rpw(args[i].n, args[i].W);
-        g = v_wide_grid(args[i].n, args[i].W, e.rpw);
+        b.v_units |= uint64_t(1) << k;
+        g = v_wide_grid(a.n, a.W, v_wide_rpw(a.n, a.W));
       }
-      e.gx = g.x;
-      e.block0 = blocks;
       blocks += g.x * g.y;
     }
+    b.ktile = ktile ? 1 : 0;
     if (blocks == 0) continue;
     if (sparse && ktile) {
       EncBatch tb{};
+      tb.status = b.status;
+      tb.ktile = 1;
       uint32_t tblocks = 0;
       for (int i = 0; i < b.n_units; ++i) {
-        if (b.u[i].kind != FLK_KIND_K || b.u[i].a.n <= kTileSearchRows) continue;
+        if (((b.v_units >> i) & 1u) != 0 || b.u[i].n <= kTileSearchRows) continue;
         EncUnit& e = tb.u[tb.n_units++];
         e = b.u[i];
         e.block0 = tblocks;
-        tblocks += uint32_t((e.a.n + kThreads - 1) / kThreads);
+        tblocks += uint32_t((e.n + kThreads - 1) / kThreads);
       }
       if (tblocks > 0)
         hipLaunchKernelGGL(tile_index_batch_kernel, dim3(tblocks), dim3(kThreads), 0, stream, tb);

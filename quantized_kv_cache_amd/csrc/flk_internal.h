@@ -40,8 +40,8 @@ struct EncArgs {
 };
 
 // Largest number of tensors one batched launch covers (the unit table travels as kernel
-// arguments, at most 4 KiB).
-constexpr int kEncBatch = 40;
+// arguments, at most 4 KiB; 56 covers every layer's K and V of a 24-layer request).
+constexpr int kEncBatch = 56;
 
 // Encode one loop (base when resid == false); a.rows == nullptr is a dense loop.  The
 // pointers are already offset to the window (codes, params, tile_start).
