@@ -453,12 +453,42 @@ struct GatherArgs {
   float scale;
 };
 
+// The K parameters of the lane's channels 32 kb .. 32 kb + 31 of one key: 16-byte chunks 8 kb ..
+// 8 kb + 7 of the key's 512-byte row ((f16 scale, f16 zero) per channel), 128 contiguous bytes.
+// Loaded lane by lane that would be 8 loads each touching 64 cache lines per wave; instead load i
+// takes chunk 4 i + kb, so a key's 4 lanes read 64 contiguous bytes per load, and a 4 x 4
+// transpose of 8-dword blocks across the 16-lane rows (permlane32 then permlane16 swaps) hands
+// every lane its own chunks: afterwards e[r][0..3] is chunk 8 kb + r and e[r][4..7] chunk
+// 8 kb + 4 + r.  All 4 lanes of a key take this path together or not at all.
+__device__ __forceinline__ void k_params_row(const uint32_t* __restrict__ row, int kb, uint32_t e[4][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {                // block i / 2 is bound for row i / 2
+    const uint4 v = *reinterpret_cast<const uint4*>(row + 4 * (4 * i + kb));
+    uint32_t* d = &e[i >> 1][4 * (i & 1)];
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {                // rows 2, 3 of blocks 0, 1 <-> rows 0, 1 of blocks 2, 3
+    const auto a = __builtin_amdgcn_permlane32_swap(e[0][x], e[2][x], false, false);
+    e[0][x] = a[0]; e[2][x] = a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(e[1][x], e[3][x], false, false);
+    e[1][x] = b[0]; e[3][x] = b[1];
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {                // odd rows of blocks 0, 2 <-> even rows of blocks 1, 3
+    const auto a = __builtin_amdgcn_permlane16_swap(e[0][x], e[1][x], false, false);
+    e[0][x] = a[0]; e[1][x] = a[1];
+    const auto b = __builtin_amdgcn_permlane16_swap(e[2][x], e[3][x], false, false);
+    e[2][x] = b[0]; e[3][x] = b[1];
+  }
+}
+
 // The lane's 32 channels 32 kb .. 32 kb + 31 of key position p of KV head h at the chain's
 // depth, as binary32 values that are exactly the BF16 reconstruction.  One 16-byte code load
 // per loop (the four octets are contiguous); an INT4 V loop's group word is one load (the 32
-// channels lie in one 64-channel group).  The chain's sums bf16(acc) + bf16(d) go through
-// v_dot2_f32_bf16 (add_rounded_bf16x8).  FMT: the chain's stream formats (INT4, or FP4 loops as
-// the fused decode attention takes them).
+// channels lie in one 64-channel group); INT4 K parameters through k_params_row.  The chain's
+// sums bf16(acc) + bf16(d) go through v_dot2_f32_bf16 (add_rounded_bf16x8).  FMT: the chain's
+// stream formats (INT4, or FP4 loops as the fused decode attention takes them).
 template <int KIND, int NL, int FMT>
 __device__ __forceinline__ void gather_row32(const ChainArgs& c, const int32_t* const* maps, int32_t p, int32_t H,
                                              int32_t h, int kb, uint32_t ones, float acc[32]) {
@@ -473,6 +503,11 @@ __device__ __forceinline__ void gather_row32(const ChainArgs& c, const int32_t* 
     const uint32_t cws[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
     uint32_t vw = 0;
     if (KIND == FLK_KIND_V && !loop_fp4<FMT>(l)) vw = st.params[item * 2u + uint32_t(kb >> 1)];
+    uint32_t kp[4][8];
+    if (KIND == FLK_KIND_K && !loop_fp4<FMT>(l)) {
+      const uint32_t row = c.ktile ? uint32_t(p) / kGroup : uint32_t(j) / kGroup;
+      k_params_row(st.params + (row * uint32_t(H) + uint32_t(h)) * kSD, kb, kp);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int oc = 4 * kb + i;
@@ -483,10 +518,11 @@ __device__ __forceinline__ void gather_row32(const ChainArgs& c, const int32_t* 
       } else {
         uint32_t pw[8];
         if (KIND == FLK_KIND_K) {
-          const uint32_t row = c.ktile ? uint32_t(p) / kGroup : uint32_t(j) / kGroup;
-          const uint4* pp = reinterpret_cast<const uint4*>(st.params + (row * uint32_t(H) + uint32_t(h)) * kSD + uint32_t(oc) * 8u);
-          const uint4 a = pp[0], b = pp[1];
-          pw[0] = a.x; pw[1] = a.y; pw[2] = a.z; pw[3] = a.w; pw[4] = b.x; pw[5] = b.y; pw[6] = b.z; pw[7] = b.w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {           // octet i: chunks 8 kb + 2 i and 8 kb + 2 i + 1
+            pw[e] = kp[(2 * i) & 3][4 * (i >> 1) + e];
+            pw[4 + e] = kp[(2 * i + 1) & 3][4 * (i >> 1) + e];
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) pw[e] = vw;
@@ -643,38 +679,82 @@ __global__ __launch_bounds__(kSThreads) void sparse_gather_kernel(GatherArgs g) 
   }
 }
 
-// Per query head (block), thread c = channel: merge the blocks' partials.
-// MODE 0: mass[qh] = sum of masses, c_ref[qh][c] = sum.  MODE 1: out = O_ref - C_ref + m * o / l.
+// Per query head (block): merge the gather blocks' partials.  Thread (grp, c) = (tid / 128,
+// tid % 128) folds channel c of the blocks grp, grp + kCombGroups, ..., kCombBatch of them per
+// batch of loads (nblk <= kCombGroups * kCombBatch is one batch), and the groups' folds merge
+// through LDS.  MODE 0: mass[qh] = sum of masses, c_ref[qh][c] = sum.  MODE 1: out = O_ref -
+// C_ref + m * o / l, the partials (max, sum, o) merged as in an online softmax.
+constexpr int kCombGroups = 8;
+constexpr int kCombBatch = 8;
 template <int MODE>
-__global__ __launch_bounds__(kSD) void sparse_combine_kernel(const float* __restrict__ part, int32_t nblk,
-                                                             float* __restrict__ mass_out, float* __restrict__ c_out,
-                                                             const float* __restrict__ mass,
-                                                             const float* __restrict__ o_ref,
-                                                             const float* __restrict__ c_ref,
-                                                             uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(kCombGroups * kSD) void sparse_combine_kernel(
+    const float* __restrict__ part, int32_t nblk, float* __restrict__ mass_out, float* __restrict__ c_out,
+    const float* __restrict__ mass, const float* __restrict__ o_ref, const float* __restrict__ c_ref,
+    uint16_t* __restrict__ out) {
+  __shared__ float s_m[kCombGroups], s_l[kCombGroups];
+  __shared__ float s_o[kCombGroups][kSD];
   const int32_t qh = blockIdx.x;
-  const int c = threadIdx.x;
+  const int c = threadIdx.x % kSD, grp = threadIdx.x / kSD;
   const float* pp = part + int64_t(qh) * nblk * (2 + kSD);
+  float M = MODE == 1 ? -__builtin_inff() : 0.0f;           // mode 0: the mass
+  float L = 0.0f, O = 0.0f;
+  for (int32_t b0 = grp; b0 < nblk; b0 += kCombGroups * kCombBatch) {
+    float mb[kCombBatch], lb[kCombBatch], ob[kCombBatch];
+#pragma unroll
+    for (int i = 0; i < kCombBatch; ++i) {
+      const int32_t b = b0 + i * kCombGroups;
+      const bool ok = b < nblk;
+      mb[i] = ok ? pp[b * (2 + kSD)] : (MODE == 1 ? -__builtin_inff() : 0.0f);
+      lb[i] = ok && MODE == 1 ? pp[b * (2 + kSD) + 1] : 0.0f;
+      ob[i] = ok ? pp[b * (2 + kSD) + 2 + c] : 0.0f;
+    }
+    if (MODE == 0) {
+#pragma unroll
+      for (int i = 0; i < kCombBatch; ++i) {
+        M += mb[i];
+        O += ob[i];
+      }
+    } else {
+      float mx = M;
+#pragma unroll
+      for (int i = 0; i < kCombBatch; ++i) mx = fmaxf(mx, mb[i]);
+      const float f0 = M == -__builtin_inff() ? 0.0f : __expf(M - mx);
+      L *= f0;
+      O *= f0;
+#pragma unroll
+      for (int i = 0; i < kCombBatch; ++i) {
+        const float f = mb[i] == -__builtin_inff() ? 0.0f : __expf(mb[i] - mx);
+        L += lb[i] * f;
+        O += ob[i] * f;
+      }
+      M = mx;
+    }
+  }
+  s_o[grp][c] = O;
+  if (c == 0) {
+    s_m[grp] = M;
+    s_l[grp] = L;
+  }
+  __syncthreads();
+  if (grp != 0) return;
   if (MODE == 0) {
-    float m = 0.0f, O = 0.0f;
-#pragma unroll 8
-    for (int32_t b = 0; b < nblk; ++b) {
-      m += pp[b * (2 + kSD)];
-      O += pp[b * (2 + kSD) + 2 + c];
+#pragma unroll
+    for (int i = 1; i < kCombGroups; ++i) {
+      O += s_o[i][c];
+      M += s_m[i];
     }
     c_out[int64_t(qh) * kSD + c] = O;
-    if (c == 0) mass_out[qh] = m;
+    if (c == 0) mass_out[qh] = M;
   } else {
-    float Mx = -__builtin_inff();
-#pragma unroll 8
-    for (int32_t b = 0; b < nblk; ++b) Mx = fmaxf(Mx, pp[b * (2 + kSD)]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll 8
-    for (int32_t b = 0; b < nblk; ++b) {
-      const float mb = pp[b * (2 + kSD)];
-      const float f = mb == -__builtin_inff() ? 0.0f : __expf(mb - Mx);
-      L += pp[b * (2 + kSD) + 1] * f;
-      O += pp[b * (2 + kSD) + 2 + c] * f;
+#pragma unroll
+    for (int i = 1; i < kCombGroups; ++i) M = fmaxf(M, s_m[i]);
+    L = 0.0f;
+    O = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCombGroups; ++i) {
+      const float f = s_m[i] == -__builtin_inff() ? 0.0f : __expf(s_m[i] - M);
+      L += s_l[i] * f;
+      O += s_o[i][c] * f;
     }
     const int64_t i = int64_t(qh) * kSD + c;
     const float c_new = L > 0.0f ? mass[qh] * (O / L) : 0.0f;
@@ -715,16 +795,31 @@ size_t sparse_workspace_bytes(int32_t T, int32_t H, int32_t Hq, int32_t k, int32
   return sparse_layout(T, H, Hq, k, n_loops).total;
 }
 
-static hipError_t build_maps(const ChainArgs& c, int32_t T, int32_t* base, const int32_t** maps, hipStream_t stream) {
+// One launch builds the maps of every compact loop of both chains.  A V loop that shares its
+// rows and tile index with a K loop (one selection stored once) reuses the K loop's map.
+static hipError_t build_maps(const ChainArgs* kc, const ChainArgs& vc, int32_t T, int32_t* kbase, int32_t* vbase,
+                             const int32_t** kmaps, const int32_t** vmaps, hipStream_t stream) {
   MapJobs jobs{};
   jobs.T = T;
   const size_t stride = align256(size_t(T) * sizeof(int32_t)) / sizeof(int32_t);
-  for (int l = 0; l < FLK_MAX_LOOPS; ++l) maps[l] = nullptr;
-  for (int l = 0; l < c.n_loops; ++l) {
-    if (c.s[l].rows == nullptr) continue;
-    int32_t* m = base + size_t(l) * stride;
-    jobs.j[jobs.n_jobs++] = MapJob{c.s[l].rows, c.s[l].tile_start, m, c.s[l].n};
-    maps[l] = m;
+  for (int l = 0; l < FLK_MAX_LOOPS; ++l) kmaps[l] = vmaps[l] = nullptr;
+  if (kc != nullptr) {
+    for (int l = 0; l < kc->n_loops; ++l) {
+      if (kc->s[l].rows == nullptr) continue;
+      int32_t* m = kbase + size_t(l) * stride;
+      jobs.j[jobs.n_jobs++] = MapJob{kc->s[l].rows, kc->s[l].tile_start, m, kc->s[l].n};
+      kmaps[l] = m;
+    }
+  }
+  for (int l = 0; l < vc.n_loops; ++l) {
+    if (vc.s[l].rows == nullptr) continue;
+    for (int i = 0; i < jobs.n_jobs && vmaps[l] == nullptr; ++i)
+      if (jobs.j[i].rows == vc.s[l].rows && jobs.j[i].tile_start == vc.s[l].tile_start && jobs.j[i].n == vc.s[l].n)
+        vmaps[l] = jobs.j[i].map;
+    if (vmaps[l] != nullptr) continue;
+    int32_t* m = vbase + size_t(l) * stride;
+    jobs.j[jobs.n_jobs++] = MapJob{vc.s[l].rows, vc.s[l].tile_start, m, vc.s[l].n};
+    vmaps[l] = m;
   }
   if (jobs.n_jobs == 0) return hipSuccess;
   const int32_t ntiles = (T + kGroup - 1) / kGroup;
@@ -797,7 +892,9 @@ hipError_t launch_sparse_reference(int fmt, int32_t T, int32_t H, int32_t Hq, in
   GatherArgs g{};
   g.kc = kc;
   g.vc = vc;
-  if ((e = build_maps(vc, T, reinterpret_cast<int32_t*>(w + L.vmaps), g.vmap, stream)) != hipSuccess) return e;
+  if ((e = build_maps(nullptr, vc, T, nullptr, reinterpret_cast<int32_t*>(w + L.vmaps), g.kmap, g.vmap, stream)) !=
+      hipSuccess)
+    return e;
   g.sel = sel;
   g.scores = scores;
   g.ml = ml;
@@ -809,8 +906,8 @@ hipError_t launch_sparse_reference(int fmt, int32_t T, int32_t H, int32_t Hq, in
   g.nblk = gather_blocks(k);
   g.scale = scale;
   if ((e = launch_gather<0>(g, vc.n_loops, fmt, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_combine_kernel<0>), dim3(unsigned(Hq)), dim3(kSD), 0, stream, g.part, g.nblk, mass,
-                     c_ref, nullptr, nullptr, nullptr, nullptr);
+  hipLaunchKernelGGL((sparse_combine_kernel<0>), dim3(unsigned(Hq)), dim3(kCombGroups * kSD), 0, stream, g.part,
+                     g.nblk, mass, c_ref, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -827,9 +924,9 @@ hipError_t launch_sparse_loop(int fmt, int32_t T, int32_t H, int32_t Hq, int32_t
   GatherArgs g{};
   g.kc = kc;
   g.vc = vc;
-  hipError_t e = build_maps(kc, T, reinterpret_cast<int32_t*>(w + L.kmaps), g.kmap, stream);
+  hipError_t e = build_maps(&kc, vc, T, reinterpret_cast<int32_t*>(w + L.kmaps),
+                            reinterpret_cast<int32_t*>(w + L.vmaps), g.kmap, g.vmap, stream);
   if (e != hipSuccess) return e;
-  if ((e = build_maps(vc, T, reinterpret_cast<int32_t*>(w + L.vmaps), g.vmap, stream)) != hipSuccess) return e;
   g.q = static_cast<const uint16_t*>(q);
   g.sel = sel;
   g.part = reinterpret_cast<float*>(w + L.part);
@@ -840,8 +937,8 @@ hipError_t launch_sparse_loop(int fmt, int32_t T, int32_t H, int32_t Hq, int32_t
   g.nblk = gather_blocks(k);
   g.scale = scale;
   if ((e = launch_gather<1>(g, nl, fmt, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((sparse_combine_kernel<1>), dim3(unsigned(Hq)), dim3(kSD), 0, stream, g.part, g.nblk, nullptr,
-                     nullptr, mass, o_ref, c_ref, static_cast<uint16_t*>(out));
+  hipLaunchKernelGGL((sparse_combine_kernel<1>), dim3(unsigned(Hq)), dim3(kCombGroups * kSD), 0, stream, g.part,
+                     g.nblk, nullptr, nullptr, mass, o_ref, c_ref, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
