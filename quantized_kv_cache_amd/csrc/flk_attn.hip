@@ -471,9 +471,11 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
                               size_t ws_bytes, hipStream_t stream) {
   if (ws == nullptr || ws_bytes < attn_workspace_need(T, tail_len, H, Hq)) return hipErrorInvalidValue;
   const int32_t tiles = attn_tiles(T, tail_len);
-  // INT4 chains with packed tokens take the two-pass reader (the score-writing call only
-  // without a tail, whose scores rows count the packed positions alone)
-  const bool two_pass = FMT == 0 && T > 0 && (!SC || tail_len == 0);
+  // Chains with packed tokens take the two-pass reader (the score-writing call only without a
+  // tail, whose scores rows count the packed positions alone); FP4 chains without a tail and of
+  // at most kSplitFp4Loops loops
+  const bool two_pass = T > 0 && (!SC || tail_len == 0) &&
+                        (FMT == 0 || (tail_len == 0 && kc.n_loops <= kSplitFp4Loops && vc.n_loops <= kSplitFp4Loops));
   const int32_t nw = two_pass ? kSplitAttnWaves : kAttnWaves;
   const int32_t wph = waves_per_head(tiles, H, nw);
   const int32_t splits = n_splits(tiles, H, nw);
@@ -491,7 +493,7 @@ static hipError_t launch_attn(int32_t T, int32_t H, int32_t Hq, const void* q, c
     // from the V codes (the tail's V as stored)
     float* block_max = ws_o + size_t(splits) * Hq * kAttnD;
     float* sc = SC ? scores : block_max + size_t(splits) * Hq;
-    const hipError_t e = launch_attn_split(0, T, H, Hq, q, kc, vc, k_tail, v_tail, tail_len, scale, wph, splits, sc,
+    const hipError_t e = launch_attn_split(FMT, T, H, Hq, q, kc, vc, k_tail, v_tail, tail_len, scale, wph, splits, sc,
                                            block_max, ws_ml, ws_o, stream);
     if (e != hipSuccess) return e;
   } else {

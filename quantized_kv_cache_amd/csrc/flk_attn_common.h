@@ -25,6 +25,7 @@ constexpr int kAttnWaves = FLK_ATTN_WAVES;    // aim for about this many waves p
 #define FLK_SPLIT_ATTN_WAVES 4096
 #endif
 constexpr int kSplitAttnWaves = FLK_SPLIT_ATTN_WAVES;
+constexpr int kSplitFp4Loops = 4;          // FP4 chains up to this depth take the two-pass reader
 #ifndef FLK_ATTN_OCC
 #define FLK_ATTN_OCC 3   // waves per SIMD the register budget must allow
 #endif

@@ -56,13 +56,16 @@ struct ScoreLds {
 // lane past the end decodes a copy of the last row, whose score goes nowhere (an MFMA output
 // row depends on its own input row only).  A compact loop's absent token reads row 0 and
 // skips the decode.  So every load is unconditional and no register needs a default value.
+// An FP4 loop (FMT) adds the lane's block scale bytes: NVFP4 the E4M3 bytes of its two 16-channel
+// blocks (2 kb, 2 kb + 1), MXFP4 the E8M0 byte of its 32-channel block kb.
 template <int NL>
 struct KSliceLoads {
   int32_t j[NL];
   uint4 cw[NL];
+  uint32_t sw[NL];
 };
 
-template <int NL>
+template <int NL, int FMT>
 __device__ __forceinline__ void issue_k_slice(const ChainArgs& c, const TileRows<NL>& r, int32_t t, int32_t T,
                                               int32_t H, int32_t h, int kb, const int32_t (*map)[kGroup],
                                               int tk, KSliceLoads<NL>& ld) {
@@ -71,25 +74,49 @@ __device__ __forceinline__ void issue_k_slice(const ChainArgs& c, const TileRows
     ld.j[l] = r.dense[l] ? min(t, T - 1) : map[l][tk];
     const uint32_t item = uint32_t(max(ld.j[l], 0)) * uint32_t(H) + uint32_t(h);
     ld.cw[l] = *reinterpret_cast<const uint4*>(c.s[l].codes + (item * (kAttnD / 2) + 16u * uint32_t(kb)));
+    if (loop_fp4<FMT>(l)) {
+      const uint8_t* pb = reinterpret_cast<const uint8_t*>(c.s[l].params);
+      ld.sw[l] = loop_mx<FMT>(l)
+                     ? uint32_t(pb[item * 4u + uint32_t(kb)])
+                     : uint32_t(*reinterpret_cast<const uint16_t*>(pb + 16u + item * 8u + 2u * uint32_t(kb)));
+    }
   }
 }
 
 // K_hat of the lane's item i (8 channels), packed BF16 for the MFMA: the chain's
-// bf16(... bf16(bf16(base) + bf16(d2)) ... + bf16(dR)) with d = RN(code * s + m).
-template <int NL>
+// bf16(... bf16(bf16(base) + bf16(d2)) ... + bf16(dR)) with d = RN(code * s + m) for an INT4
+// loop and d = RN(e2m1 * block scale) for an FP4 loop (as flk_reconstruct decodes them).
+template <int NL, int FMT>
 __device__ __forceinline__ uint4 decode_k_item(const ChainArgs& c, const KSliceLoads<NL>& ld, int kb, int i,
                                                const ScoreLds<NL>& L, uint32_t ones) {
   float acc[8];
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
     if (l > 0 && ld.j[l] < 0) continue;                  // the base is dense: every lane decodes it
+    const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
+    if (loop_fp4<FMT>(l)) {
+      float d[8], bs;
+      if (loop_mx<FMT>(l)) {
+        bs = fp4_e8m0_value(ld.sw[l] & 0xFFu);
+      } else {                                           // item i lies in the lane's block i / 2
+        const fp4_f32x2 s2 = e4m3x2_value(ld.sw[l]);
+        bs = (i < 2 ? s2.x : s2.y) * __uint_as_float(c.s[l].params[0]);
+      }
+      fp4_decode8(cwi, bs, d);
+      if (l == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = d[e];
+      } else {
+        add_rounded_bf16x8(acc, d, ones);
+      }
+      continue;
+    }
     const int rg = c.ktile ? 0 : (ld.j[l] / kGroup) & 1;   // staged by rowgroup parity
     const float4 s0 = *reinterpret_cast<const float4*>(&L.ks[l][rg][kb][8 * i]);
     const float4 s1 = *reinterpret_cast<const float4*>(&L.ks[l][rg][kb][8 * i + 4]);
     const uint4 mw = *reinterpret_cast<const uint4*>(&L.km[l][rg][kb][8 * i]);
     const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     const uint32_t mv[4] = {mw.x, mw.y, mw.z, mw.w};
-    const uint32_t cwi = i == 0 ? ld.cw[l].x : i == 1 ? ld.cw[l].y : i == 2 ? ld.cw[l].z : ld.cw[l].w;
     uint32_t wq[4];
     codes8_to_f16_halves(cwi, wq);
     float d[8];
@@ -110,7 +137,7 @@ __device__ __forceinline__ uint4 decode_k_item(const ChainArgs& c, const KSliceL
 
 // One slice: decode K_hat, S^T = K_hat Q^T on the MFMA, the scaled scores to their positions'
 // entries of the scores rows and into the running maximum.
-template <int NL>
+template <int NL, int FMT>
 __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoads<NL>& ld, int kb,
                                             const ScoreLds<NL>& L, uint32_t ones, const bf16x8_t qb[4], int sl,
                                             int32_t n_valid, int32_t t0, int n, int32_t G, float scale,
@@ -119,7 +146,7 @@ __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoa
   float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const uint4 item = decode_k_item<NL>(kc, ld, kb, ks, L, ones);
+    const uint4 item = decode_k_item<NL, FMT>(kc, ld, kb, ks, L, ones);
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item), qb[ks], sacc, 0, 0, 0);
   }
 #pragma unroll
@@ -135,7 +162,7 @@ __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoa
 
 // TAIL: the call has a BF16 tail (an instance of its own, so the packed-only loop keeps its
 // register allocation).
-template <int NL, bool TAIL>
+template <int NL, bool TAIL, int FMT>
 __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(ChainArgs kc, int32_t T, int32_t H, int32_t G,
                                                                    const uint16_t* __restrict__ q, float scale,
                                                                    int32_t wph, float* __restrict__ scores,
@@ -201,7 +228,7 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
     build_maps<NL>(kc, rk, t0, L.map, lane);
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      if (l >= kc.n_loops) continue;
+      if (l >= kc.n_loops || loop_fp4<FMT>(l)) continue;  // an FP4 loop's scales come per token
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         int32_t row;                                      // the parameter row staged in slot r
@@ -248,21 +275,21 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
     // two slices' loads in flight: slice sl + 1 is requested before slice sl is decoded (the
     // loop takes the slices in pairs, so each slice's loads have fixed registers)
     KSliceLoads<NL> la, lb;
-    issue_k_slice<NL>(kc, rk, t0 + L.perm[n], T, H, h, kb, L.map, L.perm[n], la);
+    issue_k_slice<NL, FMT>(kc, rk, t0 + L.perm[n], T, H, h, kb, L.map, L.perm[n], la);
 #pragma nounroll
     for (int sl = 0; sl * 16 < n_valid; sl += 2) {
       const bool second = (sl + 1) * 16 < n_valid;
       if (second) {
         const int tk = L.perm[16 * (sl + 1) + n];
-        issue_k_slice<NL>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, lb);
+        issue_k_slice<NL, FMT>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, lb);
       }
-      score_slice<NL>(kc, la, kb, L, ones, qb, sl, n_valid, t0, n, G, scale, srow, mx);
+      score_slice<NL, FMT>(kc, la, kb, L, ones, qb, sl, n_valid, t0, n, G, scale, srow, mx);
       if (!second) break;
       if ((sl + 2) * 16 < n_valid) {
         const int tk = L.perm[16 * (sl + 2) + n];
-        issue_k_slice<NL>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, la);
+        issue_k_slice<NL, FMT>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, la);
       }
-      score_slice<NL>(kc, lb, kb, L, ones, qb, sl + 1, n_valid, t0, n, G, scale, srow, mx);
+      score_slice<NL, FMT>(kc, lb, kb, L, ones, qb, sl + 1, n_valid, t0, n, G, scale, srow, mx);
     }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -305,7 +332,7 @@ union PvLds {
   } merge;
 };
 
-template <int NL>
+template <int NL, int FMT>
 __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int32_t T, int32_t H, int32_t G,
                                                                const float* __restrict__ scores,
                                                                const float* __restrict__ block_max, int32_t wph,
@@ -392,7 +419,11 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
     const int32_t b = dense ? P1 : uniform(st.tile_start[tile1]);
     const uint32_t nbytes = uint32_t(st.n) * uint32_t(H);
     const BufRsrc cb = make_buf(st.codes, nbytes * (kAttnD / 2));
-    const BufRsrc pb = make_buf(st.params, nbytes * 8u);
+    // parameter bytes per row: INT4 two (min, scale) words; NVFP4 8 E4M3 bytes after a 16-byte
+    // header; MXFP4 4 E8M0 bytes (staged in the row's first word)
+    const bool fp4 = loop_fp4<FMT>(l), mx = loop_mx<FMT>(l);
+    const uint32_t p_hdr = fp4 && !mx ? 16u : 0u, p_row = mx ? 4u : 8u;
+    const BufRsrc pb = make_buf(st.params, p_hdr + nbytes * p_row);
     const BufRsrc rb = make_buf(dense ? nullptr : st.rows, dense ? 0u : uint32_t(st.n) * 4u);
     // batches of kPvBatch 16-row slices: every load of a batch (staging, positions, scores)
     // goes out before any of it is used, so a batch costs one exposed round trip, not one per slice
@@ -405,8 +436,9 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
         const int32_t jc = j0 + crow, jp = j0 + prow;
         const uint32_t co = jc < b ? (uint32_t(jc) * uint32_t(H) + uint32_t(h)) * (kAttnD / 2) + 16u * uint32_t(cq)
                                    : kOutOfRange;
-        const uint32_t po = lane < 32 && jp < b ? (uint32_t(jp) * uint32_t(H) + uint32_t(h)) * 8u + 4u * uint32_t(lane & 1)
-                                                : kOutOfRange;
+        const uint32_t po = lane < 32 && jp < b && !(mx && (lane & 1))
+                                ? p_hdr + (uint32_t(jp) * uint32_t(H) + uint32_t(h)) * p_row + 4u * uint32_t(lane & 1)
+                                : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(cb, (lds_ptr_t)&Sw[sb].codes[0][0], 16, co, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(pb, (lds_ptr_t)&Sw[sb].params[0], 4, po, 0, 0, 0);
       }
@@ -454,6 +486,51 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
           const uint32_t hi = cr[(16 * pv_chunk(row, 2 + (n >> 3)) + ((2 * n) & 15)) >> 1];
           d[r] = lo | (hi << 16);
           vpw[r] = *reinterpret_cast<const uint2*>(&S.params[2 * row]);
+        }
+        if (fp4) {
+          // FP4: A = e2m1 * block scale per element (exact in BF16), B = p (times the NVFP4
+          // stream scale) in BF16, on the BF16 MFMA.  Tile mt's channel of this lane lies in
+          // channel group g = mt / 4, block 4 g + n / 4 (NVFP4) or 2 g + n / 8 (MXFP4).
+          const float gs = mx ? 1.0f : __uint_as_float(st.params[0]);
+          short4_t bp;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bp[r] = short(__builtin_bit_cast(uint16_t, (__bf16)(p[r] * gs)));
+          float sc[4][2];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (mx) {
+              sc[r][0] = fp4_e8m0_value((vpw[r].x >> (8 * (n >> 3))) & 0xFFu);
+              sc[r][1] = fp4_e8m0_value((vpw[r].x >> (8 * (2 + (n >> 3)))) & 0xFFu);
+            } else {                                     // bytes n / 4 of both words, one conversion
+              const uint32_t bsel = uint32_t(n >> 2);
+              const fp4_f32x2 s2 = e4m3x2_value(__builtin_amdgcn_perm(vpw[r].y, vpw[r].x, bsel | ((4u + bsel) << 8)));
+              sc[r][0] = s2.x;
+              sc[r][1] = s2.y;
+            }
+          }
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt) {
+            const uint32_t bsel = uint32_t(mt >> 1);
+            const uint32_t sel = bsel | ((4u + bsel) << 8) | 0x0C0C0000u;   // [x0.b, x1.b, 0, 0]
+            uint32_t x01 = __builtin_amdgcn_perm(d[1], d[0], sel), x23 = __builtin_amdgcn_perm(d[3], d[2], sel);
+            if (mt & 1) {                                  // high nibbles: one byte of two codes
+              x01 = ((x01 >> 4) & 0x0Fu) | ((x01 >> 8) & 0xF0u);
+              x23 = ((x23 >> 4) & 0x0Fu) | ((x23 >> 8) & 0xF0u);
+            } else {
+              x01 = (x01 & 0x0Fu) | ((x01 >> 4) & 0xF0u);
+              x23 = (x23 & 0x0Fu) | ((x23 >> 4) & 0xF0u);
+            }
+            const fp4_f32x2 v01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x01, 1.0f, 0);
+            const fp4_f32x2 v23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x23, 1.0f, 0);
+            const int g = mt >> 2;
+            short4_t av;
+            av[0] = short(__builtin_bit_cast(uint16_t, (__bf16)(v01.x * sc[0][g])));
+            av[1] = short(__builtin_bit_cast(uint16_t, (__bf16)(v01.y * sc[1][g])));
+            av[2] = short(__builtin_bit_cast(uint16_t, (__bf16)(v23.x * sc[2][g])));
+            av[3] = short(__builtin_bit_cast(uint16_t, (__bf16)(v23.y * sc[3][g])));
+            o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, o[mt], 0, 0, 0);
+          }
+          continue;
         }
         f16x4_t bg[2];
 #pragma unroll
@@ -519,6 +596,52 @@ __global__ __launch_bounds__(kAThreads, 4) void attn_pv_kernel(ChainArgs vc, int
   }
 }
 
+// The two passes of one stream format; FP4 chains (FMT 1..4) of at most kSplitFp4Loops loops and
+// without a tail.
+template <int FMT, bool TL>
+static hipError_t launch_split_fmt(const dim3& grid, const ChainArgs& kc, const ChainArgs& vc, int32_t T, int32_t H,
+                                   int32_t G, const uint16_t* qp, float scale, int32_t wph, float* scores,
+                                   float* block_max, float* ws_ml, float* ws_o, const uint16_t* kt,
+                                   const uint16_t* vt, int32_t tail_len, hipStream_t stream) {
+#define FLK_S(NLV)                                                                                         \
+  case NLV:                                                                                                \
+    hipLaunchKernelGGL((attn_scores_kernel<NLV, TL, FMT>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp, \
+                       scale, wph, scores, block_max, kt, tail_len);                                       \
+    break;
+#define FLK_P(NLV)                                                                                         \
+  case NLV:                                                                                                \
+    hipLaunchKernelGGL((attn_pv_kernel<NLV, FMT>), grid, dim3(kAThreads), 0, stream, vc, T, H, G, scores,    \
+                       block_max, wph, ws_ml, ws_o, vt, tail_len);                                         \
+    break;
+  if constexpr (FMT == 0) {
+    switch (kc.n_loops) {
+      FLK_S(1) FLK_S(2) FLK_S(3) FLK_S(4) FLK_S(5) FLK_S(6) FLK_S(7) FLK_S(8)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kc.n_loops) {
+      FLK_S(1) FLK_S(2) FLK_S(3) FLK_S(4)
+      default: return hipErrorInvalidValue;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (FMT == 0) {
+    switch (vc.n_loops) {
+      FLK_P(1) FLK_P(2) FLK_P(3) FLK_P(4) FLK_P(5) FLK_P(6) FLK_P(7) FLK_P(8)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (vc.n_loops) {
+      FLK_P(1) FLK_P(2) FLK_P(3) FLK_P(4)
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef FLK_P
+#undef FLK_S
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_split(int fmt, int32_t T, int32_t H, int32_t Hq, const void* q, const ChainArgs& kc,
                              const ChainArgs& vc, const void* k_tail, const void* v_tail, int32_t tail_len,
                              float scale, int32_t wph, int32_t splits, float* scores, float* block_max, float* ws_ml,
@@ -528,38 +651,19 @@ hipError_t launch_attn_split(int fmt, int32_t T, int32_t H, int32_t Hq, const vo
   const int32_t G = Hq / H;
   const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(H));
   const uint16_t* qp = static_cast<const uint16_t*>(q);
-  const int nlk = kc.n_loops, nlv = vc.n_loops;
-  if (fmt != 0) return hipErrorInvalidValue;
-#define FLK_S(NLV, TL)                                                                                     \
-  case NLV:                                                                                                \
-    hipLaunchKernelGGL((attn_scores_kernel<NLV, TL>), grid, dim3(kAThreads), 0, stream, kc, T, H, G, qp,     \
-                       scale, wph, scores, block_max, kt, tail_len);                                       \
-    break;
-#define FLK_ST(TL)                                                                                         \
-  switch (nlk) {                                                                                           \
-    FLK_S(1, TL) FLK_S(2, TL) FLK_S(3, TL) FLK_S(4, TL) FLK_S(5, TL) FLK_S(6, TL) FLK_S(7, TL) FLK_S(8, TL) \
-    default: return hipErrorInvalidValue;                                                                  \
-  }
-  if (tail_len > 0) {
-    FLK_ST(true)
-  } else {
-    FLK_ST(false)
-  }
-#undef FLK_ST
-#undef FLK_S
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-#define FLK_P(NLV)                                                                                         \
-  case NLV:                                                                                                \
-    hipLaunchKernelGGL((attn_pv_kernel<NLV>), grid, dim3(kAThreads), 0, stream, vc, T, H, G, scores, block_max, \
-                       wph, ws_ml, ws_o, vt, tail_len);                                                    \
-    break;
-  switch (nlv) {
-    FLK_P(1) FLK_P(2) FLK_P(3) FLK_P(4) FLK_P(5) FLK_P(6) FLK_P(7) FLK_P(8)
+  if (fmt != 0 && (tail_len > 0 || kc.n_loops > kSplitFp4Loops || vc.n_loops > kSplitFp4Loops))
+    return hipErrorInvalidValue;
+#define FLK_F(F, TL)                                                                                       \
+  case F:                                                                                                  \
+    return launch_split_fmt<F, TL>(grid, kc, vc, T, H, G, qp, scale, wph, scores, block_max, ws_ml, ws_o, kt, vt, \
+                                   tail_len, stream);
+  if (tail_len > 0) return launch_split_fmt<0, true>(grid, kc, vc, T, H, G, qp, scale, wph, scores, block_max, ws_ml,
+                                                     ws_o, kt, vt, tail_len, stream);
+  switch (fmt) {
+    FLK_F(0, false) FLK_F(1, false) FLK_F(2, false) FLK_F(3, false) FLK_F(4, false)
     default: return hipErrorInvalidValue;
   }
-#undef FLK_P
-  return hipGetLastError();
+#undef FLK_F
 }
 
 }  // namespace flk

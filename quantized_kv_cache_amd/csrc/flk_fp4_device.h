@@ -34,6 +34,14 @@ __device__ __forceinline__ void fp4_decode8(uint32_t cw, float bs, float d[8]) {
   v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3); d[6] = v.x * bs; d[7] = v.y * bs;
 }
 
+// The two E4M3 bytes of 16-bit half HI of w (low byte first) as binary32, by gfx950's
+// v_cvt_scalef32_pk_f32_fp8 with a scale of 1: for the non-negative finite bytes a stream's
+// block scales use, exactly fp4_e4m3_value of each (checked exhaustively on the GPU).
+template <bool HI = false>
+__device__ __forceinline__ fp4_f32x2 e4m3x2_value(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);
+}
+
 // Stream formats of a chain as the readers take them: FMT 0 = INT4 throughout, 1 = INT4 base
 // with NVFP4 residual loops, 2 = NVFP4 throughout, 3 = INT4 base with MXFP4 residual loops,
 // 4 = MXFP4 throughout.

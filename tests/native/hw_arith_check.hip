@@ -13,11 +13,15 @@
 //    and 512 minima (zeros, denormals, both signs, the extremes).
 // 3. The encoders' three-instruction RN(x / 15) (flk::div15) equals the IEEE division for every
 //    finite binary32 x >= +0, denormals included.
+// 4. v_cvt_scalef32_pk_f32_fp8 with scale 1 (flk::e4m3x2_value), either 16-bit half, gives
+//    flk::fp4_e4m3_value of both bytes for every pair of non-negative finite E4M3 bytes (the
+//    NVFP4 block scales the decode-attention readers convert with it).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cstdio>
 
 #include "../../quantized_kv_cache_amd/csrc/flk_device.h"
+#include "../../quantized_kv_cache_amd/csrc/flk_fp4_device.h"
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -93,6 +97,20 @@ __global__ void check_div15(unsigned long long* cnt) {
   if (bad) atomicAdd(&cnt[6], bad);
 }
 
+// grid 256 x 256: block a, thread t checks bytes (a, t) in both halves of the word
+__global__ void check_e4m3(unsigned long long* cnt) {
+  const uint32_t b0 = blockIdx.x, b1 = threadIdx.x;
+  if (b0 >= 0x7Fu || b1 >= 0x7Fu) return;       // non-negative finite bytes only (0x7F is NaN)
+  uint32_t w = b0 | (b1 << 8) | (b0 << 16) | (b1 << 24);
+  asm volatile("" : "+v"(w));                   // a run-time value
+  const flk::fp4_f32x2 lo = flk::e4m3x2_value<false>(w), hi = flk::e4m3x2_value<true>(w);
+  const float e0 = flk::fp4_e4m3_value(b0), e1 = flk::fp4_e4m3_value(b1);
+  const bool ok = __float_as_uint(lo.x) == __float_as_uint(e0) && __float_as_uint(lo.y) == __float_as_uint(e1) &&
+                  __float_as_uint(hi.x) == __float_as_uint(e0) && __float_as_uint(hi.y) == __float_as_uint(e1);
+  atomicAdd(&cnt[7], 1ull);
+  if (!ok) atomicAdd(&cnt[8], 1ull);
+}
+
 int main() {
   uint16_t hm[512];
   uint32_t x = 12345u;
@@ -108,21 +126,23 @@ int main() {
   unsigned long long* cnt = nullptr;
   const uint32_t one2 = 0x3F803F80u;
   if (hipMalloc(&ones, 4) != hipSuccess || hipMalloc(&ms, sizeof(hm)) != hipSuccess ||
-      hipMalloc(&cnt, 8 * 7) != hipSuccess || hipMemcpy(ones, &one2, 4, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(ms, hm, sizeof(hm), hipMemcpyHostToDevice) != hipSuccess || hipMemset(cnt, 0, 8 * 7) != hipSuccess) {
+      hipMalloc(&cnt, 8 * 9) != hipSuccess || hipMemcpy(ones, &one2, 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ms, hm, sizeof(hm), hipMemcpyHostToDevice) != hipSuccess || hipMemset(cnt, 0, 8 * 9) != hipSuccess) {
     printf("setup failed\n");
     return 2;
   }
   hipLaunchKernelGGL(check_dot2, dim3(65536), dim3(256), 0, 0, ones, cnt);
   hipLaunchKernelGGL(check_fma_mix, dim3(0x7C00), dim3(512), 0, 0, ms, cnt);
   hipLaunchKernelGGL(check_div15, dim3(65536), dim3(256), 0, 0, cnt);
-  unsigned long long c[7] = {0, 0, 0, 0, 0, 0, 0};
-  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(c, cnt, 8 * 7, hipMemcpyDeviceToHost) != hipSuccess) {
+  hipLaunchKernelGGL(check_e4m3, dim3(256), dim3(256), 0, 0, cnt);
+  unsigned long long c[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(c, cnt, 8 * 9, hipMemcpyDeviceToHost) != hipSuccess) {
     printf("run failed\n");
     return 2;
   }
   printf("dot2_pairs %llu dot2_bf16_mismatch %llu dot2_inexact_below_16 %llu\n", c[0], c[1], c[2]);
   printf("fma_mix_cases %llu fma_mix_mismatch %llu\n", c[3], c[4]);
   printf("div15_cases %llu div15_mismatch %llu\n", c[5], c[6]);
-  return (c[1] == 0 && c[4] == 0 && c[6] == 0) ? 0 : 1;
+  printf("e4m3_pairs %llu e4m3_mismatch %llu\n", c[7], c[8]);
+  return (c[1] == 0 && c[4] == 0 && c[6] == 0 && c[8] == 0) ? 0 : 1;
 }

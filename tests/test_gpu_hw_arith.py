@@ -7,7 +7,9 @@ encoders rest on, checked exhaustively on the GPU by tests/native/hw_arith_check
   equals fma(code, s, m), for every finite non-negative binary16 scale, every code and 512
   minima;
 * the encoders' three-instruction RN(x / 15) equals the IEEE division for every finite
-  binary32 x >= +0.
+  binary32 x >= +0;
+* v_cvt_scalef32_pk_f32_fp8 with scale 1 gives the E4M3 value of both bytes, in either half of
+  the word, for every pair of non-negative finite E4M3 bytes (the NVFP4 block scales).
 """
 import os
 import subprocess
@@ -39,4 +41,6 @@ def test_hw_arith_facts():
     # every finite binary32 x >= +0
     assert vals["div15_cases"] == 0x7F800000
     assert vals["div15_mismatch"] == 0
+    assert vals["e4m3_pairs"] == 127 * 127
+    assert vals["e4m3_mismatch"] == 0
 
