@@ -88,7 +88,7 @@ __device__ __forceinline__ void issue_k_slice(const ChainArgs& c, const TileRows
 // loop and d = RN(e2m1 * block scale) for an FP4 loop (as flk_reconstruct decodes them).
 template <int NL, int FMT>
 __device__ __forceinline__ uint4 decode_k_item(const ChainArgs& c, const KSliceLoads<NL>& ld, int kb, int i,
-                                               const ScoreLds<NL>& L, uint32_t ones) {
+                                               const ScoreLds<NL>& L, uint32_t ones, const float* gsc) {
   float acc[8];
 #pragma unroll
   for (int l = 0; l < NL; ++l) {
@@ -100,7 +100,7 @@ __device__ __forceinline__ uint4 decode_k_item(const ChainArgs& c, const KSliceL
         bs = fp4_e8m0_value(ld.sw[l] & 0xFFu);
       } else {                                           // item i lies in the lane's block i / 2
         const fp4_f32x2 s2 = e4m3x2_value(ld.sw[l]);
-        bs = (i < 2 ? s2.x : s2.y) * __uint_as_float(c.s[l].params[0]);
+        bs = (i < 2 ? s2.x : s2.y) * gsc[l];
       }
       fp4_decode8(cwi, bs, d);
       if (l == 0) {
@@ -141,12 +141,12 @@ template <int NL, int FMT>
 __device__ __forceinline__ void score_slice(const ChainArgs& kc, const KSliceLoads<NL>& ld, int kb,
                                             const ScoreLds<NL>& L, uint32_t ones, const bf16x8_t qb[4], int sl,
                                             int32_t n_valid, int32_t t0, int n, int32_t G, float scale,
-                                            float* srow, float& mx) {
+                                            float* srow, float& mx, const float* gsc) {
   // each item goes to the MFMA as soon as it is decoded, so one item's registers are live
   float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const uint4 item = decode_k_item<NL, FMT>(kc, ld, kb, ks, L, ones);
+    const uint4 item = decode_k_item<NL, FMT>(kc, ld, kb, ks, L, ones, gsc);
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, item), qb[ks], sacc, 0, 0, 0);
   }
 #pragma unroll
@@ -199,6 +199,11 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
 
   float* srow = scores + int64_t(h * G + (n < G ? n : 0)) * Tpad;
   float mx = -__builtin_inff();
+  // the NVFP4 loops' stream scales, read once (the scores stores in the loop below would
+  // otherwise make the compiler reload them for every slice)
+  float gsc[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) gsc[l] = loop_nv<FMT>(l) && l < kc.n_loops ? __uint_as_float(kc.s[l].params[0]) : 1.0f;
   // The BF16 tail, read as stored, in 16-token slices: slice s goes to waves s, s + wph, ...
   // of every head (a small addition to many waves); its scores follow the packed positions.
   const int32_t tail_slices = (tail_len + 15) / 16;
@@ -283,13 +288,13 @@ __global__ __launch_bounds__(kAThreads, FLK_SCORES_OCC) void attn_scores_kernel(
         const int tk = L.perm[16 * (sl + 1) + n];
         issue_k_slice<NL, FMT>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, lb);
       }
-      score_slice<NL, FMT>(kc, la, kb, L, ones, qb, sl, n_valid, t0, n, G, scale, srow, mx);
+      score_slice<NL, FMT>(kc, la, kb, L, ones, qb, sl, n_valid, t0, n, G, scale, srow, mx, gsc);
       if (!second) break;
       if ((sl + 2) * 16 < n_valid) {
         const int tk = L.perm[16 * (sl + 2) + n];
         issue_k_slice<NL, FMT>(kc, rk, t0 + tk, T, H, h, kb, L.map, tk, la);
       }
-      score_slice<NL, FMT>(kc, lb, kb, L, ones, qb, sl + 1, n_valid, t0, n, G, scale, srow, mx);
+      score_slice<NL, FMT>(kc, lb, kb, L, ones, qb, sl + 1, n_valid, t0, n, G, scale, srow, mx, gsc);
     }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
