@@ -503,6 +503,21 @@ __device__ __forceinline__ void gather_row32(const ChainArgs& c, const int32_t* 
     const uint32_t cws[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
     uint32_t vw = 0;
     if (KIND == FLK_KIND_V && !loop_fp4<FMT>(l)) vw = st.params[item * 2u + uint32_t(kb >> 1)];
+    // an FP4 loop's block scales of the lane's 32 channels, one load per loop: NVFP4 the E4M3
+    // pair of blocks 2 kb, 2 kb + 1 (octets 0-1 and 2-3) times the stream scale, MXFP4 the E8M0
+    // byte of block kb
+    float fs[2] = {0.0f, 0.0f};
+    if (loop_fp4<FMT>(l)) {
+      const uint8_t* pb = reinterpret_cast<const uint8_t*>(st.params);
+      if (loop_mx<FMT>(l)) {
+        fs[0] = fs[1] = fp4_e8m0_value(pb[item * 4u + uint32_t(kb)]);
+      } else {
+        const fp4_f32x2 s2 = e4m3x2_value(*reinterpret_cast<const uint16_t*>(pb + 16u + item * 8u + 2u * uint32_t(kb)));
+        const float gs = __uint_as_float(st.params[0]);
+        fs[0] = s2.x * gs;
+        fs[1] = s2.y * gs;
+      }
+    }
     uint32_t kp[4][8];
     if (KIND == FLK_KIND_K && !loop_fp4<FMT>(l)) {
       const uint32_t row = c.ktile ? uint32_t(p) / kGroup : uint32_t(j) / kGroup;
@@ -510,11 +525,9 @@ __device__ __forceinline__ void gather_row32(const ChainArgs& c, const int32_t* 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int oc = 4 * kb + i;
       float d[8];
       if (loop_fp4<FMT>(l)) {
-        const uint32_t sb = fp4_scale_byte_128(st.params, item, oc, loop_mx<FMT>(l));
-        fp4_decode8(cws[i], loop_mx<FMT>(l) ? fp4_e8m0_value(sb) : fp4_e4m3_value(sb) * __uint_as_float(st.params[0]), d);
+        fp4_decode8(cws[i], fs[i >> 1], d);
       } else {
         uint32_t pw[8];
         if (KIND == FLK_KIND_K) {
