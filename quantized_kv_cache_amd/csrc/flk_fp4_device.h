@@ -52,12 +52,4 @@ __device__ __forceinline__ constexpr bool loop_mx(int l) { return FMT == 4 || (F
 template <int FMT>
 __device__ __forceinline__ constexpr bool loop_fp4(int l) { return loop_nv<FMT>(l) || loop_mx<FMT>(l); }
 
-// The scale byte of the FP4 block holding channel octet oc (8 channels) of item = row * H +
-// head, in a stream whose rows hold H heads of 128 channels: MXFP4 (mx) the block's E8M0 byte,
-// NVFP4 its E4M3 byte after the 16-byte header (whose binary32 s_g multiplies it).
-__device__ __forceinline__ uint32_t fp4_scale_byte_128(const uint32_t* params, uint32_t item, int oc, bool mx) {
-  const uint8_t* b = reinterpret_cast<const uint8_t*>(params);
-  return mx ? b[item * 4u + uint32_t(oc >> 2)] : b[16u + item * 8u + uint32_t(oc >> 1)];
-}
-
 }  // namespace flk
